@@ -1,0 +1,290 @@
+"""Python side of the plain CPU oracle for the QSA MQA indexer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this module.  The product library
+never loads it and shares no code with it.
+
+``qsa_oracle.c`` holds the score, metadata and top-k arithmetic (plain loops,
+double accumulation).  This module compiles it with gcc, marshals numpy arrays
+into it, and splits rows over threads (ctypes releases the GIL for the call,
+and rows are independent).  The batch split is host bookkeeping and is written
+here in plain Python.
+
+Sources (page title, section):
+  "vLLM/vllm/models/qwen4_exp/common/qsa_cache.py", QSAMetadataBuilder.__init__
+  and .build: decode threshold 1 with speculative tokens counted as decode,
+  decodes ordered first, one uniform decode query length over the non-empty
+  decode requests.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "qsa_oracle.c")
+LIB = os.path.join(HERE, "libqsa_oracle.so")
+
+HEADS = 4
+DIM = 128
+
+_lib = None
+
+
+def build(src: str = SRC, out: str = LIB) -> str:
+    """Compile the oracle with gcc.  No fast-math and no FP contraction, so the
+    double arithmetic is exactly what the source says."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    P = ctypes.c_void_p
+    i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.oracle_token_metadata.argtypes = [P, P, i32, i32, i32, P, P, P]
+    lib.oracle_token_metadata.restype = None
+    lib.oracle_comp_lens.argtypes = [P, i32, i32, P]
+    lib.oracle_comp_lens.restype = None
+    lib.oracle_prefill_intervals.argtypes = [P, P, P, i32, P, P]
+    lib.oracle_prefill_intervals.restype = None
+    lib.oracle_decode.argtypes = [P, i64, i64, i64, P, i64, i32, P, i64, i32, P, P,
+                                  i32, i32, f32, P, i64, i32, i32, i32]
+    lib.oracle_decode.restype = None
+    lib.oracle_prefill.argtypes = [P, i64, i64, P, i64, i64, P, P, i32, f32, P, i64,
+                                   i32, i32, i32]
+    lib.oracle_prefill.restype = None
+    lib.oracle_topk.argtypes = [P, i64, i32, i32, P, i64, i32, i32]
+    lib.oracle_topk.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the compiled oracle, building it first if it is missing or older
+    than its source."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        _lib = _declare(ctypes.CDLL(LIB))
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data
+
+
+def _threads(threads: int | None) -> int:
+    if threads is None:
+        threads = int(os.environ.get("QSA_ORACLE_THREADS", "0")) or (os.cpu_count() or 1)
+    return max(1, int(threads))
+
+
+def _run_rows(fn, num_rows: int, threads: int | None) -> int:
+    """Call fn(row_begin, row_end) over [0, num_rows) on a thread pool.
+    Returns the number of threads used."""
+    n = min(_threads(threads), max(num_rows, 1))
+    if n <= 1 or num_rows <= 1:
+        fn(0, num_rows)
+        return 1
+    bounds = np.linspace(0, num_rows, n + 1).astype(np.int64)
+    with ThreadPoolExecutor(max_workers=n) as pool:
+        list(pool.map(lambda i: fn(int(bounds[i]), int(bounds[i + 1])), range(n)))
+    return n
+
+
+# ----------------------------------------------------------------------------
+# a1: batch split and per-token metadata
+
+
+def split_batch(query_start_loc, decode_threshold: int, reorder: bool = False):
+    """Decode/prefill split of one batch.
+
+    A request qualifies as a decode when its query length is between 1 and
+    ``decode_threshold`` and equals the decode query length (DQL): the length
+    of the first request (in batch order) whose length is in that range.
+    Empty requests are not decodes.
+
+    ``reorder=False``: the batch is taken as ordered decodes-first, and the
+    decodes are its longest qualifying prefix.  ``reorder=True``: returns the
+    stable order that puts every qualifying request first.
+
+    Returns (order or None, num_decodes, num_decode_tokens, num_prefills,
+    num_prefill_tokens, dql)."""
+    qsl = [int(x) for x in query_start_loc]
+    num_reqs = len(qsl) - 1
+    lens = [qsl[r + 1] - qsl[r] for r in range(num_reqs)]
+    dql = 0
+    for n in lens:
+        if 1 <= n <= decode_threshold:
+            dql = n
+            break
+    qualifies = [dql > 0 and n == dql for n in lens]
+    if reorder:
+        order = [r for r in range(num_reqs) if qualifies[r]] + \
+                [r for r in range(num_reqs) if not qualifies[r]]
+        num_decodes = sum(qualifies)
+        lens_in_order = [lens[r] for r in order]
+    else:
+        order = None
+        num_decodes = 0
+        while num_decodes < num_reqs and qualifies[num_decodes]:
+            num_decodes += 1
+        lens_in_order = lens
+    num_decode_tokens = sum(lens_in_order[:num_decodes])
+    num_prefill_tokens = sum(lens_in_order[num_decodes:])
+    if num_decodes == 0:
+        dql = 0
+    return (order, num_decodes, num_decode_tokens, num_reqs - num_decodes,
+            num_prefill_tokens, dql)
+
+
+def token_metadata(query_start_loc, seq_lens, num_tokens: int, compress_ratio: int = 4):
+    """Per-token (request, logical position, visible blocks)."""
+    lib = load()
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    req = np.empty(num_tokens, np.int32)
+    pos = np.empty(num_tokens, np.int64)
+    vis = np.empty(num_tokens, np.int32)
+    lib.oracle_token_metadata(_ptr(qsl), _ptr(sl), len(sl), num_tokens, compress_ratio,
+                              _ptr(req), _ptr(pos), _ptr(vis))
+    return req, pos, vis
+
+
+def comp_lens(seq_lens, compress_ratio: int = 4):
+    lib = load()
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    out = np.empty(len(sl), np.int32)
+    lib.oracle_comp_lens(_ptr(sl), len(sl), compress_ratio, _ptr(out))
+    return out
+
+
+def prefill_intervals(token_to_req, visible, key_offsets):
+    lib = load()
+    req = np.ascontiguousarray(token_to_req, dtype=np.int32)
+    vis = np.ascontiguousarray(visible, dtype=np.int32)
+    off = np.ascontiguousarray(key_offsets, dtype=np.int32)
+    ks = np.empty(len(req), np.int32)
+    ke = np.empty(len(req), np.int32)
+    lib.oracle_prefill_intervals(_ptr(req), _ptr(vis), _ptr(off), len(req), _ptr(ks), _ptr(ke))
+    return ks, ke
+
+
+# ----------------------------------------------------------------------------
+# a2/a4: decode, a3/a4: prefill, a5: top-k
+
+
+def default_scale() -> float:
+    """1/sqrt(head_dim) for head_dim 128, as an fp32 multiplier."""
+    return float(np.float32(1.0 / np.sqrt(np.float64(DIM))))
+
+
+def _row_list(rows, total):
+    """None -> every row as one contiguous range; else the given row indices."""
+    if rows is None:
+        return None
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    assert np.all((rows >= 0) & (rows < total))
+    return rows
+
+
+def decode(q_bits, k_pool_bits, page_table, comp_lens_arr, visible, out_cols: int,
+           scale: float | None = None, rows=None, threads: int | None = None):
+    """Decode scores.
+
+    q_bits: uint16 [R, DQL, 4, 128] (any strides, unit feature stride);
+    k_pool_bits: uint16 [P, page_size, 1, 128]; page_table int32 [R, W];
+    comp_lens_arr int32 [R]; visible int32 [R*DQL] or None.
+    rows: None for every row, else a sequence of row indices r*DQL+j.
+    Returns fp32 [len(rows) or R*DQL, out_cols]."""
+    lib = load()
+    q = np.asarray(q_bits)
+    assert q.dtype == np.uint16 and q.ndim == 4 and q.shape[2:] == (HEADS, DIM)
+    assert q.strides[3] == 2
+    kp = np.ascontiguousarray(k_pool_bits, dtype=np.uint16)
+    assert kp.ndim == 4 and kp.shape[2:] == (1, DIM)
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    assert pt.ndim == 2
+    cl = np.ascontiguousarray(comp_lens_arr, dtype=np.int32)
+    vis = None if visible is None else np.ascontiguousarray(visible, dtype=np.int32)
+    num_reqs, dql = q.shape[0], q.shape[1]
+    sr, sj, sh = (s // 2 for s in q.strides[:3])
+    scale = default_scale() if scale is None else float(scale)
+    total = num_reqs * dql
+    sel = _row_list(rows, total)
+    out = np.empty((total if sel is None else len(sel), out_cols), np.float32)
+
+    def call(row_begin, row_end, dst_row):
+        lib.oracle_decode(_ptr(q), sr, sj, sh, _ptr(kp), kp.shape[0], kp.shape[1],
+                          _ptr(pt), pt.shape[1], pt.shape[1], _ptr(cl), _ptr(vis),
+                          num_reqs, dql, scale, out.ctypes.data + dst_row * out_cols * 4,
+                          out_cols, out_cols, row_begin, row_end)
+
+    if sel is None:
+        _run_rows(lambda b, e: call(b, e, b), total, threads)
+    else:
+        _run_rows(lambda b, e: [call(int(sel[i]), int(sel[i]) + 1, i) for i in range(b, e)],
+                  len(sel), threads)
+    return out
+
+
+def prefill(q_bits, k_bits, row_k_start, row_k_end, out_cols: int, scale: float | None = None,
+            rows=None, threads: int | None = None):
+    """Prefill scores.
+
+    q_bits: uint16 [T, 4, 128] (unit feature stride); k_bits: uint16 [NK, 128]
+    (unit feature stride); row_k_start/row_k_end int32 [T].
+    rows: None for all rows, else a sequence of row indices.
+    Returns fp32 [len(rows) or T, out_cols]."""
+    lib = load()
+    q = np.asarray(q_bits)
+    assert q.dtype == np.uint16 and q.ndim == 3 and q.shape[1:] == (HEADS, DIM)
+    assert q.strides[2] == 2
+    k = np.asarray(k_bits)
+    assert k.dtype == np.uint16 and k.ndim == 2 and k.shape[1] == DIM and k.strides[1] == 2
+    ks = np.ascontiguousarray(row_k_start, dtype=np.int32)
+    ke = np.ascontiguousarray(row_k_end, dtype=np.int32)
+    num_rows = q.shape[0]
+    scale = default_scale() if scale is None else float(scale)
+    sq, sh = q.strides[0] // 2, q.strides[1] // 2
+    sk = k.strides[0] // 2
+    sel = _row_list(rows, num_rows)
+    out = np.empty((num_rows if sel is None else len(sel), out_cols), np.float32)
+
+    def call(row_begin, row_end, dst_row):
+        lib.oracle_prefill(_ptr(q), sq, sh, _ptr(k), sk, k.shape[0], _ptr(ks), _ptr(ke),
+                           num_rows, scale, out.ctypes.data + dst_row * out_cols * 4,
+                           out_cols, out_cols, row_begin, row_end)
+
+    if sel is None:
+        _run_rows(lambda b, e: call(b, e, b), num_rows, threads)
+    else:
+        _run_rows(lambda b, e: [call(int(sel[i]), int(sel[i]) + 1, i) for i in range(b, e)],
+                  len(sel), threads)
+    return out
+
+
+def topk(logits, k: int, threads: int | None = None):
+    """Per-row top-k columns of fp32 logits [T, C]: int32 [T, k], ascending,
+    -1 padded."""
+    lib = load()
+    x = np.ascontiguousarray(logits, dtype=np.float32)
+    assert x.ndim == 2 and k >= 1
+    out = np.empty((x.shape[0], k), np.int32)
+
+    def fn(b, e):
+        rc = lib.oracle_topk(x.ctypes.data, x.shape[1], x.shape[1], k,
+                             out.ctypes.data + b * k * 4, k, b, e)
+        if rc != 0:
+            raise MemoryError("oracle_topk: allocation failed")
+    _run_rows(fn, x.shape[0], threads)
+    return out

@@ -1,0 +1,262 @@
+/*
+ * Plain CPU oracle for the QSA lightweight MQA indexer (block scoring).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or constant with the
+ * HIP library; it is written from the definitions on the pages, slowly and
+ * plainly, so that a reader can check every line against them.
+ *
+ * Arithmetic: bf16 inputs are widened exactly to double, every dot product
+ * and the head sum are accumulated in double, and the scaled result is
+ * rounded once to fp32.
+ *
+ * Sources (page title, section):
+ *   [MATE-QSA]  "QSA (Qwen Sparse Attention)" (MATE API docs), intro and
+ *               section "MQA score": score = sum over the 4 query heads of
+ *               ReLU(q_h . k), times 1/sqrt(128); incomplete/future blocks
+ *               masked; paged keys [pages, page_size, 1, dim] with a page
+ *               table whose unused entries may be -1 and whose missing or
+ *               out-of-range pages score -inf; packed prefill queries with
+ *               per-row key intervals; "scale" is a multiplier.
+ *               Section "Core Attention": selected block indices are
+ *               request-local int32, padded with -1, at most 512 per row.
+ *   [QSA-CACHE] "vLLM/vllm/models/qwen4_exp/common/qsa_cache.py",
+ *               functions _logical_positions, _build_qsa_metadata_kernel,
+ *               _build_qsa_metadata_torch and QSAMetadataBuilder.build:
+ *               logical position of a query token, visible_blocks =
+ *               max(0, min((pos+1)//cr, seq_len//cr)), decode/prefill split
+ *               with a uniform decode query length.
+ *   [PR-54513]  "[Qwen3.8-Flash-Next] Separate prefill and decode paths for
+ *               QSA indexer" (vLLM PR 54513), section "Main changes":
+ *               visible_blocks = (logical_position + 1) // compress_ratio
+ *               moves into the per-step metadata.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - scale multiplies the head sum (equal to scaling before ReLU for
+ *     scale > 0);  ReLU(x) = x > 0 ? x : +0.0, so unmasked cells are >= +0.
+ *   - decode row (r, j) sees min(max(visible[r*dql+j], 0), comp_len[r])
+ *     blocks; with no visible array it sees comp_len[r].
+ *   - prefill column c of row t holds key row_k_start[t] + c; it is valid
+ *     iff that key lies in [0, num_keys) and below row_k_end[t].
+ *   - top-k keeps the k largest cells that are > -inf (NaN excluded),
+ *     breaks ties toward the lower column, compares with IEEE ordering
+ *     (-0 == +0), emits the picks in ascending column order and pads -1.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define QSA_ORACLE_HEADS 4
+#define QSA_ORACLE_DIM 128
+
+/* bf16 bit pattern -> double.  A bf16 value is the upper half of an IEEE
+ * binary32 value, so the widening is exact. */
+static double bf16_bits_to_double(uint16_t bits)
+{
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static float neg_inf(void) { return -INFINITY; }
+
+/* Python-style floor division for the metadata formulas (C '/' truncates). */
+static int64_t floor_div(int64_t a, int64_t b)
+{
+    int64_t q = a / b;
+    if ((a % b != 0) && ((a < 0) != (b < 0))) q -= 1;
+    return q;
+}
+
+/* One score cell [MATE-QSA, "MQA score"]:
+ *   scale * sum_h max(0, sum_d q[h][d] * k[d]),
+ * accumulated in double, rounded once to fp32. */
+static float score_cell(const uint16_t *q_row, int64_t q_stride_head,
+                        const uint16_t *key, float scale)
+{
+    double head_sum = 0.0;
+    for (int h = 0; h < QSA_ORACLE_HEADS; ++h) {
+        double dot = 0.0;
+        for (int d = 0; d < QSA_ORACLE_DIM; ++d)
+            dot += bf16_bits_to_double(q_row[h * q_stride_head + d]) *
+                   bf16_bits_to_double(key[d]);
+        head_sum += (dot > 0.0) ? dot : 0.0;
+    }
+    return (float)(head_sum * (double)scale);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Per-step metadata [QSA-CACHE _logical_positions / metadata kernels].     */
+
+/* For every query token t in [0, num_tokens):
+ *   request r = the one whose [qsl[r], qsl[r+1]) holds t (linear scan),
+ *   pos = seq_len[r] - query_len[r] + (t - qsl[r]),
+ *   visible = max(0, min(floor((pos+1)/cr), floor(seq_len[r]/cr))).
+ * Tokens past qsl[num_reqs] are padding: request 0, position -1,
+ * visible 0 (the padding rule of the metadata kernel). */
+void oracle_token_metadata(const int32_t *query_start_loc, const int32_t *seq_lens,
+                           int32_t num_reqs, int32_t num_tokens, int32_t compress_ratio,
+                           int32_t *token_to_req, int64_t *positions, int32_t *visible)
+{
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        int32_t req = -1;
+        for (int32_t r = 0; r < num_reqs; ++r)
+            if (query_start_loc[r] <= t && t < query_start_loc[r + 1]) { req = r; break; }
+        if (req < 0) {
+            if (token_to_req) token_to_req[t] = 0;
+            if (positions) positions[t] = -1;
+            if (visible) visible[t] = 0;
+            continue;
+        }
+        int64_t query_len = (int64_t)query_start_loc[req + 1] - query_start_loc[req];
+        int64_t pos = (int64_t)seq_lens[req] - query_len + (t - query_start_loc[req]);
+        int64_t by_pos = floor_div(pos + 1, compress_ratio);
+        int64_t by_len = floor_div(seq_lens[req], compress_ratio);
+        int64_t v = by_pos < by_len ? by_pos : by_len;
+        if (v < 0) v = 0;
+        if (token_to_req) token_to_req[t] = req;
+        if (positions) positions[t] = pos;
+        if (visible) visible[t] = (int32_t)v;
+    }
+}
+
+/* Number of complete compressed blocks per request: floor(seq_len / cr). */
+void oracle_comp_lens(const int32_t *seq_lens, int32_t num_reqs, int32_t compress_ratio,
+                      int32_t *comp_lens)
+{
+    for (int32_t r = 0; r < num_reqs; ++r)
+        comp_lens[r] = (int32_t)floor_div(seq_lens[r], compress_ratio);
+}
+
+/* Prefill key intervals for packed keys: request r's compressed keys start
+ * at key_offsets[r]; token t may read keys [start, start + visible[t]). */
+void oracle_prefill_intervals(const int32_t *token_to_req, const int32_t *visible,
+                              const int32_t *key_offsets, int32_t num_tokens,
+                              int32_t *row_k_start, int32_t *row_k_end)
+{
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        int32_t start = key_offsets[token_to_req[t]];
+        row_k_start[t] = start;
+        row_k_end[t] = start + visible[t];
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Decode over paged compressed keys [MATE-QSA "MQA score", paged form].     */
+
+/* Rows [row_begin, row_end) of the [num_reqs*dql, out_cols] output; row
+ * `row` is written at out + (row - row_begin) * out_stride.
+ * Row index = r*dql + j.  Element strides (bf16 elements) for q;
+ * k_cache is [num_pages][page_size][1][128] contiguous. */
+void oracle_decode(const uint16_t *q, int64_t q_stride_req, int64_t q_stride_row,
+                   int64_t q_stride_head, const uint16_t *k_cache, int64_t num_pages,
+                   int32_t page_size, const int32_t *page_table, int64_t page_table_stride,
+                   int32_t page_table_cols, const int32_t *comp_lens, const int32_t *visible,
+                   int32_t num_reqs, int32_t dql, float scale, float *out,
+                   int64_t out_stride, int32_t out_cols, int32_t row_begin, int32_t row_end)
+{
+    (void)num_reqs;
+    for (int32_t row = row_begin; row < row_end; ++row) {
+        int32_t r = row / dql;
+        int32_t j = row % dql;
+        int64_t seen = visible ? (int64_t)visible[row] : (int64_t)comp_lens[r];
+        if (seen > comp_lens[r]) seen = comp_lens[r];
+        if (seen < 0) seen = 0;
+        const uint16_t *q_row = q + r * q_stride_req + j * q_stride_row;
+        for (int32_t c = 0; c < out_cols; ++c) {
+            float value = neg_inf();
+            if (c < seen) {
+                int64_t slot = c / page_size;
+                if (slot < page_table_cols) {
+                    int64_t page = page_table[r * page_table_stride + slot];
+                    if (page >= 0 && page < num_pages) {
+                        const uint16_t *key =
+                            k_cache + (page * page_size + (c % page_size)) * QSA_ORACLE_DIM;
+                        value = score_cell(q_row, q_stride_head, key, scale);
+                    }
+                }
+            }
+            out[(int64_t)(row - row_begin) * out_stride + c] = value;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Prefill over packed queries and shared keys [MATE-QSA "MQA score"].      */
+
+/* Rows [row_begin, row_end) of the [num_rows, out_cols] output; row t is
+ * written at out + (t - row_begin) * out_stride.  Column c of row t scores
+ * key n = row_k_start[t] + c when 0 <= n < num_keys and n < row_k_end[t];
+ * every other cell is -inf. */
+void oracle_prefill(const uint16_t *q, int64_t q_stride_row, int64_t q_stride_head,
+                    const uint16_t *k, int64_t k_stride, int64_t num_keys,
+                    const int32_t *row_k_start, const int32_t *row_k_end, int32_t num_rows,
+                    float scale, float *out, int64_t out_stride, int32_t out_cols,
+                    int32_t row_begin, int32_t row_end)
+{
+    (void)num_rows;
+    for (int32_t t = row_begin; t < row_end; ++t) {
+        const uint16_t *q_row = q + (int64_t)t * q_stride_row;
+        for (int32_t c = 0; c < out_cols; ++c) {
+            int64_t n = (int64_t)row_k_start[t] + c;
+            float value = neg_inf();
+            if (n >= 0 && n < num_keys && n < row_k_end[t])
+                value = score_cell(q_row, q_stride_head, k + n * k_stride, scale);
+            out[(int64_t)(t - row_begin) * out_stride + c] = value;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Top-k block selection [MATE-QSA intro: the caller keeps the best blocks;  */
+/* "Core Attention": request-local int32 indices, -1 padding].              */
+
+typedef struct {
+    float value;
+    int32_t col;
+} oracle_cand;
+
+/* Larger value first; equal values (IEEE, so -0 == +0) by lower column. */
+static int by_score_then_col(const void *a, const void *b)
+{
+    const oracle_cand *x = (const oracle_cand *)a, *y = (const oracle_cand *)b;
+    if (x->value > y->value) return -1;
+    if (x->value < y->value) return 1;
+    return (x->col > y->col) - (x->col < y->col);
+}
+
+static int by_col(const void *a, const void *b)
+{
+    const oracle_cand *x = (const oracle_cand *)a, *y = (const oracle_cand *)b;
+    return (x->col > y->col) - (x->col < y->col);
+}
+
+/* Rows [row_begin, row_end) of logits (row t at logits + t*logits_stride):
+ * out_idx + (t - row_begin)*out_stride receives the picked columns in
+ * ascending order, then -1.  Returns 0, or -1 when memory runs out. */
+int oracle_topk(const float *logits, int64_t logits_stride, int32_t num_cols, int32_t k,
+                int32_t *out_idx, int64_t out_stride, int32_t row_begin, int32_t row_end)
+{
+    oracle_cand *cand = (oracle_cand *)malloc(sizeof(oracle_cand) * (size_t)(num_cols > 0 ? num_cols : 1));
+    if (!cand) return -1;
+    for (int32_t t = row_begin; t < row_end; ++t) {
+        const float *row = logits + (int64_t)t * logits_stride;
+        int32_t n = 0;
+        for (int32_t c = 0; c < num_cols; ++c)
+            if (row[c] > neg_inf()) { /* false for -inf and for NaN */
+                cand[n].value = row[c];
+                cand[n].col = c;
+                ++n;
+            }
+        qsort(cand, (size_t)n, sizeof(oracle_cand), by_score_then_col);
+        int32_t keep = n < k ? n : k;
+        qsort(cand, (size_t)keep, sizeof(oracle_cand), by_col);
+        int32_t *dst = out_idx + (int64_t)(t - row_begin) * out_stride;
+        for (int32_t i = 0; i < k; ++i) dst[i] = i < keep ? cand[i].col : -1;
+    }
+    free(cand);
+    return 0;
+}

@@ -1,0 +1,495 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics
+fix, never against the oracle itself.
+
+Each pin is a plain function that raises AssertionError on a mismatch.
+``test_oracle_pins.py`` runs them against the oracle; ``test_oracle_mutants.py``
+runs them against deliberately broken copies of the oracle and expects at
+least one pin to fail for every plausible mistake.
+
+Kinds of pin used here:
+  * hand-worked values (tests/golden/*.txt, each with its citation);
+  * closed forms (all-ones inputs);
+  * brute force on tiny inputs in pure Python and in numpy float64 with an
+    independent gather (a special case that reduces to a library matmul);
+  * invariants the definition implies (page permutation, head permutation,
+    negation symmetry, decode == prefill on gathered keys, DQL independence,
+    scale linearity, mask pattern, non-negativity).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+from oracle import oracle as O
+from workloads import bf16_bits, bits_to_f32, decode_inputs, normal_bf16
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+NEG_INF_BITS = 0xFF800000
+SCALE = float(np.float32(1.0 / math.sqrt(128.0)))
+
+
+def _f32_bits(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _onehot_inputs(page_size=3):
+    """q[h][0] = (1,-1,2,0.5)[h]; key n has feature 0 = n-2, others 0."""
+    a = np.array([1.0, -1.0, 2.0, 0.5], np.float32)
+    q = np.zeros((1, 1, 4, 128), np.float32)
+    q[0, 0, :, 0] = a
+    keys = np.zeros((8, 128), np.float32)
+    keys[:, 0] = np.arange(8) - 2
+    return bf16_bits(q), bf16_bits(keys)
+
+
+def _paged(keys_bits, page_size, order=None, spare=0, seed=0):
+    """Place keys [n,128] into a shuffled page pool; returns (pool, table).
+    Unused rows and spare pages hold random noise."""
+    rng = np.random.default_rng(seed)
+    n = keys_bits.shape[0]
+    pages = -(-n // page_size)
+    total = pages + spare
+    pool = normal_bf16(rng, (total, page_size, 1, 128))
+    phys = rng.permutation(total) if order is None else np.asarray(order)
+    for i in range(n):
+        pool[phys[i // page_size], i % page_size, 0] = keys_bits[i]
+    table = np.full((1, pages + 2), -1, np.int32)
+    table[0, :pages] = phys[:pages]
+    return pool, table
+
+
+# ----------------------------------------------------------------------------
+# hand-worked values and closed forms
+
+
+def pin_onehot_decode():
+    golden = _read_golden("onehot_scores.txt")
+    expect = np.array([int(r[3], 16) for r in golden], np.uint32)
+    q, keys = _onehot_inputs()
+    for ps in (1, 3, 8):
+        pool, table = _paged(keys, ps, seed=ps)
+        out = O.decode(q, pool, table, np.array([8], np.int32), np.array([8], np.int32), 8,
+                       scale=SCALE)
+        assert np.array_equal(_f32_bits(out[0]), expect), (ps, _f32_bits(out[0]), expect)
+
+
+def pin_onehot_prefill():
+    golden = _read_golden("onehot_scores.txt")
+    expect = np.array([int(r[3], 16) for r in golden], np.uint32)
+    q, keys = _onehot_inputs()
+    out = O.prefill(q[:, 0], keys, np.array([0], np.int32), np.array([8], np.int32), 8,
+                    scale=SCALE)
+    assert np.array_equal(_f32_bits(out[0]), expect)
+    # The same keys behind an offset interval: column c is key start + c.
+    padded = np.concatenate([bf16_bits(np.full((5, 128), 7.0, np.float32)), keys])
+    out = O.prefill(q[:, 0], padded, np.array([5], np.int32), np.array([13], np.int32), 10,
+                    scale=SCALE)
+    assert np.array_equal(_f32_bits(out[0, :8]), expect)
+    assert np.all(_f32_bits(out[0, 8:]) == NEG_INF_BITS)
+
+
+def pin_all_ones_closed_form():
+    # Every head dot is 128, so the score is 4*128*scale; with head 2 negated
+    # its dot is -128 and ReLU drops it: 3*128*scale.
+    q = bf16_bits(np.ones((1, 4, 128), np.float32))
+    k = bf16_bits(np.ones((3, 128), np.float32))
+    out = O.prefill(q, k, np.array([0], np.int32), np.array([3], np.int32), 3, scale=SCALE)
+    assert np.all(_f32_bits(out) == 0x423504F3), _f32_bits(out)
+    qn = np.ones((1, 4, 128), np.float32)
+    qn[0, 2] = -1.0
+    out = O.prefill(bf16_bits(qn), k, np.array([0], np.int32), np.array([3], np.int32), 3,
+                    scale=SCALE)
+    assert np.all(out == np.float32(384 * np.float64(SCALE)))
+
+
+def pin_visible_golden():
+    rows = _read_golden("visible_blocks.txt")
+    # Each golden request alone, then all of them packed in one batch (so the
+    # per-request query offset matters).
+    ctxs, dqls, expects = [], [], []
+    for ctx, dql, vis in rows:
+        ctx, dql = int(ctx), int(dql)
+        vis = [int(v) for v in vis.split(",")]
+        qsl = np.array([0, dql], np.int32)
+        _, pos, got = O.token_metadata(qsl, np.array([ctx], np.int32), dql)
+        assert list(got) == vis, (ctx, dql, list(got), vis)
+        assert list(pos) == list(range(ctx - dql, ctx))
+        ctxs.append(ctx), dqls.append(dql), expects.extend(vis)
+    qsl = np.concatenate([[0], np.cumsum(dqls)]).astype(np.int32)
+    req, _, got = O.token_metadata(qsl, np.array(ctxs, np.int32), int(qsl[-1]) + 3)
+    assert list(got[:-3]) == expects
+    assert list(got[-3:]) == [0, 0, 0]  # padding tokens past the last request
+    assert list(req[:-3]) == [r for r, d in enumerate(dqls) for _ in range(d)]
+    assert list(O.comp_lens(np.array(ctxs, np.int32))) == [c // 4 for c in ctxs]
+
+
+def pin_visible_counts_complete_blocks():
+    # Independent characterisation: the number of 4-token blocks whose last
+    # token is at or before pos, among the blocks complete within seq_len.
+    rng = np.random.default_rng(7)
+    for _ in range(30):
+        nreq = int(rng.integers(1, 5))
+        qlens = rng.integers(1, 9, nreq)
+        seq = qlens + rng.integers(0, 40, nreq)
+        qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+        _, pos, vis = O.token_metadata(qsl, seq.astype(np.int32), int(qsl[-1]))
+        t = 0
+        for r in range(nreq):
+            for i in range(qlens[r]):
+                p = seq[r] - qlens[r] + i
+                assert pos[t] == p
+                count = sum(1 for n in range(seq[r]) if 4 * n + 3 <= p and 4 * n + 3 < seq[r])
+                assert vis[t] == count, (seq[r], p, vis[t], count)
+                t += 1
+
+
+# ----------------------------------------------------------------------------
+# brute force
+
+
+def _numpy_decode_reference(inp, visible, out_cols, scale):
+    """Dense float64 evaluation with an independent gather: for each request,
+    walk its page table in Python, stack its keys, and use a numpy matmul for
+    the dots."""
+    q = bits_to_f32(inp.q).astype(np.float64)
+    pool = bits_to_f32(inp.k_pool).astype(np.float64)
+    R, dql = inp.q.shape[:2]
+    ps = inp.page_size
+    out = np.full((R * dql, out_cols), -np.inf, np.float32)
+    comp = [int(s) // 4 for s in inp.seq_lens]
+    for r in range(R):
+        keys, ok = [], []
+        for c in range(out_cols):
+            slot = c // ps
+            page = inp.page_table[r, slot] if slot < inp.page_table.shape[1] else -1
+            good = 0 <= page < pool.shape[0]
+            keys.append(pool[page, c % ps, 0] if good else np.zeros(128))
+            ok.append(good)
+        K = np.stack(keys)
+        for j in range(dql):
+            row = r * dql + j
+            dots = q[r, j] @ K.T                                # [4, cols]
+            s = np.maximum(dots, 0.0).sum(axis=0) * np.float64(scale)
+            seen = min(max(int(visible[row]), 0), comp[r])
+            for c in range(min(seen, out_cols)):
+                if ok[c]:
+                    out[row, c] = np.float32(s[c])
+    return out
+
+
+def _assert_close_exact_mask(got, ref, ulps=1):
+    gb, rb = _f32_bits(got), _f32_bits(ref)
+    ninf_g, ninf_r = gb == NEG_INF_BITS, rb == NEG_INF_BITS
+    assert np.array_equal(ninf_g, ninf_r), "-inf pattern differs"
+    fin = ~ninf_r
+    diff = np.abs(gb[fin].astype(np.int64) - rb[fin].astype(np.int64))
+    assert diff.size == 0 or diff.max() <= ulps, f"max ulp diff {diff.max()}"
+
+
+def pin_bruteforce_numpy_decode():
+    rng = np.random.default_rng(11)
+    for case in range(8):
+        R = int(rng.integers(1, 4))
+        dql = int(rng.integers(1, 5))
+        ps = [1, 3, 16, 5][case % 4]
+        ctx = [int(x) for x in rng.integers(1, 800, R)]
+        cols = max(c // 4 for c in ctx) + int(rng.integers(0, 5))
+        table_cols = max(-(-(-(-c // 4)) // ps) for c in ctx) + 1
+        inp = decode_inputs(ctx, dql, ps, table_cols, spare_pages=2, out_cols=cols,
+                            seed=100 + case)
+        # Knock out one page-table entry and plant an out-of-range id.
+        if inp.page_table[0, 0] >= 0 and table_cols > 2:
+            inp.page_table[0, 1] = -1
+            inp.page_table[R - 1, 0] = inp.k_pool.shape[0] + 3
+        _, _, vis = O.token_metadata(inp.query_start_loc, inp.seq_lens, R * dql)
+        got = O.decode(inp.q, inp.k_pool, inp.page_table, O.comp_lens(inp.seq_lens), vis, cols,
+                       scale=SCALE)
+        ref = _numpy_decode_reference(inp, vis, cols, SCALE)
+        _assert_close_exact_mask(got, ref)
+
+
+def pin_bruteforce_python_loops():
+    # Pure-Python loops on a tiny prefill case, same summation order as the
+    # definition (features, then heads): bit-exact.
+    rng = np.random.default_rng(12)
+    q = normal_bf16(rng, (3, 4, 128))
+    k = normal_bf16(rng, (7, 128))
+    ks = np.array([0, 2, 5], np.int32)
+    ke = np.array([4, 9, 3], np.int32)
+    cols = 6
+    got = O.prefill(q, k, ks, ke, cols, scale=SCALE)
+    qf, kf = bits_to_f32(q), bits_to_f32(k)
+    for t in range(3):
+        for c in range(cols):
+            n = int(ks[t]) + c
+            if n < int(ke[t]) and 0 <= n < 7:
+                total = 0.0
+                for h in range(4):
+                    dot = 0.0
+                    for d in range(128):
+                        dot += float(qf[t, h, d]) * float(kf[n, d])
+                    total += dot if dot > 0.0 else 0.0
+                want = np.float32(total * SCALE)
+                assert _f32_bits(got[t, c]) == _f32_bits(want), (t, c, got[t, c], want)
+            else:
+                assert _f32_bits(got[t, c]) == NEG_INF_BITS, (t, c)
+
+
+def pin_bruteforce_numpy_prefill():
+    rng = np.random.default_rng(13)
+    T, NK, cols = 9, 40, 30
+    q = normal_bf16(rng, (T, 4, 128))
+    k = normal_bf16(rng, (NK, 128))
+    ks = rng.integers(-3, 25, T).astype(np.int32)
+    ke = (ks + rng.integers(-2, 35, T)).astype(np.int32)
+    got = O.prefill(q, k, ks, ke, cols, scale=SCALE)
+    qf = bits_to_f32(q).astype(np.float64)
+    kf = bits_to_f32(k).astype(np.float64)
+    ref = np.full((T, cols), -np.inf, np.float32)
+    for t in range(T):
+        s = np.maximum(qf[t] @ kf.T, 0).sum(axis=0) * SCALE      # [NK]
+        for c in range(cols):
+            n = ks[t] + c
+            if 0 <= n < NK and n < ke[t]:
+                ref[t, c] = np.float32(s[n])
+    _assert_close_exact_mask(got, ref)
+
+
+# ----------------------------------------------------------------------------
+# invariants
+
+
+def _small_decode(seed=21, dql=3, ps=7, ctx=(301, 77, 5)):
+    ctx = list(ctx)
+    inp = decode_inputs(ctx, dql, ps, table_cols=12, spare_pages=4,
+                        out_cols=max(ctx) // 4 + 3, seed=seed)
+    _, _, vis = O.token_metadata(inp.query_start_loc, inp.seq_lens, len(ctx) * dql)
+    return inp, vis
+
+
+def _run_decode(inp, vis, scale=SCALE, q=None):
+    return O.decode(inp.q if q is None else q, inp.k_pool, inp.page_table,
+                    O.comp_lens(inp.seq_lens), vis, inp.out_cols, scale=scale)
+
+
+def pin_mask_pattern_and_sign():
+    inp, vis = _small_decode()
+    out = _run_decode(inp, vis)
+    bits = _f32_bits(out)
+    comp = [int(s) // 4 for s in inp.seq_lens]
+    for row in range(out.shape[0]):
+        r = row // inp.dql
+        seen = min(int(vis[row]), comp[r])
+        assert np.all(bits[row, seen:] == NEG_INF_BITS)
+        assert np.all(np.isfinite(out[row, :seen]))
+        assert np.all(bits[row, :seen] < 0x80000000)   # >= +0.0, never -0.0
+    # Some cells must be exactly +0 (all four heads negative) and most positive.
+    fin = out[np.isfinite(out)]
+    assert (fin > 0).mean() > 0.5
+
+
+def pin_page_permutation_invariance():
+    inp, vis = _small_decode()
+    base = _run_decode(inp, vis)
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(inp.k_pool.shape[0])          # new_pool[perm[p]] = pool[p]
+    pool2 = np.empty_like(inp.k_pool)
+    pool2[perm] = inp.k_pool
+    table2 = np.where(inp.page_table >= 0, perm[np.maximum(inp.page_table, 0)], -1)
+    inp2 = type(inp)(inp.q, pool2, table2.astype(np.int32), inp.seq_lens,
+                     inp.query_start_loc, inp.page_size, inp.out_cols)
+    assert np.array_equal(_f32_bits(_run_decode(inp2, vis)), _f32_bits(base))
+
+
+def pin_head_permutation():
+    inp, vis = _small_decode()
+    base = _run_decode(inp, vis)
+    perm = _run_decode(inp, vis, q=np.ascontiguousarray(inp.q[:, :, [2, 0, 3, 1]]))
+    _assert_close_exact_mask(perm, base, ulps=1)
+
+
+def pin_negation_symmetry():
+    inp, vis = _small_decode()
+    base = _run_decode(inp, vis)
+    neg = type(inp)(inp.q ^ np.uint16(0x8000), inp.k_pool ^ np.uint16(0x8000), inp.page_table,
+                    inp.seq_lens, inp.query_start_loc, inp.page_size, inp.out_cols)
+    assert np.array_equal(_f32_bits(_run_decode(neg, vis)), _f32_bits(base))
+
+
+def pin_strided_q():
+    inp, vis = _small_decode()
+    base = _run_decode(inp, vis)
+    R, dql = inp.q.shape[:2]
+    wide = np.zeros((R, dql + 1, 5, 136), np.uint16)
+    wide[:, :dql, :4, :128] = inp.q
+    view = wide[:, :dql, :4, :128]
+    assert not view.flags.c_contiguous
+    assert np.array_equal(_f32_bits(_run_decode(inp, vis, q=view)), _f32_bits(base))
+
+
+def pin_dql_independence():
+    inp, vis = _small_decode(dql=4, ctx=(123, 64))
+    base = _run_decode(inp, vis)
+    comp = O.comp_lens(inp.seq_lens)
+    for r in range(2):
+        for j in range(4):
+            row = r * 4 + j
+            one = O.decode(np.ascontiguousarray(inp.q[r:r + 1, j:j + 1]), inp.k_pool,
+                           inp.page_table[r:r + 1], comp[r:r + 1], vis[row:row + 1],
+                           inp.out_cols, scale=SCALE)
+            assert np.array_equal(_f32_bits(one[0]), _f32_bits(base[row]))
+
+
+def pin_decode_equals_prefill():
+    inp, vis = _small_decode()
+    base = _run_decode(inp, vis)
+    ps = inp.page_size
+    for r in range(inp.num_reqs):
+        n = int(inp.seq_lens[r]) // 4
+        keys = np.stack([inp.k_pool[inp.page_table[r, c // ps], c % ps, 0] for c in range(n)]) \
+            if n else np.zeros((0, 128), np.uint16)
+        keys = np.concatenate([keys, np.zeros((1, 128), np.uint16)])  # never read
+        for j in range(inp.dql):
+            row = r * inp.dql + j
+            got = O.prefill(np.ascontiguousarray(inp.q[r, j:j + 1]), keys,
+                            np.array([0], np.int32), np.array([vis[row]], np.int32),
+                            inp.out_cols, scale=SCALE)
+            assert np.array_equal(_f32_bits(got[0]), _f32_bits(base[row])), (r, j)
+
+
+def pin_scale_linearity():
+    inp, vis = _small_decode()
+    base = _run_decode(inp, vis)
+    dbl = _run_decode(inp, vis, scale=2 * SCALE)
+    fin = np.isfinite(base)
+    assert np.array_equal(dbl[fin], 2 * base[fin])
+    assert np.array_equal(np.isfinite(dbl), fin)
+
+
+def pin_invalid_pages_mask():
+    inp, vis = _small_decode(ctx=(301, 300, 299))
+    base = _run_decode(inp, vis)
+    table = inp.page_table.copy()
+    table[0, 2] = -1
+    table[1, 0] = inp.k_pool.shape[0]          # one past the pool
+    table[2, 5] = 1 << 30
+    inp2 = type(inp)(inp.q, inp.k_pool, table, inp.seq_lens, inp.query_start_loc,
+                     inp.page_size, inp.out_cols)
+    got = _run_decode(inp2, vis)
+    ps, dql = inp.page_size, inp.dql
+    expect = base.copy()
+    expect[0 * dql:1 * dql, 2 * ps:3 * ps] = -np.inf
+    expect[1 * dql:2 * dql, 0:ps] = -np.inf
+    expect[2 * dql:3 * dql, 5 * ps:6 * ps] = -np.inf
+    assert np.array_equal(_f32_bits(got), _f32_bits(expect))
+    # A page table narrower than the visible range masks the columns past it.
+    narrow = np.ascontiguousarray(inp.page_table[:, :3])
+    inp3 = type(inp)(inp.q, inp.k_pool, narrow, inp.seq_lens, inp.query_start_loc,
+                     inp.page_size, inp.out_cols)
+    got = _run_decode(inp3, vis)
+    expect = base.copy()
+    expect[:, 3 * ps:] = -np.inf
+    assert np.array_equal(_f32_bits(got), _f32_bits(expect))
+
+
+def pin_decode_visible_override():
+    # No visible array: each row sees comp_len; a visible value above comp_len
+    # is clamped; a negative one masks the whole row.
+    inp, vis = _small_decode(dql=2, ctx=(90, 41))
+    comp = O.comp_lens(inp.seq_lens)
+    full = O.decode(inp.q, inp.k_pool, inp.page_table, comp, None, inp.out_cols, scale=SCALE)
+    want = _run_decode(inp, np.repeat(comp, 2))
+    assert np.array_equal(_f32_bits(full), _f32_bits(want))
+    odd = np.array([10_000, -5, 3, 0], np.int32)
+    got = _run_decode(inp, odd)
+    assert np.array_equal(_f32_bits(got[0]), _f32_bits(full[0]))
+    assert np.all(_f32_bits(got[1]) == NEG_INF_BITS)
+    assert np.array_equal(_f32_bits(got[2, :3]), _f32_bits(full[2, :3]))
+    assert np.all(_f32_bits(got[2, 3:]) == NEG_INF_BITS)
+    assert np.all(_f32_bits(got[3]) == NEG_INF_BITS)
+
+
+def pin_prefill_degenerate_intervals():
+    rng = np.random.default_rng(31)
+    q = normal_bf16(rng, (4, 4, 128))
+    k = normal_bf16(rng, (10, 128))
+    ks = np.array([3, 5, -2, 8], np.int32)
+    ke = np.array([3, 2, 4, 50], np.int32)
+    got = O.prefill(q, k, ks, ke, 6, scale=SCALE)
+    bits = _f32_bits(got)
+    assert np.all(bits[0] == NEG_INF_BITS)             # empty interval
+    assert np.all(bits[1] == NEG_INF_BITS)             # end before start
+    assert np.all(bits[2, :2] == NEG_INF_BITS)         # keys -2, -1 do not exist
+    assert np.all(np.isfinite(got[2, 2:6]))            # keys 0..3
+    assert np.all(np.isfinite(got[3, :2]))             # keys 8, 9
+    assert np.all(bits[3, 2:] == NEG_INF_BITS)         # past the last key
+
+
+# ----------------------------------------------------------------------------
+# top-k
+
+
+def _topk_by_sort(x, k):
+    out = np.full((x.shape[0], k), -1, np.int32)
+    for t in range(x.shape[0]):
+        cols = np.nonzero(x[t] > -np.inf)[0]
+        vals = x[t, cols].astype(np.float64) + 0.0      # -0.0 and +0.0 compare equal
+        order = np.lexsort((cols, -vals))                # score desc, column asc
+        pick = np.sort(cols[order[:k]])
+        out[t, :len(pick)] = pick
+    return out
+
+
+def pin_topk_against_sort():
+    rng = np.random.default_rng(41)
+    for cols, k in ((50, 7), (300, 64), (1000, 512), (20, 30), (1, 1)):
+        x = rng.standard_normal((6, cols)).astype(np.float32)
+        x[1, cols // 2:] = -np.inf                     # short row
+        x[2] = -np.inf                                 # nothing to pick
+        x[3] = np.round(x[3] * 2) / 2                  # many exact ties
+        x[4, ::3] = 0.0
+        x[4, 1::3] = -0.0                              # -0 ties +0
+        x[5] = np.abs(x[5])
+        got = O.topk(x, k)
+        assert np.array_equal(got, _topk_by_sort(x, k)), (cols, k)
+
+
+def pin_topk_ties_lowest_index():
+    x = np.full((1, 40), 1.5, np.float32)
+    x[0, 7] = 2.0
+    got = O.topk(x, 5)
+    assert list(got[0]) == [0, 1, 2, 3, 7]
+    x = np.array([[3.0, -np.inf, 3.0, 1.0, 3.0]], np.float32)
+    assert list(O.topk(x, 6)[0]) == [0, 2, 3, 4, -1, -1]
+    assert list(O.topk(x, 2)[0]) == [0, 2]
+
+
+def pin_split_batch():
+    # Decodes first, uniform length: two DQL-4 decodes then prefills.
+    assert O.split_batch([0, 4, 8, 9, 9, 17], 4) == (None, 2, 8, 3, 9, 4)
+    # Plain decode batch (threshold 1, one token each).
+    assert O.split_batch([0, 1, 2, 3], 1) == (None, 3, 3, 0, 0, 1)
+    # All prefills.
+    assert O.split_batch([0, 10, 30], 4) == (None, 0, 0, 2, 30, 0)
+    # Non-uniform decode lengths: the run ends at the first other length.
+    assert O.split_batch([0, 2, 4, 7, 9], 4) == (None, 2, 4, 2, 5, 2)
+    # Reordering moves qualifying requests first, stably.
+    order, nd, ndt, npf, npt, dql = O.split_batch([0, 9, 11, 12, 14, 14], 2, reorder=True)
+    assert order == [1, 3, 0, 2, 4] and (nd, ndt, npf, npt, dql) == (2, 4, 3, 10, 2)
+    # Empty batch.
+    assert O.split_batch([0], 4) == (None, 0, 0, 0, 0, 0)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

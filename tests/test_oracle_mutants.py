@@ -1,0 +1,94 @@
+"""Pins are strong enough: each plausible mistake planted in a copy of the
+oracle's C source (on the CPU, in a temporary directory) must make at least
+one pin fail.  The oracle itself is never modified."""
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+from oracle import oracle as O
+
+MUTANTS = {
+    "relu_dropped": ("head_sum += (dot > 0.0) ? dot : 0.0;", "head_sum += dot;"),
+    "relu_after_head_sum": ("head_sum += (dot > 0.0) ? dot : 0.0;",
+                            "head_sum += dot; if (h == 3 && head_sum < 0) head_sum = 0;"),
+    "scale_as_divisor": ("return (float)(head_sum * (double)scale);",
+                         "return (float)(head_sum / (double)scale);"),
+    "head_dropped": ("for (int h = 0; h < QSA_ORACLE_HEADS; ++h) {",
+                     "for (int h = 0; h < QSA_ORACLE_HEADS - 1; ++h) {"),
+    "head_stride_ignored": ("q_row[h * q_stride_head + d]", "q_row[h * QSA_ORACLE_DIM + d]"),
+    "feature_index_shifted": ("bf16_bits_to_double(key[d]);",
+                              "bf16_bits_to_double(key[(d + 1) % QSA_ORACLE_DIM]);"),
+    "bf16_widening_wrong": ("uint32_t u = ((uint32_t)bits) << 16;",
+                            "uint32_t u = ((uint32_t)bits) << 15;"),
+    "visible_off_by_one": ("int64_t by_pos = floor_div(pos + 1, compress_ratio);",
+                           "int64_t by_pos = floor_div(pos, compress_ratio);"),
+    "position_ignores_request_start": ("+ (t - query_start_loc[req]);", "+ t;"),
+    "decode_mask_inclusive": ("if (c < seen) {", "if (c <= seen && c < comp_lens[r]) {"),
+    "decode_no_comp_clamp": ("if (seen > comp_lens[r]) seen = comp_lens[r];", ""),
+    "page_slot_swapped": ("int64_t slot = c / page_size;", "int64_t slot = c % page_size;"),
+    "page_row_wrong": ("(page * page_size + (c % page_size))", "(page * page_size + (c / page_size))"),
+    "page_range_unchecked": ("if (page >= 0 && page < num_pages) {", "if (page >= 0) {"),
+    "page_table_width_unchecked": ("if (slot < page_table_cols) {", "if (slot < page_table_cols + 1) {"),
+    "decode_row_request_wrong": ("int32_t r = row / dql;", "int32_t r = row % dql;"),
+    "prefill_absolute_columns": ("int64_t n = (int64_t)row_k_start[t] + c;", "int64_t n = c;"),
+    "prefill_end_inclusive": ("n < row_k_end[t])", "n <= row_k_end[t])"),
+    "prefill_no_lower_bound": ("if (n >= 0 && n < num_keys", "if (n >= -2 && n < num_keys"),
+    "topk_ties_high_index": ("return (x->col > y->col) - (x->col < y->col);\n}\n\nstatic int by_col",
+                             "return (x->col < y->col) - (x->col > y->col);\n}\n\nstatic int by_col"),
+    "topk_keeps_neg_inf": ("if (row[c] > neg_inf()) {", "if (row[c] >= neg_inf()) {"),
+    "topk_descending_output": ("qsort(cand, (size_t)keep, sizeof(oracle_cand), by_col);", ""),
+    "topk_smallest": ("if (x->value > y->value) return -1;\n    if (x->value < y->value) return 1;",
+                      "if (x->value < y->value) return -1;\n    if (x->value > y->value) return 1;"),
+}
+
+
+RUNNER = """
+import sys
+sys.path.insert(0, {root!r})
+from oracle import oracle as O
+O._lib = O.load({lib!r})
+from tests import oracle_pins as P
+failed = []
+for pin in P.ALL_PINS:
+    try:
+        pin()
+    except AssertionError:
+        failed.append(pin.__name__)
+print("FAILED_PINS", ",".join(failed))
+"""
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="qsa_mutants_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, workdir):
+    """Each mutant runs in its own process: a mutant that reads out of bounds
+    may die on a signal, which also counts as caught; any other error fails
+    the test."""
+    old, new = MUTANTS[name]
+    src = open(O.SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique or missing: {old!r}"
+    path = os.path.join(workdir, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib_path = O.build(path, os.path.join(workdir, f"lib_{name}.so"))
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = RUNNER.format(root=root, lib=lib_path)
+    env = dict(os.environ, QSA_ORACLE_THREADS="1")
+    proc = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                          timeout=300, env=env)
+    if proc.returncode < 0:
+        return  # killed by a signal (an out-of-bounds read): caught
+    assert proc.returncode == 0, proc.stderr[-2000:]
+    line = [x for x in proc.stdout.splitlines() if x.startswith("FAILED_PINS")][-1]
+    failed = [x for x in line.split(" ", 1)[1].split(",") if x]
+    assert failed, f"no pin caught mutant {name}"

@@ -1,0 +1,207 @@
+"""Seeded synthetic inputs for the QSA indexer workloads.
+
+Both the HIP path and the oracle consume these inputs, so this module holds
+none of the scoring arithmetic: no dot products, no masks, no visibility
+formula, no top-k.  It draws random numbers, rounds them to bf16 bit patterns,
+picks context lengths, allocates pages and shuffles page tables.
+
+Shapes follow the pages' workloads: the decode microbenchmarks of vLLM PR 54513
+("[Qwen3.8-Flash-Next] Separate prefill and decode paths for QSA indexer",
+section "Microbenchmarks": single request at 100K context, 16 requests with
+log-normal contexts of min/mean/max 3,508 / 51,200 / 102,400 tokens at DQL 4)
+and its prefill table (1x8K and 4x4K query layouts over 8K and 100K
+prefixes); the compressed-key page layout [pages, page_size, 1, 128] from the
+MATE "QSA (Qwen Sparse Attention)" page, section "MQA score".
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+HEADS = 4
+DIM = 128
+TOKENS_PER_ROW = 4  # each compressed-cache row stores one 4-token group
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even.  Inputs
+    here are finite normals, so NaN handling is not needed."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 values (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """i.i.d. N(0,1) drawn in float32, stored as bf16 bit patterns."""
+    return bf16_bits(rng.standard_normal(size=shape, dtype=np.float32))
+
+
+def lognormal_contexts(n: int, lo: int, mean: int, hi: int, seed: int = 1) -> list[int]:
+    """Skewed context lengths with exact min, mean and max.
+
+    Sorted exp(N(0,1)) draws; the extremes are set to lo and hi; the inner
+    draws are scaled (bisection on the factor, clipped to [lo, hi]) so that the
+    total is n*mean; values are rounded and the rounding residue goes to the
+    element at index n//2."""
+    rng = np.random.default_rng(seed)
+    x = np.sort(np.exp(rng.standard_normal(n)))
+    inner = x[1:-1]
+    target = n * mean - lo - hi
+    a, b = 0.0, 1e9
+    for _ in range(200):
+        s = 0.5 * (a + b)
+        if np.clip(s * inner, lo, hi).sum() < target:
+            a = s
+        else:
+            b = s
+    v = np.round(np.clip(s * inner, lo, hi)).astype(np.int64)
+    ctx = np.concatenate([[lo], v, [hi]])
+    ctx[n // 2] += target - v.sum()
+    return [int(c) for c in ctx]
+
+
+# ----------------------------------------------------------------------------
+# Decode inputs: paged compressed keys
+
+
+@dataclass
+class DecodeInputs:
+    q: np.ndarray            # uint16 [R, DQL, 4, 128]
+    k_pool: np.ndarray       # uint16 [P, page_size, 1, 128]
+    page_table: np.ndarray   # int32 [R, W]; -1 = unused
+    seq_lens: np.ndarray     # int32 [R] tokens in context (query tokens included)
+    query_start_loc: np.ndarray  # int32 [R+1]: DQL query tokens per request
+    page_size: int
+    out_cols: int
+
+    @property
+    def num_reqs(self):
+        return self.q.shape[0]
+
+    @property
+    def dql(self):
+        return self.q.shape[1]
+
+
+def pages_for(ctx: int, page_size: int) -> int:
+    """Pages allocated for a context of ctx tokens: enough rows for every
+    4-token group that has started (a page may hold a partial group's row,
+    which the cache never writes; here it holds noise)."""
+    rows = -(-ctx // TOKENS_PER_ROW)
+    return -(-rows // page_size)
+
+
+def decode_inputs(ctx_lens, dql: int, page_size: int, table_cols: int, spare_pages: int,
+                  out_cols: int, seed: int, shuffle: bool = True) -> DecodeInputs:
+    """Paged decode batch.  Every page (used, spare, tails) holds N(0,1) bf16
+    noise, so reading a wrong page or row changes a score.  Page tables give
+    each request distinct physical pages, shuffled over one pool, and -1 after
+    the request's last page."""
+    rng = np.random.default_rng(seed)
+    ctx_lens = [int(c) for c in ctx_lens]
+    num_reqs = len(ctx_lens)
+    need = [pages_for(c, page_size) for c in ctx_lens]
+    assert max(need + [0]) <= table_cols, "page table too narrow for the longest context"
+    num_pages = sum(need) + spare_pages
+    q = normal_bf16(rng, (num_reqs, dql, HEADS, DIM))
+    k_pool = normal_bf16(rng, (num_pages, page_size, 1, DIM))
+    phys = rng.permutation(num_pages) if shuffle else np.arange(num_pages)
+    table = np.full((num_reqs, table_cols), -1, np.int32)
+    at = 0
+    for r, n in enumerate(need):
+        table[r, :n] = phys[at:at + n]
+        at += n
+    seq_lens = np.asarray(ctx_lens, np.int32)
+    qsl = np.arange(num_reqs + 1, dtype=np.int32) * dql
+    return DecodeInputs(q, k_pool, table, seq_lens, qsl, page_size, out_cols)
+
+
+# ----------------------------------------------------------------------------
+# Prefill inputs: packed queries, packed per-request keys
+
+
+@dataclass
+class PrefillInputs:
+    q: np.ndarray            # uint16 [T, 4, 128]
+    k: np.ndarray            # uint16 [NK, 128], request r's keys at key_offsets[r]
+    seq_lens: np.ndarray     # int32 [R]: prefix + query tokens
+    query_start_loc: np.ndarray  # int32 [R+1]
+    key_offsets: np.ndarray  # int32 [R]
+    out_cols: int
+
+
+def prefill_inputs(num_reqs: int, query_len: int, prefix: int, seed: int) -> PrefillInputs:
+    """num_reqs requests, each with query_len new tokens after `prefix` cached
+    tokens.  Each request owns one compressed-key row per complete 4-token
+    group of its whole context, packed one request after another."""
+    rng = np.random.default_rng(seed)
+    seq = prefix + query_len
+    rows = seq // TOKENS_PER_ROW
+    q = normal_bf16(rng, (num_reqs * query_len, HEADS, DIM))
+    k = normal_bf16(rng, (num_reqs * rows, DIM))
+    seq_lens = np.full(num_reqs, seq, np.int32)
+    qsl = np.arange(num_reqs + 1, dtype=np.int32) * query_len
+    key_offsets = np.arange(num_reqs, dtype=np.int32) * rows
+    return PrefillInputs(q, k, seq_lens, qsl, key_offsets, rows)
+
+
+# ----------------------------------------------------------------------------
+# The workloads
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str          # "decode" or "prefill"
+    seed: int
+    description: str
+    params: dict = field(default_factory=dict)
+
+    def make(self):
+        p = self.params
+        if self.kind == "decode":
+            ctx = p["ctx"] if isinstance(p["ctx"], list) else [p["ctx"]] * p["num_reqs"]
+            return decode_inputs(ctx, p["dql"], p["page_size"], p["table_cols"],
+                                 p["spare_pages"], p["out_cols"], self.seed)
+        return prefill_inputs(p["num_reqs"], p["query_len"], p["prefix"], self.seed)
+
+
+C3_CONTEXTS = lognormal_contexts(16, 3508, 51200, 102400, seed=1)
+
+WORKLOADS = {
+    "tiny_decode": Workload(
+        "tiny_decode", "decode", 1,
+        "1 request, DQL 1, context 256 (64 compressed keys), page_size 16, 4 pages",
+        dict(ctx=256, num_reqs=1, dql=1, page_size=16, table_cols=4, spare_pages=0,
+             out_cols=64)),
+    "decode_100k": Workload(
+        "decode_100k", "decode", 2,
+        "1 request, DQL 1, context 100,000 (25,000 compressed keys), page_size 64",
+        dict(ctx=100_000, num_reqs=1, dql=1, page_size=64, table_cols=400, spare_pages=32,
+             out_cols=25_000)),
+    "specdecode_16x51k": Workload(
+        "specdecode_16x51k", "decode", 3,
+        "16 requests, DQL 4, log-normal contexts 3,508/51,200/102,400 (min/mean/max), "
+        "page_size 64",
+        dict(ctx=C3_CONTEXTS, num_reqs=16, dql=4, page_size=64, table_cols=400,
+             spare_pages=0, out_cols=25_600)),
+    "prefill_1x8k_8k": Workload(
+        "prefill_1x8k_8k", "prefill", 4,
+        "1 request, 8,192 query tokens after an 8,192-token prefix (4,096 keys)",
+        dict(num_reqs=1, query_len=8192, prefix=8192)),
+    "prefill_4x4k_100k": Workload(
+        "prefill_4x4k_100k", "prefill", 5,
+        "4 requests x 4,096 query tokens over a 100,000-token prefix (26,024 keys each), "
+        "then top-512 blocks per row",
+        dict(num_reqs=4, query_len=4096, prefix=100_000, topk=512)),
+    "prefill_1x8k_100k": Workload(
+        "prefill_1x8k_100k", "prefill", 6,
+        "1 request, 8,192 query tokens over a 100,000-token prefix (27,048 keys)",
+        dict(num_reqs=1, query_len=8192, prefix=100_000, topk=512)),
+}
