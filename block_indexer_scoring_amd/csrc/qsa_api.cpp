@@ -1,0 +1,249 @@
+// C ABI of the QSA MQA indexer: argument checks (host arguments only, never
+// device contents), error text, and dispatch to the gfx950 kernels.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "qsa.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+int prefill_col_chunk(int64_t num_rows, int32_t out_cols);
+int prefill_rows_per_block();
+}  // namespace qsa
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return QSA_OK;
+}
+
+int device_status(const char *what, hipError_t err) {
+    if (err != hipSuccess)
+        return fail(QSA_ERR_DEVICE, "%s: kernel launch failed: %s", what, hipGetErrorString(err));
+    return ok();
+}
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Vector-load layout rule: 16-byte aligned base, and every axis with more
+// than one element has a positive stride that is a multiple of 8 bf16.
+bool axis_ok(int64_t size, int64_t stride) { return size <= 1 || (stride > 0 && stride % 8 == 0); }
+
+int check_heads(const char *fn, int32_t num_heads, int32_t head_dim) {
+    if (num_heads != 4 || head_dim != 128)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: only (num_heads, head_dim) = (4, 128) is supported, got (%d, %d)",
+                    fn, num_heads, head_dim);
+    return QSA_OK;
+}
+
+int check_scale(const char *fn, float scale) {
+    if (!std::isfinite(scale) || !(scale > 0.0f))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: scale must be finite and > 0, got %g", fn, (double)scale);
+    return QSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+const char *qsa_last_error(void) { return g_last_error.c_str(); }
+
+int qsa_split_batch(const int32_t *query_start_loc, int32_t num_reqs, int32_t decode_threshold,
+                    int32_t *order, int32_t *counts) {
+    const char *fn = "qsa_split_batch";
+    if (!query_start_loc || !counts) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL query_start_loc or counts", fn);
+    if (num_reqs < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: num_reqs < 0", fn);
+    if (decode_threshold < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: decode_threshold < 1", fn);
+    for (int32_t r = 0; r < num_reqs; ++r)
+        if (query_start_loc[r + 1] < query_start_loc[r])
+            return fail(QSA_ERR_INVALID_ARGUMENT, "%s: query_start_loc decreases at request %d", fn, r);
+    // DQL: length of the first request whose length is in [1, threshold].
+    int32_t dql = 0;
+    for (int32_t r = 0; r < num_reqs && dql == 0; ++r) {
+        const int32_t len = query_start_loc[r + 1] - query_start_loc[r];
+        if (len >= 1 && len <= decode_threshold) dql = len;
+    }
+    auto is_decode = [&](int32_t r) {
+        return dql > 0 && query_start_loc[r + 1] - query_start_loc[r] == dql;
+    };
+    int64_t num_decodes = 0, decode_tokens = 0, prefill_tokens = 0;
+    if (order) {
+        int32_t at = 0;
+        for (int32_t r = 0; r < num_reqs; ++r)
+            if (is_decode(r)) order[at++] = r;
+        num_decodes = at;
+        for (int32_t r = 0; r < num_reqs; ++r)
+            if (!is_decode(r)) order[at++] = r;
+    } else {
+        while (num_decodes < num_reqs && is_decode((int32_t)num_decodes)) ++num_decodes;
+    }
+    const int64_t total = num_reqs > 0 ? (int64_t)query_start_loc[num_reqs] - query_start_loc[0] : 0;
+    decode_tokens = num_decodes * dql;
+    prefill_tokens = total - decode_tokens;
+    counts[0] = (int32_t)num_decodes;
+    counts[1] = (int32_t)decode_tokens;
+    counts[2] = num_reqs - (int32_t)num_decodes;
+    counts[3] = (int32_t)prefill_tokens;
+    counts[4] = num_decodes > 0 ? dql : 0;
+    return ok();
+}
+
+int qsa_build_metadata(const int32_t *query_start_loc, const int32_t *seq_lens, int32_t num_reqs,
+                       int32_t num_tokens, int32_t compress_ratio, const int32_t *key_offsets,
+                       int32_t *token_to_req, int64_t *positions, int32_t *visible,
+                       int32_t *comp_lens, int32_t *row_k_start, int32_t *row_k_end, void *stream) {
+    const char *fn = "qsa_build_metadata";
+    if (num_reqs < 0 || num_tokens < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative count", fn);
+    if (compress_ratio < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: compress_ratio < 1", fn);
+    if (!query_start_loc) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL query_start_loc", fn);
+    if (num_reqs > 0 && !seq_lens) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL seq_lens", fn);
+    if (key_offsets && (!row_k_start || !row_k_end))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: key_offsets needs row_k_start and row_k_end", fn);
+    if (!key_offsets && (row_k_start || row_k_end))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: row_k_start/row_k_end need key_offsets", fn);
+    if (num_tokens == 0 && (num_reqs == 0 || !comp_lens)) return ok();
+    qsa::MetaParams p{query_start_loc, seq_lens, key_offsets, num_reqs, num_tokens, compress_ratio,
+                      token_to_req, positions, visible, comp_lens, row_k_start, row_k_end};
+    return device_status(fn, qsa::launch_metadata(p, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_mqa_decode(const void *q, int64_t q_stride_req, int64_t q_stride_row, int64_t q_stride_head,
+                   const void *k_cache, int64_t num_pages, int32_t page_size, const int32_t *page_table,
+                   int64_t page_table_stride, int32_t page_table_cols, const int32_t *comp_lens,
+                   const int32_t *visible, int32_t num_reqs, int32_t dql, int32_t num_heads,
+                   int32_t head_dim, float scale, float *out, int64_t out_stride, int32_t out_cols,
+                   void *stream) {
+    const char *fn = "qsa_mqa_decode";
+    int rc;
+    if ((rc = check_heads(fn, num_heads, head_dim))) return rc;
+    if ((rc = check_scale(fn, scale))) return rc;
+    if (num_reqs < 0 || out_cols < 0 || num_pages < 0 || page_table_cols < 0)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+    if (dql < 1 || dql > 16) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: dql must be in [1, 16], got %d", fn, dql);
+    if (page_size < 1 || page_size > (1 << 20))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: page_size must be in [1, 2^20], got %d", fn, page_size);
+    if (out_stride < out_cols) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: out_stride < out_cols", fn);
+    if (num_reqs > 1 && page_table_stride < page_table_cols)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: page_table_stride < page_table_cols", fn);
+    if (num_pages > ((int64_t)1 << 46) / page_size)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: key cache too large", fn);
+    if (num_reqs == 0 || out_cols == 0) return ok();
+    if (!q || !comp_lens || !out) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL q, comp_lens or out", fn);
+    if (num_pages > 0 && !k_cache) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL k_cache", fn);
+    if (page_table_cols > 0 && !page_table) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL page_table", fn);
+    if (num_pages > 0 && !aligned(k_cache, 16))
+        return fail(QSA_ERR_LAYOUT, "%s: k_cache must be 16-byte aligned (16-byte vector loads)", fn);
+    if (!aligned(out, 4)) return fail(QSA_ERR_LAYOUT, "%s: out must be 4-byte aligned", fn);
+    if (!aligned(q, 2)) return fail(QSA_ERR_LAYOUT, "%s: q must be 2-byte aligned", fn);
+    const int64_t spans = ((int64_t)out_cols + 63) / 64;
+    if ((int64_t)num_reqs * dql > INT32_MAX || (int64_t)num_reqs * spans / 4 >= INT32_MAX)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
+
+    qsa::DecodeParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.q_stride_req = q_stride_req;
+    p.q_stride_row = q_stride_row;
+    p.q_stride_head = q_stride_head;
+    p.k = static_cast<const uint16_t *>(k_cache);
+    p.num_pages = num_pages;
+    p.page_size = page_size;
+    p.page_table = page_table;
+    p.page_table_stride = page_table_stride;
+    p.page_table_cols = page_table_cols;
+    p.comp_lens = comp_lens;
+    p.visible = visible;
+    p.num_reqs = num_reqs;
+    p.dql = dql;
+    p.scale = scale;
+    p.out = out;
+    p.out_stride = out_stride;
+    p.out_cols = out_cols;
+    p.spans = (int32_t)spans;
+    p.q_vec = aligned(q, 16) && q_stride_req % 8 == 0 && q_stride_row % 8 == 0 && q_stride_head % 8 == 0;
+    p.out_vec = aligned(out, 16) && out_stride % 4 == 0;
+    return device_status(fn, qsa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_mqa_prefill(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
+                    int64_t k_stride, int64_t num_keys, const int32_t *row_k_start,
+                    const int32_t *row_k_end, int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                    float scale, float *out, int64_t out_stride, int32_t out_cols, void *stream) {
+    const char *fn = "qsa_mqa_prefill";
+    int rc;
+    if ((rc = check_heads(fn, num_heads, head_dim))) return rc;
+    if ((rc = check_scale(fn, scale))) return rc;
+    if (num_rows < 0 || out_cols < 0 || num_keys < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+    if (out_stride < out_cols) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: out_stride < out_cols", fn);
+    if (num_rows == 0 || out_cols == 0) return ok();
+    if (!q || !out || !row_k_start || !row_k_end)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL q, out, row_k_start or row_k_end", fn);
+    if (num_keys > 0 && !k) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL k", fn);
+    if (!aligned(q, 16) || !axis_ok(num_rows, q_stride_row) || !axis_ok(4, q_stride_head) ||
+        (num_keys > 0 && (!aligned(k, 16) || !axis_ok(num_keys, k_stride))))
+        return fail(QSA_ERR_LAYOUT,
+                    "%s: q and k need a 16-byte aligned base and positive strides that are multiples "
+                    "of 8 elements on every axis longer than 1 (16-byte vector loads)", fn);
+    if (!aligned(out, 4)) return fail(QSA_ERR_LAYOUT, "%s: out must be 4-byte aligned", fn);
+
+    const int bm = qsa::prefill_rows_per_block();
+    const int chunk = qsa::prefill_col_chunk(num_rows, out_cols);
+    const int64_t row_blocks = ((int64_t)num_rows + bm - 1) / bm;
+    const int64_t col_chunks = ((int64_t)out_cols + chunk - 1) / chunk;
+    if (row_blocks * col_chunks >= INT32_MAX)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
+
+    qsa::PrefillParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.q_stride_row = q_stride_row;
+    p.q_stride_head = q_stride_head;
+    p.k = static_cast<const uint16_t *>(k);
+    p.k_stride = k_stride;
+    p.num_keys = num_keys;
+    p.row_k_start = row_k_start;
+    p.row_k_end = row_k_end;
+    p.num_rows = num_rows;
+    p.scale = scale;
+    p.out = out;
+    p.out_stride = out_stride;
+    p.out_cols = out_cols;
+    p.col_chunk = chunk;
+    p.row_blocks = (int32_t)row_blocks;
+    p.col_chunks = (int32_t)col_chunks;
+    p.out_vec = aligned(out, 16) && out_stride % 4 == 0;
+    return device_status(fn, qsa::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_topk_blocks(const float *logits, int64_t logits_stride, int32_t num_rows, int32_t num_cols,
+                    int32_t k, int32_t *out_idx, int64_t out_stride, void *stream) {
+    const char *fn = "qsa_topk_blocks";
+    if (num_rows < 0 || num_cols < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+    if (k < 1 || k > (1 << 20)) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: k must be in [1, 2^20], got %d", fn, k);
+    if (logits_stride < num_cols) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: logits_stride < num_cols", fn);
+    if (out_stride < k) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: out_stride < k", fn);
+    if (num_rows == 0) return ok();
+    if (!out_idx || (num_cols > 0 && !logits))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL logits or out_idx", fn);
+    if (!aligned(logits, 4) || !aligned(out_idx, 4))
+        return fail(QSA_ERR_LAYOUT, "%s: logits and out_idx must be 4-byte aligned", fn);
+    qsa::TopkParams p{logits, logits_stride, num_rows, num_cols, k, out_idx, out_stride};
+    return device_status(fn, qsa::launch_topk(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Internal launch interface between the C ABI layer (qsa_api.cpp) and the
+// HIP kernels.  Everything here has already been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+struct DecodeParams {
+    const uint16_t *q;          // bf16 bits
+    int64_t q_stride_req, q_stride_row, q_stride_head;
+    const uint16_t *k;          // bf16 bits [num_pages][page_size][128]
+    int64_t num_pages;
+    int32_t page_size;
+    const int32_t *page_table;
+    int64_t page_table_stride;
+    int32_t page_table_cols;
+    const int32_t *comp_lens;
+    const int32_t *visible;     // may be null
+    int32_t num_reqs, dql;
+    float scale;
+    float *out;
+    int64_t out_stride;
+    int32_t out_cols;
+    int32_t spans;              // ceil(out_cols / 64)
+    int32_t q_vec;              // Q may be read with 16-byte loads
+    int32_t out_vec;            // out rows may be written with 16-byte stores
+};
+
+struct PrefillParams {
+    const uint16_t *q;
+    int64_t q_stride_row, q_stride_head;
+    const uint16_t *k;
+    int64_t k_stride, num_keys;
+    const int32_t *row_k_start, *row_k_end;
+    int32_t num_rows;
+    float scale;
+    float *out;
+    int64_t out_stride;
+    int32_t out_cols;
+    int32_t col_chunk;          // output columns per workgroup (multiple of 64)
+    int32_t row_blocks, col_chunks;
+    int32_t out_vec;
+};
+
+struct TopkParams {
+    const float *logits;
+    int64_t logits_stride;
+    int32_t num_rows, num_cols, k;
+    int32_t *out;
+    int64_t out_stride;
+};
+
+struct MetaParams {
+    const int32_t *query_start_loc, *seq_lens, *key_offsets;
+    int32_t num_reqs, num_tokens, compress_ratio;
+    int32_t *token_to_req;
+    int64_t *positions;
+    int32_t *visible, *comp_lens, *row_k_start, *row_k_end;
+};
+
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_topk(const TopkParams &p, hipStream_t stream);
+hipError_t launch_metadata(const MetaParams &p, hipStream_t stream);
+
+}  // namespace qsa

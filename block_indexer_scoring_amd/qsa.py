@@ -1,0 +1,243 @@
+"""Python binding of the C ABI in include/qsa.h (libqsa.so).
+
+Argument marshalling only: shapes, dtypes and strides of torch tensors are
+turned into the pointers and sizes of the C entry points, and every step of
+the computation runs in the library's HIP kernels.  Tensors must live on the
+GPU; there is no CPU path.  The functions keep the C names.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqsa.so")
+
+QSA_OK = 0
+QSA_ERR_INVALID_ARGUMENT = 1
+QSA_ERR_UNSUPPORTED = 2
+QSA_ERR_LAYOUT = 3
+QSA_ERR_DEVICE = 4
+ABI_VERSION = 1
+
+SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_split_batch", "qsa_build_metadata",
+           "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks")
+
+DEFAULT_SCALE = 1.0 / math.sqrt(128.0)
+
+
+class QSAError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libqsa.so.  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with block_indexer_scoring_amd/build.py "
+                           "(or __graft_entry__.build()); there is no CPU fallback")
+    lib = ctypes.CDLL(path)
+    P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.qsa_abi_version.argtypes = []
+    lib.qsa_abi_version.restype = ctypes.c_int
+    lib.qsa_last_error.argtypes = []
+    lib.qsa_last_error.restype = ctypes.c_char_p
+    lib.qsa_split_batch.argtypes = [P, i32, i32, P, P]
+    lib.qsa_split_batch.restype = ctypes.c_int
+    lib.qsa_build_metadata.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P]
+    lib.qsa_build_metadata.restype = ctypes.c_int
+    lib.qsa_mqa_decode.argtypes = [P, i64, i64, i64, P, i64, i32, P, i64, i32, P, P, i32, i32,
+                                   i32, i32, f32, P, i64, i32, P]
+    lib.qsa_mqa_decode.restype = ctypes.c_int
+    lib.qsa_mqa_prefill.argtypes = [P, i64, i64, P, i64, i64, P, P, i32, i32, i32, f32, P, i64,
+                                    i32, P]
+    lib.qsa_mqa_prefill.restype = ctypes.c_int
+    lib.qsa_topk_blocks.argtypes = [P, i64, i32, i32, i32, P, i64, P]
+    lib.qsa_topk_blocks.restype = ctypes.c_int
+    if lib.qsa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libqsa ABI {lib.qsa_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != QSA_OK:
+        raise QSAError(rc, _lib.qsa_last_error().decode())
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+def _gpu(name: str, t: torch.Tensor, dtype: torch.dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+# ----------------------------------------------------------------------------
+
+
+def qsa_split_batch(query_start_loc, decode_threshold: int, reorder: bool = False):
+    """Host-side decode/prefill split.  query_start_loc: host int sequence.
+    Returns (order list or None, num_decodes, num_decode_tokens, num_prefills,
+    num_prefill_tokens, dql)."""
+    lib = load_library()
+    qsl = (ctypes.c_int32 * len(query_start_loc))(*[int(x) for x in query_start_loc])
+    num_reqs = len(query_start_loc) - 1
+    order = (ctypes.c_int32 * max(num_reqs, 1))() if reorder else None
+    counts = (ctypes.c_int32 * 5)()
+    _check(lib.qsa_split_batch(ctypes.addressof(qsl), num_reqs, int(decode_threshold),
+                               ctypes.addressof(order) if order is not None else None,
+                               ctypes.addressof(counts)))
+    return ((list(order[:num_reqs]) if reorder else None),) + tuple(int(c) for c in counts)
+
+
+def qsa_build_metadata(query_start_loc: torch.Tensor, seq_lens: torch.Tensor, num_tokens: int,
+                       compress_ratio: int = 4, key_offsets: torch.Tensor | None = None,
+                       stream=None):
+    """Per-token metadata on the GPU.  Returns a dict of device tensors:
+    token_to_req, positions (int64), visible, comp_lens, and with key_offsets
+    row_k_start / row_k_end."""
+    lib = load_library()
+    _gpu("query_start_loc", query_start_loc, torch.int32)
+    _gpu("seq_lens", seq_lens, torch.int32)
+    assert query_start_loc.is_contiguous() and seq_lens.is_contiguous()
+    num_reqs = seq_lens.numel()
+    assert query_start_loc.numel() == num_reqs + 1
+    dev = seq_lens.device
+    res = {
+        "token_to_req": torch.empty(num_tokens, dtype=torch.int32, device=dev),
+        "positions": torch.empty(num_tokens, dtype=torch.int64, device=dev),
+        "visible": torch.empty(num_tokens, dtype=torch.int32, device=dev),
+        "comp_lens": torch.empty(num_reqs, dtype=torch.int32, device=dev),
+    }
+    if key_offsets is not None:
+        _gpu("key_offsets", key_offsets, torch.int32)
+        assert key_offsets.is_contiguous() and key_offsets.numel() == num_reqs
+        res["row_k_start"] = torch.empty(num_tokens, dtype=torch.int32, device=dev)
+        res["row_k_end"] = torch.empty(num_tokens, dtype=torch.int32, device=dev)
+    _check(lib.qsa_build_metadata(
+        _ptr(query_start_loc), _ptr(seq_lens), num_reqs, int(num_tokens), int(compress_ratio),
+        _ptr(key_offsets), _ptr(res["token_to_req"]), _ptr(res["positions"]),
+        _ptr(res["visible"]), _ptr(res["comp_lens"]), _ptr(res.get("row_k_start")),
+        _ptr(res.get("row_k_end")), _stream_handle(stream)))
+    return res
+
+
+def qsa_mqa_decode(q: torch.Tensor, k_cache: torch.Tensor, page_table: torch.Tensor,
+                   comp_lens: torch.Tensor, visible: torch.Tensor | None = None,
+                   out_cols: int | None = None, scale: float = DEFAULT_SCALE,
+                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode scores.  q: bf16 [R, DQL, 4, 128] (unit feature stride, any other
+    strides); k_cache: bf16 [P, page_size, 1, 128] contiguous; page_table:
+    int32 [R, W] (unit column stride); comp_lens: int32 [R]; visible: int32
+    [R*DQL] or None.  Returns fp32 [R*DQL, out_cols] (written into `out` if
+    given; `out` may be a row-strided view)."""
+    lib = load_library()
+    _gpu("q", q, torch.bfloat16)
+    _gpu("k_cache", k_cache, torch.bfloat16)
+    _gpu("page_table", page_table, torch.int32)
+    _gpu("comp_lens", comp_lens, torch.int32)
+    if q.dim() != 4 or k_cache.dim() != 4 or page_table.dim() != 2:
+        raise ValueError("q must be [R, DQL, H, D], k_cache [P, page_size, 1, D], page_table [R, W]")
+    num_reqs, dql, heads, dim = q.shape
+    if q.stride(3) != 1 and dim > 1:
+        raise QSAError(QSA_ERR_LAYOUT, "q needs unit feature stride")
+    if k_cache.shape[2] != 1 or k_cache.shape[3] != dim or not k_cache.is_contiguous():
+        raise ValueError("k_cache must be a contiguous [P, page_size, 1, 128] tensor")
+    if page_table.shape[0] != num_reqs or (page_table.shape[1] > 1 and page_table.stride(1) != 1):
+        raise ValueError("page_table must be [R, W] with unit column stride")
+    if comp_lens.numel() != num_reqs or not comp_lens.is_contiguous():
+        raise ValueError("comp_lens must be a contiguous [R] tensor")
+    if visible is not None:
+        _gpu("visible", visible, torch.int32)
+        if visible.numel() != num_reqs * dql or not visible.is_contiguous():
+            raise ValueError("visible must be a contiguous [R*DQL] tensor")
+    if out is None:
+        if out_cols is None:
+            raise ValueError("give out_cols or out")
+        out = torch.empty((num_reqs * dql, out_cols), dtype=torch.float32, device=q.device)
+    _gpu("out", out, torch.float32)
+    if out.dim() != 2 or out.shape[0] != num_reqs * dql or (out.shape[1] > 1 and out.stride(1) != 1):
+        raise ValueError("out must be [R*DQL, out_cols] with unit column stride")
+    _check(lib.qsa_mqa_decode(
+        _ptr(q), q.stride(0), q.stride(1), q.stride(2), _ptr(k_cache), k_cache.shape[0],
+        k_cache.shape[1], _ptr(page_table), page_table.stride(0), page_table.shape[1],
+        _ptr(comp_lens), _ptr(visible), num_reqs, dql, heads, dim, float(scale), _ptr(out),
+        out.stride(0), out.shape[1], _stream_handle(stream)))
+    return out
+
+
+def qsa_mqa_prefill(q: torch.Tensor, k: torch.Tensor, row_k_start: torch.Tensor,
+                    row_k_end: torch.Tensor, out_cols: int | None = None,
+                    scale: float = DEFAULT_SCALE, out: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Prefill scores.  q: bf16 [T, 4, 128]; k: bf16 [NK, 128] (both unit
+    feature stride, 16-byte aligned, outer strides multiples of 8); row_k_start,
+    row_k_end: int32 [T].  Returns fp32 [T, out_cols]."""
+    lib = load_library()
+    _gpu("q", q, torch.bfloat16)
+    _gpu("k", k, torch.bfloat16)
+    _gpu("row_k_start", row_k_start, torch.int32)
+    _gpu("row_k_end", row_k_end, torch.int32)
+    if q.dim() != 3 or k.dim() != 2:
+        raise ValueError("q must be [T, H, D] and k [NK, D]")
+    num_rows, heads, dim = q.shape
+    if (q.stride(2) != 1 and dim > 1) or (k.stride(1) != 1 and k.shape[1] > 1):
+        raise QSAError(QSA_ERR_LAYOUT, "q and k need unit feature stride")
+    if k.shape[1] != dim:
+        raise ValueError("q and k head_dim differ")
+    for name, t in (("row_k_start", row_k_start), ("row_k_end", row_k_end)):
+        if t.numel() != num_rows or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [T] tensor")
+    if out is None:
+        if out_cols is None:
+            raise ValueError("give out_cols or out")
+        out = torch.empty((num_rows, out_cols), dtype=torch.float32, device=q.device)
+    _gpu("out", out, torch.float32)
+    if out.dim() != 2 or out.shape[0] != num_rows or (out.shape[1] > 1 and out.stride(1) != 1):
+        raise ValueError("out must be [T, out_cols] with unit column stride")
+    _check(lib.qsa_mqa_prefill(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.shape[0], _ptr(row_k_start),
+        _ptr(row_k_end), num_rows, heads, dim, float(scale), _ptr(out), out.stride(0),
+        out.shape[1], _stream_handle(stream)))
+    return out
+
+
+def qsa_topk_blocks(logits: torch.Tensor, k: int, out: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Per-row top-k column indices of fp32 logits [T, C]: int32 [T, k],
+    ascending, -1 padded."""
+    lib = load_library()
+    _gpu("logits", logits, torch.float32)
+    if logits.dim() != 2 or (logits.shape[1] > 1 and logits.stride(1) != 1):
+        raise ValueError("logits must be [T, C] with unit column stride")
+    rows, cols = logits.shape
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
+    _gpu("out", out, torch.int32)
+    if out.dim() != 2 or out.shape[0] != rows or out.shape[1] != k or (k > 1 and out.stride(1) != 1):
+        raise ValueError("out must be [T, k] with unit column stride")
+    _check(lib.qsa_topk_blocks(_ptr(logits), logits.stride(0), rows, cols, int(k), _ptr(out),
+                               out.stride(0), _stream_handle(stream)))
+    return out

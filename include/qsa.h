@@ -1,0 +1,200 @@
+/*
+ * qsa.h -- C ABI of the MI355X (gfx950) QSA lightweight MQA indexer.
+ *
+ * The indexer scores compressed 4-token key blocks for every query row:
+ *
+ *   score(row, n) = scale * sum_{h<4} max(0, q[row][h][:] . k[n][:])
+ *
+ * with 4 query heads sharing one 128-wide compressed key head, scale normally
+ * 1/sqrt(128), and -inf for every block the row may not see.  Definitions:
+ * MATE API docs, page "QSA (Qwen Sparse Attention)", section "MQA score"
+ * (score, paged decode form, packed prefill form, layout rules) and section
+ * "Core Attention" (request-local int32 block indices, -1 padding); the
+ * visibility rule is from the vLLM page "vllm/models/qwen4_exp/common/
+ * qsa_cache.py" (_build_qsa_metadata_kernel) and vLLM PR 54513 "Separate
+ * prefill and decode paths for QSA indexer" (section "Main changes").
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned device memory (hipMalloc'd or from a
+ *     framework allocator).  Host pointers are marked "host".  The library
+ *     allocates nothing and keeps no device state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All device work is enqueued on it; no call synchronizes.
+ *   - Argument checks read only the host-side arguments, never device
+ *     contents, so every call may be captured into a HIP graph.
+ *   - Strides are in elements, not bytes.
+ *   - Return value: QSA_OK, or an error code with a message available from
+ *     qsa_last_error() on the calling thread.  Calls with nothing to compute
+ *     (zero rows) return QSA_OK without launching.
+ *   - Entry points are thread-safe; calls that write overlapping outputs on
+ *     different streams race, as with any kernel.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+
+enum qsa_status {
+    QSA_OK = 0,
+    QSA_ERR_INVALID_ARGUMENT = 1, /* a size, count, pointer or value is invalid   */
+    QSA_ERR_UNSUPPORTED = 2,      /* heads/head_dim other than (4, 128)          */
+    QSA_ERR_LAYOUT = 3,           /* alignment or stride rule of the vector loads */
+    QSA_ERR_DEVICE = 4            /* the HIP runtime reported an error            */
+};
+
+/* QSA_ABI_VERSION of the loaded library. */
+int qsa_abi_version(void);
+
+/* Text of the last error returned on this thread ("" if none). */
+const char *qsa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Per-step metadata (host and device helpers).
+ *
+ * qsa_split_batch -- decode/prefill split of one batch (host only).
+ *   Source: vLLM page qsa_cache.py, QSAMetadataBuilder (decode threshold
+ *   with speculative tokens counted as decode, decodes ordered first, one
+ *   uniform decode query length).  Rule used here: a request is a decode when
+ *   its query length L satisfies 1 <= L <= decode_threshold and L equals the
+ *   decode query length DQL, the length of the first request (in batch order)
+ *   with 1 <= L <= decode_threshold.  Empty requests are not decodes.
+ *   query_start_loc : host int32 [num_reqs+1], non-decreasing, from 0.
+ *   order           : host int32 [num_reqs] or NULL.  NULL: the batch is
+ *                     taken as already ordered decodes-first and the decodes
+ *                     are its longest qualifying prefix.  Non-NULL: receives
+ *                     the stable order that puts every decode first, and the
+ *                     counts describe the batch in that order.
+ *   counts          : host int32 [5] receives num_decodes, num_decode_tokens,
+ *                     num_prefills, num_prefill_tokens, DQL (0 if no decode).
+ *   Errors: INVALID_ARGUMENT for NULL query_start_loc/counts, num_reqs < 0,
+ *   decode_threshold < 1, or a decreasing query_start_loc.
+ */
+int qsa_split_batch(const int32_t *query_start_loc, int32_t num_reqs, int32_t decode_threshold,
+                    int32_t *order, int32_t *counts);
+
+/* qsa_build_metadata -- per-token metadata on the device.
+ *   For query token t in [0, num_tokens): its request r (the one with
+ *   query_start_loc[r] <= t < query_start_loc[r+1]), its logical position
+ *   pos = seq_lens[r] - query_len[r] + (t - query_start_loc[r]) and its
+ *   visible block count max(0, min((pos+1)/cr, seq_lens[r]/cr)) (floor
+ *   division).  Tokens at or past query_start_loc[num_reqs] are padding:
+ *   request 0, position -1, 0 visible blocks.  Also comp_lens[r] =
+ *   seq_lens[r]/cr, and -- when key_offsets is given -- the prefill key
+ *   interval of each token over packed keys: row_k_start[t] =
+ *   key_offsets[r], row_k_end[t] = key_offsets[r] + visible[t].
+ *   Source: vLLM page qsa_cache.py (_logical_positions,
+ *   _build_qsa_metadata_kernel); PR 54513 "Main changes".
+ *   query_start_loc : device int32 [num_reqs+1];  seq_lens : device int32 [num_reqs]
+ *   key_offsets     : device int32 [num_reqs] or NULL
+ *   token_to_req    : device int32 [num_tokens] or NULL
+ *   positions       : device int64 [num_tokens] or NULL
+ *   visible         : device int32 [num_tokens] or NULL
+ *   comp_lens       : device int32 [num_reqs] or NULL
+ *   row_k_start, row_k_end : device int32 [num_tokens]; required iff key_offsets
+ *   Errors: INVALID_ARGUMENT for negative counts, compress_ratio < 1, NULL
+ *   required pointers.
+ */
+int qsa_build_metadata(const int32_t *query_start_loc, const int32_t *seq_lens,
+                       int32_t num_reqs, int32_t num_tokens, int32_t compress_ratio,
+                       const int32_t *key_offsets, int32_t *token_to_req, int64_t *positions,
+                       int32_t *visible, int32_t *comp_lens, int32_t *row_k_start,
+                       int32_t *row_k_end, void *stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_mqa_decode -- decode scores over the paged compressed-key cache.
+ *   Source: MATE "QSA (Qwen Sparse Attention)", section "MQA score" (paged
+ *   keys [pages, page_size, 1, dim], page table with -1 for unused entries,
+ *   compressed context lengths, missing or out-of-range pages score -inf,
+ *   broadcast Q accepted); visibility per row from vLLM qsa_cache.py.
+ *
+ *   q          : device bf16 [num_reqs][dql][4][128]; element strides
+ *                q_stride_req, q_stride_row, q_stride_head (any value,
+ *                including 0 for broadcast); unit feature stride.  No
+ *                alignment rule: aligned Q uses 16-byte loads, other Q
+ *                element loads.
+ *   k_cache    : device bf16 [num_pages][page_size][1][128], contiguous,
+ *                16-byte aligned.  Row p*page_size + i holds compressed key
+ *                i of page p.
+ *   page_table : device int32 [num_reqs][page_table_cols], row stride
+ *                page_table_stride.  Entry -1 (or any id outside
+ *                [0, num_pages)) = no page: those blocks score -inf.
+ *   comp_lens  : device int32 [num_reqs]: complete 4-token blocks of each
+ *                request (seq_len / 4).
+ *   visible    : device int32 [num_reqs*dql] or NULL: blocks visible to row
+ *                r*dql+j; values are clamped to [0, comp_lens[r]].  NULL:
+ *                every row sees comp_lens[r] blocks.
+ *   scale      : finite, > 0; multiplies the head sum (1/sqrt(128) normally).
+ *   out        : device fp32 [num_reqs*dql][out_cols], row stride out_stride
+ *                (>= out_cols), 4-byte aligned.  Column c = block c of the
+ *                request.  Every cell is written: the score, or -inf when
+ *                c >= visible, the page is missing, or c >= page_table_cols
+ *                * page_size.
+ *   Errors: UNSUPPORTED unless (num_heads, head_dim) == (4, 128);
+ *   INVALID_ARGUMENT for negative sizes, dql outside [1, 16], page_size
+ *   outside [1, 1<<20], out_stride < out_cols, a bad scale or a NULL pointer
+ *   that has work to feed; LAYOUT for a misaligned k_cache or out.
+ */
+int qsa_mqa_decode(const void *q, int64_t q_stride_req, int64_t q_stride_row,
+                   int64_t q_stride_head, const void *k_cache, int64_t num_pages,
+                   int32_t page_size, const int32_t *page_table, int64_t page_table_stride,
+                   int32_t page_table_cols, const int32_t *comp_lens, const int32_t *visible,
+                   int32_t num_reqs, int32_t dql, int32_t num_heads, int32_t head_dim,
+                   float scale, float *out, int64_t out_stride, int32_t out_cols,
+                   void *stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_mqa_prefill -- prefill scores over packed queries and shared keys.
+ *   Source: MATE "QSA (Qwen Sparse Attention)", section "MQA score" (packed
+ *   queries, shared keys, per-row key intervals; the vector-load layout
+ *   rules for query and keys).
+ *
+ *   q          : device bf16 [num_rows][4][128], element strides
+ *                q_stride_row, q_stride_head; unit feature stride.
+ *   k          : device bf16 [num_keys][128], element row stride k_stride;
+ *                unit feature stride.
+ *   Layout rule (q and k): base 16-byte aligned; every axis with more than
+ *   one element has a positive stride that is a multiple of 8 elements.
+ *   row_k_start, row_k_end : device int32 [num_rows].  Column c of row t
+ *                holds key row_k_start[t] + c; the cell is a score when that
+ *                key lies in [0, num_keys) and below row_k_end[t], else -inf
+ *                (an empty or reversed interval masks the whole row).
+ *   out        : device fp32 [num_rows][out_cols], row stride out_stride
+ *                (>= out_cols), 4-byte aligned; every cell is written.
+ *   Errors: as qsa_mqa_decode, plus LAYOUT when q or k breaks the layout rule.
+ */
+int qsa_mqa_prefill(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
+                    int64_t k_stride, int64_t num_keys, const int32_t *row_k_start,
+                    const int32_t *row_k_end, int32_t num_rows, int32_t num_heads,
+                    int32_t head_dim, float scale, float *out, int64_t out_stride,
+                    int32_t out_cols, void *stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_topk_blocks -- per-row top-k block indices.
+ *   Source: MATE "QSA (Qwen Sparse Attention)": the caller keeps the
+ *   top-scoring blocks (intro) as request-local int32 indices padded with -1
+ *   (section "Core Attention").  Rule used here: candidates are the cells
+ *   greater than -inf (NaN is never a candidate); the k largest are kept,
+ *   equal values (with -0 equal to +0) going to the lower column; the picks
+ *   are written in ascending column order followed by -1 up to k.
+ *
+ *   logits  : device fp32 [num_rows][num_cols], row stride logits_stride
+ *             (>= num_cols), 4-byte aligned.
+ *   out_idx : device int32 [num_rows][k], row stride out_stride (>= k).
+ *   Errors: INVALID_ARGUMENT for negative sizes, k < 1, k > 1<<20, strides
+ *   below the row width or NULL pointers that have work to feed.
+ */
+int qsa_topk_blocks(const float *logits, int64_t logits_stride, int32_t num_rows,
+                    int32_t num_cols, int32_t k, int32_t *out_idx, int64_t out_stride,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

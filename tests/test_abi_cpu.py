@@ -1,0 +1,200 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry
+point include/qsa.h declares, and rejects bad arguments before touching the
+device.  No compute call runs here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_indexer_scoring_amd import qsa
+    if not os.path.exists(qsa.LIB_PATH):
+        from block_indexer_scoring_amd import build
+        build.build()
+    return qsa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks", "qsa_build_metadata",
+              "qsa_split_batch", "qsa_last_error", "qsa_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libqsa.so does not export {name}"
+    from block_indexer_scoring_amd import qsa
+    assert set(qsa.SYMBOLS) == set(declared_functions())
+
+
+def test_abi_version(lib):
+    assert lib.qsa_abi_version() == 1
+
+
+def _err(lib):
+    return lib.qsa_last_error().decode()
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails its checks first
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, sr=512, sj=512, sh=128, k=FAKE, num_pages=4, page_size=16, pt=FAKE,
+             pt_stride=4, pt_cols=4, comp=FAKE, vis=None, num_reqs=1, dql=1, heads=4, dim=128,
+             scale=0.088, out=FAKE, out_stride=64, out_cols=64)
+    a.update(kw)
+    return lib.qsa_mqa_decode(a["q"], a["sr"], a["sj"], a["sh"], a["k"], a["num_pages"],
+                              a["page_size"], a["pt"], a["pt_stride"], a["pt_cols"], a["comp"],
+                              a["vis"], a["num_reqs"], a["dql"], a["heads"], a["dim"], a["scale"],
+                              a["out"], a["out_stride"], a["out_cols"], None)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(heads=8), 2, "(4, 128)"),
+    (dict(dim=64), 2, "(4, 128)"),
+    (dict(scale=0.0), 1, "scale"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(scale=float("inf")), 1, "scale"),
+    (dict(scale=-1.0), 1, "scale"),
+    (dict(dql=0), 1, "dql"),
+    (dict(dql=17), 1, "dql"),
+    (dict(page_size=0), 1, "page_size"),
+    (dict(page_size=(1 << 20) + 1), 1, "page_size"),
+    (dict(out_stride=10), 1, "out_stride"),
+    (dict(num_reqs=-1), 1, "negative"),
+    (dict(out_cols=-5, out_stride=0), 1, "negative"),
+    (dict(num_reqs=2, pt_stride=2), 1, "page_table_stride"),
+    (dict(q=None), 1, "NULL"),
+    (dict(comp=None), 1, "NULL"),
+    (dict(out=None), 1, "NULL"),
+    (dict(k=None), 1, "k_cache"),
+    (dict(pt=None), 1, "page_table"),
+    (dict(k=FAKE + 8), 3, "aligned"),
+    (dict(out=FAKE + 2), 3, "aligned"),
+])
+def test_decode_rejects(lib, kw, code, text):
+    assert _decode(lib, **kw) == code
+    assert text in _err(lib)
+
+
+def test_decode_zero_work_is_ok_without_device(lib):
+    assert _decode(lib, num_reqs=0, q=None, comp=None, out=None) == 0
+    assert _decode(lib, out_cols=0, out_stride=0, q=None, out=None) == 0
+    assert _err(lib) == ""
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, sq=512, sh=128, k=FAKE, sk=128, nk=100, ks=FAKE, ke=FAKE, rows=10, heads=4,
+             dim=128, scale=0.088, out=FAKE, out_stride=100, out_cols=100)
+    a.update(kw)
+    return lib.qsa_mqa_prefill(a["q"], a["sq"], a["sh"], a["k"], a["sk"], a["nk"], a["ks"], a["ke"],
+                               a["rows"], a["heads"], a["dim"], a["scale"], a["out"],
+                               a["out_stride"], a["out_cols"], None)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(heads=2), 2, "(4, 128)"),
+    (dict(scale=0.0), 1, "scale"),
+    (dict(out_stride=99), 1, "out_stride"),
+    (dict(rows=-1), 1, "negative"),
+    (dict(nk=-1), 1, "negative"),
+    (dict(q=None), 1, "NULL"),
+    (dict(ks=None), 1, "NULL"),
+    (dict(k=None), 1, "NULL k"),
+    (dict(q=FAKE + 2), 3, "16-byte"),
+    (dict(k=FAKE + 4), 3, "16-byte"),
+    (dict(sq=516), 3, "multiples"),
+    (dict(sq=0), 3, "multiples"),
+    (dict(sh=130), 3, "multiples"),
+    (dict(sh=0), 3, "multiples"),
+    (dict(sk=132), 3, "multiples"),
+    (dict(sk=-128), 3, "multiples"),
+    (dict(out=FAKE + 1), 3, "aligned"),
+])
+def test_prefill_rejects(lib, kw, code, text):
+    assert _prefill(lib, **kw) == code
+    assert text in _err(lib)
+
+
+def test_prefill_layout_exemptions_for_single_element_axes(lib):
+    # An axis of one element is exempt from the stride rule; nothing to
+    # compute (out_cols 0) so no launch happens.
+    assert _prefill(lib, rows=1, sq=3, out_cols=0, out_stride=0) == 0
+    assert _prefill(lib, rows=0, q=None) == 0
+
+
+@pytest.mark.parametrize("args,code,text", [
+    ((FAKE, 10, 2, 10, 0, FAKE, 4), 1, "k must"),
+    ((FAKE, 10, 2, 10, (1 << 20) + 1, FAKE, 1 << 21), 1, "k must"),
+    ((FAKE, 9, 2, 10, 4, FAKE, 4), 1, "logits_stride"),
+    ((FAKE, 10, 2, 10, 4, FAKE, 3), 1, "out_stride"),
+    ((FAKE, 10, -2, 10, 4, FAKE, 4), 1, "negative"),
+    ((None, 10, 2, 10, 4, FAKE, 4), 1, "NULL"),
+    ((FAKE, 10, 2, 10, 4, None, 4), 1, "NULL"),
+    ((FAKE + 2, 10, 2, 10, 4, FAKE, 4), 3, "aligned"),
+])
+def test_topk_rejects(lib, args, code, text):
+    assert lib.qsa_topk_blocks(*args, None) == code
+    assert text in _err(lib)
+
+
+def test_metadata_rejects(lib):
+    assert lib.qsa_build_metadata(FAKE, FAKE, -1, 4, 4, None, None, None, None, None, None, None, None) == 1
+    assert lib.qsa_build_metadata(FAKE, FAKE, 1, 4, 0, None, None, None, None, None, None, None, None) == 1
+    assert "compress_ratio" in _err(lib)
+    assert lib.qsa_build_metadata(None, FAKE, 1, 4, 4, None, None, None, None, None, None, None, None) == 1
+    assert lib.qsa_build_metadata(FAKE, FAKE, 1, 4, 4, FAKE, None, None, None, None, None, None, None) == 1
+    assert "key_offsets" in _err(lib)
+    assert lib.qsa_build_metadata(FAKE, FAKE, 1, 4, 4, None, None, None, None, None, FAKE, None, None) == 1
+    assert lib.qsa_build_metadata(FAKE, None, 0, 0, 4, None, None, None, None, None, None, None, None) == 0
+
+
+def test_split_batch_matches_oracle(lib):
+    from block_indexer_scoring_amd import qsa
+    rng = np.random.default_rng(1)
+    for _ in range(300):
+        R = int(rng.integers(0, 12))
+        lens = rng.choice([0, 1, 2, 3, 4, 5, 9, 40], size=R, p=[.1, .2, .1, .05, .3, .05, .1, .1])
+        qsl = [0] + np.cumsum(lens).tolist()
+        thr = int(rng.integers(1, 6))
+        for reorder in (False, True):
+            assert qsa.qsa_split_batch(qsl, thr, reorder) == O.split_batch(qsl, thr, reorder), (qsl, thr)
+
+
+def test_split_batch_rejects(lib):
+    counts = (ctypes.c_int32 * 5)()
+    bad = (ctypes.c_int32 * 3)(0, 5, 4)
+    assert lib.qsa_split_batch(ctypes.addressof(bad), 2, 4, None, ctypes.addressof(counts)) == 1
+    assert "decreases" in _err(lib)
+    good = (ctypes.c_int32 * 3)(0, 4, 8)
+    assert lib.qsa_split_batch(ctypes.addressof(good), 2, 0, None, ctypes.addressof(counts)) == 1
+    assert lib.qsa_split_batch(None, 2, 4, None, ctypes.addressof(counts)) == 1
+    assert lib.qsa_split_batch(ctypes.addressof(good), 2, 4, None, ctypes.addressof(counts)) == 0
+    assert list(counts) == [2, 8, 0, 0, 4]
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    from block_indexer_scoring_amd import qsa
+    q = torch.zeros((1, 1, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        qsa.qsa_mqa_decode(q, q, torch.zeros((1, 1), dtype=torch.int32),
+                           torch.zeros(1, dtype=torch.int32), out_cols=4)
+    with pytest.raises(ValueError, match="GPU"):
+        qsa.qsa_topk_blocks(torch.zeros((2, 3)), 1)
