@@ -1,0 +1,327 @@
+"""Benchmark of the QSA MQA indexer hot path on one MI355X.
+
+One step = one pass of the whole path over one mixed batch, as a serving step
+would run it (decodes first, then prefills):
+  1. qsa_build_metadata  per-token request, position, visible blocks, key
+                         intervals for all 8,256 query tokens of the batch;
+  2. qsa_mqa_decode      16 requests x DQL 4, log-normal contexts
+                         3,508 / 51,200 / 102,400 tokens (min/mean/max),
+                         page_size 64, keys read through the page table;
+  3. qsa_mqa_prefill     1 request: 8,192 query tokens over a 100,000-token
+                         prefix (27,048 compressed keys);
+  4. qsa_topk_blocks     top-512 blocks of every decode row and every
+                         prefill row.
+Inputs are resident in HBM before timing.  The decode key cache rotates over
+several independently generated pools (more bytes than the 256 MB Infinity
+Cache), so every decode launch streams its keys from HBM.
+
+Headline `value`: decode throughput in GB/s with the pages' accounting
+(unique bf16 keys + bf16 queries + fp32 logits of visible blocks), from the
+decode kernel's average duration measured with HIP events on its stream.
+Prefill is reported in TFLOP/s (2*4*128 FLOPs per visible block per row) and
+top-k in GB/s (logits read + indices written).
+
+Work accounting follows vLLM PR 54513 ("Separate prefill and decode paths for
+QSA indexer", section "Microbenchmarks"); tests/test_bench_accounting.py pins
+these formulas to the GB/s and TFLOP/s printed there.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode GB/s (% HBM peak) @16 req ~51K ctx; prefill TFLOP/s (% MFMA peak) 1x8K"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+PAGES_DECODE_GBPS = 3374.0      # GB300, 16 req x DQL 4, 3,508/51,200/102,400 (PR 54513)
+HEAD_DIM = 128
+HEADS = 4
+
+
+# ----------------------------------------------------------------------------
+# Work accounting (the pages' convention)
+
+
+def decode_bytes(num_reqs: int, dql: int, comp_total: float) -> float:
+    """Unique bf16 keys (read once per request) + bf16 queries + fp32 logits of
+    the visible blocks.  comp_total = sum over requests of compressed keys."""
+    keys = comp_total * HEAD_DIM * 2
+    queries = num_reqs * dql * HEADS * HEAD_DIM * 2
+    logits = dql * comp_total * 4
+    return keys + queries + logits
+
+
+def prefill_flops(visible_total: int) -> float:
+    """2 * heads * head_dim FLOPs per visible (row, block) pair."""
+    return 2.0 * HEADS * HEAD_DIM * visible_total
+
+
+def topk_bytes(rows: int, cols: int, k: int) -> float:
+    """fp32 logits read + int32 indices written."""
+    return rows * cols * 4.0 + rows * k * 4.0
+
+
+# ----------------------------------------------------------------------------
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel_file: str, kernel: str):
+    """HBM traffic per launch from a committed rocprofv3 PMC summary, or None
+    when no summary exists or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{kernel}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    src = os.path.join(ROOT, "block_indexer_scoring_amd", "csrc", kernel_file)
+    if vals.get("source_sha256_16") != source_digest(src):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(dec_inp, dec_vis, min_cpu_seconds: float = 10.0, max_passes: int = 8):
+    """The oracle, as it stands, on this host's cores: full decode passes over
+    the decode workload until about min_cpu_seconds of CPU work (wall x
+    threads) have run."""
+    from oracle import oracle as O
+    threads = O._threads(None)
+    comp = O.comp_lens(dec_inp.seq_lens)
+    passes, wall = 0, 0.0
+    while passes < max_passes and wall * threads < min_cpu_seconds:
+        t0 = time.perf_counter()
+        O.decode(dec_inp.q, dec_inp.k_pool, dec_inp.page_table, comp, dec_vis, dec_inp.out_cols,
+                 threads=threads)
+        wall += time.perf_counter() - t0
+        passes += 1
+    nbytes = decode_bytes(dec_inp.num_reqs, dec_inp.dql, float(comp.sum()))
+    return {
+        "value": round(nbytes / (wall / passes) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{passes} full pass(es) of the oracle decode over the 16-request DQL-4 batch "
+                  f"(64 rows x {dec_inp.out_cols} columns, {int(comp.sum())} keys), "
+                  f"{wall:.2f} s wall on {threads} threads",
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--pools", type=int, default=8, help="decode key pools rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (PMC calibration)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "the indexer path has no multi-GPU mode here.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_indexer_scoring_amd as qsa
+    from workloads import WORKLOADS, decode_inputs
+
+    qsa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def to_i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    # --- inputs -------------------------------------------------------------
+    dw = WORKLOADS["specdecode_16x51k"]
+    dec = dw.make()
+    pw = WORKLOADS["prefill_1x8k_100k"]
+    pre = pw.make()
+    R, DQL = dec.num_reqs, dec.dql
+    T_dec = R * DQL
+    T_pre = pre.q.shape[0]
+    qlens = [DQL] * R + [T_pre]
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    seq = np.concatenate([dec.seq_lens, pre.seq_lens]).astype(np.int32)
+    key_offsets = np.zeros(R + 1, np.int32)  # the prefill request's keys start at 0
+    split = qsa.qsa_split_batch(qsl.tolist(), DQL)
+    assert split[1:] == (R, T_dec, 1, T_pre, DQL), split
+
+    q_dec = to_bf16(dec.q)
+    page_table = to_i32(dec.page_table)
+    pools = [to_bf16(dec.k_pool)]
+    for i in range(1, args.pools):
+        pool = decode_inputs([int(x) for x in dec.seq_lens], DQL, dec.page_size,
+                             dec.page_table.shape[1], 0, dec.out_cols, seed=1000 + i,
+                             shuffle=False).k_pool
+        assert pool.shape == dec.k_pool.shape
+        pools.append(to_bf16(pool))
+    q_pre, k_pre = to_bf16(pre.q), to_bf16(pre.k)
+    qsl_d, seq_d, off_d = to_i32(qsl), to_i32(seq), to_i32(key_offsets)
+
+    T_all = T_dec + T_pre
+    meta = {
+        "token_to_req": torch.empty(T_all, dtype=torch.int32, device=dev),
+        "positions": torch.empty(T_all, dtype=torch.int64, device=dev),
+        "visible": torch.empty(T_all, dtype=torch.int32, device=dev),
+        "comp_lens": torch.empty(R + 1, dtype=torch.int32, device=dev),
+        "row_k_start": torch.empty(T_all, dtype=torch.int32, device=dev),
+        "row_k_end": torch.empty(T_all, dtype=torch.int32, device=dev),
+    }
+    dec_out = torch.empty((T_dec, dec.out_cols), dtype=torch.float32, device=dev)
+    pre_out = torch.empty((T_pre, pre.out_cols), dtype=torch.float32, device=dev)
+    TOPK = 512
+    dec_top = torch.empty((T_dec, TOPK), dtype=torch.int32, device=dev)
+    pre_top = torch.empty((T_pre, TOPK), dtype=torch.int32, device=dev)
+    lib = qsa.load_library()
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(lib.qsa_last_error().decode())
+
+    scale = qsa.DEFAULT_SCALE
+    NAMES = ["metadata", "decode", "prefill", "topk_decode", "topk_prefill"]
+
+    def step(i, events=None):
+        pool = pools[i % len(pools)]
+        rec = (lambda j: events[j].record(stream)) if events else (lambda j: None)
+        rec(0)
+        check(lib.qsa_build_metadata(
+            qsl_d.data_ptr(), seq_d.data_ptr(), R + 1, T_all, 4, off_d.data_ptr(),
+            meta["token_to_req"].data_ptr(), meta["positions"].data_ptr(),
+            meta["visible"].data_ptr(), meta["comp_lens"].data_ptr(),
+            meta["row_k_start"].data_ptr(), meta["row_k_end"].data_ptr(), sh))
+        rec(1)
+        check(lib.qsa_mqa_decode(
+            q_dec.data_ptr(), q_dec.stride(0), q_dec.stride(1), q_dec.stride(2), pool.data_ptr(),
+            pool.shape[0], pool.shape[1], page_table.data_ptr(), page_table.stride(0),
+            page_table.shape[1], meta["comp_lens"].data_ptr(), meta["visible"].data_ptr(), R, DQL,
+            4, 128, scale, dec_out.data_ptr(), dec_out.stride(0), dec_out.shape[1], sh))
+        rec(2)
+        check(lib.qsa_mqa_prefill(
+            q_pre.data_ptr(), q_pre.stride(0), q_pre.stride(1), k_pre.data_ptr(), k_pre.stride(0),
+            k_pre.shape[0], meta["row_k_start"].data_ptr() + 4 * T_dec,
+            meta["row_k_end"].data_ptr() + 4 * T_dec, T_pre, 4, 128, scale, pre_out.data_ptr(),
+            pre_out.stride(0), pre_out.shape[1], sh))
+        rec(3)
+        check(lib.qsa_topk_blocks(dec_out.data_ptr(), dec_out.stride(0), T_dec, dec_out.shape[1],
+                                  TOPK, dec_top.data_ptr(), TOPK, sh))
+        rec(4)
+        check(lib.qsa_topk_blocks(pre_out.data_ptr(), pre_out.stride(0), T_pre, pre_out.shape[1],
+                                  TOPK, pre_top.data_ptr(), TOPK, sh))
+        rec(5)
+
+    # --- warmup -------------------------------------------------------------
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    vis_host = meta["visible"].cpu().numpy()
+    comp_host = meta["comp_lens"].cpu().numpy()
+
+    # --- timed region -------------------------------------------------------
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {n: [] for n in NAMES}
+    for e in evs:
+        for j, n in enumerate(NAMES):
+            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)  # microseconds
+    avg = {n: float(np.mean(v)) for n, v in per.items()}
+    med = {n: float(np.median(v)) for n, v in per.items()}
+
+    comp_total = float(comp_host[:R].sum())
+    dbytes = decode_bytes(R, DQL, comp_total)
+    decode_gbps = dbytes / (avg["decode"] * 1e-6) / 1e9
+    vis_pre_total = int(vis_host[T_dec:].astype(np.int64).sum())
+    pflops = prefill_flops(vis_pre_total)
+    prefill_tflops = pflops / (avg["prefill"] * 1e-6) / 1e12
+    tk_bytes = topk_bytes(T_pre, pre.out_cols, TOPK)
+    topk_gbps = tk_bytes / (avg["topk_prefill"] * 1e-6) / 1e9
+
+    def roof(bound, achieved, peak, unit, traffic):
+        return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic}
+
+    result = {
+        "metric": METRIC,
+        "value": round(decode_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(decode_gbps / PAGES_DECODE_GBPS, 4),
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "mixed batch: decode 16 req x DQL 4, contexts 3,508/51,200/102,400 "
+                        "(min/mean/max), page_size 64 + prefill 1x8,192 queries over a 100,000-token "
+                        "prefix; top-512 per row",
+            "decode_requests": R, "decode_query_len": DQL, "decode_keys": int(comp_total),
+            "page_size": dec.page_size, "decode_key_pools": len(pools),
+            "prefill_rows": T_pre, "prefill_keys": int(pre.k.shape[0]), "topk": TOPK,
+        },
+        "roofline": roof("hbm", decode_gbps, HBM_PEAK_GBPS, "GB/s",
+                         read_traffic("decode.hip", "decode")),
+        "roofline_prefill": roof("mfma", prefill_tflops, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
+                                 read_traffic("prefill.hip", "prefill")),
+        "roofline_topk": roof("hbm", topk_gbps, HBM_PEAK_GBPS, "GB/s",
+                              read_traffic("topk.hip", "topk")),
+        "kernel_us_avg": {n: round(v, 3) for n, v in avg.items()},
+        "kernel_us_median": {n: round(v, 3) for n, v in med.items()},
+        "prefill_tflops": round(prefill_tflops, 2),
+        "decode_bytes": dbytes, "prefill_flops": pflops, "topk_prefill_bytes": tk_bytes,
+    }
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n * 4
+
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        _, _, dec_vis = O.token_metadata(dec.query_start_loc, dec.seq_lens, T_dec)
+        result["cpu_baseline"] = cpu_baseline(dec, dec_vis)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
