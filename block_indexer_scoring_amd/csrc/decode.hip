@@ -8,28 +8,39 @@
 //
 // Work split: one wavefront per (request, 64-key span).  A span's keys are
 // read from HBM exactly once and shared by all DQL rows of the request, so
-// HBM traffic is the unique key bytes plus the output.
+// HBM traffic is the unique key bytes plus the output.  Spans that hold keys
+// are dispatched first (request-major), spans past a request's keys (-inf
+// only) after them, so every key-reading wave starts in the first wave of
+// the launch.  A wave issues all 16 KB of its span's loads before the first
+// MFMA; a mapped page is read without per-lane predication.
 //
-// Inside a span the wave runs the dot products on the matrix cores: the
-// query vectors of the request, ordered (row j, head h) -> m = 4j + h, form
-// the A operand of v_mfma_f32_16x16x32_bf16 (one 16-row tile per 4 rows),
-// and 16 keys form the B columns.  In the MFMA result layout a lane holds the
-// 4 consecutive m rows of one column, i.e. all 4 heads of one (row, key):
-// ReLU, head sum, scale and mask are applied in-lane with no shuffles.
-// Span key c0 + 4n + g (n = column 0..15, g = group 0..3) goes to column n of
-// group g, so after 4 groups each lane owns 4 consecutive keys and writes
-// them with one 16-byte store.
+// Inside a span the dot products run on the matrix cores: the query vectors
+// of the request, ordered (row j, head h) -> m = 4j + h, form the A operand
+// of v_mfma_f32_16x16x32_bf16 (one 16-row tile per 4 rows), and 16 keys form
+// the B columns.  In the MFMA result layout a lane holds the 4 consecutive m
+// rows of one column, i.e. all 4 heads of one (row, key): ReLU, head sum,
+// scale and mask are applied in-lane with no shuffles.  Key c0 + 4n + g of a
+// span (n = column 0..15, g = group 0..3) goes to column n of group g, so
+// after 4 groups each lane owns 4 consecutive keys and writes them with one
+// 16-byte store.
 #include "qsa_device.h"
 #include "qsa_internal.h"
+
+#ifndef QSA_DECODE_WAVES_PER_BLOCK
+#define QSA_DECODE_WAVES_PER_BLOCK 1
+#endif
 
 namespace qsa {
 namespace {
 
-constexpr int kSpan = 64;          // keys per wavefront task
-constexpr int kWavesPerBlock = 4;
+constexpr int kSpan = 64;     // keys per wavefront task
+constexpr int kPadSpans = 4;  // spans per -inf-only task
+constexpr int kWavesPerBlock = QSA_DECODE_WAVES_PER_BLOCK;
 
-// Q fragment for 16x16x32 step `ks` (features 32*ks .. 32*ks+31): lane
-// (n, q4) supplies query vector m = n of tile mt, features 32*ks + 8*q4 .. +7.
+enum PageMode { kPageGeneric = 0, kPageMultiple64 = 1, kPage64 = 2 };
+
+// Q fragment: lane (n, q4) supplies query vector (row j, head h) of its
+// tile, features `feature` .. +7.
 __device__ __forceinline__ u32x4 load_q_fragment(const DecodeParams &p, int r, int j, int h,
                                                  int feature) {
     const uint16_t *src = p.q + (int64_t)r * p.q_stride_req + (int64_t)j * p.q_stride_row +
@@ -42,77 +53,98 @@ __device__ __forceinline__ u32x4 load_q_fragment(const DecodeParams &p, int r, i
     return v;
 }
 
-template <int MT, bool PAGE_ALIGNED>
+__device__ __forceinline__ int wave_inclusive_sum(int x, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+struct Task {
+    int r;
+    int span;  // first span of the task
+    bool compute;
+    bool valid;
+};
+
+// Task order: first every span that holds keys (request-major, one span per
+// task), then the spans past a request's keys (-inf only, kPadSpans spans per
+// task).  Spans of request r that hold keys: ceil(comp_r / 64), capped at the
+// spans covering out_cols.  Each wave derives its task from the compressed
+// lengths with a wave-wide prefix sum, 64 requests per pass, so no task list
+// is needed.
+__device__ Task map_task(const DecodeParams &p, int task, int lane) {
+    int before = 0;  // tasks of earlier requests in the current pass
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll 1
+        for (int r0 = 0; r0 < p.num_reqs; r0 += 64) {
+            const int rr = r0 + lane;
+            int cnt = 0;
+            if (rr < p.num_reqs) {
+                const int comp = p.comp_lens[rr];
+                int keyed = comp > 0 ? (comp + kSpan - 1) / kSpan : 0;
+                keyed = keyed < p.spans ? keyed : p.spans;
+                cnt = pass == 0 ? keyed : (p.spans - keyed + kPadSpans - 1) / kPadSpans;
+            }
+            const int incl = wave_inclusive_sum(cnt, lane);
+            const int chunk_total = __builtin_amdgcn_readlane(incl, 63);
+            const int local = task - before;
+            if (local < chunk_total) {
+                const uint64_t below = __ballot(incl <= local);
+                const int idx = __popcll(below);  // first lane whose range holds `local`
+                const int excl = __builtin_amdgcn_readlane(incl - cnt, idx);
+                if (pass == 0) return Task{r0 + idx, local - excl, true, true};
+                int keyed_r = 0;
+                if (lane == idx) {
+                    const int comp = p.comp_lens[r0 + idx];
+                    keyed_r = comp > 0 ? (comp + kSpan - 1) / kSpan : 0;
+                    keyed_r = keyed_r < p.spans ? keyed_r : p.spans;
+                }
+                keyed_r = __builtin_amdgcn_readlane(keyed_r, idx);
+                return Task{r0 + idx, keyed_r + (local - excl) * kPadSpans, false, true};
+            }
+            before += chunk_total;
+        }
+        task -= before;
+        before = 0;
+    }
+    // The launch covers num_reqs * spans tasks, an upper bound of the real
+    // count (keyed spans plus padding groups); the surplus waves do nothing.
+    return Task{0, 0, false, false};
+}
+
+template <int MT, int PAGE_MODE>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    const int64_t num_tasks = (int64_t)p.num_reqs * p.spans;
-    if (task >= num_tasks) return;
-    // Span-major order: every request's first spans (which always hold keys)
-    // are dispatched before the later, mostly masked, spans.
-    const int span = (int)(task / p.num_reqs);
-    const int r = (int)(task % p.num_reqs);
+    const int task_id = blockIdx.x * kWavesPerBlock + wave;
+    const Task task = map_task(p, task_id, lane);
+    if (!task.valid) return;
+    const int r = __builtin_amdgcn_readfirstlane(task.r);
+    const int span = __builtin_amdgcn_readfirstlane(task.span);
     const int n = lane & 15;
     const int q4 = lane >> 4;
     const int c0 = span * kSpan;
 
-    const int comp = p.comp_lens[r];
-    int vis_row[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) vis_row[mt] = 0;
-    int vis_max = 0;
-    for (int j = 0; j < p.dql; ++j) {
-        int v = p.visible ? p.visible[(int64_t)r * p.dql + j] : comp;
-        v = v < 0 ? 0 : (v > comp ? comp : v);
-        vis_max = v > vis_max ? v : vis_max;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            if (j == 4 * mt + q4) vis_row[mt] = v;
-    }
-
     float res[MT][4];
-    if (c0 < vis_max) {
-        // Keys of this span: issue all 16 loads before any MFMA.
-        u32x4 kb[4][4];
-        bool key_ok[4];
-        int64_t key_row[4];
-        if (PAGE_ALIGNED) {
-            // page_size is a multiple of 64: the whole span is on one page.
-            const int slot = c0 / p.page_size;
-            int page = -1;
-            if (slot < p.page_table_cols) page = p.page_table[(int64_t)r * p.page_table_stride + slot];
-            const bool page_ok = page >= 0 && page < p.num_pages;
-            const int64_t base = (int64_t)page * p.page_size + (c0 % p.page_size);
+    if (task.compute) {
+        const int comp = p.comp_lens[r];
+        const int64_t pt_row = (int64_t)r * p.page_table_stride;
+        // Per-row visible counts (lane row j = 4*mt + q4).
+        int vis_row[MT];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c = c0 + 4 * n + g;
-                key_ok[g] = page_ok && c < vis_max;
-                key_row[g] = base + 4 * n + g;
-            }
-        } else {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c = c0 + 4 * n + g;
-                int page = -1;
-                if (c < vis_max) {
-                    const int slot = c / p.page_size;
-                    if (slot < p.page_table_cols)
-                        page = p.page_table[(int64_t)r * p.page_table_stride + slot];
-                }
-                key_ok[g] = page >= 0 && page < p.num_pages;
-                key_row[g] = (int64_t)page * p.page_size + (c % p.page_size);
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                kb[g][ks] = key_ok[g] ? load_u32x4(p.k + key_row[g] * kDim + 32 * ks + 8 * q4)
-                                      : zero_u32x4();
+        for (int mt = 0; mt < MT; ++mt) {
+            const int j = 4 * mt + q4;
+            int v = 0;
+            if (j < p.dql) v = p.visible ? p.visible[(int64_t)r * p.dql + j] : comp;
+            vis_row[mt] = v < 0 ? 0 : (v > comp ? comp : v);
         }
 
-        // Query fragments: tile mt holds rows j = 4*mt .. 4*mt+3.
+        // Query fragments (issued first: they hit in L2): tile mt holds rows
+        // j = 4*mt .. 4*mt+3.
         u32x4 qa[MT][4];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -123,6 +155,47 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
                 qa[mt][ks] = j < p.dql ? load_q_fragment(p, r, j, h, 32 * ks + 8 * q4) : zero_u32x4();
         }
 
+        // Key c0 + 4n + g, features 32ks + 8q4 .. +7, for every g and ks:
+        // all 16 loads issued before any MFMA.
+        u32x4 kb[4][4];
+        bool key_ok[4];
+        if (PAGE_MODE != kPageGeneric) {
+            // The span lies on one page; a mapped page is read whole (keys
+            // past comp are in bounds and masked below).
+            const int slot = PAGE_MODE == kPage64 ? span : c0 / p.page_size;
+            const int page = slot < p.page_table_cols ? p.page_table[pt_row + slot] : -1;
+            const bool page_ok = page >= 0 && page < p.num_pages;
+            if (page_ok) {
+                const int in_page = PAGE_MODE == kPage64 ? 0 : c0 % p.page_size;
+                const uint16_t *src = p.k + ((int64_t)page * p.page_size + in_page + 4 * n) * kDim + 8 * q4;
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) kb[g][ks] = load_u32x4(src + g * kDim + 32 * ks);
+            } else {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) kb[g][ks] = zero_u32x4();
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) key_ok[g] = page_ok && c0 + 4 * n + g < comp;
+        } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = c0 + 4 * n + g;
+                int page = -1;
+                if (c < comp) {
+                    const int slot = c / p.page_size;
+                    if (slot < p.page_table_cols) page = p.page_table[pt_row + slot];
+                }
+                key_ok[g] = page >= 0 && page < p.num_pages;
+                const uint16_t *src = p.k + ((int64_t)page * p.page_size + (c % p.page_size)) * kDim + 8 * q4;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) kb[g][ks] = key_ok[g] ? load_u32x4(src + 32 * ks) : zero_u32x4();
+            }
+        }
+
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -131,15 +204,30 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(qa[mt][ks], kb[g][ks], acc);
                 const int c = c0 + 4 * n + g;
-                const bool ok = key_ok[g] && c < vis_row[mt];
-                res[mt][g] = ok ? head_sum_score(acc, p.scale) : neg_inf();
+                res[mt][g] = (key_ok[g] && c < vis_row[mt]) ? head_sum_score(acc, p.scale) : neg_inf();
             }
         }
     } else {
+        // -inf only: spans span .. span + kPadSpans - 1 (clipped to out_cols).
+        const float ni = neg_inf();
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            const int j = 4 * mt + q4;
+            if (j >= p.dql) continue;
+            float *row = p.out + ((int64_t)r * p.dql + j) * p.out_stride;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) res[mt][g] = neg_inf();
+            for (int s = 0; s < kPadSpans; ++s) {
+                const int col = c0 + s * kSpan + 4 * n;
+                if (p.out_vec && col + 3 < p.out_cols) {
+                    *reinterpret_cast<f32x4 *>(row + col) = f32x4{ni, ni, ni, ni};
+                } else {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        if (col + g < p.out_cols) row[col + g] = ni;
+                }
+            }
+        }
+        return;
     }
 
     // Lane (n, q4) owns row j = 4*mt + q4, keys c0 + 4n .. c0 + 4n + 3.
@@ -161,14 +249,18 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
 
 template <int MT>
 hipError_t launch_mt(const DecodeParams &p, hipStream_t stream, dim3 grid, dim3 block) {
-    if (p.page_size % kSpan == 0)
-        hipLaunchKernelGGL((decode_kernel<MT, true>), grid, block, 0, stream, p);
+    if (p.page_size == kSpan)
+        hipLaunchKernelGGL((decode_kernel<MT, kPage64>), grid, block, 0, stream, p);
+    else if (p.page_size % kSpan == 0)
+        hipLaunchKernelGGL((decode_kernel<MT, kPageMultiple64>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_kernel<MT, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_kernel<MT, kPageGeneric>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
+
+int decode_span_keys() { return kSpan; }
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
     const int64_t tasks = (int64_t)p.num_reqs * p.spans;

@@ -8,11 +8,6 @@
 #include "qsa.h"
 #include "qsa_internal.h"
 
-namespace qsa {
-int prefill_col_chunk(int64_t num_rows, int32_t out_cols);
-int prefill_rows_per_block();
-}  // namespace qsa
-
 namespace {
 
 thread_local std::string g_last_error;
@@ -152,8 +147,9 @@ int qsa_mqa_decode(const void *q, int64_t q_stride_req, int64_t q_stride_row, in
         return fail(QSA_ERR_LAYOUT, "%s: k_cache must be 16-byte aligned (16-byte vector loads)", fn);
     if (!aligned(out, 4)) return fail(QSA_ERR_LAYOUT, "%s: out must be 4-byte aligned", fn);
     if (!aligned(q, 2)) return fail(QSA_ERR_LAYOUT, "%s: q must be 2-byte aligned", fn);
-    const int64_t spans = ((int64_t)out_cols + 63) / 64;
-    if ((int64_t)num_reqs * dql > INT32_MAX || (int64_t)num_reqs * spans / 4 >= INT32_MAX)
+    const int64_t span_keys = qsa::decode_span_keys();
+    const int64_t spans = ((int64_t)out_cols + span_keys - 1) / span_keys;
+    if ((int64_t)num_reqs * dql > INT32_MAX || (int64_t)num_reqs * spans >= INT32_MAX)
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
 
     qsa::DecodeParams p{};

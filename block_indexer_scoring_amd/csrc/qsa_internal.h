@@ -23,7 +23,7 @@ struct DecodeParams {
     float *out;
     int64_t out_stride;
     int32_t out_cols;
-    int32_t spans;              // ceil(out_cols / 64)
+    int32_t spans;              // ceil(out_cols / decode_span_keys())
     int32_t q_vec;              // Q may be read with 16-byte loads
     int32_t out_vec;            // out rows may be written with 16-byte stores
 };
@@ -61,6 +61,9 @@ struct MetaParams {
 };
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+int decode_span_keys();
+int prefill_col_chunk(int64_t num_rows, int32_t out_cols);
+int prefill_rows_per_block();
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams &p, hipStream_t stream);
 hipError_t launch_metadata(const MetaParams &p, hipStream_t stream);
