@@ -24,15 +24,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ u32x4 zero_u32x4() { return u32x4{0u, 0u, 0u, 0u}; }
 
-// ReLU that maps -0.0 to +0.0, so an all-negative head set gives +0.0.
-__device__ __forceinline__ float relu(float x) { return x > 0.0f ? x : 0.0f; }
+// ReLU as a signed-integer max on the bit pattern: positive floats order
+// like their bits, every non-positive float (-0 included) has the sign bit
+// set and maps to the bits of +0.0.  One VALU op, and an all-negative head
+// set gives exactly +0.0.
+__device__ __forceinline__ float relu(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
 
 // One MFMA accumulator quad holds the 4 head dots of one (query, key) pair:
 // score = scale * sum_h relu(dot_h).
 __device__ __forceinline__ float head_sum_score(f32x4 acc, float scale) {
-    float s = relu(acc[0]) + relu(acc[1]);
-    s += relu(acc[2]);
-    s += relu(acc[3]);
+    const float s = (relu(acc[0]) + relu(acc[1])) + (relu(acc[2]) + relu(acc[3]));
     return s * scale;
 }
 
