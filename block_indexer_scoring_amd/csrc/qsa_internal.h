@@ -50,6 +50,7 @@ struct TopkParams {
     int32_t num_rows, num_cols, k;
     int32_t *out;
     int64_t out_stride;
+    int32_t vec;                // logits rows may be read with 16-byte loads
 };
 
 struct MetaParams {

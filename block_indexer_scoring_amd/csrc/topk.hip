@@ -6,15 +6,22 @@
 // values going to the lower column, and write the picks in ascending column
 // order followed by -1.
 //
-// One 1024-thread workgroup per row.  Each float maps to an order-preserving
-// 32-bit key (+0 and -0 share one key; non-candidates get key 0, below every
-// candidate).  An exact radix select over the key bits (11 + 11 + 10, LDS
-// histograms) finds the k-th largest key T and how many of the keys equal to
-// T are needed.  The picks are then compacted in column order: a cell is
-// taken if key > T, or key == T and fewer than `need` equal keys precede it;
-// its output slot is (#greater before it) + min(#equal before it, need).
-// Rows up to 32768 columns stay in registers for the whole select; longer
-// rows are re-read from memory in each phase.
+// One 1024-thread workgroup per row, two rows per CU.  Each float maps to an
+// order-preserving 32-bit key (+0 and -0 share one key; non-candidates get
+// key 0, below every candidate).  An exact radix select over the key bits
+// (11 + 11 + 10, LDS histograms) finds the k-th largest key T and how many of
+// the keys equal to T are needed; a cell is picked if key > T, or key == T
+// and fewer than `need` equal keys precede it.
+//
+// Rows up to 32768 columns stay in registers, each thread owning a
+// contiguous run of columns, so thread order is column order and the picks
+// are placed with a single prefix sum.  Before the select, a floor F is
+// taken from the per-thread maxima: each thread's largest key witnesses one
+// key >= itself, so when the k largest maxima are >= F at least k keys are,
+// and T >= F.  The keys >= F (a few hundred for score rows) are compacted in
+// column order into an LDS list and the select and the output run over that
+// list only.  If the list would overflow, the same select runs over the
+// registers.  Longer rows are re-read from memory in each phase.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -23,6 +30,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kListCap = 4096;  // keys >= floor kept in LDS
 
 __device__ __forceinline__ uint32_t order_key(float v) {
     if (!(v > neg_inf())) return 0u;  // -inf and NaN are never picked
@@ -31,52 +39,40 @@ __device__ __forceinline__ uint32_t order_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over a wavefront with DPP moves (no LDS): a
+// Hillis-Steele scan inside each 16-lane row (row_shr 1, 2, 4, 8 with zero
+// fill), then row 0's total broadcast into row 1 and row 2's into row 3
+// (row_bcast:15), then rows 0-1's total into rows 2 and 3 (row_bcast:31).
+// Arithmetic is modulo 2^32.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false); // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false); // row_bcast:31
+    return x;
+}
+
 // Exclusive prefix sum over the workgroup in thread order; *total gets the
 // sum.  Arithmetic is modulo 2^32 (callers may pack two counters in one word).
-__device__ int block_exclusive_scan(int v, int *s_wave, int *total) {
+__device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave, int *total) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    uint32_t x = (uint32_t)v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)x, d, 64);
-        if (lane >= d) x += y;
-    }
+    const uint32_t x = wave_inclusive_scan((uint32_t)v);
     if (lane == 63) s_wave[wave] = (int)x;
     __syncthreads();
-    if (wave == 0) {
-        uint32_t w = lane < kWaves ? (uint32_t)s_wave[lane] : 0u;
+    uint32_t before = x - (uint32_t)v, all = 0u;
 #pragma unroll
-        for (int d = 1; d < kWaves; d <<= 1) {
-            const uint32_t y = (uint32_t)__shfl_up((int)w, d, 64);
-            if (lane >= d) w += y;
-        }
-        if (lane < kWaves) s_wave[lane] = (int)w;
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t t = (uint32_t)s_wave[w];
+        before += w < wave ? t : 0u;
+        all += t;
     }
-    __syncthreads();
-    const uint32_t before = (wave > 0 ? (uint32_t)s_wave[wave - 1] : 0u) + x - (uint32_t)v;
-    *total = s_wave[kWaves - 1];
+    *total = (int)all;
     __syncthreads();
     return (int)before;
 }
-
-__device__ __forceinline__ int lanes_below(uint64_t mask) {
-    const int lane = threadIdx.x & 63;
-    return __popcll(mask & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-}
-
-// Key source: registers (RESIDENT, E slots per thread) or the row in memory.
-template <int E, bool RESIDENT>
-struct RowKeys {
-    uint32_t reg[RESIDENT ? E : 1];
-    const float *row;
-    int cols;
-    __device__ __forceinline__ uint32_t get(int e) const {
-        if (RESIDENT) return reg[e];
-        const int i = e * kThreads + (int)threadIdx.x;
-        return i < cols ? order_key(row[i]) : 0u;
-    }
-};
 
 struct SelectShared {
     int hist[2048];
@@ -84,11 +80,97 @@ struct SelectShared {
     int pick_bin, pick_above;
 };
 
-// Radix-select the k-th largest candidate key.  Returns T and sets *need to
-// the number of keys equal to T that are picked.  Requires candidates > k.
-template <int E, bool RESIDENT>
-__device__ uint32_t radix_threshold(const RowKeys<E, RESIDENT> &keys, int slots, int k,
-                                    SelectShared &sh, int *need) {
+// Finds the bin of hist[0..nb) holding the kk-th largest counted key (bins
+// ordered by key, the top bin holding the largest keys).  Thread tid owns
+// nb/1024 bins counted down from the top; a prefix sum of the thread sums
+// locates the one thread whose bins hold it, and that thread walks them.
+// Returns the bin (-1 if fewer than kk keys were counted) and sets
+// *above_out to the count in higher bins.  Call after the histogram is
+// complete (a barrier after the last count); uniform result.
+// Kept out of line: inlined at its five call sites it pushes the kernel
+// past 64 VGPRs (the budget for two 1024-thread workgroups per CU).
+__device__ __noinline__ int find_bin(SelectShared &sh, int nb, int kk, int *above_out) {
+    const int tid = threadIdx.x;
+    const int per = nb / kThreads;
+    const int hi = nb - 1 - tid * per;
+    int s = 0;
+    for (int b = 0; b < per; ++b) s += sh.hist[hi - b];
+    int total;
+    int above = block_exclusive_scan(s, sh.wave_tmp, &total);
+    if (tid == 0 && total < kk) {
+        sh.pick_bin = -1;
+        sh.pick_above = 0;
+    }
+    if (above < kk && kk <= above + s) {
+        for (int b = 0; b < per; ++b) {
+            const int c = sh.hist[hi - b];
+            if (above + c >= kk) {
+                sh.pick_bin = hi - b;
+                sh.pick_above = above;
+                break;
+            }
+            above += c;
+        }
+    }
+    __syncthreads();
+    const int bin = sh.pick_bin;
+    *above_out = sh.pick_above;
+    __syncthreads();
+    return bin;
+}
+
+// Where a thread's keys come from during the select: the LDS list of keys
+// >= floor (entries tid, tid+1024, ... for counting; one contiguous slice
+// for placing), the row in memory as columns col0 .. col0+E-1 (the
+// register-resident layout, re-read), or the row in memory as columns
+// e*1024 + tid (rows too long for registers).
+enum KeySource { kFromList, kFromRowRun, kFromMemory };
+
+struct ListView {
+    const uint32_t *key;
+    const int *col;
+    int size;
+};
+
+struct RowView {
+    const float *x;
+    int cols;
+    int slots;
+    int col0;  // first column of this thread's run (kFromRowRun)
+};
+
+// Count into hist the keys >= floor whose bits under mask equal prefix.
+template <int E, int SRC>
+__device__ __forceinline__ void count_bins(const ListView &list, const RowView &row,
+                                           uint32_t floor, uint32_t mask,
+                                           uint32_t prefix, int shift, int nb, int *hist) {
+    auto visit = [&](uint32_t k) {
+        if (k >= floor && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1);
+    };
+    if (SRC == kFromRowRun) {
+#pragma unroll 1
+        for (int e = 0; e < E; ++e) {
+            const int c = row.col0 + e;
+            visit(c < row.cols ? order_key(row.x[c]) : 0u);
+        }
+    } else if (SRC == kFromList) {
+#pragma unroll 1
+        for (int i = threadIdx.x; i < list.size; i += kThreads) visit(list.key[i]);
+    } else {
+#pragma unroll 1
+        for (int e = 0; e < row.slots; ++e) {
+            const int i = e * kThreads + (int)threadIdx.x;
+            visit(i < row.cols ? order_key(row.x[i]) : 0u);
+        }
+    }
+}
+
+// Radix-select the k-th largest key among this thread's keys >= floor
+// (summed over the workgroup).  Requires at least k such keys.  Returns T
+// and sets *need to the number of keys equal to T that are picked.
+template <int E, int SRC>
+__device__ __forceinline__ uint32_t radix_threshold(const ListView &list, const RowView &row, int k,
+                                                    uint32_t floor, SelectShared &sh, int *need) {
     const int tid = threadIdx.x;
     uint32_t prefix = 0u, mask = 0u;
     int kk = k;
@@ -98,105 +180,164 @@ __device__ uint32_t radix_threshold(const RowKeys<E, RESIDENT> &keys, int slots,
         const int nb = pass == 2 ? 1024 : 2048;
         for (int b = tid; b < nb; b += kThreads) sh.hist[b] = 0;
         __syncthreads();
-        for (int e = 0; e < slots; ++e) {
-            const uint32_t key = keys.get(e);
-            if (key != 0u && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1);
-        }
+        count_bins<E, SRC>(list, row, floor, mask, prefix, shift, nb, sh.hist);
         __syncthreads();
-        // Thread tid owns the bins_per bins starting at the top, descending.
-        const int bins_per = nb / kThreads;
-        const int hi = nb - 1 - tid * bins_per;
-        int s = 0;
-        for (int b = 0; b < bins_per; ++b) s += sh.hist[hi - b];
-        int total;
-        int above = block_exclusive_scan(s, sh.wave_tmp, &total);
-        if (above < kk && kk <= above + s) {
-            for (int b = 0; b < bins_per; ++b) {
-                const int c = sh.hist[hi - b];
-                if (above + c >= kk) {
-                    sh.pick_bin = hi - b;
-                    sh.pick_above = above;
-                    break;
-                }
-                above += c;
-            }
-        }
-        __syncthreads();
-        kk -= sh.pick_above;
-        prefix |= (uint32_t)sh.pick_bin << shift;
+        int above;
+        const int bin = find_bin(sh, nb, kk, &above);
+        kk -= above;
+        prefix |= (uint32_t)bin << shift;
         mask |= (uint32_t)(nb - 1) << shift;
-        __syncthreads();
     }
     *need = kk;
     return prefix;
 }
 
-template <int E>
-__global__ __launch_bounds__(kThreads) void topk_resident_kernel(TopkParams p) {
-    __shared__ SelectShared sh;
-    __shared__ int s_off[E * kWaves];  // packed (greater << 16) | equal, per (slot, wave)
+// Floor from per-thread maxima: the lower edge of the 11-bit bin holding the
+// k-th largest thread maximum.  Returns 1 (no filtering) when fewer than k
+// threads hold a candidate (or the bin is the lowest one).
+__device__ __forceinline__ uint32_t prefilter_floor(uint32_t tmax, int k, SelectShared &sh) {
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    for (int b = tid; b < 2048; b += kThreads) sh.hist[b] = 0;
+    __syncthreads();
+    if (tmax != 0u) atomicAdd(&sh.hist[tmax >> 21], 1);
+    __syncthreads();
+    int above;
+    const int bin = find_bin(sh, 2048, k, &above);
+    return bin <= 0 ? 1u : ((uint32_t)bin << 21);
+}
+
+// Writes the picks of this thread's keys, which it visits in column order
+// (a run of the row, or the contiguous list slice [lo, hi)): one prefix sum
+// of packed (greater, equal) counts places every pick.  Counts stay below
+// 2^16 (at most 32768 keys per row here), so the low half never carries
+// into the high half.
+template <int E, int SRC>
+__device__ __forceinline__ void place_picks(const ListView &list, const RowView &row, int lo, int hi,
+                                            uint32_t T, int need, int32_t *out, SelectShared &sh) {
+    auto row_key = [&](int e) {
+        const int c = row.col0 + e;
+        return c < row.cols ? order_key(row.x[c]) : 0u;
+    };
+    int gt = 0, eq = 0;
+    if (SRC == kFromRowRun) {
+#pragma unroll 1
+        for (int e = 0; e < E; ++e) {
+            const uint32_t k = row_key(e);
+            gt += k > T;
+            eq += k == T && k != 0u;
+        }
+    } else {
+#pragma unroll 1
+        for (int i = lo; i < hi; ++i) {
+            gt += list.key[i] > T;
+            eq += list.key[i] == T;
+        }
+    }
+    int total;
+    const uint32_t base = (uint32_t)block_exclusive_scan((gt << 16) | eq, sh.wave_tmp, &total);
+    int gt_before = (int)(base >> 16);
+    int eq_before = (int)(base & 0xffffu);
+    auto place = [&](uint32_t k, int col) {
+        const bool is_gt = k > T;
+        const bool is_eq = k == T && k != 0u;
+        if (is_gt) out[gt_before + min(eq_before, need)] = col;
+        else if (is_eq && eq_before < need) out[gt_before + eq_before] = col;
+        gt_before += is_gt;  // counters advance arithmetically (no branches on them)
+        eq_before += is_eq;
+    };
+    if (SRC == kFromRowRun) {
+#pragma unroll 1
+        for (int e = 0; e < E; ++e) place(row_key(e), row.col0 + e);
+    } else {
+#pragma unroll 1
+        for (int i = lo; i < hi; ++i) place(list.key[i], list.col[i]);
+    }
+}
+
+template <int E>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void topk_resident_kernel(TopkParams p) {
+    __shared__ SelectShared sh;
+    __shared__ uint32_t list_key[kListCap];
+    __shared__ int list_col[kListCap];
+    const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const float *x = p.logits + row * p.logits_stride;
     int32_t *out = p.out + row * p.out_stride;
+    const int col0 = tid * E;  // this thread's columns: col0 .. col0 + E - 1
 
-    RowKeys<E, true> keys;
-    keys.row = x;
-    keys.cols = p.num_cols;
+    // Keys stay in registers as their top 16 bits, two per register: enough
+    // to test key >= floor exactly (the floor is a multiple of 2^21); the
+    // few keys that pass are re-read in full when the list is built.
+    uint32_t top16[(E + 1) / 2];
     int cand = 0;
+    uint32_t tmax = 0u;
+    auto absorb = [&](int e, uint32_t k) {
+        cand += k != 0u;
+        tmax = max(tmax, k);
+        if (e % 2 == 0) top16[e / 2] = k >> 16;
+        else top16[e / 2] |= k & 0xffff0000u;
+    };
+    if (p.vec && col0 + E <= p.num_cols) {
+        // The whole run is inside the row: 16-byte loads.
+        f32x4 v[E / 4];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int i = e * kThreads + tid;
-        keys.reg[e] = i < p.num_cols ? order_key(x[i]) : 0u;
-        cand += keys.reg[e] != 0u;
+        for (int e = 0; e < E / 4; ++e) v[e] = *reinterpret_cast<const f32x4 *>(x + col0 + 4 * e);
+#pragma unroll
+        for (int e = 0; e < E; ++e) absorb(e, order_key(v[e / 4][e % 4]));
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) absorb(e, col0 + e < p.num_cols ? order_key(x[col0 + e]) : 0u);
     }
+    auto key_top = [&](int e) { return e % 2 == 0 ? (top16[e / 2] & 0xffffu) : (top16[e / 2] >> 16); };
     int num_cand;
     block_exclusive_scan(cand, sh.wave_tmp, &num_cand);
 
-    uint32_t T = 0u;
-    int need = 0;
-    if (num_cand > p.k) T = radix_threshold<E, true>(keys, E, p.k, sh, &need);
-
-    // Counts of greater / equal keys per (slot, wave), then one scan in
-    // column order (slot-major, wave-minor, lane within the wave).
+    // Paths that need every key again (few candidates, no useful floor, or
+    // a list overflow) re-read this thread's run of the row (in L2 by then).
+    const RowView run{x, p.num_cols, 0, col0};
+    const ListView no_list{nullptr, nullptr, 0};
+    if (num_cand <= p.k) {
+        place_picks<E, kFromRowRun>(no_list, run, 0, 0, 0u, 0, out, sh);  // every candidate
+    } else {
+        const uint32_t floor = prefilter_floor(tmax, p.k, sh);
+        const uint32_t floor_top = floor >> 16;
+        int mine = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const uint32_t key = keys.reg[e];
-        const uint64_t gt = __ballot(key > T);
-        const uint64_t eq = __ballot(key == T && key != 0u);
-        if (lane == 0) s_off[e * kWaves + wave] = (int)(((uint32_t)__popcll(gt) << 16) | (uint32_t)__popcll(eq));
-    }
-    __syncthreads();
-    {
-        const int v = tid < E * kWaves ? s_off[tid] : 0;
-        int total;
-        const int before = block_exclusive_scan(v, sh.wave_tmp, &total);
-        if (tid < E * kWaves) s_off[tid] = before;
-        __syncthreads();
-    }
+        for (int e = 0; e < E; ++e) mine += key_top(e) >= floor_top;
+        int listed;
+        const int at = block_exclusive_scan(mine, sh.wave_tmp, &listed);
+        int need = 0;
+        const ListView list{list_key, list_col, listed};
+        if (floor > 1u && listed <= kListCap) {
+            if (mine > 0) {
+                int w = at;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const uint32_t key = keys.reg[e];
-        const bool is_gt = key > T;
-        const bool is_eq = key == T && key != 0u;
-        const uint64_t gt = __ballot(is_gt);
-        const uint64_t eq = __ballot(is_eq);
-        // Both counts are at most 32768 (at most 32768 columns), so the low
-        // half of the packed prefix never carries into the high half.
-        const uint32_t base = (uint32_t)s_off[e * kWaves + wave];
-        const int gt_before = (int)(base >> 16) + lanes_below(gt);
-        const int eq_before = (int)(base & 0xffffu) + lanes_below(eq);
-        const int col = e * kThreads + tid;
-        if (is_gt) out[gt_before + min(eq_before, need)] = col;
-        else if (is_eq && eq_before < need) out[gt_before + eq_before] = col;
+                for (int e = 0; e < E; ++e) {
+                    if (key_top(e) >= floor_top) {
+                        list_key[w] = order_key(x[col0 + e]);
+                        list_col[w] = col0 + e;
+                    }
+                    w += key_top(e) >= floor_top;
+                }
+            }
+            __syncthreads();
+            const uint32_t T = radix_threshold<E, kFromList>(list, run, p.k, floor, sh, &need);
+            // Contiguous slices of the list (column order) per thread.
+            const int per = (listed + kThreads - 1) / kThreads;
+            const int lo = min(tid * per, listed), hi = min(lo + per, listed);
+            place_picks<E, kFromList>(list, run, lo, hi, T, need, out, sh);
+        } else {
+            const uint32_t T = radix_threshold<E, kFromRowRun>(no_list, run, p.k, floor, sh, &need);
+            place_picks<E, kFromRowRun>(no_list, run, 0, 0, T, need, out, sh);
+        }
     }
     const int picked = min(num_cand, p.k);
     for (int i = picked + tid; i < p.k; i += kThreads) out[i] = -1;
 }
 
-// Rows longer than the register-resident limit: each phase re-reads the row.
+// Rows longer than the register-resident limit: each phase re-reads the row,
+// column c owned by thread c % 1024; picks are placed slot by slot.
 __global__ __launch_bounds__(kThreads) void topk_streaming_kernel(TopkParams p) {
     __shared__ SelectShared sh;
     __shared__ int s_cnt[2][kWaves];
@@ -207,22 +348,27 @@ __global__ __launch_bounds__(kThreads) void topk_streaming_kernel(TopkParams p) 
     const float *x = p.logits + row * p.logits_stride;
     int32_t *out = p.out + row * p.out_stride;
     const int slots = (p.num_cols + kThreads - 1) / kThreads;
+    auto key_at = [&](int e) {
+        const int i = e * kThreads + tid;
+        return i < p.num_cols ? order_key(x[i]) : 0u;
+    };
 
-    RowKeys<1, false> keys;
-    keys.row = x;
-    keys.cols = p.num_cols;
     int cand = 0;
-    for (int e = 0; e < slots; ++e) cand += keys.get(e) != 0u;
+    for (int e = 0; e < slots; ++e) cand += key_at(e) != 0u;
     int num_cand;
     block_exclusive_scan(cand, sh.wave_tmp, &num_cand);
 
     uint32_t T = 0u;
     int need = 0;
-    if (num_cand > p.k) T = radix_threshold<1, false>(keys, slots, p.k, sh, &need);
+    if (num_cand > p.k) {
+        const ListView no_list{nullptr, nullptr, 0};
+        const RowView mem{x, p.num_cols, slots, 0};
+        T = radix_threshold<1, kFromMemory>(no_list, mem, p.k, 1u, sh, &need);
+    }
 
     int gt_run = 0, eq_run = 0;  // greater / equal keys in earlier slots
     for (int e = 0; e < slots; ++e) {
-        const uint32_t key = keys.get(e);
+        const uint32_t key = key_at(e);
         const bool is_gt = key > T;
         const bool is_eq = key == T && key != 0u;
         const uint64_t gt = __ballot(is_gt);
@@ -241,8 +387,9 @@ __global__ __launch_bounds__(kThreads) void topk_streaming_kernel(TopkParams p) 
             gt_slot += s_cnt[0][w];
             eq_slot += s_cnt[1][w];
         }
-        const int gt_before = gt_run + gt_wave + lanes_below(gt);
-        const int eq_before = eq_run + eq_wave + lanes_below(eq);
+        const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        const int gt_before = gt_run + gt_wave + __popcll(gt & below);
+        const int eq_before = eq_run + eq_wave + __popcll(eq & below);
         const int col = e * kThreads + tid;
         if (is_gt) out[gt_before + min(eq_before, need)] = col;
         else if (is_eq && eq_before < need) out[gt_before + eq_before] = col;
@@ -254,22 +401,30 @@ __global__ __launch_bounds__(kThreads) void topk_streaming_kernel(TopkParams p) 
     for (int i = picked + tid; i < p.k; i += kThreads) out[i] = -1;
 }
 
+template <int E>
+void launch_resident(const TopkParams &p, hipStream_t stream, dim3 grid, dim3 block) {
+    hipLaunchKernelGGL(topk_resident_kernel<E>, grid, block, 0, stream, p);
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)p.num_rows);
     const dim3 block(kThreads);
-    const int slots = (p.num_cols + kThreads - 1) / kThreads;
-    if (slots <= 4)
-        hipLaunchKernelGGL(topk_resident_kernel<4>, grid, block, 0, stream, p);
-    else if (slots <= 8)
-        hipLaunchKernelGGL(topk_resident_kernel<8>, grid, block, 0, stream, p);
-    else if (slots <= 16)
-        hipLaunchKernelGGL(topk_resident_kernel<16>, grid, block, 0, stream, p);
-    else if (slots <= 32)
-        hipLaunchKernelGGL(topk_resident_kernel<32>, grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL(topk_streaming_kernel, grid, block, 0, stream, p);
+    // Columns per thread, rounded up to a multiple of 4 (16-byte loads).
+    const int per = ((p.num_cols + kThreads - 1) / kThreads + 3) / 4 * 4;
+    switch (per) {
+        case 0:
+        case 4: launch_resident<4>(p, stream, grid, block); break;
+        case 8: launch_resident<8>(p, stream, grid, block); break;
+        case 12: launch_resident<12>(p, stream, grid, block); break;
+        case 16: launch_resident<16>(p, stream, grid, block); break;
+        case 20: launch_resident<20>(p, stream, grid, block); break;
+        case 24: launch_resident<24>(p, stream, grid, block); break;
+        case 28: launch_resident<28>(p, stream, grid, block); break;
+        case 32: launch_resident<32>(p, stream, grid, block); break;
+        default: hipLaunchKernelGGL(topk_streaming_kernel, grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 
