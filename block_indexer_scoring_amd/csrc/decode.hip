@@ -249,13 +249,10 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
 
 template <int MT>
 hipError_t launch_mt(const DecodeParams &p, hipStream_t stream, dim3 grid, dim3 block) {
-    if (p.page_size == kSpan)
-        hipLaunchKernelGGL((decode_kernel<MT, kPage64>), grid, block, 0, stream, p);
-    else if (p.page_size % kSpan == 0)
-        hipLaunchKernelGGL((decode_kernel<MT, kPageMultiple64>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((decode_kernel<MT, kPageGeneric>), grid, block, 0, stream, p);
-    return hipGetLastError();
+    if (p.page_size == kSpan) return launch_kernel(decode_kernel<MT, kPage64>, grid, block, stream, p);
+    if (p.page_size % kSpan == 0)
+        return launch_kernel(decode_kernel<MT, kPageMultiple64>, grid, block, stream, p);
+    return launch_kernel(decode_kernel<MT, kPageGeneric>, grid, block, stream, p);
 }
 
 }  // namespace

@@ -64,8 +64,7 @@ __global__ __launch_bounds__(kThreads) void metadata_kernel(MetaParams p) {
 hipError_t launch_metadata(const MetaParams &p, hipStream_t stream) {
     const int64_t n = p.num_tokens > p.num_reqs ? p.num_tokens : p.num_reqs;
     const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
-    hipLaunchKernelGGL(metadata_kernel, grid, dim3(kThreads), 0, stream, p);
-    return hipGetLastError();
+    return launch_kernel(metadata_kernel, grid, dim3(kThreads), stream, p);
 }
 
 }  // namespace qsa

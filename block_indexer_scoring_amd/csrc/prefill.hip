@@ -318,8 +318,7 @@ int prefill_col_chunk(int64_t num_rows, int32_t out_cols) {
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
-    hipLaunchKernelGGL(prefill_kernel, grid, dim3(kThreads), 0, stream, p);
-    return hipGetLastError();
+    return launch_kernel(prefill_kernel, grid, dim3(kThreads), stream, p);
 }
 
 int prefill_rows_per_block() { return kBM; }

@@ -11,6 +11,7 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local qsa::LaunchEvents g_launch_events{nullptr, nullptr};
 
 int fail(int code, const char *fmt, ...) {
     char buf[512];
@@ -59,6 +60,11 @@ extern "C" {
 int qsa_abi_version(void) { return QSA_ABI_VERSION; }
 
 const char *qsa_last_error(void) { return g_last_error.c_str(); }
+
+int qsa_set_launch_events(void *start_event, void *stop_event) {
+    g_launch_events = {static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+    return QSA_OK;
+}
 
 int qsa_split_batch(const int32_t *query_start_loc, int32_t num_reqs, int32_t decode_threshold,
                     int32_t *order, int32_t *counts) {
@@ -244,3 +250,7 @@ int qsa_topk_blocks(const float *logits, int64_t logits_stride, int32_t num_rows
 }
 
 }  // extern "C"
+
+namespace qsa {
+LaunchEvents launch_events() { return g_launch_events; }
+}  // namespace qsa

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <hip/hip_ext.h>
+
 namespace qsa {
 
 struct DecodeParams {
@@ -60,6 +62,22 @@ struct MetaParams {
     int64_t *positions;
     int32_t *visible, *comp_lens, *row_k_start, *row_k_end;
 };
+
+// Timing events attached to every launch from the calling thread (both null
+// unless the caller armed them through the C ABI).
+struct LaunchEvents {
+    hipEvent_t start, stop;
+};
+LaunchEvents launch_events();
+
+// Launches kernel(p) on stream with the calling thread's timing events.
+template <typename P>
+hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t stream, P p) {
+    const LaunchEvents ev = launch_events();
+    void *args[] = {&p};
+    return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, args, 0, stream,
+                              ev.start, ev.stop, 0);
+}
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 int decode_span_keys();

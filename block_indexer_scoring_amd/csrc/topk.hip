@@ -402,8 +402,8 @@ __global__ __launch_bounds__(kThreads) void topk_streaming_kernel(TopkParams p) 
 }
 
 template <int E>
-void launch_resident(const TopkParams &p, hipStream_t stream, dim3 grid, dim3 block) {
-    hipLaunchKernelGGL(topk_resident_kernel<E>, grid, block, 0, stream, p);
+hipError_t launch_resident(const TopkParams &p, hipStream_t stream, dim3 grid, dim3 block) {
+    return launch_kernel(topk_resident_kernel<E>, grid, block, stream, p);
 }
 
 }  // namespace
@@ -415,17 +415,16 @@ hipError_t launch_topk(const TopkParams &p, hipStream_t stream) {
     const int per = ((p.num_cols + kThreads - 1) / kThreads + 3) / 4 * 4;
     switch (per) {
         case 0:
-        case 4: launch_resident<4>(p, stream, grid, block); break;
-        case 8: launch_resident<8>(p, stream, grid, block); break;
-        case 12: launch_resident<12>(p, stream, grid, block); break;
-        case 16: launch_resident<16>(p, stream, grid, block); break;
-        case 20: launch_resident<20>(p, stream, grid, block); break;
-        case 24: launch_resident<24>(p, stream, grid, block); break;
-        case 28: launch_resident<28>(p, stream, grid, block); break;
-        case 32: launch_resident<32>(p, stream, grid, block); break;
-        default: hipLaunchKernelGGL(topk_streaming_kernel, grid, block, 0, stream, p);
+        case 4: return launch_resident<4>(p, stream, grid, block);
+        case 8: return launch_resident<8>(p, stream, grid, block);
+        case 12: return launch_resident<12>(p, stream, grid, block);
+        case 16: return launch_resident<16>(p, stream, grid, block);
+        case 20: return launch_resident<20>(p, stream, grid, block);
+        case 24: return launch_resident<24>(p, stream, grid, block);
+        case 28: return launch_resident<28>(p, stream, grid, block);
+        case 32: return launch_resident<32>(p, stream, grid, block);
+        default: return launch_kernel(topk_streaming_kernel, grid, block, stream, p);
     }
-    return hipGetLastError();
 }
 
 }  // namespace qsa

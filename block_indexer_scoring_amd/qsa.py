@@ -23,8 +23,8 @@ QSA_ERR_LAYOUT = 3
 QSA_ERR_DEVICE = 4
 ABI_VERSION = 1
 
-SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_split_batch", "qsa_build_metadata",
-           "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks")
+SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_set_launch_events", "qsa_split_batch",
+           "qsa_build_metadata", "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks")
 
 DEFAULT_SCALE = 1.0 / math.sqrt(128.0)
 
@@ -52,6 +52,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_abi_version.restype = ctypes.c_int
     lib.qsa_last_error.argtypes = []
     lib.qsa_last_error.restype = ctypes.c_char_p
+    lib.qsa_set_launch_events.argtypes = [P, P]
+    lib.qsa_set_launch_events.restype = ctypes.c_int
     lib.qsa_split_batch.argtypes = [P, i32, i32, P, P]
     lib.qsa_split_batch.restype = ctypes.c_int
     lib.qsa_build_metadata.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P, P, P]
@@ -95,6 +97,12 @@ def _ptr(t: torch.Tensor | None):
 
 
 # ----------------------------------------------------------------------------
+
+
+def qsa_set_launch_events(start_event: int | None, stop_event: int | None) -> None:
+    """Attach caller-owned hipEvent_t handles (as integers) to every kernel the
+    library launches from this thread; None, None stops it."""
+    _check(load_library().qsa_set_launch_events(start_event, stop_event))
 
 
 def qsa_split_batch(query_start_loc, decode_threshold: int, reorder: bool = False):

@@ -54,6 +54,22 @@ int qsa_abi_version(void);
 /* Text of the last error returned on this thread ("" if none). */
 const char *qsa_last_error(void);
 
+/* qsa_set_launch_events -- per-kernel timing hook (instrumentation; not an
+ * operation of the indexer).
+ *   While set, every kernel that this library launches from the calling
+ *   thread is launched with hipExtLaunchKernel and these events: the runtime
+ *   marks start_event when the kernel begins executing and stop_event when
+ *   it ends, so hipEventElapsedTime(start, stop) is the kernel's own
+ *   duration, without the dispatch latency that an event pair recorded on
+ *   the stream around the call adds.  Each entry point below launches one
+ *   kernel (none when it has nothing to compute).
+ *   start_event, stop_event : hipEvent_t handles created by the caller (may
+ *                             be NULL); owned by the caller, who must keep
+ *                             them alive until the launches complete.
+ *   Pass NULL, NULL to stop timing.  The setting is per calling thread.
+ *   Returns QSA_OK. */
+int qsa_set_launch_events(void *start_event, void *stop_event);
+
 /* ------------------------------------------------------------------------
  * Per-step metadata (host and device helpers).
  *

@@ -84,7 +84,9 @@ def _ptr(a: np.ndarray | None):
 
 def _threads(threads: int | None) -> int:
     if threads is None:
-        threads = int(os.environ.get("QSA_ORACLE_THREADS", "0")) or (os.cpu_count() or 1)
+        threads = (int(os.environ.get("QSA_ORACLE_THREADS", "0"))
+                   or int(os.environ.get("OMP_NUM_THREADS", "0"))
+                   or len(os.sched_getaffinity(0)))
     return max(1, int(threads))
 
 

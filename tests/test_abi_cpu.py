@@ -47,6 +47,10 @@ def test_abi_version(lib):
     assert lib.qsa_abi_version() == 1
 
 
+def test_launch_events_set_and_clear_without_device(lib):
+    assert lib.qsa_set_launch_events(None, None) == 0
+
+
 def _err(lib):
     return lib.qsa_last_error().decode()
 

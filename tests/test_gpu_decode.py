@@ -169,3 +169,26 @@ def test_decode_empty_calls():
     out = qsa.qsa_mqa_decode(q, kd, empty_table, comp, None, out_cols=25)
     torch.cuda.synchronize()
     assert np.all(f32_bits(out) == 0xFF800000)
+
+
+def test_launch_events_time_the_kernel():
+    """qsa_set_launch_events: the attached events bracket the decode kernel
+    and the scores are unchanged; clearing them leaves the events alone."""
+    import bench
+    qsa = _qsa()
+    inp = WORKLOADS["tiny_decode"].make()
+    _, _, vis = O.token_metadata(inp.query_start_loc, inp.seq_lens, inp.num_reqs * inp.dql)
+    ev = bench.HipEvents(2)
+    try:
+        qsa.qsa_set_launch_events(ev.ev[0], ev.ev[1])
+        try:
+            out = _run_gpu(inp, vis)
+        finally:
+            qsa.qsa_set_launch_events(None, None)
+        first = ev.elapsed_us(0, 1)
+        assert 0.0 < first < 1e6
+        assert_scores_match(out.cpu().numpy(), _oracle(inp, vis))
+        _run_gpu(inp, vis)
+        assert ev.elapsed_us(0, 1) == first
+    finally:
+        ev.close()
