@@ -17,9 +17,12 @@ Cache), so every decode launch streams its keys from HBM.
 
 Headline `value`: decode throughput in GB/s with the pages' accounting
 (unique bf16 keys + bf16 queries + fp32 logits of visible blocks), from the
-decode kernel's average duration measured with HIP events on its stream.
-Prefill is reported in TFLOP/s (2*4*128 FLOPs per visible block per row) and
-top-k in GB/s (logits read + indices written).
+decode kernel's average duration.  Each kernel is timed by HIP events that
+the library attaches to its launch (qsa_set_launch_events), which mark the
+kernel's own begin and end on the stream it runs on.  Prefill is reported in
+TFLOP/s (2*4*128 FLOPs per visible block per row, the pages' figure) and
+against HBM (the score matrix it writes), which is the tighter bound at this
+shape; top-k in GB/s (logits read + indices written).
 
 Work accounting follows vLLM PR 54513 ("Separate prefill and decode paths for
 QSA indexer", section "Microbenchmarks"); tests/test_bench_accounting.py pins
@@ -64,6 +67,11 @@ def prefill_flops(visible_total: int) -> float:
     return 2.0 * HEADS * HEAD_DIM * visible_total
 
 
+def prefill_bytes(rows: int, cols: int, num_keys: int) -> float:
+    """fp32 score matrix written + bf16 queries + bf16 keys read once."""
+    return rows * cols * 4.0 + rows * HEADS * HEAD_DIM * 2.0 + num_keys * HEAD_DIM * 2.0
+
+
 def topk_bytes(rows: int, cols: int, k: int) -> float:
     """fp32 logits read + int32 indices written."""
     return rows * cols * 4.0 + rows * k * 4.0
@@ -72,9 +80,15 @@ def topk_bytes(rows: int, cols: int, k: int) -> float:
 # ----------------------------------------------------------------------------
 
 
-def source_digest(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(kernel_file: str) -> str:
+    """First 16 hex digits of the SHA-256 of a kernel's source file followed
+    by the device and launch headers it includes."""
+    csrc = os.path.join(ROOT, "block_indexer_scoring_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (kernel_file, "qsa_device.h", "qsa_internal.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel_file: str, kernel: str):
@@ -89,8 +103,7 @@ def read_traffic(kernel_file: str, kernel: str):
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 vals[key.strip()] = val.strip()
-    src = os.path.join(ROOT, "block_indexer_scoring_amd", "csrc", kernel_file)
-    if vals.get("source_sha256_16") != source_digest(src):
+    if vals.get("source_sha256_16") != source_digest(kernel_file):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -312,6 +325,8 @@ def main(argv=None) -> int:
     vis_pre_total = int(vis_host[T_dec:].astype(np.int64).sum())
     pflops = prefill_flops(vis_pre_total)
     prefill_tflops = pflops / (avg["prefill"] * 1e-6) / 1e12
+    pbytes = prefill_bytes(T_pre, pre.out_cols, int(pre.k.shape[0]))
+    prefill_gbps = pbytes / (avg["prefill"] * 1e-6) / 1e9
     tk_bytes = topk_bytes(T_pre, pre.out_cols, TOPK)
     topk_gbps = tk_bytes / (avg["topk_prefill"] * 1e-6) / 1e9
 
@@ -342,14 +357,16 @@ def main(argv=None) -> int:
         },
         "roofline": roof("hbm", decode_gbps, HBM_PEAK_GBPS, "GB/s",
                          read_traffic("decode.hip", "decode")),
-        "roofline_prefill": roof("mfma", prefill_tflops, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
+        "roofline_prefill": roof("hbm", prefill_gbps, HBM_PEAK_GBPS, "GB/s",
                                  read_traffic("prefill.hip", "prefill")),
+        "prefill_mfma": roof("mfma", prefill_tflops, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", None),
         "roofline_topk": roof("hbm", topk_gbps, HBM_PEAK_GBPS, "GB/s",
                               read_traffic("topk.hip", "topk")),
         "kernel_us_avg": {n: round(v, 3) for n, v in avg.items()},
         "kernel_us_median": {n: round(v, 3) for n, v in med.items()},
         "prefill_tflops": round(prefill_tflops, 2),
-        "decode_bytes": dbytes, "prefill_flops": pflops, "topk_prefill_bytes": tk_bytes,
+        "decode_bytes": dbytes, "prefill_bytes": pbytes, "prefill_flops": pflops,
+        "topk_prefill_bytes": tk_bytes,
     }
 
     if args.copy_calibration_mib > 0:
