@@ -184,6 +184,7 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--pools", type=int, default=8, help="decode key pools rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lib", default=None, help="load this libqsa.so instead of the in-tree build")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
     args = ap.parse_args(argv)
@@ -198,7 +199,7 @@ def main(argv=None) -> int:
     import block_indexer_scoring_amd as qsa
     from workloads import WORKLOADS, decode_inputs
 
-    qsa.load_library()
+    lib = qsa.load_library(args.lib) if args.lib else qsa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -249,7 +250,6 @@ def main(argv=None) -> int:
     TOPK = 512
     dec_top = torch.empty((T_dec, TOPK), dtype=torch.int32, device=dev)
     pre_top = torch.empty((T_pre, TOPK), dtype=torch.int32, device=dev)
-    lib = qsa.load_library()
     stream = torch.cuda.Stream(device=dev)
     sh = stream.cuda_stream
 

@@ -97,13 +97,9 @@ __device__ Task map_task(const DecodeParams &p, int task, int lane) {
                 const int idx = __popcll(below);  // first lane whose range holds `local`
                 const int excl = __builtin_amdgcn_readlane(incl - cnt, idx);
                 if (pass == 0) return Task{r0 + idx, local - excl, true, true};
-                int keyed_r = 0;
-                if (lane == idx) {
-                    const int comp = p.comp_lens[r0 + idx];
-                    keyed_r = comp > 0 ? (comp + kSpan - 1) / kSpan : 0;
-                    keyed_r = keyed_r < p.spans ? keyed_r : p.spans;
-                }
-                keyed_r = __builtin_amdgcn_readlane(keyed_r, idx);
+                const int comp = load_uniform(p.comp_lens + r0 + idx);
+                int keyed_r = comp > 0 ? (comp + kSpan - 1) / kSpan : 0;
+                keyed_r = keyed_r < p.spans ? keyed_r : p.spans;
                 return Task{r0 + idx, keyed_r + (local - excl) * kPadSpans, false, true};
             }
             before += chunk_total;
@@ -131,16 +127,23 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
 
     float res[MT][4];
     if (task.compute) {
-        const int comp = p.comp_lens[r];
+        // Request-level reads are scalar loads, so the page-table read that
+        // gates the key loads never waits behind the query loads.
+        const int comp = load_uniform(p.comp_lens + r);
         const int64_t pt_row = (int64_t)r * p.page_table_stride;
-        // Per-row visible counts (lane row j = 4*mt + q4).
+        // Per-row visible counts (lane row j = 4*mt + q4), read as scalars.
         int vis_row[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int j = 4 * mt + q4;
-            int v = 0;
-            if (j < p.dql) v = p.visible ? p.visible[(int64_t)r * p.dql + j] : comp;
-            vis_row[mt] = v < 0 ? 0 : (v > comp ? comp : v);
+            int v4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * mt + i;
+                int v = 0;
+                if (j < p.dql) v = p.visible ? load_uniform(p.visible + (int64_t)r * p.dql + j) : comp;
+                v4[i] = v < 0 ? 0 : (v > comp ? comp : v);
+            }
+            vis_row[mt] = q4 == 0 ? v4[0] : (q4 == 1 ? v4[1] : (q4 == 2 ? v4[2] : v4[3]));
         }
 
         // Query fragments (issued first: they hit in L2): tile mt holds rows
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
             // The span lies on one page; a mapped page is read whole (keys
             // past comp are in bounds and masked below).
             const int slot = PAGE_MODE == kPage64 ? span : c0 / p.page_size;
-            const int page = slot < p.page_table_cols ? p.page_table[pt_row + slot] : -1;
+            const int page = slot < p.page_table_cols ? load_uniform(p.page_table + pt_row + slot) : -1;
             const bool page_ok = page >= 0 && page < p.num_pages;
             if (page_ok) {
                 const int in_page = PAGE_MODE == kPage64 ? 0 : c0 % p.page_size;

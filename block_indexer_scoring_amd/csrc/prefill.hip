@@ -12,8 +12,9 @@
 //     output columns.  Each wavefront keeps its 16 rows x 4 heads of Q in
 //     registers as MFMA A fragments for the whole chunk (m = 4*row + head).
 //   - Key tiles of 64 keys (16 KB) are staged in LDS with direct
-//     global-to-LDS loads, double-buffered: the loads of tile i+1 are in
-//     flight while tile i is multiplied, and every wave of the workgroup
+//     global-to-LDS loads, two tiles per buffer and two buffers: the loads
+//     of the next pair are in flight while the current pair is multiplied
+//     (one workgroup barrier per 128 keys), and every wave of the workgroup
 //     reuses each staged tile.  LDS rows are XOR-swizzled in 16-byte units
 //     so the B-fragment reads are free of bank conflicts.
 //   - Registers are held to two wavefronts per SIMD, so one wave's epilogue
@@ -37,6 +38,9 @@
 #ifndef QSA_PREFILL_WAVES
 #define QSA_PREFILL_WAVES 4
 #endif
+#ifndef QSA_PREFILL_TILES_PER_STAGE
+#define QSA_PREFILL_TILES_PER_STAGE 2
+#endif
 
 namespace qsa {
 namespace {
@@ -48,6 +52,7 @@ constexpr int kBM = kWaves * kRowsPerWave;  // query rows per workgroup
 constexpr int kBN = 64;                     // keys per LDS tile
 constexpr int kTileElems = kBN * kDim;      // bf16 elements per tile
 constexpr int kBlocksPerWave = kBN / 4 / kWaves;  // 1 KB LDS blocks staged per wave per tile
+constexpr int kTilesPerStage = QSA_PREFILL_TILES_PER_STAGE;  // key tiles per LDS buffer
 
 // LDS element offset of 16-byte chunk `chunk` (0..15) of tile key `key`.
 __device__ __forceinline__ int lds_offset(int key, int chunk) {
@@ -81,8 +86,8 @@ void prefill_kernel(PrefillParams p) {
     // Two separate LDS objects (not one [2][...] array), so the compiler can
     // tell the buffer being read from the one being filled and does not wait
     // for the prefetch before reading the current tile.
-    __shared__ __attribute__((aligned(16))) uint16_t ktile0[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t ktile1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t ktile0[kTilesPerStage * kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t ktile1[kTilesPerStage * kTileElems];
     __shared__ int s_start[kBM];
     __shared__ int s_end[kBM];  // min(row_k_end, num_keys)
     __shared__ int s_done[kBM];
@@ -236,14 +241,7 @@ void prefill_kernel(PrefillParams p) {
             pend_c = -1;
         };
 
-        auto compute_tile = [&](int it, const uint16_t *tile, uint16_t *next) {
-            const int tile_c = c_begin + it * kBN;
-            // Tile it is in LDS once every wave's loads for it have landed.
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            flush();
-            if (it + 1 < n_compute) stage(tile_c + kBN, next);
-
+        auto compute_tile = [&](int tile_c, const uint16_t *tile) {
             f32x4 acc[4][4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -279,10 +277,32 @@ void prefill_kernel(PrefillParams p) {
             pend_c = tile_c;
         };
 
-        if (n_compute > 0) stage(c_begin, ktile0);
-        for (int it = 0; it < n_compute; it += 2) {
-            compute_tile(it, ktile0, ktile1);
-            if (it + 1 < n_compute) compute_tile(it + 1, ktile1, ktile0);
+        // One LDS buffer holds kTilesPerStage consecutive tiles; the next
+        // buffer's loads are in flight while this one is multiplied.
+        auto stage_tiles = [&](int it, uint16_t *buf) {
+#pragma unroll
+            for (int h = 0; h < kTilesPerStage; ++h)
+                if (it + h < n_compute) stage(c_begin + (it + h) * kBN, buf + h * kTileElems);
+        };
+        auto run_stage = [&](int it, const uint16_t *cur_buf, uint16_t *next_buf) {
+            // The buffer is in LDS once every wave's loads for it have landed.
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            flush();
+            if (it + kTilesPerStage < n_compute) stage_tiles(it + kTilesPerStage, next_buf);
+#pragma unroll
+            for (int h = 0; h < kTilesPerStage; ++h) {
+                if (it + h < n_compute) {
+                    if (h > 0) flush();
+                    compute_tile(c_begin + (it + h) * kBN, cur_buf + h * kTileElems);
+                }
+            }
+        };
+
+        if (n_compute > 0) stage_tiles(0, ktile0);
+        for (int it = 0; it < n_compute; it += 2 * kTilesPerStage) {
+            run_stage(it, ktile0, ktile1);
+            if (it + kTilesPerStage < n_compute) run_stage(it + kTilesPerStage, ktile1, ktile0);
         }
         flush();
 

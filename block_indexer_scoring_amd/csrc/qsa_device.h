@@ -20,6 +20,17 @@ __device__ __forceinline__ u32x4 load_u32x4(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Load through the constant address space.  At a wave-uniform address this
+// becomes a scalar load, which the vector-memory counter does not track, so
+// waiting for it does not also wait for the wave's outstanding vector loads.
+// Only for memory that no kernel writes while the reading kernel runs (the
+// scalar cache is invalidated at each kernel launch).
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T *ptr) {
+    typedef const __attribute__((address_space(4))) T *constant_ptr;
+    return *(constant_ptr)(ptr);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ u32x4 zero_u32x4() { return u32x4{0u, 0u, 0u, 0u}; }
