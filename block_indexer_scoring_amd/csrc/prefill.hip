@@ -81,6 +81,9 @@ __device__ __forceinline__ void store4(float *dst, bool vec, int col, int c_end,
     }
 }
 
+// Fourth word of a raw buffer resource (32-bit data format) on gfx9-class GPUs.
+constexpr int kBufferWord3 = 0x00020000;
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillParams p) {
     // Two separate LDS objects (not one [2][...] array), so the compiler can
@@ -225,10 +228,32 @@ void prefill_kernel(PrefillParams p) {
         // had a whole tile of MFMA time to drain.
         f32x4 pend[4];
         int pend_c = -1;  // tile column of the pending scores, -1 if none
+        // The workgroup's output rows as one raw buffer.  A full tile's
+        // scores go out as exactly four buffer stores per wave: lanes whose
+        // row is not in this pass store to an offset past the buffer's end,
+        // which the hardware drops.  With that fixed count, the wait before
+        // a buffer of keys can leave the most recent tile's stores in flight.
+        const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            p.out + (int64_t)row0 * p.out_stride, 0,
+            p.exact_stores ? (int)((int64_t)min(kBM, p.num_rows - row0) * p.out_stride * 4) : 0, kBufferWord3);
+        uint32_t row_boff[4];  // byte offset of (row, column 4n) in out_rsrc
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int idx = wave * kRowsPerWave + 4 * mt + q4;
+            row_boff[mt] = in_pass[mt] ? (uint32_t)(((int64_t)idx * p.out_stride + 4 * n) * 4) : 0x80000000u;
+        }
         auto flush = [&]() {
             if (pend_c < 0) return;
             const int col = pend_c + 4 * n;
             const bool full = p.out_vec && pend_c + kBN <= c_end;
+            if (full && p.exact_stores) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    __builtin_amdgcn_raw_buffer_store_b128(pend[mt], out_rsrc, row_boff[mt] + 4u * (uint32_t)pend_c,
+                                                           0, 0);
+                pend_c = -1;
+                return;
+            }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 if (!in_pass[mt]) continue;
@@ -286,7 +311,12 @@ void prefill_kernel(PrefillParams p) {
         };
         auto run_stage = [&](int it, const uint16_t *cur_buf, uint16_t *next_buf) {
             // The buffer is in LDS once every wave's loads for it have landed.
-            __builtin_amdgcn_s_waitcnt(0);
+            // Vector-memory ops complete in issue order; from the third
+            // stage on, the only ops issued after this buffer's loads are
+            // the four stores of the previous stage's first tile, which may
+            // stay in flight (s_waitcnt vmcnt(4) lgkmcnt(0)).
+            if (p.exact_stores && it >= 2 * kTilesPerStage) __builtin_amdgcn_s_waitcnt(0x0074);
+            else __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             flush();
             if (it + kTilesPerStage < n_compute) stage_tiles(it + kTilesPerStage, next_buf);
@@ -324,11 +354,13 @@ void prefill_kernel(PrefillParams p) {
 
 }  // namespace
 
-int prefill_col_chunk(int64_t num_rows, int32_t out_cols) {
-    // Enough workgroups to fill 256 CUs several times over, in whole tiles.
+int prefill_col_chunk(int64_t num_rows, int32_t out_cols, int num_cus) {
+    // One round of workgroups (two per CU), each walking a long run of
+    // columns: the per-workgroup setup is paid once, and each workgroup's
+    // stores cover long stretches of its rows.
     const int64_t row_blocks = (num_rows + kBM - 1) / kBM;
     const int64_t tiles = ((int64_t)out_cols + kBN - 1) / kBN;
-    const int64_t target_groups = 2048;
+    const int64_t target_groups = 2 * (int64_t)(num_cus > 0 ? num_cus : 256);
     int64_t per_chunk = (tiles * row_blocks + target_groups - 1) / target_groups;
     if (per_chunk < 8) per_chunk = 8;
     if (per_chunk > tiles) per_chunk = tiles;

@@ -1,5 +1,6 @@
 // C ABI of the QSA MQA indexer: argument checks (host arguments only, never
 // device contents), error text, and dispatch to the gfx950 kernels.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -32,6 +33,19 @@ int device_status(const char *what, hipError_t err) {
     if (err != hipSuccess)
         return fail(QSA_ERR_DEVICE, "%s: kernel launch failed: %s", what, hipGetErrorString(err));
     return ok();
+}
+
+// Compute units of the current device (cached per device; 0 if unknown).
+int current_cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
 }
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -205,7 +219,7 @@ int qsa_mqa_prefill(const void *q, int64_t q_stride_row, int64_t q_stride_head, 
     if (!aligned(out, 4)) return fail(QSA_ERR_LAYOUT, "%s: out must be 4-byte aligned", fn);
 
     const int bm = qsa::prefill_rows_per_block();
-    const int chunk = qsa::prefill_col_chunk(num_rows, out_cols);
+    const int chunk = qsa::prefill_col_chunk(num_rows, out_cols, current_cu_count());
     const int64_t row_blocks = ((int64_t)num_rows + bm - 1) / bm;
     const int64_t col_chunks = ((int64_t)out_cols + chunk - 1) / chunk;
     if (row_blocks * col_chunks >= INT32_MAX)
@@ -229,6 +243,7 @@ int qsa_mqa_prefill(const void *q, int64_t q_stride_row, int64_t q_stride_head, 
     p.row_blocks = (int32_t)row_blocks;
     p.col_chunks = (int32_t)col_chunks;
     p.out_vec = aligned(out, 16) && out_stride % 4 == 0;
+    p.exact_stores = p.out_vec && (int64_t)bm * out_stride * 4 < ((int64_t)1 << 31);
     return device_status(fn, qsa::launch_prefill(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -44,6 +44,7 @@ struct PrefillParams {
     int32_t col_chunk;          // output columns per workgroup (multiple of 64)
     int32_t row_blocks, col_chunks;
     int32_t out_vec;
+    int32_t exact_stores;       // out_vec, and a row block's output spans < 2^31 bytes
 };
 
 struct TopkParams {
@@ -81,7 +82,7 @@ hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t s
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 int decode_span_keys();
-int prefill_col_chunk(int64_t num_rows, int32_t out_cols);
+int prefill_col_chunk(int64_t num_rows, int32_t out_cols, int num_cus);
 int prefill_rows_per_block();
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams &p, hipStream_t stream);
