@@ -6,31 +6,37 @@
 // values going to the lower column, and write the picks in ascending column
 // order followed by -1.
 //
-// One 1024-thread workgroup per row, two rows per CU.  Each float maps to an
+// One 512-thread workgroup per row, four rows per CU.  Each float maps to an
 // order-preserving 32-bit key (+0 and -0 share one key; non-candidates get
 // key 0, below every candidate).  An exact radix select over the key bits
-// (11 + 11 + 10, LDS histograms) finds the k-th largest key T and how many of
-// the keys equal to T are needed; a cell is picked if key > T, or key == T
-// and fewer than `need` equal keys precede it.
+// finds the k-th largest key T and how many of the keys equal to T are
+// needed; a cell is picked if key > T, or key == T and fewer than `need`
+// equal keys precede it.
 //
 // Rows up to 32768 columns stay in registers, each thread owning a
-// contiguous run of columns, so thread order is column order and the picks
-// are placed with a single prefix sum.  Before the select, a floor F is
-// taken from the per-thread maxima: each thread's largest key witnesses one
-// key >= itself, so when the k largest maxima are >= F at least k keys are,
-// and T >= F.  The keys >= F (a few hundred for score rows) are compacted in
-// column order into an LDS list and the select and the output run over that
-// list only.  If the list would overflow, the same select runs over the
-// registers.  Longer rows are re-read from memory in each phase.
+// contiguous run of columns (kept as the keys' top 16 bits), so thread order
+// is column order and the picks are placed with a single prefix sum.
+// Before the select, a floor F is taken from the maxima of four sub-runs per
+// thread: each maximum is a distinct key, so when k of them are >= F at least
+// k keys are, and T >= F.  The keys >= F (a few hundred for score rows) are
+// compacted in column order into an LDS list, and one wave runs the select
+// over the list without workgroup barriers: 11 + 5 bits on the top halves,
+// then, only if some of the keys sharing T's top half are left out, those
+// keys are re-read in full and two 8-bit passes finish T.  If the list would
+// overflow, the select runs over the row itself.  Longer rows are re-read
+// from memory in each phase.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
 
-constexpr int kThreads = 1024;
+#ifndef QSA_TOPK_THREADS
+#define QSA_TOPK_THREADS 512
+#endif
+constexpr int kThreads = QSA_TOPK_THREADS;
 constexpr int kWaves = kThreads / 64;
-constexpr int kListCap = 4096;  // keys >= floor kept in LDS
+constexpr int kListCap = kThreads * 4;  // keys >= floor kept in LDS
 
 __device__ __forceinline__ uint32_t order_key(float v) {
     if (!(v > neg_inf())) return 0u;  // -inf and NaN are never picked
@@ -80,36 +86,46 @@ struct SelectShared {
     int pick_bin, pick_above;
 };
 
-// Finds the bin of hist[0..nb) holding the kk-th largest counted key (bins
-// ordered by key, the top bin holding the largest keys).  Thread tid owns
-// nb/1024 bins counted down from the top; a prefix sum of the thread sums
-// locates the one thread whose bins hold it, and that thread walks them.
+// One wave finds the bin of hist[0..nb) (nb a power of two, at most 4096)
+// holding the kk-th largest counted key: lane l sums the max(nb/64, 1) bins
+// counted down from the top, a wave scan of the sums picks the lane whose
+// bins hold it, then a second wave scan over that lane's bins picks the bin.
 // Returns the bin (-1 if fewer than kk keys were counted) and sets
-// *above_out to the count in higher bins.  Call after the histogram is
-// complete (a barrier after the last count); uniform result.
-// Kept out of line: inlined at its five call sites it pushes the kernel
-// past 64 VGPRs (the budget for two 1024-thread workgroups per CU).
-__device__ __noinline__ int find_bin(SelectShared &sh, int nb, int kk, int *above_out) {
-    const int tid = threadIdx.x;
-    const int per = nb / kThreads;
-    const int hi = nb - 1 - tid * per;
-    int s = 0;
-    for (int b = 0; b < per; ++b) s += sh.hist[hi - b];
-    int total;
-    int above = block_exclusive_scan(s, sh.wave_tmp, &total);
-    if (tid == 0 && total < kk) {
-        sh.pick_bin = -1;
-        sh.pick_above = 0;
+// *above_out to the count in higher bins.  Wave-uniform; no barriers.
+__device__ __forceinline__ int wave_find_bin(const int *hist, int nb, int kk, int *above_out) {
+    const int lane = threadIdx.x & 63;
+    const int per = nb >= 64 ? nb / 64 : 1;
+    const int hi = nb - 1 - lane * per;
+    int sum = 0;
+    if (hi >= 0)
+        for (int b = 0; b < per; ++b) sum += hist[hi - b];
+    const int incl = (int)wave_inclusive_scan((uint32_t)sum);
+    const uint64_t hit = __ballot(incl - sum < kk && kk <= incl);
+    if (hit == 0) {
+        *above_out = 0;
+        return -1;
     }
-    if (above < kk && kk <= above + s) {
-        for (int b = 0; b < per; ++b) {
-            const int c = sh.hist[hi - b];
-            if (above + c >= kk) {
-                sh.pick_bin = hi - b;
-                sh.pick_above = above;
-                break;
-            }
-            above += c;
+    const int src = __builtin_ctzll(hit);
+    const int above0 = __builtin_amdgcn_readlane(incl - sum, src);
+    const int top = nb - 1 - src * per;  // highest bin of lane src
+    const int c = lane < per ? hist[top - lane] : 0;
+    const int incl2 = (int)wave_inclusive_scan((uint32_t)c);
+    const uint64_t hit2 = __ballot(lane < per && above0 + incl2 >= kk);
+    const int f = __builtin_ctzll(hit2);
+    *above_out = above0 + __builtin_amdgcn_readlane(incl2 - c, f);
+    return top - f;
+}
+
+// The same search for the whole workgroup: call once the histogram is
+// complete (after a barrier); wave 0 searches and publishes the result.
+// Uniform result.
+__device__ __forceinline__ int find_bin(SelectShared &sh, int nb, int kk, int *above_out) {
+    if (threadIdx.x < 64) {
+        int above;
+        const int bin = wave_find_bin(sh.hist, nb, kk, &above);
+        if (threadIdx.x == 0) {
+            sh.pick_bin = bin;
+            sh.pick_above = above;
         }
     }
     __syncthreads();
@@ -254,80 +270,201 @@ __device__ __forceinline__ void place_picks(const ListView &list, const RowView 
     }
 }
 
+// The k-th largest key T of the listed keys and how many keys equal to T
+// are picked, by one wave (wave 0).  The list holds each key's top 16 bits
+// (key >> 16 << 16); hist0 counts the list by the top 11 bits.  A radix
+// select over the top 16 bits (11 + 5) finds T's top half; if only some of
+// the keys sharing it are picked, those keys (few, normally) are re-read in
+// full from the row into the list and two more 8-bit passes resolve T.
+// Keys with other top halves compare with T correctly either way.
+// Requires at least k listed keys.
+__device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *cols, int n, int k,
+                                                     const int *hist0, int *hist, const float *x,
+                                                     int *need_out) {
+    const int lane = threadIdx.x & 63;
+    int above;
+    int kk = k;
+    const int b0 = wave_find_bin(hist0, 2048, kk, &above);
+    kk -= above;
+    // One wave: its LDS operations take effect in issue order.
+    if (lane < 32) hist[lane] = 0;
+    for (int i = lane; i < n; i += 64) {
+        const uint32_t key = list[i];
+        if ((key >> 21) == (uint32_t)b0) atomicAdd(&hist[(key >> 16) & 31], 1);
+    }
+    const int b1 = wave_find_bin(hist, 32, kk, &above);
+    kk -= above;
+    const uint32_t top = ((uint32_t)b0 << 5) | (uint32_t)b1;
+    const int tied = hist[b1];  // listed keys whose top half is `top`
+    if (kk == tied) {           // all of them are picked
+        *need_out = kk;
+        return top << 16;
+    }
+    for (int i = lane; i < n; i += 64)
+        if ((list[i] >> 16) == top) list[i] = order_key(x[cols[i]]);
+    uint32_t prefix = top << 16, shift_mask = 0xffffu << 16;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = pass == 0 ? 8 : 0;
+        for (int b = lane; b < 256; b += 64) hist[b] = 0;
+        for (int i = lane; i < n; i += 64) {
+            const uint32_t key = list[i];
+            if ((key & shift_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+        }
+        const int bin = wave_find_bin(hist, 256, kk, &above);
+        kk -= above;
+        prefix |= (uint32_t)bin << shift;
+        shift_mask |= 255u << shift;
+    }
+    *need_out = kk;
+    return prefix;
+}
+
+#ifndef QSA_TOPK_WAVES_PER_EU
+#define QSA_TOPK_WAVES_PER_EU 8
+#endif
 template <int E>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QSA_TOPK_WAVES_PER_EU)))
 void topk_resident_kernel(TopkParams p) {
+    constexpr int kSub = 4;  // sub-runs per thread, one maximum each
+    constexpr int kSubLen = (E + kSub - 1) / kSub;
     __shared__ SelectShared sh;
+    __shared__ int hist_list[2048];  // listed keys by their top 11 bits
     __shared__ uint32_t list_key[kListCap];
     __shared__ int list_col[kListCap];
+    __shared__ uint32_t s_floor, s_T;
+    __shared__ int s_need;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int64_t row = blockIdx.x;
     const float *x = p.logits + row * p.logits_stride;
     int32_t *out = p.out + row * p.out_stride;
     const int col0 = tid * E;  // this thread's columns: col0 .. col0 + E - 1
 
+    for (int b = tid; b < 2048; b += kThreads) {
+        sh.hist[b] = 0;
+        hist_list[b] = 0;
+    }
+
     // Keys stay in registers as their top 16 bits, two per register: enough
-    // to test key >= floor exactly (the floor is a multiple of 2^21); the
-    // few keys that pass are re-read in full when the list is built.
+    // to test key >= floor exactly (the floor is a multiple of 2^21).  The
+    // maximum of each sub-run of the thread's keys is kept in full; the
+    // sub-run maxima are distinct keys, each witnessing one key >= itself.
     uint32_t top16[(E + 1) / 2];
+    uint32_t smax[kSub] = {};
     int cand = 0;
-    uint32_t tmax = 0u;
     auto absorb = [&](int e, uint32_t k) {
         cand += k != 0u;
-        tmax = max(tmax, k);
+        smax[e / kSubLen] = max(smax[e / kSubLen], k);
         if (e % 2 == 0) top16[e / 2] = k >> 16;
         else top16[e / 2] |= k & 0xffff0000u;
     };
     if (p.vec && col0 + E <= p.num_cols) {
-        // The whole run is inside the row: 16-byte loads.
-        f32x4 v[E / 4];
+        // The whole run is inside the row: 16-byte loads, issued in chunks
+        // of kChunk loads one chunk ahead of their use, so only two chunks
+        // of raw values occupy registers at a time.
+        constexpr int kVecs = E / 4;
+        constexpr int kChunk = 4;
+        f32x4 v[kVecs];
 #pragma unroll
-        for (int e = 0; e < E / 4; ++e) v[e] = *reinterpret_cast<const f32x4 *>(x + col0 + 4 * e);
+        for (int c = 0; c < kVecs; c += kChunk) {
+            if (c == 0) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) absorb(e, order_key(v[e / 4][e % 4]));
+                for (int i = 0; i < kChunk && i < kVecs; ++i)
+                    v[i] = *reinterpret_cast<const f32x4 *>(x + col0 + 4 * i);
+            }
+#pragma unroll
+            for (int i = c + kChunk; i < c + 2 * kChunk && i < kVecs; ++i)
+                v[i] = *reinterpret_cast<const f32x4 *>(x + col0 + 4 * i);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = c; i < c + kChunk && i < kVecs; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) absorb(4 * i + j, order_key(v[i][j]));
+            __builtin_amdgcn_sched_barrier(0);
+        }
     } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) absorb(e, col0 + e < p.num_cols ? order_key(x[col0 + e]) : 0u);
     }
     auto key_top = [&](int e) { return e % 2 == 0 ? (top16[e / 2] & 0xffffu) : (top16[e / 2] >> 16); };
     int num_cand;
-    block_exclusive_scan(cand, sh.wave_tmp, &num_cand);
+    block_exclusive_scan(cand, sh.wave_tmp, &num_cand);  // its barriers also publish the cleared histograms
 
-    // Paths that need every key again (few candidates, no useful floor, or
-    // a list overflow) re-read this thread's run of the row (in L2 by then).
+    // Paths that need every key again (few candidates, or a list overflow)
+    // re-read this thread's run of the row.
     const RowView run{x, p.num_cols, 0, col0};
     const ListView no_list{nullptr, nullptr, 0};
     if (num_cand <= p.k) {
         place_picks<E, kFromRowRun>(no_list, run, 0, 0, 0u, 0, out, sh);  // every candidate
     } else {
-        const uint32_t floor = prefilter_floor(tmax, p.k, sh);
-        const uint32_t floor_top = floor >> 16;
-        int mine = 0;
+        // Floor: the lower edge of the 11-bit bin holding the k-th largest
+        // sub-run maximum; at least k keys are >= it.  1 (no filtering) when
+        // fewer than k sub-runs hold a candidate.
 #pragma unroll
-        for (int e = 0; e < E; ++e) mine += key_top(e) >= floor_top;
+        for (int j = 0; j < kSub; ++j)
+            if (smax[j] != 0u) atomicAdd(&sh.hist[smax[j] >> 21], 1);
+        __syncthreads();
+        if (tid < 64) {
+            int above;
+            const int bin = wave_find_bin(sh.hist, 2048, p.k, &above);
+            if (lane == 0) s_floor = bin <= 0 ? 1u : ((uint32_t)bin << 21);
+        }
+        __syncthreads();
+        const uint32_t floor = s_floor;
+        // Listed: top half >= floor_top (candidates' top halves are never 0,
+        // so floor_top >= 1 also drops the non-candidates).  Counted with
+        // integer arithmetic: for 16-bit t and f, (t + 2^16 - f) >> 16 is
+        // 1 exactly when t >= f.
+        const uint32_t floor_top = max(floor >> 16, 1u);
+        uint32_t mine_u = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) mine_u += (key_top(e) + 0x10000u - floor_top) >> 16;
+        const int mine = (int)mine_u;
         int listed;
         const int at = block_exclusive_scan(mine, sh.wave_tmp, &listed);
         int need = 0;
-        const ListView list{list_key, list_col, listed};
-        if (floor > 1u && listed <= kListCap) {
+        if (listed <= kListCap) {
+            // The keys >= floor in column order (top halves), counted by
+            // their top 11 bits.
             if (mine > 0) {
                 int w = at;
+                // The same test as the count above, against a copy of the
+                // floor the compiler cannot prove equal, so it recomputes the
+                // tests here instead of keeping one lane mask per key alive.
+                const uint32_t floor_top2 = __builtin_amdgcn_readfirstlane(floor_top);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    if (key_top(e) >= floor_top) {
-                        list_key[w] = order_key(x[col0 + e]);
+                    const uint32_t t = key_top(e);
+                    const bool in = t >= floor_top2;
+                    if (in) {
+                        list_key[w] = t << 16;
                         list_col[w] = col0 + e;
+                        atomicAdd(&hist_list[t >> 5], 1);
                     }
-                    w += key_top(e) >= floor_top;
+                    w += in;
                 }
             }
             __syncthreads();
-            const uint32_t T = radix_threshold<E, kFromList>(list, run, p.k, floor, sh, &need);
+            if (tid < 64) {
+                const uint32_t T = wave_list_select(list_key, list_col, listed, p.k, hist_list, sh.hist, x, &need);
+                if (lane == 0) {
+                    s_T = T;
+                    s_need = need;
+                }
+            }
+            __syncthreads();
+            const uint32_t T = s_T;
+            need = s_need;
             // Contiguous slices of the list (column order) per thread.
+            const ListView list{list_key, list_col, listed};
             const int per = (listed + kThreads - 1) / kThreads;
             const int lo = min(tid * per, listed), hi = min(lo + per, listed);
             place_picks<E, kFromList>(list, run, lo, hi, T, need, out, sh);
         } else {
+            // More keys above the floor than the list holds: select and place
+            // over the row itself (re-read).
+            __syncthreads();
             const uint32_t T = radix_threshold<E, kFromRowRun>(no_list, run, p.k, floor, sh, &need);
             place_picks<E, kFromRowRun>(no_list, run, 0, 0, T, need, out, sh);
         }
@@ -423,6 +560,14 @@ hipError_t launch_topk(const TopkParams &p, hipStream_t stream) {
         case 24: return launch_resident<24>(p, stream, grid, block);
         case 28: return launch_resident<28>(p, stream, grid, block);
         case 32: return launch_resident<32>(p, stream, grid, block);
+        case 36: return launch_resident<36>(p, stream, grid, block);
+        case 40: return launch_resident<40>(p, stream, grid, block);
+        case 44: return launch_resident<44>(p, stream, grid, block);
+        case 48: return launch_resident<48>(p, stream, grid, block);
+        case 52: return launch_resident<52>(p, stream, grid, block);
+        case 56: return launch_resident<56>(p, stream, grid, block);
+        case 60: return launch_resident<60>(p, stream, grid, block);
+        case 64: return launch_resident<64>(p, stream, grid, block);
         default: return launch_kernel(topk_streaming_kernel, grid, block, stream, p);
     }
 }
