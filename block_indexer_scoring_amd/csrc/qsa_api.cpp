@@ -261,7 +261,7 @@ int qsa_topk_blocks(const float *logits, int64_t logits_stride, int32_t num_rows
         return fail(QSA_ERR_LAYOUT, "%s: logits and out_idx must be 4-byte aligned", fn);
     qsa::TopkParams p{logits, logits_stride, num_rows, num_cols, k, out_idx, out_stride,
                       aligned(logits, 16) && logits_stride % 4 == 0};
-    return device_status(fn, qsa::launch_topk(p, static_cast<hipStream_t>(stream)));
+    return device_status(fn, qsa::launch_topk(p, static_cast<hipStream_t>(stream), current_cu_count()));
 }
 
 }  // extern "C"

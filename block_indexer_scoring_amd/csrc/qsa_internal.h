@@ -85,7 +85,7 @@ int decode_span_keys();
 int prefill_col_chunk(int64_t num_rows, int32_t out_cols, int num_cus);
 int prefill_rows_per_block();
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
-hipError_t launch_topk(const TopkParams &p, hipStream_t stream);
+hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus);
 hipError_t launch_metadata(const MetaParams &p, hipStream_t stream);
 
 }  // namespace qsa

@@ -31,12 +31,7 @@
 namespace qsa {
 namespace {
 
-#ifndef QSA_TOPK_THREADS
-#define QSA_TOPK_THREADS 512
-#endif
-constexpr int kThreads = QSA_TOPK_THREADS;
-constexpr int kWaves = kThreads / 64;
-constexpr int kListCap = kThreads * 4;  // keys >= floor kept in LDS
+constexpr int kMaxWaves = 16;  // workgroups of at most 1024 threads
 
 __device__ __forceinline__ uint32_t order_key(float v) {
     if (!(v > neg_inf())) return 0u;  // -inf and NaN are never picked
@@ -62,6 +57,7 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 
 // Exclusive prefix sum over the workgroup in thread order; *total gets the
 // sum.  Arithmetic is modulo 2^32 (callers may pack two counters in one word).
+template <int THREADS>
 __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave, int *total) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -70,7 +66,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave, int *tot
     __syncthreads();
     uint32_t before = x - (uint32_t)v, all = 0u;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < THREADS / 64; ++w) {
         const uint32_t t = (uint32_t)s_wave[w];
         before += w < wave ? t : 0u;
         all += t;
@@ -81,24 +77,38 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave, int *tot
 }
 
 struct SelectShared {
-    int hist[2048];
-    int wave_tmp[kWaves];
+    alignas(16) int hist[2048];  // 16-byte aligned: wave_find_bin reads it in int4 units
+    int wave_tmp[kMaxWaves];
     int pick_bin, pick_above;
 };
 
-// One wave finds the bin of hist[0..nb) (nb a power of two, at most 4096)
-// holding the kk-th largest counted key: lane l sums the max(nb/64, 1) bins
+// One wave finds the bin of hist[0..NB) (NB a power of two, at most 4096)
+// holding the kk-th largest counted key: lane l sums the max(NB/64, 1) bins
 // counted down from the top, a wave scan of the sums picks the lane whose
 // bins hold it, then a second wave scan over that lane's bins picks the bin.
 // Returns the bin (-1 if fewer than kk keys were counted) and sets
 // *above_out to the count in higher bins.  Wave-uniform; no barriers.
-__device__ __forceinline__ int wave_find_bin(const int *hist, int nb, int kk, int *above_out) {
+template <int NB>
+__device__ __forceinline__ int wave_find_bin(const int *hist, int kk, int *above_out) {
+    constexpr int kPer = NB >= 64 ? NB / 64 : 1;
     const int lane = threadIdx.x & 63;
-    const int per = nb >= 64 ? nb / 64 : 1;
-    const int hi = nb - 1 - lane * per;
+    const int hi = NB - 1 - lane * kPer;
     int sum = 0;
-    if (hi >= 0)
-        for (int b = 0; b < per; ++b) sum += hist[hi - b];
+    if (NB >= 64 || lane < NB) {
+        if constexpr (kPer % 4 == 0) {
+            // The lane's bins are contiguous: 16-byte reads, two in flight
+            // (a kernel-wide register budget is shared with the other waves).
+            const int4 *q = reinterpret_cast<const int4 *>(hist + hi - (kPer - 1));
+#pragma unroll 2
+            for (int j = 0; j < kPer / 4; ++j) {
+                const int4 v = q[j];
+                sum += (v.x + v.y) + (v.z + v.w);
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < kPer; ++b) sum += hist[hi - b];
+        }
+    }
     const int incl = (int)wave_inclusive_scan((uint32_t)sum);
     const uint64_t hit = __ballot(incl - sum < kk && kk <= incl);
     if (hit == 0) {
@@ -107,10 +117,10 @@ __device__ __forceinline__ int wave_find_bin(const int *hist, int nb, int kk, in
     }
     const int src = __builtin_ctzll(hit);
     const int above0 = __builtin_amdgcn_readlane(incl - sum, src);
-    const int top = nb - 1 - src * per;  // highest bin of lane src
-    const int c = lane < per ? hist[top - lane] : 0;
+    const int top = NB - 1 - src * kPer;  // highest bin of lane src
+    const int c = lane < kPer ? hist[top - lane] : 0;
     const int incl2 = (int)wave_inclusive_scan((uint32_t)c);
-    const uint64_t hit2 = __ballot(lane < per && above0 + incl2 >= kk);
+    const uint64_t hit2 = __ballot(lane < kPer && above0 + incl2 >= kk);
     const int f = __builtin_ctzll(hit2);
     *above_out = above0 + __builtin_amdgcn_readlane(incl2 - c, f);
     return top - f;
@@ -122,7 +132,8 @@ __device__ __forceinline__ int wave_find_bin(const int *hist, int nb, int kk, in
 __device__ __forceinline__ int find_bin(SelectShared &sh, int nb, int kk, int *above_out) {
     if (threadIdx.x < 64) {
         int above;
-        const int bin = wave_find_bin(sh.hist, nb, kk, &above);
+        const int bin = nb == 2048 ? wave_find_bin<2048>(sh.hist, kk, &above)
+                                   : wave_find_bin<1024>(sh.hist, kk, &above);
         if (threadIdx.x == 0) {
             sh.pick_bin = bin;
             sh.pick_above = above;
@@ -156,7 +167,7 @@ struct RowView {
 };
 
 // Count into hist the keys >= floor whose bits under mask equal prefix.
-template <int E, int SRC>
+template <int E, int SRC, int THREADS>
 __device__ __forceinline__ void count_bins(const ListView &list, const RowView &row,
                                            uint32_t floor, uint32_t mask,
                                            uint32_t prefix, int shift, int nb, int *hist) {
@@ -171,11 +182,11 @@ __device__ __forceinline__ void count_bins(const ListView &list, const RowView &
         }
     } else if (SRC == kFromList) {
 #pragma unroll 1
-        for (int i = threadIdx.x; i < list.size; i += kThreads) visit(list.key[i]);
+        for (int i = threadIdx.x; i < list.size; i += THREADS) visit(list.key[i]);
     } else {
 #pragma unroll 1
         for (int e = 0; e < row.slots; ++e) {
-            const int i = e * kThreads + (int)threadIdx.x;
+            const int i = e * THREADS + (int)threadIdx.x;
             visit(i < row.cols ? order_key(row.x[i]) : 0u);
         }
     }
@@ -184,7 +195,7 @@ __device__ __forceinline__ void count_bins(const ListView &list, const RowView &
 // Radix-select the k-th largest key among this thread's keys >= floor
 // (summed over the workgroup).  Requires at least k such keys.  Returns T
 // and sets *need to the number of keys equal to T that are picked.
-template <int E, int SRC>
+template <int E, int SRC, int THREADS>
 __device__ __forceinline__ uint32_t radix_threshold(const ListView &list, const RowView &row, int k,
                                                     uint32_t floor, SelectShared &sh, int *need) {
     const int tid = threadIdx.x;
@@ -194,9 +205,9 @@ __device__ __forceinline__ uint32_t radix_threshold(const ListView &list, const 
     for (int pass = 0; pass < 3; ++pass) {
         const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
         const int nb = pass == 2 ? 1024 : 2048;
-        for (int b = tid; b < nb; b += kThreads) sh.hist[b] = 0;
+        for (int b = tid; b < nb; b += THREADS) sh.hist[b] = 0;
         __syncthreads();
-        count_bins<E, SRC>(list, row, floor, mask, prefix, shift, nb, sh.hist);
+        count_bins<E, SRC, THREADS>(list, row, floor, mask, prefix, shift, nb, sh.hist);
         __syncthreads();
         int above;
         const int bin = find_bin(sh, nb, kk, &above);
@@ -208,26 +219,12 @@ __device__ __forceinline__ uint32_t radix_threshold(const ListView &list, const 
     return prefix;
 }
 
-// Floor from per-thread maxima: the lower edge of the 11-bit bin holding the
-// k-th largest thread maximum.  Returns 1 (no filtering) when fewer than k
-// threads hold a candidate (or the bin is the lowest one).
-__device__ __forceinline__ uint32_t prefilter_floor(uint32_t tmax, int k, SelectShared &sh) {
-    const int tid = threadIdx.x;
-    for (int b = tid; b < 2048; b += kThreads) sh.hist[b] = 0;
-    __syncthreads();
-    if (tmax != 0u) atomicAdd(&sh.hist[tmax >> 21], 1);
-    __syncthreads();
-    int above;
-    const int bin = find_bin(sh, 2048, k, &above);
-    return bin <= 0 ? 1u : ((uint32_t)bin << 21);
-}
-
 // Writes the picks of this thread's keys, which it visits in column order
 // (a run of the row, or the contiguous list slice [lo, hi)): one prefix sum
 // of packed (greater, equal) counts places every pick.  Counts stay below
 // 2^16 (at most 32768 keys per row here), so the low half never carries
 // into the high half.
-template <int E, int SRC>
+template <int E, int SRC, int THREADS>
 __device__ __forceinline__ void place_picks(const ListView &list, const RowView &row, int lo, int hi,
                                             uint32_t T, int need, int32_t *out, SelectShared &sh) {
     auto row_key = [&](int e) {
@@ -250,7 +247,7 @@ __device__ __forceinline__ void place_picks(const ListView &list, const RowView 
         }
     }
     int total;
-    const uint32_t base = (uint32_t)block_exclusive_scan((gt << 16) | eq, sh.wave_tmp, &total);
+    const uint32_t base = (uint32_t)block_exclusive_scan<THREADS>((gt << 16) | eq, sh.wave_tmp, &total);
     int gt_before = (int)(base >> 16);
     int eq_before = (int)(base & 0xffffu);
     auto place = [&](uint32_t k, int col) {
@@ -273,32 +270,70 @@ __device__ __forceinline__ void place_picks(const ListView &list, const RowView 
 // The k-th largest key T of the listed keys and how many keys equal to T
 // are picked, by one wave (wave 0).  The list holds each key's top 16 bits
 // (key >> 16 << 16); hist0 counts the list by the top 11 bits.  A radix
-// select over the top 16 bits (11 + 5) finds T's top half; if only some of
-// the keys sharing it are picked, those keys (few, normally) are re-read in
-// full from the row into the list and two more 8-bit passes resolve T.
-// Keys with other top halves compare with T correctly either way.
-// Requires at least k listed keys.
+// select over the top 16 bits (11 + 5) finds T's top half.  If only some of
+// the keys sharing it are picked, those keys are re-read in full from the
+// row and written back into the list; with at most 64 of them, one per
+// lane, T is the kk-th largest by direct comparison, otherwise two 8-bit
+// passes over the list finish it.  Keys with other top halves compare with
+// T correctly either way.  tied_idx is 64 ints of scratch.  Requires at
+// least k listed keys.
 __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *cols, int n, int k,
-                                                     const int *hist0, int *hist, const float *x,
-                                                     int *need_out) {
+                                                     const int *hist0, int *hist, int *tied_idx,
+                                                     const float *x, int *need_out) {
     const int lane = threadIdx.x & 63;
     int above;
     int kk = k;
-    const int b0 = wave_find_bin(hist0, 2048, kk, &above);
+    const int b0 = wave_find_bin<2048>(hist0, kk, &above);
     kk -= above;
     // One wave: its LDS operations take effect in issue order.
     if (lane < 32) hist[lane] = 0;
-    for (int i = lane; i < n; i += 64) {
-        const uint32_t key = list[i];
-        if ((key >> 21) == (uint32_t)b0) atomicAdd(&hist[(key >> 16) & 31], 1);
+#pragma unroll 1
+    for (int i0 = 0; i0 < n; i0 += 256) {
+        uint32_t key[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + 64 * u + lane;
+            key[u] = i < n ? list[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if ((key[u] >> 21) == (uint32_t)b0) atomicAdd(&hist[(key[u] >> 16) & 31], 1);
     }
-    const int b1 = wave_find_bin(hist, 32, kk, &above);
+    const int b1 = wave_find_bin<32>(hist, kk, &above);
     kk -= above;
     const uint32_t top = ((uint32_t)b0 << 5) | (uint32_t)b1;
     const int tied = hist[b1];  // listed keys whose top half is `top`
     if (kk == tied) {           // all of them are picked
         *need_out = kk;
         return top << 16;
+    }
+    if (tied <= 64) {
+        // Lane p takes the p-th tied entry in list (column) order.
+        int base = 0;
+#pragma unroll 1
+        for (int i0 = 0; i0 < n; i0 += 64) {
+            const int i = i0 + lane;
+            const bool match = i < n && (list[i] >> 16) == top;
+            const uint64_t m = __ballot(match);
+            if (match) tied_idx[base + __popcll(m & ((1ull << lane) - 1ull))] = i;
+            base += __popcll(m);
+        }
+        uint32_t key = 0u;
+        if (lane < tied) {
+            const int idx = tied_idx[lane];
+            key = order_key(x[cols[idx]]);
+            list[idx] = key;
+        }
+        int gt = 0, eq = 0;
+        for (int m = 0; m < tied; ++m) {
+            const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)key, m);
+            gt += km > key;
+            eq += km == key;
+        }
+        const uint64_t hit = __ballot(lane < tied && gt < kk && kk <= gt + eq);
+        const int src = __builtin_ctzll(hit);
+        *need_out = kk - __builtin_amdgcn_readlane(gt, src);
+        return (uint32_t)__builtin_amdgcn_readlane((int)key, src);
     }
     for (int i = lane; i < n; i += 64)
         if ((list[i] >> 16) == top) list[i] = order_key(x[cols[i]]);
@@ -311,7 +346,7 @@ __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *
             const uint32_t key = list[i];
             if ((key & shift_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
         }
-        const int bin = wave_find_bin(hist, 256, kk, &above);
+        const int bin = wave_find_bin<256>(hist, kk, &above);
         kk -= above;
         prefix |= (uint32_t)bin << shift;
         shift_mask |= 255u << shift;
@@ -320,18 +355,20 @@ __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *
     return prefix;
 }
 
-#ifndef QSA_TOPK_WAVES_PER_EU
-#define QSA_TOPK_WAVES_PER_EU 8
-#endif
-template <int E>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QSA_TOPK_WAVES_PER_EU)))
+// THREADS threads per row; WPE waves per SIMD the registers are sized for;
+// CHUNK 16-byte loads per thread in flight per step of the row load (0:
+// every load at once).
+template <int E, int THREADS, int WPE, int CHUNK>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE)))
 void topk_resident_kernel(TopkParams p) {
+    constexpr int kListCap = THREADS * 4;  // keys >= floor kept in LDS
     constexpr int kSub = 4;  // sub-runs per thread, one maximum each
     constexpr int kSubLen = (E + kSub - 1) / kSub;
     __shared__ SelectShared sh;
-    __shared__ int hist_list[2048];  // listed keys by their top 11 bits
+    __shared__ __attribute__((aligned(16))) int hist_list[2048];  // listed keys by their top 11 bits
     __shared__ uint32_t list_key[kListCap];
     __shared__ int list_col[kListCap];
+    __shared__ int tied_idx[64];
     __shared__ uint32_t s_floor, s_T;
     __shared__ int s_need;
     const int tid = threadIdx.x;
@@ -341,7 +378,7 @@ void topk_resident_kernel(TopkParams p) {
     int32_t *out = p.out + row * p.out_stride;
     const int col0 = tid * E;  // this thread's columns: col0 .. col0 + E - 1
 
-    for (int b = tid; b < 2048; b += kThreads) {
+    for (int b = tid; b < 2048; b += THREADS) {
         sh.hist[b] = 0;
         hist_list[b] = 0;
     }
@@ -364,7 +401,7 @@ void topk_resident_kernel(TopkParams p) {
         // of kChunk loads one chunk ahead of their use, so only two chunks
         // of raw values occupy registers at a time.
         constexpr int kVecs = E / 4;
-        constexpr int kChunk = 4;
+        constexpr int kChunk = CHUNK > 0 ? CHUNK : kVecs;
         f32x4 v[kVecs];
 #pragma unroll
         for (int c = 0; c < kVecs; c += kChunk) {
@@ -389,14 +426,14 @@ void topk_resident_kernel(TopkParams p) {
     }
     auto key_top = [&](int e) { return e % 2 == 0 ? (top16[e / 2] & 0xffffu) : (top16[e / 2] >> 16); };
     int num_cand;
-    block_exclusive_scan(cand, sh.wave_tmp, &num_cand);  // its barriers also publish the cleared histograms
+    block_exclusive_scan<THREADS>(cand, sh.wave_tmp, &num_cand);  // its barriers also publish the cleared histograms
 
     // Paths that need every key again (few candidates, or a list overflow)
     // re-read this thread's run of the row.
     const RowView run{x, p.num_cols, 0, col0};
     const ListView no_list{nullptr, nullptr, 0};
     if (num_cand <= p.k) {
-        place_picks<E, kFromRowRun>(no_list, run, 0, 0, 0u, 0, out, sh);  // every candidate
+        place_picks<E, kFromRowRun, THREADS>(no_list, run, 0, 0, 0u, 0, out, sh);  // every candidate
     } else {
         // Floor: the lower edge of the 11-bit bin holding the k-th largest
         // sub-run maximum; at least k keys are >= it.  1 (no filtering) when
@@ -407,7 +444,7 @@ void topk_resident_kernel(TopkParams p) {
         __syncthreads();
         if (tid < 64) {
             int above;
-            const int bin = wave_find_bin(sh.hist, 2048, p.k, &above);
+            const int bin = wave_find_bin<2048>(sh.hist, p.k, &above);
             if (lane == 0) s_floor = bin <= 0 ? 1u : ((uint32_t)bin << 21);
         }
         __syncthreads();
@@ -422,7 +459,7 @@ void topk_resident_kernel(TopkParams p) {
         for (int e = 0; e < E; ++e) mine_u += (key_top(e) + 0x10000u - floor_top) >> 16;
         const int mine = (int)mine_u;
         int listed;
-        const int at = block_exclusive_scan(mine, sh.wave_tmp, &listed);
+        const int at = block_exclusive_scan<THREADS>(mine, sh.wave_tmp, &listed);
         int need = 0;
         if (listed <= kListCap) {
             // The keys >= floor in column order (top halves), counted by
@@ -447,7 +484,7 @@ void topk_resident_kernel(TopkParams p) {
             }
             __syncthreads();
             if (tid < 64) {
-                const uint32_t T = wave_list_select(list_key, list_col, listed, p.k, hist_list, sh.hist, x, &need);
+                const uint32_t T = wave_list_select(list_key, list_col, listed, p.k, hist_list, sh.hist, tied_idx, x, &need);
                 if (lane == 0) {
                     s_T = T;
                     s_need = need;
@@ -458,24 +495,26 @@ void topk_resident_kernel(TopkParams p) {
             need = s_need;
             // Contiguous slices of the list (column order) per thread.
             const ListView list{list_key, list_col, listed};
-            const int per = (listed + kThreads - 1) / kThreads;
+            const int per = (listed + THREADS - 1) / THREADS;
             const int lo = min(tid * per, listed), hi = min(lo + per, listed);
-            place_picks<E, kFromList>(list, run, lo, hi, T, need, out, sh);
+            place_picks<E, kFromList, THREADS>(list, run, lo, hi, T, need, out, sh);
         } else {
             // More keys above the floor than the list holds: select and place
             // over the row itself (re-read).
             __syncthreads();
-            const uint32_t T = radix_threshold<E, kFromRowRun>(no_list, run, p.k, floor, sh, &need);
-            place_picks<E, kFromRowRun>(no_list, run, 0, 0, T, need, out, sh);
+            const uint32_t T = radix_threshold<E, kFromRowRun, THREADS>(no_list, run, p.k, floor, sh, &need);
+            place_picks<E, kFromRowRun, THREADS>(no_list, run, 0, 0, T, need, out, sh);
         }
     }
     const int picked = min(num_cand, p.k);
-    for (int i = picked + tid; i < p.k; i += kThreads) out[i] = -1;
+    for (int i = picked + tid; i < p.k; i += THREADS) out[i] = -1;
 }
 
 // Rows longer than the register-resident limit: each phase re-reads the row,
 // column c owned by thread c % 1024; picks are placed slot by slot.
-__global__ __launch_bounds__(kThreads) void topk_streaming_kernel(TopkParams p) {
+__global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
+    constexpr int kThreads = 1024;
+    constexpr int kWaves = kThreads / 64;
     __shared__ SelectShared sh;
     __shared__ int s_cnt[2][kWaves];
     const int tid = threadIdx.x;
@@ -493,14 +532,14 @@ __global__ __launch_bounds__(kThreads) void topk_streaming_kernel(TopkParams p) 
     int cand = 0;
     for (int e = 0; e < slots; ++e) cand += key_at(e) != 0u;
     int num_cand;
-    block_exclusive_scan(cand, sh.wave_tmp, &num_cand);
+    block_exclusive_scan<kThreads>(cand, sh.wave_tmp, &num_cand);
 
     uint32_t T = 0u;
     int need = 0;
     if (num_cand > p.k) {
         const ListView no_list{nullptr, nullptr, 0};
         const RowView mem{x, p.num_cols, slots, 0};
-        T = radix_threshold<1, kFromMemory>(no_list, mem, p.k, 1u, sh, &need);
+        T = radix_threshold<1, kFromMemory, kThreads>(no_list, mem, p.k, 1u, sh, &need);
     }
 
     int gt_run = 0, eq_run = 0;  // greater / equal keys in earlier slots
@@ -538,38 +577,35 @@ __global__ __launch_bounds__(kThreads) void topk_streaming_kernel(TopkParams p) 
     for (int i = picked + tid; i < p.k; i += kThreads) out[i] = -1;
 }
 
-template <int E>
-hipError_t launch_resident(const TopkParams &p, hipStream_t stream, dim3 grid, dim3 block) {
-    return launch_kernel(topk_resident_kernel<E>, grid, block, stream, p);
+template <int E, int THREADS, int WPE, int CHUNK>
+hipError_t launch_resident(const TopkParams &p, hipStream_t stream) {
+    return launch_kernel(topk_resident_kernel<E, THREADS, WPE, CHUNK>, dim3((unsigned)p.num_rows),
+                         dim3(THREADS), stream, p);
+}
+
+// Columns per thread, rounded up to a multiple of 4 (16-byte loads); rows
+// longer than 32768 columns go to the streaming kernel.
+template <int THREADS, int WPE, int CHUNK, int E = 4>
+hipError_t launch_config(const TopkParams &p, hipStream_t stream) {
+    constexpr int kMaxE = 32768 / THREADS;
+    const int per = ((p.num_cols + THREADS - 1) / THREADS + 3) / 4 * 4;
+    if (per <= E) return launch_resident<E, THREADS, WPE, CHUNK>(p, stream);
+    if constexpr (E + 4 <= kMaxE) {
+        return launch_config<THREADS, WPE, CHUNK, E + 4>(p, stream);
+    } else {
+        return launch_kernel(topk_streaming_kernel, dim3((unsigned)p.num_rows), dim3(1024), stream, p);
+    }
 }
 
 }  // namespace
 
-hipError_t launch_topk(const TopkParams &p, hipStream_t stream) {
-    const dim3 grid((unsigned)p.num_rows);
-    const dim3 block(kThreads);
-    // Columns per thread, rounded up to a multiple of 4 (16-byte loads).
-    const int per = ((p.num_cols + kThreads - 1) / kThreads + 3) / 4 * 4;
-    switch (per) {
-        case 0:
-        case 4: return launch_resident<4>(p, stream, grid, block);
-        case 8: return launch_resident<8>(p, stream, grid, block);
-        case 12: return launch_resident<12>(p, stream, grid, block);
-        case 16: return launch_resident<16>(p, stream, grid, block);
-        case 20: return launch_resident<20>(p, stream, grid, block);
-        case 24: return launch_resident<24>(p, stream, grid, block);
-        case 28: return launch_resident<28>(p, stream, grid, block);
-        case 32: return launch_resident<32>(p, stream, grid, block);
-        case 36: return launch_resident<36>(p, stream, grid, block);
-        case 40: return launch_resident<40>(p, stream, grid, block);
-        case 44: return launch_resident<44>(p, stream, grid, block);
-        case 48: return launch_resident<48>(p, stream, grid, block);
-        case 52: return launch_resident<52>(p, stream, grid, block);
-        case 56: return launch_resident<56>(p, stream, grid, block);
-        case 60: return launch_resident<60>(p, stream, grid, block);
-        case 64: return launch_resident<64>(p, stream, grid, block);
-        default: return launch_kernel(topk_streaming_kernel, grid, block, stream, p);
-    }
+hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus) {
+    // Many rows: 512-thread rows, four per CU (registers for eight waves per
+    // SIMD), each thread's loads issued two at a time.  At most one row per
+    // CU: the latency of one row is the whole cost, so 1024-thread rows with
+    // every load in flight at once (registers for four waves per SIMD).
+    if (p.num_rows <= (num_cus > 0 ? num_cus : 256)) return launch_config<1024, 4, 0>(p, stream);
+    return launch_config<512, 8, 2>(p, stream);
 }
 
 }  // namespace qsa
