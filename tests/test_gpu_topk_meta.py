@@ -47,6 +47,43 @@ def test_topk_bit_exact_on_given_logits(cols, k):
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
+def _pattern_rows(rng, rows, cols):
+    """Rows cycling through the edge patterns of the test above."""
+    x = (np.abs(rng.standard_normal((rows, cols))) * 3).astype(np.float32)
+    for r in range(rows):
+        kind = r % 10
+        if kind == 1:
+            x[r, (r * 7919) % cols:] = -np.inf
+        elif kind == 2:
+            x[r] = -np.inf
+        elif kind == 3:
+            x[r] = np.round(x[r] * 2) / 2
+        elif kind == 4:
+            x[r] = 1.0
+        elif kind == 5:
+            x[r, ::2] = 0.0
+            x[r, 1::2] = -0.0
+        elif kind == 6:
+            x[r] = rng.standard_normal(cols).astype(np.float32)
+        elif kind == 7:
+            x[r, ::5] = np.nan
+        elif kind == 8:
+            x[r] = np.arange(cols, dtype=np.float32)
+        elif kind == 9:
+            x[r] = np.round(x[r] * 64) / 64   # ties inside one 16-bit key prefix
+    return x
+
+
+@pytest.mark.parametrize("cols,k", [(5000, 512), (26024, 512), (32768, 512), (27048, 2048)])
+def test_topk_patterns_many_rows(cols, k):
+    """Enough rows for the many-row launch shape, with the edge patterns."""
+    rng = np.random.default_rng(cols ^ k)
+    x = _pattern_rows(rng, 300, cols)
+    got = _topk_gpu(x, k)
+    want = O.topk(x, k)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
 def test_topk_many_rows_and_strided_logits():
     rng = np.random.default_rng(5)
     big = rng.standard_normal((300, 700)).astype(np.float32)
