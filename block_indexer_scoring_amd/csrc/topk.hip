@@ -355,10 +355,8 @@ __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *
     return prefix;
 }
 
-// THREADS threads per row; WPE waves per SIMD the registers are sized for;
-// CHUNK 16-byte loads per thread in flight per step of the row load (0:
-// every load at once).
-template <int E, int THREADS, int WPE, int CHUNK>
+// THREADS threads per row; WPE waves per SIMD the registers are sized for.
+template <int E, int THREADS, int WPE>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE)))
 void topk_resident_kernel(TopkParams p) {
     constexpr int kListCap = THREADS * 4;  // keys >= floor kept in LDS
@@ -397,29 +395,14 @@ void topk_resident_kernel(TopkParams p) {
         else top16[e / 2] |= k & 0xffff0000u;
     };
     if (p.vec && col0 + E <= p.num_cols) {
-        // The whole run is inside the row: 16-byte loads, issued in chunks
-        // of kChunk loads one chunk ahead of their use, so only two chunks
-        // of raw values occupy registers at a time.
-        constexpr int kVecs = E / 4;
-        constexpr int kChunk = CHUNK > 0 ? CHUNK : kVecs;
-        f32x4 v[kVecs];
+        // The whole run is inside the row: 16-byte loads, all in flight at
+        // once (so each cache line is read while its neighbours' loads are
+        // still pending, before it can be evicted).
+        f32x4 v[E / 4];
 #pragma unroll
-        for (int c = 0; c < kVecs; c += kChunk) {
-            if (c == 0) {
+        for (int e = 0; e < E / 4; ++e) v[e] = *reinterpret_cast<const f32x4 *>(x + col0 + 4 * e);
 #pragma unroll
-                for (int i = 0; i < kChunk && i < kVecs; ++i)
-                    v[i] = *reinterpret_cast<const f32x4 *>(x + col0 + 4 * i);
-            }
-#pragma unroll
-            for (int i = c + kChunk; i < c + 2 * kChunk && i < kVecs; ++i)
-                v[i] = *reinterpret_cast<const f32x4 *>(x + col0 + 4 * i);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = c; i < c + kChunk && i < kVecs; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) absorb(4 * i + j, order_key(v[i][j]));
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int e = 0; e < E; ++e) absorb(e, order_key(v[e / 4][e % 4]));
     } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) absorb(e, col0 + e < p.num_cols ? order_key(x[col0 + e]) : 0u);
@@ -577,35 +560,34 @@ __global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
     for (int i = picked + tid; i < p.k; i += kThreads) out[i] = -1;
 }
 
-template <int E, int THREADS, int WPE, int CHUNK>
+template <int E, int THREADS, int WPE>
 hipError_t launch_resident(const TopkParams &p, hipStream_t stream) {
-    return launch_kernel(topk_resident_kernel<E, THREADS, WPE, CHUNK>, dim3((unsigned)p.num_rows),
+    return launch_kernel(topk_resident_kernel<E, THREADS, WPE>, dim3((unsigned)p.num_rows),
                          dim3(THREADS), stream, p);
 }
 
-// Columns per thread, rounded up to a multiple of 4 (16-byte loads); rows
-// longer than 32768 columns go to the streaming kernel.
-template <int THREADS, int WPE, int CHUNK, int E = 4>
+// Columns per thread, rounded up to a multiple of 4 (16-byte loads), up to
+// MAXE; the caller routes longer rows elsewhere.
+template <int THREADS, int WPE, int MAXE, int E = 4>
 hipError_t launch_config(const TopkParams &p, hipStream_t stream) {
-    constexpr int kMaxE = 32768 / THREADS;
     const int per = ((p.num_cols + THREADS - 1) / THREADS + 3) / 4 * 4;
-    if (per <= E) return launch_resident<E, THREADS, WPE, CHUNK>(p, stream);
-    if constexpr (E + 4 <= kMaxE) {
-        return launch_config<THREADS, WPE, CHUNK, E + 4>(p, stream);
-    } else {
-        return launch_kernel(topk_streaming_kernel, dim3((unsigned)p.num_rows), dim3(1024), stream, p);
-    }
+    if (per <= E || E == MAXE) return launch_resident<E, THREADS, WPE>(p, stream);
+    if constexpr (E + 4 <= MAXE) return launch_config<THREADS, WPE, MAXE, E + 4>(p, stream);
+    return hipErrorInvalidValue;  // not reached
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus) {
-    // Many rows: 512-thread rows, four per CU (registers for eight waves per
-    // SIMD), each thread's loads issued two at a time.  At most one row per
-    // CU: the latency of one row is the whole cost, so 1024-thread rows with
-    // every load in flight at once (registers for four waves per SIMD).
-    if (p.num_rows <= (num_cus > 0 ? num_cus : 256)) return launch_config<1024, 4, 0>(p, stream);
-    return launch_config<512, 8, 2>(p, stream);
+    if (p.num_cols > 32768)  // longer than the register-resident shapes hold
+        return launch_kernel(topk_streaming_kernel, dim3((unsigned)p.num_rows), dim3(1024), stream, p);
+    // At most one row per CU: the latency of one row is the whole cost, so
+    // 1024-thread rows (registers for four waves per SIMD).  Many rows:
+    // 512-thread rows, four per CU (registers for eight waves per SIMD),
+    // up to 56 columns per thread; longer rows, 1024-thread rows two per CU.
+    if (p.num_rows <= (num_cus > 0 ? num_cus : 256)) return launch_config<1024, 4, 32>(p, stream);
+    if (p.num_cols <= 512 * 56) return launch_config<512, 8, 56>(p, stream);
+    return launch_config<1024, 8, 32>(p, stream);
 }
 
 }  // namespace qsa
