@@ -318,6 +318,8 @@ def main(argv=None) -> int:
         e.close()
     avg = {n: float(np.mean(v)) for n, v in per.items()}
     med = {n: float(np.median(v)) for n, v in per.items()}
+    p10 = {n: float(np.percentile(v, 10)) for n, v in per.items()}
+    p90 = {n: float(np.percentile(v, 90)) for n, v in per.items()}
 
     comp_total = float(comp_host[:R].sum())
     dbytes = decode_bytes(R, DQL, comp_total)
@@ -364,9 +366,34 @@ def main(argv=None) -> int:
                               read_traffic("topk.hip", "topk")),
         "kernel_us_avg": {n: round(v, 3) for n, v in avg.items()},
         "kernel_us_median": {n: round(v, 3) for n, v in med.items()},
+        "kernel_us_p10": {n: round(v, 3) for n, v in p10.items()},
+        "kernel_us_p90": {n: round(v, 3) for n, v in p90.items()},
         "prefill_tflops": round(prefill_tflops, 2),
         "decode_bytes": dbytes, "prefill_bytes": pbytes, "prefill_flops": pflops,
         "topk_prefill_bytes": tk_bytes,
+    }
+
+    # A measured bandwidth for context: a plain 1 GiB device-to-device copy
+    # (read + write bytes over its time), and each HBM-bound kernel's rate as
+    # a fraction of it.
+    n_copy = (1 << 30) // 4
+    c_src = torch.ones(n_copy, dtype=torch.float32, device=dev)
+    c_dst = torch.empty_like(c_src)
+    c_dst.copy_(c_src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        c_dst.copy_(c_src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2.0 * n_copy * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del c_src, c_dst
+    result["measured_copy_gbps"] = round(copy_gbps, 1)
+    result["frac_of_measured_copy"] = {
+        "decode": round(decode_gbps / copy_gbps, 4),
+        "prefill": round(prefill_gbps / copy_gbps, 4),
+        "topk_prefill": round(topk_gbps / copy_gbps, 4),
     }
 
     if args.copy_calibration_mib > 0:
