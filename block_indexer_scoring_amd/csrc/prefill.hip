@@ -8,24 +8,32 @@
 // The scores are one dense contraction [rows*4 heads x 128] x [128 x keys]
 // followed by a per-(row, key) epilogue, run on the matrix cores with
 // v_mfma_f32_16x16x32_bf16:
-//   - A workgroup owns kBM query rows (16 per wavefront) and a chunk of
-//     output columns.  Each wavefront keeps its 16 rows x 4 heads of Q in
+//   - A workgroup of 8 wavefronts owns kBM = 128 query rows (16 per wave)
+//     and a chunk of output columns; one workgroup fills a CU (two waves
+//     per SIMD).  Each wavefront keeps its 16 rows x 4 heads of Q in
 //     registers as MFMA A fragments for the whole chunk (m = 4*row + head).
-//   - Key tiles of 64 keys (16 KB) are staged in LDS with direct
-//     global-to-LDS loads, two tiles per buffer and two buffers: the loads
-//     of the next pair are in flight while the current pair is multiplied
-//     (one workgroup barrier per 128 keys), and every wave of the workgroup
-//     reuses each staged tile.  LDS rows are XOR-swizzled in 16-byte units
-//     so the B-fragment reads are free of bank conflicts.
-//   - Registers are held to two wavefronts per SIMD, so one wave's epilogue
-//     and stores overlap the other's MFMAs.
+//   - Key tiles of 64 keys (16 KB) are staged in LDS by buffer loads that
+//     write LDS directly, two tiles per buffer and two buffers: the loads of
+//     the next pair are in flight while the current pair is multiplied (one
+//     workgroup barrier per 128 keys), and all 8 waves reuse each staged
+//     tile.  The buffer resource spans exactly the existing keys, so keys
+//     outside [0, num_keys) arrive as zeros with no per-key edge path.  LDS
+//     rows are XOR-swizzled in 16-byte units so the B-fragment reads are
+//     free of bank conflicts.
 //   - In the MFMA result a lane holds the 4 heads of one (row, key), so
 //     ReLU, head sum and scale run in-lane; tile key c + 4n + g sits in
 //     column n of group g, giving each lane 4 consecutive keys for one
-//     16-byte store.  Only tiles that cross a row's interval end (or start)
-//     evaluate the mask.  The output (4 bytes per cell, the bulk of the
-//     traffic) goes out with ordinary cached stores: on this GPU they write
-//     the tiled pattern markedly faster than non-temporal stores.
+//     16-byte store.  A wave works through its tile in 4-row slices, and
+//     the epilogue and store of each slice run while the matrix cores
+//     multiply the next (software pipeline, instruction groups interleaved
+//     MFMA / VALU), so the vector ALU work hides under MFMA time.  Only
+//     tiles that cross a row's interval end (or start) evaluate the mask.
+//   - Stores and key loads share the in-order vector-memory counter; every
+//     slice's scores leave as exactly one buffer store, so the wait for a
+//     key buffer can leave the most recent stores in flight.
+//   - Workgroups are numbered so that those on one XCD (launch order is
+//     round-robin over the 8 XCDs) share a column chunk: each XCD's L2
+//     then holds one chunk's keys rather than all of them.
 //   - Tiles past the last key any row of the workgroup may see are not
 //     multiplied: they are written as -inf only (causal tile skip).
 // Rows of one workgroup normally share row_k_start (packed requests); rows
@@ -35,24 +43,20 @@
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
-#ifndef QSA_PREFILL_WAVES
-#define QSA_PREFILL_WAVES 4
-#endif
-#ifndef QSA_PREFILL_TILES_PER_STAGE
-#define QSA_PREFILL_TILES_PER_STAGE 2
-#endif
 
 namespace qsa {
 namespace {
 
-constexpr int kWaves = QSA_PREFILL_WAVES;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 16;
 constexpr int kBM = kWaves * kRowsPerWave;  // query rows per workgroup
 constexpr int kBN = 64;                     // keys per LDS tile
 constexpr int kTileElems = kBN * kDim;      // bf16 elements per tile
 constexpr int kBlocksPerWave = kBN / 4 / kWaves;  // 1 KB LDS blocks staged per wave per tile
-constexpr int kTilesPerStage = QSA_PREFILL_TILES_PER_STAGE;  // key tiles per LDS buffer
+constexpr int kTilesPerStage = 2;                // key tiles per LDS buffer
+constexpr int kStoresInFlight = 4;               // stores a key-buffer wait leaves outstanding
+constexpr int kXcds = 8;                         // XCDs that launch order cycles through
 
 // LDS element offset of 16-byte chunk `chunk` (0..15) of tile key `key`.
 __device__ __forceinline__ int lds_offset(int key, int chunk) {
@@ -84,6 +88,10 @@ __device__ __forceinline__ void store4(float *dst, bool vec, int col, int c_end,
 // Fourth word of a raw buffer resource (32-bit data format) on gfx9-class GPUs.
 constexpr int kBufferWord3 = 0x00020000;
 
+// kExact: every slice of scores goes out as exactly one buffer store per
+// lane (the output rows of a workgroup span less than 2 GiB), so the number
+// of vector-memory ops after each key prefetch is fixed on every path.
+template <bool kExact>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillParams p) {
     // Two separate LDS objects (not one [2][...] array), so the compiler can
@@ -101,8 +109,13 @@ void prefill_kernel(PrefillParams p) {
     const int wave = tid >> 6;
     const int n = lane & 15;
     const int q4 = lane >> 4;
-    const int rb = blockIdx.x % p.row_blocks;
-    const int cc = blockIdx.x / p.row_blocks;
+    // Workgroup i runs on XCD i % 8.  Renumber so that the workgroups of
+    // one XCD take consecutive (row block, chunk) slots, chunk-major.
+    const int groups = p.row_blocks * p.col_chunks;
+    const int xcd = blockIdx.x % kXcds;
+    const int slot = xcd * (groups / kXcds) + min(xcd, groups % kXcds) + (int)blockIdx.x / kXcds;
+    const int rb = slot % p.row_blocks;
+    const int cc = slot / p.row_blocks;
     const int row0 = rb * kBM;
     const int c_begin = cc * p.col_chunk;
     const int c_end = min(c_begin + p.col_chunk, p.out_cols);
@@ -165,13 +178,13 @@ void prefill_kernel(PrefillParams p) {
         for (int i = tid; i < kBM; i += kThreads)
             if (!s_done[i]) atomicMin(&s_cur, s_start[i]);
         __syncthreads();
-        const int cur = s_cur;
+        const int cur = __builtin_amdgcn_readfirstlane(s_cur);
         if (cur == INT_MAX) break;
         for (int i = tid; i < kBM; i += kThreads)
             if (!s_done[i] && s_start[i] == cur)
                 atomicMax(&s_lim, clamp_cols((int64_t)s_end[i] - cur, -1, INT_MAX - kBN));
         __syncthreads();
-        const int lim = s_lim;  // columns >= lim hold no key for any row of this pass
+        const int lim = __builtin_amdgcn_readfirstlane(s_lim);  // columns >= lim hold no key for any row of this pass
 
         // This lane's output rows (MFMA result layout: row 4mt + q4).
         bool in_pass[4];
@@ -196,110 +209,146 @@ void prefill_kernel(PrefillParams p) {
         // Stage one key tile (64 keys x 256 bytes) into LDS buffer `buf`: a
         // uniform base plus per-lane constant offsets; a tile that reaches
         // past either end of the keys is zero-filled and loaded per key.
+        // Keys of this pass as one raw buffer that starts at the first key
+        // the chunk can touch (or key 0) and ends at the last key: a lane
+        // whose key lies outside [0, num_keys) gets an offset outside the
+        // buffer (negative offsets wrap past its end), and the hardware
+        // writes zeros to LDS for it.  Staging is therefore the same four
+        // direct-to-LDS loads for every tile, edges included.
+        int64_t k_first = (int64_t)cur + c_begin;
+        if (k_first < 0) k_first = 0;
+        int64_t k_bytes = p.num_keys - k_first;
+        k_bytes = k_bytes < 0 ? 0 : k_bytes * p.k_stride * 2;
+        const int k_records = __builtin_amdgcn_readfirstlane((int)(k_bytes > INT_MAX ? INT_MAX : k_bytes));
+        const uint64_t k_base = (uint64_t)(p.k + k_first * p.k_stride);
+        const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void *>(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(k_base >> 32)) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)k_base)),
+            0, k_records, kBufferWord3);
+        // Stage one key tile (64 keys x 256 bytes) into LDS buffer `buf`.
         auto stage = [&](int tile_c, uint16_t *buf) {
-            const int64_t first = (int64_t)cur + tile_c;
-            if (first >= 0 && first + kBN <= p.num_keys) {
-                const char *base = reinterpret_cast<const char *>(p.k + first * p.k_stride);
+            const uint32_t tile_off = (uint32_t)(((int64_t)cur + tile_c - k_first) * p.k_stride * 2);
 #pragma unroll
-                for (int i = 0; i < kBlocksPerWave; ++i) {
-                    const int b = wave * kBlocksPerWave + i;
-                    __builtin_amdgcn_global_load_lds(
-                        (const __attribute__((address_space(1))) void *)(base + st_goff[i]),
-                        (__attribute__((address_space(3))) void *)&buf[b * 512], 16, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < kBlocksPerWave; ++i) {
-                    const int b = wave * kBlocksPerWave + i;
-                    const int key = 4 * b + (lane >> 4);
-                    const int chunk = (lane & 15) ^ (b & 15);
-                    const int64_t kn = first + key;
-                    const u32x4 v = (kn >= 0 && kn < p.num_keys) ? load_u32x4(p.k + kn * p.k_stride + chunk * 8)
-                                                                 : zero_u32x4();
-                    *reinterpret_cast<u32x4 *>(&buf[b * 512 + lane * 8]) = v;
-                }
+            for (int i = 0; i < kBlocksPerWave; ++i) {
+                const int b = wave * kBlocksPerWave + i;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (__attribute__((address_space(3))) void *)&buf[b * 512],
+                                                         16, tile_off + st_goff[i], 0, 0, 0);
             }
         };
 
-        // Scores of the previous tile wait in registers and are stored at the
-        // start of the next iteration, before its key prefetch is issued:
-        // stores count in the same in-order vector-memory counter as loads,
-        // so the wait for the prefetch then only covers stores that have
-        // had a whole tile of MFMA time to drain.
-        f32x4 pend[4];
-        int pend_c = -1;  // tile column of the pending scores, -1 if none
-        // The workgroup's output rows as one raw buffer.  A full tile's
-        // scores go out as exactly four buffer stores per wave: lanes whose
-        // row is not in this pass store to an offset past the buffer's end,
-        // which the hardware drops.  With that fixed count, the wait before
-        // a buffer of keys can leave the most recent tile's stores in flight.
+        // The workgroup's output rows as one raw buffer.  A slice of scores
+        // (4 rows x 64 keys of one wave) goes out as exactly one buffer store
+        // per lane: lanes whose row is not in this pass, and the placeholder
+        // slice before a pass's first tile, store to an offset past the
+        // buffer's end, which the hardware drops.  With that fixed count the
+        // wait for a buffer of keys can leave the latest stores in flight.
         const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
             p.out + (int64_t)row0 * p.out_stride, 0,
-            p.exact_stores ? (int)((int64_t)min(kBM, p.num_rows - row0) * p.out_stride * 4) : 0, kBufferWord3);
+            kExact ? (int)((int64_t)min(kBM, p.num_rows - row0) * p.out_stride * 4) : 0, kBufferWord3);
+        constexpr uint32_t kDropped = 0x80000000u;
         uint32_t row_boff[4];  // byte offset of (row, column 4n) in out_rsrc
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const int idx = wave * kRowsPerWave + 4 * mt + q4;
-            row_boff[mt] = in_pass[mt] ? (uint32_t)(((int64_t)idx * p.out_stride + 4 * n) * 4) : 0x80000000u;
+            row_boff[mt] = in_pass[mt] ? (uint32_t)(((int64_t)idx * p.out_stride + 4 * n) * 4) : kDropped;
         }
-        auto flush = [&]() {
-            if (pend_c < 0) return;
-            const int col = pend_c + 4 * n;
-            const bool full = p.out_vec && pend_c + kBN <= c_end;
-            if (full && p.exact_stores) {
+
+        // Scores of one slice: rows 4mt .. 4mt+3 of the wave (x 4 heads, the
+        // MFMA's m = 4 * row + head) against the tile's 64 keys.
+        auto multiply = [&](int mt, const u32x4 (&b)[4][4], f32x4 (&acc)[4]) {
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    __builtin_amdgcn_raw_buffer_store_b128(pend[mt], out_rsrc, row_boff[mt] + 4u * (uint32_t)pend_c,
-                                                           0, 0);
-                pend_c = -1;
-                return;
-            }
+            for (int g = 0; g < 4; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                if (!in_pass[mt]) continue;
-                if (full)
-                    *reinterpret_cast<f32x4 *>(row_ptr[mt] + pend_c) = pend[mt];
-                else
-                    store4(row_ptr[mt] + pend_c, p.out_vec, col, c_end, pend[mt][0], pend[mt][1], pend[mt][2],
-                           pend[mt][3]);
-            }
-            pend_c = -1;
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) acc[g] = mfma16x16x32(qa[mt][ks], b[ks][g], acc[g]);
         };
-
-        auto compute_tile = [&](int tile_c, const uint16_t *tile) {
-            f32x4 acc[4][4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const u32x4 b = *reinterpret_cast<const u32x4 *>(&tile[rd_off[ks] + g * kDim]);
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) acc[mt][g] = mfma16x16x32(qa[mt][ks], b, acc[mt][g]);
-                }
-            }
-
-            const bool masked = !(tile_c + kBN <= wave_lim && tile_c >= col_min);
+        // Epilogue and store of a slice whose tile needs no mask and lies
+        // wholly inside the chunk (tile_c < 0: placeholder, store dropped).
+        auto finish_fast = [&](int mt, int tile_c, const f32x4 (&acc)[4]) {
+            const f32x4 v{head_sum_score(acc[0], p.scale), head_sum_score(acc[1], p.scale),
+                          head_sum_score(acc[2], p.scale), head_sum_score(acc[3], p.scale)};
+            __builtin_amdgcn_raw_buffer_store_b128(v, out_rsrc, tile_c >= 0 ? row_boff[mt] : kDropped,
+                                                   4 * max(tile_c, 0), 0);
+        };
+        // Any slice: mask per cell, partial tiles and unbounded rows.
+        auto finish_general = [&](int mt, int tile_c, bool masked, const f32x4 (&acc)[4]) {
+            f32x4 v;
             if (!masked) {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    pend[mt] = f32x4{head_sum_score(acc[mt][0], p.scale), head_sum_score(acc[mt][1], p.scale),
-                                     head_sum_score(acc[mt][2], p.scale), head_sum_score(acc[mt][3], p.scale)};
+                v = f32x4{head_sum_score(acc[0], p.scale), head_sum_score(acc[1], p.scale),
+                          head_sum_score(acc[2], p.scale), head_sum_score(acc[3], p.scale)};
             } else {
                 const int col = tile_c + 4 * n;
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int c = col + g;
-                        pend[mt][g] = (c < row_lim[mt] && c >= col_min) ? head_sum_score(acc[mt][g], p.scale)
-                                                                        : neg_inf();
-                    }
+                for (int g = 0; g < 4; ++g) {
+                    const int c = col + g;
+                    v[g] = (c < row_lim[mt] && c >= col_min) ? head_sum_score(acc[g], p.scale) : neg_inf();
+                }
             }
-            pend_c = tile_c;
+            const int col = tile_c + 4 * n;
+            if (kExact) {
+                // Lanes wholly inside the chunk take the buffer store; the one
+                // lane that straddles the chunk's end stores its cells singly.
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, out_rsrc, (tile_c >= 0 && col + 3 < c_end) ? row_boff[mt] : kDropped, 4 * max(tile_c, 0), 0);
+                if (tile_c >= 0 && in_pass[mt] && col < c_end && col + 3 >= c_end)
+                    store4(row_ptr[mt] + tile_c, false, col, c_end, v[0], v[1], v[2], v[3]);
+            } else if (tile_c >= 0 && in_pass[mt]) {
+                store4(row_ptr[mt] + tile_c, p.out_vec, col, c_end, v[0], v[1], v[2], v[3]);
+            }
+        };
+        // Software pipeline over slices: the epilogue and store of slice s
+        // run while the matrix cores multiply slice s + 1, so vector ALU work
+        // and stores hide under MFMA time.  Slice 3 of a tile is finished
+        // during slice 0 of the next.  accA/accB alternate; accB carries the
+        // deferred slice from tile to tile.
+        f32x4 accA[4], accB[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) accB[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        int prev_c = -1;
+        bool prev_masked = false;
+        auto interleave = [&]() {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+            }
+            __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);      // the store
+        };
+        auto load_b = [&](const uint16_t *tile, u32x4 (&b)[4][4]) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) b[ks][g] = *reinterpret_cast<const u32x4 *>(&tile[rd_off[ks] + g * kDim]);
+        };
+        auto do_tile = [&](int tile_c, const u32x4 (&b)[4][4]) {
+            const bool masked = !(tile_c + kBN <= wave_lim && tile_c >= col_min);
+            const bool full = p.out_vec && tile_c + kBN <= c_end;
+            if (kExact && full && !masked && !prev_masked) {
+                multiply(0, b, accA);
+                finish_fast(3, prev_c, accB);
+                interleave();
+                multiply(1, b, accB);
+                finish_fast(0, tile_c, accA);
+                interleave();
+                multiply(2, b, accA);
+                finish_fast(1, tile_c, accB);
+                interleave();
+                multiply(3, b, accB);
+                finish_fast(2, tile_c, accA);
+                interleave();
+            } else {
+                multiply(0, b, accA);
+                finish_general(3, prev_c, prev_masked, accB);
+                multiply(1, b, accB);
+                finish_general(0, tile_c, masked, accA);
+                multiply(2, b, accA);
+                finish_general(1, tile_c, masked, accB);
+                multiply(3, b, accB);
+                finish_general(2, tile_c, masked, accA);
+            }
+            prev_c = tile_c;
+            prev_masked = masked;
         };
 
         // One LDS buffer holds kTilesPerStage consecutive tiles; the next
@@ -309,32 +358,50 @@ void prefill_kernel(PrefillParams p) {
             for (int h = 0; h < kTilesPerStage; ++h)
                 if (it + h < n_compute) stage(c_begin + (it + h) * kBN, buf + h * kTileElems);
         };
+        // Stores issued after a buffer's loads: one per slice, 4 per tile.
+        constexpr int kStoresPerStage = 4 * kTilesPerStage;
+        static_assert(kStoresInFlight <= kStoresPerStage && kStoresInFlight <= 15, "vmcnt field");
         auto run_stage = [&](int it, const uint16_t *cur_buf, uint16_t *next_buf) {
-            // The buffer is in LDS once every wave's loads for it have landed.
-            // Vector-memory ops complete in issue order; from the third
-            // stage on, the only ops issued after this buffer's loads are
-            // the four stores of the previous stage's first tile, which may
-            // stay in flight (s_waitcnt vmcnt(4) lgkmcnt(0)).
-            if (p.exact_stores && it >= 2 * kTilesPerStage) __builtin_amdgcn_s_waitcnt(0x0074);
+            // The buffer is in LDS once every wave's loads for it have
+            // landed.  Vector-memory ops complete in issue order, and the
+            // previous stage issued exactly kStoresPerStage stores after
+            // them, so up to that many may stay in flight.
+            if (kExact) __builtin_amdgcn_s_waitcnt(0x0070 | kStoresInFlight);  // vmcnt(N) lgkmcnt(0)
             else __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            flush();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            // The first tile's key fragments are read before the next
+            // buffer's loads are issued.
+            u32x4 b0[4][4];
+            load_b(cur_buf, b0);
             if (it + kTilesPerStage < n_compute) stage_tiles(it + kTilesPerStage, next_buf);
 #pragma unroll
             for (int h = 0; h < kTilesPerStage; ++h) {
-                if (it + h < n_compute) {
-                    if (h > 0) flush();
-                    compute_tile(c_begin + (it + h) * kBN, cur_buf + h * kTileElems);
+                if (h == 0) {
+                    do_tile(c_begin + it * kBN, b0);
+                } else if (it + h < n_compute) {
+                    u32x4 b[4][4];
+                    load_b(cur_buf + h * kTileElems, b);
+                    do_tile(c_begin + (it + h) * kBN, b);
+                } else if (kExact) {
+                    // Keep the store count of a stage fixed (dropped stores).
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        __builtin_amdgcn_raw_buffer_store_b128(f32x4{0.f, 0.f, 0.f, 0.f}, out_rsrc, kDropped, 0, 0);
                 }
             }
         };
 
-        if (n_compute > 0) stage_tiles(0, ktile0);
+        if (n_compute > 0) {
+            stage_tiles(0, ktile0);
+            __builtin_amdgcn_s_waitcnt(0);
+        }
         for (int it = 0; it < n_compute; it += 2 * kTilesPerStage) {
             run_stage(it, ktile0, ktile1);
             if (it + kTilesPerStage < n_compute) run_stage(it + kTilesPerStage, ktile1, ktile0);
         }
-        flush();
+        if (prev_c >= 0) finish_general(3, prev_c, prev_masked, accB);
 
         // Tiles that no row of this pass can see: -inf only.
         const float ni = neg_inf();
@@ -354,23 +421,30 @@ void prefill_kernel(PrefillParams p) {
 
 }  // namespace
 
-int prefill_col_chunk(int64_t num_rows, int32_t out_cols, int num_cus) {
-    // One round of workgroups (two per CU), each walking a long run of
+int prefill_col_chunk(int64_t num_rows, int32_t out_cols, int64_t k_stride, int num_cus) {
+    // One round of workgroups (one per CU), each walking a long run of
     // columns: the per-workgroup setup is paid once, and each workgroup's
     // stores cover long stretches of its rows.
     const int64_t row_blocks = (num_rows + kBM - 1) / kBM;
     const int64_t tiles = ((int64_t)out_cols + kBN - 1) / kBN;
-    const int64_t target_groups = 2 * (int64_t)(num_cus > 0 ? num_cus : 256);
+    const int64_t target_groups = (int64_t)(num_cus > 0 ? num_cus : 256);
     int64_t per_chunk = (tiles * row_blocks + target_groups - 1) / target_groups;
     if (per_chunk < 8) per_chunk = 8;
+    // Key offsets inside a chunk's buffer resource are 32-bit: keep a
+    // chunk's keys (plus one tile) within 2^30 bytes.
+    const int64_t max_chunk = ((int64_t)1 << 30) / (kBN * k_stride * 2) - 1;
+    if (per_chunk > max_chunk) per_chunk = max_chunk;
     if (per_chunk > tiles) per_chunk = tiles;
     if (per_chunk < 1) per_chunk = 1;
     return (int)(per_chunk * kBN);
 }
 
+int64_t prefill_max_k_stride() { return ((int64_t)1 << 30) / (2 * kBN * 2); }
+
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
-    return launch_kernel(prefill_kernel, grid, dim3(kThreads), stream, p);
+    if (p.exact_stores) return launch_kernel(prefill_kernel<true>, grid, dim3(kThreads), stream, p);
+    return launch_kernel(prefill_kernel<false>, grid, dim3(kThreads), stream, p);
 }
 
 int prefill_rows_per_block() { return kBM; }

@@ -217,9 +217,14 @@ int qsa_mqa_prefill(const void *q, int64_t q_stride_row, int64_t q_stride_head, 
                     "%s: q and k need a 16-byte aligned base and positive strides that are multiples "
                     "of 8 elements on every axis longer than 1 (16-byte vector loads)", fn);
     if (!aligned(out, 4)) return fail(QSA_ERR_LAYOUT, "%s: out must be 4-byte aligned", fn);
+    // The stride of a single key is never used; normalise it.
+    if (num_keys <= 1) k_stride = 128;
+    if (k_stride > qsa::prefill_max_k_stride())
+        return fail(QSA_ERR_UNSUPPORTED, "%s: k_stride %lld exceeds %lld elements", fn, (long long)k_stride,
+                    (long long)qsa::prefill_max_k_stride());
 
     const int bm = qsa::prefill_rows_per_block();
-    const int chunk = qsa::prefill_col_chunk(num_rows, out_cols, current_cu_count());
+    const int chunk = qsa::prefill_col_chunk(num_rows, out_cols, k_stride, current_cu_count());
     const int64_t row_blocks = ((int64_t)num_rows + bm - 1) / bm;
     const int64_t col_chunks = ((int64_t)out_cols + chunk - 1) / chunk;
     if (row_blocks * col_chunks >= INT32_MAX)

@@ -82,7 +82,8 @@ hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t s
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 int decode_span_keys();
-int prefill_col_chunk(int64_t num_rows, int32_t out_cols, int num_cus);
+int prefill_col_chunk(int64_t num_rows, int32_t out_cols, int64_t k_stride, int num_cus);
+int64_t prefill_max_k_stride();  // larger key strides overflow the kernel's 32-bit key offsets
 int prefill_rows_per_block();
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus);

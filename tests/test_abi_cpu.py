@@ -130,6 +130,9 @@ def _prefill(lib, **kw):
     (dict(sk=132), 3, "multiples"),
     (dict(sk=-128), 3, "multiples"),
     (dict(out=FAKE + 1), 3, "aligned"),
+    # Key offsets inside the kernel are 32-bit: strides past 2^22 elements
+    # (8 MiB per key row) are refused before any launch.
+    (dict(sk=(1 << 22) + 8), 2, "k_stride"),
 ])
 def test_prefill_rejects(lib, kw, code, text):
     assert _prefill(lib, **kw) == code
