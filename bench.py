@@ -396,6 +396,24 @@ def main(argv=None) -> int:
         "topk_prefill": round(topk_gbps / copy_gbps, 4),
     }
 
+    # A measured matrix-core rate for context: a large square bf16 GEMM
+    # (8192^3, fp32 accumulate) through the vendor BLAS, and the prefill
+    # kernel's rate as a fraction of it.
+    g = 8192
+    ga = torch.randn(g, g, device=dev).to(torch.bfloat16)
+    gb = torch.randn(g, g, device=dev).to(torch.bfloat16)
+    gc = torch.mm(ga, gb)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        torch.mm(ga, gb, out=gc)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2.0 * g ** 3 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del ga, gb, gc
+    result["measured_gemm_tflops"] = round(gemm_tflops, 1)
+    result["prefill_frac_of_measured_gemm"] = round(prefill_tflops / gemm_tflops, 4)
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
