@@ -88,12 +88,44 @@ __device__ __forceinline__ void store4(float *dst, bool vec, int col, int c_end,
 // Fourth word of a raw buffer resource (32-bit data format) on gfx9-class GPUs.
 constexpr int kBufferWord3 = 0x00020000;
 
-// kExact: every slice of scores goes out as exactly one buffer store per
-// lane (the output rows of a workgroup span less than 2 GiB), so the number
-// of vector-memory ops after each key prefetch is fixed on every path.
-template <bool kExact>
+// What the kernel does with each slice of scores:
+//   kModeScores       store them (plain stores);
+//   kModeScoresExact  store them as exactly one buffer store per lane (the
+//                     output rows of a workgroup span less than 2 GiB), so
+//                     the number of vector-memory ops after each key
+//                     prefetch is fixed on every path;
+//   kModeGroupMax     (fused top-k, first pass) keep the maximum of each
+//                     16-key group of a row: the keys 4n .. 4n+3 of four
+//                     consecutive tiles that lane n holds;
+//   kModeCandidates   (fused top-k, second pass) append the cells at or
+//                     above the row's floor to the row's candidate list.
+constexpr int kModeScores = 0, kModeScoresExact = 1, kModeGroupMax = 2, kModeCandidates = 3;
+constexpr int kGroupTiles = 4;  // tiles per group in kModeGroupMax (columns per group row: 256)
+
+// Inclusive prefix sum within each 16-lane row of a wavefront (DPP
+// row_shr 1, 2, 4, 8 with zero fill).
+__device__ __forceinline__ uint32_t row16_inclusive_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    return x;
+}
+
+// Order-preserving key of a score (scores are >= +0 or -inf): 0 for -inf,
+// so every visible cell has a key above 0.
+__device__ __forceinline__ uint32_t score_key(float v) {
+    if (!(v > neg_inf())) return 0u;
+    uint32_t u = __float_as_uint(v);
+    if ((u << 1) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int kMode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillParams p) {
+    constexpr bool kExact = kMode == kModeScoresExact;
+    constexpr bool kFused = kMode == kModeGroupMax || kMode == kModeCandidates;
     // Two separate LDS objects (not one [2][...] array), so the compiler can
     // tell the buffer being read from the one being filled and does not wait
     // for the prefetch before reading the current tile.
@@ -151,9 +183,9 @@ void prefill_kernel(PrefillParams p) {
     // cover them (the loop's only vector-memory loads are the key prefetch).
     __builtin_amdgcn_s_waitcnt(0);
 
-    // Key staging goes straight from global memory to LDS
-    // (global_load_lds_dwordx4): one instruction moves 1 KB, lane l writing
-    // bytes 16l .. 16l+15 of the block.  Block b of a tile holds keys
+    // Key staging goes straight from global memory to LDS (buffer loads
+    // that write LDS): one instruction moves 1 KB, lane l writing bytes
+    // 16l .. 16l+15 of the block.  Block b of a tile holds keys
     // 4b .. 4b+3; lane l of block b therefore fetches key 4b + l/16, chunk
     // (l%16) ^ (b%16), which puts the XOR swizzle of lds_offset() in place.
     // Wave w stages blocks w*kBlocksPerWave .. +kBlocksPerWave-1.
@@ -201,6 +233,18 @@ void prefill_kernel(PrefillParams p) {
         }
         // Tiles inside [col_min, wave_lim) need no mask for any row of this wave.
         const int wave_lim = wave_min(lane_min_lim);
+
+        // Fused top-k state, per slice row of this lane.
+        float gm[4];        // kModeGroupMax: maximum of the open group
+        uint32_t fkey[4];   // kModeCandidates: the row's floor as a score key
+        int teq[4];         // kModeCandidates: keys equal to the floor seen in this chunk
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int row = row0 + wave * kRowsPerWave + 4 * mt + q4;
+            gm[mt] = neg_inf();
+            teq[mt] = 0;
+            fkey[mt] = (kMode == kModeCandidates && in_pass[mt]) ? score_key(p.floorv[row]) : 0u;
+        }
         const int col_min = clamp_cols(-(int64_t)cur, 0, INT_MAX - kBN);  // key index >= 0
 
         int n_compute = 0;
@@ -297,6 +341,66 @@ void prefill_kernel(PrefillParams p) {
                 store4(row_ptr[mt] + tile_c, p.out_vec, col, c_end, v[0], v[1], v[2], v[3]);
             }
         };
+        // Fused top-k epilogue of one slice (kModeGroupMax, kModeCandidates).
+        // `masked` is a literal at each call, so the unmasked form folds.
+        auto finish_topk = [&](int mt, int tile_c, bool masked, const f32x4 (&acc)[4]) {
+            if (tile_c < 0) return;  // placeholder before a pass's first tile
+            const int row = row0 + wave * kRowsPerWave + 4 * mt + q4;
+            const int col = tile_c + 4 * n;
+            f32x4 v;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = col + g;
+                const bool ok = in_pass[mt] && (!masked || (c < row_lim[mt] && c >= col_min && c < c_end));
+                v[g] = ok ? head_sum_score(acc[g], p.scale) : neg_inf();
+            }
+            if (kMode == kModeGroupMax) {
+                gm[mt] = max(gm[mt], max(max(v[0], v[1]), max(v[2], v[3])));
+                const int tix = tile_c / kBN;  // chunks start on group boundaries
+                if (tix % kGroupTiles == kGroupTiles - 1 || tile_c + kBN >= c_end) {
+                    if (in_pass[mt]) p.gmax[(int64_t)row * p.gmax_stride + (tix / kGroupTiles) * 16 + n] = gm[mt];
+                    gm[mt] = neg_inf();
+                }
+            } else {
+                // Cells above the floor, and the first `topk` cells equal to
+                // it in this chunk, in column order (lanes 16q4 .. 16q4+15
+                // hold this row's keys 4n .. 4n+3).
+                uint32_t kv[4];
+                int ngt = 0, neq = 0;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    kv[g] = score_key(v[g]);
+                    ngt += kv[g] > fkey[mt];
+                    neq += kv[g] == fkey[mt] && kv[g] != 0u;
+                }
+                const uint32_t packed = ((uint32_t)ngt << 16) | (uint32_t)neq;
+                const uint32_t incl = row16_inclusive_scan(packed);
+                const uint32_t excl = incl - packed;
+                const uint32_t tot = (uint32_t)__shfl((int)incl, (lane & 48) + 15, 64);
+                const int avail = max(p.topk - teq[mt], 0);
+                const int nw = (int)(tot >> 16) + min((int)(tot & 0xffffu), avail);
+                teq[mt] += (int)(tot & 0xffffu);
+                int base = 0;
+                if (n == 0 && nw > 0) base = atomicAdd(&p.cand_cnt[row], nw);
+                base = __shfl(base, lane & 48, 64);
+                int eqi = (int)(excl & 0xffffu);
+                int pos = base + (int)(excl >> 16) + min(eqi, avail);
+                const int64_t rbase = (int64_t)row * p.cand_cap;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const bool is_gt = kv[g] > fkey[mt];
+                    const bool is_eq = kv[g] == fkey[mt] && kv[g] != 0u;
+                    const bool take = is_gt || (is_eq && eqi < avail);
+                    if (take && pos < p.cand_cap) {
+                        p.cand_key[rbase + pos] = kv[g];
+                        p.cand_col[rbase + pos] = col + g;
+                    }
+                    pos += take;
+                    eqi += is_eq;
+                }
+            }
+        };
+
         // Software pipeline over slices: the epilogue and store of slice s
         // run while the matrix cores multiply slice s + 1, so vector ALU work
         // and stores hide under MFMA time.  Slice 3 of a tile is finished
@@ -322,9 +426,29 @@ void prefill_kernel(PrefillParams p) {
                 for (int g = 0; g < 4; ++g) b[ks][g] = *reinterpret_cast<const u32x4 *>(&tile[rd_off[ks] + g * kDim]);
         };
         auto do_tile = [&](int tile_c, const u32x4 (&b)[4][4]) {
-            const bool masked = !(tile_c + kBN <= wave_lim && tile_c >= col_min);
+            const bool masked = !(tile_c + kBN <= wave_lim && tile_c >= col_min) || (kFused && tile_c + kBN > c_end);
             const bool full = p.out_vec && tile_c + kBN <= c_end;
-            if (kExact && full && !masked && !prev_masked) {
+            if (kFused) {
+                if (!masked && !prev_masked) {
+                    multiply(0, b, accA);
+                    finish_topk(3, prev_c, false, accB);
+                    multiply(1, b, accB);
+                    finish_topk(0, tile_c, false, accA);
+                    multiply(2, b, accA);
+                    finish_topk(1, tile_c, false, accB);
+                    multiply(3, b, accB);
+                    finish_topk(2, tile_c, false, accA);
+                } else {
+                    multiply(0, b, accA);
+                    finish_topk(3, prev_c, prev_masked, accB);
+                    multiply(1, b, accB);
+                    finish_topk(0, tile_c, masked, accA);
+                    multiply(2, b, accA);
+                    finish_topk(1, tile_c, masked, accB);
+                    multiply(3, b, accB);
+                    finish_topk(2, tile_c, masked, accA);
+                }
+            } else if (kExact && full && !masked && !prev_masked) {
                 multiply(0, b, accA);
                 finish_fast(3, prev_c, accB);
                 interleave();
@@ -401,11 +525,40 @@ void prefill_kernel(PrefillParams p) {
             run_stage(it, ktile0, ktile1);
             if (it + kTilesPerStage < n_compute) run_stage(it + kTilesPerStage, ktile1, ktile0);
         }
-        if (prev_c >= 0) finish_general(3, prev_c, prev_masked, accB);
+        if (prev_c >= 0) {
+            if (kFused) finish_topk(3, prev_c, prev_masked, accB);
+            else finish_general(3, prev_c, prev_masked, accB);
+        }
+        if (kMode == kModeGroupMax) {
+            // Close the group the last computed tile left open, and give the
+            // chunk's groups past the last visible key -inf.
+            constexpr int kGroupCols = kGroupTiles * kBN;
+            int g_next = c_begin / kGroupCols;
+            if (n_compute > 0) {
+                const int last = c_begin / kBN + n_compute - 1;  // global tile index
+                const bool closed = last % kGroupTiles == kGroupTiles - 1 || (last + 1) * kBN >= c_end;
+                g_next = last / kGroupTiles + 1;
+                if (!closed) {
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        const int row = row0 + wave * kRowsPerWave + 4 * mt + q4;
+                        if (in_pass[mt]) p.gmax[(int64_t)row * p.gmax_stride + (last / kGroupTiles) * 16 + n] = gm[mt];
+                    }
+                }
+            }
+            const int g_end = (c_end + kGroupCols - 1) / kGroupCols;
+            for (int gi = g_next; gi < g_end; ++gi) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const int row = row0 + wave * kRowsPerWave + 4 * mt + q4;
+                    if (in_pass[mt]) p.gmax[(int64_t)row * p.gmax_stride + gi * 16 + n] = neg_inf();
+                }
+            }
+        }
 
-        // Tiles that no row of this pass can see: -inf only.
+        // Tiles that no row of this pass can see: -inf only (score modes).
         const float ni = neg_inf();
-        for (int it = n_compute; it < n_tiles; ++it) {
+        for (int it = n_compute; !kFused && it < n_tiles; ++it) {
             const int tile_c = c_begin + it * kBN;
             const int col = tile_c + 4 * n;
 #pragma unroll
@@ -443,8 +596,18 @@ int64_t prefill_max_k_stride() { return ((int64_t)1 << 30) / (2 * kBN * 2); }
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
-    if (p.exact_stores) return launch_kernel(prefill_kernel<true>, grid, dim3(kThreads), stream, p);
-    return launch_kernel(prefill_kernel<false>, grid, dim3(kThreads), stream, p);
+    if (p.exact_stores) return launch_kernel(prefill_kernel<kModeScoresExact>, grid, dim3(kThreads), stream, p);
+    return launch_kernel(prefill_kernel<kModeScores>, grid, dim3(kThreads), stream, p);
+}
+
+hipError_t launch_prefill_group_max(const PrefillParams &p, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
+    return launch_kernel(prefill_kernel<kModeGroupMax>, grid, dim3(kThreads), stream, p);
+}
+
+hipError_t launch_prefill_candidates(const PrefillParams &p, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
+    return launch_kernel(prefill_kernel<kModeCandidates>, grid, dim3(kThreads), stream, p);
 }
 
 int prefill_rows_per_block() { return kBM; }

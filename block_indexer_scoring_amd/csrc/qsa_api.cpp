@@ -50,6 +50,37 @@ int current_cu_count() {
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// Fused prefill top-k workspace: per row the maxima of 16-key groups, the
+// top-k group indices, the floor, the candidate count and the candidate
+// list (keys, columns).  The list holds every key above the floor (at most
+// 16 (k - 1)) and at most k keys equal to it per column chunk.
+constexpr int64_t kFusedMaxKStride = (int64_t)1 << 14;
+struct FusedLayout {
+    int chunk;
+    int64_t col_chunks, groups, cap;
+    int64_t off_gmax, off_sel, off_floor, off_cnt, off_key, off_col, total;
+};
+FusedLayout fused_layout(int32_t num_rows, int32_t out_cols, int32_t topk, int num_cus) {
+    FusedLayout L{};
+    // Column chunks on 256-column group boundaries; sized for the largest
+    // key stride accepted, so the same layout serves every call.
+    int chunk = qsa::prefill_col_chunk(num_rows, out_cols, kFusedMaxKStride, num_cus) / 256 * 256;
+    L.chunk = chunk < 256 ? 256 : chunk;
+    L.col_chunks = out_cols > 0 ? ((int64_t)out_cols + L.chunk - 1) / L.chunk : 0;
+    L.groups = 16 * (((int64_t)out_cols + 255) / 256);
+    L.cap = 16 * (int64_t)(topk - 1) + L.col_chunks * topk;
+    auto seg = [](int64_t b) { return (b + 255) / 256 * 256; };
+    int64_t o = 0;
+    L.off_gmax = o; o += seg((int64_t)num_rows * L.groups * 4);
+    L.off_sel = o; o += seg((int64_t)num_rows * topk * 4);
+    L.off_floor = o; o += seg((int64_t)num_rows * 4);
+    L.off_cnt = o; o += seg((int64_t)num_rows * 4);
+    L.off_key = o; o += seg((int64_t)num_rows * L.cap * 4);
+    L.off_col = o; o += seg((int64_t)num_rows * L.cap * 4);
+    L.total = o;
+    return L;
+}
+
 // Vector-load layout rule: 16-byte aligned base, and every axis with more
 // than one element has a positive stride that is a multiple of 8 bf16.
 bool axis_ok(int64_t size, int64_t stride) { return size <= 1 || (stride > 0 && stride % 8 == 0); }
@@ -267,6 +298,115 @@ int qsa_topk_blocks(const float *logits, int64_t logits_stride, int32_t num_rows
     qsa::TopkParams p{logits, logits_stride, num_rows, num_cols, k, out_idx, out_stride,
                       aligned(logits, 16) && logits_stride % 4 == 0};
     return device_status(fn, qsa::launch_topk(p, static_cast<hipStream_t>(stream), current_cu_count()));
+}
+
+int qsa_prefill_topk_workspace_bytes(int32_t num_rows, int32_t out_cols, int32_t topk, int64_t *bytes) {
+    const char *fn = "qsa_prefill_topk_workspace_bytes";
+    if (!bytes) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL bytes", fn);
+    if (num_rows < 0 || out_cols < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+    if (topk < 1 || topk > qsa::kFusedMaxK)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: topk must be in [1, %d], got %d", fn, qsa::kFusedMaxK, topk);
+    *bytes = fused_layout(num_rows, out_cols, topk, current_cu_count()).total;
+    return ok();
+}
+
+int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
+                         int64_t k_stride, int64_t num_keys, const int32_t *row_k_start,
+                         const int32_t *row_k_end, int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                         float scale, int32_t out_cols, int32_t topk, int32_t *out_idx, int64_t out_stride,
+                         void *workspace, int64_t workspace_bytes, void *stream) {
+    const char *fn = "qsa_mqa_prefill_topk";
+    int rc;
+    if ((rc = check_heads(fn, num_heads, head_dim))) return rc;
+    if ((rc = check_scale(fn, scale))) return rc;
+    if (num_rows < 0 || out_cols < 0 || num_keys < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+    if (topk < 1 || topk > qsa::kFusedMaxK)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: topk must be in [1, %d], got %d", fn, qsa::kFusedMaxK, topk);
+    if (out_stride < topk) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: out_stride < topk", fn);
+    if (num_rows == 0) return ok();
+    if (!out_idx || !workspace) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL out_idx or workspace", fn);
+    if (!aligned(out_idx, 4)) return fail(QSA_ERR_LAYOUT, "%s: out_idx must be 4-byte aligned", fn);
+    if (!aligned(workspace, 256)) return fail(QSA_ERR_LAYOUT, "%s: workspace must be 256-byte aligned", fn);
+    const int cus = current_cu_count();
+    const FusedLayout L = fused_layout(num_rows, out_cols, topk, cus);
+    if (workspace_bytes < L.total)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: workspace of %lld bytes, %lld needed", fn,
+                    (long long)workspace_bytes, (long long)L.total);
+    char *ws = static_cast<char *>(workspace);
+    qsa::FusedTopkParams fp{};
+    fp.num_rows = num_rows;
+    fp.k = topk;
+    fp.gmax = reinterpret_cast<float *>(ws + L.off_gmax);
+    fp.gmax_stride = (int32_t)L.groups;
+    fp.sel = reinterpret_cast<int32_t *>(ws + L.off_sel);
+    fp.floorv = reinterpret_cast<float *>(ws + L.off_floor);
+    fp.cand_key = reinterpret_cast<uint32_t *>(ws + L.off_key);
+    fp.cand_col = reinterpret_cast<int32_t *>(ws + L.off_col);
+    fp.cand_cnt = reinterpret_cast<int32_t *>(ws + L.off_cnt);
+    fp.cand_cap = (int32_t)L.cap;
+    fp.out = out_idx;
+    fp.out_stride = out_stride;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (out_cols == 0) {  // no columns: every row is -1
+        fp.cand_cnt = nullptr;
+        return device_status(fn, qsa::launch_topk_candidates(fp, st));
+    }
+    if (!q || !row_k_start || !row_k_end) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL q, row_k_start or row_k_end", fn);
+    if (num_keys > 0 && !k) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL k", fn);
+    if (!aligned(q, 16) || !axis_ok(num_rows, q_stride_row) || !axis_ok(4, q_stride_head) ||
+        (num_keys > 0 && (!aligned(k, 16) || !axis_ok(num_keys, k_stride))))
+        return fail(QSA_ERR_LAYOUT,
+                    "%s: q and k need a 16-byte aligned base and positive strides that are multiples "
+                    "of 8 elements on every axis longer than 1 (16-byte vector loads)", fn);
+    if (num_keys <= 1) k_stride = 128;
+    if (k_stride > kFusedMaxKStride)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: k_stride %lld exceeds %lld elements", fn, (long long)k_stride,
+                    (long long)kFusedMaxKStride);
+
+    qsa::PrefillParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.q_stride_row = q_stride_row;
+    p.q_stride_head = q_stride_head;
+    p.k = static_cast<const uint16_t *>(k);
+    p.k_stride = k_stride;
+    p.num_keys = num_keys;
+    p.row_k_start = row_k_start;
+    p.row_k_end = row_k_end;
+    p.num_rows = num_rows;
+    p.scale = scale;
+    p.out_cols = out_cols;
+    p.col_chunk = L.chunk;
+    p.row_blocks = (int32_t)((num_rows + qsa::prefill_rows_per_block() - 1) / qsa::prefill_rows_per_block());
+    p.col_chunks = (int32_t)L.col_chunks;
+    if ((int64_t)p.row_blocks * p.col_chunks >= INT32_MAX)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
+    p.topk = topk;
+    p.gmax = reinterpret_cast<float *>(ws + L.off_gmax);
+    p.gmax_stride = fp.gmax_stride;
+    p.floorv = fp.floorv;
+    p.cand_key = reinterpret_cast<uint32_t *>(ws + L.off_key);
+    p.cand_col = reinterpret_cast<int32_t *>(ws + L.off_col);
+    p.cand_cnt = fp.cand_cnt;
+    p.cand_cap = fp.cand_cap;
+    qsa::TopkParams tp{fp.gmax, L.groups, num_rows, (int32_t)L.groups, topk,
+                       reinterpret_cast<int32_t *>(ws + L.off_sel), topk, 1};
+
+    // Five launches; armed timing events span them (start on the first,
+    // stop on the last).
+    const qsa::LaunchEvents ev = g_launch_events;
+    auto arm = [&](bool first, bool last) {
+        g_launch_events = {first ? ev.start : nullptr, last ? ev.stop : nullptr};
+    };
+    arm(true, false);
+    hipError_t err = qsa::launch_prefill_group_max(p, st);
+    arm(false, false);
+    if (err == hipSuccess) err = qsa::launch_topk(tp, st, cus);
+    if (err == hipSuccess) err = qsa::launch_topk_floor(fp, st);
+    if (err == hipSuccess) err = qsa::launch_prefill_candidates(p, st);
+    arm(false, true);
+    if (err == hipSuccess) err = qsa::launch_topk_candidates(fp, st);
+    g_launch_events = ev;
+    return device_status(fn, err);
 }
 
 }  // extern "C"

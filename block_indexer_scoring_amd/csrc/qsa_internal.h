@@ -45,6 +45,15 @@ struct PrefillParams {
     int32_t row_blocks, col_chunks;
     int32_t out_vec;
     int32_t exact_stores;       // out_vec, and a row block's output spans < 2^31 bytes
+    // Fused top-k passes (qsa_mqa_prefill_topk); unused by the score kernel.
+    int32_t topk;
+    float *gmax;                // [rows][gmax_stride] maxima of 16-key groups
+    int32_t gmax_stride;        // groups per row: 16 * ceil(out_cols / 256)
+    const float *floorv;        // [rows] per-row floor
+    uint32_t *cand_key;         // [rows][cand_cap] candidate score keys
+    int32_t *cand_col;          // [rows][cand_cap] candidate columns
+    int32_t *cand_cnt;          // [rows] candidates appended
+    int32_t cand_cap;
 };
 
 struct TopkParams {
@@ -54,6 +63,22 @@ struct TopkParams {
     int32_t *out;
     int64_t out_stride;
     int32_t vec;                // logits rows may be read with 16-byte loads
+};
+
+// Fused prefill top-k: floor and final select (see topk.hip).
+constexpr int kFusedMaxK = 2048;
+struct FusedTopkParams {
+    int32_t num_rows, k;
+    const float *gmax;
+    int32_t gmax_stride;
+    const int32_t *sel;         // [rows][k] top-k group indices
+    float *floorv;              // [rows]
+    const uint32_t *cand_key;   // [rows][cand_cap]
+    const int32_t *cand_col;    // [rows][cand_cap]
+    int32_t *cand_cnt;          // [rows]
+    int32_t cand_cap;
+    int32_t *out;
+    int64_t out_stride;
 };
 
 struct MetaParams {
@@ -86,7 +111,11 @@ int prefill_col_chunk(int64_t num_rows, int32_t out_cols, int64_t k_stride, int 
 int64_t prefill_max_k_stride();  // larger key strides overflow the kernel's 32-bit key offsets
 int prefill_rows_per_block();
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_prefill_group_max(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_prefill_candidates(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus);
+hipError_t launch_topk_floor(const FusedTopkParams &p, hipStream_t stream);
+hipError_t launch_topk_candidates(const FusedTopkParams &p, hipStream_t stream);
 hipError_t launch_metadata(const MetaParams &p, hipStream_t stream);
 
 }  // namespace qsa

@@ -25,6 +25,8 @@
 // keys are re-read in full and two 8-bit passes finish T.  If the list would
 // overflow, the select runs over the row itself.  Longer rows are re-read
 // from memory in each phase.
+#include <climits>
+
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -560,6 +562,126 @@ __global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
     for (int i = picked + tid; i < p.k; i += kThreads) out[i] = -1;
 }
 
+// ---- Fused prefill top-k: the per-row floor and the final select. ----
+//
+// The fused path never writes the score matrix.  A first pass over the
+// scores keeps, per row, the maximum of each 16-key group; the k largest
+// group maxima are distinct keys, so at least k keys of the row are >= the
+// smallest of them, the floor F, and every key of the row's top k is >= F.
+// Keys > F can lie only in the fewer than k groups whose maximum is > F
+// (at most 16 (k-1) keys); of the keys equal to F only the lowest columns
+// can be picked, so each column chunk appends at most its first k of them.
+// A second pass appends those candidates to a per-row list, in any order
+// across chunks; the select below takes the exact top k of the list.
+
+// F per row: the smallest of the row's top-k group maxima, or -inf when
+// fewer than k groups hold a visible key (every visible key is then a
+// candidate).  Also clears the row's candidate count.  One wave per row.
+__global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+    if (row >= p.num_rows) return;  // wave-uniform
+    const int32_t *sel = p.sel + row * p.k;
+    const float *g = p.gmax + row * p.gmax_stride;
+    float m = __builtin_inff();
+    bool missing = false;
+    for (int j = lane; j < p.k; j += 64) {
+        const int c = sel[j];
+        if (c < 0) missing = true;
+        else m = fminf(m, g[c]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fminf(m, __shfl_xor(m, off, 64));
+    const bool any_missing = __ballot(missing) != 0ull;
+    if (lane == 0) {
+        p.floorv[row] = any_missing ? neg_inf() : m;
+        p.cand_cnt[row] = 0;
+    }
+}
+
+// The exact top k of one row's candidate list (score keys and columns, any
+// order): larger keys first, equal keys to the lower column; the picks are
+// written in ascending column order, -1 padded.  One workgroup per row.
+__global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p) {
+    constexpr int kThreads = 256;
+    __shared__ SelectShared sh;
+    __shared__ int picks[kFusedMaxK];
+    __shared__ int s_n;
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int n = p.cand_cnt ? min(p.cand_cnt[row], p.cand_cap) : 0;
+    const uint32_t *key = p.cand_key + row * p.cand_cap;
+    const int32_t *col = p.cand_col + row * p.cand_cap;
+    int32_t *out = p.out + row * p.out_stride;
+    const int k = p.k;
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    int npick;
+    if (n <= k) {
+        for (int i = tid; i < n; i += kThreads) picks[i] = col[i];
+        npick = n;
+    } else {
+        // T: the k-th largest key; `need` of the keys equal to T are picked.
+        int need;
+        const ListView list{key, col, n};
+        const RowView none{nullptr, 0, 0, 0};
+        const uint32_t T = radix_threshold<1, kFromList, kThreads>(list, none, k, 1u, sh, &need);
+        // The need lowest columns among the keys equal to T: radix select of
+        // the need-th largest 0x7fffffff - column over those entries.
+        uint32_t prefix = 0u, mask = 0u;
+        int kk = need;
+#pragma unroll 1
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+            const int nb = pass == 2 ? 1024 : 2048;
+            for (int b = tid; b < nb; b += kThreads) sh.hist[b] = 0;
+            __syncthreads();
+            for (int i = tid; i < n; i += kThreads) {
+                if (key[i] != T) continue;
+                const uint32_t ck = 0x7fffffffu - (uint32_t)col[i];
+                if ((ck & mask) == prefix) atomicAdd(&sh.hist[(ck >> shift) & (nb - 1)], 1);
+            }
+            __syncthreads();
+            int above;
+            const int bin = find_bin(sh, nb, kk, &above);
+            kk -= above;
+            prefix |= (uint32_t)bin << shift;
+            mask |= (uint32_t)(nb - 1) << shift;
+        }
+        const uint32_t last_col = 0x7fffffffu - prefix;  // highest picked column among the ties
+        for (int i = tid; i < n; i += kThreads) {
+            const uint32_t ki = key[i];
+            if (ki > T || (ki == T && (uint32_t)col[i] <= last_col)) {
+                const int slot = atomicAdd(&s_n, 1);  // exactly k picks; the bound only guards LDS
+                if (slot < kFusedMaxK) picks[slot] = col[i];
+            }
+        }
+        npick = k;
+    }
+    __syncthreads();
+    // Bitonic sort of the picks (padded to a power of two), ascending.
+    int size = 1;
+    while (size < npick) size <<= 1;
+    for (int i = npick + tid; i < size; i += kThreads) picks[i] = INT_MAX;
+    __syncthreads();
+    for (int len = 2; len <= size; len <<= 1) {
+        for (int stride = len >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < size / 2; i += kThreads) {
+                const int a = 2 * i - (i & (stride - 1));
+                const int b = a + stride;
+                const int x = picks[a], y = picks[b];
+                if ((x > y) == ((a & len) == 0)) {
+                    picks[a] = y;
+                    picks[b] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = tid; i < k; i += kThreads) out[i] = i < npick ? picks[i] : -1;
+}
+
 template <int E, int THREADS, int WPE>
 hipError_t launch_resident(const TopkParams &p, hipStream_t stream) {
     return launch_kernel(topk_resident_kernel<E, THREADS, WPE>, dim3((unsigned)p.num_rows),
@@ -577,6 +699,14 @@ hipError_t launch_config(const TopkParams &p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_topk_floor(const FusedTopkParams &p, hipStream_t stream) {
+    return launch_kernel(topk_floor_kernel, dim3((unsigned)((p.num_rows + 3) / 4)), dim3(256), stream, p);
+}
+
+hipError_t launch_topk_candidates(const FusedTopkParams &p, hipStream_t stream) {
+    return launch_kernel(topk_candidates_kernel, dim3((unsigned)p.num_rows), dim3(256), stream, p);
+}
 
 hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus) {
     if (p.num_cols > 32768)  // longer than the register-resident shapes hold

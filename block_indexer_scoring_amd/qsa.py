@@ -21,10 +21,11 @@ QSA_ERR_INVALID_ARGUMENT = 1
 QSA_ERR_UNSUPPORTED = 2
 QSA_ERR_LAYOUT = 3
 QSA_ERR_DEVICE = 4
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_set_launch_events", "qsa_split_batch",
-           "qsa_build_metadata", "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks")
+           "qsa_build_metadata", "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks",
+           "qsa_mqa_prefill_topk", "qsa_prefill_topk_workspace_bytes")
 
 DEFAULT_SCALE = 1.0 / math.sqrt(128.0)
 
@@ -66,6 +67,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_mqa_prefill.restype = ctypes.c_int
     lib.qsa_topk_blocks.argtypes = [P, i64, i32, i32, i32, P, i64, P]
     lib.qsa_topk_blocks.restype = ctypes.c_int
+    lib.qsa_mqa_prefill_topk.argtypes = [P, i64, i64, P, i64, i64, P, P, i32, i32, i32, f32, i32, i32,
+                                         P, i64, P, i64, P]
+    lib.qsa_mqa_prefill_topk.restype = ctypes.c_int
+    lib.qsa_prefill_topk_workspace_bytes.argtypes = [i32, i32, i32, P]
+    lib.qsa_prefill_topk_workspace_bytes.restype = ctypes.c_int
     if lib.qsa_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libqsa ABI {lib.qsa_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -248,4 +254,51 @@ def qsa_topk_blocks(logits: torch.Tensor, k: int, out: torch.Tensor | None = Non
         raise ValueError("out must be [T, k] with unit column stride")
     _check(lib.qsa_topk_blocks(_ptr(logits), logits.stride(0), rows, cols, int(k), _ptr(out),
                                out.stride(0), _stream_handle(stream)))
+    return out
+
+
+def qsa_prefill_topk_workspace_bytes(num_rows: int, out_cols: int, topk: int) -> int:
+    """Workspace bytes qsa_mqa_prefill_topk needs on the current device."""
+    lib = load_library()
+    n = ctypes.c_int64(0)
+    _check(lib.qsa_prefill_topk_workspace_bytes(int(num_rows), int(out_cols), int(topk), ctypes.byref(n)))
+    return int(n.value)
+
+
+def qsa_mqa_prefill_topk(q: torch.Tensor, k: torch.Tensor, row_k_start: torch.Tensor,
+                         row_k_end: torch.Tensor, out_cols: int, topk: int,
+                         scale: float = DEFAULT_SCALE, out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Prefill scores and per-row top-k in one call, without the score matrix:
+    int32 [T, topk], equal to qsa_topk_blocks(qsa_mqa_prefill(...), topk).
+    workspace: uint8 device tensor of at least qsa_prefill_topk_workspace_bytes
+    bytes (allocated here when not given)."""
+    lib = load_library()
+    _gpu("q", q, torch.bfloat16)
+    _gpu("k", k, torch.bfloat16)
+    _gpu("row_k_start", row_k_start, torch.int32)
+    _gpu("row_k_end", row_k_end, torch.int32)
+    if q.dim() != 3 or k.dim() != 2:
+        raise ValueError("q must be [T, H, D] and k [NK, D]")
+    num_rows, heads, dim = q.shape
+    if (q.stride(2) != 1 and dim > 1) or (k.stride(1) != 1 and k.shape[1] > 1):
+        raise QSAError(QSA_ERR_LAYOUT, "q and k need unit feature stride")
+    if k.shape[1] != dim:
+        raise ValueError("q and k head_dim differ")
+    for name, t in (("row_k_start", row_k_start), ("row_k_end", row_k_end)):
+        if t.numel() != num_rows or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [T] tensor")
+    if out is None:
+        out = torch.empty((num_rows, topk), dtype=torch.int32, device=q.device)
+    _gpu("out", out, torch.int32)
+    if out.dim() != 2 or out.shape[0] != num_rows or out.shape[1] != topk or (topk > 1 and out.stride(1) != 1):
+        raise ValueError("out must be [T, topk] with unit column stride")
+    need = qsa_prefill_topk_workspace_bytes(num_rows, out_cols, topk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _gpu("workspace", workspace, torch.uint8)
+    _check(lib.qsa_mqa_prefill_topk(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.shape[0], _ptr(row_k_start),
+        _ptr(row_k_end), num_rows, heads, dim, float(scale), int(out_cols), int(topk), _ptr(out),
+        out.stride(0), _ptr(workspace), workspace.numel(), _stream_handle(stream)))
     return out

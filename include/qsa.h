@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 
 enum qsa_status {
     QSA_OK = 0,
@@ -182,7 +182,9 @@ int qsa_mqa_decode(const void *q, int64_t q_stride_req, int64_t q_stride_row,
  *                (an empty or reversed interval masks the whole row).
  *   out        : device fp32 [num_rows][out_cols], row stride out_stride
  *                (>= out_cols), 4-byte aligned; every cell is written.
- *   Errors: as qsa_mqa_decode, plus LAYOUT when q or k breaks the layout rule.
+ *   Errors: as qsa_mqa_decode, plus LAYOUT when q or k breaks the layout rule,
+ *   and UNSUPPORTED for k_stride above 4,194,304 elements (the kernel's key
+ *   offsets are 32-bit).
  */
 int qsa_mqa_prefill(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
                     int64_t k_stride, int64_t num_keys, const int32_t *row_k_start,
@@ -208,6 +210,52 @@ int qsa_mqa_prefill(const void *q, int64_t q_stride_row, int64_t q_stride_head, 
 int qsa_topk_blocks(const float *logits, int64_t logits_stride, int32_t num_rows,
                     int32_t num_cols, int32_t k, int32_t *out_idx, int64_t out_stride,
                     void *stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_mqa_prefill_topk -- prefill scores and per-row top-k in one call,
+ *   without writing the fp32 score matrix.
+ *   Source: the two operations above (MATE "QSA (Qwen Sparse Attention)",
+ *   sections "MQA score" and "Core Attention"), composed; keeping the
+ *   logits workspace out of the prefill step is the motivation in the vLLM
+ *   pull request "[Qwen3.8-Flash-Next] Separate prefill and decode paths
+ *   for QSA indexer", section "Main changes" (chunked prefill bounds a
+ *   512 MiB logits workspace).
+ *   Result: out_idx equals qsa_topk_blocks(k = topk) applied to the
+ *   out_cols-wide output of qsa_mqa_prefill with the same arguments, bit for
+ *   bit (the same scores; ties to the lower column; ascending; -1 padded).
+ *   q, k, row_k_start, row_k_end, num_rows, num_heads, head_dim, scale,
+ *   out_cols : as qsa_mqa_prefill; k_stride at most 16,384 elements.
+ *   topk       : 1 .. 2048.
+ *   out_idx    : device int32 [num_rows][topk], row stride out_stride (>= topk).
+ *   workspace  : device memory of at least qsa_prefill_topk_workspace_bytes
+ *                bytes, 256-byte aligned, owned by the caller; its contents
+ *                on entry do not matter and are clobbered.  About
+ *                num_rows * (8 * (16 * (topk - 1) + 2 * topk) + out_cols / 4)
+ *                bytes at the usual sizes, of which a call touches a few
+ *                percent.
+ *   The call enqueues five kernels on stream (a group-maximum pass over the
+ *   scores, a top-k over the group maxima, the per-row floor, a candidate
+ *   pass over the scores, the final select); with timing events armed the
+ *   start event marks the first kernel's begin and the stop event the last
+ *   kernel's end.
+ *   Errors: as qsa_mqa_prefill (UNSUPPORTED also for k_stride > 16,384),
+ *   INVALID_ARGUMENT for topk outside [1, 2048], out_stride < topk, a NULL
+ *   out_idx or workspace, or a workspace below the size needed; LAYOUT for a
+ *   misaligned out_idx or workspace.
+ */
+int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
+                         int64_t k_stride, int64_t num_keys, const int32_t *row_k_start,
+                         const int32_t *row_k_end, int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                         float scale, int32_t out_cols, int32_t topk, int32_t *out_idx, int64_t out_stride,
+                         void *workspace, int64_t workspace_bytes, void *stream);
+
+/* qsa_prefill_topk_workspace_bytes -- workspace size qsa_mqa_prefill_topk
+ *   needs for these sizes on the current device (host only; the column
+ *   split depends on the device's compute-unit count).
+ *   Errors: INVALID_ARGUMENT for a NULL bytes, negative sizes or topk
+ *   outside [1, 2048].
+ */
+int qsa_prefill_topk_workspace_bytes(int32_t num_rows, int32_t out_cols, int32_t topk, int64_t *bytes);
 
 #ifdef __cplusplus
 }

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.qsa_abi_version() == 1
+    assert lib.qsa_abi_version() == 2
 
 
 def test_launch_events_set_and_clear_without_device(lib):
@@ -137,6 +137,51 @@ def _prefill(lib, **kw):
 def test_prefill_rejects(lib, kw, code, text):
     assert _prefill(lib, **kw) == code
     assert text in _err(lib)
+
+
+def _fused(lib, **kw):
+    a = dict(q=FAKE, sq=512, sh=128, k=FAKE, sk=128, nk=100, ks=FAKE, ke=FAKE, rows=10, heads=4,
+             dim=128, scale=0.088, out_cols=100, topk=16, out=FAKE, out_stride=16, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.qsa_mqa_prefill_topk(a["q"], a["sq"], a["sh"], a["k"], a["sk"], a["nk"], a["ks"], a["ke"],
+                                    a["rows"], a["heads"], a["dim"], a["scale"], a["out_cols"], a["topk"],
+                                    a["out"], a["out_stride"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(heads=2), 2, "(4, 128)"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(topk=0), 1, "topk"),
+    (dict(topk=2049, out_stride=4096), 1, "topk"),
+    (dict(out_stride=15), 1, "out_stride"),
+    (dict(rows=-1), 1, "negative"),
+    (dict(out=None), 1, "NULL"),
+    (dict(ws=None), 1, "NULL"),
+    (dict(out=FAKE + 2), 3, "aligned"),
+    (dict(ws=FAKE + 16), 3, "256-byte"),
+    (dict(ws_bytes=1000), 1, "needed"),
+    (dict(q=None), 1, "NULL"),
+    (dict(k=FAKE + 4), 3, "16-byte"),
+    (dict(sk=(1 << 14) + 8), 2, "k_stride"),
+])
+def test_fused_prefill_topk_rejects(lib, kw, code, text):
+    assert _fused(lib, **kw) == code
+    assert text in _err(lib)
+
+
+def test_fused_prefill_topk_zero_rows_and_workspace_size(lib):
+    assert _fused(lib, rows=0, q=None, out=None, ws=None) == 0
+    n = ctypes.c_int64(-1)
+    assert lib.qsa_prefill_topk_workspace_bytes(8192, 27048, 512, ctypes.byref(n)) == 0
+    # Group maxima, top-k group indices and two candidate arrays of
+    # 16 (k - 1) + chunks * k entries per row, each a few bytes per entry.
+    assert 8192 * 8 * (16 * 511 + 512) < n.value < 8192 * (8 * (16 * 511 + 8 * 512) + 27048)
+    m = ctypes.c_int64(-1)
+    assert lib.qsa_prefill_topk_workspace_bytes(100, 27048, 512, ctypes.byref(m)) == 0
+    assert 0 < m.value < n.value
+    assert lib.qsa_prefill_topk_workspace_bytes(100, 1000, 0, ctypes.byref(m)) == 1
+    assert lib.qsa_prefill_topk_workspace_bytes(100, 1000, 16, None) == 1
+    assert lib.qsa_prefill_topk_workspace_bytes(-1, 1000, 16, ctypes.byref(m)) == 1
 
 
 def test_prefill_layout_exemptions_for_single_element_axes(lib):

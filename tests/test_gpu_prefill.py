@@ -82,7 +82,7 @@ def test_prefill_small_full(T, NK, cols):
 
 
 def test_prefill_mixed_starts_in_one_workgroup():
-    # Packed requests whose boundaries fall inside 64-row workgroups, plus
+    # Packed requests whose boundaries fall inside workgroups, plus
     # negative starts, reversed and empty intervals and ends past the keys.
     rng = np.random.default_rng(21)
     T, NK, cols = 200, 900, 420
