@@ -135,6 +135,12 @@ void prefill_kernel(PrefillParams p) {
     __shared__ int s_end[kBM];  // min(row_k_end, num_keys)
     __shared__ int s_done[kBM];
     __shared__ int s_cur, s_lim;
+    // kModeCandidates, per row of the workgroup: the floor key, the segment's
+    // offset and size in the row's candidate pool, keys equal to the floor
+    // seen so far in this chunk, and candidates written.
+    __shared__ uint32_t c_fkey[kFused ? kBM : 1];
+    __shared__ int c_seg0[kFused ? kBM : 1], c_segn[kFused ? kBM : 1], c_teq[kFused ? kBM : 1],
+        c_ncand[kFused ? kBM : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -236,14 +242,21 @@ void prefill_kernel(PrefillParams p) {
 
         // Fused top-k state, per slice row of this lane.
         float gm[4];        // kModeGroupMax: maximum of the open group
-        uint32_t fkey[4];   // kModeCandidates: the row's floor as a score key
-        int teq[4];         // kModeCandidates: keys equal to the floor seen in this chunk
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int row = row0 + wave * kRowsPerWave + 4 * mt + q4;
-            gm[mt] = neg_inf();
-            teq[mt] = 0;
-            fkey[mt] = (kMode == kModeCandidates && in_pass[mt]) ? score_key(p.floorv[row]) : 0u;
+        for (int mt = 0; mt < 4; ++mt) gm[mt] = neg_inf();
+        if (kMode == kModeCandidates) {
+            for (int i = tid; i < kBM; i += kThreads) {
+                const int row = row0 + i;
+                const bool cand = !s_done[i] && s_start[i] == cur;
+                const int32_t *so = p.seg_off + (int64_t)row * (p.col_chunks + 1) + cc;
+                const int s0 = cand ? min(so[0], p.pool_cap) : 0;
+                c_fkey[i] = cand ? p.floor_key[row] : 0u;
+                c_seg0[i] = s0;
+                c_segn[i] = cand ? min(so[1], p.pool_cap) - s0 : 0;  // within the pool in any case
+                c_teq[i] = 0;
+                c_ncand[i] = 0;
+            }
+            __syncthreads();
         }
         const int col_min = clamp_cols(-(int64_t)cur, 0, INT_MAX - kBN);  // key index >= 0
 
@@ -363,37 +376,41 @@ void prefill_kernel(PrefillParams p) {
                 }
             } else {
                 // Cells above the floor, and the first `topk` cells equal to
-                // it in this chunk, in column order (lanes 16q4 .. 16q4+15
-                // hold this row's keys 4n .. 4n+3).
+                // it in this chunk, appended in column order to the row's
+                // segment for this chunk (lanes 16q4 .. 16q4+15 hold this
+                // row's keys 4n .. 4n+3).
+                const int ri = wave * kRowsPerWave + 4 * mt + q4;  // row in the workgroup
+                const uint32_t fk = c_fkey[ri];
                 uint32_t kv[4];
                 int ngt = 0, neq = 0;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     kv[g] = score_key(v[g]);
-                    ngt += kv[g] > fkey[mt];
-                    neq += kv[g] == fkey[mt] && kv[g] != 0u;
+                    ngt += kv[g] > fk;
+                    neq += kv[g] == fk && kv[g] != 0u;
                 }
                 const uint32_t packed = ((uint32_t)ngt << 16) | (uint32_t)neq;
                 const uint32_t incl = row16_inclusive_scan(packed);
                 const uint32_t excl = incl - packed;
                 const uint32_t tot = (uint32_t)__shfl((int)incl, (lane & 48) + 15, 64);
-                const int avail = max(p.topk - teq[mt], 0);
+                const int teq = c_teq[ri], nc = c_ncand[ri], segn = c_segn[ri];
+                const int avail = max(p.topk - teq, 0);
                 const int nw = (int)(tot >> 16) + min((int)(tot & 0xffffu), avail);
-                teq[mt] += (int)(tot & 0xffffu);
-                int base = 0;
-                if (n == 0 && nw > 0) base = atomicAdd(&p.cand_cnt[row], nw);
-                base = __shfl(base, lane & 48, 64);
                 int eqi = (int)(excl & 0xffffu);
-                int pos = base + (int)(excl >> 16) + min(eqi, avail);
-                const int64_t rbase = (int64_t)row * p.cand_cap;
+                int pos = nc + (int)(excl >> 16) + min(eqi, avail);
+                if (n == 0) {  // one lane per row keeps the row's counters
+                    c_teq[ri] = teq + (int)(tot & 0xffffu);
+                    c_ncand[ri] = nc + nw;
+                }
+                const int64_t sbase = (int64_t)row * p.pool_cap + c_seg0[ri];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const bool is_gt = kv[g] > fkey[mt];
-                    const bool is_eq = kv[g] == fkey[mt] && kv[g] != 0u;
+                    const bool is_gt = kv[g] > fk;
+                    const bool is_eq = kv[g] == fk && kv[g] != 0u;
                     const bool take = is_gt || (is_eq && eqi < avail);
-                    if (take && pos < p.cand_cap) {
-                        p.cand_key[rbase + pos] = kv[g];
-                        p.cand_col[rbase + pos] = col + g;
+                    if (take && pos < segn) {
+                        p.cand_key[sbase + pos] = kv[g];
+                        p.cand_col[sbase + pos] = col + g;
                     }
                     pos += take;
                     eqi += is_eq;
@@ -528,6 +545,11 @@ void prefill_kernel(PrefillParams p) {
         if (prev_c >= 0) {
             if (kFused) finish_topk(3, prev_c, prev_masked, accB);
             else finish_general(3, prev_c, prev_masked, accB);
+        }
+        if (kMode == kModeCandidates) {
+            __syncthreads();  // every wave's last counter updates are in LDS
+            for (int i = tid; i < kBM; i += kThreads)
+                if (!s_done[i] && s_start[i] == cur) p.cand_cnt[(int64_t)(row0 + i) * p.col_chunks + cc] = c_ncand[i];
         }
         if (kMode == kModeGroupMax) {
             // Close the group the last computed tile left open, and give the

@@ -1,5 +1,6 @@
 // C ABI of the QSA MQA indexer: argument checks (host arguments only, never
 // device contents), error text, and dispatch to the gfx950 kernels.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -51,14 +52,16 @@ int current_cu_count() {
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 // Fused prefill top-k workspace: per row the maxima of 16-key groups, the
-// top-k group indices, the floor, the candidate count and the candidate
-// list (keys, columns).  The list holds every key above the floor (at most
-// 16 (k - 1)) and at most k keys equal to it per column chunk.
+// floor key, the offsets of the column chunks' segments in the row's
+// candidate pool, a candidate count per chunk, and the pool (keys,
+// columns).  The pool holds every key above the floor (at most 16 (k - 1))
+// and at most k keys equal to it per chunk, so it never overflows; the
+// floor kernel sizes each segment from the group maxima.
 constexpr int64_t kFusedMaxKStride = (int64_t)1 << 14;
 struct FusedLayout {
     int chunk;
-    int64_t col_chunks, groups, cap;
-    int64_t off_gmax, off_sel, off_floor, off_cnt, off_key, off_col, total;
+    int64_t col_chunks, groups, pool_cap;
+    int64_t off_gmax, off_floor, off_segoff, off_cnt, off_key, off_col, total;
 };
 FusedLayout fused_layout(int32_t num_rows, int32_t out_cols, int32_t topk, int num_cus) {
     FusedLayout L{};
@@ -67,16 +70,20 @@ FusedLayout fused_layout(int32_t num_rows, int32_t out_cols, int32_t topk, int n
     int chunk = qsa::prefill_col_chunk(num_rows, out_cols, kFusedMaxKStride, num_cus) / 256 * 256;
     L.chunk = chunk < 256 ? 256 : chunk;
     L.col_chunks = out_cols > 0 ? ((int64_t)out_cols + L.chunk - 1) / L.chunk : 0;
+    if (L.col_chunks > qsa::kFusedMaxSegs) {  // wide rows: fewer, wider chunks
+        L.chunk = (int)((((int64_t)out_cols + qsa::kFusedMaxSegs - 1) / qsa::kFusedMaxSegs + 255) / 256 * 256);
+        L.col_chunks = ((int64_t)out_cols + L.chunk - 1) / L.chunk;
+    }
     L.groups = 16 * (((int64_t)out_cols + 255) / 256);
-    L.cap = 16 * (int64_t)(topk - 1) + L.col_chunks * topk;
+    L.pool_cap = 16 * (int64_t)(topk - 1) + L.col_chunks * topk;
     auto seg = [](int64_t b) { return (b + 255) / 256 * 256; };
     int64_t o = 0;
     L.off_gmax = o; o += seg((int64_t)num_rows * L.groups * 4);
-    L.off_sel = o; o += seg((int64_t)num_rows * topk * 4);
     L.off_floor = o; o += seg((int64_t)num_rows * 4);
-    L.off_cnt = o; o += seg((int64_t)num_rows * 4);
-    L.off_key = o; o += seg((int64_t)num_rows * L.cap * 4);
-    L.off_col = o; o += seg((int64_t)num_rows * L.cap * 4);
+    L.off_segoff = o; o += seg((int64_t)num_rows * (L.col_chunks + 1) * 4);
+    L.off_cnt = o; o += seg((int64_t)num_rows * L.col_chunks * 4);
+    L.off_key = o; o += seg((int64_t)num_rows * L.pool_cap * 4);
+    L.off_col = o; o += seg((int64_t)num_rows * L.pool_cap * 4);
     L.total = o;
     return L;
 }
@@ -338,12 +345,14 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     fp.k = topk;
     fp.gmax = reinterpret_cast<float *>(ws + L.off_gmax);
     fp.gmax_stride = (int32_t)L.groups;
-    fp.sel = reinterpret_cast<int32_t *>(ws + L.off_sel);
-    fp.floorv = reinterpret_cast<float *>(ws + L.off_floor);
+    fp.floor_key = reinterpret_cast<uint32_t *>(ws + L.off_floor);
     fp.cand_key = reinterpret_cast<uint32_t *>(ws + L.off_key);
     fp.cand_col = reinterpret_cast<int32_t *>(ws + L.off_col);
     fp.cand_cnt = reinterpret_cast<int32_t *>(ws + L.off_cnt);
-    fp.cand_cap = (int32_t)L.cap;
+    fp.seg_off = reinterpret_cast<int32_t *>(ws + L.off_segoff);
+    fp.segs = (int32_t)L.col_chunks;
+    fp.groups_per_seg = L.chunk / 16;
+    fp.pool_cap = (int32_t)L.pool_cap;
     fp.out = out_idx;
     fp.out_stride = out_stride;
     const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -362,6 +371,8 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     if (k_stride > kFusedMaxKStride)
         return fail(QSA_ERR_UNSUPPORTED, "%s: k_stride %lld exceeds %lld elements", fn, (long long)k_stride,
                     (long long)kFusedMaxKStride);
+    if (((int64_t)L.chunk + 64) * k_stride * 2 > ((int64_t)1 << 30))  // 32-bit key offsets per chunk
+        return fail(QSA_ERR_UNSUPPORTED, "%s: rows of %d columns are too wide", fn, out_cols);
 
     qsa::PrefillParams p{};
     p.q = static_cast<const uint16_t *>(q);
@@ -383,15 +394,14 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     p.topk = topk;
     p.gmax = reinterpret_cast<float *>(ws + L.off_gmax);
     p.gmax_stride = fp.gmax_stride;
-    p.floorv = fp.floorv;
+    p.floor_key = fp.floor_key;
     p.cand_key = reinterpret_cast<uint32_t *>(ws + L.off_key);
     p.cand_col = reinterpret_cast<int32_t *>(ws + L.off_col);
-    p.cand_cnt = fp.cand_cnt;
-    p.cand_cap = fp.cand_cap;
-    qsa::TopkParams tp{fp.gmax, L.groups, num_rows, (int32_t)L.groups, topk,
-                       reinterpret_cast<int32_t *>(ws + L.off_sel), topk, 1};
+    p.cand_cnt = reinterpret_cast<int32_t *>(ws + L.off_cnt);
+    p.seg_off = fp.seg_off;
+    p.pool_cap = fp.pool_cap;
 
-    // Five launches; armed timing events span them (start on the first,
+    // Four launches; armed timing events span them (start on the first,
     // stop on the last).
     const qsa::LaunchEvents ev = g_launch_events;
     auto arm = [&](bool first, bool last) {
@@ -400,7 +410,6 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     arm(true, false);
     hipError_t err = qsa::launch_prefill_group_max(p, st);
     arm(false, false);
-    if (err == hipSuccess) err = qsa::launch_topk(tp, st, cus);
     if (err == hipSuccess) err = qsa::launch_topk_floor(fp, st);
     if (err == hipSuccess) err = qsa::launch_prefill_candidates(p, st);
     arm(false, true);

@@ -49,11 +49,12 @@ struct PrefillParams {
     int32_t topk;
     float *gmax;                // [rows][gmax_stride] maxima of 16-key groups
     int32_t gmax_stride;        // groups per row: 16 * ceil(out_cols / 256)
-    const float *floorv;        // [rows] per-row floor
-    uint32_t *cand_key;         // [rows][cand_cap] candidate score keys
-    int32_t *cand_col;          // [rows][cand_cap] candidate columns
-    int32_t *cand_cnt;          // [rows] candidates appended
-    int32_t cand_cap;
+    const uint32_t *floor_key;  // [rows] per-row floor (score key)
+    const int32_t *seg_off;     // [rows][col_chunks + 1] segment offsets in the row's pool
+    uint32_t *cand_key;         // [rows][pool_cap] candidate score keys
+    int32_t *cand_col;          // [rows][pool_cap] candidate columns
+    int32_t *cand_cnt;          // [rows][col_chunks] candidates per segment
+    int32_t pool_cap;
 };
 
 struct TopkParams {
@@ -67,16 +68,19 @@ struct TopkParams {
 
 // Fused prefill top-k: floor and final select (see topk.hip).
 constexpr int kFusedMaxK = 2048;
+constexpr int kFusedMaxSegs = 256;   // column chunks per row
 struct FusedTopkParams {
     int32_t num_rows, k;
     const float *gmax;
-    int32_t gmax_stride;
-    const int32_t *sel;         // [rows][k] top-k group indices
-    float *floorv;              // [rows]
-    const uint32_t *cand_key;   // [rows][cand_cap]
-    const int32_t *cand_col;    // [rows][cand_cap]
-    int32_t *cand_cnt;          // [rows]
-    int32_t cand_cap;
+    int32_t gmax_stride;        // groups per row
+    uint32_t *floor_key;        // [rows] the floor as a score key
+    int32_t *seg_off;           // [rows][segs + 1] segment offsets in the row's pool
+    const uint32_t *cand_key;   // [rows][pool_cap]
+    const int32_t *cand_col;    // [rows][pool_cap]
+    const int32_t *cand_cnt;    // [rows][segs]
+    int32_t segs;               // column chunks
+    int32_t groups_per_seg;     // groups per column chunk
+    int32_t pool_cap;
     int32_t *out;
     int64_t out_stride;
 };

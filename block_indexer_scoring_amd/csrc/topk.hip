@@ -565,121 +565,241 @@ __global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
 // ---- Fused prefill top-k: the per-row floor and the final select. ----
 //
 // The fused path never writes the score matrix.  A first pass over the
-// scores keeps, per row, the maximum of each 16-key group; the k largest
-// group maxima are distinct keys, so at least k keys of the row are >= the
-// smallest of them, the floor F, and every key of the row's top k is >= F.
-// Keys > F can lie only in the fewer than k groups whose maximum is > F
-// (at most 16 (k-1) keys); of the keys equal to F only the lowest columns
-// can be picked, so each column chunk appends at most its first k of them.
-// A second pass appends those candidates to a per-row list, in any order
-// across chunks; the select below takes the exact top k of the list.
+// scores keeps, per row, the maximum of each 16-key group.  The k-th largest
+// group maximum is the floor F: at least k keys of the row are >= F, so every
+// key of the row's top k is >= F; and keys > F can lie only in the fewer
+// than k groups whose maximum is > F (at most 16 (k-1) keys).  Of the keys
+// equal to F only the lowest columns can be picked, so each column chunk
+// keeps at most its first k of them.  A second pass writes those candidates,
+// per (row, column chunk) segment in column order, and the select below
+// takes the exact top k of the concatenated segments (column order), which
+// is the top k of the row.
 
-// F per row: the smallest of the row's top-k group maxima, or -inf when
-// fewer than k groups hold a visible key (every visible key is then a
-// candidate).  Also clears the row's candidate count.  One wave per row.
+// F per row as a score key: the k-th largest group maximum, or 0 (every
+// visible key is a candidate) when fewer than k groups hold a visible key.
+// One wave per row, an exact radix select over the keys' 11 + 11 + 10 bits.
+// Then each column chunk's room in the row's candidate pool: 16 per group
+// whose maximum is above F (every key in it may be), plus the keys equal to
+// F it may keep, at most k and at most 16 per group whose maximum is >= F.
+// These sum to at most 16 (k - 1) + chunks * k, the pool's size.
 __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
+    __shared__ __attribute__((aligned(16))) int hist[4][2048];
+    __shared__ int groups_gt[4][kFusedMaxSegs], groups_eq[4][kFusedMaxSegs];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-    if (row >= p.num_rows) return;  // wave-uniform
-    const int32_t *sel = p.sel + row * p.k;
+    if (row >= p.num_rows) return;  // wave-uniform; this wave works alone below
     const float *g = p.gmax + row * p.gmax_stride;
-    float m = __builtin_inff();
-    bool missing = false;
-    for (int j = lane; j < p.k; j += 64) {
-        const int c = sel[j];
-        if (c < 0) missing = true;
-        else m = fminf(m, g[c]);
-    }
+    int *h = hist[wave];
+    uint32_t prefix = 0u, mask = 0u;
+    int kk = p.k;
+    bool found = true;
+    // Rows of up to 64 * kFloorRegs groups keep their keys in registers
+    // (lane l: groups l, l + 64, ...), loaded all at once; longer rows are
+    // read from memory in each pass.
+    constexpr int kFloorRegs = 32;
+    const bool in_regs = p.gmax_stride <= 64 * kFloorRegs;
+    uint32_t rk[kFloorRegs];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fminf(m, __shfl_xor(m, off, 64));
-    const bool any_missing = __ballot(missing) != 0ull;
-    if (lane == 0) {
-        p.floorv[row] = any_missing ? neg_inf() : m;
-        p.cand_cnt[row] = 0;
+    for (int j = 0; j < kFloorRegs; ++j) {
+        const int i = lane + 64 * j;
+        rk[j] = (in_regs && i < p.gmax_stride) ? order_key(g[i]) : 0u;
     }
+    // One wave: its LDS operations take effect in issue order.
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nb = pass == 2 ? 1024 : 2048;
+        for (int b = lane; b < nb; b += 64) h[b] = 0;
+        if (in_regs) {
+#pragma unroll
+            for (int j = 0; j < kFloorRegs; ++j) {
+                const uint32_t key = rk[j];
+                if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & (nb - 1)], 1);
+            }
+        } else {
+            for (int i = lane; i < p.gmax_stride; i += 64) {
+                const uint32_t key = order_key(g[i]);
+                if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & (nb - 1)], 1);
+            }
+        }
+        int above;
+        const int bin = nb == 2048 ? wave_find_bin<2048>(h, kk, &above) : wave_find_bin<1024>(h, kk, &above);
+        if (bin < 0) {  // fewer than k visible group maxima
+            found = false;
+            break;
+        }
+        kk -= above;
+        prefix |= (uint32_t)bin << shift;
+        mask |= (uint32_t)(nb - 1) << shift;
+    }
+    const uint32_t T = found ? prefix : 0u;
+    if (lane == 0) p.floor_key[row] = T;
+    int *cgt = groups_gt[wave], *ceq = groups_eq[wave];
+    for (int sg = lane; sg < p.segs; sg += 64) {
+        cgt[sg] = 0;
+        ceq[sg] = 0;
+    }
+    if (in_regs) {
+#pragma unroll
+        for (int j = 0; j < kFloorRegs; ++j) {
+            const int i = lane + 64 * j;
+            const uint32_t key = rk[j];
+            if (i < p.gmax_stride) {
+                const int sg = i / p.groups_per_seg;
+                if (key > T) atomicAdd(&cgt[sg], 1);
+                else if (key == T && key != 0u) atomicAdd(&ceq[sg], 1);
+            }
+        }
+    } else {
+        for (int i = lane; i < p.gmax_stride; i += 64) {
+            const uint32_t key = order_key(g[i]);
+            const int sg = i / p.groups_per_seg;
+            if (key > T) atomicAdd(&cgt[sg], 1);
+            else if (key == T && key != 0u) atomicAdd(&ceq[sg], 1);
+        }
+    }
+    int32_t *off = p.seg_off + row * (p.segs + 1);
+    int run = 0;
+    for (int s0 = 0; s0 < p.segs; s0 += 64) {
+        const int sg = s0 + lane;
+        int room = 0;
+        if (sg < p.segs) room = 16 * cgt[sg] + min(p.k, 16 * (cgt[sg] + ceq[sg]));
+        const int incl = (int)wave_inclusive_scan((uint32_t)room);
+        if (sg < p.segs) off[sg] = run + incl - room;
+        run += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) off[p.segs] = run;
 }
 
-// The exact top k of one row's candidate list (score keys and columns, any
-// order): larger keys first, equal keys to the lower column; the picks are
-// written in ascending column order, -1 padded.  One workgroup per row.
+// The exact top k of one row's candidates: larger keys first, equal keys to
+// the lower column (the earlier position, segments being in column order);
+// the picks are written in ascending column order, -1 padded.  Lists of up
+// to kFusedListCap entries are staged in LDS and reuse the row select above;
+// longer ones are read in place.  One workgroup per row.
+constexpr int kFusedListCap = 2048;
 __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p) {
     constexpr int kThreads = 256;
     __shared__ SelectShared sh;
-    __shared__ int picks[kFusedMaxK];
-    __shared__ int s_n;
+    __shared__ uint32_t lkey[kFusedListCap];
+    __shared__ int lcol[kFusedListCap];
+    __shared__ int seg_start[kFusedMaxSegs + 1];
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
-    const int n = p.cand_cnt ? min(p.cand_cnt[row], p.cand_cap) : 0;
-    const uint32_t *key = p.cand_key + row * p.cand_cap;
-    const int32_t *col = p.cand_col + row * p.cand_cap;
     int32_t *out = p.out + row * p.out_stride;
     const int k = p.k;
-    if (tid == 0) s_n = 0;
-    __syncthreads();
-    int npick;
+    const int segs = p.segs;
+    const int64_t rbase = row * (int64_t)p.pool_cap;
+    const uint32_t *gkey = p.cand_key + rbase;
+    const int32_t *gcol = p.cand_col + rbase;
+    const int32_t *off = p.seg_off + row * (segs + 1);
+    __shared__ int seg_base[kFusedMaxSegs];
+    {
+        // Candidates written per segment, never more than the segment's room.
+        const int c = (p.cand_cnt && tid < segs) ? min(p.cand_cnt[row * segs + tid], off[tid + 1] - off[tid]) : 0;
+        if (tid < segs) seg_base[tid] = off[tid];
+        int total;
+        const int before = block_exclusive_scan<kThreads>(c, sh.wave_tmp, &total);
+        if (tid < segs) seg_start[tid] = before;
+        if (tid == 0) seg_start[segs] = total;
+        __syncthreads();
+    }
+    const int n = seg_start[segs];
+    // Index into the row's region of candidate number pos (column order).
+    auto locate = [&](int pos) {
+        int lo = 0, hi = segs - 1;  // the last segment starting at or before pos
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (seg_start[mid] <= pos) lo = mid;
+            else hi = mid - 1;
+        }
+        return (int64_t)seg_base[lo] + (pos - seg_start[lo]);
+    };
     if (n <= k) {
-        for (int i = tid; i < n; i += kThreads) picks[i] = col[i];
-        npick = n;
-    } else {
-        // T: the k-th largest key; `need` of the keys equal to T are picked.
+        for (int pos = tid; pos < k; pos += kThreads) out[pos] = pos < n ? gcol[locate(pos)] : -1;
+        return;
+    }
+    const RowView none{nullptr, 0, 0, 0};
+    if (n <= kFusedListCap) {
+        for (int pos = tid; pos < n; pos += kThreads) {
+            const int64_t e = locate(pos);
+            lkey[pos] = gkey[e];
+            lcol[pos] = gcol[e];
+        }
+        __syncthreads();
+        const ListView list{lkey, lcol, n};
         int need;
-        const ListView list{key, col, n};
-        const RowView none{nullptr, 0, 0, 0};
         const uint32_t T = radix_threshold<1, kFromList, kThreads>(list, none, k, 1u, sh, &need);
-        // The need lowest columns among the keys equal to T: radix select of
-        // the need-th largest 0x7fffffff - column over those entries.
-        uint32_t prefix = 0u, mask = 0u;
-        int kk = need;
+        const int per = (n + kThreads - 1) / kThreads;
+        const int lo = min(tid * per, n), hi = min(lo + per, n);
+        place_picks<1, kFromList, kThreads>(list, none, lo, hi, T, need, out, sh);
+        return;
+    }
+    // Long lists, read in place: the same radix select, counting segment by
+    // segment, then placement over contiguous position slices.
+    uint32_t prefix = 0u, mask = 0u;
+    int kk = k;
 #pragma unroll 1
-        for (int pass = 0; pass < 3; ++pass) {
-            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-            const int nb = pass == 2 ? 1024 : 2048;
-            for (int b = tid; b < nb; b += kThreads) sh.hist[b] = 0;
-            __syncthreads();
-            for (int i = tid; i < n; i += kThreads) {
-                if (key[i] != T) continue;
-                const uint32_t ck = 0x7fffffffu - (uint32_t)col[i];
-                if ((ck & mask) == prefix) atomicAdd(&sh.hist[(ck >> shift) & (nb - 1)], 1);
-            }
-            __syncthreads();
-            int above;
-            const int bin = find_bin(sh, nb, kk, &above);
-            kk -= above;
-            prefix |= (uint32_t)bin << shift;
-            mask |= (uint32_t)(nb - 1) << shift;
-        }
-        const uint32_t last_col = 0x7fffffffu - prefix;  // highest picked column among the ties
-        for (int i = tid; i < n; i += kThreads) {
-            const uint32_t ki = key[i];
-            if (ki > T || (ki == T && (uint32_t)col[i] <= last_col)) {
-                const int slot = atomicAdd(&s_n, 1);  // exactly k picks; the bound only guards LDS
-                if (slot < kFusedMaxK) picks[slot] = col[i];
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nb = pass == 2 ? 1024 : 2048;
+        for (int b = tid; b < nb; b += kThreads) sh.hist[b] = 0;
+        __syncthreads();
+        for (int sgi = 0; sgi < segs; ++sgi) {
+            const int cnt = seg_start[sgi + 1] - seg_start[sgi];
+            const uint32_t *sk = gkey + seg_base[sgi];
+            for (int i = tid; i < cnt; i += kThreads) {
+                const uint32_t key = sk[i];
+                if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1);
             }
         }
-        npick = k;
+        __syncthreads();
+        int above;
+        const int bin = find_bin(sh, nb, kk, &above);
+        kk -= above;
+        prefix |= (uint32_t)bin << shift;
+        mask |= (uint32_t)(nb - 1) << shift;
     }
-    __syncthreads();
-    // Bitonic sort of the picks (padded to a power of two), ascending.
-    int size = 1;
-    while (size < npick) size <<= 1;
-    for (int i = npick + tid; i < size; i += kThreads) picks[i] = INT_MAX;
-    __syncthreads();
-    for (int len = 2; len <= size; len <<= 1) {
-        for (int stride = len >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < size / 2; i += kThreads) {
-                const int a = 2 * i - (i & (stride - 1));
-                const int b = a + stride;
-                const int x = picks[a], y = picks[b];
-                if ((x > y) == ((a & len) == 0)) {
-                    picks[a] = y;
-                    picks[b] = x;
-                }
-            }
-            __syncthreads();
+    const uint32_t T = prefix;
+    const int need = kk;
+    const int per = (n + kThreads - 1) / kThreads;
+    const int lo = min(tid * per, n), hi = min(lo + per, n);
+    int gt = 0, eq = 0;
+    // The segment holding position pos (the last one starting at or before it).
+    auto seg_of = [&](int pos) {
+        int a = 0, b = segs - 1;
+        while (a < b) {
+            const int mid = (a + b + 1) >> 1;
+            if (seg_start[mid] <= pos) a = mid;
+            else b = mid - 1;
+        }
+        return a;
+    };
+    if (lo < hi) {
+        int sgi = seg_of(lo);
+        for (int pos = lo; pos < hi; ++pos) {
+            while (pos >= seg_start[sgi + 1]) ++sgi;
+            const uint32_t key = gkey[(int64_t)seg_base[sgi] + (pos - seg_start[sgi])];
+            gt += key > T;
+            eq += key == T;
         }
     }
-    for (int i = tid; i < k; i += kThreads) out[i] = i < npick ? picks[i] : -1;
+    int gt_total, eq_total;
+    int gt_before = block_exclusive_scan<kThreads>(gt, sh.wave_tmp, &gt_total);
+    int eq_before = block_exclusive_scan<kThreads>(eq, sh.wave_tmp, &eq_total);
+    if (lo < hi) {
+        int sgi = seg_of(lo);
+        for (int pos = lo; pos < hi; ++pos) {
+            while (pos >= seg_start[sgi + 1]) ++sgi;
+            const int64_t e = (int64_t)seg_base[sgi] + (pos - seg_start[sgi]);
+            const uint32_t key = gkey[e];
+            const bool is_gt = key > T, is_eq = key == T;
+            if (is_gt) out[gt_before + min(eq_before, need)] = gcol[e];
+            else if (is_eq && eq_before < need) out[gt_before + eq_before] = gcol[e];
+            gt_before += is_gt;
+            eq_before += is_eq;
+        }
+    }
 }
 
 template <int E, int THREADS, int WPE>
