@@ -31,6 +31,7 @@ these formulas to the GB/s and TFLOP/s printed there.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -372,6 +373,35 @@ def main(argv=None) -> int:
         "decode_bytes": dbytes, "prefill_bytes": pbytes, "prefill_flops": pflops,
         "topk_prefill_bytes": tk_bytes,
     }
+
+    # The fused prefill top-k on the same prefill rows, for context: its
+    # time (first kernel's begin to last kernel's end), the unfused pair's,
+    # and whether its picks equal the step's own top-k of the prefill rows.
+    nws = ctypes.c_int64(0)
+    check(lib.qsa_prefill_topk_workspace_bytes(T_pre, pre.out_cols, TOPK, ctypes.byref(nws)))
+    fz_ws = torch.empty(nws.value, dtype=torch.uint8, device=dev)
+    fz_top = torch.empty_like(pre_top)
+    fz_ev = [HipEvents(2) for _ in range(5)]
+    for j in range(6):
+        if j > 0:
+            check(lib.qsa_set_launch_events(fz_ev[j - 1].ev[0], fz_ev[j - 1].ev[1]))
+        check(lib.qsa_mqa_prefill_topk(
+            q_pre.data_ptr(), q_pre.stride(0), q_pre.stride(1), k_pre.data_ptr(), k_pre.stride(0),
+            k_pre.shape[0], meta["row_k_start"].data_ptr() + 4 * T_dec,
+            meta["row_k_end"].data_ptr() + 4 * T_dec, T_pre, 4, 128, scale, pre.out_cols, TOPK,
+            fz_top.data_ptr(), TOPK, fz_ws.data_ptr(), nws.value, sh))
+        check(lib.qsa_set_launch_events(None, None))
+    torch.cuda.synchronize()
+    fz_us = [e.elapsed_us(0, 1) for e in fz_ev]
+    for e in fz_ev:
+        e.close()
+    result["prefill_topk_fused"] = {
+        "us": round(float(np.mean(fz_us)), 3),
+        "unfused_us": round(avg["prefill"] + avg["topk_prefill"], 3),
+        "workspace_bytes": int(nws.value),
+        "matches_unfused": bool(torch.equal(fz_top, pre_top)),
+    }
+    del fz_ws
 
     # A measured bandwidth for context: a plain 1 GiB device-to-device copy
     # (read + write bytes over its time), and each HBM-bound kernel's rate as
