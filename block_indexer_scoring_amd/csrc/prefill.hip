@@ -144,7 +144,7 @@ void prefill_kernel(PrefillParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15;
     const int q4 = lane >> 4;
     // Workgroup i runs on XCD i % 8.  Renumber so that the workgroups of
@@ -158,6 +158,31 @@ void prefill_kernel(PrefillParams p) {
     const int c_begin = cc * p.col_chunk;
     const int c_end = min(c_begin + p.col_chunk, p.out_cols);
     const int n_tiles = (c_end - c_begin + kBN - 1) / kBN;
+
+    // Line-aligned stores (kModeScoresExact).  A row that starts partway
+    // into a 128-byte line would have every 256-byte tile segment straddle
+    // three lines, two of them partly written, which costs HBM write
+    // throughput.  So the 16 rows of a wave are spaced `dl` rows apart,
+    // which puts all of them at the same offset within a line (dl * row
+    // pitch is a multiple of 128 bytes), and each lane's columns are rotated
+    // by that offset: lane n computes tile columns 4*((n - rot) mod 16) ..
+    // +3 (B fragments read rotated), and the store of a slice covers the
+    // line-aligned columns tile_c - 4*rot .. tile_c + 63 - 4*rot.  Lanes
+    // n < rot store the previous tile's cells, which they still hold.  With
+    // the other modes, or a row pitch that is a multiple of 128 bytes,
+    // dl = 1 and rot = 0.
+    int dl = 1;
+    if (kExact) {
+        const int u = (int)((p.out_stride >> 2) & 7);  // 16-byte units per row, mod 8
+        dl = u == 0 ? 1 : ((u & 1) ? 8 : ((u & 2) ? 4 : 2));
+    }
+    const int a_w = (wave % dl) + kRowsPerWave * dl * (wave / dl);  // wave row j is a_w + dl * j
+    const int rot = kExact ? __builtin_amdgcn_readfirstlane(
+                                 (int)((((uintptr_t)p.out + (uint64_t)(row0 + a_w) * (uint64_t)p.out_stride * 4) >> 4) & 7))
+                           : 0;
+    const int lc = 4 * ((n - rot) & 15);  // first tile column of this lane's cells
+    const int sc = 4 * (n - rot);         // first column of this lane's store, relative to the tile
+    const bool lo = n < rot;              // stores the previous tile's cells
 
     for (int i = tid; i < kBM; i += kThreads) {
         const int t = row0 + i;
@@ -179,7 +204,7 @@ void prefill_kernel(PrefillParams p) {
     u32x4 qa[4][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        const int t = row0 + wave * kRowsPerWave + 4 * mt + (n >> 2);
+        const int t = row0 + a_w + dl * (4 * mt + (n >> 2));
         const uint16_t *src = p.q + (int64_t)t * p.q_stride_row + (int64_t)(n & 3) * p.q_stride_head + 8 * q4;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -202,10 +227,10 @@ void prefill_kernel(PrefillParams p) {
         const int key = 4 * b + (lane >> 4);
         st_goff[i] = (uint32_t)(key * p.k_stride * 2 + (((lane & 15) ^ (b & 15)) << 4));
     }
-    // B-fragment read offsets: key 4n + g, chunk 4ks + q4; g adds 128 elements.
+    // B-fragment read offsets: key lc + g, chunk 4ks + q4; g adds 128 elements.
     int rd_off[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) rd_off[ks] = lds_offset(4 * n, 4 * ks + q4);
+    for (int ks = 0; ks < 4; ++ks) rd_off[ks] = lds_offset(lc, 4 * ks + q4);
 
     for (;;) {
         if (tid == 0) {
@@ -227,14 +252,12 @@ void prefill_kernel(PrefillParams p) {
         // This lane's output rows (MFMA result layout: row 4mt + q4).
         bool in_pass[4];
         int row_lim[4];
-        float *row_ptr[4];
         int lane_min_lim = INT_MAX;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const int idx = wave * kRowsPerWave + 4 * mt + q4;
+            const int idx = a_w + dl * (4 * mt + q4);
             in_pass[mt] = !s_done[idx] && s_start[idx] == cur;
             row_lim[mt] = clamp_cols((int64_t)s_end[idx] - cur, -1, INT_MAX - kBN);
-            row_ptr[mt] = p.out + (int64_t)(row0 + idx) * p.out_stride + 4 * n;
             if (in_pass[mt]) lane_min_lim = min(lane_min_lim, row_lim[mt]);
         }
         // Tiles inside [col_min, wave_lim) need no mask for any row of this wave.
@@ -303,12 +326,25 @@ void prefill_kernel(PrefillParams p) {
             p.out + (int64_t)row0 * p.out_stride, 0,
             kExact ? (int)((int64_t)min(kBM, p.num_rows - row0) * p.out_stride * 4) : 0, kBufferWord3);
         constexpr uint32_t kDropped = 0x80000000u;
-        uint32_t row_boff[4];  // byte offset of (row, column 4n) in out_rsrc
+        // Byte offset of (row, column sc) in out_rsrc, modulo 2^32: it is
+        // negative for row 0 and lanes n < rot, whose stores then lie at
+        // least one tile in (the first tile's are dropped).
+        uint32_t row_boff[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const int idx = wave * kRowsPerWave + 4 * mt + q4;
-            row_boff[mt] = in_pass[mt] ? (uint32_t)(((int64_t)idx * p.out_stride + 4 * n) * 4) : kDropped;
+            const int idx = a_w + dl * (4 * mt + q4);
+            row_boff[mt] = in_pass[mt] ? (uint32_t)(((int64_t)idx * p.out_stride + sc) * 4) : kDropped;
         }
+        // Element offset of (row of slice mt, column col) from out_wg, for the
+        // plain stores of partial and -inf-only tiles.
+        float *const out_wg = p.out + (int64_t)row0 * p.out_stride;
+        auto row_elem = [&](int mt, int col) {
+            return (int64_t)(a_w + dl * (4 * mt + q4)) * p.out_stride + col;
+        };
+        // kModeScoresExact: the cells of the previous tile, per slice.
+        f32x4 keep[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) keep[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // Scores of one slice: rows 4mt .. 4mt+3 of the wave (x 4 heads, the
         // MFMA's m = 4 * row + head) against the tile's 64 keys.
@@ -325,8 +361,10 @@ void prefill_kernel(PrefillParams p) {
         auto finish_fast = [&](int mt, int tile_c, const f32x4 (&acc)[4]) {
             const f32x4 v{head_sum_score(acc[0], p.scale), head_sum_score(acc[1], p.scale),
                           head_sum_score(acc[2], p.scale), head_sum_score(acc[3], p.scale)};
-            __builtin_amdgcn_raw_buffer_store_b128(v, out_rsrc, tile_c >= 0 ? row_boff[mt] : kDropped,
-                                                   4 * max(tile_c, 0), 0);
+            const f32x4 w = lo ? keep[mt] : v;
+            keep[mt] = v;
+            const bool drop = tile_c < 0 || (lo && tile_c == c_begin);
+            __builtin_amdgcn_raw_buffer_store_b128(w, out_rsrc, drop ? kDropped : row_boff[mt] + 4 * tile_c, 0, 0);
         };
         // Any slice: mask per cell, partial tiles and unbounded rows.
         auto finish_general = [&](int mt, int tile_c, bool masked, const f32x4 (&acc)[4]) {
@@ -335,31 +373,35 @@ void prefill_kernel(PrefillParams p) {
                 v = f32x4{head_sum_score(acc[0], p.scale), head_sum_score(acc[1], p.scale),
                           head_sum_score(acc[2], p.scale), head_sum_score(acc[3], p.scale)};
             } else {
-                const int col = tile_c + 4 * n;
+                const int col = tile_c + lc;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int c = col + g;
                     v[g] = (c < row_lim[mt] && c >= col_min) ? head_sum_score(acc[g], p.scale) : neg_inf();
                 }
             }
-            const int col = tile_c + 4 * n;
             if (kExact) {
                 // Lanes wholly inside the chunk take the buffer store; the one
                 // lane that straddles the chunk's end stores its cells singly.
+                const f32x4 w = lo ? keep[mt] : v;
+                keep[mt] = v;
+                const int cs = tile_c + sc;
+                const bool drop = tile_c < 0 || (lo && tile_c == c_begin);
                 __builtin_amdgcn_raw_buffer_store_b128(
-                    v, out_rsrc, (tile_c >= 0 && col + 3 < c_end) ? row_boff[mt] : kDropped, 4 * max(tile_c, 0), 0);
-                if (tile_c >= 0 && in_pass[mt] && col < c_end && col + 3 >= c_end)
-                    store4(row_ptr[mt] + tile_c, false, col, c_end, v[0], v[1], v[2], v[3]);
+                    w, out_rsrc, (!drop && cs + 3 < c_end) ? row_boff[mt] + 4 * tile_c : kDropped, 0, 0);
+                if (!drop && in_pass[mt] && cs < c_end && cs + 3 >= c_end)
+                    store4(out_wg + row_elem(mt, cs), false, cs, c_end, w[0], w[1], w[2], w[3]);
             } else if (tile_c >= 0 && in_pass[mt]) {
-                store4(row_ptr[mt] + tile_c, p.out_vec, col, c_end, v[0], v[1], v[2], v[3]);
+                const int col = tile_c + 4 * n;
+                store4(out_wg + row_elem(mt, col), p.out_vec, col, c_end, v[0], v[1], v[2], v[3]);
             }
         };
         // Fused top-k epilogue of one slice (kModeGroupMax, kModeCandidates).
         // `masked` is a literal at each call, so the unmasked form folds.
         auto finish_topk = [&](int mt, int tile_c, bool masked, const f32x4 (&acc)[4]) {
             if (tile_c < 0) return;  // placeholder before a pass's first tile
-            const int row = row0 + wave * kRowsPerWave + 4 * mt + q4;
-            const int col = tile_c + 4 * n;
+            const int row = row0 + a_w + dl * (4 * mt + q4);
+            const int col = tile_c + lc;
             f32x4 v;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -379,7 +421,7 @@ void prefill_kernel(PrefillParams p) {
                 // it in this chunk, appended in column order to the row's
                 // segment for this chunk (lanes 16q4 .. 16q4+15 hold this
                 // row's keys 4n .. 4n+3).
-                const int ri = wave * kRowsPerWave + 4 * mt + q4;  // row in the workgroup
+                const int ri = a_w + dl * (4 * mt + q4);  // row in the workgroup
                 const uint32_t fk = c_fkey[ri];
                 uint32_t kv[4];
                 int ngt = 0, neq = 0;
@@ -546,6 +588,15 @@ void prefill_kernel(PrefillParams p) {
             if (kFused) finish_topk(3, prev_c, prev_masked, accB);
             else finish_general(3, prev_c, prev_masked, accB);
         }
+        if (kExact && n_compute > 0 && lo) {
+            // The last segment's end: columns end - 4*rot .. end - 1 of the
+            // last computed tile, held by lanes n < rot.
+            const int cs = c_begin + n_compute * kBN + sc;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                if (in_pass[mt] && cs < c_end)
+                    store4(out_wg + row_elem(mt, cs), true, cs, c_end, keep[mt][0], keep[mt][1], keep[mt][2], keep[mt][3]);
+        }
         if (kMode == kModeCandidates) {
             __syncthreads();  // every wave's last counter updates are in LDS
             for (int i = tid; i < kBM; i += kThreads)
@@ -563,7 +614,7 @@ void prefill_kernel(PrefillParams p) {
                 if (!closed) {
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) {
-                        const int row = row0 + wave * kRowsPerWave + 4 * mt + q4;
+                        const int row = row0 + a_w + dl * (4 * mt + q4);
                         if (in_pass[mt]) p.gmax[(int64_t)row * p.gmax_stride + (last / kGroupTiles) * 16 + n] = gm[mt];
                     }
                 }
@@ -572,7 +623,7 @@ void prefill_kernel(PrefillParams p) {
             for (int gi = g_next; gi < g_end; ++gi) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
-                    const int row = row0 + wave * kRowsPerWave + 4 * mt + q4;
+                    const int row = row0 + a_w + dl * (4 * mt + q4);
                     if (in_pass[mt]) p.gmax[(int64_t)row * p.gmax_stride + gi * 16 + n] = neg_inf();
                 }
             }
@@ -585,7 +636,7 @@ void prefill_kernel(PrefillParams p) {
             const int col = tile_c + 4 * n;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
-                if (in_pass[mt]) store4(row_ptr[mt] + tile_c, p.out_vec, col, c_end, ni, ni, ni, ni);
+                if (in_pass[mt]) store4(out_wg + row_elem(mt, col), p.out_vec, col, c_end, ni, ni, ni, ni);
         }
 
         __syncthreads();

@@ -128,6 +128,36 @@ def test_prefill_strided_inputs_and_out():
     assert np.all(host[:, 0] == 9.0) and np.all(host[:, 334:] == 9.0)
 
 
+@pytest.mark.parametrize("pad", [0, 4, 8, 16])
+def test_prefill_any_row_pitch_and_base(pad):
+    """Line-aligned stores: rows are spaced so that a wave's rows share their
+    offset within a 128-byte line, and lanes are rotated by that offset.
+    Every row pitch residue (mod 32 floats) and several base offsets, over
+    4 column chunks, 2 passes per workgroup, a ragged last tile and rows cut
+    short (tiles that are -inf only); the cells around the view must stay
+    untouched."""
+    rng = np.random.default_rng(23)
+    T, NK, cols = 300, 2600, 2000
+    q = normal_bf16(rng, (T, 4, 128))
+    k = normal_bf16(rng, (NK, 128))
+    ks = np.where(np.arange(T) < 150, 0, 40).astype(np.int32)  # two starts in the second row block
+    ke = (ks + rng.integers(0, cols + 50, T)).astype(np.int32)
+    ke[:10] = ks[:10] + cols                                     # full rows
+    ref = O.prefill(q, k, ks, ke, cols)
+    stride = cols + pad
+    for base in (0, 4, 12, 28):                                  # floats: 0, 16, 48, 112 bytes into a line
+        buf = torch.full((T * stride + 64,), 5.0, dtype=torch.float32, device="cuda")
+        out = buf[base:base + T * stride].view(T, stride)[:, :cols]
+        _gpu(q, k, ks, ke, cols, out=out, poison=False)
+        assert_scores_match(out, ref, f"stride {stride} base +{base}")
+        host = buf.cpu().numpy()
+        inside = np.zeros(host.shape, bool)
+        idx = base + np.arange(T)[:, None] * stride + np.arange(cols)[None, :]
+        inside[idx.ravel()] = True
+        assert np.all(host[~inside] == 5.0), f"stride {stride} base +{base}: write outside the view"
+
+
+
 def test_prefill_onehot_bit_exact_and_scale():
     a = np.array([1.0, -1.0, 2.0, 0.5], np.float32)
     q = np.zeros((3, 4, 128), np.float32)
