@@ -62,6 +62,13 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_prefill.restype = None
     lib.oracle_topk.argtypes = [P, i64, i32, i32, P, i64, i32, i32]
     lib.oracle_topk.restype = ctypes.c_int
+    f64 = ctypes.c_double
+    lib.oracle_decode_typed.argtypes = [P, ctypes.c_int, i64, i64, i64, P, ctypes.c_int, f64, i64,
+                                        i32, P, i64, i32, P, P, i32, i32, f32, P, i64, i32, i32, i32]
+    lib.oracle_decode_typed.restype = None
+    lib.oracle_prefill_typed.argtypes = [P, ctypes.c_int, i64, i64, P, ctypes.c_int, f64, i64, i64,
+                                         P, P, i32, f32, P, i64, i32, i32, i32]
+    lib.oracle_prefill_typed.restype = None
     return lib
 
 
@@ -266,6 +273,85 @@ def prefill(q_bits, k_bits, row_k_start, row_k_end, out_cols: int, scale: float 
         lib.oracle_prefill(_ptr(q), sq, sh, _ptr(k), sk, k.shape[0], _ptr(ks), _ptr(ke),
                            num_rows, scale, out.ctypes.data + dst_row * out_cols * 4,
                            out_cols, out_cols, row_begin, row_end)
+
+    if sel is None:
+        _run_rows(lambda b, e: call(b, e, b), num_rows, threads)
+    else:
+        _run_rows(lambda b, e: [call(int(sel[i]), int(sel[i]) + 1, i) for i in range(b, e)],
+                  len(sel), threads)
+    return out
+
+
+# Element formats of the typed functions: name -> (code, numpy container dtype).
+FORMATS = {"bf16": (0, np.uint16), "fp16": (1, np.uint16), "fp8_e4m3": (2, np.uint8)}
+
+
+def _typed(bits, fmt):
+    code, container = FORMATS[fmt]
+    a = np.asarray(bits)
+    assert a.dtype == container, f"{fmt} elements are {np.dtype(container).name} bit patterns"
+    return code, a
+
+
+def decode_typed(q_bits, q_format: str, k_pool_bits, k_format: str, page_table, comp_lens_arr,
+                 visible, out_cols: int, k_scale: float = 1.0, scale: float | None = None,
+                 rows=None, threads: int | None = None):
+    """decode() for typed elements: q in "bf16" or "fp16", the key pool in
+    "bf16", "fp16" or "fp8_e4m3" (bit patterns: uint16, or uint8 for fp8).
+    An fp8 key element stands for its value times k_scale."""
+    lib = load()
+    qf, q = _typed(q_bits, q_format)
+    assert q.ndim == 4 and q.shape[2:] == (HEADS, DIM) and q.strides[3] == q.itemsize
+    kf, kp = _typed(k_pool_bits, k_format)
+    kp = np.ascontiguousarray(kp)
+    assert kp.ndim == 4 and kp.shape[2:] == (1, DIM)
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    cl = np.ascontiguousarray(comp_lens_arr, dtype=np.int32)
+    vis = None if visible is None else np.ascontiguousarray(visible, dtype=np.int32)
+    num_reqs, dql = q.shape[0], q.shape[1]
+    sr, sj, sh = (st // q.itemsize for st in q.strides[:3])
+    scale = default_scale() if scale is None else float(scale)
+    total = num_reqs * dql
+    sel = _row_list(rows, total)
+    out = np.empty((total if sel is None else len(sel), out_cols), np.float32)
+
+    def call(row_begin, row_end, dst_row):
+        lib.oracle_decode_typed(_ptr(q), qf, sr, sj, sh, _ptr(kp), kf, float(k_scale), kp.shape[0],
+                                kp.shape[1], _ptr(pt), pt.shape[1], pt.shape[1], _ptr(cl), _ptr(vis),
+                                num_reqs, dql, scale, out.ctypes.data + dst_row * out_cols * 4,
+                                out_cols, out_cols, row_begin, row_end)
+
+    if sel is None:
+        _run_rows(lambda b, e: call(b, e, b), total, threads)
+    else:
+        _run_rows(lambda b, e: [call(int(sel[i]), int(sel[i]) + 1, i) for i in range(b, e)],
+                  len(sel), threads)
+    return out
+
+
+def prefill_typed(q_bits, q_format: str, k_bits, k_format: str, row_k_start, row_k_end,
+                  out_cols: int, k_scale: float = 1.0, scale: float | None = None, rows=None,
+                  threads: int | None = None):
+    """prefill() for typed elements (formats as in decode_typed)."""
+    lib = load()
+    qf, q = _typed(q_bits, q_format)
+    assert q.ndim == 3 and q.shape[1:] == (HEADS, DIM) and q.strides[2] == q.itemsize
+    kf, k = _typed(k_bits, k_format)
+    assert k.ndim == 2 and k.shape[1] == DIM and k.strides[1] == k.itemsize
+    ks = np.ascontiguousarray(row_k_start, dtype=np.int32)
+    ke = np.ascontiguousarray(row_k_end, dtype=np.int32)
+    num_rows = q.shape[0]
+    scale = default_scale() if scale is None else float(scale)
+    sq, sh = q.strides[0] // q.itemsize, q.strides[1] // q.itemsize
+    sk = k.strides[0] // k.itemsize
+    sel = _row_list(rows, num_rows)
+    out = np.empty((num_rows if sel is None else len(sel), out_cols), np.float32)
+
+    def call(row_begin, row_end, dst_row):
+        lib.oracle_prefill_typed(_ptr(q), qf, sq, sh, _ptr(k), kf, float(k_scale), sk, k.shape[0],
+                                 _ptr(ks), _ptr(ke), num_rows, scale,
+                                 out.ctypes.data + dst_row * out_cols * 4, out_cols, out_cols,
+                                 row_begin, row_end)
 
     if sel is None:
         _run_rows(lambda b, e: call(b, e, b), num_rows, threads)

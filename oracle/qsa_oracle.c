@@ -31,6 +31,12 @@
  *               QSA indexer" (vLLM PR 54513), section "Main changes":
  *               visible_blocks = (logical_position + 1) // compress_ratio
  *               moves into the per-step metadata.
+ *   [QSA-CACHE] QSAStateBackend: the compressed indexer cache may hold fp8
+ *               e4m3 entries.
+ *   [QSA-PREP]  "vllm/models/qwen4_exp/amd/ops/qsa_prepare.py", _to_dst_dtype:
+ *               a value bound for an fp8 cache is rounded to bf16, divided
+ *               by the cache's scale, then converted to fp8.
+ *   [MATE-QSA]  "MQA score": query and compressed key are BF16 or FP16.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - scale multiplies the head sum (equal to scaling before ReLU for
@@ -39,6 +45,10 @@
  *     blocks; with no visible array it sees comp_len[r].
  *   - prefill column c of row t holds key row_k_start[t] + c; it is valid
  *     iff that key lies in [0, num_keys) and below row_k_end[t].
+ *   - an fp8 key element stands for its e4m3 value times the cache's scale
+ *     (the inverse of the division on the write side); the scale applies
+ *     to fp8 keys only.  fp8 is the OCP e4m3 format (the "fp8_e4m3" cache
+ *     dtype).  NaN codes are outside the contract.
  *   - top-k keeps the k largest cells that are > -inf (NaN excluded),
  *     breaks ties toward the lower column, compares with IEEE ordering
  *     (-0 == +0), emits the picks in ascending column order and pads -1.
@@ -61,6 +71,56 @@ static double bf16_bits_to_double(uint16_t bits)
     return (double)f;
 }
 
+/* IEEE 754 binary16 bit pattern -> double: sign, 5-bit exponent with bias
+ * 15, 10-bit fraction.  Exponent 0 holds zero and the subnormals (fraction
+ * times 2^-24); exponent 31 holds infinities (fraction 0) and NaN.  Exact. */
+static double fp16_bits_to_double(uint16_t bits)
+{
+    int sign = bits >> 15;
+    int exponent = (bits >> 10) & 31;
+    int fraction = bits & 1023;
+    double v;
+    if (exponent == 0)
+        v = ldexp((double)fraction, -24);
+    else if (exponent == 31)
+        v = fraction ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + fraction), exponent - 25);  /* 2^(e-15) * (1 + f/1024) */
+    return sign ? -v : v;
+}
+
+/* OCP 8-bit floating point E4M3 bit pattern -> double: sign, 4-bit exponent
+ * with bias 7, 3-bit fraction.  Exponent 0 holds zero and the subnormals
+ * (fraction times 2^-9); S.1111.111 is NaN; there are no infinities (the
+ * largest finite magnitude is 448).  Exact. */
+static double e4m3_bits_to_double(uint8_t bits)
+{
+    int sign = bits >> 7;
+    int exponent = (bits >> 3) & 15;
+    int fraction = bits & 7;
+    double v;
+    if (exponent == 15 && fraction == 7)
+        v = NAN;
+    else if (exponent == 0)
+        v = ldexp((double)fraction, -9);
+    else
+        v = ldexp((double)(8 + fraction), exponent - 10);  /* 2^(e-7) * (1 + f/8) */
+    return sign ? -v : v;
+}
+
+/* Element formats of the typed entry points. */
+#define ORACLE_BF16 0
+#define ORACLE_FP16 1
+#define ORACLE_FP8_E4M3 2
+
+/* Element `index` of an array of `format` elements, widened exactly. */
+static double element(const void *base, int64_t index, int format)
+{
+    if (format == ORACLE_FP8_E4M3) return e4m3_bits_to_double(((const uint8_t *)base)[index]);
+    uint16_t bits = ((const uint16_t *)base)[index];
+    return format == ORACLE_FP16 ? fp16_bits_to_double(bits) : bf16_bits_to_double(bits);
+}
+
 static float neg_inf(void) { return -INFINITY; }
 
 /* Python-style floor division for the metadata formulas (C '/' truncates). */
@@ -73,16 +133,21 @@ static int64_t floor_div(int64_t a, int64_t b)
 
 /* One score cell [MATE-QSA, "MQA score"]:
  *   scale * sum_h max(0, sum_d q[h][d] * k[d]),
- * accumulated in double, rounded once to fp32. */
-static float score_cell(const uint16_t *q_row, int64_t q_stride_head,
-                        const uint16_t *key, float scale)
+ * with query element q[q_off + h*q_stride_head + d] in q_format and key
+ * element k[k_off + d] in k_format; an fp8 key element counts as its value
+ * times k_scale.  Accumulated in double, rounded once to fp32. */
+static float score_cell_typed(const void *q, int64_t q_off, int64_t q_stride_head, int q_format,
+                              const void *k, int64_t k_off, int k_format, double k_scale,
+                              float scale)
 {
     double head_sum = 0.0;
     for (int h = 0; h < QSA_ORACLE_HEADS; ++h) {
         double dot = 0.0;
-        for (int d = 0; d < QSA_ORACLE_DIM; ++d)
-            dot += bf16_bits_to_double(q_row[h * q_stride_head + d]) *
-                   bf16_bits_to_double(key[d]);
+        for (int d = 0; d < QSA_ORACLE_DIM; ++d) {
+            double kv = element(k, k_off + d, k_format);
+            if (k_format == ORACLE_FP8_E4M3) kv *= k_scale;
+            dot += element(q, q_off + h * q_stride_head + d, q_format) * kv;
+        }
         head_sum += (dot > 0.0) ? dot : 0.0;
     }
     return (float)(head_sum * (double)scale);
@@ -145,18 +210,22 @@ void oracle_prefill_intervals(const int32_t *token_to_req, const int32_t *visibl
 }
 
 /* ---------------------------------------------------------------------- */
-/* Decode over paged compressed keys [MATE-QSA "MQA score", paged form].     */
+/* Typed inputs: BF16 or FP16 queries and keys [MATE-QSA "MQA score"], and   */
+/* fp8 e4m3 keys scaled by the cache's scale [QSA-CACHE, QSA-PREP].          */
 
-/* Rows [row_begin, row_end) of the [num_reqs*dql, out_cols] output; row
- * `row` is written at out + (row - row_begin) * out_stride.
- * Row index = r*dql + j.  Element strides (bf16 elements) for q;
- * k_cache is [num_pages][page_size][1][128] contiguous. */
-void oracle_decode(const uint16_t *q, int64_t q_stride_req, int64_t q_stride_row,
-                   int64_t q_stride_head, const uint16_t *k_cache, int64_t num_pages,
-                   int32_t page_size, const int32_t *page_table, int64_t page_table_stride,
-                   int32_t page_table_cols, const int32_t *comp_lens, const int32_t *visible,
-                   int32_t num_reqs, int32_t dql, float scale, float *out,
-                   int64_t out_stride, int32_t out_cols, int32_t row_begin, int32_t row_end)
+/* Decode over paged compressed keys [MATE-QSA "MQA score", paged form].
+ * Rows [row_begin, row_end) of the [num_reqs*dql, out_cols] output; row
+ * `row` is written at out + (row - row_begin) * out_stride.  Row index =
+ * r*dql + j.  Query elements in q_format, key elements in k_format; strides
+ * in elements; k_cache is [num_pages][page_size][1][128] elements,
+ * contiguous. */
+void oracle_decode_typed(const void *q, int q_format, int64_t q_stride_req, int64_t q_stride_row,
+                         int64_t q_stride_head, const void *k_cache, int k_format, double k_scale,
+                         int64_t num_pages, int32_t page_size, const int32_t *page_table,
+                         int64_t page_table_stride, int32_t page_table_cols,
+                         const int32_t *comp_lens, const int32_t *visible, int32_t num_reqs,
+                         int32_t dql, float scale, float *out, int64_t out_stride,
+                         int32_t out_cols, int32_t row_begin, int32_t row_end)
 {
     (void)num_reqs;
     for (int32_t row = row_begin; row < row_end; ++row) {
@@ -165,7 +234,7 @@ void oracle_decode(const uint16_t *q, int64_t q_stride_req, int64_t q_stride_row
         int64_t seen = visible ? (int64_t)visible[row] : (int64_t)comp_lens[r];
         if (seen > comp_lens[r]) seen = comp_lens[r];
         if (seen < 0) seen = 0;
-        const uint16_t *q_row = q + r * q_stride_req + j * q_stride_row;
+        int64_t q_off = r * q_stride_req + j * q_stride_row;
         for (int32_t c = 0; c < out_cols; ++c) {
             float value = neg_inf();
             if (c < seen) {
@@ -173,9 +242,9 @@ void oracle_decode(const uint16_t *q, int64_t q_stride_req, int64_t q_stride_row
                 if (slot < page_table_cols) {
                     int64_t page = page_table[r * page_table_stride + slot];
                     if (page >= 0 && page < num_pages) {
-                        const uint16_t *key =
-                            k_cache + (page * page_size + (c % page_size)) * QSA_ORACLE_DIM;
-                        value = score_cell(q_row, q_stride_head, key, scale);
+                        int64_t k_off = (page * page_size + (c % page_size)) * QSA_ORACLE_DIM;
+                        value = score_cell_typed(q, q_off, q_stride_head, q_format, k_cache, k_off,
+                                                 k_format, k_scale, scale);
                     }
                 }
             }
@@ -184,30 +253,58 @@ void oracle_decode(const uint16_t *q, int64_t q_stride_req, int64_t q_stride_row
     }
 }
 
-/* ---------------------------------------------------------------------- */
-/* Prefill over packed queries and shared keys [MATE-QSA "MQA score"].      */
-
-/* Rows [row_begin, row_end) of the [num_rows, out_cols] output; row t is
+/* Prefill over packed queries and shared keys [MATE-QSA "MQA score"].
+ * Rows [row_begin, row_end) of the [num_rows, out_cols] output; row t is
  * written at out + (t - row_begin) * out_stride.  Column c of row t scores
  * key n = row_k_start[t] + c when 0 <= n < num_keys and n < row_k_end[t];
- * every other cell is -inf. */
+ * every other cell is -inf.  Element formats and strides as in
+ * oracle_decode_typed. */
+void oracle_prefill_typed(const void *q, int q_format, int64_t q_stride_row, int64_t q_stride_head,
+                          const void *k, int k_format, double k_scale, int64_t k_stride,
+                          int64_t num_keys, const int32_t *row_k_start, const int32_t *row_k_end,
+                          int32_t num_rows, float scale, float *out, int64_t out_stride,
+                          int32_t out_cols, int32_t row_begin, int32_t row_end)
+{
+    (void)num_rows;
+    for (int32_t t = row_begin; t < row_end; ++t) {
+        for (int32_t c = 0; c < out_cols; ++c) {
+            int64_t n = (int64_t)row_k_start[t] + c;
+            float value = neg_inf();
+            if (n >= 0 && n < num_keys && n < row_k_end[t])
+                value = score_cell_typed(q, (int64_t)t * q_stride_row, q_stride_head, q_format, k,
+                                         n * k_stride, k_format, k_scale, scale);
+            out[(int64_t)(t - row_begin) * out_stride + c] = value;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* BF16 queries and keys (the canonical inputs).                            */
+
+/* oracle_decode_typed with bf16 queries and keys. */
+void oracle_decode(const uint16_t *q, int64_t q_stride_req, int64_t q_stride_row,
+                   int64_t q_stride_head, const uint16_t *k_cache, int64_t num_pages,
+                   int32_t page_size, const int32_t *page_table, int64_t page_table_stride,
+                   int32_t page_table_cols, const int32_t *comp_lens, const int32_t *visible,
+                   int32_t num_reqs, int32_t dql, float scale, float *out,
+                   int64_t out_stride, int32_t out_cols, int32_t row_begin, int32_t row_end)
+{
+    oracle_decode_typed(q, ORACLE_BF16, q_stride_req, q_stride_row, q_stride_head, k_cache,
+                        ORACLE_BF16, 1.0, num_pages, page_size, page_table, page_table_stride,
+                        page_table_cols, comp_lens, visible, num_reqs, dql, scale, out, out_stride,
+                        out_cols, row_begin, row_end);
+}
+
+/* oracle_prefill_typed with bf16 queries and keys. */
 void oracle_prefill(const uint16_t *q, int64_t q_stride_row, int64_t q_stride_head,
                     const uint16_t *k, int64_t k_stride, int64_t num_keys,
                     const int32_t *row_k_start, const int32_t *row_k_end, int32_t num_rows,
                     float scale, float *out, int64_t out_stride, int32_t out_cols,
                     int32_t row_begin, int32_t row_end)
 {
-    (void)num_rows;
-    for (int32_t t = row_begin; t < row_end; ++t) {
-        const uint16_t *q_row = q + (int64_t)t * q_stride_row;
-        for (int32_t c = 0; c < out_cols; ++c) {
-            int64_t n = (int64_t)row_k_start[t] + c;
-            float value = neg_inf();
-            if (n >= 0 && n < num_keys && n < row_k_end[t])
-                value = score_cell(q_row, q_stride_head, k + n * k_stride, scale);
-            out[(int64_t)(t - row_begin) * out_stride + c] = value;
-        }
-    }
+    oracle_prefill_typed(q, ORACLE_BF16, q_stride_row, q_stride_head, k, ORACLE_BF16, 1.0, k_stride,
+                         num_keys, row_k_start, row_k_end, num_rows, scale, out, out_stride, out_cols,
+                         row_begin, row_end);
 }
 
 /* ---------------------------------------------------------------------- */

@@ -492,4 +492,119 @@ def pin_split_batch():
     assert O.split_batch([0], 4) == (None, 0, 0, 0, 0, 0)
 
 
+# ---------------------------------------------------------------------------
+# Typed inputs (fp16 queries/keys, fp8 e4m3 keys with a cache scale).
+
+
+def _row_unit(n, value_bits, dtype):
+    """n rows [n, 4, 128]: head 0, feature 0 holds value_bits[i]; all else 0."""
+    q = np.zeros((n, 4, 128), dtype)
+    q[:, 0, 0] = value_bits
+    return q
+
+
+def _relu_pair(v):
+    """Scores of a unit query against keys +v and -v at scale 1: relu(v), relu(-v)."""
+    v = np.asarray(v, np.float64)
+    return np.maximum(v, 0.0).astype(np.float32), np.maximum(-v, 0.0).astype(np.float32)
+
+
+def pin_fp16_decoding_all_codes():
+    """Every binary16 code, as a query element and as a key element, against
+    numpy's float16 conversion (a library routine).  NaN codes are skipped."""
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = codes.view(np.float16).astype(np.float64)
+    keep = ~np.isnan(vals)
+    want_pos, want_neg = _relu_pair(vals[keep])
+    one, minus_one = 0x3C00, 0xBC00  # binary16 +1, -1
+    # As a query element: rows hold the codes, keys are +1 and -1.
+    q = _row_unit(len(codes), codes, np.uint16)[keep]
+    k = np.zeros((2, 128), np.uint16)
+    k[0, 0], k[1, 0] = one, minus_one
+    n = len(q)
+    got = O.prefill_typed(q, "fp16", k, "fp16", np.zeros(n, np.int32), np.full(n, 2, np.int32), 2,
+                          scale=1.0)
+    assert np.array_equal(_f32_bits(got[:, 0]), _f32_bits(want_pos))
+    assert np.array_equal(_f32_bits(got[:, 1]), _f32_bits(want_neg))
+    # As a key element: one query row +1 against every code.
+    qk = _row_unit(2, [one, minus_one], np.uint16)
+    keys = np.zeros((int(keep.sum()), 128), np.uint16)
+    keys[:, 0] = codes[keep]
+    m = len(keys)
+    got = O.prefill_typed(qk, "fp16", keys, "fp16", np.zeros(2, np.int32), np.full(2, m, np.int32), m,
+                          scale=1.0)
+    assert np.array_equal(_f32_bits(got[0]), _f32_bits(want_pos))
+    assert np.array_equal(_f32_bits(got[1]), _f32_bits(want_neg))
+
+
+def pin_e4m3_decoding_all_codes():
+    """Every OCP e4m3 code as a key element, against torch's float8_e4m3fn
+    conversion (a library routine), at k_scale 1 and at k_scale 0.375 (the
+    products are exact in fp32).  NaN codes are skipped."""
+    import torch
+    codes = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    vals = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    keep = ~np.isnan(vals)
+    keys = np.zeros((int(keep.sum()), 128), np.uint8)
+    keys[:, 0] = codes[keep]
+    m = len(keys)
+    q = _row_unit(2, [0x3F80, 0xBF80], np.uint16)  # bf16 +1, -1
+    for k_scale in (1.0, 0.375):
+        want_pos, want_neg = _relu_pair(vals[keep] * k_scale)
+        got = O.prefill_typed(q, "bf16", keys, "fp8_e4m3", np.zeros(2, np.int32), np.full(2, m, np.int32),
+                              m, k_scale=k_scale, scale=1.0)
+        assert np.array_equal(_f32_bits(got[0]), _f32_bits(want_pos)), k_scale
+        assert np.array_equal(_f32_bits(got[1]), _f32_bits(want_neg)), k_scale
+    # Range facts of the format: largest finite 448, smallest subnormal 2^-9.
+    fin = vals[keep]
+    assert fin.max() == 448.0 and np.min(np.abs(fin[fin != 0])) == 2.0 ** -9
+
+
+def _exact_case(seed=31):
+    """Values every format holds exactly: queries are integers in [-8, 8],
+    fp8 key codes are integers in [-15, 15] with k_scale 0.5, so every key
+    value is a multiple of 0.5 below 8 in magnitude."""
+    import torch
+    rng = np.random.default_rng(seed)
+    inp = decode_inputs([37, 201, 90], 3, 5, 20, 2, 60, seed=seed)
+    qv = rng.integers(-8, 9, inp.q.shape).astype(np.float32)
+    kv = rng.integers(-15, 16, inp.k_pool.shape).astype(np.float32)
+    k8 = torch.from_numpy(kv).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return inp, qv, kv, k8
+
+
+def pin_typed_equal_bf16_on_exact_values():
+    """On inputs every format represents exactly, the typed decode and
+    prefill equal the bf16 oracle bit for bit: fp16 q and keys, and fp8 keys
+    whose codes times k_scale equal the bf16 keys."""
+    inp, qv, kv, k8 = _exact_case()
+    vis = O.token_metadata(inp.query_start_loc, inp.seq_lens, inp.q.shape[0] * inp.q.shape[1])[2]
+    comp = O.comp_lens(inp.seq_lens)
+    q16, qh = bf16_bits(qv), qv.astype(np.float16).view(np.uint16)
+    kb, kh = bf16_bits(kv * 0.5), (kv * 0.5).astype(np.float16).view(np.uint16)
+    base = O.decode(q16, kb, inp.page_table, comp, vis, inp.out_cols, scale=SCALE)
+    for qb, qf, kbits, kf in ((q16, "bf16", kb, "bf16"), (qh, "fp16", kh, "fp16"),
+                              (q16, "bf16", k8, "fp8_e4m3"), (qh, "fp16", k8, "fp8_e4m3")):
+        got = O.decode_typed(qb, qf, kbits, kf, inp.page_table, comp, vis, inp.out_cols,
+                             k_scale=0.5, scale=SCALE)
+        assert np.array_equal(_f32_bits(got), _f32_bits(base)), (qf, kf)
+    # Prefill over the flattened pool, keys read through a padded row stride.
+    T = 7
+    qp = qv.reshape(-1, 4, 128)[:T]
+    flat = kv.reshape(-1, 128)
+    nk = flat.shape[0]
+    ks = np.array([0, 3, -2, 5, 0, 10, 1], np.int32)
+    ke = np.array([nk, 40, 9, 5, 77, nk + 5, 2], np.int32)
+    cols = nk + 3
+    base = O.prefill(bf16_bits(qp), bf16_bits(flat * 0.5), ks, ke, cols, scale=SCALE)
+    padded = np.zeros((nk, 144), np.uint8)
+    padded[:, :128] = k8.reshape(-1, 128)
+    kh_pad = np.zeros((nk, 136), np.uint16)
+    kh_pad[:, :128] = (flat * 0.5).astype(np.float16).view(np.uint16)
+    for qb, qf, kbits, kf in ((qp.astype(np.float16).view(np.uint16), "fp16", kh_pad[:, :128], "fp16"),
+                              (bf16_bits(qp), "bf16", padded[:, :128], "fp8_e4m3")):
+        got = O.prefill_typed(qb, qf, kbits, kf, ks, ke, cols, k_scale=0.5, scale=SCALE)
+        assert np.array_equal(_f32_bits(got), _f32_bits(base)), (qf, kf)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -19,9 +19,9 @@ MUTANTS = {
                          "return (float)(head_sum / (double)scale);"),
     "head_dropped": ("for (int h = 0; h < QSA_ORACLE_HEADS; ++h) {",
                      "for (int h = 0; h < QSA_ORACLE_HEADS - 1; ++h) {"),
-    "head_stride_ignored": ("q_row[h * q_stride_head + d]", "q_row[h * QSA_ORACLE_DIM + d]"),
-    "feature_index_shifted": ("bf16_bits_to_double(key[d]);",
-                              "bf16_bits_to_double(key[(d + 1) % QSA_ORACLE_DIM]);"),
+    "head_stride_ignored": ("q_off + h * q_stride_head + d, q_format)", "q_off + h * QSA_ORACLE_DIM + d, q_format)"),
+    "feature_index_shifted": ("double kv = element(k, k_off + d, k_format);",
+                              "double kv = element(k, k_off + (d + 1) % QSA_ORACLE_DIM, k_format);"),
     "bf16_widening_wrong": ("uint32_t u = ((uint32_t)bits) << 16;",
                             "uint32_t u = ((uint32_t)bits) << 15;"),
     "visible_off_by_one": ("int64_t by_pos = floor_div(pos + 1, compress_ratio);",
@@ -41,6 +41,24 @@ MUTANTS = {
                              "return (x->col < y->col) - (x->col > y->col);\n}\n\nstatic int by_col"),
     "topk_keeps_neg_inf": ("if (row[c] > neg_inf()) {", "if (row[c] >= neg_inf()) {"),
     "topk_descending_output": ("qsort(cand, (size_t)keep, sizeof(oracle_cand), by_col);", ""),
+    "fp16_exponent_bias_wrong": ("v = ldexp((double)(1024 + fraction), exponent - 25);",
+                                 "v = ldexp((double)(1024 + fraction), exponent - 24);"),
+    "fp16_subnormal_scale_wrong": ("v = ldexp((double)fraction, -24);", "v = ldexp((double)fraction, -25);"),
+    "fp16_sign_dropped": ("    return sign ? -v : v;\n}\n\n/* OCP", "    return v;\n}\n\n/* OCP"),
+    "e4m3_bias_of_fnuz": ("v = ldexp((double)(8 + fraction), exponent - 10);",
+                          "v = ldexp((double)(8 + fraction), exponent - 11);"),
+    "e4m3_subnormal_scale_wrong": ("v = ldexp((double)fraction, -9);", "v = ldexp((double)fraction, -10);"),
+    "e4m3_no_implicit_one": ("ldexp((double)(8 + fraction), exponent - 10)", "ldexp((double)(fraction), exponent - 7)"),
+    "e4m3_top_binade_as_nan": ("if (exponent == 15 && fraction == 7)", "if (exponent == 15)"),
+    "k_scale_divides": ("if (k_format == ORACLE_FP8_E4M3) kv *= k_scale;",
+                        "if (k_format == ORACLE_FP8_E4M3) kv /= k_scale;"),
+    "k_scale_ignored": ("if (k_format == ORACLE_FP8_E4M3) kv *= k_scale;", ""),
+    "typed_query_read_as_bf16": ("dot += element(q, q_off + h * q_stride_head + d, q_format) * kv;",
+                                 "dot += element(q, q_off + h * q_stride_head + d, ORACLE_BF16) * kv;"),
+    "typed_prefill_key_stride_ignored": ("n * k_stride, k_format, k_scale, scale);",
+                                         "n * QSA_ORACLE_DIM, k_format, k_scale, scale);"),
+    "typed_decode_page_row_wrong": ("int64_t k_off = (page * page_size + (c % page_size)) * QSA_ORACLE_DIM;",
+                                    "int64_t k_off = (page * page_size + (c / page_size)) * QSA_ORACLE_DIM;"),
     "topk_smallest": ("if (x->value > y->value) return -1;\n    if (x->value < y->value) return 1;",
                       "if (x->value < y->value) return -1;\n    if (x->value > y->value) return 1;"),
 }

@@ -32,6 +32,28 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return rounded.astype(np.uint16)
 
 
+def fp16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bit patterns (uint16), round to nearest even
+    (numpy's conversion)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+# Cache scale of the synthetic fp8 key caches: 448 * scale = 5.6, so N(0,1)
+# keys essentially never saturate.
+FP8_K_SCALE = float(np.float32(0.0125))
+
+
+def fp8_e4m3_cache(k_bf16_bits: np.ndarray, k_scale: float = FP8_K_SCALE) -> np.ndarray:
+    """bf16 key bit patterns -> OCP e4m3 codes (uint8) by the fp8 cache write
+    rule of qsa_prepare ("_to_dst_dtype": round to bf16, divide by the cache
+    scale in fp32, convert to fp8); the conversion is torch's float8_e4m3fn
+    (round to nearest even).  Magnitudes above 448 saturate to 448."""
+    import torch
+    x = bits_to_f32(k_bf16_bits) / np.float32(k_scale)
+    x = np.clip(x, -448.0, 448.0).astype(np.float32)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns -> float32 values (exact)."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
