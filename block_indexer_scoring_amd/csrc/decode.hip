@@ -23,6 +23,16 @@
 // span (n = column 0..15, g = group 0..3) goes to column n of group g, so
 // after 4 groups each lane owns 4 consecutive keys and writes them with one
 // 16-byte store.
+//
+// Element formats: queries and keys in bf16 or fp16 (MATE "MQA score": both
+// are canonical inputs), or fp8 e4m3 keys (the optional e4m3 compressed
+// indexer cache of the vLLM QSA state backend) with bf16 or fp16 queries.
+// An e4m3 key row is 128 bytes: lane q4 reads its contiguous quarter (32
+// codes, two 16-byte loads per key), converts it exactly to the query's
+// 16-bit format, and the query fragments use the same feature order
+// (features 32*q4 + 8*ks .. +7 in k-step ks), so the products are
+// unchanged.  The cache scale multiplies the head sum together with the
+// score scale (relu commutes with a positive factor).
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -38,6 +48,9 @@ constexpr int kPadSpans = 4;  // spans per -inf-only task
 constexpr int kWavesPerBlock = QSA_DECODE_WAVES_PER_BLOCK;
 
 enum PageMode { kPageGeneric = 0, kPageMultiple64 = 1, kPage64 = 2 };
+
+// Kernel formats: query format plus whether keys are e4m3 codes.
+enum DecodeFormat { kBf16 = 0, kFp16 = 1, kBf16Fp8 = 2, kFp16Fp8 = 3 };
 
 // Q fragment: lane (n, q4) supplies query vector (row j, head h) of its
 // tile, features `feature` .. +7.
@@ -112,8 +125,10 @@ __device__ Task map_task(const DecodeParams &p, int task, int lane) {
     return Task{0, 0, false, false};
 }
 
-template <int MT, int PAGE_MODE>
+template <int MT, int PAGE_MODE, int FMT>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParams p) {
+    constexpr bool kQF16 = FMT == kFp16 || FMT == kFp16Fp8;
+    constexpr bool kKFp8 = FMT == kBf16Fp8 || FMT == kFp16Fp8;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int task_id = blockIdx.x * kWavesPerBlock + wave;
@@ -155,7 +170,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
             const int h = n & 3;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                qa[mt][ks] = j < p.dql ? load_q_fragment(p, r, j, h, 32 * ks + 8 * q4) : zero_u32x4();
+                qa[mt][ks] = j < p.dql ? load_q_fragment(p, r, j, h, kKFp8 ? 32 * q4 + 8 * ks : 32 * ks + 8 * q4)
+                                       : zero_u32x4();
         }
 
         // Key c0 + 4n + g, features 32ks + 8q4 .. +7, for every g and ks:
@@ -170,11 +186,29 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
             const bool page_ok = page >= 0 && page < p.num_pages;
             if (page_ok) {
                 const int in_page = PAGE_MODE == kPage64 ? 0 : c0 % p.page_size;
-                const uint16_t *src = p.k + ((int64_t)page * p.page_size + in_page + 4 * n) * kDim + 8 * q4;
+                const int64_t key0 = (int64_t)page * p.page_size + in_page + 4 * n;
+                if (kKFp8) {
+                    const uint8_t *src = reinterpret_cast<const uint8_t *>(p.k) + key0 * kDim + 32 * q4;
+                    u32x4 raw[4][2];
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
+                    for (int g = 0; g < 4; ++g) {
+                        raw[g][0] = load_u32x4(src + g * kDim);
+                        raw[g][1] = load_u32x4(src + g * kDim + 16);
+                    }
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) kb[g][ks] = load_u32x4(src + g * kDim + 32 * ks);
+                    for (int g = 0; g < 4; ++g) {
+                        kb[g][0] = e4m3x8_to_16bit<kQF16>(raw[g][0][0], raw[g][0][1]);
+                        kb[g][1] = e4m3x8_to_16bit<kQF16>(raw[g][0][2], raw[g][0][3]);
+                        kb[g][2] = e4m3x8_to_16bit<kQF16>(raw[g][1][0], raw[g][1][1]);
+                        kb[g][3] = e4m3x8_to_16bit<kQF16>(raw[g][1][2], raw[g][1][3]);
+                    }
+                } else {
+                    const uint16_t *src = p.k + key0 * kDim + 8 * q4;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int ks = 0; ks < 4; ++ks) kb[g][ks] = load_u32x4(src + g * kDim + 32 * ks);
+                }
             } else {
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
@@ -193,9 +227,20 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
                     if (slot < p.page_table_cols) page = p.page_table[pt_row + slot];
                 }
                 key_ok[g] = page >= 0 && page < p.num_pages;
-                const uint16_t *src = p.k + ((int64_t)page * p.page_size + (c % p.page_size)) * kDim + 8 * q4;
+                const int64_t key = (int64_t)page * p.page_size + (c % p.page_size);
+                if (kKFp8) {
+                    const uint8_t *src = reinterpret_cast<const uint8_t *>(p.k) + key * kDim + 32 * q4;
+                    const u32x4 lo = key_ok[g] ? load_u32x4(src) : zero_u32x4();
+                    const u32x4 hi = key_ok[g] ? load_u32x4(src + 16) : zero_u32x4();
+                    kb[g][0] = e4m3x8_to_16bit<kQF16>(lo[0], lo[1]);
+                    kb[g][1] = e4m3x8_to_16bit<kQF16>(lo[2], lo[3]);
+                    kb[g][2] = e4m3x8_to_16bit<kQF16>(hi[0], hi[1]);
+                    kb[g][3] = e4m3x8_to_16bit<kQF16>(hi[2], hi[3]);
+                } else {
+                    const uint16_t *src = p.k + key * kDim + 8 * q4;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) kb[g][ks] = key_ok[g] ? load_u32x4(src + 32 * ks) : zero_u32x4();
+                    for (int ks = 0; ks < 4; ++ks) kb[g][ks] = key_ok[g] ? load_u32x4(src + 32 * ks) : zero_u32x4();
+                }
             }
         }
 
@@ -205,7 +250,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
             for (int g = 0; g < 4; ++g) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(qa[mt][ks], kb[g][ks], acc);
+                for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<kQF16>(qa[mt][ks], kb[g][ks], acc);
                 const int c = c0 + 4 * n + g;
                 res[mt][g] = (key_ok[g] && c < vis_row[mt]) ? head_sum_score(acc, p.scale) : neg_inf();
             }
@@ -250,12 +295,22 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
     }
 }
 
+template <int MT, int FMT>
+hipError_t launch_fmt(const DecodeParams &p, hipStream_t stream, dim3 grid, dim3 block) {
+    if (p.page_size == kSpan) return launch_kernel(decode_kernel<MT, kPage64, FMT>, grid, block, stream, p);
+    if (p.page_size % kSpan == 0)
+        return launch_kernel(decode_kernel<MT, kPageMultiple64, FMT>, grid, block, stream, p);
+    return launch_kernel(decode_kernel<MT, kPageGeneric, FMT>, grid, block, stream, p);
+}
+
 template <int MT>
 hipError_t launch_mt(const DecodeParams &p, hipStream_t stream, dim3 grid, dim3 block) {
-    if (p.page_size == kSpan) return launch_kernel(decode_kernel<MT, kPage64>, grid, block, stream, p);
-    if (p.page_size % kSpan == 0)
-        return launch_kernel(decode_kernel<MT, kPageMultiple64>, grid, block, stream, p);
-    return launch_kernel(decode_kernel<MT, kPageGeneric>, grid, block, stream, p);
+    if (p.k_fp8) {
+        if (p.q_f16) return launch_fmt<MT, kFp16Fp8>(p, stream, grid, block);
+        return launch_fmt<MT, kBf16Fp8>(p, stream, grid, block);
+    }
+    if (p.q_f16) return launch_fmt<MT, kFp16>(p, stream, grid, block);
+    return launch_fmt<MT, kBf16>(p, stream, grid, block);
 }
 
 }  // namespace

@@ -126,7 +126,9 @@ __device__ __forceinline__ uint32_t score_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int kMode>
+// kF16: Q and K are fp16 rather than bf16 (the same layout and staging; only
+// the MFMA's operand type differs).
+template <int kMode, bool kF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillParams p) {
     constexpr bool kExact = kMode == kModeScoresExact;
@@ -359,7 +361,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) acc[g] = mfma16x16x32(qa[mt][ks], b[ks][g], acc[g]);
+                for (int g = 0; g < 4; ++g) acc[g] = mfma_qk<kF16>(qa[mt][ks], b[ks][g], acc[g]);
         };
         // Epilogue and store of a slice whose tile needs no mask and lies
         // wholly inside the chunk (tile_c < 0: placeholder, store dropped).
@@ -675,18 +677,23 @@ int64_t prefill_max_k_stride() { return ((int64_t)1 << 30) / (2 * kBN * 2); }
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
-    if (p.exact_stores) return launch_kernel(prefill_kernel<kModeScoresExact>, grid, dim3(kThreads), stream, p);
-    return launch_kernel(prefill_kernel<kModeScores>, grid, dim3(kThreads), stream, p);
+    if (p.f16) {
+        if (p.exact_stores)
+            return launch_kernel(prefill_kernel<kModeScoresExact, true>, grid, dim3(kThreads), stream, p);
+        return launch_kernel(prefill_kernel<kModeScores, true>, grid, dim3(kThreads), stream, p);
+    }
+    if (p.exact_stores) return launch_kernel(prefill_kernel<kModeScoresExact, false>, grid, dim3(kThreads), stream, p);
+    return launch_kernel(prefill_kernel<kModeScores, false>, grid, dim3(kThreads), stream, p);
 }
 
 hipError_t launch_prefill_group_max(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
-    return launch_kernel(prefill_kernel<kModeGroupMax>, grid, dim3(kThreads), stream, p);
+    return launch_kernel(prefill_kernel<kModeGroupMax, false>, grid, dim3(kThreads), stream, p);
 }
 
 hipError_t launch_prefill_candidates(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
-    return launch_kernel(prefill_kernel<kModeCandidates>, grid, dim3(kThreads), stream, p);
+    return launch_kernel(prefill_kernel<kModeCandidates, false>, grid, dim3(kThreads), stream, p);
 }
 
 int prefill_rows_per_block() { return kBM; }

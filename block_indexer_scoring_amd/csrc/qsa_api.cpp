@@ -177,16 +177,37 @@ int qsa_build_metadata(const int32_t *query_start_loc, const int32_t *seq_lens, 
     return device_status(fn, qsa::launch_metadata(p, static_cast<hipStream_t>(stream)));
 }
 
-int qsa_mqa_decode(const void *q, int64_t q_stride_req, int64_t q_stride_row, int64_t q_stride_head,
-                   const void *k_cache, int64_t num_pages, int32_t page_size, const int32_t *page_table,
-                   int64_t page_table_stride, int32_t page_table_cols, const int32_t *comp_lens,
-                   const int32_t *visible, int32_t num_reqs, int32_t dql, int32_t num_heads,
-                   int32_t head_dim, float scale, float *out, int64_t out_stride, int32_t out_cols,
-                   void *stream) {
-    const char *fn = "qsa_mqa_decode";
+// Query format must be bf16 or fp16; keys share it or are e4m3 codes with a
+// positive finite cache scale.
+static int check_formats(const char *fn, int32_t q_dtype, int32_t k_dtype, float k_scale) {
+    if (q_dtype != QSA_DTYPE_BF16 && q_dtype != QSA_DTYPE_FP16)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: query format %d is not QSA_DTYPE_BF16 or QSA_DTYPE_FP16", fn,
+                    q_dtype);
+    if (k_dtype != q_dtype && k_dtype != QSA_DTYPE_FP8_E4M3)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: key format %d: keys are the query's format or QSA_DTYPE_FP8_E4M3",
+                    fn, k_dtype);
+    if (k_dtype == QSA_DTYPE_FP8_E4M3 && !(std::isfinite(k_scale) && k_scale > 0.0f))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: k_scale must be finite and > 0 for fp8 keys", fn);
+    return QSA_OK;
+}
+
+static int decode_impl(const char *fn, const void *q, int32_t q_dtype, int64_t q_stride_req,
+                       int64_t q_stride_row, int64_t q_stride_head, const void *k_cache, int32_t k_dtype,
+                       float k_scale, int64_t num_pages, int32_t page_size, const int32_t *page_table,
+                       int64_t page_table_stride, int32_t page_table_cols, const int32_t *comp_lens,
+                       const int32_t *visible, int32_t num_reqs, int32_t dql, int32_t num_heads,
+                       int32_t head_dim, float scale, float *out, int64_t out_stride, int32_t out_cols,
+                       void *stream) {
     int rc;
     if ((rc = check_heads(fn, num_heads, head_dim))) return rc;
     if ((rc = check_scale(fn, scale))) return rc;
+    if ((rc = check_formats(fn, q_dtype, k_dtype, k_scale))) return rc;
+    const bool k_fp8 = k_dtype == QSA_DTYPE_FP8_E4M3;
+    // The cache scale multiplies each key element; it leaves the ReLU and
+    // head sum as a positive factor, so it joins the score multiplier.
+    const float mult = k_fp8 ? scale * k_scale : scale;
+    if (!(std::isfinite(mult) && mult > 0.0f))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: scale * k_scale is not a finite positive fp32", fn);
     if (num_reqs < 0 || out_cols < 0 || num_pages < 0 || page_table_cols < 0)
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
     if (dql < 1 || dql > 16) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: dql must be in [1, 16], got %d", fn, dql);
@@ -225,24 +246,53 @@ int qsa_mqa_decode(const void *q, int64_t q_stride_req, int64_t q_stride_row, in
     p.visible = visible;
     p.num_reqs = num_reqs;
     p.dql = dql;
-    p.scale = scale;
+    p.scale = mult;
     p.out = out;
     p.out_stride = out_stride;
     p.out_cols = out_cols;
     p.spans = (int32_t)spans;
     p.q_vec = aligned(q, 16) && q_stride_req % 8 == 0 && q_stride_row % 8 == 0 && q_stride_head % 8 == 0;
     p.out_vec = aligned(out, 16) && out_stride % 4 == 0;
+    p.q_f16 = q_dtype == QSA_DTYPE_FP16;
+    p.k_fp8 = k_fp8;
     return device_status(fn, qsa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
-int qsa_mqa_prefill(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
-                    int64_t k_stride, int64_t num_keys, const int32_t *row_k_start,
-                    const int32_t *row_k_end, int32_t num_rows, int32_t num_heads, int32_t head_dim,
-                    float scale, float *out, int64_t out_stride, int32_t out_cols, void *stream) {
-    const char *fn = "qsa_mqa_prefill";
+int qsa_mqa_decode(const void *q, int64_t q_stride_req, int64_t q_stride_row, int64_t q_stride_head,
+                   const void *k_cache, int64_t num_pages, int32_t page_size, const int32_t *page_table,
+                   int64_t page_table_stride, int32_t page_table_cols, const int32_t *comp_lens,
+                   const int32_t *visible, int32_t num_reqs, int32_t dql, int32_t num_heads,
+                   int32_t head_dim, float scale, float *out, int64_t out_stride, int32_t out_cols,
+                   void *stream) {
+    return decode_impl("qsa_mqa_decode", q, QSA_DTYPE_BF16, q_stride_req, q_stride_row, q_stride_head, k_cache,
+                       QSA_DTYPE_BF16, 1.0f, num_pages, page_size, page_table, page_table_stride,
+                       page_table_cols, comp_lens, visible, num_reqs, dql, num_heads, head_dim, scale, out,
+                       out_stride, out_cols, stream);
+}
+
+int qsa_mqa_decode_typed(const void *q, int32_t q_dtype, int64_t q_stride_req, int64_t q_stride_row,
+                         int64_t q_stride_head, const void *k_cache, int32_t k_dtype, float k_scale,
+                         int64_t num_pages, int32_t page_size, const int32_t *page_table,
+                         int64_t page_table_stride, int32_t page_table_cols, const int32_t *comp_lens,
+                         const int32_t *visible, int32_t num_reqs, int32_t dql, int32_t num_heads,
+                         int32_t head_dim, float scale, float *out, int64_t out_stride, int32_t out_cols,
+                         void *stream) {
+    return decode_impl("qsa_mqa_decode_typed", q, q_dtype, q_stride_req, q_stride_row, q_stride_head, k_cache,
+                       k_dtype, k_scale, num_pages, page_size, page_table, page_table_stride, page_table_cols,
+                       comp_lens, visible, num_reqs, dql, num_heads, head_dim, scale, out, out_stride, out_cols,
+                       stream);
+}
+
+static int prefill_impl(const char *fn, const void *q, int64_t q_stride_row, int64_t q_stride_head,
+                        const void *k, int64_t k_stride, int64_t num_keys, int32_t dtype,
+                        const int32_t *row_k_start, const int32_t *row_k_end, int32_t num_rows,
+                        int32_t num_heads, int32_t head_dim, float scale, float *out, int64_t out_stride,
+                        int32_t out_cols, void *stream) {
     int rc;
     if ((rc = check_heads(fn, num_heads, head_dim))) return rc;
     if ((rc = check_scale(fn, scale))) return rc;
+    if (dtype != QSA_DTYPE_BF16 && dtype != QSA_DTYPE_FP16)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: format %d is not QSA_DTYPE_BF16 or QSA_DTYPE_FP16", fn, dtype);
     if (num_rows < 0 || out_cols < 0 || num_keys < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
     if (out_stride < out_cols) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: out_stride < out_cols", fn);
     if (num_rows == 0 || out_cols == 0) return ok();
@@ -287,7 +337,26 @@ int qsa_mqa_prefill(const void *q, int64_t q_stride_row, int64_t q_stride_head, 
     p.col_chunks = (int32_t)col_chunks;
     p.out_vec = aligned(out, 16) && out_stride % 4 == 0;
     p.exact_stores = p.out_vec && (int64_t)bm * out_stride * 4 < ((int64_t)1 << 31);
+    p.f16 = dtype == QSA_DTYPE_FP16;
     return device_status(fn, qsa::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_mqa_prefill(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
+                    int64_t k_stride, int64_t num_keys, const int32_t *row_k_start,
+                    const int32_t *row_k_end, int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                    float scale, float *out, int64_t out_stride, int32_t out_cols, void *stream) {
+    return prefill_impl("qsa_mqa_prefill", q, q_stride_row, q_stride_head, k, k_stride, num_keys, QSA_DTYPE_BF16,
+                        row_k_start, row_k_end, num_rows, num_heads, head_dim, scale, out, out_stride, out_cols,
+                        stream);
+}
+
+int qsa_mqa_prefill_typed(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
+                          int64_t k_stride, int64_t num_keys, int32_t dtype, const int32_t *row_k_start,
+                          const int32_t *row_k_end, int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                          float scale, float *out, int64_t out_stride, int32_t out_cols, void *stream) {
+    return prefill_impl("qsa_mqa_prefill_typed", q, q_stride_row, q_stride_head, k, k_stride, num_keys, dtype,
+                        row_k_start, row_k_end, num_rows, num_heads, head_dim, scale, out, out_stride, out_cols,
+                        stream);
 }
 
 int qsa_topk_blocks(const float *logits, int64_t logits_stride, int32_t num_rows, int32_t num_cols,

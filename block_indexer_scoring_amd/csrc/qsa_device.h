@@ -33,6 +33,9 @@ __device__ __forceinline__ T load_uniform(const T *ptr) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
 __device__ __forceinline__ u32x4 zero_u32x4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 // ReLU as a signed-integer max on the bit pattern: positive floats order
@@ -54,6 +57,40 @@ __device__ __forceinline__ float head_sum_score(f32x4 acc, float scale) {
 // and B[k = 8*(l/16) .. +7][n = l%16]; it receives C[4*(l/16) + i][l%16].
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// The same product on fp16 operands (same lane layout).
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+}
+
+// Query . key product for 16-bit operands in bf16 (kF16 false) or fp16.
+template <bool kF16>
+__device__ __forceinline__ f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (kF16) return mfma16x16x32_f16(a, b, c);
+    else return mfma16x16x32(a, b, c);
+}
+
+// Eight OCP e4m3 codes (two words, code i in byte i%4 of word i/4) -> the
+// same eight values as 16-bit bf16 (kF16 false) or fp16, element i in half
+// i%2 of word i/2.  Exact: every e4m3 value is representable in both
+// (3 fraction bits, exponents 2^-9 .. 2^8).  The gfx950 conversion reads
+// its fp8 operand as OCP e4m3; a scale of 1.0 leaves the value unchanged.
+template <bool kF16>
+__device__ __forceinline__ u32x4 e4m3x8_to_16bit(uint32_t w0, uint32_t w1) {
+    u32x4 r;
+    if constexpr (kF16) {
+        r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false));
+        r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true));
+        r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false));
+        r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
+    } else {
+        r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+        r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+        r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+        r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+    }
+    return r;
 }
 
 }  // namespace qsa

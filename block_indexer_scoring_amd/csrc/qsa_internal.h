@@ -9,10 +9,13 @@
 
 namespace qsa {
 
+// Element formats (the values of QSA_DTYPE_* in qsa.h).
+constexpr int kFmtBf16 = 0, kFmtFp16 = 1, kFmtFp8E4m3 = 2;
+
 struct DecodeParams {
-    const uint16_t *q;          // bf16 bits
+    const uint16_t *q;          // bf16 or fp16 bits
     int64_t q_stride_req, q_stride_row, q_stride_head;
-    const uint16_t *k;          // bf16 bits [num_pages][page_size][128]
+    const uint16_t *k;          // [num_pages][page_size][128] elements: 16-bit, or 1-byte e4m3 codes
     int64_t num_pages;
     int32_t page_size;
     const int32_t *page_table;
@@ -28,6 +31,8 @@ struct DecodeParams {
     int32_t spans;              // ceil(out_cols / decode_span_keys())
     int32_t q_vec;              // Q may be read with 16-byte loads
     int32_t out_vec;            // out rows may be written with 16-byte stores
+    int32_t q_f16;              // Q (and 16-bit keys) are fp16, not bf16
+    int32_t k_fp8;              // keys are e4m3 codes (scale already holds the cache scale)
 };
 
 struct PrefillParams {
@@ -45,6 +50,7 @@ struct PrefillParams {
     int32_t row_blocks, col_chunks;
     int32_t out_vec;
     int32_t exact_stores;       // out_vec, and a row block's output spans < 2^31 bytes
+    int32_t f16;                // Q and K are fp16, not bf16 (scores launch only)
     // Fused top-k passes (qsa_mqa_prefill_topk); unused by the score kernel.
     int32_t topk;
     float *gmax;                // [rows][gmax_stride] maxima of 16-key groups

@@ -21,11 +21,19 @@ QSA_ERR_INVALID_ARGUMENT = 1
 QSA_ERR_UNSUPPORTED = 2
 QSA_ERR_LAYOUT = 3
 QSA_ERR_DEVICE = 4
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_set_launch_events", "qsa_split_batch",
            "qsa_build_metadata", "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks",
-           "qsa_mqa_prefill_topk", "qsa_prefill_topk_workspace_bytes")
+           "qsa_mqa_prefill_topk", "qsa_prefill_topk_workspace_bytes", "qsa_mqa_decode_typed",
+           "qsa_mqa_prefill_typed")
+
+# enum qsa_dtype
+QSA_DTYPE_BF16 = 0
+QSA_DTYPE_FP16 = 1
+QSA_DTYPE_FP8_E4M3 = 2
+_DTYPES = {torch.bfloat16: QSA_DTYPE_BF16, torch.float16: QSA_DTYPE_FP16,
+           torch.float8_e4m3fn: QSA_DTYPE_FP8_E4M3}
 
 DEFAULT_SCALE = 1.0 / math.sqrt(128.0)
 
@@ -62,6 +70,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_mqa_decode.argtypes = [P, i64, i64, i64, P, i64, i32, P, i64, i32, P, P, i32, i32,
                                    i32, i32, f32, P, i64, i32, P]
     lib.qsa_mqa_decode.restype = ctypes.c_int
+    lib.qsa_mqa_decode_typed.argtypes = [P, i32, i64, i64, i64, P, i32, f32, i64, i32, P, i64, i32, P, P,
+                                         i32, i32, i32, i32, f32, P, i64, i32, P]
+    lib.qsa_mqa_decode_typed.restype = ctypes.c_int
+    lib.qsa_mqa_prefill_typed.argtypes = [P, i64, i64, P, i64, i64, i32, P, P, i32, i32, i32, f32, P,
+                                          i64, i32, P]
+    lib.qsa_mqa_prefill_typed.restype = ctypes.c_int
     lib.qsa_mqa_prefill.argtypes = [P, i64, i64, P, i64, i64, P, P, i32, i32, i32, f32, P, i64,
                                     i32, P]
     lib.qsa_mqa_prefill.restype = ctypes.c_int
@@ -100,6 +114,17 @@ def _gpu(name: str, t: torch.Tensor, dtype: torch.dtype) -> None:
 
 def _ptr(t: torch.Tensor | None):
     return None if t is None else t.data_ptr()
+
+
+def _gpu_format(name: str, t: torch.Tensor, allowed) -> int:
+    """The enum qsa_dtype of a GPU tensor whose dtype is one of `allowed`."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
+    if t.dtype not in allowed:
+        raise TypeError(f"{name} must be one of {[str(d) for d in allowed]}, got {t.dtype}")
+    return _DTYPES[t.dtype]
 
 
 # ----------------------------------------------------------------------------
@@ -233,6 +258,84 @@ def qsa_mqa_prefill(q: torch.Tensor, k: torch.Tensor, row_k_start: torch.Tensor,
         raise ValueError("out must be [T, out_cols] with unit column stride")
     _check(lib.qsa_mqa_prefill(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.shape[0], _ptr(row_k_start),
+        _ptr(row_k_end), num_rows, heads, dim, float(scale), _ptr(out), out.stride(0),
+        out.shape[1], _stream_handle(stream)))
+    return out
+
+
+def qsa_mqa_decode_typed(q: torch.Tensor, k_cache: torch.Tensor, page_table: torch.Tensor,
+                         comp_lens: torch.Tensor, visible: torch.Tensor | None = None,
+                         out_cols: int | None = None, k_scale: float = 1.0,
+                         scale: float = DEFAULT_SCALE, out: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """qsa_mqa_decode with typed elements: q bf16 or fp16; k_cache the same
+    dtype as q, or float8_e4m3fn (an e4m3 cache whose elements stand for their
+    value times k_scale).  Shapes and the rest as qsa_mqa_decode."""
+    lib = load_library()
+    q_fmt = _gpu_format("q", q, (torch.bfloat16, torch.float16))
+    k_fmt = _gpu_format("k_cache", k_cache, (torch.bfloat16, torch.float16, torch.float8_e4m3fn))
+    _gpu("page_table", page_table, torch.int32)
+    _gpu("comp_lens", comp_lens, torch.int32)
+    if q.dim() != 4 or k_cache.dim() != 4 or page_table.dim() != 2:
+        raise ValueError("q must be [R, DQL, H, D], k_cache [P, page_size, 1, D], page_table [R, W]")
+    num_reqs, dql, heads, dim = q.shape
+    if q.stride(3) != 1 and dim > 1:
+        raise QSAError(QSA_ERR_LAYOUT, "q needs unit feature stride")
+    if k_cache.shape[2] != 1 or k_cache.shape[3] != dim or not k_cache.is_contiguous():
+        raise ValueError("k_cache must be a contiguous [P, page_size, 1, 128] tensor")
+    if page_table.shape[0] != num_reqs or (page_table.shape[1] > 1 and page_table.stride(1) != 1):
+        raise ValueError("page_table must be [R, W] with unit column stride")
+    if comp_lens.numel() != num_reqs or not comp_lens.is_contiguous():
+        raise ValueError("comp_lens must be a contiguous [R] tensor")
+    if visible is not None:
+        _gpu("visible", visible, torch.int32)
+        if visible.numel() != num_reqs * dql or not visible.is_contiguous():
+            raise ValueError("visible must be a contiguous [R*DQL] tensor")
+    if out is None:
+        if out_cols is None:
+            raise ValueError("give out_cols or out")
+        out = torch.empty((num_reqs * dql, out_cols), dtype=torch.float32, device=q.device)
+    _gpu("out", out, torch.float32)
+    if out.dim() != 2 or out.shape[0] != num_reqs * dql or (out.shape[1] > 1 and out.stride(1) != 1):
+        raise ValueError("out must be [R*DQL, out_cols] with unit column stride")
+    _check(lib.qsa_mqa_decode_typed(
+        _ptr(q), q_fmt, q.stride(0), q.stride(1), q.stride(2), _ptr(k_cache), k_fmt, float(k_scale),
+        k_cache.shape[0], k_cache.shape[1], _ptr(page_table), page_table.stride(0), page_table.shape[1],
+        _ptr(comp_lens), _ptr(visible), num_reqs, dql, heads, dim, float(scale), _ptr(out),
+        out.stride(0), out.shape[1], _stream_handle(stream)))
+    return out
+
+
+def qsa_mqa_prefill_typed(q: torch.Tensor, k: torch.Tensor, row_k_start: torch.Tensor,
+                          row_k_end: torch.Tensor, out_cols: int | None = None,
+                          scale: float = DEFAULT_SCALE, out: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """qsa_mqa_prefill with q and k both bf16 or both fp16."""
+    lib = load_library()
+    fmt = _gpu_format("q", q, (torch.bfloat16, torch.float16))
+    if _gpu_format("k", k, (torch.bfloat16, torch.float16)) != fmt:
+        raise TypeError("q and k must share their dtype")
+    _gpu("row_k_start", row_k_start, torch.int32)
+    _gpu("row_k_end", row_k_end, torch.int32)
+    if q.dim() != 3 or k.dim() != 2:
+        raise ValueError("q must be [T, H, D] and k [NK, D]")
+    num_rows, heads, dim = q.shape
+    if (q.stride(2) != 1 and dim > 1) or (k.stride(1) != 1 and k.shape[1] > 1):
+        raise QSAError(QSA_ERR_LAYOUT, "q and k need unit feature stride")
+    if k.shape[1] != dim:
+        raise ValueError("q and k head_dim differ")
+    for name, t in (("row_k_start", row_k_start), ("row_k_end", row_k_end)):
+        if t.numel() != num_rows or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [T] tensor")
+    if out is None:
+        if out_cols is None:
+            raise ValueError("give out_cols or out")
+        out = torch.empty((num_rows, out_cols), dtype=torch.float32, device=q.device)
+    _gpu("out", out, torch.float32)
+    if out.dim() != 2 or out.shape[0] != num_rows or (out.shape[1] > 1 and out.stride(1) != 1):
+        raise ValueError("out must be [T, out_cols] with unit column stride")
+    _check(lib.qsa_mqa_prefill_typed(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.shape[0], fmt, _ptr(row_k_start),
         _ptr(row_k_end), num_rows, heads, dim, float(scale), _ptr(out), out.stride(0),
         out.shape[1], _stream_handle(stream)))
     return out

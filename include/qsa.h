@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 
 enum qsa_status {
     QSA_OK = 0,
@@ -47,6 +47,19 @@ enum qsa_status {
     QSA_ERR_LAYOUT = 3,           /* alignment or stride rule of the vector loads */
     QSA_ERR_DEVICE = 4            /* the HIP runtime reported an error            */
 };
+
+/* Element formats of the typed entry points (qsa_mqa_decode_typed,
+ * qsa_mqa_prefill_typed).
+ *   QSA_DTYPE_BF16, QSA_DTYPE_FP16: 2-byte elements.  MATE "QSA (Qwen Sparse
+ *     Attention)", section "MQA score": the query and the compressed key are
+ *     BF16 or FP16.
+ *   QSA_DTYPE_FP8_E4M3: 1-byte OCP e4m3 codes (bias 7; S.1111.111 is NaN;
+ *     largest finite 448), keys only.  The vLLM QSA state backend allows an
+ *     e4m3 compressed indexer cache; qsa_prepare's _to_dst_dtype writes it
+ *     by rounding to bf16, dividing by the cache scale and converting.  Read
+ *     here as the inverse: a key element is its e4m3 value times k_scale.
+ *     NaN codes are outside the contract. */
+enum qsa_dtype { QSA_DTYPE_BF16 = 0, QSA_DTYPE_FP16 = 1, QSA_DTYPE_FP8_E4M3 = 2 };
 
 /* QSA_ABI_VERSION of the loaded library. */
 int qsa_abi_version(void);
@@ -191,6 +204,46 @@ int qsa_mqa_prefill(const void *q, int64_t q_stride_row, int64_t q_stride_head, 
                     const int32_t *row_k_end, int32_t num_rows, int32_t num_heads,
                     int32_t head_dim, float scale, float *out, int64_t out_stride,
                     int32_t out_cols, void *stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_mqa_decode_typed -- qsa_mqa_decode with typed queries and keys.
+ *   Source: as qsa_mqa_decode; formats per enum qsa_dtype above.
+ *
+ *   q_dtype : QSA_DTYPE_BF16 or QSA_DTYPE_FP16 (2-byte elements; strides in
+ *             elements as for qsa_mqa_decode).
+ *   k_dtype : q_dtype (a [num_pages][page_size][1][128] cache of 2-byte
+ *             elements), or QSA_DTYPE_FP8_E4M3 (the same shape in 1-byte
+ *             codes: 128 bytes per key).  k_cache is 16-byte aligned.
+ *   k_scale : fp8 keys only: the cache scale, finite and > 0; key element =
+ *             e4m3 value * k_scale.  Ignored for 2-byte keys.
+ *   The scores equal scale * k_scale * sum_h relu(q_h . code) for fp8 keys;
+ *   scale * k_scale is formed once in fp32 and must be finite and > 0.
+ *   Other arguments, output and errors as qsa_mqa_decode, plus UNSUPPORTED
+ *   for other formats or 2-byte keys in a format other than the query's,
+ *   and INVALID_ARGUMENT for a bad k_scale.
+ */
+int qsa_mqa_decode_typed(const void *q, int32_t q_dtype, int64_t q_stride_req,
+                         int64_t q_stride_row, int64_t q_stride_head, const void *k_cache,
+                         int32_t k_dtype, float k_scale, int64_t num_pages, int32_t page_size,
+                         const int32_t *page_table, int64_t page_table_stride,
+                         int32_t page_table_cols, const int32_t *comp_lens,
+                         const int32_t *visible, int32_t num_reqs, int32_t dql,
+                         int32_t num_heads, int32_t head_dim, float scale, float *out,
+                         int64_t out_stride, int32_t out_cols, void *stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_mqa_prefill_typed -- qsa_mqa_prefill with BF16 or FP16 queries and
+ * keys (dtype QSA_DTYPE_BF16 or QSA_DTYPE_FP16; both share it).
+ *   Source: MATE "QSA (Qwen Sparse Attention)", section "MQA score" (BF16
+ *   or FP16 query and key; packed queries, per-row key intervals).
+ *   Arguments, layout rule, output and errors as qsa_mqa_prefill (strides in
+ *   elements), plus UNSUPPORTED for any other dtype.
+ */
+int qsa_mqa_prefill_typed(const void *q, int64_t q_stride_row, int64_t q_stride_head,
+                          const void *k, int64_t k_stride, int64_t num_keys, int32_t dtype,
+                          const int32_t *row_k_start, const int32_t *row_k_end,
+                          int32_t num_rows, int32_t num_heads, int32_t head_dim, float scale,
+                          float *out, int64_t out_stride, int32_t out_cols, void *stream);
 
 /* ------------------------------------------------------------------------
  * qsa_topk_blocks -- per-row top-k block indices.

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.qsa_abi_version() == 2
+    assert lib.qsa_abi_version() == 3
 
 
 def test_launch_events_set_and_clear_without_device(lib):
@@ -95,6 +95,68 @@ def _decode(lib, **kw):
 def test_decode_rejects(lib, kw, code, text):
     assert _decode(lib, **kw) == code
     assert text in _err(lib)
+
+
+def _decode_typed(lib, q_dtype=0, k_dtype=0, k_scale=1.0, **kw):
+    a = dict(q=FAKE, sr=512, sj=512, sh=128, k=FAKE, num_pages=4, page_size=16, pt=FAKE,
+             pt_stride=4, pt_cols=4, comp=FAKE, vis=None, num_reqs=1, dql=1, heads=4, dim=128,
+             scale=0.088, out=FAKE, out_stride=64, out_cols=64)
+    a.update(kw)
+    return lib.qsa_mqa_decode_typed(a["q"], q_dtype, a["sr"], a["sj"], a["sh"], a["k"], k_dtype, k_scale,
+                                    a["num_pages"], a["page_size"], a["pt"], a["pt_stride"], a["pt_cols"],
+                                    a["comp"], a["vis"], a["num_reqs"], a["dql"], a["heads"], a["dim"],
+                                    a["scale"], a["out"], a["out_stride"], a["out_cols"], None)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(q_dtype=2, k_dtype=2), 2, "query format"),
+    (dict(q_dtype=5), 2, "query format"),
+    (dict(q_dtype=0, k_dtype=1), 2, "key format"),
+    (dict(q_dtype=1, k_dtype=0), 2, "key format"),
+    (dict(k_dtype=3), 2, "key format"),
+    (dict(k_dtype=2, k_scale=0.0), 1, "k_scale"),
+    (dict(k_dtype=2, k_scale=-1.0), 1, "k_scale"),
+    (dict(k_dtype=2, k_scale=float("nan")), 1, "k_scale"),
+    (dict(k_dtype=2, k_scale=float("inf")), 1, "k_scale"),
+    (dict(k_dtype=2, k_scale=1e30, scale=1e30), 1, "scale * k_scale"),
+    (dict(k_dtype=2, k_scale=1e-30, scale=1e-30), 1, "scale * k_scale"),
+    (dict(k_dtype=2, k_scale=0.5, heads=8), 2, "(4, 128)"),
+    (dict(k_dtype=2, k_scale=0.5, k=FAKE + 8), 3, "aligned"),
+    (dict(q_dtype=1, k_dtype=1, dql=0), 1, "dql"),
+])
+def test_decode_typed_rejects(lib, kw, code, text):
+    assert _decode_typed(lib, **kw) == code
+    assert text in _err(lib)
+    assert "qsa_mqa_decode_typed" in _err(lib)
+
+
+def test_decode_typed_zero_work_and_ignored_scale(lib):
+    # 16-bit keys ignore k_scale; zero work returns OK with no device call.
+    assert _decode_typed(lib, q_dtype=1, k_dtype=1, k_scale=float("nan"), num_reqs=0, q=None) == 0
+    assert _decode_typed(lib, q_dtype=0, k_dtype=2, k_scale=0.0125, out_cols=0, out_stride=0) == 0
+    assert _err(lib) == ""
+
+
+def _prefill_typed(lib, dtype, **kw):
+    a = dict(q=FAKE, sq=512, sh=128, k=FAKE, sk=128, nk=100, ks=FAKE, ke=FAKE, rows=10, heads=4,
+             dim=128, scale=0.088, out=FAKE, out_stride=100, out_cols=100)
+    a.update(kw)
+    return lib.qsa_mqa_prefill_typed(a["q"], a["sq"], a["sh"], a["k"], a["sk"], a["nk"], dtype, a["ks"],
+                                     a["ke"], a["rows"], a["heads"], a["dim"], a["scale"], a["out"],
+                                     a["out_stride"], a["out_cols"], None)
+
+
+@pytest.mark.parametrize("dtype,kw,code,text", [
+    (2, {}, 2, "format 2"),
+    (-1, {}, 2, "format -1"),
+    (1, dict(heads=2), 2, "(4, 128)"),
+    (1, dict(out_stride=99), 1, "out_stride"),
+    (1, dict(q=FAKE + 2), 3, "16-byte"),
+])
+def test_prefill_typed_rejects(lib, dtype, kw, code, text):
+    assert _prefill_typed(lib, dtype, **kw) == code
+    assert text in _err(lib)
+    assert "qsa_mqa_prefill_typed" in _err(lib)
 
 
 def test_decode_zero_work_is_ok_without_device(lib):
