@@ -403,6 +403,61 @@ def main(argv=None) -> int:
     }
     del fz_ws
 
+    # The typed entry points on the same workloads, for context.  Decode
+    # reads the batch's key caches written as e4m3 codes (the fp8 cache write
+    # rule of the shared input generator): the 8 pools' codes and their
+    # sign-flipped copies, 16 caches of 26 MB, more than the Infinity Cache
+    # holds, so each launch streams from HBM.  Prefill runs on the step's
+    # prefill rows with queries and keys in fp16.
+    from workloads import FP8_K_SCALE, fp8_e4m3_cache
+    f8_pools = []
+    for pool in pools:
+        codes = fp8_e4m3_cache(pool.view(torch.int16).cpu().numpy().view(np.uint16))
+        f8_pools.append(torch.from_numpy(codes).to(dev))
+        f8_pools.append(torch.from_numpy(codes ^ np.uint8(0x80)).to(dev))
+    n_typed = 20
+    ty_ev = [HipEvents(2) for _ in range(n_typed)]
+    f8_out = torch.empty_like(dec_out)
+    for j in range(n_typed + 4):
+        if j >= 4:
+            check(lib.qsa_set_launch_events(ty_ev[j - 4].ev[0], ty_ev[j - 4].ev[1]))
+        pool8 = f8_pools[j % len(f8_pools)]
+        check(lib.qsa_mqa_decode_typed(
+            q_dec.data_ptr(), qsa.QSA_DTYPE_BF16, q_dec.stride(0), q_dec.stride(1), q_dec.stride(2),
+            pool8.data_ptr(), qsa.QSA_DTYPE_FP8_E4M3, FP8_K_SCALE, dec.k_pool.shape[0], dec.page_size,
+            page_table.data_ptr(), page_table.stride(0), page_table.shape[1], meta["comp_lens"].data_ptr(),
+            meta["visible"].data_ptr(), R, DQL, 4, 128, scale, f8_out.data_ptr(), f8_out.stride(0),
+            f8_out.shape[1], sh))
+        check(lib.qsa_set_launch_events(None, None))
+    torch.cuda.synchronize()
+    f8_us = float(np.mean([e.elapsed_us(0, 1) for e in ty_ev]))
+    f8_bytes = dbytes - 128.0 * comp_total  # 128-byte keys instead of 256
+    result["decode_fp8_e4m3"] = {
+        "us": round(f8_us, 3), "gbps": round(f8_bytes / (f8_us * 1e-6) / 1e9, 2),
+        "frac_of_hbm": round(f8_bytes / (f8_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "bytes": f8_bytes, "key_caches": len(f8_pools), "k_scale": FP8_K_SCALE,
+    }
+    del f8_pools
+    q16, k16 = q_pre.to(torch.float16), k_pre.to(torch.float16)
+    for j in range(6 + 4):
+        if j >= 4:
+            check(lib.qsa_set_launch_events(ty_ev[j - 4].ev[0], ty_ev[j - 4].ev[1]))
+        check(lib.qsa_mqa_prefill_typed(
+            q16.data_ptr(), q16.stride(0), q16.stride(1), k16.data_ptr(), k16.stride(0), k16.shape[0],
+            qsa.QSA_DTYPE_FP16, meta["row_k_start"].data_ptr() + 4 * T_dec,
+            meta["row_k_end"].data_ptr() + 4 * T_dec, T_pre, 4, 128, scale, pre_out.data_ptr(),
+            pre_out.stride(0), pre_out.shape[1], sh))
+        check(lib.qsa_set_launch_events(None, None))
+    torch.cuda.synchronize()
+    f16_us = float(np.mean([e.elapsed_us(0, 1) for e in ty_ev[:6]]))
+    result["prefill_fp16"] = {
+        "us": round(f16_us, 3), "tflops": round(pflops / (f16_us * 1e-6) / 1e12, 2),
+        "frac_of_mfma": round(pflops / (f16_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+    }
+    for e in ty_ev:
+        e.close()
+    del q16, k16
+
     # A measured bandwidth for context: a plain 1 GiB device-to-device copy
     # (read + write bytes over its time), and each HBM-bound kernel's rate as
     # a fraction of it.
