@@ -127,11 +127,15 @@ __device__ __forceinline__ uint32_t score_key(float v) {
 }
 
 // kF16: Q and K are fp16 rather than bf16 (the same layout and staging; only
-// the MFMA's operand type differs).
-template <int kMode, bool kF16>
+// the MFMA's operand type differs).  kRotate (kModeScoresExact only): the
+// line-aligned store layout below, for outputs whose rows do not all start
+// on a 128-byte line; with aligned rows the plain layout is the same stores
+// without the carried cells.
+template <int kMode, bool kF16, bool kRotate>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillParams p) {
     constexpr bool kExact = kMode == kModeScoresExact;
+    static_assert(!kRotate || kExact, "line-aligned layout is for exact score stores");
     constexpr bool kFused = kMode == kModeGroupMax || kMode == kModeCandidates;
     // Two separate LDS objects (not one [2][...] array), so the compiler can
     // tell the buffer being read from the one being filled and does not wait
@@ -175,21 +179,21 @@ void prefill_kernel(PrefillParams p) {
     // by that offset: lane n computes tile columns 4*((n - rot) mod 16) ..
     // +3 (B fragments read rotated), and the store of a slice covers the
     // line-aligned columns tile_c - 4*rot .. tile_c + 63 - 4*rot.  Lanes
-    // n < rot store the previous tile's cells, which they still hold.  With
-    // the other modes, or a row pitch that is a multiple of 128 bytes,
+    // n < rot store the previous tile's cells, which they still hold.
+    // Without kRotate (the other modes, or every row on a line boundary),
     // dl = 1 and rot = 0.
     int dl = 1;
-    if (kExact) {
+    if (kRotate) {
         const int u = (int)((p.out_stride >> 2) & 7);  // 16-byte units per row, mod 8
         dl = u == 0 ? 1 : ((u & 1) ? 8 : ((u & 2) ? 4 : 2));
     }
     const int a_w = (wave % dl) + kRowsPerWave * dl * (wave / dl);  // wave row j is a_w + dl * j
-    const int rot = kExact ? __builtin_amdgcn_readfirstlane(
-                                 (int)((((uintptr_t)p.out + (uint64_t)(row0 + a_w) * (uint64_t)p.out_stride * 4) >> 4) & 7))
-                           : 0;
+    const int rot = kRotate ? __builtin_amdgcn_readfirstlane(
+                                  (int)((((uintptr_t)p.out + (uint64_t)(row0 + a_w) * (uint64_t)p.out_stride * 4) >> 4) & 7))
+                            : 0;
     const int lc = 4 * ((n - rot) & 15);  // first tile column of this lane's cells
     const int sc = 4 * (n - rot);         // first column of this lane's store, relative to the tile
-    const bool lo = n < rot;              // stores the previous tile's cells
+    const bool lo = kRotate && n < rot;   // stores the previous tile's cells
 
     for (int i = tid; i < kBM; i += kThreads) {
         const int t = row0 + i;
@@ -368,11 +372,16 @@ void prefill_kernel(PrefillParams p) {
         auto finish_fast = [&](int mt, int tile_c, const f32x4 (&acc)[4]) {
             const f32x4 v{head_sum_score(acc[0], p.scale), head_sum_score(acc[1], p.scale),
                           head_sum_score(acc[2], p.scale), head_sum_score(acc[3], p.scale)};
-            const f32x4 w = lo ? keep[mt] : v;
-            keep[mt] = v;
-            const bool drop = tile_c < 0 || (lo && tile_c == c_begin);
-            __builtin_amdgcn_raw_buffer_store_b128(w, out_rsrc, drop ? kDropped : row_boff[mt] + 4 * tile_c, 0,
-                                                   kStoreNT);
+            if constexpr (kRotate) {
+                const f32x4 w = lo ? keep[mt] : v;
+                keep[mt] = v;
+                const bool drop = tile_c < 0 || (lo && tile_c == c_begin);
+                __builtin_amdgcn_raw_buffer_store_b128(w, out_rsrc, drop ? kDropped : row_boff[mt] + 4 * tile_c, 0,
+                                                       kStoreNT);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b128(v, out_rsrc, tile_c >= 0 ? row_boff[mt] : kDropped,
+                                                       4 * max(tile_c, 0), kStoreNT);
+            }
         };
         // Any slice: mask per cell, partial tiles and unbounded rows.
         auto finish_general = [&](int mt, int tile_c, bool masked, const f32x4 (&acc)[4]) {
@@ -391,12 +400,19 @@ void prefill_kernel(PrefillParams p) {
             if (kExact) {
                 // Lanes wholly inside the chunk take the buffer store; the one
                 // lane that straddles the chunk's end stores its cells singly.
-                const f32x4 w = lo ? keep[mt] : v;
-                keep[mt] = v;
+                f32x4 w = v;
+                if constexpr (kRotate) {
+                    w = lo ? keep[mt] : v;
+                    keep[mt] = v;
+                }
                 const int cs = tile_c + sc;
                 const bool drop = tile_c < 0 || (lo && tile_c == c_begin);
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    w, out_rsrc, (!drop && cs + 3 < c_end) ? row_boff[mt] + 4 * tile_c : kDropped, 0, kStoreNT);
+                if constexpr (kRotate)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        w, out_rsrc, (!drop && cs + 3 < c_end) ? row_boff[mt] + 4 * tile_c : kDropped, 0, kStoreNT);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b128(w, out_rsrc, (!drop && cs + 3 < c_end) ? row_boff[mt] : kDropped,
+                                                           4 * max(tile_c, 0), kStoreNT);
                 if (!drop && in_pass[mt] && cs < c_end && cs + 3 >= c_end)
                     store4(out_wg + row_elem(mt, cs), false, cs, c_end, w[0], w[1], w[2], w[3]);
             } else if (tile_c >= 0 && in_pass[mt]) {
@@ -596,7 +612,7 @@ void prefill_kernel(PrefillParams p) {
             if (kFused) finish_topk(3, prev_c, prev_masked, accB);
             else finish_general(3, prev_c, prev_masked, accB);
         }
-        if (kExact && n_compute > 0 && lo) {
+        if (kRotate && n_compute > 0 && lo) {
             // The last segment's end: columns end - 4*rot .. end - 1 of the
             // last computed tile, held by lanes n < rot.
             const int cs = c_begin + n_compute * kBN + sc;
@@ -678,22 +694,27 @@ int64_t prefill_max_k_stride() { return ((int64_t)1 << 30) / (2 * kBN * 2); }
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
     if (p.f16) {
+        if (p.exact_stores && p.rotate)
+            return launch_kernel(prefill_kernel<kModeScoresExact, true, true>, grid, dim3(kThreads), stream, p);
         if (p.exact_stores)
-            return launch_kernel(prefill_kernel<kModeScoresExact, true>, grid, dim3(kThreads), stream, p);
-        return launch_kernel(prefill_kernel<kModeScores, true>, grid, dim3(kThreads), stream, p);
+            return launch_kernel(prefill_kernel<kModeScoresExact, true, false>, grid, dim3(kThreads), stream, p);
+        return launch_kernel(prefill_kernel<kModeScores, true, false>, grid, dim3(kThreads), stream, p);
     }
-    if (p.exact_stores) return launch_kernel(prefill_kernel<kModeScoresExact, false>, grid, dim3(kThreads), stream, p);
-    return launch_kernel(prefill_kernel<kModeScores, false>, grid, dim3(kThreads), stream, p);
+    if (p.exact_stores && p.rotate)
+        return launch_kernel(prefill_kernel<kModeScoresExact, false, true>, grid, dim3(kThreads), stream, p);
+    if (p.exact_stores)
+        return launch_kernel(prefill_kernel<kModeScoresExact, false, false>, grid, dim3(kThreads), stream, p);
+    return launch_kernel(prefill_kernel<kModeScores, false, false>, grid, dim3(kThreads), stream, p);
 }
 
 hipError_t launch_prefill_group_max(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
-    return launch_kernel(prefill_kernel<kModeGroupMax, false>, grid, dim3(kThreads), stream, p);
+    return launch_kernel(prefill_kernel<kModeGroupMax, false, false>, grid, dim3(kThreads), stream, p);
 }
 
 hipError_t launch_prefill_candidates(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
-    return launch_kernel(prefill_kernel<kModeCandidates, false>, grid, dim3(kThreads), stream, p);
+    return launch_kernel(prefill_kernel<kModeCandidates, false, false>, grid, dim3(kThreads), stream, p);
 }
 
 int prefill_rows_per_block() { return kBM; }

@@ -338,6 +338,8 @@ static int prefill_impl(const char *fn, const void *q, int64_t q_stride_row, int
     p.out_vec = aligned(out, 16) && out_stride % 4 == 0;
     p.exact_stores = p.out_vec && (int64_t)bm * out_stride * 4 < ((int64_t)1 << 31);
     p.f16 = dtype == QSA_DTYPE_FP16;
+    // Rows that all start on a 128-byte line need no line-aligned layout.
+    p.rotate = p.exact_stores && !(aligned(out, 128) && (out_stride * 4) % 128 == 0);
     return device_status(fn, qsa::launch_prefill(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -51,6 +51,7 @@ struct PrefillParams {
     int32_t out_vec;
     int32_t exact_stores;       // out_vec, and a row block's output spans < 2^31 bytes
     int32_t f16;                // Q and K are fp16, not bf16 (scores launch only)
+    int32_t rotate;             // exact_stores, and some row does not start on a 128-byte line
     // Fused top-k passes (qsa_mqa_prefill_topk); unused by the score kernel.
     int32_t topk;
     float *gmax;                // [rows][gmax_stride] maxima of 16-key groups
