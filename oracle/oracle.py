@@ -62,6 +62,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_prefill.restype = None
     lib.oracle_topk.argtypes = [P, i64, i32, i32, P, i64, i32, i32]
     lib.oracle_topk.restype = ctypes.c_int
+    lib.oracle_cache_slots.argtypes = [P, P, i32, i32, i32, P, i64, i32, i32, P, P]
+    lib.oracle_cache_slots.restype = None
+    lib.oracle_k_work.argtypes = [P, P, i32, i32, P, i32]
+    lib.oracle_k_work.restype = None
     f64 = ctypes.c_double
     lib.oracle_decode_typed.argtypes = [P, ctypes.c_int, i64, i64, i64, P, ctypes.c_int, f64, i64,
                                         i32, P, i64, i32, P, P, i32, i32, f32, P, i64, i32, i32, i32]
@@ -358,6 +362,52 @@ def prefill_typed(q_bits, q_format: str, k_bits, k_format: str, row_k_start, row
     else:
         _run_rows(lambda b, e: [call(int(sel[i]), int(sel[i]) + 1, i) for i in range(b, e)],
                   len(sel), threads)
+    return out
+
+
+def cache_slots(query_start_loc, seq_lens, num_tokens: int, block_table, storage_block_size: int,
+                compress_ratio: int = 4, common_slot_mapping=None):
+    """int64 [num_tokens]: the compressed-cache slot each token writes, or -1
+    (see oracle_cache_slots)."""
+    lib = load()
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    seq = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    assert bt.ndim == 2
+    common = None if common_slot_mapping is None else np.ascontiguousarray(common_slot_mapping, dtype=np.int64)
+    out = np.empty(num_tokens, np.int64)
+    lib.oracle_cache_slots(_ptr(qsl), _ptr(seq), len(seq), num_tokens, compress_ratio, _ptr(bt), bt.shape[1],
+                           bt.shape[1], storage_block_size, _ptr(common), _ptr(out))
+    return out
+
+
+def k_work(query_start_loc, seq_lens, max_num_work: int, compress_ratio: int = 4):
+    """int32 [max_num_work, 2]: (request, index) work items, (-1, -1) past the last."""
+    lib = load()
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    seq = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    out = np.empty((max_num_work, 2), np.int32)
+    lib.oracle_k_work(_ptr(qsl), _ptr(seq), len(seq), compress_ratio, _ptr(out), max_num_work)
+    return out
+
+
+def gather_keys(k_pool, page_table, key_counts, key_offsets, out):
+    """Paged compressed keys gathered into contiguous rows, in place in `out`
+    ([rows, 128] of the pool's element type): row key_offsets[r] + c holds
+    request r's compressed key c for c < key_counts[r], i.e. row c % page_size
+    of page page_table[r][c // page_size]; a missing page (negative id, id
+    >= the pool's pages, or past the table's columns) gives a zero row.
+    Rows no request covers are left as they are."""
+    pool = np.asarray(k_pool)
+    assert pool.ndim == 4 and pool.shape[2] == 1
+    num_pages, page_size = pool.shape[0], pool.shape[1]
+    pt = np.asarray(page_table)
+    for r in range(len(key_counts)):
+        for c in range(int(key_counts[r])):
+            slot = c // page_size
+            page = int(pt[r, slot]) if slot < pt.shape[1] else -1
+            row = int(key_offsets[r]) + c
+            out[row] = pool[page, c % page_size, 0] if 0 <= page < num_pages else 0
     return out
 
 

@@ -308,6 +308,75 @@ void oracle_prefill(const uint16_t *q, int64_t q_stride_row, int64_t q_stride_he
 }
 
 /* ---------------------------------------------------------------------- */
+/* Compressed-cache metadata [CACHE compressed_qsa_slot_mapping and the      */
+/* slot and k_work parts of _build_qsa_metadata_kernel].                    */
+
+/* Slot of the compressed key each query token writes.  Token t of request r
+ * (query_start_loc[r] <= t < query_start_loc[r+1]) at logical position pos
+ * closes a group of compress_ratio tokens when pos >= 0 and (pos+1) % cr ==
+ * 0; its compressed position cp = pos / cr lies in logical block
+ * cp / storage_block_size of the request's block-table row, at row
+ * cp % storage_block_size, so slot = block * storage_block_size +
+ * cp % storage_block_size.  -1 when the token closes no group, the logical
+ * block is past the table's columns, the block entry is negative, the
+ * token's main-cache slot (common_slot_mapping, when given) is negative, or
+ * the token is padding (past query_start_loc[num_reqs]). */
+void oracle_cache_slots(const int32_t *query_start_loc, const int32_t *seq_lens, int32_t num_reqs,
+                        int32_t num_tokens, int32_t compress_ratio, const int32_t *block_table,
+                        int64_t block_table_stride, int32_t block_table_cols,
+                        int32_t storage_block_size, const int64_t *common_slot_mapping,
+                        int64_t *slot_mapping)
+{
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        int64_t slot = -1;
+        for (int32_t r = 0; r < num_reqs; ++r) {
+            if (t < query_start_loc[r] || t >= query_start_loc[r + 1]) continue;
+            int64_t query_len = (int64_t)query_start_loc[r + 1] - query_start_loc[r];
+            int64_t pos = (int64_t)seq_lens[r] - query_len + (t - query_start_loc[r]);
+            if (pos < 0 || (pos + 1) % compress_ratio != 0) break;
+            int64_t cp = pos / compress_ratio;
+            int64_t logical_block = cp / storage_block_size;
+            if (logical_block >= block_table_cols) break;
+            int64_t block = block_table[r * block_table_stride + logical_block];
+            if (block < 0) break;
+            if (common_slot_mapping && common_slot_mapping[t] < 0) break;
+            slot = block * storage_block_size + cp % storage_block_size;
+            break;
+        }
+        slot_mapping[t] = slot;
+    }
+}
+
+/* Work items of the compressed-cache writer.  A request with query tokens
+ * owns max(seq_len//cr - (seq_len - query_len)//cr, 1) items: one per group
+ * its chunk completes, and at least one (which also commits the raw-key
+ * suffix); a request without query tokens owns none.  Items are numbered
+ * request by request; item w holds (request, index within the request),
+ * and every item past the last holds (-1, -1).  k_work is [max_num_work][2]. */
+void oracle_k_work(const int32_t *query_start_loc, const int32_t *seq_lens, int32_t num_reqs,
+                   int32_t compress_ratio, int32_t *k_work, int32_t max_num_work)
+{
+    int64_t w = 0;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        int64_t query_len = (int64_t)query_start_loc[r + 1] - query_start_loc[r];
+        if (query_len <= 0) continue;
+        int64_t groups = floor_div(seq_lens[r], compress_ratio) -
+                         floor_div((int64_t)seq_lens[r] - query_len, compress_ratio);
+        int64_t count = groups > 1 ? groups : 1;
+        for (int64_t i = 0; i < count; ++i, ++w) {
+            if (w < max_num_work) {
+                k_work[2 * w] = r;
+                k_work[2 * w + 1] = (int32_t)i;
+            }
+        }
+    }
+    for (; w < max_num_work; ++w) {
+        k_work[2 * w] = -1;
+        k_work[2 * w + 1] = -1;
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Top-k block selection [MATE-QSA intro: the caller keeps the best blocks;  */
 /* "Core Attention": request-local int32 indices, -1 padding].              */
 

@@ -607,4 +607,128 @@ def pin_typed_equal_bf16_on_exact_values():
         assert np.array_equal(_f32_bits(got), _f32_bits(base)), (qf, kf)
 
 
+# ---------------------------------------------------------------------------
+# Compressed-cache metadata and the paged key gather.
+
+_CM_QSL = np.array([0, 6, 8, 11, 15, 16, 17, 18, 18], np.int32)
+_CM_SEQ = np.array([12, 8, 12, 24, 4, 4, 2, 9], np.int32)
+_CM_BT = np.array([[5, 2], [7, -1], [4, -1], [1, 0], [3, 6], [0, 10], [11, 12], [13, 14]], np.int32)
+
+
+def pin_cache_metadata_golden():
+    rows = {r[0]: r[1:] for r in _read_golden("cache_metadata.txt")}
+    common = np.zeros(19, np.int64)
+    common[15] = -1
+    got = O.cache_slots(_CM_QSL, _CM_SEQ, 19, _CM_BT, 2, 4, common)
+    assert got.tolist() == [int(x) for x in rows["slots"]], got.tolist()
+    want = [[int(v) for v in item.split(",")] for item in rows["work"]]
+    assert O.k_work(_CM_QSL, _CM_SEQ, 12).tolist() == want
+    assert O.k_work(_CM_QSL, _CM_SEQ, 5).tolist() == want[:5]  # truncated list
+    # Without main-cache slots token 15 keeps its slot 3*2+0.
+    assert O.cache_slots(_CM_QSL, _CM_SEQ, 19, _CM_BT, 2, 4)[15] == 6
+
+
+def pin_cache_metadata_counting():
+    """Random batches against an independent characterisation: the tokens
+    with a slot are exactly the group-closing tokens (positions 3, 7, 11, ...)
+    whose block exists, each such slot names the block that holds its
+    compressed row, no two tokens share a slot, and each request owns as many
+    work items as it has group-closing tokens (at least one when it has query
+    tokens)."""
+    rng = np.random.default_rng(41)
+    for cr, sbs in ((4, 16), (4, 3), (2, 5), (1, 7)):
+        n = 9
+        qlens = rng.integers(0, 40, n)
+        seqs = (qlens + rng.integers(0, 200, n)).astype(np.int32)
+        qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+        T = int(qsl[-1]) + 2
+        cols = int(seqs.max()) // cr // sbs + 1
+        perm = rng.permutation(n * cols).astype(np.int32).reshape(n, cols)
+        perm[rng.random(perm.shape) < 0.15] = -1
+        slots = O.cache_slots(qsl, seqs, T, perm, sbs, cr)
+        seen = set()
+        for r in range(n):
+            for i in range(int(qlens[r])):
+                t = int(qsl[r]) + i
+                pos = int(seqs[r]) - int(qlens[r]) + i
+                closes = pos >= 0 and pos % cr == cr - 1
+                blk = perm[r, (pos // cr) // sbs] if closes else -1
+                if closes and blk >= 0:
+                    assert slots[t] >= 0 and slots[t] // sbs == blk and slots[t] % sbs == (pos // cr) % sbs
+                    assert int(slots[t]) not in seen
+                    seen.add(int(slots[t]))
+                else:
+                    assert slots[t] == -1, (cr, sbs, r, i)
+        assert np.all(slots[int(qsl[-1]):] == -1)
+        work = O.k_work(qsl, seqs, 4000, cr)
+        live = work[work[:, 0] >= 0]
+        for r in range(n):
+            closing = sum(1 for p in range(int(seqs[r]) - int(qlens[r]), int(seqs[r])) if p % cr == cr - 1)
+            mine = live[live[:, 0] == r]
+            want = max(closing, 1) if qlens[r] > 0 else 0
+            assert len(mine) == want and mine[:, 1].tolist() == list(range(want)), (cr, r)
+        assert live[:, 0].tolist() == sorted(live[:, 0].tolist())
+        assert np.all(work[len(live):] == -1)
+
+
+def _labelled_pool(num_pages, page_size, seed):
+    """A pool whose every row is distinct noise except feature 0, which holds
+    a label set per test."""
+    rng = np.random.default_rng(seed)
+    return normal_bf16(rng, (num_pages, page_size, 1, 128))
+
+
+def pin_gather_keys_labels():
+    """Keys labelled with their request and logical index land at rows
+    key_offsets[r] + c in order; missing pages give zero rows; rows no
+    request covers are untouched."""
+    rng = np.random.default_rng(5)
+    ps, R = 5, 4
+    counts = np.array([13, 0, 7, 22], np.int32)
+    pages = [(int(c) + ps - 1) // ps for c in counts]
+    P = sum(pages) + 3
+    order = rng.permutation(P)
+    pool = np.zeros((P, ps, 1, 128), np.uint16)
+    table = np.full((R, 6), -1, np.int32)
+    k = 0
+    for r in range(R):
+        for j in range(pages[r]):
+            table[r, j] = order[k]
+            for i in range(ps):
+                pool[order[k], i, 0, 0] = 1000 * (r + 1) + j * ps + i   # label (as bits)
+            k += 1
+    table[3, 2] = -1                                                   # a missing page
+    offsets = np.array([4, 40, 17, 60], np.int32)
+    out = np.full((90, 128), 7, np.uint16)
+    O.gather_keys(pool, table, counts, offsets, out)
+    for r in range(R):
+        for c in range(int(counts[r])):
+            row = out[offsets[r] + c]
+            if r == 3 and c // ps == 2:
+                assert np.all(row == 0)
+            else:
+                assert row[0] == 1000 * (r + 1) + c and np.all(row[1:] == 0)
+    covered = {int(offsets[r]) + c for r in range(R) for c in range(int(counts[r]))}
+    for row in range(90):
+        if row not in covered:
+            assert np.all(out[row] == 7)
+
+
+def pin_gather_then_prefill_equals_decode():
+    """Prefill over the gathered keys, each row seeing [offset_r, offset_r +
+    visible), reproduces decode over the paged cache bit for bit."""
+    inp, vis = _small_decode()
+    comp = O.comp_lens(inp.seq_lens)
+    offsets = np.concatenate([[0], np.cumsum(comp[:-1])]).astype(np.int32) + 3
+    k = np.zeros((int(comp.sum()) + 5, 128), np.uint16)
+    O.gather_keys(inp.k_pool, inp.page_table, comp, offsets, k)
+    base = _run_decode(inp, vis)
+    rows = inp.q.shape[0] * inp.q.shape[1]
+    q = np.ascontiguousarray(inp.q.reshape(rows, 4, 128))
+    req = np.repeat(np.arange(inp.q.shape[0]), inp.q.shape[1])
+    ks = offsets[req]
+    got = O.prefill(q, k, ks, ks + vis, inp.out_cols, scale=SCALE)
+    assert np.array_equal(_f32_bits(got), _f32_bits(base))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -59,6 +59,19 @@ MUTANTS = {
                                          "n * QSA_ORACLE_DIM, k_format, k_scale, scale);"),
     "typed_decode_page_row_wrong": ("int64_t k_off = (page * page_size + (c % page_size)) * QSA_ORACLE_DIM;",
                                     "int64_t k_off = (page * page_size + (c / page_size)) * QSA_ORACLE_DIM;"),
+    "slot_closing_test_shifted": ("if (pos < 0 || (pos + 1) % compress_ratio != 0) break;",
+                                  "if (pos < 0 || pos % compress_ratio != 0) break;"),
+    "slot_row_in_block_wrong": ("slot = block * storage_block_size + cp % storage_block_size;",
+                                "slot = block * storage_block_size + cp / storage_block_size;"),
+    "slot_table_width_unchecked": ("if (logical_block >= block_table_cols) break;",
+                                   "if (logical_block > block_table_cols) break;"),
+    "slot_block_zero_rejected": ("if (block < 0) break;", "if (block <= 0) break;"),
+    "slot_main_cache_ignored": ("if (common_slot_mapping && common_slot_mapping[t] < 0) break;", ""),
+    "slot_compressed_position_wrong": ("int64_t cp = pos / compress_ratio;", "int64_t cp = (pos + 1) / compress_ratio;"),
+    "work_no_minimum_item": ("int64_t count = groups > 1 ? groups : 1;", "int64_t count = groups;"),
+    "work_empty_requests_counted": ("if (query_len <= 0) continue;", "if (query_len < 0) continue;"),
+    "work_chunk_start_wrong": ("floor_div((int64_t)seq_lens[r] - query_len, compress_ratio);",
+                               "floor_div((int64_t)seq_lens[r] - query_len + 1, compress_ratio);"),
     "topk_smallest": ("if (x->value > y->value) return -1;\n    if (x->value < y->value) return 1;",
                       "if (x->value < y->value) return -1;\n    if (x->value > y->value) return 1;"),
 }
