@@ -177,6 +177,89 @@ int qsa_build_metadata(const int32_t *query_start_loc, const int32_t *seq_lens, 
     return device_status(fn, qsa::launch_metadata(p, static_cast<hipStream_t>(stream)));
 }
 
+int qsa_build_cache_metadata(const int32_t *query_start_loc, const int32_t *seq_lens, int32_t num_reqs,
+                             int32_t num_tokens, int32_t compress_ratio, const int32_t *block_table,
+                             int64_t block_table_stride, int32_t block_table_cols, int32_t storage_block_size,
+                             const int64_t *common_slot_mapping, int64_t *slot_mapping, int32_t *k_work,
+                             int32_t max_num_work, void *stream) {
+    const char *fn = "qsa_build_cache_metadata";
+    if (num_reqs < 0 || num_tokens < 0 || max_num_work < 0 || block_table_cols < 0)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative count", fn);
+    if (compress_ratio < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: compress_ratio < 1", fn);
+    if (storage_block_size < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: storage_block_size < 1", fn);
+    if (num_reqs > 1 && block_table_cols > 0 && block_table_stride < block_table_cols)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: block_table_stride < block_table_cols", fn);
+    const bool slots = slot_mapping && num_tokens > 0;
+    const bool work = k_work && max_num_work > 0;
+    if (!slots && !work) return ok();
+    if (!query_start_loc) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL query_start_loc", fn);
+    if (num_reqs > 0 && !seq_lens) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL seq_lens", fn);
+    if (slots && num_reqs > 0 && block_table_cols > 0 && !block_table)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL block_table", fn);
+    if (work && num_reqs > qsa::kCacheMetaMaxReqs)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: work items for more than %d requests", fn, qsa::kCacheMetaMaxReqs);
+    qsa::CacheMetaParams p{};
+    p.query_start_loc = query_start_loc;
+    p.seq_lens = seq_lens;
+    p.num_reqs = num_reqs;
+    p.num_tokens = num_tokens;
+    p.compress_ratio = compress_ratio;
+    p.block_table = block_table;
+    p.block_table_stride = block_table_stride;
+    p.block_table_cols = block_table ? block_table_cols : 0;
+    p.storage_block_size = storage_block_size;
+    p.common_slot_mapping = common_slot_mapping;
+    p.slot_mapping = slots ? slot_mapping : nullptr;
+    p.k_work = work ? k_work : nullptr;
+    p.max_num_work = max_num_work;
+    return device_status(fn, qsa::launch_cache_metadata(p, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_gather_keys(const void *k_cache, int32_t k_dtype, int64_t num_pages, int32_t page_size,
+                    const int32_t *page_table, int64_t page_table_stride, int32_t page_table_cols,
+                    const int32_t *key_counts, const int32_t *key_offsets, int32_t num_reqs, int32_t max_keys,
+                    void *k_out, int64_t k_out_stride, int64_t k_out_rows, void *stream) {
+    const char *fn = "qsa_gather_keys";
+    if (k_dtype != QSA_DTYPE_BF16 && k_dtype != QSA_DTYPE_FP16 && k_dtype != QSA_DTYPE_FP8_E4M3)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: key format %d", fn, k_dtype);
+    if (num_reqs < 0 || num_pages < 0 || page_table_cols < 0 || max_keys < 0 || k_out_rows < 0)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+    if (page_size < 1 || page_size > (1 << 20))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: page_size must be in [1, 2^20], got %d", fn, page_size);
+    if (max_keys > (1 << 30)) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: max_keys above 2^30", fn);
+    const int64_t elem = k_dtype == QSA_DTYPE_FP8_E4M3 ? 1 : 2;
+    if (k_out_stride < 128) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: k_out_stride < 128", fn);
+    if (num_reqs > 1 && page_table_stride < page_table_cols)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: page_table_stride < page_table_cols", fn);
+    if (num_pages > ((int64_t)1 << 46) / page_size) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: key cache too large", fn);
+    if (num_reqs == 0 || max_keys == 0 || k_out_rows == 0) return ok();
+    if (!key_counts || !key_offsets || !k_out)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL key_counts, key_offsets or k_out", fn);
+    if (num_pages > 0 && !k_cache) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL k_cache", fn);
+    if (page_table_cols > 0 && !page_table) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL page_table", fn);
+    if ((num_pages > 0 && !aligned(k_cache, 16)) || !aligned(k_out, 16) || (k_out_stride * elem) % 16 != 0)
+        return fail(QSA_ERR_LAYOUT, "%s: k_cache, k_out and the k_out row stride must be 16-byte aligned "
+                                    "(16-byte vector copies)", fn);
+    const int64_t chunks = ((int64_t)max_keys + 255) / 256;
+    if (chunks * num_reqs >= INT32_MAX) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
+    qsa::GatherParams p{};
+    p.k_cache = static_cast<const uint8_t *>(k_cache);
+    p.row_bytes = (int32_t)(128 * elem);
+    p.num_pages = num_pages;
+    p.page_size = page_size;
+    p.page_table = page_table;
+    p.page_table_stride = page_table_stride;
+    p.page_table_cols = page_table ? page_table_cols : 0;
+    p.key_counts = key_counts;
+    p.key_offsets = key_offsets;
+    p.num_reqs = num_reqs;
+    p.max_keys = max_keys;
+    p.k_out = static_cast<uint8_t *>(k_out);
+    p.k_out_stride_bytes = k_out_stride * elem;
+    p.k_out_rows = k_out_rows;
+    return device_status(fn, qsa::launch_gather_keys(p, static_cast<hipStream_t>(stream)));
+}
+
 // Query format must be bf16 or fp16; keys share it or are e4m3 codes with a
 // positive finite cache scale.
 static int check_formats(const char *fn, int32_t q_dtype, int32_t k_dtype, float k_scale) {

@@ -100,6 +100,34 @@ struct MetaParams {
     int32_t *visible, *comp_lens, *row_k_start, *row_k_end;
 };
 
+struct CacheMetaParams {
+    const int32_t *query_start_loc, *seq_lens;
+    int32_t num_reqs, num_tokens, compress_ratio;
+    const int32_t *block_table;
+    int64_t block_table_stride;
+    int32_t block_table_cols, storage_block_size;
+    const int64_t *common_slot_mapping;  // may be null
+    int64_t *slot_mapping;               // [num_tokens] or null
+    int32_t *k_work;                     // [max_num_work][2] or null
+    int32_t max_num_work;
+};
+constexpr int kCacheMetaMaxReqs = 8192;  // requests one work-item block scans in LDS
+
+struct GatherParams {
+    const uint8_t *k_cache;              // [num_pages][page_size][row_bytes]
+    int32_t row_bytes;                   // 256 (2-byte elements) or 128 (e4m3)
+    int64_t num_pages;
+    int32_t page_size;
+    const int32_t *page_table;
+    int64_t page_table_stride;
+    int32_t page_table_cols;
+    const int32_t *key_counts, *key_offsets;
+    int32_t num_reqs;
+    int32_t max_keys;                    // bound on key_counts (grid size)
+    uint8_t *k_out;
+    int64_t k_out_stride_bytes, k_out_rows;
+};
+
 // Timing events attached to every launch from the calling thread (both null
 // unless the caller armed them through the C ABI).
 struct LaunchEvents {
@@ -128,5 +156,7 @@ hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus);
 hipError_t launch_topk_floor(const FusedTopkParams &p, hipStream_t stream);
 hipError_t launch_topk_candidates(const FusedTopkParams &p, hipStream_t stream);
 hipError_t launch_metadata(const MetaParams &p, hipStream_t stream);
+hipError_t launch_cache_metadata(const CacheMetaParams &p, hipStream_t stream);
+hipError_t launch_gather_keys(const GatherParams &p, hipStream_t stream);
 
 }  // namespace qsa

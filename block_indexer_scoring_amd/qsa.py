@@ -21,12 +21,12 @@ QSA_ERR_INVALID_ARGUMENT = 1
 QSA_ERR_UNSUPPORTED = 2
 QSA_ERR_LAYOUT = 3
 QSA_ERR_DEVICE = 4
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_set_launch_events", "qsa_split_batch",
            "qsa_build_metadata", "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks",
            "qsa_mqa_prefill_topk", "qsa_prefill_topk_workspace_bytes", "qsa_mqa_decode_typed",
-           "qsa_mqa_prefill_typed")
+           "qsa_mqa_prefill_typed", "qsa_build_cache_metadata", "qsa_gather_keys")
 
 # enum qsa_dtype
 QSA_DTYPE_BF16 = 0
@@ -70,6 +70,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_mqa_decode.argtypes = [P, i64, i64, i64, P, i64, i32, P, i64, i32, P, P, i32, i32,
                                    i32, i32, f32, P, i64, i32, P]
     lib.qsa_mqa_decode.restype = ctypes.c_int
+    lib.qsa_build_cache_metadata.argtypes = [P, P, i32, i32, i32, P, i64, i32, i32, P, P, P, i32, P]
+    lib.qsa_build_cache_metadata.restype = ctypes.c_int
+    lib.qsa_gather_keys.argtypes = [P, i32, i64, i32, P, i64, i32, P, P, i32, i32, P, i64, i64, P]
+    lib.qsa_gather_keys.restype = ctypes.c_int
     lib.qsa_mqa_decode_typed.argtypes = [P, i32, i64, i64, i64, P, i32, f32, i64, i32, P, i64, i32, P, P,
                                          i32, i32, i32, i32, f32, P, i64, i32, P]
     lib.qsa_mqa_decode_typed.restype = ctypes.c_int
@@ -260,6 +264,81 @@ def qsa_mqa_prefill(q: torch.Tensor, k: torch.Tensor, row_k_start: torch.Tensor,
         _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.shape[0], _ptr(row_k_start),
         _ptr(row_k_end), num_rows, heads, dim, float(scale), _ptr(out), out.stride(0),
         out.shape[1], _stream_handle(stream)))
+    return out
+
+
+def qsa_build_cache_metadata(query_start_loc: torch.Tensor, seq_lens: torch.Tensor, num_tokens: int,
+                             block_table: torch.Tensor, storage_block_size: int, compress_ratio: int = 4,
+                             common_slot_mapping: torch.Tensor | None = None, max_num_work: int = 0,
+                             slot_mapping: torch.Tensor | None = None, k_work: torch.Tensor | None = None,
+                             stream=None):
+    """Compressed-cache slot of each token (int64 [num_tokens], -1 = none) and
+    the cache writer's work items (int32 [max_num_work, 2], (-1, -1) past the
+    last; None when max_num_work is 0).  block_table: int32 [R, cols] with unit
+    column stride."""
+    lib = load_library()
+    _gpu("query_start_loc", query_start_loc, torch.int32)
+    _gpu("seq_lens", seq_lens, torch.int32)
+    _gpu("block_table", block_table, torch.int32)
+    num_reqs = seq_lens.numel()
+    if query_start_loc.numel() != num_reqs + 1 or not query_start_loc.is_contiguous() or not seq_lens.is_contiguous():
+        raise ValueError("query_start_loc must be a contiguous [R+1] and seq_lens a contiguous [R] tensor")
+    if block_table.dim() != 2 or block_table.shape[0] != num_reqs or (block_table.shape[1] > 1 and block_table.stride(1) != 1):
+        raise ValueError("block_table must be [R, cols] with unit column stride")
+    dev = query_start_loc.device
+    if common_slot_mapping is not None:
+        _gpu("common_slot_mapping", common_slot_mapping, torch.int64)
+        if common_slot_mapping.numel() < num_tokens or not common_slot_mapping.is_contiguous():
+            raise ValueError("common_slot_mapping must be a contiguous [num_tokens] tensor")
+    if slot_mapping is None:
+        slot_mapping = torch.empty(num_tokens, dtype=torch.int64, device=dev)
+    _gpu("slot_mapping", slot_mapping, torch.int64)
+    if slot_mapping.numel() < num_tokens or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous [num_tokens] tensor")
+    if max_num_work > 0:
+        if k_work is None:
+            k_work = torch.empty((max_num_work, 2), dtype=torch.int32, device=dev)
+        _gpu("k_work", k_work, torch.int32)
+        if k_work.numel() < 2 * max_num_work or not k_work.is_contiguous():
+            raise ValueError("k_work must be a contiguous [max_num_work, 2] tensor")
+    else:
+        k_work = None
+    _check(lib.qsa_build_cache_metadata(
+        _ptr(query_start_loc), _ptr(seq_lens), num_reqs, num_tokens, compress_ratio, _ptr(block_table),
+        block_table.stride(0), block_table.shape[1], storage_block_size, _ptr(common_slot_mapping),
+        _ptr(slot_mapping), _ptr(k_work), max_num_work if k_work is not None else 0, _stream_handle(stream)))
+    return slot_mapping, k_work
+
+
+def qsa_gather_keys(k_cache: torch.Tensor, page_table: torch.Tensor, key_counts: torch.Tensor,
+                    key_offsets: torch.Tensor, max_keys: int, out: torch.Tensor | None = None,
+                    out_rows: int | None = None, stream=None) -> torch.Tensor:
+    """Request r's compressed keys 0 .. key_counts[r]-1 from the paged cache
+    (bf16, fp16 or float8_e4m3fn [P, page_size, 1, 128], contiguous) into rows
+    key_offsets[r] .. of `out` ([rows, 128] view of the same dtype, unit
+    feature stride); a missing page gives a zero row."""
+    lib = load_library()
+    fmt = _gpu_format("k_cache", k_cache, (torch.bfloat16, torch.float16, torch.float8_e4m3fn))
+    _gpu("page_table", page_table, torch.int32)
+    _gpu("key_counts", key_counts, torch.int32)
+    _gpu("key_offsets", key_offsets, torch.int32)
+    if k_cache.dim() != 4 or k_cache.shape[2] != 1 or k_cache.shape[3] != 128 or not k_cache.is_contiguous():
+        raise ValueError("k_cache must be a contiguous [P, page_size, 1, 128] tensor")
+    num_reqs = key_counts.numel()
+    if page_table.dim() != 2 or page_table.shape[0] != num_reqs or (page_table.shape[1] > 1 and page_table.stride(1) != 1):
+        raise ValueError("page_table must be [R, W] with unit column stride")
+    if key_offsets.numel() != num_reqs or not key_offsets.is_contiguous() or not key_counts.is_contiguous():
+        raise ValueError("key_counts and key_offsets must be contiguous [R] tensors")
+    if out is None:
+        if out_rows is None:
+            raise ValueError("give out_rows or out")
+        out = torch.zeros((out_rows, 128), dtype=k_cache.dtype, device=k_cache.device)
+    if out.dtype != k_cache.dtype or out.dim() != 2 or out.shape[1] != 128 or out.stride(1) != 1:
+        raise ValueError("out must be a [rows, 128] tensor of k_cache's dtype with unit feature stride")
+    _check(lib.qsa_gather_keys(
+        _ptr(k_cache), fmt, k_cache.shape[0], k_cache.shape[1], _ptr(page_table), page_table.stride(0),
+        page_table.shape[1], _ptr(key_counts), _ptr(key_offsets), num_reqs, int(max_keys), _ptr(out),
+        out.stride(0), out.shape[0], _stream_handle(stream)))
     return out
 
 

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 3
+#define QSA_ABI_VERSION 4
 
 enum qsa_status {
     QSA_OK = 0,
@@ -134,6 +134,77 @@ int qsa_build_metadata(const int32_t *query_start_loc, const int32_t *seq_lens,
                        const int32_t *key_offsets, int32_t *token_to_req, int64_t *positions,
                        int32_t *visible, int32_t *comp_lens, int32_t *row_k_start,
                        int32_t *row_k_end, void *stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_build_cache_metadata -- where each token's compressed key goes, and the
+ * work items of the compressed-cache writer.
+ *   Source: vLLM qsa_cache.py, compressed_qsa_slot_mapping and the slot
+ *   mapping (compress_ratio != 1) and k_work_metadata parts of
+ *   _build_qsa_metadata_kernel.
+ *
+ *   query_start_loc, seq_lens, num_reqs, num_tokens, compress_ratio: as
+ *     qsa_build_metadata (positions pos = seq_len - query_len + (t - start)).
+ *   block_table : device int32 [num_reqs][block_table_cols], row stride
+ *     block_table_stride: the physical block of each logical block of
+ *     storage_block_size compressed rows (-1 = none).
+ *   common_slot_mapping : device int64 [num_tokens] (the main cache's slots)
+ *     or NULL; a token whose entry is negative writes no compressed key.
+ *   slot_mapping : device int64 [num_tokens] out, or NULL.  Token t writes
+ *     the compressed key of its group when pos >= 0 and (pos+1) %
+ *     compress_ratio == 0: cp = pos / compress_ratio, slot = block_table[r]
+ *     [cp / storage_block_size] * storage_block_size + cp % storage_block_size.
+ *     -1 when no group closes, the logical block is past the table, the
+ *     entry is negative, the main-cache slot is negative, or t is padding.
+ *   k_work : device int32 [max_num_work][2] out, or NULL.  A request with
+ *     query tokens owns max(seq_len/cr - (seq_len - query_len)/cr, 1) items
+ *     (floor division), numbered request by request; item w = (request,
+ *     index within the request); items past the last are (-1, -1).
+ *   Errors: INVALID_ARGUMENT for negative counts, compress_ratio or
+ *   storage_block_size < 1, a short block_table_stride or a NULL pointer that
+ *   has work to feed; UNSUPPORTED for work items over more than 8,192
+ *   requests.  Two kernels (slots, work items) run on `stream`.
+ */
+int qsa_build_cache_metadata(const int32_t *query_start_loc, const int32_t *seq_lens,
+                             int32_t num_reqs, int32_t num_tokens, int32_t compress_ratio,
+                             const int32_t *block_table, int64_t block_table_stride,
+                             int32_t block_table_cols, int32_t storage_block_size,
+                             const int64_t *common_slot_mapping, int64_t *slot_mapping,
+                             int32_t *k_work, int32_t max_num_work, void *stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_gather_keys -- paged compressed keys gathered into contiguous rows,
+ * so that qsa_mqa_prefill can score a chunk straight from the cache.
+ *   Source: MATE "QSA (Qwen Sparse Attention)", section "MQA score" (paged
+ *   keys [pages, page_size, 1, dim], page table with -1 entries; packed
+ *   prefill keys with per-row intervals).
+ *
+ *   k_cache    : device [num_pages][page_size][1][128] elements of k_dtype
+ *                (QSA_DTYPE_BF16, QSA_DTYPE_FP16: 256 bytes per key;
+ *                QSA_DTYPE_FP8_E4M3: 128), contiguous, 16-byte aligned.
+ *                The elements are copied as they are.
+ *   page_table : device int32 [num_reqs][page_table_cols], row stride
+ *                page_table_stride.
+ *   key_counts, key_offsets : device int32 [num_reqs]: request r's keys
+ *                0 .. key_counts[r]-1 (clamped to [0, max_keys]) go to rows
+ *                key_offsets[r] .. of k_out, in order.
+ *   max_keys   : host bound on key_counts (sizes the launch).
+ *   k_out      : device [k_out_rows][k_out_stride] elements of k_dtype,
+ *                16-byte aligned, row stride k_out_stride >= 128 with
+ *                16-byte rows.  Key c of request r is row c % page_size of
+ *                page page_table[r][c / page_size]; a missing page (id < 0,
+ *                >= num_pages, or a slot past the table) gives a zero row.
+ *                Rows outside [0, k_out_rows) are skipped; rows no request
+ *                covers are left untouched.
+ *   Errors: UNSUPPORTED for another k_dtype; INVALID_ARGUMENT for negative
+ *   sizes, page_size outside [1, 1<<20], max_keys above 2^30, a short
+ *   stride or a NULL pointer that has work to feed; LAYOUT for misaligned
+ *   k_cache, k_out or rows.
+ */
+int qsa_gather_keys(const void *k_cache, int32_t k_dtype, int64_t num_pages, int32_t page_size,
+                    const int32_t *page_table, int64_t page_table_stride, int32_t page_table_cols,
+                    const int32_t *key_counts, const int32_t *key_offsets, int32_t num_reqs,
+                    int32_t max_keys, void *k_out, int64_t k_out_stride, int64_t k_out_rows,
+                    void *stream);
 
 /* ------------------------------------------------------------------------
  * qsa_mqa_decode -- decode scores over the paged compressed-key cache.

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.qsa_abi_version() == 3
+    assert lib.qsa_abi_version() == 4
 
 
 def test_launch_events_set_and_clear_without_device(lib):
@@ -157,6 +157,74 @@ def test_prefill_typed_rejects(lib, dtype, kw, code, text):
     assert _prefill_typed(lib, dtype, **kw) == code
     assert text in _err(lib)
     assert "qsa_mqa_prefill_typed" in _err(lib)
+
+
+def _cache_meta(lib, **kw):
+    a = dict(qsl=FAKE, seq=FAKE, num_reqs=3, num_tokens=10, cr=4, bt=FAKE, bt_stride=8, bt_cols=8, sbs=64,
+             common=None, slots=FAKE, work=FAKE, max_work=16)
+    a.update(kw)
+    return lib.qsa_build_cache_metadata(a["qsl"], a["seq"], a["num_reqs"], a["num_tokens"], a["cr"], a["bt"],
+                                        a["bt_stride"], a["bt_cols"], a["sbs"], a["common"], a["slots"], a["work"],
+                                        a["max_work"], None)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(num_reqs=-1), 1, "negative"),
+    (dict(max_work=-1), 1, "negative"),
+    (dict(cr=0), 1, "compress_ratio"),
+    (dict(sbs=0), 1, "storage_block_size"),
+    (dict(bt_stride=4), 1, "block_table_stride"),
+    (dict(qsl=None), 1, "query_start_loc"),
+    (dict(seq=None), 1, "seq_lens"),
+    (dict(bt=None), 1, "block_table"),
+    (dict(num_reqs=9000), 2, "8192"),
+])
+def test_cache_metadata_rejects(lib, kw, code, text):
+    assert _cache_meta(lib, **kw) == code
+    assert text in _err(lib)
+
+
+def test_cache_metadata_nothing_to_do(lib):
+    assert _cache_meta(lib, slots=None, work=None, qsl=None) == 0
+    assert _cache_meta(lib, num_tokens=0, max_work=0, qsl=None) == 0
+    assert _err(lib) == ""
+
+
+def _gather(lib, **kw):
+    a = dict(k=FAKE, fmt=0, pages=8, ps=64, pt=FAKE, pt_stride=4, pt_cols=4, counts=FAKE, offs=FAKE, num_reqs=2,
+             max_keys=256, out=FAKE, out_stride=128, out_rows=512)
+    a.update(kw)
+    return lib.qsa_gather_keys(a["k"], a["fmt"], a["pages"], a["ps"], a["pt"], a["pt_stride"], a["pt_cols"],
+                               a["counts"], a["offs"], a["num_reqs"], a["max_keys"], a["out"], a["out_stride"],
+                               a["out_rows"], None)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(fmt=3), 2, "key format"),
+    (dict(num_reqs=-1), 1, "negative"),
+    (dict(ps=0), 1, "page_size"),
+    (dict(max_keys=(1 << 30) + 1), 1, "max_keys"),
+    (dict(out_stride=100), 1, "k_out_stride"),
+    (dict(pt_stride=2), 1, "page_table_stride"),
+    (dict(counts=None), 1, "NULL"),
+    (dict(out=None), 1, "NULL"),
+    (dict(k=None), 1, "k_cache"),
+    (dict(pt=None), 1, "page_table"),
+    (dict(k=FAKE + 8), 3, "aligned"),
+    (dict(out=FAKE + 4), 3, "aligned"),
+    (dict(out_stride=132), 3, "aligned"),
+    (dict(fmt=2, out_stride=136), 3, "aligned"),
+])
+def test_gather_rejects(lib, kw, code, text):
+    assert _gather(lib, **kw) == code
+    assert text in _err(lib)
+
+
+def test_gather_nothing_to_do(lib):
+    assert _gather(lib, num_reqs=0, counts=None, out=None) == 0
+    assert _gather(lib, max_keys=0, counts=None) == 0
+    assert _gather(lib, fmt=2, out_stride=144, out_rows=0) == 0
+    assert _err(lib) == ""
 
 
 def test_decode_zero_work_is_ok_without_device(lib):

@@ -1,0 +1,151 @@
+"""GPU parity: qsa_build_cache_metadata (compressed-cache slots, writer work
+items) and qsa_gather_keys (paged keys into contiguous rows) against the
+oracle; bit-exact (integer and copy work)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tests.oracle_pins import _CM_BT, _CM_QSL, _CM_SEQ, _read_golden
+from tests.parity import bf16_to_device, f32_bits, i32_to_device
+from workloads import FP8_K_SCALE, WORKLOADS, decode_inputs, fp8_e4m3_cache
+
+pytestmark = pytest.mark.gpu
+
+
+def _qsa():
+    import block_indexer_scoring_amd as qsa
+    qsa.load_library()
+    return qsa
+
+
+def _meta(qsl, seq, T, bt, sbs, cr=4, common=None, max_work=0):
+    qsa = _qsa()
+    cm = None if common is None else torch.from_numpy(np.ascontiguousarray(common, np.int64)).cuda()
+    slots = torch.full((T,), 12345, dtype=torch.int64, device="cuda")
+    work = torch.full((max(max_work, 1), 2), 777, dtype=torch.int32, device="cuda")
+    s, w = qsa.qsa_build_cache_metadata(i32_to_device(qsl), i32_to_device(seq), T, i32_to_device(bt), sbs, cr,
+                                        common_slot_mapping=cm, max_num_work=max_work, slot_mapping=slots,
+                                        k_work=work if max_work else None)
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), (None if w is None else w.cpu().numpy())
+
+
+def test_cache_metadata_golden_batch():
+    rows = {r[0]: r[1:] for r in _read_golden("cache_metadata.txt")}
+    common = np.zeros(19, np.int64)
+    common[15] = -1
+    slots, work = _meta(_CM_QSL, _CM_SEQ, 19, _CM_BT, 2, 4, common, max_work=12)
+    assert slots.tolist() == [int(x) for x in rows["slots"]]
+    assert work.tolist() == [[int(v) for v in it.split(",")] for it in rows["work"]]
+    _, work5 = _meta(_CM_QSL, _CM_SEQ, 19, _CM_BT, 2, 4, common, max_work=5)
+    assert np.array_equal(work5, work[:5])
+
+
+@pytest.mark.parametrize("seed,cr,sbs,n", [(1, 4, 64, 40), (2, 4, 3, 300), (3, 2, 7, 9), (4, 1, 16, 2000),
+                                           (5, 4, 16, 8192)])
+def test_cache_metadata_random_batches(seed, cr, sbs, n):
+    rng = np.random.default_rng(seed)
+    qlens = rng.integers(0, 12, n)
+    qlens[rng.integers(0, n)] = 900                        # one long prefill chunk
+    seqs = (qlens + rng.integers(0, 5000, n)).astype(np.int32)
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qsl[-1]) + 37                                   # padding tokens
+    cols = int(seqs.max()) // cr // sbs + 2
+    bt = rng.integers(-1, 1 << 20, (n, cols)).astype(np.int32)
+    common = rng.integers(-1, 1 << 30, T).astype(np.int64)
+    W = int(rng.integers(1, 3 * T))
+    slots, work = _meta(qsl, seqs, T, bt, sbs, cr, common, max_work=W)
+    assert np.array_equal(slots, O.cache_slots(qsl, seqs, T, bt, sbs, cr, common))
+    assert np.array_equal(work, O.k_work(qsl, seqs, W, cr))
+    slots2, _ = _meta(qsl, seqs, T, bt, sbs, cr)           # no main-cache slots
+    assert np.array_equal(slots2, O.cache_slots(qsl, seqs, T, bt, sbs, cr))
+
+
+def test_cache_metadata_mixed_step_batch():
+    # The mixed step's batch: 16 decode requests (DQL 4) and one 8,192-token
+    # prefill chunk over a 100,000-token prefix; page size 64.
+    dec = WORKLOADS["specdecode_16x51k"].make()
+    R, DQL = dec.q.shape[0], dec.q.shape[1]
+    qlens = [DQL] * R + [8192]
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    seqs = np.concatenate([dec.seq_lens, [108192]]).astype(np.int32)
+    cols = max(dec.page_table.shape[1], 108192 // 4 // 64 + 1)
+    bt = np.full((R + 1, cols), -1, np.int32)
+    bt[:R, :dec.page_table.shape[1]] = dec.page_table
+    bt[R] = np.random.default_rng(9).permutation(cols) + 5000
+    T = int(qsl[-1])
+    slots, work = _meta(qsl, seqs, T, bt, 64, 4, max_work=4096)
+    assert np.array_equal(slots, O.cache_slots(qsl, seqs, T, bt, 64, 4))
+    assert np.array_equal(work, O.k_work(qsl, seqs, 4096, 4))
+    assert (slots >= 0).sum() == R + 8192 // 4  # one closing token per decode request, 2,048 in the chunk
+
+
+def _gather(pool, table, counts, offsets, max_keys, out):
+    qsa = _qsa()
+    qsa.qsa_gather_keys(pool, i32_to_device(table), i32_to_device(counts), i32_to_device(offsets), max_keys, out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("fmt,page_size", [("bf16", 64), ("bf16", 5), ("fp16", 16), ("fp8_e4m3", 64), ("fp8_e4m3", 7)])
+def test_gather_keys_against_oracle(fmt, page_size):
+    rng = np.random.default_rng(page_size)
+    inp = decode_inputs([3000, 517, 12, 8400, 0], 1, page_size, 500, 4, 2200, seed=page_size)
+    table = inp.page_table.copy()
+    table[1, 2] = -1
+    table[3, 5] = inp.k_pool.shape[0] + 3
+    counts = O.comp_lens(inp.seq_lens).astype(np.int32)
+    counts[0] += 9                                          # runs past the request's pages into -1 entries
+    # Disjoint destinations; the end of request 3 falls past the last row.
+    offsets = np.array([5, 800, 950, 1000, 40], np.int32)
+    rows = 3000
+    if fmt == "fp8_e4m3":
+        pool_bits = fp8_e4m3_cache(inp.k_pool)
+        pool = torch.from_numpy(pool_bits).cuda().view(torch.float8_e4m3fn)
+        out = torch.full((rows, 128), 0x5A, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+        host = np.full((rows, 128), 0x5A, np.uint8)
+    else:
+        pool_bits = inp.k_pool
+        dt = torch.bfloat16 if fmt == "bf16" else torch.float16
+        pool = torch.from_numpy(pool_bits.view(np.int16)).cuda().view(dt)
+        out = torch.full((rows, 128), 0x3A5A, dtype=torch.int16, device="cuda").view(dt)
+        host = np.full((rows, 128), 0x3A5A, np.uint16)
+    max_keys = int(counts.max())
+    _gather(pool, table, counts, offsets, max_keys, out)
+    # The oracle's gather, restricted to destinations inside the output.
+    want = np.concatenate([host, np.zeros((4000, 128), host.dtype)])
+    O.gather_keys(pool_bits, table, counts, offsets, want)
+    want = want[:rows]
+    got = out.view(torch.uint8 if fmt == "fp8_e4m3" else torch.int16).cpu().numpy().view(host.dtype)
+    assert np.array_equal(got, want)
+    # A smaller max_keys clamps every request's count.
+    out2 = out.clone().view(torch.uint8 if fmt == "fp8_e4m3" else torch.int16).fill_(0x11).view(out.dtype)
+    _gather(pool, table, counts, offsets, 100, out2)
+    want2 = np.concatenate([np.full((rows, 128), 0x11 if fmt == "fp8_e4m3" else 0x0011, host.dtype),
+                            np.zeros((4000, 128), host.dtype)])
+    O.gather_keys(pool_bits, table, np.minimum(counts, 100), offsets, want2)
+    got2 = out2.view(torch.uint8 if fmt == "fp8_e4m3" else torch.int16).cpu().numpy().view(host.dtype)
+    assert np.array_equal(got2, want2[:rows])
+
+
+def test_gather_then_prefill_equals_decode():
+    # The spec-decode batch scored by decode over its paged cache, and by
+    # prefill over the same keys gathered into one packed K: bit-exact.
+    qsa = _qsa()
+    inp = WORKLOADS["specdecode_16x51k"].make()
+    R, DQL = inp.q.shape[0], inp.q.shape[1]
+    _, _, vis = O.token_metadata(inp.query_start_loc, inp.seq_lens, R * DQL)
+    comp = O.comp_lens(inp.seq_lens).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(comp[:-1])]).astype(np.int32)
+    pool, table = bf16_to_device(inp.k_pool), i32_to_device(inp.page_table)
+    k = torch.zeros((int(comp.sum()), 128), dtype=torch.bfloat16, device="cuda")
+    qsa.qsa_gather_keys(pool, table, i32_to_device(comp), i32_to_device(offsets), int(comp.max()), out=k)
+    dec = qsa.qsa_mqa_decode(bf16_to_device(inp.q), pool, table, i32_to_device(comp), i32_to_device(vis),
+                             out_cols=inp.out_cols)
+    req = np.repeat(np.arange(R), DQL)
+    ks = offsets[req]
+    pre = qsa.qsa_mqa_prefill(bf16_to_device(inp.q).reshape(R * DQL, 4, 128), k, i32_to_device(ks),
+                              i32_to_device(ks + vis), out_cols=inp.out_cols)
+    torch.cuda.synchronize()
+    assert np.array_equal(f32_bits(pre), f32_bits(dec))
