@@ -458,6 +458,53 @@ def main(argv=None) -> int:
         e.close()
     del q16, k16
 
+    # The compressed-cache metadata of the step's batch (the decode requests'
+    # page tables and a block table for the prefill chunk, page size 64,
+    # 4,096 work-item slots), and the paged-key gather of the decode batch's
+    # whole key set into one packed K (the keys a prefill over those requests
+    # would read), both timed over 20 launches; the gather rotates the pools.
+    cols = max(dec.page_table.shape[1], int(seq[-1]) // 4 // dec.page_size + 1)
+    bt_host = np.full((R + 1, cols), -1, np.int32)
+    bt_host[:R, :dec.page_table.shape[1]] = dec.page_table
+    bt_host[R] = np.random.default_rng(6).permutation(cols) + dec.k_pool.shape[0]
+    bt = to_i32(bt_host)
+    cm_slots = torch.empty(T_all, dtype=torch.int64, device=dev)
+    cm_work = torch.empty((4096, 2), dtype=torch.int32, device=dev)
+    comp_dec = to_i32(comp_host[:R])
+    gk_off = to_i32(np.concatenate([[0], np.cumsum(comp_host[:R - 1])]))
+    gk_out = torch.empty((int(comp_total), 128), dtype=torch.bfloat16, device=dev)
+    cm_ev = [HipEvents(2) for _ in range(20)]
+    gk_ev = [HipEvents(2) for _ in range(20)]
+    for j in range(24):
+        if j >= 4:
+            check(lib.qsa_set_launch_events(cm_ev[j - 4].ev[0], cm_ev[j - 4].ev[1]))
+        check(lib.qsa_build_cache_metadata(
+            qsl_d.data_ptr(), seq_d.data_ptr(), R + 1, T_all, 4, bt.data_ptr(), bt.stride(0), bt.shape[1],
+            dec.page_size, None, cm_slots.data_ptr(), cm_work.data_ptr(), 4096, sh))
+        if j >= 4:
+            check(lib.qsa_set_launch_events(gk_ev[j - 4].ev[0], gk_ev[j - 4].ev[1]))
+        pool = pools[j % len(pools)]
+        check(lib.qsa_gather_keys(
+            pool.data_ptr(), qsa.QSA_DTYPE_BF16, pool.shape[0], pool.shape[1], page_table.data_ptr(),
+            page_table.stride(0), page_table.shape[1], comp_dec.data_ptr(), gk_off.data_ptr(), R,
+            int(comp_host[:R].max()), gk_out.data_ptr(), gk_out.stride(0), gk_out.shape[0], sh))
+        check(lib.qsa_set_launch_events(None, None))
+    torch.cuda.synchronize()
+    # The cache-metadata call is two kernels; the events bracket the first
+    # kernel's begin and the last one's end.
+    cm_us = float(np.mean([e.elapsed_us(0, 1) for e in cm_ev]))
+    gk_us = float(np.mean([e.elapsed_us(0, 1) for e in gk_ev]))
+    gk_bytes = 2.0 * comp_total * 256
+    result["cache_metadata"] = {"us": round(cm_us, 3), "tokens": T_all, "requests": R + 1, "work_items": 4096}
+    result["gather_keys"] = {
+        "us": round(gk_us, 3), "keys": int(comp_total), "bytes": gk_bytes,
+        "gbps": round(gk_bytes / (gk_us * 1e-6) / 1e9, 2),
+        "frac_of_hbm": round(gk_bytes / (gk_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+    }
+    for e in cm_ev + gk_ev:
+        e.close()
+    del gk_out
+
     # A measured bandwidth for context: a plain 1 GiB device-to-device copy
     # (read + write bytes over its time), and each HBM-bound kernel's rate as
     # a fraction of it.

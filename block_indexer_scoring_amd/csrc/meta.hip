@@ -168,15 +168,14 @@ __global__ __launch_bounds__(kThreads) void k_work_kernel(CacheMetaParams p) {
 
 }  // namespace
 
-hipError_t launch_cache_metadata(const CacheMetaParams &p, hipStream_t stream) {
-    hipError_t e = hipSuccess;
-    if (p.slot_mapping && p.num_tokens > 0)
-        e = launch_kernel(cache_slots_kernel, dim3((unsigned)((p.num_tokens + kThreads - 1) / kThreads)),
-                          dim3(kThreads), stream, p);
-    if (e == hipSuccess && p.k_work && p.max_num_work > 0)
-        e = launch_kernel(k_work_kernel, dim3((unsigned)((p.max_num_work + kThreads - 1) / kThreads)),
-                          dim3(kThreads), stream, p);
-    return e;
+hipError_t launch_cache_slots(const CacheMetaParams &p, hipStream_t stream) {
+    return launch_kernel(cache_slots_kernel, dim3((unsigned)((p.num_tokens + kThreads - 1) / kThreads)),
+                         dim3(kThreads), stream, p);
+}
+
+hipError_t launch_k_work(const CacheMetaParams &p, hipStream_t stream) {
+    return launch_kernel(k_work_kernel, dim3((unsigned)((p.max_num_work + kThreads - 1) / kThreads)),
+                         dim3(kThreads), stream, p);
 }
 
 hipError_t launch_metadata(const MetaParams &p, hipStream_t stream) {

@@ -212,7 +212,21 @@ int qsa_build_cache_metadata(const int32_t *query_start_loc, const int32_t *seq_
     p.slot_mapping = slots ? slot_mapping : nullptr;
     p.k_work = work ? k_work : nullptr;
     p.max_num_work = max_num_work;
-    return device_status(fn, qsa::launch_cache_metadata(p, static_cast<hipStream_t>(stream)));
+    // Up to two launches; armed timing events span them (start on the first,
+    // stop on the last).
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const qsa::LaunchEvents ev = g_launch_events;
+    hipError_t err = hipSuccess;
+    if (slots) {
+        g_launch_events = {ev.start, work ? nullptr : ev.stop};
+        err = qsa::launch_cache_slots(p, st);
+    }
+    if (work && err == hipSuccess) {
+        g_launch_events = {slots ? nullptr : ev.start, ev.stop};
+        err = qsa::launch_k_work(p, st);
+    }
+    g_launch_events = ev;
+    return device_status(fn, err);
 }
 
 int qsa_gather_keys(const void *k_cache, int32_t k_dtype, int64_t num_pages, int32_t page_size,

@@ -156,7 +156,8 @@ hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus);
 hipError_t launch_topk_floor(const FusedTopkParams &p, hipStream_t stream);
 hipError_t launch_topk_candidates(const FusedTopkParams &p, hipStream_t stream);
 hipError_t launch_metadata(const MetaParams &p, hipStream_t stream);
-hipError_t launch_cache_metadata(const CacheMetaParams &p, hipStream_t stream);
+hipError_t launch_cache_slots(const CacheMetaParams &p, hipStream_t stream);  // p.slot_mapping set
+hipError_t launch_k_work(const CacheMetaParams &p, hipStream_t stream);       // p.k_work set
 hipError_t launch_gather_keys(const GatherParams &p, hipStream_t stream);
 
 }  // namespace qsa
