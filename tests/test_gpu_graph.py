@@ -11,7 +11,7 @@ import torch
 
 from oracle import oracle as O
 from tests.parity import bf16_to_device, i32_to_device
-from workloads import decode_inputs, normal_bf16
+from workloads import FP8_K_SCALE, decode_inputs, fp8_e4m3_cache, normal_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,17 @@ def test_capture_and_replay_all_entry_points():
     top = torch.empty((T, K), dtype=torch.int32, device=dev)
     fused = torch.empty((T, K), dtype=torch.int32, device=dev)
     ws = torch.empty(qsa.qsa_prefill_topk_workspace_bytes(T, cols, K), dtype=torch.uint8, device=dev)
-    outs = (dec_out, pre_out, top, fused, meta[0], meta[1], meta[2], meta[3])
+    # Typed decode over an e4m3 copy of the cache, the cache metadata and
+    # the key gather of the decode batch.
+    pool8 = torch.from_numpy(fp8_e4m3_cache(dec.k_pool)).cuda().view(torch.float8_e4m3fn)
+    dec8 = torch.empty_like(dec_out)
+    bt = pt
+    slots = torch.empty(n_tok, dtype=torch.int64, device=dev)
+    work = torch.empty((32, 2), dtype=torch.int32, device=dev)
+    comp_np = O.comp_lens(dec.seq_lens).astype(np.int32)
+    offs = i32_to_device(np.concatenate([[0], np.cumsum(comp_np[:-1])]))
+    kg = torch.empty((int(comp_np.sum()), 128), dtype=torch.bfloat16, device=dev)
+    outs = (dec_out, pre_out, top, fused, meta[0], meta[1], meta[2], meta[3], dec8, slots, work, kg)
 
     def run():
         assert lib.qsa_build_metadata(qsl.data_ptr(), seq.data_ptr(), 3, n_tok, 4, None, meta[0].data_ptr(),
@@ -54,6 +64,9 @@ def test_capture_and_replay_all_entry_points():
         qsa.qsa_mqa_prefill(q_pre, k_pre, ks, ke, out=pre_out)
         qsa.qsa_topk_blocks(pre_out, K, out=top)
         qsa.qsa_mqa_prefill_topk(q_pre, k_pre, ks, ke, cols, K, out=fused, workspace=ws)
+        qsa.qsa_mqa_decode_typed(q_dec, pool8, pt, comp, visd, k_scale=FP8_K_SCALE, out=dec8)
+        qsa.qsa_build_cache_metadata(qsl, seq, n_tok, bt, 16, 4, max_num_work=32, slot_mapping=slots, k_work=work)
+        qsa.qsa_gather_keys(pool, pt, comp, offs, int(comp_np.max()), out=kg)
 
     run()
     torch.cuda.synchronize()
@@ -63,6 +76,9 @@ def test_capture_and_replay_all_entry_points():
     assert np.array_equal(want[4].cpu().numpy(), req) and np.array_equal(want[5].cpu().numpy(), pos)
     assert np.array_equal(want[6].cpu().numpy(), vis_o)
     assert np.array_equal(want[7].cpu().numpy(), O.comp_lens(dec.seq_lens))
+    assert np.array_equal(want[9].cpu().numpy(), O.cache_slots(dec.query_start_loc, dec.seq_lens, n_tok,
+                                                               dec.page_table, 16, 4))
+    assert np.array_equal(want[10].cpu().numpy(), O.k_work(dec.query_start_loc, dec.seq_lens, 32, 4))
 
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -76,14 +92,15 @@ def test_capture_and_replay_all_entry_points():
     torch.cuda.synchronize()
     for rep in range(4):
         for o in outs:
-            o.view(torch.int32).fill_(0x7FC00000 + rep)   # poison between replays (eager)
+            o.view(torch.int16).fill_(0x7FC0 + rep)     # poison between replays (eager)
         assert not torch.equal(outs[0], want[0])
         scratch = torch.empty_like(dec_out)
         qsa.qsa_mqa_decode(q_dec, pool, pt, comp, visd, out=scratch)  # eager library work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        names = ("decode", "prefill", "top-k", "fused top-k", "token_to_req", "positions", "visible", "comp_lens")
+        names = ("decode", "prefill", "top-k", "fused top-k", "token_to_req", "positions", "visible", "comp_lens",
+                 "fp8 decode", "cache slots", "work items", "gathered keys")
         for name, o, w in zip(names, outs, want):
             assert torch.equal(o, w), f"replay {rep}: {name} differs"
         assert torch.equal(scratch.view(torch.int32), want[0].view(torch.int32))
