@@ -57,7 +57,7 @@ def assert_scores_match(gpu, ref, what=""):
 
 
 def assert_topk_valid(picks, ref_scores, k):
-    """Top-k picks made on GPU scores, judged with the oracle's scores."""
+    """Top-k picks made on GPU scores, checked with the oracle's scores."""
     picks = picks.detach().cpu().numpy() if isinstance(picks, torch.Tensor) else np.asarray(picks)
     ref = np.asarray(ref_scores)
     for t in range(picks.shape[0]):

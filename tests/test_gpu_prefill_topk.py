@@ -4,7 +4,7 @@ The fused call must return exactly what qsa_topk_blocks returns on the
 output of qsa_mqa_prefill with the same arguments (bit for bit: same scores,
 same tie rule).  That composition is itself checked against the oracle in
 test_gpu_prefill.py and test_gpu_topk_meta.py; here the fused picks are also
-judged against the oracle's scores (the top-k tolerance rule) and, for
+checked against the oracle's scores (the top-k tolerance rule) and, for
 exact ties, against the oracle's selection rule run on the GPU scores.
 """
 import numpy as np
@@ -59,7 +59,7 @@ def test_fused_equals_composition_full_size(name, topk):
     ks, ke = _intervals(inp)
     fused, composed, _ = _both(inp.q, inp.k, ks, ke, inp.out_cols, topk)
     _assert_same(fused, composed, f"{name} top-{topk}")
-    # Sampled rows judged with the oracle's own scores.
+    # Sampled rows checked with the oracle's own scores.
     rows = np.array([0, 1, 2, 127, 128, 4095, inp.q.shape[0] - 1])
     ref = O.prefill(inp.q, inp.k, ks, ke, inp.out_cols, rows=rows)
     assert_topk_valid(fused[torch.from_numpy(rows).cuda()], ref, topk)

@@ -133,7 +133,7 @@ def test_prefill_fp16_small_full(T, NK, cols):
     assert_scores_match(gpu, O.prefill_typed(q, "fp16", k, "fp16", ks, ke, cols), f"fp16 T={T}")
 
 
-def test_prefill_fp16_north_star_shape_sampled():
+def test_prefill_fp16_1x8k_over_100k_sampled():
     # 1x8K queries over a 100K prefix, inputs rounded to fp16.
     inp = WORKLOADS["prefill_1x8k_100k"].make()
     T = inp.q.shape[0]
