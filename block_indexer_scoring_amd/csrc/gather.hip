@@ -6,7 +6,11 @@
 // receives request r's compressed key c (c < key_counts[r]): row c %
 // page_size of page page_table[r][c / page_size].  A missing page (negative
 // or out-of-range id, or a slot past the table) gives a zero row;
-// destinations outside [0, k_out_rows) are skipped.
+// destinations outside [0, k_out_rows) are skipped.  Rows are copied as
+// they are, or e4m3 codes are widened exactly to bf16 or fp16 values on the
+// way (the same conversion as the e4m3 decode path): with the cache scale
+// folded into the score multiplier, the 16-bit prefill then scores an e4m3
+// cache exactly as the e4m3 decode does.
 //
 // The copy is HBM-bound: one wavefront moves 64 key rows.  A key row
 // (256 bytes of 2-byte elements, or 128 bytes of e4m3 codes) is spread over
@@ -24,9 +28,13 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kKeysPerWave = 64;
 
-template <int ROW_BYTES, bool kOnePage>
+// IN_ROW / OUT_ROW: bytes per key row read / written; WIDEN: 0 copy, 1 e4m3
+// -> bf16, 2 e4m3 -> fp16 (OUT_ROW = 2 * IN_ROW).
+template <int IN_ROW, int OUT_ROW, int WIDEN, bool kOnePage>
 __global__ __launch_bounds__(kWaves * 64) void gather_keys_kernel(GatherParams p) {
-    constexpr int kLanesPerRow = ROW_BYTES / 16;
+    static_assert(WIDEN == 0 ? IN_ROW == OUT_ROW : 2 * IN_ROW == OUT_ROW, "row sizes");
+    constexpr int kLanesPerRow = OUT_ROW / 16;
+    constexpr int kInBytes = IN_ROW / kLanesPerRow;  // bytes each lane reads per row: 16, or 8 when widening
     constexpr int kRowsPerOp = 64 / kLanesPerRow;
     constexpr int kOps = kKeysPerWave / kRowsPerOp;
     const int lane = threadIdx.x & 63;
@@ -57,9 +65,22 @@ __global__ __launch_bounds__(kWaves * 64) void gather_keys_kernel(GatherParams p
                 const int slot = c / p.page_size;
                 page = slot < p.page_table_cols ? p.page_table[(int64_t)r * p.page_table_stride + slot] : -1;
             }
-            if (page >= 0 && page < p.num_pages)
-                v[i] = load_u32x4(p.k_cache + ((int64_t)page * p.page_size + c % p.page_size) * ROW_BYTES + 16 * part);
+            if (page >= 0 && page < p.num_pages) {
+                const uint8_t *src = p.k_cache + ((int64_t)page * p.page_size + c % p.page_size) * IN_ROW + kInBytes * part;
+                if constexpr (WIDEN == 0) {
+                    v[i] = load_u32x4(src);
+                } else {
+                    const uint2 w = *reinterpret_cast<const uint2 *>(src);
+                    v[i][0] = w.x;
+                    v[i][1] = w.y;
+                }
+            }
         }
+    }
+    if constexpr (WIDEN != 0) {
+        // Code 0 (and the zero row of a missing page) widens to +0.
+#pragma unroll
+        for (int i = 0; i < kOps; ++i) v[i] = e4m3x8_to_16bit<WIDEN == 2>(v[i][0], v[i][1]);
     }
 #pragma unroll
     for (int i = 0; i < kOps; ++i) {
@@ -75,13 +96,22 @@ __global__ __launch_bounds__(kWaves * 64) void gather_keys_kernel(GatherParams p
 hipError_t launch_gather_keys(const GatherParams &p, hipStream_t stream) {
     const int64_t chunks = ((int64_t)p.max_keys + kKeysPerWave * kWaves - 1) / (kKeysPerWave * kWaves);
     const dim3 grid((unsigned)(chunks * p.num_reqs));
+    const dim3 block(kWaves * 64);
     const bool one_page = p.page_size % kKeysPerWave == 0;
-    if (p.row_bytes == 128) {
-        if (one_page) return launch_kernel(gather_keys_kernel<128, true>, grid, dim3(kWaves * 64), stream, p);
-        return launch_kernel(gather_keys_kernel<128, false>, grid, dim3(kWaves * 64), stream, p);
+    if (p.widen == 1) {
+        if (one_page) return launch_kernel(gather_keys_kernel<128, 256, 1, true>, grid, block, stream, p);
+        return launch_kernel(gather_keys_kernel<128, 256, 1, false>, grid, block, stream, p);
     }
-    if (one_page) return launch_kernel(gather_keys_kernel<256, true>, grid, dim3(kWaves * 64), stream, p);
-    return launch_kernel(gather_keys_kernel<256, false>, grid, dim3(kWaves * 64), stream, p);
+    if (p.widen == 2) {
+        if (one_page) return launch_kernel(gather_keys_kernel<128, 256, 2, true>, grid, block, stream, p);
+        return launch_kernel(gather_keys_kernel<128, 256, 2, false>, grid, block, stream, p);
+    }
+    if (p.row_bytes == 128) {
+        if (one_page) return launch_kernel(gather_keys_kernel<128, 128, 0, true>, grid, block, stream, p);
+        return launch_kernel(gather_keys_kernel<128, 128, 0, false>, grid, block, stream, p);
+    }
+    if (one_page) return launch_kernel(gather_keys_kernel<256, 256, 0, true>, grid, block, stream, p);
+    return launch_kernel(gather_keys_kernel<256, 256, 0, false>, grid, block, stream, p);
 }
 
 }  // namespace qsa

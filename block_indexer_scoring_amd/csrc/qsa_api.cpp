@@ -232,16 +232,20 @@ int qsa_build_cache_metadata(const int32_t *query_start_loc, const int32_t *seq_
 int qsa_gather_keys(const void *k_cache, int32_t k_dtype, int64_t num_pages, int32_t page_size,
                     const int32_t *page_table, int64_t page_table_stride, int32_t page_table_cols,
                     const int32_t *key_counts, const int32_t *key_offsets, int32_t num_reqs, int32_t max_keys,
-                    void *k_out, int64_t k_out_stride, int64_t k_out_rows, void *stream) {
+                    void *k_out, int32_t out_dtype, int64_t k_out_stride, int64_t k_out_rows, void *stream) {
     const char *fn = "qsa_gather_keys";
     if (k_dtype != QSA_DTYPE_BF16 && k_dtype != QSA_DTYPE_FP16 && k_dtype != QSA_DTYPE_FP8_E4M3)
         return fail(QSA_ERR_UNSUPPORTED, "%s: key format %d", fn, k_dtype);
+    const bool widen = k_dtype == QSA_DTYPE_FP8_E4M3 && (out_dtype == QSA_DTYPE_BF16 || out_dtype == QSA_DTYPE_FP16);
+    if (out_dtype != k_dtype && !widen)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: output format %d: the key format, or bf16/fp16 for e4m3 keys", fn,
+                    out_dtype);
     if (num_reqs < 0 || num_pages < 0 || page_table_cols < 0 || max_keys < 0 || k_out_rows < 0)
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
     if (page_size < 1 || page_size > (1 << 20))
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: page_size must be in [1, 2^20], got %d", fn, page_size);
     if (max_keys > (1 << 30)) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: max_keys above 2^30", fn);
-    const int64_t elem = k_dtype == QSA_DTYPE_FP8_E4M3 ? 1 : 2;
+    const int64_t elem = out_dtype == QSA_DTYPE_FP8_E4M3 ? 1 : 2;  // output element bytes
     if (k_out_stride < 128) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: k_out_stride < 128", fn);
     if (num_reqs > 1 && page_table_stride < page_table_cols)
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: page_table_stride < page_table_cols", fn);
@@ -258,7 +262,8 @@ int qsa_gather_keys(const void *k_cache, int32_t k_dtype, int64_t num_pages, int
     if (chunks * num_reqs >= INT32_MAX) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
     qsa::GatherParams p{};
     p.k_cache = static_cast<const uint8_t *>(k_cache);
-    p.row_bytes = (int32_t)(128 * elem);
+    p.row_bytes = k_dtype == QSA_DTYPE_FP8_E4M3 ? 128 : 256;
+    p.widen = widen ? (out_dtype == QSA_DTYPE_FP16 ? 2 : 1) : 0;
     p.num_pages = num_pages;
     p.page_size = page_size;
     p.page_table = page_table;

@@ -126,6 +126,7 @@ struct GatherParams {
     int32_t max_keys;                    // bound on key_counts (grid size)
     uint8_t *k_out;
     int64_t k_out_stride_bytes, k_out_rows;
+    int32_t widen;                       // 0: copy rows; 1 / 2: e4m3 codes -> bf16 / fp16 values
 };
 
 // Timing events attached to every launch from the calling thread (both null

@@ -21,7 +21,7 @@ QSA_ERR_INVALID_ARGUMENT = 1
 QSA_ERR_UNSUPPORTED = 2
 QSA_ERR_LAYOUT = 3
 QSA_ERR_DEVICE = 4
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_set_launch_events", "qsa_split_batch",
            "qsa_build_metadata", "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks",
@@ -72,7 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_mqa_decode.restype = ctypes.c_int
     lib.qsa_build_cache_metadata.argtypes = [P, P, i32, i32, i32, P, i64, i32, i32, P, P, P, i32, P]
     lib.qsa_build_cache_metadata.restype = ctypes.c_int
-    lib.qsa_gather_keys.argtypes = [P, i32, i64, i32, P, i64, i32, P, P, i32, i32, P, i64, i64, P]
+    lib.qsa_gather_keys.argtypes = [P, i32, i64, i32, P, i64, i32, P, P, i32, i32, P, i32, i64, i64, P]
     lib.qsa_gather_keys.restype = ctypes.c_int
     lib.qsa_mqa_decode_typed.argtypes = [P, i32, i64, i64, i64, P, i32, f32, i64, i32, P, i64, i32, P, P,
                                          i32, i32, i32, i32, f32, P, i64, i32, P]
@@ -315,8 +315,9 @@ def qsa_gather_keys(k_cache: torch.Tensor, page_table: torch.Tensor, key_counts:
                     out_rows: int | None = None, stream=None) -> torch.Tensor:
     """Request r's compressed keys 0 .. key_counts[r]-1 from the paged cache
     (bf16, fp16 or float8_e4m3fn [P, page_size, 1, 128], contiguous) into rows
-    key_offsets[r] .. of `out` ([rows, 128] view of the same dtype, unit
-    feature stride); a missing page gives a zero row."""
+    key_offsets[r] .. of `out` ([rows, 128], unit feature stride; the cache's
+    dtype, or bf16/fp16 for an e4m3 cache, whose codes are then widened
+    exactly); a missing page gives a zero row."""
     lib = load_library()
     fmt = _gpu_format("k_cache", k_cache, (torch.bfloat16, torch.float16, torch.float8_e4m3fn))
     _gpu("page_table", page_table, torch.int32)
@@ -333,12 +334,14 @@ def qsa_gather_keys(k_cache: torch.Tensor, page_table: torch.Tensor, key_counts:
         if out_rows is None:
             raise ValueError("give out_rows or out")
         out = torch.zeros((out_rows, 128), dtype=k_cache.dtype, device=k_cache.device)
-    if out.dtype != k_cache.dtype or out.dim() != 2 or out.shape[1] != 128 or out.stride(1) != 1:
-        raise ValueError("out must be a [rows, 128] tensor of k_cache's dtype with unit feature stride")
+    widen_ok = k_cache.dtype == torch.float8_e4m3fn and out.dtype in (torch.bfloat16, torch.float16)
+    if (out.dtype != k_cache.dtype and not widen_ok) or out.dim() != 2 or out.shape[1] != 128 or out.stride(1) != 1:
+        raise ValueError("out must be a [rows, 128] tensor of k_cache's dtype (or bf16/fp16 for an e4m3 cache) "
+                         "with unit feature stride")
     _check(lib.qsa_gather_keys(
         _ptr(k_cache), fmt, k_cache.shape[0], k_cache.shape[1], _ptr(page_table), page_table.stride(0),
         page_table.shape[1], _ptr(key_counts), _ptr(key_offsets), num_reqs, int(max_keys), _ptr(out),
-        out.stride(0), out.shape[0], _stream_handle(stream)))
+        _DTYPES[out.dtype], out.stride(0), out.shape[0], _stream_handle(stream)))
     return out
 
 

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 4
+#define QSA_ABI_VERSION 5
 
 enum qsa_status {
     QSA_OK = 0,
@@ -188,14 +188,19 @@ int qsa_build_cache_metadata(const int32_t *query_start_loc, const int32_t *seq_
  *                0 .. key_counts[r]-1 (clamped to [0, max_keys]) go to rows
  *                key_offsets[r] .. of k_out, in order.
  *   max_keys   : host bound on key_counts (sizes the launch).
- *   k_out      : device [k_out_rows][k_out_stride] elements of k_dtype,
+ *   out_dtype  : k_dtype (rows copied as they are), or for e4m3 keys
+ *                QSA_DTYPE_BF16 / QSA_DTYPE_FP16: the codes' values widened
+ *                exactly (no scale).  qsa_mqa_prefill over bf16 keys widened
+ *                from an e4m3 cache, with scale * k_scale as its multiplier,
+ *                then scores the cache as qsa_mqa_decode_typed does.
+ *   k_out      : device [k_out_rows][k_out_stride] elements of out_dtype,
  *                16-byte aligned, row stride k_out_stride >= 128 with
  *                16-byte rows.  Key c of request r is row c % page_size of
  *                page page_table[r][c / page_size]; a missing page (id < 0,
  *                >= num_pages, or a slot past the table) gives a zero row.
  *                Rows outside [0, k_out_rows) are skipped; rows no request
  *                covers are left untouched.
- *   Errors: UNSUPPORTED for another k_dtype; INVALID_ARGUMENT for negative
+ *   Errors: UNSUPPORTED for another k_dtype or out_dtype; INVALID_ARGUMENT for negative
  *   sizes, page_size outside [1, 1<<20], max_keys above 2^30, a short
  *   stride or a NULL pointer that has work to feed; LAYOUT for misaligned
  *   k_cache, k_out or rows.
@@ -203,8 +208,8 @@ int qsa_build_cache_metadata(const int32_t *query_start_loc, const int32_t *seq_
 int qsa_gather_keys(const void *k_cache, int32_t k_dtype, int64_t num_pages, int32_t page_size,
                     const int32_t *page_table, int64_t page_table_stride, int32_t page_table_cols,
                     const int32_t *key_counts, const int32_t *key_offsets, int32_t num_reqs,
-                    int32_t max_keys, void *k_out, int64_t k_out_stride, int64_t k_out_rows,
-                    void *stream);
+                    int32_t max_keys, void *k_out, int32_t out_dtype, int64_t k_out_stride,
+                    int64_t k_out_rows, void *stream);
 
 /* ------------------------------------------------------------------------
  * qsa_mqa_decode -- decode scores over the paged compressed-key cache.

@@ -391,14 +391,28 @@ def k_work(query_start_loc, seq_lens, max_num_work: int, compress_ratio: int = 4
     return out
 
 
-def gather_keys(k_pool, page_table, key_counts, key_offsets, out):
+def e4m3_to_16bit(codes, fmt: str):
+    """OCP e4m3 codes (uint8) -> the same values as bf16 or fp16 bit patterns
+    (uint16); exact (every e4m3 value is representable in both).  The
+    decoding is torch's float8_e4m3fn, a library routine."""
+    import torch
+    vals = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    dt = torch.bfloat16 if fmt == "bf16" else torch.float16
+    return vals.to(dt).view(torch.int16).numpy().view(np.uint16)
+
+
+def gather_keys(k_pool, page_table, key_counts, key_offsets, out, widen: str | None = None):
     """Paged compressed keys gathered into contiguous rows, in place in `out`
     ([rows, 128] of the pool's element type): row key_offsets[r] + c holds
     request r's compressed key c for c < key_counts[r], i.e. row c % page_size
     of page page_table[r][c // page_size]; a missing page (negative id, id
     >= the pool's pages, or past the table's columns) gives a zero row.
-    Rows no request covers are left as they are."""
+    Rows no request covers are left as they are.  widen ("bf16" or "fp16"):
+    the pool holds e4m3 codes and `out` receives their values in that 16-bit
+    format."""
     pool = np.asarray(k_pool)
+    if widen is not None:
+        pool = e4m3_to_16bit(pool, widen)
     assert pool.ndim == 4 and pool.shape[2] == 1
     num_pages, page_size = pool.shape[0], pool.shape[1]
     pt = np.asarray(page_table)

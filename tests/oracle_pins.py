@@ -731,4 +731,27 @@ def pin_gather_then_prefill_equals_decode():
     assert np.array_equal(_f32_bits(got), _f32_bits(base))
 
 
+def pin_widened_gather_then_prefill_equals_typed_prefill():
+    """e4m3 keys gathered with widening to bf16, then the bf16 prefill with
+    scale * k_scale, equal the typed prefill over the codes bit for bit (the
+    widening is exact and k_scale is a positive factor of every dot)."""
+    import torch
+    inp, vis = _small_decode()
+    k8 = torch.from_numpy(bits_to_f32(inp.k_pool) * 16).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    comp = O.comp_lens(inp.seq_lens)
+    offsets = np.concatenate([[0], np.cumsum(comp[:-1])]).astype(np.int32)
+    kw = np.zeros((int(comp.sum()) + 1, 128), np.uint16)
+    O.gather_keys(k8, inp.page_table, comp, offsets, kw, widen="bf16")
+    k8g = np.zeros((int(comp.sum()) + 1, 128), np.uint8)
+    O.gather_keys(k8, inp.page_table, comp, offsets, k8g)
+    rows = inp.q.shape[0] * inp.q.shape[1]
+    q = np.ascontiguousarray(inp.q.reshape(rows, 4, 128))
+    req = np.repeat(np.arange(inp.q.shape[0]), inp.q.shape[1])
+    ks = offsets[req]
+    k_scale = 0.0625  # a power of two: scale * k_scale is exact in fp32
+    a = O.prefill(q, kw, ks, ks + vis, inp.out_cols, scale=float(np.float32(SCALE * k_scale)))
+    b = O.prefill_typed(q, "bf16", k8g, "fp8_e4m3", ks, ks + vis, inp.out_cols, k_scale=k_scale, scale=SCALE)
+    assert np.array_equal(_f32_bits(a), _f32_bits(b))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

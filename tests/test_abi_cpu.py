@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.qsa_abi_version() == 4
+    assert lib.qsa_abi_version() == 5
 
 
 def test_launch_events_set_and_clear_without_device(lib):
@@ -192,11 +192,12 @@ def test_cache_metadata_nothing_to_do(lib):
 
 def _gather(lib, **kw):
     a = dict(k=FAKE, fmt=0, pages=8, ps=64, pt=FAKE, pt_stride=4, pt_cols=4, counts=FAKE, offs=FAKE, num_reqs=2,
-             max_keys=256, out=FAKE, out_stride=128, out_rows=512)
+             max_keys=256, out=FAKE, out_fmt=None, out_stride=128, out_rows=512)
     a.update(kw)
+    out_fmt = a["fmt"] if a["out_fmt"] is None else a["out_fmt"]
     return lib.qsa_gather_keys(a["k"], a["fmt"], a["pages"], a["ps"], a["pt"], a["pt_stride"], a["pt_cols"],
-                               a["counts"], a["offs"], a["num_reqs"], a["max_keys"], a["out"], a["out_stride"],
-                               a["out_rows"], None)
+                               a["counts"], a["offs"], a["num_reqs"], a["max_keys"], a["out"], out_fmt,
+                               a["out_stride"], a["out_rows"], None)
 
 
 @pytest.mark.parametrize("kw,code,text", [
@@ -214,6 +215,10 @@ def _gather(lib, **kw):
     (dict(out=FAKE + 4), 3, "aligned"),
     (dict(out_stride=132), 3, "aligned"),
     (dict(fmt=2, out_stride=136), 3, "aligned"),
+    (dict(fmt=0, out_fmt=1), 2, "output format"),
+    (dict(fmt=1, out_fmt=2), 2, "output format"),
+    (dict(fmt=2, out_fmt=7), 2, "output format"),
+    (dict(fmt=2, out_fmt=0, out_stride=132), 3, "aligned"),
 ])
 def test_gather_rejects(lib, kw, code, text):
     assert _gather(lib, **kw) == code

@@ -149,3 +149,54 @@ def test_gather_then_prefill_equals_decode():
                               i32_to_device(ks + vis), out_cols=inp.out_cols)
     torch.cuda.synchronize()
     assert np.array_equal(f32_bits(pre), f32_bits(dec))
+
+
+@pytest.mark.parametrize("widen,page_size", [("bf16", 64), ("fp16", 64), ("bf16", 7)])
+def test_gather_widening_e4m3_against_oracle(widen, page_size):
+    inp = decode_inputs([3000, 517, 12, 8400], 1, page_size, 500, 4, 2200, seed=page_size + 1)
+    table = inp.page_table.copy()
+    table[1, 1] = -1
+    counts = O.comp_lens(inp.seq_lens).astype(np.int32)
+    offsets = np.array([0, 800, 950, 1000], np.int32)
+    rows = 3200
+    codes = fp8_e4m3_cache(inp.k_pool)
+    pool = torch.from_numpy(codes).cuda().view(torch.float8_e4m3fn)
+    dt = torch.bfloat16 if widen == "bf16" else torch.float16
+    out = torch.full((rows, 128), 0x2A2A, dtype=torch.int16, device="cuda").view(dt)
+    _gather(pool, table, counts, offsets, int(counts.max()), out)
+    want = np.full((rows, 128), 0x2A2A, np.uint16)
+    O.gather_keys(codes, table, counts, offsets, want, widen=widen)
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+def test_prefill_over_widened_e4m3_cache():
+    # The spec-decode batch over its e4m3 cache: keys gathered and widened to
+    # bf16, then the bf16 prefill with scale * k_scale, against the oracle's
+    # typed prefill over the codes (and the e4m3 decode, within tolerance).
+    from tests.parity import assert_scores_match
+    qsa = _qsa()
+    inp = WORKLOADS["specdecode_16x51k"].make()
+    R, DQL = inp.q.shape[0], inp.q.shape[1]
+    _, _, vis = O.token_metadata(inp.query_start_loc, inp.seq_lens, R * DQL)
+    comp = O.comp_lens(inp.seq_lens).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(comp[:-1])]).astype(np.int32)
+    codes = fp8_e4m3_cache(inp.k_pool)
+    pool = torch.from_numpy(codes).cuda().view(torch.float8_e4m3fn)
+    table = i32_to_device(inp.page_table)
+    k = torch.zeros((int(comp.sum()), 128), dtype=torch.bfloat16, device="cuda")
+    qsa.qsa_gather_keys(pool, table, i32_to_device(comp), i32_to_device(offsets), int(comp.max()), out=k)
+    req = np.repeat(np.arange(R), DQL)
+    ks = offsets[req]
+    mult = float(np.float32(qsa.DEFAULT_SCALE) * np.float32(FP8_K_SCALE))
+    q = bf16_to_device(inp.q).reshape(R * DQL, 4, 128)
+    pre = qsa.qsa_mqa_prefill(q, k, i32_to_device(ks), i32_to_device(ks + vis), out_cols=inp.out_cols, scale=mult)
+    dec = qsa.qsa_mqa_decode_typed(bf16_to_device(inp.q), pool, table, i32_to_device(comp), i32_to_device(vis),
+                                   out_cols=inp.out_cols, k_scale=FP8_K_SCALE)
+    torch.cuda.synchronize()
+    k8 = np.zeros((int(comp.sum()), 128), np.uint8)
+    O.gather_keys(codes, inp.page_table, comp, offsets, k8)
+    rows = np.arange(0, R * DQL, 3)
+    ref = O.prefill_typed(np.ascontiguousarray(inp.q.reshape(R * DQL, 4, 128)), "bf16", k8, "fp8_e4m3", ks, ks + vis,
+                          inp.out_cols, k_scale=FP8_K_SCALE, rows=rows)
+    assert_scores_match(pre[torch.from_numpy(rows).cuda()], ref, "prefill over the widened e4m3 cache")
+    assert_scores_match(pre, dec.cpu().numpy(), "prefill vs e4m3 decode")
