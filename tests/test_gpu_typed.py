@@ -175,3 +175,19 @@ def test_prefill_fp16_bit_exact_on_exact_values():
     f16 = _prefill_typed(fp16_bits(qv), fp16_bits(kv), ks, ke, cols)
     b16 = _prefill_typed(bf16_bits(qv), bf16_bits(kv), ks, ke, cols, dtype=torch.bfloat16)
     assert np.array_equal(f32_bits(f16), f32_bits(b16))
+
+
+@pytest.mark.parametrize("dql,qf,kf", [(5, "bf16", "fp8_e4m3"), (8, "fp16", "fp8_e4m3"), (13, "fp16", "fp16"),
+                                       (16, "bf16", "fp8_e4m3"), (16, "fp16", "fp16"), (9, "fp16", "fp8_e4m3")])
+def test_decode_typed_query_lengths(dql, qf, kf):
+    # 2, 3 and 4 query tiles per wave (DQL 5..16) in every format.
+    inp = decode_inputs([2600, 700, 64 + dql, 5000], dql, 64, 90, 2, 1300, seed=100 + dql)
+    vis, comp = _meta(inp)
+    q_bits = fp16_bits(bits_to_f32(inp.q)) if qf == "fp16" else inp.q
+    if kf == "fp8_e4m3":
+        k_bits, k_scale = fp8_e4m3_cache(inp.k_pool, 0.011), 0.011
+    else:
+        k_bits, k_scale = fp16_bits(bits_to_f32(inp.k_pool)), 1.0
+    gpu = _decode_typed(inp, q_bits, qf, k_bits, kf, k_scale, vis, comp)
+    ref = O.decode_typed(q_bits, qf, k_bits, kf, inp.page_table, comp, vis, inp.out_cols, k_scale=k_scale)
+    assert_scores_match(gpu, ref, f"DQL {dql} {qf}/{kf}")
