@@ -487,7 +487,7 @@ def main(argv=None) -> int:
         check(lib.qsa_gather_keys(
             pool.data_ptr(), qsa.QSA_DTYPE_BF16, pool.shape[0], pool.shape[1], page_table.data_ptr(),
             page_table.stride(0), page_table.shape[1], comp_dec.data_ptr(), gk_off.data_ptr(), R,
-            int(comp_host[:R].max()), gk_out.data_ptr(), gk_out.stride(0), gk_out.shape[0], sh))
+            int(comp_host[:R].max()), gk_out.data_ptr(), qsa.QSA_DTYPE_BF16, gk_out.stride(0), gk_out.shape[0], sh))
         check(lib.qsa_set_launch_events(None, None))
     torch.cuda.synchronize()
     # The cache-metadata call is two kernels; the events bracket the first

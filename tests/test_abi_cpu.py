@@ -385,3 +385,17 @@ def test_binding_refuses_cpu_tensors(lib):
                            torch.zeros(1, dtype=torch.int32), out_cols=4)
     with pytest.raises(ValueError, match="GPU"):
         qsa.qsa_topk_blocks(torch.zeros((2, 3)), 1)
+
+
+def test_bench_direct_calls_match_the_abi(lib):
+    """bench.py calls the library directly (to time launches without Python
+    wrappers); each such call must pass as many arguments as the declared
+    signature has."""
+    import ast
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    calls = [n for n in ast.walk(ast.parse(src)) if isinstance(n, ast.Call) and isinstance(n.func, ast.Attribute)
+             and isinstance(n.func.value, ast.Name) and n.func.value.id == "lib" and n.func.attr.startswith("qsa_")]
+    assert len(calls) >= 8
+    for c in calls:
+        want = len(getattr(lib, c.func.attr).argtypes)
+        assert len(c.args) == want, f"bench.py line {c.lineno}: {c.func.attr} takes {want} arguments, given {len(c.args)}"
