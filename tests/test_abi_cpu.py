@@ -399,3 +399,31 @@ def test_bench_direct_calls_match_the_abi(lib):
     for c in calls:
         want = len(getattr(lib, c.func.attr).argtypes)
         assert len(c.args) == want, f"bench.py line {c.lineno}: {c.func.attr} takes {want} arguments, given {len(c.args)}"
+
+
+def test_error_text_is_per_thread(lib):
+    """The last-error text is thread-local: threads that fail different checks
+    at the same time each read back their own message."""
+    import threading
+    results, barrier = {}, threading.Barrier(8)
+
+    def worker(i):
+        barrier.wait()
+        for _ in range(200):
+            if i % 2:
+                rc = _decode(lib, dql=0)
+                ok = rc == 1 and "dql" in _err(lib)
+            else:
+                rc = _prefill(lib, heads=2)
+                ok = rc == 2 and "(4, 128)" in _err(lib)
+            if not ok:
+                results[i] = False
+                return
+        results[i] = True
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert all(results.get(i) for i in range(8)), results
