@@ -73,6 +73,13 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_prefill_typed.argtypes = [P, ctypes.c_int, i64, i64, P, ctypes.c_int, f64, i64, i64,
                                          P, P, i32, f32, P, i64, i32, i32, i32]
     lib.oracle_prefill_typed.restype = None
+    lib.oracle_round_bf16.argtypes = [P, i64, P]
+    lib.oracle_round_bf16.restype = None
+    lib.oracle_round_e4m3.argtypes = [P, i64, P]
+    lib.oracle_round_e4m3.restype = None
+    lib.oracle_prepare_q.argtypes = [P, i64, i32, P, i64, i64, P, ctypes.c_int, i64, P, ctypes.c_int, f32,
+                                     P, P, ctypes.c_int, f32, i64, i64, i32, i32]
+    lib.oracle_prepare_q.restype = None
     return lib
 
 
@@ -439,4 +446,67 @@ def topk(logits, k: int, threads: int | None = None):
         if rc != 0:
             raise MemoryError("oracle_topk: allocation failed")
     _run_rows(fn, x.shape[0], threads)
+    return out
+
+
+def round_bf16(x):
+    """fp32 values -> bf16 bit patterns (uint16), nearest with ties to even."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(a.shape, np.uint16)
+    load().oracle_round_bf16(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def round_e4m3(x):
+    """fp32 values -> OCP e4m3 codes (uint8): nearest finite value, ties to
+    the even code (so beyond 448 the result is +-448); NaN -> 0x7F."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(a.shape, np.uint8)
+    load().oracle_round_e4m3(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def _rot_table(a):
+    """(code, array) of a cos/sin table or norm weight: bf16 bit patterns
+    (uint16) or float32 values."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return FORMATS["bf16"][0], a
+    assert a.dtype == np.float32, "bf16 bit patterns (uint16) or float32"
+    return 3, a
+
+
+def prepare_q(q_bits, positions, cos_sin, weight, eps: float, mrope_section=None,
+              out_format: str = "bf16", out_scale: float = 1.0, threads: int | None = None):
+    """Query preparation (see oracle_prepare_q): q_bits [T, H*128] bf16 bit
+    patterns (uint16; the token stride may exceed H*128), positions int64 [T]
+    or [3, T], cos_sin [rows, 64] (bf16 bits or float32), weight [128] (bf16
+    bits or float32).  Returns [T, H, 128]: uint16 bf16 patterns, or uint8
+    e4m3 codes of value / out_scale when out_format is "fp8_e4m3"."""
+    lib = load()
+    q = np.asarray(q_bits)
+    assert q.dtype == np.uint16 and q.ndim == 2 and q.strides[1] == 2 and q.shape[1] % DIM == 0
+    T, H = q.shape[0], q.shape[1] // DIM
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    if pos.ndim == 1:
+        assert pos.shape == (T,)
+        sa, st = 0, 1
+    else:
+        assert pos.shape == (3, T)
+        sa, st = T, 1
+    rf, cs = _rot_table(cos_sin)
+    assert cs.ndim == 2 and cs.shape[1] == 64
+    wf, w = _rot_table(weight)
+    assert w.shape == (DIM,)
+    sec = None if mrope_section is None else np.ascontiguousarray(mrope_section, dtype=np.int32)
+    assert sec is None or (sec.shape == (3,) and int(sec.sum()) == 32)
+    of = FORMATS[out_format][0]
+    assert out_format in ("bf16", "fp8_e4m3")
+    out = np.empty((T, H, DIM), FORMATS[out_format][1])
+    sq = q.strides[0] // 2
+
+    def fn(b, e):
+        lib.oracle_prepare_q(_ptr(q), sq, H, _ptr(pos), sa, st, _ptr(cs), rf, cs.shape[0], _ptr(w), wf,
+                             float(eps), _ptr(sec), _ptr(out), of, float(out_scale), H * DIM, DIM, b, e)
+    _run_rows(fn, T, threads)
     return out

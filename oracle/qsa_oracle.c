@@ -37,6 +37,14 @@
  *               a value bound for an fp8 cache is rounded to bf16, divided
  *               by the cache's scale, then converted to fp8.
  *   [MATE-QSA]  "MQA score": query and compressed key are BF16 or FP16.
+ *   [QSA-PREP]  _norm_rope: Gemma RMSNorm (weight + 1) in fp32, the result
+ *               rounded to the cos/sin table's type, then NeoX rotation of
+ *               the first half of the rotary slice with per-axis (MRoPE)
+ *               table rows; _store_rotated: the first 64 features are the
+ *               rotated ones; _to_dst_dtype: round to bf16 (then / scale
+ *               and fp8 for an fp8 destination).  supports_fused_pre_indexer:
+ *               head dim 128, rotary dim 64, NeoX style, interleaved MRoPE
+ *               whose section sums to 32.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - scale multiplies the head sum (equal to scaling before ReLU for
@@ -112,11 +120,13 @@ static double e4m3_bits_to_double(uint8_t bits)
 #define ORACLE_BF16 0
 #define ORACLE_FP16 1
 #define ORACLE_FP8_E4M3 2
+#define ORACLE_FP32 3
 
 /* Element `index` of an array of `format` elements, widened exactly. */
 static double element(const void *base, int64_t index, int format)
 {
     if (format == ORACLE_FP8_E4M3) return e4m3_bits_to_double(((const uint8_t *)base)[index]);
+    if (format == ORACLE_FP32) return (double)((const float *)base)[index];
     uint16_t bits = ((const uint16_t *)base)[index];
     return format == ORACLE_FP16 ? fp16_bits_to_double(bits) : bf16_bits_to_double(bits);
 }
@@ -425,4 +435,140 @@ int oracle_topk(const float *logits, int64_t logits_stride, int32_t num_cols, in
     }
     free(cand);
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Query preparation [QSA-PREP _norm_rope, _store_rotated, _to_dst_dtype].   */
+/*                                                                          */
+/* Readings where the page leaves a detail open:                            */
+/*   - the sum of squares is the fp32 rounding of the exact sum (it is      */
+/*     accumulated here in double); the page sums in fp32 in an unstated    */
+/*     order, which can differ from this by a few fp32 ulps;                */
+/*   - rrms is the fp32 rounding of 1/sqrt(mean + eps);                     */
+/*   - arithmetic in the table's type rounds once per operation, with no    */
+/*     fused multiply-add (bf16 operations computed in fp32 and rounded     */
+/*     once are exact bf16 operations: 24 >= 2*8 + 2 bits);                 */
+/*   - under MRoPE the page adds the three masked table reads to a zero     */
+/*     start, which returns the selected entry except that -0 becomes +0;   */
+/*   - fp8 is OCP e4m3: the nearest finite value, ties to the even code, so */
+/*     magnitudes above 448 (and infinities) give 448; NaN gives 0x7F;      */
+/*   - a position outside the table's rows is the caller's error: the       */
+/*     pairs that use it read NaN for cos and sin.                          */
+/* ------------------------------------------------------------------------ */
+
+#define PREP_DIM 128
+#define PREP_PAIRS 32 /* rotary dim 64: 32 (cos, sin) pairs, NeoX halves */
+
+/* fp32 -> bf16 bit pattern, nearest with ties to even; NaN -> 0x7FC0. */
+static uint16_t float_to_bf16_bits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if (isnan(f)) return 0x7FC0;
+    uint32_t kept = u >> 16, dropped = u & 0xFFFFu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;
+    return (uint16_t)kept;
+}
+
+static float bf16_round(float f) { return (float)bf16_bits_to_double(float_to_bf16_bits(f)); }
+
+/* Rounds an fp32 result to the rotation type (bf16 or fp32). */
+static float in_type(float v, int format) { return format == ORACLE_BF16 ? bf16_round(v) : v; }
+
+/* fp32 -> e4m3 code: the nearest finite value, ties to the even code. */
+static uint8_t float_to_e4m3_bits(float f)
+{
+    if (isnan(f)) return 0x7F;
+    double a = fabs((double)f);
+    if (a > 448.0) a = 448.0;
+    int best = 0;
+    double best_err = a;
+    for (int code = 1; code <= 0x7E; ++code) {
+        double err = fabs(e4m3_bits_to_double((uint8_t)code) - a);
+        if (err < best_err || (err == best_err && (code & 1) == 0)) {
+            best = code;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(best | (signbit(f) ? 0x80 : 0));
+}
+
+void oracle_round_bf16(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = float_to_bf16_bits(x[i]);
+}
+
+void oracle_round_e4m3(const float *x, int64_t n, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = float_to_e4m3_bits(x[i]);
+}
+
+/* Interleaved MRoPE: the axis (0 temporal, 1 height, 2 width) of rotary
+ * pair j under section (t, h, w).  The page writes j <= 3h; j % 3 == 1
+ * never holds at j == 3h, so it is the same set. */
+static int mrope_axis(int j, const int32_t *section)
+{
+    if (j % 3 == 1 && j < 3 * section[1]) return 1;
+    if (j % 3 == 2 && j < 3 * section[2]) return 2;
+    return 0;
+}
+
+/* Tokens [token_begin, token_end): q holds num_heads heads of 128 bf16
+ * features per token (head h of token t at q + t*q_stride_token + h*128).
+ * positions[a*pos_stride_axis + t*pos_stride_token] is token t's position
+ * on axis a (pos_stride_axis 0 for one position per token).  cos_sin has
+ * cos_sin_rows rows of 32 cos then 32 sin in rot_format (bf16 or fp32),
+ * the weight 128 entries in weight_format (bf16 or fp32).  mrope_section
+ * is NULL (plain rotary) or (t, h, w).  Output element (t, h, d) lands at
+ * t*out_stride_token + h*out_stride_head + d as bf16, or as e4m3 of the
+ * bf16 value divided by out_scale. */
+void oracle_prepare_q(const uint16_t *q, int64_t q_stride_token, int32_t num_heads, const int64_t *positions,
+                      int64_t pos_stride_axis, int64_t pos_stride_token, const void *cos_sin, int rot_format,
+                      int64_t cos_sin_rows, const void *weight, int weight_format, float eps,
+                      const int32_t *mrope_section, void *out, int out_format, float out_scale,
+                      int64_t out_stride_token, int64_t out_stride_head, int32_t token_begin, int32_t token_end)
+{
+    for (int32_t t = token_begin; t < token_end; ++t) {
+        int64_t pos[3];
+        for (int a = 0; a < 3; ++a) pos[a] = positions[a * pos_stride_axis + (int64_t)t * pos_stride_token];
+        for (int32_t h = 0; h < num_heads; ++h) {
+            const uint16_t *xb = q + (int64_t)t * q_stride_token + (int64_t)h * PREP_DIM;
+            float x[PREP_DIM], y[PREP_DIM], o[PREP_DIM];
+            double sum_sq = 0.0;
+            for (int d = 0; d < PREP_DIM; ++d) {
+                x[d] = (float)bf16_bits_to_double(xb[d]);
+                sum_sq += (double)(x[d] * x[d]);
+            }
+            float mean_eps = (float)sum_sq / (float)PREP_DIM + eps;
+            float rrms = (float)(1.0 / sqrt((double)mean_eps));
+            for (int d = 0; d < PREP_DIM; ++d) {
+                float gain = (float)element(weight, d, weight_format) + 1.0f;
+                y[d] = in_type((x[d] * rrms) * gain, rot_format);
+            }
+            for (int j = 0; j < PREP_PAIRS; ++j) {
+                int64_t p = pos[mrope_section ? mrope_axis(j, mrope_section) : 0];
+                float c = NAN, s = NAN;
+                if (p >= 0 && p < cos_sin_rows) {
+                    c = (float)element(cos_sin, p * 2 * PREP_PAIRS + j, rot_format);
+                    s = (float)element(cos_sin, p * 2 * PREP_PAIRS + PREP_PAIRS + j, rot_format);
+                    if (mrope_section) {
+                        c = in_type(0.0f + c, rot_format);
+                        s = in_type(0.0f + s, rot_format);
+                    }
+                }
+                float lo = y[j], hi = y[j + PREP_PAIRS];
+                o[j] = in_type(in_type(lo * c, rot_format) - in_type(hi * s, rot_format), rot_format);
+                o[j + PREP_PAIRS] = in_type(in_type(hi * c, rot_format) + in_type(lo * s, rot_format), rot_format);
+            }
+            for (int d = 2 * PREP_PAIRS; d < PREP_DIM; ++d) o[d] = y[d];
+            for (int d = 0; d < PREP_DIM; ++d) {
+                uint16_t v = float_to_bf16_bits(o[d]);
+                int64_t at = (int64_t)t * out_stride_token + (int64_t)h * out_stride_head + d;
+                if (out_format == ORACLE_FP8_E4M3)
+                    ((uint8_t *)out)[at] = float_to_e4m3_bits((float)bf16_bits_to_double(v) / out_scale);
+                else
+                    ((uint16_t *)out)[at] = v;
+            }
+        }
+    }
 }

@@ -754,4 +754,229 @@ def pin_widened_gather_then_prefill_equals_typed_prefill():
     assert np.array_equal(_f32_bits(a), _f32_bits(b))
 
 
+# ---- Query preparation [QSA-PREP _norm_rope, _store_rotated, _to_dst_dtype] ----
+
+def _torch_round(x32, dtype_name):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x32, np.float32)).to(getattr(torch, dtype_name))
+    return t.view(torch.uint8 if dtype_name == "float8_e4m3fn" else torch.int16).numpy()
+
+
+def pin_bf16_rounding_matches_library():
+    # torch's float -> bfloat16 conversion (nearest, ties to even) is the
+    # library routine; exact ties with odd and even kept parts included.
+    rng = np.random.default_rng(71)
+    x = (rng.standard_normal(20000) * 3.0).astype(np.float32)
+    kept = np.arange(0x3F00, 0x4100, dtype=np.uint32)
+    ties = ((kept << 16) | 0x8000).view(np.float32)
+    near = np.concatenate([((kept << 16) | 0x7FFF), ((kept << 16) | 0x8001)]).view(np.float32)
+    tiny = np.array([1e-40, -3e-39, 0.0, -0.0, 3.0e38, -3.3e38], np.float32)
+    for v in (x, ties, near, tiny):
+        assert np.array_equal(O.round_bf16(v), _torch_round(v, "bfloat16").view(np.uint16))
+
+
+def pin_e4m3_rounding_matches_library_and_saturates():
+    # Below 448 torch's float8_e4m3fn conversion (nearest, ties to even) is
+    # the library routine: random values, every midpoint between two
+    # neighbouring codes, and values just beside the midpoints.
+    rng = np.random.default_rng(72)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-9, 5, 20000))).astype(np.float32)
+    x = x[np.abs(x) < 440]
+    import torch
+    vals = torch.arange(0, 127, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    beside = np.concatenate([np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    for v in (x, mids, -mids, beside):
+        v = v[np.abs(v) < 448]
+        assert np.array_equal(O.round_e4m3(v), _torch_round(v, "float8_e4m3fn"))
+    # The largest finite magnitude is 448: everything beyond saturates.
+    big = np.array([448.0, 449.0, 463.9, 464.0, 480.0, 1e6, np.inf], np.float32)
+    assert np.all(O.round_e4m3(big) == 0x7E) and np.all(O.round_e4m3(-big) == 0xFE)
+    assert O.round_e4m3(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+def _identity_table(rows, fmt):
+    cs = np.zeros((rows, 64), np.float32)
+    cs[:, :32] = 1.0
+    return cs if fmt == "fp32" else bf16_bits(cs)
+
+
+def _rope_table(rows, seed=None):
+    # cos/sin of position * 10000^(-j/32), rounded to fp32 (a real table).
+    j = np.arange(32)
+    ang = np.arange(rows)[:, None] * (10000.0 ** (-j / 32.0))[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def _library_norm(q_bits, weight, eps):
+    import torch
+    x = torch.from_numpy(bits_to_f32(q_bits).astype(np.float64)).reshape(q_bits.shape[0], -1, 128)
+    w = torch.from_numpy(np.asarray(weight, np.float64) + 1.0)
+    return torch.nn.functional.rms_norm(x, (128,), weight=w, eps=eps).numpy()
+
+
+def _prep_inputs(seed, T=7, H=3):
+    rng = np.random.default_rng(seed)
+    q = normal_bf16(rng, (T, H * 128))
+    q[1] = bf16_bits(bits_to_f32(q[1]) * np.float32(1e-3))   # small row: eps matters
+    w_f = (rng.standard_normal(128) * 0.3).astype(np.float32)
+    return q, bf16_bits(w_f), bits_to_f32(bf16_bits(w_f)), rng
+
+
+def pin_prepare_norm_matches_library():
+    # With cos 1 and sin 0 the output is the Gemma RMSNorm itself:
+    # torch.nn.functional.rms_norm in float64 with weight (w + 1), to bf16
+    # precision; eps large enough that its placement shows.
+    q, w_bits, w_f, _ = _prep_inputs(73)
+    for eps in (0.25, 1e-6):
+        pos = np.zeros(q.shape[0], np.int64)
+        got = bits_to_f32(O.prepare_q(q, pos, _identity_table(2, "fp32"), w_bits, eps)).astype(np.float64)
+        ref = _library_norm(q, w_f, eps)
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30), eps
+
+
+def pin_prepare_rotation_is_complex_product():
+    # NeoX pairs (j, j + 32) turn by the table's angle: y_j + i*y_{j+32}
+    # times c + i*s (numpy complex128), the last 64 features unchanged.
+    q, w_bits, w_f, rng = _prep_inputs(74)
+    table = _rope_table(50)
+    pos = rng.integers(0, 50, q.shape[0]).astype(np.int64)
+    got = bits_to_f32(O.prepare_q(q, pos, table, w_bits, 1e-6)).astype(np.float64)
+    y = _library_norm(q, w_f, 1e-6)
+    c = table[pos, :32].astype(np.float64)[:, None, :]
+    s = table[pos, 32:].astype(np.float64)[:, None, :]
+    z = (y[..., :32] + 1j * y[..., 32:64]) * (c + 1j * s)
+    want = np.concatenate([z.real, z.imag, y[..., 64:]], axis=-1)
+    mag = np.concatenate([np.abs(y[..., :32]) + np.abs(y[..., 32:64])] * 2 + [np.abs(y[..., 64:])], axis=-1)
+    assert np.all(np.abs(got - want) <= 2.0 ** -7 * mag + 1e-30)
+
+
+def pin_prepare_closed_forms():
+    # Every feature 2.0, weight w: mean(x^2) = 4, so the output is
+    # (w + 1) / sqrt(4 + eps) wherever cos is 1 and sin 0.
+    q = np.full((2, 256), 0x4000, np.uint16)               # bf16 2.0
+    pos = np.array([0, 1], np.int64)
+    for eps, w, want in ((0.0, 0.0, 1.0), (12.0, 0.0, 0.5), (12.0, 0.5, 0.75), (60.0, -0.5, 0.125)):
+        out = bits_to_f32(O.prepare_q(q, pos, _identity_table(2, "bf16"), bf16_bits(np.full(128, w, np.float32)),
+                                      eps))
+        assert np.all(out == np.float32(want)), (eps, w)
+
+
+def _worked_example(table_format):
+    # Hand-worked rounding example.  Features 5 = 1 + 2^-7, 37 = -2^-4,
+    # 9 = 1 + 2^-7 and 70 = 1.1875, all others 0; eps = 1 - sum(x^2)/128
+    # (exact in fp32) so rrms = 1; weight 0 except w_9 = w_70 = -2^-10, so
+    # y_9 = (1 + 2^-7)(1 - 2^-10) and y_70 = 1.1875 (1 - 2^-10).
+    # Table row 0: pair 5 has cos 1 - 2^-8, sin 2^-4; pair 9 cos 1.5, sin 0;
+    # every other pair cos 1, sin 0.
+    x = np.zeros(128, np.float32)
+    x[5], x[37], x[9], x[70] = 1 + 2.0 ** -7, -(2.0 ** -4), 1 + 2.0 ** -7, 1.1875
+    s = float(np.sum(x.astype(np.float64) ** 2))
+    eps = float(np.float32(1.0) - np.float32(s / 128))
+    w = np.zeros(128, np.float32)
+    w[9] = w[70] = -(2.0 ** -10)
+    cs = np.zeros((1, 64), np.float32)
+    cs[0, :32] = 1.0
+    cs[0, 5], cs[0, 32 + 5] = 1 - 2.0 ** -8, 2.0 ** -4
+    cs[0, 9] = 1.5
+    table = bf16_bits(cs) if table_format == "bf16" else cs
+    return bf16_bits(x)[None, :], bf16_bits(w), table, eps
+
+
+def pin_prepare_worked_rounding_example():
+    # bf16 table, one rounding per operation:
+    #   out_5  = bf16(1 + 2^-8 - 2^-15) - bf16(-2^-8) = 1 + 2^-8 -> tie -> 1
+    #   out_37 = (-2^-4 + 2^-12) + (2^-4 + 2^-11) = 3 * 2^-12
+    #   y_9 rounds to 1 + 2^-7; times 1.5 is the tie 1.5 + 2^-7 + 2^-8,
+    #   which goes to the even 1.5 + 2^-6.
+    # fp32 table (rounded to bf16 only at the end):
+    #   out_5 = bf16(1 + 2^-7 - 2^-15) = 1 + 2^-7
+    #   out_9 = bf16(1.5 (1 + 2^-7)(1 - 2^-10)), just below the tie: 1.5 + 2^-7.
+    pos = np.zeros(1, np.int64)
+    for fmt, o5, o9 in (("bf16", 1.0, 1.5 + 2.0 ** -6), ("fp32", 1 + 2.0 ** -7, 1.5 + 2.0 ** -7)):
+        q, w, table, eps = _worked_example(fmt)
+        out = bits_to_f32(O.prepare_q(q, pos, table, w, eps))[0, 0]
+        want = np.zeros(128, np.float32)
+        want[5], want[37], want[9], want[70] = o5, 3 * 2.0 ** -12, o9, 1.1875
+        assert np.array_equal(out, want), (fmt, np.nonzero(out != want))
+    # The e4m3 store divides the bf16 value by the scale.  bf16 table, scale
+    # 2: 1/2 -> 0x30; (1.5 + 2^-6)/2 = 0.7578125 -> 0.75 = 0x34; 1.1875/2 is
+    # the tie between 0.5625 (odd code 0x31) and 0.625 (even, 0x32);
+    # 3*2^-13 -> 0 (below half of 2^-9).
+    q, w, table, eps = _worked_example("bf16")
+    codes = O.prepare_q(q, pos, table, w, eps, out_format="fp8_e4m3", out_scale=2.0)[0, 0]
+    want = np.zeros(128, np.uint8)
+    want[5], want[9], want[70] = 0x30, 0x34, 0x32
+    assert np.array_equal(codes, want)
+    # fp32 table, scale 1: y_70 = 1.1875 - 1.1875 * 2^-10 lies below the
+    # e4m3 midpoint 1.1875, but its bf16 rounding is 1.1875, the tie between
+    # 1.125 (0x39) and 1.25 (even, 0x3A): the store gives 0x3A.  Feature 5
+    # -> 1.0 (0x38), feature 9 -> 1.5 (0x3C).
+    q, w, table, eps = _worked_example("fp32")
+    codes = O.prepare_q(q, pos, table, w, eps, out_format="fp8_e4m3", out_scale=1.0)[0, 0]
+    want = np.zeros(128, np.uint8)
+    want[5], want[9], want[70] = 0x38, 0x3C, 0x3A
+    assert np.array_equal(codes, want)
+
+
+def pin_prepare_mrope_axes():
+    # Table row p: cos 2^-p, sin 0, so output feature j (and j + 32) of an
+    # all-ones row is 2^-(position of pair j's axis).  Positions t=1, h=2,
+    # w=3 name the axis.  Interleaved MRoPE: each axis gets as many pairs as
+    # its section entry, pairs 0, 3, 6, ... are temporal, the first triples
+    # run (t, h, w), and pairs past the interleaved part are temporal.
+    cs = np.zeros((4, 64), np.float32)
+    cs[:, :32] = (2.0 ** -np.arange(4))[:, None]
+    q = np.full((1, 128), 0x3F80, np.uint16)                # bf16 1.0
+    pos = np.array([[1], [2], [3]], np.int64)
+    for sec in ((16, 8, 8), (12, 10, 10), (24, 8, 0), (32, 0, 0), (20, 6, 6)):
+        out = bits_to_f32(O.prepare_q(q, pos, bf16_bits(cs), np.zeros(128, np.uint16), 0.0,
+                                      mrope_section=sec))[0, 0]
+        axis = np.round(-np.log2(out[:32])).astype(int) - 1
+        assert np.array_equal(out[:32], out[32:64])
+        assert [int((axis == a).sum()) for a in range(3)] == list(sec), sec
+        assert np.all(axis[0::3] == 0)
+        m = 3 * min(sec[1], sec[2])
+        assert np.array_equal(axis[:m], np.arange(m) % 3)
+        assert np.all(axis[3 * max(sec[1], sec[2]):] == 0)
+    # One position per token with a section: every axis reads the same row,
+    # which is plain rotary.
+    q, w_bits, _, rng = _prep_inputs(75)
+    p1 = rng.integers(0, 50, q.shape[0]).astype(np.int64)
+    table = bf16_bits(_rope_table(50))
+    plain = O.prepare_q(q, p1, table, w_bits, 1e-6)
+    assert np.array_equal(O.prepare_q(q, p1, table, w_bits, 1e-6, mrope_section=(16, 8, 8)), plain)
+    assert np.array_equal(O.prepare_q(q, np.stack([p1] * 3), table, w_bits, 1e-6, mrope_section=(12, 10, 10)),
+                          plain)
+
+
+def pin_prepare_layout_invariants():
+    # Heads and tokens are independent: permuting heads (and tokens with
+    # their positions) permutes the output; a padded token stride reads the
+    # same values.  A position outside the table turns exactly the rotated
+    # features of the pairs that use it into NaN.
+    q, w_bits, _, rng = _prep_inputs(76, T=9, H=4)
+    table = bf16_bits(_rope_table(40))
+    pos = rng.integers(0, 40, q.shape[0]).astype(np.int64)
+    base = O.prepare_q(q, pos, table, w_bits, 1e-6)
+    hp, tp = np.array([2, 0, 3, 1]), rng.permutation(q.shape[0])
+    qh = q.reshape(9, 4, 128)[:, hp].reshape(9, 512)
+    assert np.array_equal(O.prepare_q(qh, pos, table, w_bits, 1e-6), base[:, hp])
+    assert np.array_equal(O.prepare_q(q[tp], pos[tp], table, w_bits, 1e-6), base[tp])
+    padded = np.zeros((9, 512 + 64), np.uint16)
+    padded[:, :512] = q
+    assert np.array_equal(O.prepare_q(padded[:, :512], pos, table, w_bits, 1e-6), base)
+    pos3 = np.stack([pos, pos, pos])
+    pos3[1, 4] = 40                                          # height position off the table
+    out = bits_to_f32(O.prepare_q(q, pos3, table, w_bits, 1e-6, mrope_section=(16, 8, 8)))
+    h_pairs = np.array([j for j in range(32) if j % 3 == 1 and j < 24])
+    bad = np.zeros(128, bool)
+    bad[h_pairs] = bad[h_pairs + 32] = True
+    assert np.all(np.isnan(out[4][:, bad])) and not np.any(np.isnan(out[4][:, ~bad]))
+    assert not np.any(np.isnan(np.delete(out, 4, axis=0)))
+    # The e4m3 store takes the bf16 result divided by the scale.
+    codes = O.prepare_q(q, pos, table, w_bits, 1e-6, out_format="fp8_e4m3", out_scale=0.05)
+    assert np.array_equal(codes, O.round_e4m3(bits_to_f32(base) / np.float32(0.05)))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

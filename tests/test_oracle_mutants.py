@@ -74,6 +74,40 @@ MUTANTS = {
                                "floor_div((int64_t)seq_lens[r] - query_len + 1, compress_ratio);"),
     "topk_smallest": ("if (x->value > y->value) return -1;\n    if (x->value < y->value) return 1;",
                       "if (x->value < y->value) return -1;\n    if (x->value > y->value) return 1;"),
+    "prep_gain_without_one": ("float gain = (float)element(weight, d, weight_format) + 1.0f;",
+                              "float gain = (float)element(weight, d, weight_format);"),
+    "prep_eps_dropped": ("(float)sum_sq / (float)PREP_DIM + eps;", "(float)sum_sq / (float)PREP_DIM;"),
+    "prep_sum_not_averaged": ("(float)sum_sq / (float)PREP_DIM + eps;", "(float)sum_sq + eps;"),
+    "prep_rotation_sign": ("o[j] = in_type(in_type(lo * c, rot_format) - in_type(hi * s, rot_format)",
+                           "o[j] = in_type(in_type(lo * c, rot_format) + in_type(hi * s, rot_format)"),
+    "prep_partner_wrong": ("float lo = y[j], hi = y[j + PREP_PAIRS];",
+                           "float lo = y[j], hi = y[j + 2 * PREP_PAIRS];"),
+    "prep_cos_sin_swapped": ("c = (float)element(cos_sin, p * 2 * PREP_PAIRS + j, rot_format);",
+                             "c = (float)element(cos_sin, p * 2 * PREP_PAIRS + PREP_PAIRS + j, rot_format);"),
+    "prep_table_row_stride": ("s = (float)element(cos_sin, p * 2 * PREP_PAIRS + PREP_PAIRS + j, rot_format);",
+                              "s = (float)element(cos_sin, p * PREP_PAIRS + PREP_PAIRS + j, rot_format);"),
+    "prep_mrope_height_residue": ("if (j % 3 == 1 && j < 3 * section[1]) return 1;",
+                                  "if (j % 3 == 0 && j < 3 * section[1]) return 1;"),
+    "prep_mrope_sections_swapped": ("if (j % 3 == 2 && j < 3 * section[2]) return 2;",
+                                    "if (j % 3 == 2 && j < 3 * section[1]) return 2;"),
+    "prep_no_per_op_rounding": ("o[j] = in_type(in_type(lo * c, rot_format) - in_type(hi * s, rot_format), rot_format);",
+                                "o[j] = in_type(lo * c - hi * s, rot_format);"),
+    "prep_y_not_rounded": ("y[d] = in_type((x[d] * rrms) * gain, rot_format);", "y[d] = (x[d] * rrms) * gain;"),
+    "prep_passthrough_from_rotated": ("for (int d = 2 * PREP_PAIRS; d < PREP_DIM; ++d) o[d] = y[d];",
+                                      "for (int d = 2 * PREP_PAIRS; d < PREP_DIM; ++d) o[d] = y[d - 64];"),
+    "prep_fp8_scale_multiplies": ("float_to_e4m3_bits((float)bf16_bits_to_double(v) / out_scale)",
+                                  "float_to_e4m3_bits((float)bf16_bits_to_double(v) * out_scale)"),
+    "prep_fp8_skips_bf16": ("float_to_e4m3_bits((float)bf16_bits_to_double(v) / out_scale)",
+                            "float_to_e4m3_bits(o[d] / out_scale)"),
+    "prep_head_stride_wrong": ("(int64_t)h * PREP_DIM;\n", "(int64_t)h * 64;\n"),
+    "prep_position_axis_ignored": ("int64_t p = pos[mrope_section ? mrope_axis(j, mrope_section) : 0];",
+                                   "int64_t p = pos[0];"),
+    "prep_range_unchecked_high": ("if (p >= 0 && p < cos_sin_rows) {", "if (p >= 0 && p <= cos_sin_rows) {"),
+    "bf16_ties_away": ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;",
+                       "if (dropped >= 0x8000u) kept += 1u;"),
+    "e4m3_ties_odd": ("if (err < best_err || (err == best_err && (code & 1) == 0)) {",
+                      "if (err < best_err || (err == best_err && (code & 1) == 1)) {"),
+    "e4m3_no_saturation": ("if (a > 448.0) a = 448.0;", "if (a > 448.0) return 0x7F;"),
 }
 
 
