@@ -81,6 +81,14 @@ def topk_bytes(rows: int, cols: int, k: int) -> float:
 # ----------------------------------------------------------------------------
 
 
+def prepare_bytes(tokens: int, heads: int) -> float:
+    """Algorithmic HBM bytes of qsa_prepare_q with bf16 input, table, weight
+    and output: each (token, head) row read and written once (256 + 256 B),
+    each token's table row (64 bf16) and position (int64) read once, the
+    weight once."""
+    return tokens * heads * 512.0 + tokens * (128.0 + 8.0) + 256.0
+
+
 def source_digest(kernel_file: str) -> str:
     """First 16 hex digits of the SHA-256 of a kernel's source file followed
     by the device and launch headers it includes."""
@@ -504,6 +512,39 @@ def main(argv=None) -> int:
     for e in cm_ev + gk_ev:
         e.close()
     del gk_out
+
+    # Query preparation of the prefill chunk: 8,192 tokens x 4 indexer heads
+    # at positions 100,000.. (a 131,072-row bf16 cos/sin table), bf16 out,
+    # timed over 20 launches that rotate 32 input and output buffers
+    # (537 MB, beyond the on-die caches).
+    from workloads import prepare_inputs
+    prep = prepare_inputs(T_pre, 4, seed=9, first_pos=int(pre.seq_lens[0]) - T_pre, table_rows=131_072)
+    pq0 = to_bf16(prep.q)
+    pqs = [pq0.clone() for _ in range(32)]
+    pos_d = torch.from_numpy(prep.positions).to(dev)
+    cs_d, w_d = to_bf16(prep.cos_sin), to_bf16(prep.weight)
+    pouts = [torch.empty((T_pre, 4, 128), dtype=torch.bfloat16, device=dev) for _ in range(32)]
+    pp_ev = [HipEvents(2) for _ in range(20)]
+    for j in range(24):
+        if j >= 4:
+            check(lib.qsa_set_launch_events(pp_ev[j - 4].ev[0], pp_ev[j - 4].ev[1]))
+        pq, po = pqs[j % 32], pouts[(j + 7) % 32]
+        check(lib.qsa_prepare_q(
+            pq.data_ptr(), pq.stride(0), T_pre, 4, pos_d.data_ptr(), 0, 1, cs_d.data_ptr(), qsa.QSA_DTYPE_BF16,
+            cs_d.shape[0], w_d.data_ptr(), qsa.QSA_DTYPE_BF16, prep.eps, None, po.data_ptr(), qsa.QSA_DTYPE_BF16,
+            1.0, po.stride(0), po.stride(1), sh))
+        check(lib.qsa_set_launch_events(None, None))
+    torch.cuda.synchronize()
+    pp_us = float(np.mean([e.elapsed_us(0, 1) for e in pp_ev]))
+    pp_bytes = prepare_bytes(T_pre, 4)
+    result["prepare_q"] = {
+        "us": round(pp_us, 3), "tokens": T_pre, "heads": 4, "bytes": pp_bytes,
+        "gbps": round(pp_bytes / (pp_us * 1e-6) / 1e9, 2),
+        "frac_of_hbm": round(pp_bytes / (pp_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+    }
+    for e in pp_ev:
+        e.close()
+    del pqs, pouts, pq0
 
     # A measured bandwidth for context: a plain 1 GiB device-to-device copy
     # (read + write bytes over its time), and each HBM-bound kernel's rate as

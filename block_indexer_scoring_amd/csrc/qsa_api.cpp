@@ -279,6 +279,73 @@ int qsa_gather_keys(const void *k_cache, int32_t k_dtype, int64_t num_pages, int
     return device_status(fn, qsa::launch_gather_keys(p, static_cast<hipStream_t>(stream)));
 }
 
+int qsa_prepare_q(const void *q, int64_t q_stride_token, int32_t num_tokens, int32_t num_heads,
+                  const int64_t *positions, int64_t pos_stride_axis, int64_t pos_stride_token,
+                  const void *cos_sin, int32_t cos_sin_dtype, int64_t cos_sin_rows, const void *norm_weight,
+                  int32_t weight_dtype, float eps, const int32_t *mrope_section, void *q_out,
+                  int32_t out_dtype, float out_scale, int64_t out_stride_token, int64_t out_stride_head,
+                  void *stream) {
+    const char *fn = "qsa_prepare_q";
+    if (cos_sin_dtype != QSA_DTYPE_BF16 && cos_sin_dtype != QSA_DTYPE_FP32)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: cos/sin table format %d is not bf16 or fp32", fn, cos_sin_dtype);
+    if (weight_dtype != QSA_DTYPE_BF16 && weight_dtype != QSA_DTYPE_FP32)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: norm weight format %d is not bf16 or fp32", fn, weight_dtype);
+    if (out_dtype != QSA_DTYPE_BF16 && out_dtype != QSA_DTYPE_FP8_E4M3)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: output format %d is not bf16 or e4m3", fn, out_dtype);
+    if (num_tokens < 0 || cos_sin_rows < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+    if (num_heads < 1 || num_heads > 1024)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: num_heads must be in [1, 1024], got %d", fn, num_heads);
+    if (!std::isfinite(eps)) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: eps must be finite", fn);
+    if (out_dtype == QSA_DTYPE_FP8_E4M3 && !(std::isfinite(out_scale) && out_scale > 0.0f))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: out_scale must be finite and > 0 for e4m3 output", fn);
+    int32_t sec_h = 0, sec_w = 0;
+    if (mrope_section) {
+        const int32_t a = mrope_section[0], b = mrope_section[1], c = mrope_section[2];
+        if (a < 0 || b < 0 || c < 0 || (int64_t)a + b + c != 32)
+            return fail(QSA_ERR_INVALID_ARGUMENT, "%s: MRoPE section (%d, %d, %d) must be >= 0 and sum to 32", fn,
+                        a, b, c);
+        sec_h = b;
+        sec_w = c;
+    }
+    if (num_tokens > 1 && q_stride_token < (int64_t)num_heads * 128)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: q_stride_token < num_heads * 128", fn);
+    if (num_tokens == 0) return ok();
+    if (!q || !positions || (!cos_sin && cos_sin_rows > 0) || !norm_weight || !q_out)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL q, positions, cos_sin, norm_weight or q_out", fn);
+    if ((int64_t)num_tokens * num_heads > ((int64_t)1 << 35))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
+    const int out_align = out_dtype == QSA_DTYPE_FP8_E4M3 ? 8 : 16;
+    if (!aligned(q, 16) || q_stride_token % 8 != 0 || !aligned(cos_sin, 16) || !aligned(norm_weight, 16) ||
+        !aligned(positions, 8) || !aligned(q_out, out_align) || out_stride_token % 8 != 0 ||
+        out_stride_head % 8 != 0)
+        return fail(QSA_ERR_LAYOUT, "%s: q, cos_sin and norm_weight must be 16-byte aligned, q_out %d-byte "
+                                    "aligned, and the q and q_out strides multiples of 8 elements",
+                    fn, out_align);
+    qsa::PrepareQParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.q_stride_token = q_stride_token;
+    p.num_tokens = num_tokens;
+    p.num_heads = num_heads;
+    p.positions = positions;
+    p.pos_stride_axis = mrope_section ? pos_stride_axis : 0;
+    p.pos_stride_token = pos_stride_token;
+    p.cos_sin = cos_sin;
+    p.cos_sin_rows = cos_sin_rows;
+    p.weight = norm_weight;
+    p.eps = eps;
+    p.mrope = mrope_section ? 1 : 0;
+    p.mrope_h = sec_h;
+    p.mrope_w = sec_w;
+    p.out = q_out;
+    p.out_stride_token = out_stride_token;
+    p.out_stride_head = out_stride_head;
+    p.out_scale = out_scale;
+    p.table_f32 = cos_sin_dtype == QSA_DTYPE_FP32;
+    p.weight_f32 = weight_dtype == QSA_DTYPE_FP32;
+    p.out_fp8 = out_dtype == QSA_DTYPE_FP8_E4M3;
+    return device_status(fn, qsa::launch_prepare_q(p, static_cast<hipStream_t>(stream)));
+}
+
 // Query format must be bf16 or fp16; keys share it or are e4m3 codes with a
 // positive finite cache scale.
 static int check_formats(const char *fn, int32_t q_dtype, int32_t k_dtype, float k_scale) {

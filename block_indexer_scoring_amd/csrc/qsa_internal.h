@@ -129,6 +129,23 @@ struct GatherParams {
     int32_t widen;                       // 0: copy rows; 1 / 2: e4m3 codes -> bf16 / fp16 values
 };
 
+struct PrepareQParams {
+    const uint16_t *q;                   // bf16 [num_tokens][num_heads][128], token stride q_stride_token
+    int64_t q_stride_token;
+    int32_t num_tokens, num_heads;
+    const int64_t *positions;            // positions[a * pos_stride_axis + t * pos_stride_token]
+    int64_t pos_stride_axis, pos_stride_token;
+    const void *cos_sin;                 // [cos_sin_rows][64]: 32 cos, 32 sin
+    int64_t cos_sin_rows;
+    const void *weight;                  // [128]
+    float eps;
+    int32_t mrope, mrope_h, mrope_w;     // interleaved MRoPE section (h, w) when mrope != 0
+    void *out;                           // [num_tokens][num_heads][128] at the element strides below
+    int64_t out_stride_token, out_stride_head;
+    float out_scale;                     // e4m3 output: bf16 value / out_scale
+    int32_t table_f32, weight_f32, out_fp8;
+};
+
 // Timing events attached to every launch from the calling thread (both null
 // unless the caller armed them through the C ABI).
 struct LaunchEvents {
@@ -160,5 +177,6 @@ hipError_t launch_metadata(const MetaParams &p, hipStream_t stream);
 hipError_t launch_cache_slots(const CacheMetaParams &p, hipStream_t stream);  // p.slot_mapping set
 hipError_t launch_k_work(const CacheMetaParams &p, hipStream_t stream);       // p.k_work set
 hipError_t launch_gather_keys(const GatherParams &p, hipStream_t stream);
+hipError_t launch_prepare_q(const PrepareQParams &p, hipStream_t stream);
 
 }  // namespace qsa

@@ -21,19 +21,20 @@ QSA_ERR_INVALID_ARGUMENT = 1
 QSA_ERR_UNSUPPORTED = 2
 QSA_ERR_LAYOUT = 3
 QSA_ERR_DEVICE = 4
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_set_launch_events", "qsa_split_batch",
            "qsa_build_metadata", "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks",
            "qsa_mqa_prefill_topk", "qsa_prefill_topk_workspace_bytes", "qsa_mqa_decode_typed",
-           "qsa_mqa_prefill_typed", "qsa_build_cache_metadata", "qsa_gather_keys")
+           "qsa_mqa_prefill_typed", "qsa_build_cache_metadata", "qsa_gather_keys", "qsa_prepare_q")
 
 # enum qsa_dtype
 QSA_DTYPE_BF16 = 0
 QSA_DTYPE_FP16 = 1
 QSA_DTYPE_FP8_E4M3 = 2
+QSA_DTYPE_FP32 = 3
 _DTYPES = {torch.bfloat16: QSA_DTYPE_BF16, torch.float16: QSA_DTYPE_FP16,
-           torch.float8_e4m3fn: QSA_DTYPE_FP8_E4M3}
+           torch.float8_e4m3fn: QSA_DTYPE_FP8_E4M3, torch.float32: QSA_DTYPE_FP32}
 
 DEFAULT_SCALE = 1.0 / math.sqrt(128.0)
 
@@ -90,6 +91,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_mqa_prefill_topk.restype = ctypes.c_int
     lib.qsa_prefill_topk_workspace_bytes.argtypes = [i32, i32, i32, P]
     lib.qsa_prefill_topk_workspace_bytes.restype = ctypes.c_int
+    lib.qsa_prepare_q.argtypes = [P, i64, i32, i32, P, i64, i64, P, i32, i64, P, i32, f32, P, P, i32, f32,
+                                  i64, i64, P]
+    lib.qsa_prepare_q.restype = ctypes.c_int
     if lib.qsa_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libqsa ABI {lib.qsa_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -486,4 +490,57 @@ def qsa_mqa_prefill_topk(q: torch.Tensor, k: torch.Tensor, row_k_start: torch.Te
         _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.shape[0], _ptr(row_k_start),
         _ptr(row_k_end), num_rows, heads, dim, float(scale), int(out_cols), int(topk), _ptr(out),
         out.stride(0), _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+    return out
+
+
+def qsa_prepare_q(q: torch.Tensor, positions: torch.Tensor, cos_sin: torch.Tensor, norm_weight: torch.Tensor,
+                  eps: float, mrope_section=None, out: torch.Tensor | None = None,
+                  out_dtype: torch.dtype = torch.bfloat16, out_scale: float = 1.0, stream=None) -> torch.Tensor:
+    """Gemma RMSNorm and NeoX rotary embedding of the indexer's query heads
+    (qsa_prepare_q in include/qsa.h).  q: bf16 [T, H*128] or [T, H, 128]
+    with contiguous heads; positions: int64 [T], or [3, T] (temporal, height,
+    width) with mrope_section (t, h, w) summing to 32; cos_sin: bf16 or fp32
+    [rows, 64] (32 cos, then 32 sin); norm_weight: bf16 or fp32 [128].
+    Returns (or fills) out [T, H, 128] of bf16, or of float8_e4m3fn holding
+    the bf16 result divided by out_scale."""
+    lib = load_library()
+    _gpu("q", q, torch.bfloat16)
+    _gpu("positions", positions, torch.int64)
+    cs_fmt = _gpu_format("cos_sin", cos_sin, (torch.bfloat16, torch.float32))
+    w_fmt = _gpu_format("norm_weight", norm_weight, (torch.bfloat16, torch.float32))
+    T = q.shape[0]
+    if q.dim() == 3:
+        if q.shape[2] != 128 or q.stride(2) != 1 or q.stride(1) != 128:
+            raise ValueError("q [T, H, 128] needs contiguous heads")
+        H = q.shape[1]
+    elif q.dim() == 2 and q.shape[1] % 128 == 0 and q.stride(1) == 1:
+        H = q.shape[1] // 128
+    else:
+        raise ValueError("q must be [T, H*128] or [T, H, 128] with contiguous heads")
+    if positions.dim() == 1:
+        if positions.shape[0] != T:
+            raise ValueError("positions must be [T] or [3, T]")
+        pos_axis, pos_tok = 0, positions.stride(0)
+    elif positions.dim() == 2 and positions.shape == (3, T):
+        if mrope_section is None:
+            raise ValueError("[3, T] positions need an mrope_section")
+        pos_axis, pos_tok = positions.stride(0), positions.stride(1)
+    else:
+        raise ValueError("positions must be [T] or [3, T]")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != 64 or not cos_sin.is_contiguous():
+        raise ValueError("cos_sin must be a contiguous [rows, 64] tensor")
+    if norm_weight.numel() != 128 or not norm_weight.is_contiguous():
+        raise ValueError("norm_weight must be a contiguous [128] tensor")
+    if out is None:
+        out = torch.empty((T, H, 128), dtype=out_dtype, device=q.device)
+    out_fmt = _gpu_format("out", out, (torch.bfloat16, torch.float8_e4m3fn))
+    if out.dim() != 3 or out.shape != (T, H, 128) or out.stride(2) != 1:
+        raise ValueError("out must be [T, H, 128] with unit feature stride")
+    sec = None
+    if mrope_section is not None:
+        sec = (ctypes.c_int32 * 3)(*[int(v) for v in mrope_section])
+    _check(lib.qsa_prepare_q(
+        _ptr(q), q.stride(0), T, H, _ptr(positions), pos_axis, pos_tok, _ptr(cos_sin), cs_fmt, cos_sin.shape[0],
+        _ptr(norm_weight), w_fmt, float(eps), None if sec is None else ctypes.addressof(sec), _ptr(out), out_fmt,
+        float(out_scale), out.stride(0), out.stride(1), _stream_handle(stream)))
     return out

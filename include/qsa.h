@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 5
+#define QSA_ABI_VERSION 6
 
 enum qsa_status {
     QSA_OK = 0,
@@ -49,7 +49,7 @@ enum qsa_status {
 };
 
 /* Element formats of the typed entry points (qsa_mqa_decode_typed,
- * qsa_mqa_prefill_typed).
+ * qsa_mqa_prefill_typed, qsa_gather_keys, qsa_prepare_q).
  *   QSA_DTYPE_BF16, QSA_DTYPE_FP16: 2-byte elements.  MATE "QSA (Qwen Sparse
  *     Attention)", section "MQA score": the query and the compressed key are
  *     BF16 or FP16.
@@ -58,8 +58,10 @@ enum qsa_status {
  *     e4m3 compressed indexer cache; qsa_prepare's _to_dst_dtype writes it
  *     by rounding to bf16, dividing by the cache scale and converting.  Read
  *     here as the inverse: a key element is its e4m3 value times k_scale.
- *     NaN codes are outside the contract. */
-enum qsa_dtype { QSA_DTYPE_BF16 = 0, QSA_DTYPE_FP16 = 1, QSA_DTYPE_FP8_E4M3 = 2 };
+ *     NaN codes are outside the contract.
+ *   QSA_DTYPE_FP32: 4-byte IEEE binary32 (qsa_prepare_q's cos/sin table and
+ *     norm weight). */
+enum qsa_dtype { QSA_DTYPE_BF16 = 0, QSA_DTYPE_FP16 = 1, QSA_DTYPE_FP8_E4M3 = 2, QSA_DTYPE_FP32 = 3 };
 
 /* QSA_ABI_VERSION of the loaded library. */
 int qsa_abi_version(void);
@@ -385,6 +387,67 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
  *   outside [1, 2048].
  */
 int qsa_prefill_topk_workspace_bytes(int32_t num_rows, int32_t out_cols, int32_t topk, int64_t *bytes);
+
+/* ------------------------------------------------------------------------
+ * qsa_prepare_q -- the indexer's query heads normalized and rotated.
+ *   Source: vLLM "vllm.models.qwen4_exp.amd.ops.qsa_prepare", functions
+ *   _norm_rope (Gemma RMSNorm with weight + 1, then NeoX rotary embedding of
+ *   the first 64 features, optionally interleaved MRoPE), _store_rotated and
+ *   _to_dst_dtype (round to bf16; for an fp8 destination divide by the scale
+ *   and convert); supports_fused_pre_indexer (head dim 128, rotary dim 64,
+ *   NeoX style, MRoPE section summing to 32).  The compression of the keys
+ *   that the same page's kernel performs is not covered.
+ *
+ *   For head x of a token (128 bf16 features), in fp32:
+ *     rrms = 1/sqrt(sum(x^2)/128 + eps),  y_d = (x_d * rrms) * (w_d + 1),
+ *   y rounded to cos_sin_dtype; then for pair j < 32, in cos_sin_dtype with
+ *   one rounding per operation and no fused multiply-add,
+ *     out_j = y_j c_j - y_{j+32} s_j,  out_{j+32} = y_{j+32} c_j + y_j s_j;
+ *   features 64..127 are y.  The sum of squares is the fp32 rounding of the
+ *   exact sum and rrms the fp32 rounding of 1/sqrt (the page leaves the
+ *   order and the reciprocal square root's accuracy open).
+ *
+ *   q          : device bf16 [num_tokens][num_heads][128]; token stride
+ *                q_stride_token elements (>= num_heads*128 when
+ *                num_tokens > 1, a multiple of 8), heads contiguous, 16-byte
+ *                aligned.
+ *   positions  : device int64; token t's position on axis a (0 temporal,
+ *                1 height, 2 width) at positions[a*pos_stride_axis +
+ *                t*pos_stride_token].  Without MRoPE only axis 0 is read.
+ *   cos_sin    : device [cos_sin_rows][64] of cos_sin_dtype (QSA_DTYPE_BF16
+ *                or QSA_DTYPE_FP32), contiguous, 16-byte aligned (may be NULL
+ *                when cos_sin_rows is 0): row p holds cos of pairs 0..31,
+ *                then their sin; only rows that positions name are read.  A position outside
+ *                [0, cos_sin_rows) is the caller's error: the pairs that use
+ *                it come out NaN (the other features are unaffected).
+ *   norm_weight: device [128] of weight_dtype (QSA_DTYPE_BF16 or
+ *                QSA_DTYPE_FP32), 16-byte aligned; the gain is weight + 1.
+ *   eps        : finite, added to the mean square.
+ *   mrope_section : host int32[3] (t, h, w), each >= 0, summing to 32, or
+ *                NULL for plain rotary.  Pair j reads the height position
+ *                when j % 3 == 1 and j < 3h, the width position when
+ *                j % 3 == 2 and j < 3w, else the temporal one; every axis
+ *                reads the same table.  (The page adds the three masked
+ *                reads to zero, so a -0 entry reads as +0; so does this.)
+ *   q_out      : device [num_tokens][num_heads][128] of out_dtype at element
+ *                strides out_stride_token, out_stride_head (multiples of 8),
+ *                unit feature stride, 16-byte (bf16) or 8-byte (e4m3)
+ *                aligned; must not overlap q.  QSA_DTYPE_BF16: the result
+ *                rounded to bf16 (ties to even).  QSA_DTYPE_FP8_E4M3: that
+ *                bf16 value divided by out_scale (finite, > 0) in fp32, then
+ *                the nearest finite e4m3 value (ties to the even code, so
+ *                magnitudes above 448 give 448; NaN gives 0x7F).
+ *   Errors: INVALID_ARGUMENT for negative counts, num_heads outside
+ *   [1, 1024], a bad section, eps or out_scale, a short q stride or a NULL
+ *   pointer that has work to feed; UNSUPPORTED for other dtypes; LAYOUT for
+ *   misaligned pointers or strides.  One kernel runs on `stream`.
+ */
+int qsa_prepare_q(const void *q, int64_t q_stride_token, int32_t num_tokens, int32_t num_heads,
+                  const int64_t *positions, int64_t pos_stride_axis, int64_t pos_stride_token,
+                  const void *cos_sin, int32_t cos_sin_dtype, int64_t cos_sin_rows, const void *norm_weight,
+                  int32_t weight_dtype, float eps, const int32_t *mrope_section, void *q_out,
+                  int32_t out_dtype, float out_scale, int64_t out_stride_token, int64_t out_stride_head,
+                  void *stream);
 
 #ifdef __cplusplus
 }

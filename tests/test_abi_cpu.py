@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.qsa_abi_version() == 5
+    assert lib.qsa_abi_version() == 6
 
 
 def test_launch_events_set_and_clear_without_device(lib):
@@ -229,6 +229,63 @@ def test_gather_nothing_to_do(lib):
     assert _gather(lib, num_reqs=0, counts=None, out=None) == 0
     assert _gather(lib, max_keys=0, counts=None) == 0
     assert _gather(lib, fmt=2, out_stride=144, out_rows=0) == 0
+    assert _err(lib) == ""
+
+
+def _prepare(lib, **kw):
+    import ctypes
+    a = dict(q=FAKE, qs=512, T=64, H=4, pos=FAKE, pa=0, pt=1, cs=FAKE, csf=0, rows=1000, w=FAKE, wf=0,
+             eps=1e-6, sec=None, out=FAKE, outf=0, scale=1.0, ost=512, osh=128)
+    a.update(kw)
+    sec = None
+    if a["sec"] is not None:
+        sec = (ctypes.c_int32 * 3)(*a["sec"])
+    return lib.qsa_prepare_q(a["q"], a["qs"], a["T"], a["H"], a["pos"], a["pa"], a["pt"], a["cs"], a["csf"],
+                             a["rows"], a["w"], a["wf"], a["eps"], None if sec is None else ctypes.addressof(sec),
+                             a["out"], a["outf"], a["scale"], a["ost"], a["osh"], None)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(csf=1), 2, "cos/sin table format"),
+    (dict(csf=2), 2, "cos/sin table format"),
+    (dict(wf=2), 2, "norm weight format"),
+    (dict(outf=1), 2, "output format"),
+    (dict(outf=3), 2, "output format"),
+    (dict(T=-1), 1, "negative"),
+    (dict(rows=-1), 1, "negative"),
+    (dict(cs=None, rows=-1), 1, "negative"),
+    (dict(H=0), 1, "num_heads"),
+    (dict(H=1025), 1, "num_heads"),
+    (dict(eps=float("nan")), 1, "eps"),
+    (dict(eps=float("inf")), 1, "eps"),
+    (dict(outf=2, scale=0.0), 1, "out_scale"),
+    (dict(outf=2, scale=float("inf")), 1, "out_scale"),
+    (dict(sec=(16, 8, 9)), 1, "MRoPE section"),
+    (dict(sec=(34, -1, -1)), 1, "MRoPE section"),
+    (dict(qs=256), 1, "q_stride_token"),
+    (dict(q=None), 1, "NULL"),
+    (dict(pos=None), 1, "NULL"),
+    (dict(cs=None), 1, "NULL"),
+    (dict(w=None), 1, "NULL"),
+    (dict(out=None), 1, "NULL"),
+    (dict(q=FAKE + 8), 3, "aligned"),
+    (dict(qs=516), 3, "aligned"),
+    (dict(cs=FAKE + 4), 3, "aligned"),
+    (dict(w=FAKE + 8), 3, "aligned"),
+    (dict(pos=FAKE + 4), 3, "aligned"),
+    (dict(out=FAKE + 8), 3, "aligned"),
+    (dict(outf=2, out=FAKE + 4), 3, "aligned"),
+    (dict(ost=516), 3, "aligned"),
+    (dict(osh=132), 3, "aligned"),
+])
+def test_prepare_q_rejects(lib, kw, code, text):
+    assert _prepare(lib, **kw) == code
+    assert text in _err(lib)
+
+
+def test_prepare_q_nothing_to_do(lib):
+    assert _prepare(lib, T=0, q=None, pos=None, cs=None, w=None, out=None) == 0
+    assert _prepare(lib, T=0, sec=(16, 8, 8), pa=1) == 0
     assert _err(lib) == ""
 
 

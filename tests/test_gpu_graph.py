@@ -11,7 +11,7 @@ import torch
 
 from oracle import oracle as O
 from tests.parity import bf16_to_device, i32_to_device
-from workloads import FP8_K_SCALE, decode_inputs, fp8_e4m3_cache, normal_bf16
+from workloads import FP8_K_SCALE, decode_inputs, fp8_e4m3_cache, normal_bf16, prepare_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +54,13 @@ def test_capture_and_replay_all_entry_points():
     comp_np = O.comp_lens(dec.seq_lens).astype(np.int32)
     offs = i32_to_device(np.concatenate([[0], np.cumsum(comp_np[:-1])]))
     kg = torch.empty((int(comp_np.sum()), 128), dtype=torch.bfloat16, device=dev)
-    outs = (dec_out, pre_out, top, fused, meta[0], meta[1], meta[2], meta[3], dec8, slots, work, kg)
+    # Query preparation (MRoPE, e4m3 store) of 200 tokens x 4 heads.
+    prep = prepare_inputs(200, 4, seed=63, first_pos=300, table_rows=600, mrope=True)
+    prep_q, prep_pos = bf16_to_device(prep.q), torch.from_numpy(prep.positions).cuda()
+    prep_cs, prep_w = bf16_to_device(prep.cos_sin), bf16_to_device(prep.weight)
+    prep_out = torch.empty((200, 4, 128), dtype=torch.float8_e4m3fn, device=dev)
+    outs = (dec_out, pre_out, top, fused, meta[0], meta[1], meta[2], meta[3], dec8, slots, work, kg,
+            prep_out.view(torch.uint8))
 
     def run():
         assert lib.qsa_build_metadata(qsl.data_ptr(), seq.data_ptr(), 3, n_tok, 4, None, meta[0].data_ptr(),
@@ -67,6 +73,8 @@ def test_capture_and_replay_all_entry_points():
         qsa.qsa_mqa_decode_typed(q_dec, pool8, pt, comp, visd, k_scale=FP8_K_SCALE, out=dec8)
         qsa.qsa_build_cache_metadata(qsl, seq, n_tok, bt, 16, 4, max_num_work=32, slot_mapping=slots, k_work=work)
         qsa.qsa_gather_keys(pool, pt, comp, offs, int(comp_np.max()), out=kg)
+        qsa.qsa_prepare_q(prep_q, prep_pos, prep_cs, prep_w, prep.eps, mrope_section=(16, 8, 8), out=prep_out,
+                          out_scale=0.25)
 
     run()
     torch.cuda.synchronize()
@@ -79,6 +87,8 @@ def test_capture_and_replay_all_entry_points():
     assert np.array_equal(want[9].cpu().numpy(), O.cache_slots(dec.query_start_loc, dec.seq_lens, n_tok,
                                                                dec.page_table, 16, 4))
     assert np.array_equal(want[10].cpu().numpy(), O.k_work(dec.query_start_loc, dec.seq_lens, 32, 4))
+    assert np.array_equal(want[12].cpu().numpy(), O.prepare_q(prep.q, prep.positions, prep.cos_sin, prep.weight,
+                                                              prep.eps, (16, 8, 8), "fp8_e4m3", 0.25))
 
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -92,7 +102,8 @@ def test_capture_and_replay_all_entry_points():
     torch.cuda.synchronize()
     for rep in range(4):
         for o in outs:
-            o.view(torch.int16).fill_(0x7FC0 + rep)     # poison between replays (eager)
+            (o if o.dtype == torch.uint8 else o.view(torch.int16)).fill_(0x7F - rep if o.dtype == torch.uint8
+                                                                          else 0x7FC0 + rep)  # poison (eager)
         assert not torch.equal(outs[0], want[0])
         scratch = torch.empty_like(dec_out)
         qsa.qsa_mqa_decode(q_dec, pool, pt, comp, visd, out=scratch)  # eager library work between replays
@@ -100,7 +111,7 @@ def test_capture_and_replay_all_entry_points():
         graph.replay()
         torch.cuda.synchronize()
         names = ("decode", "prefill", "top-k", "fused top-k", "token_to_req", "positions", "visible", "comp_lens",
-                 "fp8 decode", "cache slots", "work items", "gathered keys")
+                 "fp8 decode", "cache slots", "work items", "gathered keys", "prepared q")
         for name, o, w in zip(names, outs, want):
             assert torch.equal(o, w), f"replay {rep}: {name} differs"
         assert torch.equal(scratch.view(torch.int32), want[0].view(torch.int32))

@@ -227,3 +227,41 @@ WORKLOADS = {
         "1 request, 8,192 query tokens over a 100,000-token prefix (27,048 keys)",
         dict(num_reqs=1, query_len=8192, prefix=100_000, topk=512)),
 }
+
+
+@dataclass
+class PrepareInputs:
+    q: np.ndarray          # bf16 bits [T, H*128]
+    positions: np.ndarray  # int64 [T], or [3, T] (temporal, height, width)
+    cos_sin: np.ndarray    # [rows, 64]: 32 cos then 32 sin; bf16 bits (uint16) or float32
+    weight: np.ndarray     # [128]: bf16 bits or float32
+    eps: float = 1e-6
+
+
+def rope_table(rows: int, fmt: str = "bf16", base: float = 10000.0) -> np.ndarray:
+    """A NeoX rotary cos/sin table as the caller supplies it (rotary dim 64):
+    row p holds cos(p * base^(-j/32)) for pairs j < 32, then the sines."""
+    inv = base ** (-np.arange(32) / 32.0)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv[None, :]
+    t = np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+    return t if fmt == "fp32" else bf16_bits(t)
+
+
+def prepare_inputs(num_tokens: int, num_heads: int, seed: int, first_pos: int = 0, table_rows: int | None = None,
+                   table: str = "bf16", weight: str = "bf16", mrope: bool = False) -> PrepareInputs:
+    """Query heads of one prefill chunk at positions first_pos, first_pos+1, ...
+    q ~ N(0, 1) in bf16; the RMSNorm weight ~ N(0, 0.1) (a Gemma gain near 1).
+    With mrope the height and width positions trail the temporal one by up
+    to 31, as for image patches."""
+    rng = np.random.default_rng(seed)
+    q = normal_bf16(rng, (num_tokens, num_heads * DIM))
+    t = first_pos + np.arange(num_tokens, dtype=np.int64)
+    if mrope:
+        h = np.maximum(t - rng.integers(0, 32, num_tokens), 0)
+        w = np.maximum(t - rng.integers(0, 32, num_tokens), 0)
+        positions = np.stack([t, h, w]).astype(np.int64)
+    else:
+        positions = t
+    rows = table_rows if table_rows is not None else first_pos + num_tokens
+    w_f = (rng.standard_normal(DIM) * 0.1).astype(np.float32)
+    return PrepareInputs(q, positions, rope_table(rows, table), w_f if weight == "fp32" else bf16_bits(w_f))
