@@ -36,13 +36,19 @@ namespace {
 
 constexpr int kRowsPerBlock = 16;  // 256 threads, 16 lanes per (token, head) row
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
+// fp32 -> the nearest-even bf16 value, as fp32 (three integer operations).
+// A NaN whose payload sits in the upper 16 bits stays NaN; the kernel only
+// feeds it such NaNs (bf16 inputs, quiet arithmetic results, and fp32
+// weights canonicalized at load).
+__device__ __forceinline__ float bf16_round(float f) {
     const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
 }
 
-__device__ __forceinline__ float bf16_value(float f) { return __uint_as_float(bf16_rne(f) << 16); }
+// Two values that are already bf16 (low 16 bits zero) packed, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
 
 // Nearest finite OCP e4m3 value, ties to the even code; NaN -> 0x7f.
 __device__ __forceinline__ uint32_t e4m3_rne_sat(float f) {
@@ -58,10 +64,13 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float f) {
     return sign | (code > 0x7eu ? 0x7eu : code);
 }
 
+// Rounds eight values to the rotation type (bf16, or fp32: unchanged).
 template <bool kTabF32>
-__device__ __forceinline__ float in_type(float v) {
-    if constexpr (kTabF32) return v;
-    else return bf16_value(v);
+__device__ __forceinline__ void round_to_type(float (&v)[8]) {
+    if constexpr (!kTabF32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = bf16_round(v[i]);
+    }
 }
 
 __device__ __forceinline__ void unpack_bf16x8(u32x4 raw, float (&v)[8]) {
@@ -88,17 +97,81 @@ __device__ __forceinline__ void load8(const void *base, int64_t index, float (&v
     }
 }
 
+// Table entries of this lane's eight pairs for one row: cos into c, sin into
+// s, NaN where the position (of the pair's axis, under MRoPE) is off the
+// table.  Only rows inside the table are read.
+template <bool kTabF32, bool kMrope>
+__device__ __forceinline__ void load_rotation(const PrepareQParams &p, const int64_t (&pos)[3], int jb,
+                                              float (&c)[8], float (&s)[8]) {
+    if constexpr (kMrope) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = s[i] = __builtin_nanf("");
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            if (pos[a] < 0 || pos[a] >= p.cos_sin_rows) continue;
+            float ca[8], sa[8];
+            load8<kTabF32>(p.cos_sin, pos[a] * 64 + jb, ca);
+            load8<kTabF32>(p.cos_sin, pos[a] * 64 + 32 + jb, sa);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int j = jb + i;
+                const int axis = (j % 3 == 1 && j < 3 * p.mrope_h) ? 1 : (j % 3 == 2 && j < 3 * p.mrope_w) ? 2 : 0;
+                if (axis == a) {
+                    c[i] = ca[i] + 0.0f;  // the page's masked sum from +0
+                    s[i] = sa[i] + 0.0f;
+                }
+            }
+        }
+    } else {
+        if (pos[0] >= 0 && pos[0] < p.cos_sin_rows) {
+            load8<kTabF32>(p.cos_sin, pos[0] * 64 + jb, c);
+            load8<kTabF32>(p.cos_sin, pos[0] * 64 + 32 + jb, s);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = s[i] = __builtin_nanf("");
+        }
+    }
+}
+
+// Vector-ALU issue, not HBM, limits this kernel at its sizes (a wave64
+// instruction holds a 16-lane SIMD for 4 cycles), so the arithmetic is kept
+// lean: bf16 roundings are three integer operations (the packed hardware
+// convert measured slower here), the subtract of the first half is an add of
+// the negated partner (the same IEEE result), so all 16 lanes of a row run
+// one instruction stream, lanes of the pass-through half select y at the end,
+// and NaN is made canonical once, at the store.
 template <bool kTabF32, bool kWF32, bool kFp8, bool kMrope>
 __global__ __launch_bounds__(kRowsPerBlock * 16) void prepare_q_kernel(PrepareQParams p) {
 #pragma clang fp contract(off)
     const int sub = threadIdx.x & 15;  // features 8*sub .. 8*sub+7 of the row
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
-    const bool live = row < (int64_t)p.num_tokens * p.num_heads;
-    const int64_t t = live ? row / p.num_heads : 0;
-    const int64_t h = live ? row - t * p.num_heads : 0;
+    const uint32_t row = blockIdx.x * (uint32_t)kRowsPerBlock + (threadIdx.x >> 4);
+    const uint32_t heads = (uint32_t)p.num_heads;
+    const bool live = row < (uint32_t)p.num_tokens * heads;  // the host keeps this below 2^31
+    const uint32_t t = live ? row / heads : 0u;
+    const uint32_t h = live ? row - t * heads : 0u;
+
+    const u32x4 raw = live ? load_u32x4(p.q + (int64_t)t * p.q_stride_token + h * 128 + 8 * sub) : zero_u32x4();
+    int64_t pos[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+        pos[a] = live && sub < 8 && (kMrope || a == 0)
+                     ? p.positions[a * p.pos_stride_axis + (int64_t)t * p.pos_stride_token] : -1;
+    float c[8], s[8];
+    if (sub < 8) {
+        load_rotation<kTabF32, kMrope>(p, pos, 8 * (sub & 3), c, s);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = s[i] = 0.0f;
+    }
+    float gain[8];
+    load8<kWF32>(p.weight, 8 * sub, gain);
+    if constexpr (kWF32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gain[i] = gain[i] == gain[i] ? gain[i] : __builtin_nanf("");
+    }
 
     float x[8];
-    unpack_bf16x8(live ? load_u32x4(p.q + t * p.q_stride_token + h * 128 + 8 * sub) : zero_u32x4(), x);
+    unpack_bf16x8(raw, x);
     double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss += (double)(x[i] * x[i]);
@@ -107,81 +180,46 @@ __global__ __launch_bounds__(kRowsPerBlock * 16) void prepare_q_kernel(PrepareQP
     const float mean_eps = (float)ss / 128.0f + p.eps;
     const float rrms = (float)(1.0 / std::sqrt((double)mean_eps));
 
-    float g[8], y[8], partner[8];
-    load8<kWF32>(p.weight, 8 * sub, g);
+    float y[8], o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = in_type<kTabF32>((x[i] * rrms) * (g[i] + 1.0f));
+    for (int i = 0; i < 8; ++i) y[i] = (x[i] * rrms) * (gain[i] + 1.0f);
+    round_to_type<kTabF32>(y);
+    // Lanes 0-3 hold y_j and subtract their partner's term, lanes 4-7 hold
+    // y_{j+32} and add it: out = y c + (+-partner) s.
+    const uint32_t flip = sub < 4 ? 0x80000000u : 0u;
+    float a[8], b[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) partner[i] = __shfl_xor(y[i], 4);
-
-    float o[8];
-    if (sub < 8) {
-        const int jb = 8 * (sub & 3);  // first pair held by this lane
-        float c[8], s[8];
-        if constexpr (kMrope) {
-            int64_t pos[3];
-            bool ok[3];
-            float ca[3][8], sa[3][8];
+    for (int i = 0; i < 8; ++i) {
+        const float partner = __uint_as_float(__float_as_uint(__shfl_xor(y[i], 4)) ^ flip);
+        a[i] = y[i] * c[i];
+        b[i] = partner * s[i];
+    }
+    round_to_type<kTabF32>(a);
+    round_to_type<kTabF32>(b);
 #pragma unroll
-            for (int a = 0; a < 3; ++a) {
-                pos[a] = live ? p.positions[a * p.pos_stride_axis + t * p.pos_stride_token] : 0;
-                ok[a] = pos[a] >= 0 && pos[a] < p.cos_sin_rows;
-                if (ok[a]) {  // only rows inside the table are read
-                    load8<kTabF32>(p.cos_sin, pos[a] * 64 + jb, ca[a]);
-                    load8<kTabF32>(p.cos_sin, pos[a] * 64 + 32 + jb, sa[a]);
-                } else {
+    for (int i = 0; i < 8; ++i) o[i] = a[i] + b[i];
+    round_to_type<kTabF32>(o);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) ca[a][i] = sa[a][i] = 0.0f;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int j = jb + i;
-                const int a = (j % 3 == 1 && j < 3 * p.mrope_h) ? 1 : (j % 3 == 2 && j < 3 * p.mrope_w) ? 2 : 0;
-                const float ci = a == 0 ? ca[0][i] : a == 1 ? ca[1][i] : ca[2][i];
-                const float si = a == 0 ? sa[0][i] : a == 1 ? sa[1][i] : sa[2][i];
-                const bool oki = a == 0 ? ok[0] : a == 1 ? ok[1] : ok[2];
-                c[i] = oki ? ci + 0.0f : __builtin_nanf("");
-                s[i] = oki ? si + 0.0f : __builtin_nanf("");
-            }
-        } else {
-            const int64_t pos = live ? p.positions[t * p.pos_stride_token] : 0;
-            if (pos >= 0 && pos < p.cos_sin_rows) {  // only rows inside the table are read
-                load8<kTabF32>(p.cos_sin, pos * 64 + jb, c);
-                load8<kTabF32>(p.cos_sin, pos * 64 + 32 + jb, s);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) c[i] = s[i] = __builtin_nanf("");
-            }
-        }
-        if (sub < 4) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                o[i] = in_type<kTabF32>(in_type<kTabF32>(y[i] * c[i]) - in_type<kTabF32>(partner[i] * s[i]));
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                o[i] = in_type<kTabF32>(in_type<kTabF32>(y[i] * c[i]) + in_type<kTabF32>(partner[i] * s[i]));
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = y[i];
+    for (int i = 0; i < 8; ++i) {
+        o[i] = sub < 8 ? o[i] : y[i];
+        o[i] = o[i] == o[i] ? o[i] : __builtin_nanf("");  // one NaN: 0x7fc0 in bf16
     }
     if (!live) return;
 
-    const int64_t at = t * p.out_stride_token + h * p.out_stride_head + 8 * sub;
+    const int64_t at = (int64_t)t * p.out_stride_token + (int64_t)h * p.out_stride_head + 8 * sub;
+    if constexpr (kTabF32) {  // bf16 rotation values are already rounded
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = bf16_round(o[i]);
+    }
     if constexpr (kFp8) {
         uint32_t w[2] = {0u, 0u};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float v = __uint_as_float(bf16_rne(o[i]) << 16) / p.out_scale;
-            w[i / 4] |= e4m3_rne_sat(v) << (8 * (i % 4));
-        }
+        for (int i = 0; i < 8; ++i) w[i / 4] |= e4m3_rne_sat(o[i] / p.out_scale) << (8 * (i % 4));
         *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.out) + at) = make_uint2(w[0], w[1]);
     } else {
         u32x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = bf16_rne(o[2 * i]) | (bf16_rne(o[2 * i + 1]) << 16);
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
         *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(p.out) + at) = w;
     }
 }

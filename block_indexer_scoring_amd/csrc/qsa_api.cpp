@@ -312,7 +312,7 @@ int qsa_prepare_q(const void *q, int64_t q_stride_token, int32_t num_tokens, int
     if (num_tokens == 0) return ok();
     if (!q || !positions || (!cos_sin && cos_sin_rows > 0) || !norm_weight || !q_out)
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL q, positions, cos_sin, norm_weight or q_out", fn);
-    if ((int64_t)num_tokens * num_heads > ((int64_t)1 << 35))
+    if ((int64_t)num_tokens * num_heads >= ((int64_t)1 << 31))
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
     const int out_align = out_dtype == QSA_DTYPE_FP8_E4M3 ? 8 : 16;
     if (!aligned(q, 16) || q_stride_token % 8 != 0 || !aligned(cos_sin, 16) || !aligned(norm_weight, 16) ||
