@@ -541,6 +541,7 @@ def main(argv=None) -> int:
         "us": round(pp_us, 3), "tokens": T_pre, "heads": 4, "bytes": pp_bytes,
         "gbps": round(pp_bytes / (pp_us * 1e-6) / 1e9, 2),
         "frac_of_hbm": round(pp_bytes / (pp_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "traffic": read_traffic("prepare.hip", "prepare_q"),
     }
     for e in pp_ev:
         e.close()
