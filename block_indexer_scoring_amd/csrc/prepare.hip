@@ -97,39 +97,46 @@ __device__ __forceinline__ void load8(const void *base, int64_t index, float (&v
     }
 }
 
-// Table entries of this lane's eight pairs for one row: cos into c, sin into
-// s, NaN where the position (of the pair's axis, under MRoPE) is off the
-// table.  Only rows inside the table are read.
-template <bool kTabF32, bool kMrope>
-__device__ __forceinline__ void load_rotation(const PrepareQParams &p, const int64_t (&pos)[3], int jb,
-                                              float (&c)[8], float (&s)[8]) {
-    if constexpr (kMrope) {
+// Raw table words of this lane's eight pairs in one table row: cos and sin,
+// one 16-byte load each for bf16, two for fp32.
+template <bool kTabF32>
+struct TableWords {
+    u32x4 c[kTabF32 ? 2 : 1], s[kTabF32 ? 2 : 1];
+};
+
+constexpr int kBufferWord3 = 0x00020000;     // buffer descriptor word 3: raw dword access
+constexpr uint32_t kOffTable = 0x80000000u;  // a byte offset past any table: the load returns zeros
+
+__device__ __forceinline__ u32x4 load_buffer16(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+}
+
+// The table is read through a buffer resource bounded by its size, so a row
+// off the table (offset kOffTable) reads zeros without touching memory and
+// without a branch: every row's loads then issue in one fixed order.
+template <bool kTabF32>
+__device__ __forceinline__ void load_table(__amdgpu_buffer_rsrc_t rsrc, uint32_t off, TableWords<kTabF32> &w) {
+    if constexpr (kTabF32) {
+        w.c[0] = load_buffer16(rsrc, off);
+        w.c[1] = load_buffer16(rsrc, off + 16);
+        w.s[0] = load_buffer16(rsrc, off + 128);
+        w.s[1] = load_buffer16(rsrc, off + 144);
+    } else {
+        w.c[0] = load_buffer16(rsrc, off);
+        w.s[0] = load_buffer16(rsrc, off + 64);
+    }
+}
+
+template <bool kTabF32>
+__device__ __forceinline__ void unpack_words(const u32x4 (&w)[kTabF32 ? 2 : 1], float (&v)[8]) {
+    if constexpr (kTabF32) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = s[i] = __builtin_nanf("");
-#pragma unroll
-        for (int a = 0; a < 3; ++a) {
-            if (pos[a] < 0 || pos[a] >= p.cos_sin_rows) continue;
-            float ca[8], sa[8];
-            load8<kTabF32>(p.cos_sin, pos[a] * 64 + jb, ca);
-            load8<kTabF32>(p.cos_sin, pos[a] * 64 + 32 + jb, sa);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int j = jb + i;
-                const int axis = (j % 3 == 1 && j < 3 * p.mrope_h) ? 1 : (j % 3 == 2 && j < 3 * p.mrope_w) ? 2 : 0;
-                if (axis == a) {
-                    c[i] = ca[i] + 0.0f;  // the page's masked sum from +0
-                    s[i] = sa[i] + 0.0f;
-                }
-            }
+        for (int i = 0; i < 4; ++i) {
+            v[i] = __uint_as_float(w[0][i]);
+            v[4 + i] = __uint_as_float(w[1][i]);
         }
     } else {
-        if (pos[0] >= 0 && pos[0] < p.cos_sin_rows) {
-            load8<kTabF32>(p.cos_sin, pos[0] * 64 + jb, c);
-            load8<kTabF32>(p.cos_sin, pos[0] * 64 + 32 + jb, s);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) c[i] = s[i] = __builtin_nanf("");
-        }
+        unpack_bf16x8(w[0], v);
     }
 }
 
@@ -150,21 +157,39 @@ __global__ __launch_bounds__(kRowsPerBlock * 16) void prepare_q_kernel(PrepareQP
     const uint32_t t = live ? row / heads : 0u;
     const uint32_t h = live ? row - t * heads : 0u;
 
-    const u32x4 raw = live ? load_u32x4(p.q + (int64_t)t * p.q_stride_token + h * 128 + 8 * sub) : zero_u32x4();
+    // Issue order: positions and weight, then the row, then the table rows
+    // (which wait only for the positions), so the norm below overlaps the
+    // table reads.
     int64_t pos[3];
 #pragma unroll
     for (int a = 0; a < 3; ++a)
         pos[a] = live && sub < 8 && (kMrope || a == 0)
                      ? p.positions[a * p.pos_stride_axis + (int64_t)t * p.pos_stride_token] : -1;
-    float c[8], s[8];
-    if (sub < 8) {
-        load_rotation<kTabF32, kMrope>(p, pos, 8 * (sub & 3), c, s);
+    u32x4 wraw[kWF32 ? 2 : 1];
+    if constexpr (kWF32) {
+        wraw[0] = load_u32x4(static_cast<const float *>(p.weight) + 8 * sub);
+        wraw[1] = load_u32x4(static_cast<const float *>(p.weight) + 8 * sub + 4);
     } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = s[i] = 0.0f;
+        wraw[0] = load_u32x4(static_cast<const uint16_t *>(p.weight) + 8 * sub);
     }
+    const u32x4 raw = live ? load_u32x4(p.q + (int64_t)t * p.q_stride_token + h * 128 + 8 * sub) : zero_u32x4();
+    constexpr int kAxes = kMrope ? 3 : 1;
+    const int jb = 8 * (sub & 3);  // first pair of this lane (sub < 8)
+    constexpr uint32_t kRowBytes = kTabF32 ? 256 : 128;
+    // The host keeps the table below 2^31 bytes.
+    const __amdgpu_buffer_rsrc_t tab = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(p.cos_sin), 0, (int)(p.cos_sin_rows * kRowBytes), kBufferWord3);
+    TableWords<kTabF32> tw[kAxes];
+    bool ok[kAxes];
+#pragma unroll
+    for (int a = 0; a < kAxes; ++a) {
+        ok[a] = pos[a] >= 0 && pos[a] < p.cos_sin_rows;  // only rows inside the table are read
+        const uint32_t off = ok[a] ? (uint32_t)pos[a] * kRowBytes + jb * (kRowBytes / 64) : kOffTable;
+        load_table<kTabF32>(tab, off, tw[a]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the table reads issued ahead of the norm
     float gain[8];
-    load8<kWF32>(p.weight, 8 * sub, gain);
+    unpack_words<kWF32>(wraw, gain);
     if constexpr (kWF32) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) gain[i] = gain[i] == gain[i] ? gain[i] : __builtin_nanf("");
@@ -179,11 +204,39 @@ __global__ __launch_bounds__(kRowsPerBlock * 16) void prepare_q_kernel(PrepareQP
     for (int m = 1; m < 16; m <<= 1) ss += __shfl_xor(ss, m);
     const float mean_eps = (float)ss / 128.0f + p.eps;
     const float rrms = (float)(1.0 / std::sqrt((double)mean_eps));
+    __builtin_amdgcn_sched_barrier(0);  // the table words are first needed below
 
     float y[8], o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = (x[i] * rrms) * (gain[i] + 1.0f);
     round_to_type<kTabF32>(y);
+    float c[8], s[8];
+    if constexpr (kMrope) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = s[i] = __builtin_nanf("");
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            if (!ok[a]) continue;
+            float ca[8], sa[8];
+            unpack_words<kTabF32>(tw[a].c, ca);
+            unpack_words<kTabF32>(tw[a].s, sa);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int j = jb + i;
+                const int axis = (j % 3 == 1 && j < 3 * p.mrope_h) ? 1 : (j % 3 == 2 && j < 3 * p.mrope_w) ? 2 : 0;
+                if (axis == a) {
+                    c[i] = ca[i] + 0.0f;  // the page's masked sum from +0
+                    s[i] = sa[i] + 0.0f;
+                }
+            }
+        }
+    } else if (ok[0]) {
+        unpack_words<kTabF32>(tw[0].c, c);
+        unpack_words<kTabF32>(tw[0].s, s);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = s[i] = __builtin_nanf("");
+    }
     // Lanes 0-3 hold y_j and subtract their partner's term, lanes 4-7 hold
     // y_{j+32} and add it: out = y c + (+-partner) s.
     const uint32_t flip = sub < 4 ? 0x80000000u : 0u;

@@ -314,6 +314,8 @@ int qsa_prepare_q(const void *q, int64_t q_stride_token, int32_t num_tokens, int
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL q, positions, cos_sin, norm_weight or q_out", fn);
     if ((int64_t)num_tokens * num_heads >= ((int64_t)1 << 31))
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
+    if (cos_sin_rows > (int64_t)INT32_MAX / (cos_sin_dtype == QSA_DTYPE_FP32 ? 256 : 128))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: cos/sin table above 2^31 bytes", fn);
     const int out_align = out_dtype == QSA_DTYPE_FP8_E4M3 ? 8 : 16;
     if (!aligned(q, 16) || q_stride_token % 8 != 0 || !aligned(cos_sin, 16) || !aligned(norm_weight, 16) ||
         !aligned(positions, 8) || !aligned(q_out, out_align) || out_stride_token % 8 != 0 ||

@@ -438,7 +438,8 @@ int qsa_prefill_topk_workspace_bytes(int32_t num_rows, int32_t out_cols, int32_t
  *                the nearest finite e4m3 value (ties to the even code, so
  *                magnitudes above 448 give 448; NaN gives 0x7F).
  *   Errors: INVALID_ARGUMENT for negative counts, num_heads outside
- *   [1, 1024], a bad section, eps or out_scale, a short q stride or a NULL
+ *   [1, 1024], num_tokens * num_heads >= 2^31, a table of 2^31 bytes or
+ *   more, a bad section, eps or out_scale, a short q stride or a NULL
  *   pointer that has work to feed; UNSUPPORTED for other dtypes; LAYOUT for
  *   misaligned pointers or strides.  One kernel runs on `stream`.
  */

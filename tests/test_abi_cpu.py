@@ -254,6 +254,9 @@ def _prepare(lib, **kw):
     (dict(T=-1), 1, "negative"),
     (dict(rows=-1), 1, "negative"),
     (dict(cs=None, rows=-1), 1, "negative"),
+    (dict(rows=1 << 24), 1, "table above"),
+    (dict(csf=3, rows=1 << 23), 1, "table above"),
+    (dict(T=1 << 29, H=4), 1, "too large"),
     (dict(H=0), 1, "num_heads"),
     (dict(H=1025), 1, "num_heads"),
     (dict(eps=float("nan")), 1, "eps"),
