@@ -157,14 +157,16 @@ __global__ __launch_bounds__(kRowsPerBlock * 16) void prepare_q_kernel(PrepareQP
     const uint32_t t = live ? row / heads : 0u;
     const uint32_t h = live ? row - t * heads : 0u;
 
-    // Issue order: positions and weight, then the row, then the table rows
+    // Issue order: positions, the row, the weight, then the table rows
     // (which wait only for the positions), so the norm below overlaps the
     // table reads.
-    int64_t pos[3];
+    // Lanes past the last row read token 0, head 0 (which exists whenever the
+    // kernel runs) and store nothing: unconditional loads keep the issue order.
+    constexpr int kAxes = kMrope ? 3 : 1;
+    int64_t pos[kAxes];
 #pragma unroll
-    for (int a = 0; a < 3; ++a)
-        pos[a] = live && sub < 8 && (kMrope || a == 0)
-                     ? p.positions[a * p.pos_stride_axis + (int64_t)t * p.pos_stride_token] : -1;
+    for (int a = 0; a < kAxes; ++a) pos[a] = p.positions[a * p.pos_stride_axis + (int64_t)t * p.pos_stride_token];
+    const u32x4 raw = load_u32x4(p.q + (int64_t)t * p.q_stride_token + h * 128 + 8 * sub);
     u32x4 wraw[kWF32 ? 2 : 1];
     if constexpr (kWF32) {
         wraw[0] = load_u32x4(static_cast<const float *>(p.weight) + 8 * sub);
@@ -172,8 +174,6 @@ __global__ __launch_bounds__(kRowsPerBlock * 16) void prepare_q_kernel(PrepareQP
     } else {
         wraw[0] = load_u32x4(static_cast<const uint16_t *>(p.weight) + 8 * sub);
     }
-    const u32x4 raw = live ? load_u32x4(p.q + (int64_t)t * p.q_stride_token + h * 128 + 8 * sub) : zero_u32x4();
-    constexpr int kAxes = kMrope ? 3 : 1;
     const int jb = 8 * (sub & 3);  // first pair of this lane (sub < 8)
     constexpr uint32_t kRowBytes = kTabF32 ? 256 : 128;
     // The host keeps the table below 2^31 bytes.
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kRowsPerBlock * 16) void prepare_q_kernel(PrepareQP
     bool ok[kAxes];
 #pragma unroll
     for (int a = 0; a < kAxes; ++a) {
-        ok[a] = pos[a] >= 0 && pos[a] < p.cos_sin_rows;  // only rows inside the table are read
+        ok[a] = sub < 8 && pos[a] >= 0 && pos[a] < p.cos_sin_rows;  // only rows inside the table are read
         const uint32_t off = ok[a] ? (uint32_t)pos[a] * kRowBytes + jb * (kRowBytes / 64) : kOffTable;
         load_table<kTabF32>(tab, off, tw[a]);
     }
