@@ -22,10 +22,13 @@
 // MRoPE table entry is read as the page's masked sum (so -0 becomes +0).  A
 // position outside the table gives NaN for the pairs that use it.
 //
-// HBM-bound: each (token, head) row is 256 bytes in and 256 (bf16) or 128
-// (e4m3) bytes out.  Sixteen lanes hold one row, 16 bytes each, so every
-// load and store instruction moves whole rows; a lane's NeoX partner is the
-// lane 4 away (features +-32), reached with a cross-lane swizzle.
+// Each (token, head) row is 256 bytes in and 256 (bf16) or 128 (e4m3) bytes
+// out.  Sixteen lanes hold one row, 16 bytes each, so every load and store
+// instruction moves whole rows; a lane's NeoX partner is the lane 4 away
+// (features +-32), reached with a cross-lane swizzle.  At these sizes the
+// kernel is limited by vector-ALU issue and by the dependent position ->
+// table read rather than by HBM bandwidth, so the arithmetic is kept lean
+// and every load is issued in one fixed order (see the kernel).
 #include <cmath>
 
 #include "qsa_device.h"
@@ -78,22 +81,6 @@ __device__ __forceinline__ void unpack_bf16x8(u32x4 raw, float (&v)[8]) {
     for (int i = 0; i < 4; ++i) {
         v[2 * i] = __uint_as_float(raw[i] << 16);
         v[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
-    }
-}
-
-// Eight consecutive table (or weight) entries starting at `base + index`.
-template <bool kF32>
-__device__ __forceinline__ void load8(const void *base, int64_t index, float (&v)[8]) {
-    if constexpr (kF32) {
-        const u32x4 a = load_u32x4(static_cast<const float *>(base) + index);
-        const u32x4 b = load_u32x4(static_cast<const float *>(base) + index + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[i] = __uint_as_float(a[i]);
-            v[4 + i] = __uint_as_float(b[i]);
-        }
-    } else {
-        unpack_bf16x8(load_u32x4(static_cast<const uint16_t *>(base) + index), v);
     }
 }
 
