@@ -152,3 +152,22 @@ def test_prepare_zero_tokens_and_table_rows():
     got = out.cpu().view(torch.int16).numpy().view(np.uint16)
     _assert_same(got, _oracle(inp), "empty table")
     assert np.all(got[:, :, :64] == 0x7FC0) and not np.any(got[:, :, 64:] == 0x7FC0)
+
+
+@pytest.mark.parametrize("table", ["bf16", "fp32"])
+def test_prepare_non_finite_fp32_weights(table):
+    # fp32 weights holding a NaN with a full payload, infinities and a huge
+    # finite value: the non-finite results must come out exactly as the
+    # oracle's (one NaN pattern, signed infinities), in every format.
+    inp = prepare_inputs(24, 4, seed=88, first_pos=3, table_rows=40, table=table, weight="fp32")
+    w = inp.weight.copy()
+    w[[2, 40, 70]] = np.array([0x7FFFFFFF, 0xFF800000, 0x7F800000], np.uint32).view(np.float32)
+    w[100] = np.float32(3e38)
+    q = inp.q.copy()
+    q[5, :128] = 0                                   # 0 * inf gain -> NaN
+    case = type(inp)(q, inp.positions, inp.cos_sin, w, 1e-6)
+    got, want = _gpu(case), _oracle(case)
+    _assert_same(got, want, f"non-finite weights, {table} table")
+    assert (got == 0x7FC0).any() and ((got & 0x7FFF) == 0x7F80).any()
+    _assert_same(_gpu(case, out_format="fp8_e4m3", out_scale=0.5),
+                 _oracle(case, out_format="fp8_e4m3", out_scale=0.5), f"non-finite weights e4m3, {table} table")
