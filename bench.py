@@ -4,12 +4,14 @@ One step = one pass of the whole path over one mixed batch, as a serving step
 would run it (decodes first, then prefills):
   1. qsa_build_metadata  per-token request, position, visible blocks, key
                          intervals for all 8,256 query tokens of the batch;
-  2. qsa_mqa_decode      16 requests x DQL 4, log-normal contexts
+  2. qsa_build_decode_plan  the decode task table of the step (built once
+                         per step and shared by every layer's decode);
+  3. qsa_mqa_decode_planned  16 requests x DQL 4, log-normal contexts
                          3,508 / 51,200 / 102,400 tokens (min/mean/max),
                          page_size 64, keys read through the page table;
-  3. qsa_mqa_prefill     1 request: 8,192 query tokens over a 100,000-token
+  4. qsa_mqa_prefill     1 request: 8,192 query tokens over a 100,000-token
                          prefix (27,048 compressed keys);
-  4. qsa_topk_blocks     top-512 blocks of every decode row and every
+  5. qsa_topk_blocks     top-512 blocks of every decode row and every
                          prefill row.
 Inputs are resident in HBM before timing.  The decode key cache rotates over
 several independently generated pools (more bytes than the 256 MB Infinity
@@ -267,7 +269,9 @@ def main(argv=None) -> int:
             raise RuntimeError(lib.qsa_last_error().decode())
 
     scale = qsa.DEFAULT_SCALE
-    NAMES = ["metadata", "decode", "prefill", "topk_decode", "topk_prefill"]
+    NAMES = ["metadata", "decode_plan", "decode", "prefill", "topk_decode", "topk_prefill"]
+    plan_bytes = qsa.qsa_decode_plan_bytes(R, dec.out_cols)
+    plan = torch.empty(plan_bytes, dtype=torch.uint8, device=dev)
 
     def step(i, events=None):
         pool = pools[i % len(pools)]
@@ -283,21 +287,25 @@ def main(argv=None) -> int:
             meta["visible"].data_ptr(), meta["comp_lens"].data_ptr(),
             meta["row_k_start"].data_ptr(), meta["row_k_end"].data_ptr(), sh))
         rec(1)
-        check(lib.qsa_mqa_decode(
-            q_dec.data_ptr(), q_dec.stride(0), q_dec.stride(1), q_dec.stride(2), pool.data_ptr(),
-            pool.shape[0], pool.shape[1], page_table.data_ptr(), page_table.stride(0),
-            page_table.shape[1], meta["comp_lens"].data_ptr(), meta["visible"].data_ptr(), R, DQL,
-            4, 128, scale, dec_out.data_ptr(), dec_out.stride(0), dec_out.shape[1], sh))
+        check(lib.qsa_build_decode_plan(
+            meta["comp_lens"].data_ptr(), page_table.data_ptr(), page_table.stride(0), page_table.shape[1],
+            pool.shape[0], pool.shape[1], R, dec_out.shape[1], plan.data_ptr(), plan_bytes, sh))
         rec(2)
+        check(lib.qsa_mqa_decode_planned(
+            plan.data_ptr(), plan_bytes, q_dec.data_ptr(), qsa.QSA_DTYPE_BF16, q_dec.stride(0), q_dec.stride(1),
+            q_dec.stride(2), pool.data_ptr(), qsa.QSA_DTYPE_BF16, 1.0, pool.shape[0], pool.shape[1],
+            page_table.data_ptr(), page_table.stride(0), page_table.shape[1], meta["visible"].data_ptr(), R,
+            DQL, 4, 128, scale, dec_out.data_ptr(), dec_out.stride(0), dec_out.shape[1], sh))
+        rec(3)
         check(lib.qsa_mqa_prefill(
             q_pre.data_ptr(), q_pre.stride(0), q_pre.stride(1), k_pre.data_ptr(), k_pre.stride(0),
             k_pre.shape[0], meta["row_k_start"].data_ptr() + 4 * T_dec,
             meta["row_k_end"].data_ptr() + 4 * T_dec, T_pre, 4, 128, scale, pre_out.data_ptr(),
             pre_out.stride(0), pre_out.shape[1], sh))
-        rec(3)
+        rec(4)
         check(lib.qsa_topk_blocks(dec_out.data_ptr(), dec_out.stride(0), T_dec, dec_out.shape[1],
                                   TOPK, dec_top.data_ptr(), TOPK, sh))
-        rec(4)
+        rec(5)
         check(lib.qsa_topk_blocks(pre_out.data_ptr(), pre_out.stride(0), T_pre, pre_out.shape[1],
                                   TOPK, pre_top.data_ptr(), TOPK, sh))
         if events:
@@ -381,6 +389,38 @@ def main(argv=None) -> int:
         "decode_bytes": dbytes, "prefill_bytes": pbytes, "prefill_flops": pflops,
         "topk_prefill_bytes": tk_bytes,
     }
+
+    # The decode without a task table (qsa_mqa_decode: each wave finds its
+    # span from the compressed lengths), for context: 20 launches over the
+    # rotating pools, and a bitwise check that both forms score alike.
+    un_ev = [HipEvents(2) for _ in range(20)]
+    un_out = torch.empty_like(dec_out)
+
+    def mapped_decode(pool, out):
+        check(lib.qsa_mqa_decode(
+            q_dec.data_ptr(), q_dec.stride(0), q_dec.stride(1), q_dec.stride(2), pool.data_ptr(),
+            pool.shape[0], pool.shape[1], page_table.data_ptr(), page_table.stride(0),
+            page_table.shape[1], meta["comp_lens"].data_ptr(), meta["visible"].data_ptr(), R, DQL,
+            4, 128, scale, out.data_ptr(), out.stride(0), out.shape[1], sh))
+
+    for j in range(24):
+        if j >= 4:
+            check(lib.qsa_set_launch_events(un_ev[j - 4].ev[0], un_ev[j - 4].ev[1]))
+        mapped_decode(pools[j % len(pools)], un_out)
+        check(lib.qsa_set_launch_events(None, None))
+    torch.cuda.synchronize()
+    un_us = float(np.mean([e.elapsed_us(0, 1) for e in un_ev]))
+    for e in un_ev:
+        e.close()
+    last_pool = pools[(args.warmup + args.steps - 1) % len(pools)]
+    mapped_decode(last_pool, un_out)
+    torch.cuda.synchronize()
+    result["decode_unplanned"] = {
+        "us": round(un_us, 3), "gbps": round(dbytes / (un_us * 1e-6) / 1e9, 2),
+        "frac_of_hbm": round(dbytes / (un_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "matches_planned": bool(torch.equal(un_out.view(torch.int32), dec_out.view(torch.int32))),
+    }
+    del un_out
 
     # The fused prefill top-k on the same prefill rows, for context: its
     # time (first kernel's begin to last kernel's end), the unfused pair's,

@@ -11,8 +11,22 @@
 // HBM traffic is the unique key bytes plus the output.  Spans that hold keys
 // are dispatched first (request-major), spans past a request's keys (-inf
 // only) after them, so every key-reading wave starts in the first wave of
-// the launch.  A wave issues all 16 KB of its span's loads before the first
-// MFMA; a mapped page is read without per-lane predication.
+// the launch.  A wave finds its task either from the compressed lengths (a
+// wave-wide prefix sum) or, in a planned launch, from one 16-byte entry of a
+// task table built once per step (qsa_build_decode_plan), which also holds
+// the span's physical page: one scalar load stands between the wave's start
+// and its key loads.
+//
+// Loads, in issue order: the request's query fragments (shared by all spans
+// of the request, so they stay in L2), then the span's 16 KB of keys.  When
+// the span lies on one page (page sizes that are multiples of 64), every key
+// load instruction covers whole 128-byte lines: lanes 2m and 2m+1 read the
+// two halves of one line, of key pair (2m, 2m+1) in turn, and swap halves
+// with a DPP permutation afterwards.  Keys are read with the streaming
+// (non-temporal) policy: they are used once, and keeping them out of the
+// caches keeps the queries and tables there.  (Under that policy a line read
+// in halves by two instructions is fetched twice, hence the whole-line
+// layout.)
 //
 // Inside a span the dot products run on the matrix cores: the query vectors
 // of the request, ordered (row j, head h) -> m = 4j + h, form the A operand
@@ -27,38 +41,41 @@
 // Element formats: queries and keys in bf16 or fp16 (MATE "MQA score": both
 // are canonical inputs), or fp8 e4m3 keys (the optional e4m3 compressed
 // indexer cache of the vLLM QSA state backend) with bf16 or fp16 queries.
-// An e4m3 key row is 128 bytes: lane q4 reads its contiguous quarter (32
-// codes, two 16-byte loads per key), converts it exactly to the query's
-// 16-bit format, and the query fragments use the same feature order
-// (features 32*q4 + 8*ks .. +7 in k-step ks), so the products are
-// unchanged.  The cache scale multiplies the head sum together with the
-// score scale (relu commutes with a positive factor).
+// An e4m3 key row is 128 bytes: lane q4 holds its contiguous quarter (32
+// codes), converts it exactly to the query's 16-bit format, and the query
+// fragments use the same feature order (features 32*q4 + 8*ks .. +7 in
+// k-step ks), so the products are unchanged.  The cache scale multiplies the
+// head sum together with the score scale (relu commutes with a positive
+// factor).
 #include "qsa_device.h"
 #include "qsa_internal.h"
-
-#ifndef QSA_DECODE_WAVES_PER_BLOCK
-#define QSA_DECODE_WAVES_PER_BLOCK 1
-#endif
 
 namespace qsa {
 namespace {
 
 constexpr int kSpan = 64;     // keys per wavefront task
 constexpr int kPadSpans = 4;  // spans per -inf-only task
-constexpr int kWavesPerBlock = QSA_DECODE_WAVES_PER_BLOCK;
 
 enum PageMode { kPageGeneric = 0, kPageMultiple64 = 1, kPage64 = 2 };
 
 // Kernel formats: query format plus whether keys are e4m3 codes.
 enum DecodeFormat { kBf16 = 0, kFp16 = 1, kBf16Fp8 = 2, kFp16Fp8 = 3 };
 
+// Where a wave's task comes from.
+enum TaskSource { kMapped = 0, kPlanned = 1 };
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 // Q fragment: lane (n, q4) supplies query vector (row j, head h) of its
 // tile, features `feature` .. +7.
-__device__ __forceinline__ u32x4 load_q_fragment(const DecodeParams &p, int r, int j, int h,
-                                                 int feature) {
-    const uint16_t *src = p.q + (int64_t)r * p.q_stride_req + (int64_t)j * p.q_stride_row +
-                          (int64_t)h * p.q_stride_head + feature;
-    if (p.q_vec) return load_u32x4(src);
+__device__ __forceinline__ const uint16_t *q_fragment_ptr(const DecodeParams &p, int r, int j, int h,
+                                                          int feature) {
+    return p.q + (int64_t)r * p.q_stride_req + (int64_t)j * p.q_stride_row + (int64_t)h * p.q_stride_head +
+           feature;
+}
+
+// The same 8 elements read one by one (Q off the 16-byte grid).
+__device__ __forceinline__ u32x4 load_q_elements(const uint16_t *src) {
     u32x4 v;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -75,6 +92,13 @@ __device__ __forceinline__ int wave_inclusive_sum(int x, int lane) {
     return x;
 }
 
+// Spans of a request that hold keys: ceil(comp / 64), capped at the spans
+// covering out_cols.
+__device__ __forceinline__ int keyed_spans(int comp, int spans) {
+    const int keyed = comp > 0 ? (comp + kSpan - 1) / kSpan : 0;
+    return keyed < spans ? keyed : spans;
+}
+
 struct Task {
     int r;
     int span;  // first span of the task
@@ -84,10 +108,8 @@ struct Task {
 
 // Task order: first every span that holds keys (request-major, one span per
 // task), then the spans past a request's keys (-inf only, kPadSpans spans per
-// task).  Spans of request r that hold keys: ceil(comp_r / 64), capped at the
-// spans covering out_cols.  Each wave derives its task from the compressed
-// lengths with a wave-wide prefix sum, 64 requests per pass, so no task list
-// is needed.
+// task).  Each wave derives its task from the compressed lengths with a
+// wave-wide prefix sum, 64 requests per pass.
 __device__ Task map_task(const DecodeParams &p, int task, int lane) {
     int before = 0;  // tasks of earlier requests in the current pass
 #pragma unroll 1
@@ -97,9 +119,7 @@ __device__ Task map_task(const DecodeParams &p, int task, int lane) {
             const int rr = r0 + lane;
             int cnt = 0;
             if (rr < p.num_reqs) {
-                const int comp = p.comp_lens[rr];
-                int keyed = comp > 0 ? (comp + kSpan - 1) / kSpan : 0;
-                keyed = keyed < p.spans ? keyed : p.spans;
+                const int keyed = keyed_spans(p.comp_lens[rr], p.spans);
                 cnt = pass == 0 ? keyed : (p.spans - keyed + kPadSpans - 1) / kPadSpans;
             }
             const int incl = wave_inclusive_sum(cnt, lane);
@@ -110,9 +130,7 @@ __device__ Task map_task(const DecodeParams &p, int task, int lane) {
                 const int idx = __popcll(below);  // first lane whose range holds `local`
                 const int excl = __builtin_amdgcn_readlane(incl - cnt, idx);
                 if (pass == 0) return Task{r0 + idx, local - excl, true, true};
-                const int comp = load_uniform(p.comp_lens + r0 + idx);
-                int keyed_r = comp > 0 ? (comp + kSpan - 1) / kSpan : 0;
-                keyed_r = keyed_r < p.spans ? keyed_r : p.spans;
+                const int keyed_r = keyed_spans(load_uniform(p.comp_lens + r0 + idx), p.spans);
                 return Task{r0 + idx, keyed_r + (local - excl) * kPadSpans, false, true};
             }
             before += chunk_total;
@@ -125,137 +143,40 @@ __device__ Task map_task(const DecodeParams &p, int task, int lane) {
     return Task{0, 0, false, false};
 }
 
-template <int MT, int PAGE_MODE, int FMT>
-__global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParams p) {
+template <int MT, int PAGE_MODE, int FMT, int SRC>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 4 : 2))) void decode_kernel(DecodeParams p) {
     constexpr bool kQF16 = FMT == kFp16 || FMT == kFp16Fp8;
     constexpr bool kKFp8 = FMT == kBf16Fp8 || FMT == kFp16Fp8;
+    constexpr bool kUniform = PAGE_MODE != kPageGeneric;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int task_id = blockIdx.x * kWavesPerBlock + wave;
-    const Task task = map_task(p, task_id, lane);
-    if (!task.valid) return;
-    const int r = __builtin_amdgcn_readfirstlane(task.r);
-    const int span = __builtin_amdgcn_readfirstlane(task.span);
+    const int task_id = blockIdx.x;
+
+    int r, span, comp, page = -1;
+    bool compute;
+    if (SRC == kPlanned) {
+        // The entry is wave-uniform: one scalar load.  Any contents are safe:
+        // requests, spans and pages outside the launch's ranges are refused.
+        const i32x4 e = load_uniform(reinterpret_cast<const i32x4 *>(p.plan) + task_id);
+        r = e[0];
+        if (r < 0 || r >= p.num_reqs) return;
+        span = e[1] & 0x7fffffff;
+        if (span >= p.spans) return;
+        compute = e[1] >= 0;
+        page = e[2];
+        comp = e[3] > 0 ? e[3] : 0;
+    } else {
+        const Task task = map_task(p, task_id, lane);
+        if (!task.valid) return;
+        r = __builtin_amdgcn_readfirstlane(task.r);
+        span = __builtin_amdgcn_readfirstlane(task.span);
+        compute = task.compute;
+        comp = 0;
+    }
     const int n = lane & 15;
     const int q4 = lane >> 4;
     const int c0 = span * kSpan;
 
-    float res[MT][4];
-    if (task.compute) {
-        // Request-level reads are scalar loads, so the page-table read that
-        // gates the key loads never waits behind the query loads.
-        const int comp = load_uniform(p.comp_lens + r);
-        const int64_t pt_row = (int64_t)r * p.page_table_stride;
-        // Per-row visible counts (lane row j = 4*mt + q4), read as scalars.
-        int vis_row[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            int v4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 4 * mt + i;
-                int v = 0;
-                if (j < p.dql) v = p.visible ? load_uniform(p.visible + (int64_t)r * p.dql + j) : comp;
-                v4[i] = v < 0 ? 0 : (v > comp ? comp : v);
-            }
-            vis_row[mt] = q4 == 0 ? v4[0] : (q4 == 1 ? v4[1] : (q4 == 2 ? v4[2] : v4[3]));
-        }
-
-        // Query fragments (issued first: they hit in L2): tile mt holds rows
-        // j = 4*mt .. 4*mt+3.
-        u32x4 qa[MT][4];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int j = 4 * mt + (n >> 2);
-            const int h = n & 3;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                qa[mt][ks] = j < p.dql ? load_q_fragment(p, r, j, h, kKFp8 ? 32 * q4 + 8 * ks : 32 * ks + 8 * q4)
-                                       : zero_u32x4();
-        }
-
-        // Key c0 + 4n + g, features 32ks + 8q4 .. +7, for every g and ks:
-        // all 16 loads issued before any MFMA.
-        u32x4 kb[4][4];
-        bool key_ok[4];
-        if (PAGE_MODE != kPageGeneric) {
-            // The span lies on one page; a mapped page is read whole (keys
-            // past comp are in bounds and masked below).
-            const int slot = PAGE_MODE == kPage64 ? span : c0 / p.page_size;
-            const int page = slot < p.page_table_cols ? load_uniform(p.page_table + pt_row + slot) : -1;
-            const bool page_ok = page >= 0 && page < p.num_pages;
-            if (page_ok) {
-                const int in_page = PAGE_MODE == kPage64 ? 0 : c0 % p.page_size;
-                const int64_t key0 = (int64_t)page * p.page_size + in_page + 4 * n;
-                if (kKFp8) {
-                    const uint8_t *src = reinterpret_cast<const uint8_t *>(p.k) + key0 * kDim + 32 * q4;
-                    u32x4 raw[4][2];
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        raw[g][0] = load_u32x4(src + g * kDim);
-                        raw[g][1] = load_u32x4(src + g * kDim + 16);
-                    }
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        kb[g][0] = e4m3x8_to_16bit<kQF16>(raw[g][0][0], raw[g][0][1]);
-                        kb[g][1] = e4m3x8_to_16bit<kQF16>(raw[g][0][2], raw[g][0][3]);
-                        kb[g][2] = e4m3x8_to_16bit<kQF16>(raw[g][1][0], raw[g][1][1]);
-                        kb[g][3] = e4m3x8_to_16bit<kQF16>(raw[g][1][2], raw[g][1][3]);
-                    }
-                } else {
-                    const uint16_t *src = p.k + key0 * kDim + 8 * q4;
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-#pragma unroll
-                        for (int ks = 0; ks < 4; ++ks) kb[g][ks] = load_u32x4(src + g * kDim + 32 * ks);
-                }
-            } else {
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) kb[g][ks] = zero_u32x4();
-            }
-#pragma unroll
-            for (int g = 0; g < 4; ++g) key_ok[g] = page_ok && c0 + 4 * n + g < comp;
-        } else {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c = c0 + 4 * n + g;
-                int page = -1;
-                if (c < comp) {
-                    const int slot = c / p.page_size;
-                    if (slot < p.page_table_cols) page = p.page_table[pt_row + slot];
-                }
-                key_ok[g] = page >= 0 && page < p.num_pages;
-                const int64_t key = (int64_t)page * p.page_size + (c % p.page_size);
-                if (kKFp8) {
-                    const uint8_t *src = reinterpret_cast<const uint8_t *>(p.k) + key * kDim + 32 * q4;
-                    const u32x4 lo = key_ok[g] ? load_u32x4(src) : zero_u32x4();
-                    const u32x4 hi = key_ok[g] ? load_u32x4(src + 16) : zero_u32x4();
-                    kb[g][0] = e4m3x8_to_16bit<kQF16>(lo[0], lo[1]);
-                    kb[g][1] = e4m3x8_to_16bit<kQF16>(lo[2], lo[3]);
-                    kb[g][2] = e4m3x8_to_16bit<kQF16>(hi[0], hi[1]);
-                    kb[g][3] = e4m3x8_to_16bit<kQF16>(hi[2], hi[3]);
-                } else {
-                    const uint16_t *src = p.k + key * kDim + 8 * q4;
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) kb[g][ks] = key_ok[g] ? load_u32x4(src + 32 * ks) : zero_u32x4();
-                }
-            }
-        }
-
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<kQF16>(qa[mt][ks], kb[g][ks], acc);
-                const int c = c0 + 4 * n + g;
-                res[mt][g] = (key_ok[g] && c < vis_row[mt]) ? head_sum_score(acc, p.scale) : neg_inf();
-            }
-        }
-    } else {
+    if (!compute) {
         // -inf only: spans span .. span + kPadSpans - 1 (clipped to out_cols).
         const float ni = neg_inf();
 #pragma unroll
@@ -278,6 +199,170 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
         return;
     }
 
+    // Query fragments first: tile mt holds rows j = 4*mt .. 4*mt+3.
+    u32x4 qa[MT][4];
+    const int qh = n & 3;
+    if (p.q_vec) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int j = 4 * mt + (n >> 2);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qa[mt][ks] = j < p.dql ? load_u32x4(q_fragment_ptr(p, r, j, qh, kKFp8 ? 32 * q4 + 8 * ks : 32 * ks + 8 * q4))
+                                       : zero_u32x4();
+        }
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int j = 4 * mt + (n >> 2);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qa[mt][ks] = j < p.dql ? load_q_elements(q_fragment_ptr(p, r, j, qh, kKFp8 ? 32 * q4 + 8 * ks : 32 * ks + 8 * q4))
+                                       : zero_u32x4();
+        }
+    }
+
+    // The visible count of the lane's row j = 4*mt + q4, as one vector load
+    // issued ahead of the key loads: it returns with them, so the mask adds
+    // no wait of its own.
+    int vis_raw[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int j = 4 * mt + q4;
+        vis_raw[mt] = (p.visible && j < p.dql) ? p.visible[(int64_t)r * p.dql + j] : 0x7fffffff;
+    }
+
+    // A mapped launch reads the request's length and the span's page here
+    // (scalar loads, so the page read never waits behind the query loads);
+    // a planned one has both from its entry.
+    const int64_t pt_row = (int64_t)r * p.page_table_stride;
+    if (SRC == kMapped) {
+        comp = load_uniform(p.comp_lens + r);
+        if (kUniform) {
+            const int slot = PAGE_MODE == kPage64 ? span : c0 / p.page_size;
+            page = slot < p.page_table_cols ? load_uniform(p.page_table + pt_row + slot) : -1;
+        }
+    }
+
+    // Key c0 + 4n + g, features 32ks + 8q4 .. +7 (16-bit keys) or codes
+    // 32q4 .. +31 (e4m3), for every g and ks: all loads issued before any
+    // MFMA.
+    u32x4 kb[4][4];
+    bool key_ok[4];
+    if (kUniform) {
+        // The span lies on one page; a mapped page is read whole (keys past
+        // comp are in bounds and masked below).  Load t of a pair reads key
+        // 4 (2m + t) + g: lanes 2m, 2m+1 (same q4) cover one 128-byte line.
+        const bool page_ok = page >= 0 && page < p.num_pages;
+        const bool even = (n & 1) == 0;
+        const int m2 = n & ~1;
+        if (page_ok) {
+            const int ps = PAGE_MODE == kPage64 ? kSpan : p.page_size;
+            const int in_page = PAGE_MODE == kPage64 ? 0 : c0 % ps;
+            const uint8_t *base =
+                reinterpret_cast<const uint8_t *>(p.k) + ((int64_t)page * ps + in_page) * (kKFp8 ? kDim : 2 * kDim);
+            if (kKFp8) {
+                // Row of 128 codes = one line; lane (q4, 2m + par) reads its
+                // 16-byte piece 2 q4 + par, so each lane ends with pieces
+                // 2 q4 and 2 q4 + 1 (codes 32 q4 .. +31) of its own key.
+                const uint8_t *src = base + 16 * (2 * q4 + (n & 1));
+                u32x4 raw[4][2];
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) raw[g][t] = load_u32x4_stream(src + (4 * (m2 + t) + g) * kDim);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x4 lo, hi;
+                    lane_pair_exchange(even, raw[g][0], raw[g][1], lo, hi);
+                    kb[g][0] = e4m3x8_to_16bit<kQF16>(lo[0], lo[1]);
+                    kb[g][1] = e4m3x8_to_16bit<kQF16>(lo[2], lo[3]);
+                    kb[g][2] = e4m3x8_to_16bit<kQF16>(hi[0], hi[1]);
+                    kb[g][3] = e4m3x8_to_16bit<kQF16>(hi[2], hi[3]);
+                }
+            } else {
+                // Row of 256 bytes = two lines; in line hl lane (q4, 2m + par)
+                // reads piece 4 par + q4, so each lane ends with features
+                // 64 hl + 8 q4 and 64 hl + 32 + 8 q4 (k-steps 2 hl, 2 hl + 1).
+                const uint8_t *src = base + 16 * (4 * (n & 1) + q4);
+                u32x4 raw[4][2][2];
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                        for (int t = 0; t < 2; ++t)
+                            raw[g][hl][t] = load_u32x4_stream(src + (4 * (m2 + t) + g) * (2 * kDim) + 128 * hl);
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl)
+                        lane_pair_exchange(even, raw[g][hl][0], raw[g][hl][1], kb[g][2 * hl], kb[g][2 * hl + 1]);
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) kb[g][ks] = zero_u32x4();
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) key_ok[g] = page_ok && c0 + 4 * n + g < comp;
+    } else {
+        // Any page size: one page lookup per key; loads with the default
+        // policy (a lane reads half of a line).
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int c = c0 + 4 * n + g;
+            int pg = -1;
+            if (c < comp) {
+                const int slot = c / p.page_size;
+                if (slot < p.page_table_cols) pg = p.page_table[pt_row + slot];
+            }
+            key_ok[g] = pg >= 0 && pg < p.num_pages;
+            const int64_t key = (int64_t)pg * p.page_size + (c % p.page_size);
+            if (kKFp8) {
+                const uint8_t *src = reinterpret_cast<const uint8_t *>(p.k) + key * kDim + 32 * q4;
+                const u32x4 lo = key_ok[g] ? load_u32x4(src) : zero_u32x4();
+                const u32x4 hi = key_ok[g] ? load_u32x4(src + 16) : zero_u32x4();
+                kb[g][0] = e4m3x8_to_16bit<kQF16>(lo[0], lo[1]);
+                kb[g][1] = e4m3x8_to_16bit<kQF16>(lo[2], lo[3]);
+                kb[g][2] = e4m3x8_to_16bit<kQF16>(hi[0], hi[1]);
+                kb[g][3] = e4m3x8_to_16bit<kQF16>(hi[2], hi[3]);
+            } else {
+                const uint16_t *src = p.k + key * kDim + 8 * q4;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) kb[g][ks] = key_ok[g] ? load_u32x4(src + 32 * ks) : zero_u32x4();
+            }
+        }
+    }
+
+    // Visible counts of the lane's rows, clamped to [0, comp].
+    int vis_row[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int v = vis_raw[mt];
+        vis_row[mt] = v < 0 ? 0 : (v > comp ? comp : v);
+    }
+
+    // Four independent accumulator chains (one per key group), interleaved
+    // k-step by k-step, so the matrix core never waits on its own result.
+    float res[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) acc[g] = mfma_qk<kQF16>(qa[mt][ks], kb[g][ks], acc[g]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int c = c0 + 4 * n + g;
+            res[mt][g] = (key_ok[g] && c < vis_row[mt]) ? head_sum_score(acc[g], p.scale) : neg_inf();
+        }
+    }
+
     // Lane (n, q4) owns row j = 4*mt + q4, keys c0 + 4n .. c0 + 4n + 3.
     const int col = c0 + 4 * n;
 #pragma unroll
@@ -295,22 +380,119 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void decode_kernel(DecodeParam
     }
 }
 
-template <int MT, int FMT>
-hipError_t launch_fmt(const DecodeParams &p, hipStream_t stream, dim3 grid, dim3 block) {
-    if (p.page_size == kSpan) return launch_kernel(decode_kernel<MT, kPage64, FMT>, grid, block, stream, p);
-    if (p.page_size % kSpan == 0)
-        return launch_kernel(decode_kernel<MT, kPageMultiple64, FMT>, grid, block, stream, p);
-    return launch_kernel(decode_kernel<MT, kPageGeneric, FMT>, grid, block, stream, p);
+// Task table of a planned launch (qsa_build_decode_plan): entry e of
+// num_reqs * spans.  Every workgroup scans the per-request task counts into
+// LDS (keyed spans, then -inf groups), so workgroups need no grid-wide
+// ordering, then fills its entries by binary search over the offsets.
+constexpr int kPlanThreads = 256;
+
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(PlanParams p) {
+    __shared__ int32_t keyed_off[kPlanMaxReqs + 1];
+    __shared__ int32_t pad_off[kPlanMaxReqs + 1];
+    __shared__ int32_t wave_sum[2][kPlanThreads / 64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    // Thread tid counts requests [tid*per, (tid+1)*per).
+    const int per = (p.num_reqs + kPlanThreads - 1) / kPlanThreads;
+    const int r0 = tid * per;
+    int my_keyed = 0, my_pad = 0;
+    for (int r = r0; r < r0 + per && r < p.num_reqs; ++r) {
+        const int keyed = keyed_spans(p.comp_lens[r], p.spans);
+        const int pad = (p.spans - keyed + kPadSpans - 1) / kPadSpans;
+        keyed_off[r] = keyed;  // counts for now; offsets below
+        pad_off[r] = pad;
+        my_keyed += keyed;
+        my_pad += pad;
+    }
+    const int ik = wave_inclusive_sum(my_keyed, lane);
+    const int ip = wave_inclusive_sum(my_pad, lane);
+    if (lane == 63) {
+        wave_sum[0][wave] = ik;
+        wave_sum[1][wave] = ip;
+    }
+    __syncthreads();
+    int bk = 0, bp = 0;
+    for (int w = 0; w < wave; ++w) {
+        bk += wave_sum[0][w];
+        bp += wave_sum[1][w];
+    }
+    int run_k = bk + ik - my_keyed, run_p = bp + ip - my_pad;
+    for (int r = r0; r < r0 + per && r < p.num_reqs; ++r) {
+        const int ck = keyed_off[r], cp = pad_off[r];
+        keyed_off[r] = run_k;
+        pad_off[r] = run_p;
+        run_k += ck;
+        run_p += cp;
+    }
+    if (tid == kPlanThreads - 1) {
+        keyed_off[p.num_reqs] = run_k;  // all keyed tasks
+        pad_off[p.num_reqs] = run_p;    // all -inf tasks
+    }
+    __syncthreads();
+    const int64_t total_keyed = keyed_off[p.num_reqs];
+    const int64_t total = total_keyed + pad_off[p.num_reqs];
+    const bool uniform = p.page_size % kSpan == 0;
+    i32x4 *plan = reinterpret_cast<i32x4 *>(p.plan);
+    for (int64_t e = (int64_t)blockIdx.x * kPlanThreads + tid; e < p.entries; e += (int64_t)gridDim.x * kPlanThreads) {
+        i32x4 v = {-1, 0, -1, 0};
+        if (e < total) {
+            const bool keyed = e < total_keyed;
+            const int32_t *off = keyed ? keyed_off : pad_off;
+            const int64_t local = keyed ? e : e - total_keyed;
+            // Last request whose first task is <= local (requests without
+            // tasks share the next one's offset).
+            int lo = 0, hi = p.num_reqs - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= local) lo = mid;
+                else hi = mid - 1;
+            }
+            const int r = lo;
+            const int comp = p.comp_lens[r];
+            if (keyed) {
+                const int span = (int)(local - off[r]);
+                int page = -1;
+                if (uniform) {
+                    const int slot = span * kSpan / p.page_size;
+                    if (slot < p.page_table_cols) page = p.page_table[(int64_t)r * p.page_table_stride + slot];
+                    if (page < 0 || page >= p.num_pages) page = -1;
+                }
+                v = i32x4{r, span, page, comp};
+            } else {
+                const int span = keyed_spans(comp, p.spans) + (int)(local - off[r]) * kPadSpans;
+                v = i32x4{r, (int32_t)((uint32_t)span | 0x80000000u), -1, comp};
+            }
+        }
+        plan[e] = v;
+    }
 }
 
-template <int MT>
+template <int MT, int FMT, int SRC>
+hipError_t launch_fmt(const DecodeParams &p, hipStream_t stream, dim3 grid, dim3 block) {
+    if (p.page_size == kSpan) return launch_kernel(decode_kernel<MT, kPage64, FMT, SRC>, grid, block, stream, p);
+    if (p.page_size % kSpan == 0)
+        return launch_kernel(decode_kernel<MT, kPageMultiple64, FMT, SRC>, grid, block, stream, p);
+    return launch_kernel(decode_kernel<MT, kPageGeneric, FMT, SRC>, grid, block, stream, p);
+}
+
+template <int MT, int SRC>
 hipError_t launch_mt(const DecodeParams &p, hipStream_t stream, dim3 grid, dim3 block) {
     if (p.k_fp8) {
-        if (p.q_f16) return launch_fmt<MT, kFp16Fp8>(p, stream, grid, block);
-        return launch_fmt<MT, kBf16Fp8>(p, stream, grid, block);
+        if (p.q_f16) return launch_fmt<MT, kFp16Fp8, SRC>(p, stream, grid, block);
+        return launch_fmt<MT, kBf16Fp8, SRC>(p, stream, grid, block);
     }
-    if (p.q_f16) return launch_fmt<MT, kFp16>(p, stream, grid, block);
-    return launch_fmt<MT, kBf16>(p, stream, grid, block);
+    if (p.q_f16) return launch_fmt<MT, kFp16, SRC>(p, stream, grid, block);
+    return launch_fmt<MT, kBf16, SRC>(p, stream, grid, block);
+}
+
+template <int SRC>
+hipError_t launch_src(const DecodeParams &p, hipStream_t stream, dim3 grid, dim3 block) {
+    switch ((p.dql + 3) / 4) {
+        case 1: return launch_mt<1, SRC>(p, stream, grid, block);
+        case 2: return launch_mt<2, SRC>(p, stream, grid, block);
+        case 3: return launch_mt<3, SRC>(p, stream, grid, block);
+        default: return launch_mt<4, SRC>(p, stream, grid, block);
+    }
 }
 
 }  // namespace
@@ -319,14 +501,16 @@ int decode_span_keys() { return kSpan; }
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
     const int64_t tasks = (int64_t)p.num_reqs * p.spans;
-    const dim3 grid((unsigned)((tasks + kWavesPerBlock - 1) / kWavesPerBlock));
-    const dim3 block(kWavesPerBlock * 64);
-    switch ((p.dql + 3) / 4) {
-        case 1: return launch_mt<1>(p, stream, grid, block);
-        case 2: return launch_mt<2>(p, stream, grid, block);
-        case 3: return launch_mt<3>(p, stream, grid, block);
-        default: return launch_mt<4>(p, stream, grid, block);
-    }
+    const dim3 grid((unsigned)tasks);
+    const dim3 block(64);
+    if (p.plan) return launch_src<kPlanned>(p, stream, grid, block);
+    return launch_src<kMapped>(p, stream, grid, block);
+}
+
+hipError_t launch_decode_plan(const PlanParams &p, hipStream_t stream) {
+    const int64_t blocks = (p.entries + kPlanThreads - 1) / kPlanThreads;
+    const dim3 grid((unsigned)(blocks < 512 ? blocks : 512));
+    return launch_kernel(decode_plan_kernel, grid, dim3(kPlanThreads), stream, p);
 }
 
 }  // namespace qsa

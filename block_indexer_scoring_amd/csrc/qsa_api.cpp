@@ -362,13 +362,15 @@ static int check_formats(const char *fn, int32_t q_dtype, int32_t k_dtype, float
     return QSA_OK;
 }
 
+// plan: null for the mapped launch (tasks from comp_lens), else a task table
+// of plan_bytes bytes from qsa_build_decode_plan (comp_lens unused).
 static int decode_impl(const char *fn, const void *q, int32_t q_dtype, int64_t q_stride_req,
                        int64_t q_stride_row, int64_t q_stride_head, const void *k_cache, int32_t k_dtype,
                        float k_scale, int64_t num_pages, int32_t page_size, const int32_t *page_table,
                        int64_t page_table_stride, int32_t page_table_cols, const int32_t *comp_lens,
                        const int32_t *visible, int32_t num_reqs, int32_t dql, int32_t num_heads,
                        int32_t head_dim, float scale, float *out, int64_t out_stride, int32_t out_cols,
-                       void *stream) {
+                       void *stream, const void *plan = nullptr, int64_t plan_bytes = 0) {
     int rc;
     if ((rc = check_heads(fn, num_heads, head_dim))) return rc;
     if ((rc = check_scale(fn, scale))) return rc;
@@ -390,7 +392,8 @@ static int decode_impl(const char *fn, const void *q, int32_t q_dtype, int64_t q
     if (num_pages > ((int64_t)1 << 46) / page_size)
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: key cache too large", fn);
     if (num_reqs == 0 || out_cols == 0) return ok();
-    if (!q || !comp_lens || !out) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL q, comp_lens or out", fn);
+    if (!q || !out || (!plan && !comp_lens))
+        return fail(QSA_ERR_INVALID_ARGUMENT, plan ? "%s: NULL q or out" : "%s: NULL q, comp_lens or out", fn);
     if (num_pages > 0 && !k_cache) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL k_cache", fn);
     if (page_table_cols > 0 && !page_table) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL page_table", fn);
     if (num_pages > 0 && !aligned(k_cache, 16))
@@ -401,6 +404,13 @@ static int decode_impl(const char *fn, const void *q, int32_t q_dtype, int64_t q
     const int64_t spans = ((int64_t)out_cols + span_keys - 1) / span_keys;
     if ((int64_t)num_reqs * dql > INT32_MAX || (int64_t)num_reqs * spans >= INT32_MAX)
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
+    const int64_t plan_need = (int64_t)num_reqs * spans * 16;
+    if (plan) {
+        if (!aligned(plan, 16)) return fail(QSA_ERR_LAYOUT, "%s: plan must be 16-byte aligned", fn);
+        if (plan_bytes < plan_need)
+            return fail(QSA_ERR_INVALID_ARGUMENT, "%s: plan of %lld bytes, %lld needed for %d requests x %d columns",
+                        fn, (long long)plan_bytes, (long long)plan_need, num_reqs, out_cols);
+    }
 
     qsa::DecodeParams p{};
     p.q = static_cast<const uint16_t *>(q);
@@ -426,7 +436,71 @@ static int decode_impl(const char *fn, const void *q, int32_t q_dtype, int64_t q
     p.out_vec = aligned(out, 16) && out_stride % 4 == 0;
     p.q_f16 = q_dtype == QSA_DTYPE_FP16;
     p.k_fp8 = k_fp8;
+    p.plan = static_cast<const int32_t *>(plan);
+    p.plan_entries = plan ? (int64_t)num_reqs * spans : 0;
     return device_status(fn, qsa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_decode_plan_bytes(int32_t num_reqs, int32_t out_cols, int64_t *bytes) {
+    const char *fn = "qsa_decode_plan_bytes";
+    if (!bytes) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL bytes", fn);
+    if (num_reqs < 0 || out_cols < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+    const int64_t span_keys = qsa::decode_span_keys();
+    *bytes = (int64_t)num_reqs * (((int64_t)out_cols + span_keys - 1) / span_keys) * 16;
+    return ok();
+}
+
+int qsa_build_decode_plan(const int32_t *comp_lens, const int32_t *page_table, int64_t page_table_stride,
+                          int32_t page_table_cols, int64_t num_pages, int32_t page_size, int32_t num_reqs,
+                          int32_t out_cols, void *plan, int64_t plan_bytes, void *stream) {
+    const char *fn = "qsa_build_decode_plan";
+    if (num_reqs < 0 || out_cols < 0 || num_pages < 0 || page_table_cols < 0)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+    if (page_size < 1 || page_size > (1 << 20))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: page_size must be in [1, 2^20], got %d", fn, page_size);
+    if (num_reqs > 1 && page_table_stride < page_table_cols)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: page_table_stride < page_table_cols", fn);
+    if (num_reqs > qsa::kPlanMaxReqs)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: plans for more than %d requests", fn, qsa::kPlanMaxReqs);
+    const int64_t span_keys = qsa::decode_span_keys();
+    const int64_t spans = ((int64_t)out_cols + span_keys - 1) / span_keys;
+    if ((int64_t)num_reqs * spans >= INT32_MAX)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
+    const int64_t need = (int64_t)num_reqs * spans * 16;
+    if (need == 0) return ok();
+    if (!comp_lens || !plan) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL comp_lens or plan", fn);
+    if (page_table_cols > 0 && !page_table) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL page_table", fn);
+    if (!aligned(plan, 16)) return fail(QSA_ERR_LAYOUT, "%s: plan must be 16-byte aligned", fn);
+    if (plan_bytes < need)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: plan of %lld bytes, %lld needed", fn, (long long)plan_bytes,
+                    (long long)need);
+    qsa::PlanParams p{};
+    p.comp_lens = comp_lens;
+    p.page_table = page_table;
+    p.page_table_stride = page_table_stride;
+    p.page_table_cols = page_table ? page_table_cols : 0;
+    p.num_pages = num_pages;
+    p.page_size = page_size;
+    p.num_reqs = num_reqs;
+    p.spans = (int32_t)spans;
+    p.plan = static_cast<int32_t *>(plan);
+    p.entries = (int64_t)num_reqs * spans;
+    return device_status(fn, qsa::launch_decode_plan(p, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_mqa_decode_planned(const void *plan, int64_t plan_bytes, const void *q, int32_t q_dtype,
+                           int64_t q_stride_req, int64_t q_stride_row, int64_t q_stride_head, const void *k_cache,
+                           int32_t k_dtype, float k_scale, int64_t num_pages, int32_t page_size,
+                           const int32_t *page_table, int64_t page_table_stride, int32_t page_table_cols,
+                           const int32_t *visible, int32_t num_reqs, int32_t dql, int32_t num_heads,
+                           int32_t head_dim, float scale, float *out, int64_t out_stride, int32_t out_cols,
+                           void *stream) {
+    const char *fn = "qsa_mqa_decode_planned";
+    if (!plan && num_reqs > 0 && out_cols > 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL plan", fn);
+    return decode_impl(fn, q, q_dtype, q_stride_req, q_stride_row, q_stride_head, k_cache, k_dtype, k_scale,
+                       num_pages, page_size, page_table, page_table_stride, page_table_cols, nullptr, visible,
+                       num_reqs, dql, num_heads, head_dim, scale, out, out_stride, out_cols, stream, plan,
+                       plan_bytes);
 }
 
 int qsa_mqa_decode(const void *q, int64_t q_stride_req, int64_t q_stride_row, int64_t q_stride_head,

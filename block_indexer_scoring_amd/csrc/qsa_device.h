@@ -38,6 +38,36 @@ __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f
 
 __device__ __forceinline__ u32x4 zero_u32x4() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// 16-byte load with the non-temporal (streaming) policy, for data read once.
+// Only for loads whose instruction covers whole 128-byte lines: a line that
+// two instructions read half each is fetched from HBM twice under this
+// policy.
+__device__ __forceinline__ u32x4 load_u32x4_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// Exchange between lane pairs (2m, 2m+1).  Whole-line loads give each pair
+// two registers: r0 holds pieces of the even lane's item (its own piece in
+// the even lane, the even lane's next piece in the odd lane), r1 the same
+// for the odd lane's item.  Afterwards each lane holds its own two pieces:
+// lo (from the even lane's register) and hi (from the odd lane's).  The
+// partner's value is read with a DPP quad permutation [1, 0, 3, 2].
+__device__ __forceinline__ u32x4 lane_pair_swap(u32x4 v) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)v[i], 0xB1, 0xF, 0xF, true);
+    return r;
+}
+
+__device__ __forceinline__ void lane_pair_exchange(bool even, u32x4 r0, u32x4 r1, u32x4 &lo, u32x4 &hi) {
+    const u32x4 s0 = lane_pair_swap(r0), s1 = lane_pair_swap(r1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo[i] = even ? r0[i] : s1[i];
+        hi[i] = even ? s0[i] : r1[i];
+    }
+}
+
 // ReLU as a signed-integer max on the bit pattern: positive floats order
 // like their bits, every non-positive float (-0 included) has the sign bit
 // set and maps to the bits of +0.0.  One VALU op, and an all-negative head

@@ -33,7 +33,28 @@ struct DecodeParams {
     int32_t out_vec;            // out rows may be written with 16-byte stores
     int32_t q_f16;              // Q (and 16-bit keys) are fp16, not bf16
     int32_t k_fp8;              // keys are e4m3 codes (scale already holds the cache scale)
+    const int32_t *plan;        // [plan_entries][4] task table (planned launches), else null
+    int64_t plan_entries;       // num_reqs * spans for planned launches
 };
+
+// Decode task table (qsa_build_decode_plan): one 16-byte entry per wave of
+// a planned decode launch, num_reqs * spans entries.  Entry {r, span, page,
+// comp}: request r, first span (bit 31 set: a -inf-only task of up to
+// decode_pad_spans() spans), the physical page holding the span (page sizes
+// that are multiples of the span; -1 when unmapped or not page-uniform),
+// and r's compressed length.  Unused entries have r = -1.
+struct PlanParams {
+    const int32_t *comp_lens;
+    const int32_t *page_table;
+    int64_t page_table_stride;
+    int32_t page_table_cols;
+    int64_t num_pages;
+    int32_t page_size;
+    int32_t num_reqs, spans;
+    int32_t *plan;
+    int64_t entries;            // num_reqs * spans
+};
+constexpr int kPlanMaxReqs = 4096;  // requests one planning workgroup scans in LDS
 
 struct PrefillParams {
     const uint16_t *q;
@@ -162,7 +183,8 @@ hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t s
                               ev.start, ev.stop, 0);
 }
 
-hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);  // p.plan selects the planned kernel
+hipError_t launch_decode_plan(const PlanParams &p, hipStream_t stream);
 int decode_span_keys();
 int prefill_col_chunk(int64_t num_rows, int32_t out_cols, int64_t k_stride, int num_cus);
 int64_t prefill_max_k_stride();  // larger key strides overflow the kernel's 32-bit key offsets

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 6
+#define QSA_ABI_VERSION 7
 
 enum qsa_status {
     QSA_OK = 0,
@@ -308,6 +308,70 @@ int qsa_mqa_decode_typed(const void *q, int32_t q_dtype, int64_t q_stride_req,
                          const int32_t *visible, int32_t num_reqs, int32_t dql,
                          int32_t num_heads, int32_t head_dim, float scale, float *out,
                          int64_t out_stride, int32_t out_cols, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Planned decode: a task table built once per step, read by every decode
+ * launch of that step (one per layer that runs the indexer).
+ *   Source: as qsa_mqa_decode.  The vLLM metadata builder (qsa_cache.py,
+ *   QSAMetadataBuilder.build and _build_qsa_metadata_kernel) likewise builds
+ *   the step's indexer metadata once, from the compressed lengths and block
+ *   tables, for all layers.  The scores are those of qsa_mqa_decode, bit for
+ *   bit; the table only tells each wavefront its (request, 64-key span), the
+ *   span's physical page and the request's compressed length, so that a
+ *   wavefront starts its key loads after one table read.
+ *
+ * qsa_decode_plan_bytes -- size of the task table for num_reqs requests and
+ *   out_cols output columns: num_reqs * ceil(out_cols / 64) entries of 16
+ *   bytes.  bytes: host int64 out.  Errors: INVALID_ARGUMENT for a NULL
+ *   bytes or negative sizes.
+ *
+ * qsa_build_decode_plan -- fill the task table (one kernel on `stream`).
+ *   comp_lens, page_table, page_table_stride, page_table_cols, num_pages,
+ *   page_size, num_reqs, out_cols: as qsa_mqa_decode.
+ *   plan       : device buffer of plan_bytes >= qsa_decode_plan_bytes(...)
+ *                bytes, 16-byte aligned, caller-owned.  Entry {r, span,
+ *                page, comp}: the spans holding keys, request by request,
+ *                then the spans past each request's keys in groups of 4
+ *                (span | 1<<31), then unused entries (r = -1).  page is the
+ *                span's physical page when page_size is a multiple of 64,
+ *                else -1 (the decode then reads the page table per key).
+ *   The table depends on comp_lens and the page table: build it again when
+ *   either changes (normally once per step).
+ *   Errors: INVALID_ARGUMENT for negative sizes, page_size outside
+ *   [1, 1<<20], a short page_table_stride, a NULL pointer that has work to
+ *   feed or a short plan; LAYOUT for a misaligned plan; UNSUPPORTED for more
+ *   than 4,096 requests.
+ *
+ * qsa_mqa_decode_planned -- qsa_mqa_decode_typed driven by a task table.
+ *   plan, plan_bytes : a table from qsa_build_decode_plan for the same
+ *                num_reqs, out_cols, page_size, page table and compressed
+ *                lengths (a table for other arguments gives wrong scores but
+ *                never reads or writes outside the given buffers: entries
+ *                out of range are ignored, pages out of range read as
+ *                missing).
+ *   q, q_dtype, strides, k_cache, k_dtype, k_scale, num_pages, page_size,
+ *   page_table (used per key when page_size is not a multiple of 64; may be
+ *   NULL otherwise), visible, num_reqs, dql, num_heads, head_dim, scale,
+ *   out, out_stride, out_cols: as qsa_mqa_decode_typed.  The compressed
+ *   lengths come from the table.
+ *   Errors: as qsa_mqa_decode_typed, plus INVALID_ARGUMENT for a NULL plan
+ *   or plan_bytes below the table's size, and LAYOUT for a misaligned plan.
+ */
+int qsa_decode_plan_bytes(int32_t num_reqs, int32_t out_cols, int64_t *bytes);
+
+int qsa_build_decode_plan(const int32_t *comp_lens, const int32_t *page_table,
+                          int64_t page_table_stride, int32_t page_table_cols, int64_t num_pages,
+                          int32_t page_size, int32_t num_reqs, int32_t out_cols, void *plan,
+                          int64_t plan_bytes, void *stream);
+
+int qsa_mqa_decode_planned(const void *plan, int64_t plan_bytes, const void *q, int32_t q_dtype,
+                           int64_t q_stride_req, int64_t q_stride_row, int64_t q_stride_head,
+                           const void *k_cache, int32_t k_dtype, float k_scale, int64_t num_pages,
+                           int32_t page_size, const int32_t *page_table,
+                           int64_t page_table_stride, int32_t page_table_cols,
+                           const int32_t *visible, int32_t num_reqs, int32_t dql,
+                           int32_t num_heads, int32_t head_dim, float scale, float *out,
+                           int64_t out_stride, int32_t out_cols, void *stream);
 
 /* ------------------------------------------------------------------------
  * qsa_mqa_prefill_typed -- qsa_mqa_prefill with BF16 or FP16 queries and

@@ -44,7 +44,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.qsa_abi_version() == 6
+    from block_indexer_scoring_amd import qsa
+    m = re.search(r"#define QSA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.qsa_abi_version() == int(m.group(1)) == qsa.ABI_VERSION
 
 
 def test_launch_events_set_and_clear_without_device(lib):
