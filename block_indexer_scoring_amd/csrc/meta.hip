@@ -166,6 +166,22 @@ __global__ __launch_bounds__(kThreads) void k_work_kernel(CacheMetaParams p) {
     p.k_work[2 * w + 1] = index;
 }
 
+// Compressed lengths and visible blocks of a uniform decode batch: thread
+// per row r*dql + j at position seq_len - dql + j (the last dql tokens of
+// the context), 4 tokens per compressed block.
+__global__ __launch_bounds__(kThreads) void decode_visible_kernel(DecodeVisibleParams p) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (p.comp_lens && i < p.num_reqs) p.comp_lens[i] = (int32_t)floor_div(p.seq_lens[i], 4);
+    if (!p.visible || i >= (int64_t)p.num_reqs * p.dql) return;
+    const int r = (int)(i / p.dql), j = (int)(i % p.dql);
+    const int64_t seq = p.seq_lens[r];
+    const int64_t pos = seq - p.dql + j;
+    int64_t v = floor_div(pos + 1, 4);
+    const int64_t by_len = floor_div(seq, 4);
+    v = v < by_len ? v : by_len;
+    p.visible[i] = (int32_t)(v < 0 ? 0 : v);
+}
+
 }  // namespace
 
 hipError_t launch_cache_slots(const CacheMetaParams &p, hipStream_t stream) {
@@ -176,6 +192,13 @@ hipError_t launch_cache_slots(const CacheMetaParams &p, hipStream_t stream) {
 hipError_t launch_k_work(const CacheMetaParams &p, hipStream_t stream) {
     return launch_kernel(k_work_kernel, dim3((unsigned)((p.max_num_work + kThreads - 1) / kThreads)),
                          dim3(kThreads), stream, p);
+}
+
+hipError_t launch_decode_visible(const DecodeVisibleParams &p, hipStream_t stream) {
+    const int64_t rows = (int64_t)p.num_reqs * p.dql;
+    const int64_t n = rows > p.num_reqs ? rows : p.num_reqs;
+    return launch_kernel(decode_visible_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads),
+                         stream, p);
 }
 
 hipError_t launch_metadata(const MetaParams &p, hipStream_t stream) {

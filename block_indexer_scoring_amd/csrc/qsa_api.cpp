@@ -177,6 +177,19 @@ int qsa_build_metadata(const int32_t *query_start_loc, const int32_t *seq_lens, 
     return device_status(fn, qsa::launch_metadata(p, static_cast<hipStream_t>(stream)));
 }
 
+int qsa_decode_visible_blocks(const int32_t *seq_lens, int32_t num_reqs, int32_t dql, int32_t *comp_lens_out,
+                              int32_t *visible_out, void *stream) {
+    const char *fn = "qsa_decode_visible_blocks";
+    if (num_reqs < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: num_reqs < 0", fn);
+    if (dql < 1 || dql > 16) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: dql must be in [1, 16], got %d", fn, dql);
+    if (num_reqs == 0 || (!comp_lens_out && !visible_out)) return ok();
+    if (!seq_lens) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL seq_lens", fn);
+    if ((int64_t)num_reqs * dql >= INT32_MAX)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
+    qsa::DecodeVisibleParams p{seq_lens, num_reqs, dql, comp_lens_out, visible_out};
+    return device_status(fn, qsa::launch_decode_visible(p, static_cast<hipStream_t>(stream)));
+}
+
 int qsa_build_cache_metadata(const int32_t *query_start_loc, const int32_t *seq_lens, int32_t num_reqs,
                              int32_t num_tokens, int32_t compress_ratio, const int32_t *block_table,
                              int64_t block_table_stride, int32_t block_table_cols, int32_t storage_block_size,

@@ -121,6 +121,12 @@ struct MetaParams {
     int32_t *visible, *comp_lens, *row_k_start, *row_k_end;
 };
 
+struct DecodeVisibleParams {
+    const int32_t *seq_lens;
+    int32_t num_reqs, dql;
+    int32_t *comp_lens, *visible;  // either may be null
+};
+
 struct CacheMetaParams {
     const int32_t *query_start_loc, *seq_lens;
     int32_t num_reqs, num_tokens, compress_ratio;
@@ -196,6 +202,7 @@ hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus);
 hipError_t launch_topk_floor(const FusedTopkParams &p, hipStream_t stream);
 hipError_t launch_topk_candidates(const FusedTopkParams &p, hipStream_t stream);
 hipError_t launch_metadata(const MetaParams &p, hipStream_t stream);
+hipError_t launch_decode_visible(const DecodeVisibleParams &p, hipStream_t stream);
 hipError_t launch_cache_slots(const CacheMetaParams &p, hipStream_t stream);  // p.slot_mapping set
 hipError_t launch_k_work(const CacheMetaParams &p, hipStream_t stream);       // p.k_work set
 hipError_t launch_gather_keys(const GatherParams &p, hipStream_t stream);

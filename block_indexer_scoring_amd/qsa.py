@@ -21,13 +21,14 @@ QSA_ERR_INVALID_ARGUMENT = 1
 QSA_ERR_UNSUPPORTED = 2
 QSA_ERR_LAYOUT = 3
 QSA_ERR_DEVICE = 4
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_set_launch_events", "qsa_split_batch",
            "qsa_build_metadata", "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks",
            "qsa_mqa_prefill_topk", "qsa_prefill_topk_workspace_bytes", "qsa_mqa_decode_typed",
            "qsa_mqa_prefill_typed", "qsa_build_cache_metadata", "qsa_gather_keys", "qsa_prepare_q",
-           "qsa_decode_plan_bytes", "qsa_build_decode_plan", "qsa_mqa_decode_planned")
+           "qsa_decode_plan_bytes", "qsa_build_decode_plan", "qsa_mqa_decode_planned",
+           "qsa_decode_visible_blocks")
 
 # enum qsa_dtype
 QSA_DTYPE_BF16 = 0
@@ -95,6 +96,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_prepare_q.argtypes = [P, i64, i32, i32, P, i64, i64, P, i32, i64, P, i32, f32, P, P, i32, f32,
                                   i64, i64, P]
     lib.qsa_prepare_q.restype = ctypes.c_int
+    lib.qsa_decode_visible_blocks.argtypes = [P, i32, i32, P, P, P]
+    lib.qsa_decode_visible_blocks.restype = ctypes.c_int
     lib.qsa_decode_plan_bytes.argtypes = [i32, i32, P]
     lib.qsa_decode_plan_bytes.restype = ctypes.c_int
     lib.qsa_build_decode_plan.argtypes = [P, P, i64, i32, i64, i32, i32, i32, P, i64, P]
@@ -197,6 +200,20 @@ def qsa_build_metadata(query_start_loc: torch.Tensor, seq_lens: torch.Tensor, nu
         _ptr(res["visible"]), _ptr(res["comp_lens"]), _ptr(res.get("row_k_start")),
         _ptr(res.get("row_k_end")), _stream_handle(stream)))
     return res
+
+
+def qsa_decode_visible_blocks(seq_lens: torch.Tensor, dql: int, stream=None):
+    """Compressed lengths (int32 [R]) and visible blocks per decode row
+    (int32 [R*dql]) of a batch of uniform decodes, on the GPU."""
+    lib = load_library()
+    _gpu("seq_lens", seq_lens, torch.int32)
+    assert seq_lens.is_contiguous()
+    num_reqs = seq_lens.numel()
+    comp = torch.empty(num_reqs, dtype=torch.int32, device=seq_lens.device)
+    vis = torch.empty(num_reqs * int(dql), dtype=torch.int32, device=seq_lens.device)
+    _check(lib.qsa_decode_visible_blocks(_ptr(seq_lens), num_reqs, int(dql), _ptr(comp), _ptr(vis),
+                                         _stream_handle(stream)))
+    return comp, vis
 
 
 def qsa_mqa_decode(q: torch.Tensor, k_cache: torch.Tensor, page_table: torch.Tensor,

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 7
+#define QSA_ABI_VERSION 8
 
 enum qsa_status {
     QSA_OK = 0,
@@ -77,7 +77,10 @@ const char *qsa_last_error(void);
  *   it ends, so hipEventElapsedTime(start, stop) is the kernel's own
  *   duration, without the dispatch latency that an event pair recorded on
  *   the stream around the call adds.  Each entry point below launches one
- *   kernel (none when it has nothing to compute).
+ *   kernel (none when it has nothing to compute), except
+ *   qsa_build_cache_metadata (up to two) and qsa_mqa_prefill_topk (four):
+ *   for those the start event marks the first kernel's begin and the stop
+ *   event the last kernel's end.
  *   start_event, stop_event : hipEvent_t handles created by the caller (may
  *                             be NULL); owned by the caller, who must keep
  *                             them alive until the launches complete.
@@ -136,6 +139,26 @@ int qsa_build_metadata(const int32_t *query_start_loc, const int32_t *seq_lens,
                        const int32_t *key_offsets, int32_t *token_to_req, int64_t *positions,
                        int32_t *visible, int32_t *comp_lens, int32_t *row_k_start,
                        int32_t *row_k_end, void *stream);
+
+/* qsa_decode_visible_blocks -- compressed lengths and per-row visible
+ * blocks of a uniform decode batch (device).
+ *   Source: MATE "QSA (Qwen Sparse Attention)", sections "MQA score" and
+ *   "Entrypoints" (decode scores over compressed context lengths); vLLM
+ *   qsa_cache.py (_logical_positions, _build_qsa_metadata_kernel) for the
+ *   positions and the visibility rule, with 4 tokens per compressed block.
+ *   Every request is a decode of dql query tokens, the last dql tokens of its
+ *   context: row r*dql + j sits at position pos = seq_lens[r] - dql + j and
+ *   sees max(0, min((pos+1)/4, seq_lens[r]/4)) blocks (floor division);
+ *   comp_lens[r] = seq_lens[r]/4.  The same values qsa_build_metadata gives
+ *   for query_start_loc = 0, dql, 2*dql, ... (one kernel).
+ *   seq_lens      : device int32 [num_reqs]
+ *   comp_lens_out : device int32 [num_reqs] or NULL
+ *   visible_out   : device int32 [num_reqs*dql] or NULL
+ *   Errors: INVALID_ARGUMENT for num_reqs < 0, dql outside [1, 16] or a NULL
+ *   seq_lens with requests to read.
+ */
+int qsa_decode_visible_blocks(const int32_t *seq_lens, int32_t num_reqs, int32_t dql,
+                              int32_t *comp_lens_out, int32_t *visible_out, void *stream);
 
 /* ------------------------------------------------------------------------
  * qsa_build_cache_metadata -- where each token's compressed key goes, and the
@@ -428,11 +451,11 @@ int qsa_topk_blocks(const float *logits, int64_t logits_stride, int32_t num_rows
  *                num_rows * (8 * (16 * (topk - 1) + 2 * topk) + out_cols / 4)
  *                bytes at the usual sizes, of which a call touches a few
  *                percent.
- *   The call enqueues five kernels on stream (a group-maximum pass over the
- *   scores, a top-k over the group maxima, the per-row floor, a candidate
- *   pass over the scores, the final select); with timing events armed the
- *   start event marks the first kernel's begin and the stop event the last
- *   kernel's end.
+ *   The call enqueues four kernels on stream (a group-maximum pass over the
+ *   scores, the per-row floor over the group maxima, a candidate pass over
+ *   the scores, the final select); with timing events armed the start event
+ *   marks the first kernel's begin and the stop event the last kernel's
+ *   end.
  *   Errors: as qsa_mqa_prefill (UNSUPPORTED also for k_stride > 16,384),
  *   INVALID_ARGUMENT for topk outside [1, 2048], out_stride < topk, a NULL
  *   out_idx or workspace, or a workspace below the size needed; LAYOUT for a

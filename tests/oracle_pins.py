@@ -135,6 +135,28 @@ def pin_visible_golden():
     assert list(O.comp_lens(np.array(ctxs, np.int32))) == [c // 4 for c in ctxs]
 
 
+def pin_prefill_intervals_golden():
+    """The packed batch of tests/golden/prefill_intervals.txt, worked by hand:
+    request, position, visible count and key interval of every token,
+    including an empty request, non-zero key offsets and padding tokens."""
+    rows = _read_golden("prefill_intervals.txt")
+    head = {r[0]: [int(x) for x in r[1:]] for r in rows if not r[0].lstrip("-").isdigit()}
+    body = [[int(x) for x in r] for r in rows if r[0].lstrip("-").isdigit()]
+    qsl = np.array(head["query_start_loc"], np.int32)
+    seq = np.array(head["seq_lens"], np.int32)
+    off = np.array(head["key_offsets"], np.int32)
+    T = head["num_tokens"][0]
+    req, pos, vis = O.token_metadata(qsl, seq, T)
+    ks, ke = O.prefill_intervals(req, vis, off)
+    want = np.array(body, np.int64)
+    assert list(want[:, 0]) == list(range(T))
+    assert list(req) == list(want[:, 1]), list(req)
+    assert list(pos) == list(want[:, 2]), list(pos)
+    assert list(vis) == list(want[:, 3]), list(vis)
+    assert list(ks) == list(want[:, 4]), list(ks)
+    assert list(ke) == list(want[:, 5]), list(ke)
+
+
 def pin_visible_counts_complete_blocks():
     # Independent characterisation: the number of 4-token blocks whose last
     # token is at or before pos, among the blocks complete within seq_len.

@@ -294,6 +294,90 @@ def test_prepare_q_nothing_to_do(lib):
     assert _err(lib) == ""
 
 
+def _planned(lib, plan=FAKE, plan_bytes=1 << 20, q_dtype=0, k_dtype=0, k_scale=1.0, **kw):
+    a = dict(q=FAKE, sr=512, sj=512, sh=128, k=FAKE, num_pages=4, page_size=64, pt=None,
+             pt_stride=0, pt_cols=0, vis=None, num_reqs=2, dql=4, heads=4, dim=128,
+             scale=0.088, out=FAKE, out_stride=200, out_cols=200)
+    a.update(kw)
+    return lib.qsa_mqa_decode_planned(plan, plan_bytes, a["q"], q_dtype, a["sr"], a["sj"], a["sh"], a["k"],
+                                      k_dtype, k_scale, a["num_pages"], a["page_size"], a["pt"], a["pt_stride"],
+                                      a["pt_cols"], a["vis"], a["num_reqs"], a["dql"], a["heads"], a["dim"],
+                                      a["scale"], a["out"], a["out_stride"], a["out_cols"], None)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(plan=None), 1, "NULL plan"),
+    (dict(plan_bytes=2 * 4 * 16 - 1), 1, "needed"),
+    (dict(plan=FAKE + 4), 3, "plan must be 16-byte aligned"),
+    (dict(heads=8), 2, "(4, 128)"),
+    (dict(dql=0), 1, "dql"),
+    (dict(q_dtype=2, k_dtype=2), 2, "query format"),
+    (dict(k_dtype=2, k_scale=0.0), 1, "k_scale"),
+    (dict(out=None), 1, "NULL q or out"),
+    (dict(pt_cols=3), 1, "page_table"),
+])
+def test_decode_planned_rejects(lib, kw, code, text):
+    assert _planned(lib, **kw) == code
+    assert text in _err(lib)
+    assert "qsa_mqa_decode_planned" in _err(lib)
+
+
+def test_decode_planned_zero_work_and_plan_size(lib):
+    assert _planned(lib, num_reqs=0, plan=None, q=None, out=None) == 0
+    assert _planned(lib, out_cols=0, out_stride=0, plan=None) == 0
+    n = ctypes.c_int64(-1)
+    assert lib.qsa_decode_plan_bytes(16, 25600, ctypes.byref(n)) == 0 and n.value == 16 * 400 * 16
+    assert lib.qsa_decode_plan_bytes(3, 65, ctypes.byref(n)) == 0 and n.value == 3 * 2 * 16
+    assert lib.qsa_decode_plan_bytes(0, 100, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.qsa_decode_plan_bytes(-1, 100, ctypes.byref(n)) == 1
+    assert lib.qsa_decode_plan_bytes(1, 100, None) == 1
+
+
+def _build_plan(lib, **kw):
+    a = dict(comp=FAKE, pt=FAKE, pt_stride=8, pt_cols=8, num_pages=100, page_size=64, num_reqs=2, out_cols=200,
+             plan=FAKE, plan_bytes=1 << 20)
+    a.update(kw)
+    return lib.qsa_build_decode_plan(a["comp"], a["pt"], a["pt_stride"], a["pt_cols"], a["num_pages"],
+                                     a["page_size"], a["num_reqs"], a["out_cols"], a["plan"], a["plan_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(num_reqs=-1), 1, "negative"),
+    (dict(page_size=0), 1, "page_size"),
+    (dict(num_reqs=3, pt_stride=4), 1, "page_table_stride"),
+    (dict(num_reqs=4097), 2, "4096"),
+    (dict(comp=None), 1, "NULL"),
+    (dict(plan=None), 1, "NULL"),
+    (dict(pt=None), 1, "page_table"),
+    (dict(plan=FAKE + 8), 3, "aligned"),
+    (dict(plan_bytes=2 * 4 * 16 - 16), 1, "needed"),
+])
+def test_build_decode_plan_rejects(lib, kw, code, text):
+    assert _build_plan(lib, **kw) == code
+    assert text in _err(lib)
+
+
+def test_build_decode_plan_nothing_to_do(lib):
+    assert _build_plan(lib, num_reqs=0, comp=None, plan=None) == 0
+    assert _build_plan(lib, out_cols=0, comp=None, plan=None) == 0
+
+
+@pytest.mark.parametrize("args,code,text", [
+    ((FAKE, -1, 4), 1, "num_reqs"),
+    ((FAKE, 3, 0), 1, "dql"),
+    ((FAKE, 3, 17), 1, "dql"),
+    ((None, 3, 4), 1, "NULL seq_lens"),
+])
+def test_decode_visible_blocks_rejects(lib, args, code, text):
+    assert lib.qsa_decode_visible_blocks(args[0], args[1], args[2], FAKE, FAKE, None) == code
+    assert text in _err(lib)
+
+
+def test_decode_visible_blocks_nothing_to_do(lib):
+    assert lib.qsa_decode_visible_blocks(None, 0, 4, FAKE, FAKE, None) == 0
+    assert lib.qsa_decode_visible_blocks(None, 5, 4, None, None, None) == 0
+
+
 def test_decode_zero_work_is_ok_without_device(lib):
     assert _decode(lib, num_reqs=0, q=None, comp=None, out=None) == 0
     assert _decode(lib, out_cols=0, out_stride=0, q=None, out=None) == 0

@@ -52,7 +52,8 @@ def _mask_pattern_all_rows(out_host, ks, ke, num_keys):
     valid = (key >= 0) & (key < num_keys) & (key < ke.astype(np.int64)[:, None])
     bits = out_host.view(np.uint32)
     assert np.array_equal(bits == 0xFF800000, ~valid), "mask pattern"
-    assert np.all(bits[valid] < 0x80000000), "negative or -0 score"
+    # Finite and >= +0: also fails on the NaN poison of an unwritten cell.
+    assert np.all(bits[valid] < 0x7F800000), "negative, -0, infinite or NaN score (or a cell left unwritten)"
 
 
 @pytest.mark.parametrize("name", ["prefill_1x8k_8k", "prefill_4x4k_100k", "prefill_1x8k_100k"])
@@ -66,6 +67,18 @@ def test_prefill_workloads_sampled(name):
     rows = _sample_rows(inp.q.shape[0], seed=len(name), extra=64 if "100k" in name else 160)
     ref = O.prefill(inp.q, inp.k, ks, ke, inp.out_cols, rows=rows)
     assert_scores_match(host[rows], ref, name)
+
+
+def test_prefill_1x8k_8k_full():
+    """1x8K queries over an 8K prefix: every cell against the oracle."""
+    inp = WORKLOADS["prefill_1x8k_8k"].make()
+    ks, ke = _intervals(inp)
+    host = _gpu(inp.q, inp.k, ks, ke, inp.out_cols).cpu().numpy()
+    T = inp.q.shape[0]
+    for b in range(0, T, 2048):
+        rows = np.arange(b, min(T, b + 2048))
+        ref = O.prefill(inp.q, inp.k, ks, ke, inp.out_cols, rows=rows)
+        assert_scores_match(host[rows], ref, f"prefill_1x8k_8k rows {b}..")
 
 
 @pytest.mark.parametrize("T,NK,cols", [(1, 5, 5), (5, 70, 64), (63, 200, 65), (64, 64, 64),

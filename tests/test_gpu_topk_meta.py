@@ -118,6 +118,26 @@ def test_metadata_matches_oracle():
         assert np.array_equal(res["row_k_end"].cpu().numpy(), ke)
 
 
+@pytest.mark.parametrize("dql", [1, 3, 4, 16])
+def test_decode_visible_blocks_matches_oracle(dql):
+    """Uniform decode batches: compressed lengths and per-row visible blocks
+    equal the oracle's token metadata for query_start_loc = 0, dql, 2 dql ..,
+    including contexts shorter than dql, empty contexts, the golden visible
+    table's contexts and the spec-decode batch's."""
+    qsa = _qsa()
+    rng = np.random.default_rng(dql)
+    ctx = [0, 1, 2, 3, 4, 5, 7, 8, 10, 11, 256, 3508, 100_000, 102_400]
+    ctx += rng.integers(0, 200_000, 200).tolist()
+    ctx += [int(x) for x in WORKLOADS["specdecode_16x51k"].make().seq_lens]
+    seq = np.array(ctx, np.int32)
+    comp, vis = qsa.qsa_decode_visible_blocks(i32_to_device(seq), dql)
+    torch.cuda.synchronize()
+    qsl = (np.arange(len(seq) + 1) * dql).astype(np.int32)
+    _, _, want = O.token_metadata(qsl, seq, len(seq) * dql)
+    assert np.array_equal(vis.cpu().numpy(), want)
+    assert np.array_equal(comp.cpu().numpy(), O.comp_lens(seq))
+
+
 def test_whole_path_mixed_batch():
     """One step: split a mixed batch, build metadata on the GPU, score the
     decode rows through the page table and the prefill rows over packed keys,
@@ -160,7 +180,11 @@ def test_whole_path_mixed_batch():
     assert np.array_equal(ptop.cpu().numpy(), O.topk(pscores.cpu().numpy(), 64))
 
 
-def test_topk_on_prefill_4x4k_100k_sampled():
+def test_topk_on_prefill_4x4k_100k_all_rows():
+    """Top-512 of all 16,384 rows of the 4x4K-over-100K prefill: bit-exact
+    against the oracle's top-k of the same GPU scores on every row (integer
+    work on identical inputs), and valid against the oracle's own scores on
+    512 sampled rows."""
     qsa = _qsa()
     inp = WORKLOADS["prefill_4x4k_100k"].make()
     req, _, vis = O.token_metadata(inp.query_start_loc, inp.seq_lens, inp.q.shape[0])
@@ -169,10 +193,15 @@ def test_topk_on_prefill_4x4k_100k_sampled():
                                  i32_to_device(ke), out_cols=inp.out_cols)
     top = qsa.qsa_topk_blocks(scores, 512)
     torch.cuda.synchronize()
+    top_host = top.cpu().numpy()
+    T = inp.q.shape[0]
+    for b in range(0, T, 4096):
+        chunk = scores[b:b + 4096].cpu().numpy()
+        assert np.array_equal(top_host[b:b + 4096], O.topk(chunk, 512)), f"rows {b}.."
+    del chunk
     rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[0, 4095, 4096, 16383], rng.integers(0, 16384, 28)]))
+    rows = np.unique(np.concatenate([[0, 4095, 4096, 8191, 8192, 12287, 12288, 16383],
+                                     rng.choice(T, 520, replace=False)]))
+    assert len(rows) >= 512
     ref = O.prefill(inp.q, inp.k, ks, ke, inp.out_cols, rows=rows)
-    top_rows = top.cpu().numpy()[rows]
-    assert_topk_valid(top_rows, ref, 512)
-    got_scores = scores[torch.from_numpy(rows).cuda()].cpu().numpy()
-    assert np.array_equal(top_rows, O.topk(got_scores, 512))
+    assert_topk_valid(top_host[rows], ref, 512)

@@ -144,6 +144,13 @@ def test_prefill_fp16_1x8k_over_100k_sampled():
     rows = np.array([0, 1, 2, 63, 64, 127, 128, 1000, 4095, 4096, 8000, T - 1])
     ref = O.prefill_typed(q, "fp16", k, "fp16", ks, ke, inp.out_cols, rows=rows)
     assert_scores_match(gpu[torch.from_numpy(rows).cuda()], ref, "fp16 NS sampled")
+    # Every row: -inf exactly outside the interval, finite and >= +0 inside
+    # (the output started as NaN, so an unwritten cell fails).
+    bits = gpu.cpu().numpy().view(np.uint32)
+    key = ks.astype(np.int64)[:, None] + np.arange(inp.out_cols)[None, :]
+    valid = (key >= 0) & (key < inp.k.shape[0]) & (key < ke.astype(np.int64)[:, None])
+    assert np.array_equal(bits == 0xFF800000, ~valid)
+    assert np.all(bits[valid] < 0x7F800000)
 
 
 @pytest.mark.parametrize("pad,base", [(4, 12), (8, 0), (16, 28)])

@@ -34,6 +34,10 @@ MUTANTS = {
     "page_range_unchecked": ("if (page >= 0 && page < num_pages) {", "if (page >= 0) {"),
     "page_table_width_unchecked": ("if (slot < page_table_cols) {", "if (slot < page_table_cols + 1) {"),
     "decode_row_request_wrong": ("int32_t r = row / dql;", "int32_t r = row % dql;"),
+    "intervals_offset_by_token": ("int32_t start = key_offsets[token_to_req[t]];",
+                                  "int32_t start = key_offsets[t % 4];"),
+    "intervals_end_without_offset": ("row_k_end[t] = start + visible[t];", "row_k_end[t] = visible[t];"),
+    "intervals_end_one_short": ("row_k_end[t] = start + visible[t];", "row_k_end[t] = start + visible[t] - 1;"),
     "prefill_absolute_columns": ("int64_t n = (int64_t)row_k_start[t] + c;", "int64_t n = c;"),
     "prefill_end_inclusive": ("n < row_k_end[t])", "n <= row_k_end[t])"),
     "prefill_no_lower_bound": ("if (n >= 0 && n < num_keys", "if (n >= -2 && n < num_keys"),
