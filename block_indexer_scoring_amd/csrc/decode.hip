@@ -47,11 +47,21 @@
 // k-step ks), so the products are unchanged.  The cache scale multiplies the
 // head sum together with the score scale (relu commutes with a positive
 // factor).
+#include <mutex>
+
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
+
+// The library's own decode task table, for callers that cannot allocate
+// (qsa_mqa_decode_static_plan): 262,144 entries of 16 bytes (4 MiB) per
+// device, held until the process ends.  In host code `scratch` names only a
+// host-side stand-in; kernels get the device address from
+// static_plan_pointer().
+constexpr int64_t kStaticPlanEntries = 262144;
+static __device__ __align__(256) int32_t scratch[kStaticPlanEntries * 4];
 
 constexpr int kSpan = 64;     // keys per wavefront task
 constexpr int kPadSpans = 4;  // spans per -inf-only task
@@ -498,6 +508,26 @@ hipError_t launch_src(const DecodeParams &p, hipStream_t stream, dim3 grid, dim3
 }  // namespace
 
 int decode_span_keys() { return kSpan; }
+
+int64_t static_plan_entries() { return kStaticPlanEntries; }
+
+hipError_t static_plan_pointer(int32_t **table) {
+    static std::mutex mu;
+    static int32_t *addr[64] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *ptr = nullptr;
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        addr[dev] = static_cast<int32_t *>(ptr);
+    }
+    *table = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
     const int64_t tasks = (int64_t)p.num_reqs * p.spans;

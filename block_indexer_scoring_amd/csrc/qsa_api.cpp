@@ -377,13 +377,16 @@ static int check_formats(const char *fn, int32_t q_dtype, int32_t k_dtype, float
 
 // plan: null for the mapped launch (tasks from comp_lens), else a task table
 // of plan_bytes bytes from qsa_build_decode_plan (comp_lens unused).
+// static_plan: build the task table from comp_lens into the library's own
+// device array, then run the planned launch (no plan argument).
 static int decode_impl(const char *fn, const void *q, int32_t q_dtype, int64_t q_stride_req,
                        int64_t q_stride_row, int64_t q_stride_head, const void *k_cache, int32_t k_dtype,
                        float k_scale, int64_t num_pages, int32_t page_size, const int32_t *page_table,
                        int64_t page_table_stride, int32_t page_table_cols, const int32_t *comp_lens,
                        const int32_t *visible, int32_t num_reqs, int32_t dql, int32_t num_heads,
                        int32_t head_dim, float scale, float *out, int64_t out_stride, int32_t out_cols,
-                       void *stream, const void *plan = nullptr, int64_t plan_bytes = 0) {
+                       void *stream, const void *plan = nullptr, int64_t plan_bytes = 0,
+                       bool static_plan = false) {
     int rc;
     if ((rc = check_heads(fn, num_heads, head_dim))) return rc;
     if ((rc = check_scale(fn, scale))) return rc;
@@ -451,7 +454,44 @@ static int decode_impl(const char *fn, const void *q, int32_t q_dtype, int64_t q
     p.k_fp8 = k_fp8;
     p.plan = static_cast<const int32_t *>(plan);
     p.plan_entries = plan ? (int64_t)num_reqs * spans : 0;
-    return device_status(fn, qsa::launch_decode(p, static_cast<hipStream_t>(stream)));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!static_plan) return device_status(fn, qsa::launch_decode(p, st));
+
+    // The task table goes to the library's device array: two launches, no
+    // allocation.  Every entry the decode reads is written by the first.
+    const int64_t entries = (int64_t)num_reqs * spans;
+    if (entries > qsa::static_plan_entries())
+        return fail(QSA_ERR_UNSUPPORTED,
+                    "%s: %d requests x %d columns need %lld task entries; the library's table holds %lld "
+                    "(use qsa_build_decode_plan with a caller-owned table)",
+                    fn, num_reqs, out_cols, (long long)entries, (long long)qsa::static_plan_entries());
+    if (num_reqs > qsa::kPlanMaxReqs)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: plans for more than %d requests", fn, qsa::kPlanMaxReqs);
+    int32_t *table = nullptr;
+    const hipError_t terr = qsa::static_plan_pointer(&table);
+    if (terr != hipSuccess)
+        return fail(QSA_ERR_DEVICE, "%s: the library's task table is not available: %s", fn, hipGetErrorString(terr));
+    qsa::PlanParams pp{};
+    pp.comp_lens = comp_lens;
+    pp.page_table = page_table;
+    pp.page_table_stride = page_table_stride;
+    pp.page_table_cols = page_table ? page_table_cols : 0;
+    pp.num_pages = num_pages;
+    pp.page_size = page_size;
+    pp.num_reqs = num_reqs;
+    pp.spans = (int32_t)spans;
+    pp.plan = table;
+    pp.entries = entries;
+    p.plan = table;
+    p.plan_entries = entries;
+    // Armed timing events span both launches.
+    const qsa::LaunchEvents ev = g_launch_events;
+    g_launch_events = {ev.start, nullptr};
+    hipError_t err = qsa::launch_decode_plan(pp, st);
+    g_launch_events = {nullptr, ev.stop};
+    if (err == hipSuccess) err = qsa::launch_decode(p, st);
+    g_launch_events = ev;
+    return device_status(fn, err);
 }
 
 int qsa_decode_plan_bytes(int32_t num_reqs, int32_t out_cols, int64_t *bytes) {
@@ -499,6 +539,19 @@ int qsa_build_decode_plan(const int32_t *comp_lens, const int32_t *page_table, i
     p.plan = static_cast<int32_t *>(plan);
     p.entries = (int64_t)num_reqs * spans;
     return device_status(fn, qsa::launch_decode_plan(p, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_mqa_decode_static_plan(const void *q, int32_t q_dtype, int64_t q_stride_req, int64_t q_stride_row,
+                               int64_t q_stride_head, const void *k_cache, int32_t k_dtype, float k_scale,
+                               int64_t num_pages, int32_t page_size, const int32_t *page_table,
+                               int64_t page_table_stride, int32_t page_table_cols, const int32_t *comp_lens,
+                               const int32_t *visible, int32_t num_reqs, int32_t dql, int32_t num_heads,
+                               int32_t head_dim, float scale, float *out, int64_t out_stride, int32_t out_cols,
+                               void *stream) {
+    return decode_impl("qsa_mqa_decode_static_plan", q, q_dtype, q_stride_req, q_stride_row, q_stride_head, k_cache,
+                       k_dtype, k_scale, num_pages, page_size, page_table, page_table_stride, page_table_cols,
+                       comp_lens, visible, num_reqs, dql, num_heads, head_dim, scale, out, out_stride, out_cols,
+                       stream, nullptr, 0, true);
 }
 
 int qsa_mqa_decode_planned(const void *plan, int64_t plan_bytes, const void *q, int32_t q_dtype,

@@ -191,6 +191,10 @@ hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t s
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);  // p.plan selects the planned kernel
 hipError_t launch_decode_plan(const PlanParams &p, hipStream_t stream);
+// The library's own decode task table on the current device (for callers
+// that cannot allocate): its address, and its capacity in entries.
+hipError_t static_plan_pointer(int32_t **table);
+int64_t static_plan_entries();
 int decode_span_keys();
 int prefill_col_chunk(int64_t num_rows, int32_t out_cols, int64_t k_stride, int num_cus);
 int64_t prefill_max_k_stride();  // larger key strides overflow the kernel's 32-bit key offsets

@@ -21,14 +21,14 @@ QSA_ERR_INVALID_ARGUMENT = 1
 QSA_ERR_UNSUPPORTED = 2
 QSA_ERR_LAYOUT = 3
 QSA_ERR_DEVICE = 4
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_set_launch_events", "qsa_split_batch",
            "qsa_build_metadata", "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks",
            "qsa_mqa_prefill_topk", "qsa_prefill_topk_workspace_bytes", "qsa_mqa_decode_typed",
            "qsa_mqa_prefill_typed", "qsa_build_cache_metadata", "qsa_gather_keys", "qsa_prepare_q",
            "qsa_decode_plan_bytes", "qsa_build_decode_plan", "qsa_mqa_decode_planned",
-           "qsa_decode_visible_blocks")
+           "qsa_decode_visible_blocks", "qsa_mqa_decode_static_plan")
 
 # enum qsa_dtype
 QSA_DTYPE_BF16 = 0
@@ -98,6 +98,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_prepare_q.restype = ctypes.c_int
     lib.qsa_decode_visible_blocks.argtypes = [P, i32, i32, P, P, P]
     lib.qsa_decode_visible_blocks.restype = ctypes.c_int
+    lib.qsa_mqa_decode_static_plan.argtypes = [P, i32, i64, i64, i64, P, i32, f32, i64, i32, P, i64, i32, P, P,
+                                               i32, i32, i32, i32, f32, P, i64, i32, P]
+    lib.qsa_mqa_decode_static_plan.restype = ctypes.c_int
     lib.qsa_decode_plan_bytes.argtypes = [i32, i32, P]
     lib.qsa_decode_plan_bytes.restype = ctypes.c_int
     lib.qsa_build_decode_plan.argtypes = [P, P, i64, i32, i64, i32, i32, i32, P, i64, P]
@@ -410,6 +413,50 @@ def qsa_mqa_decode_typed(q: torch.Tensor, k_cache: torch.Tensor, page_table: tor
     if out.dim() != 2 or out.shape[0] != num_reqs * dql or (out.shape[1] > 1 and out.stride(1) != 1):
         raise ValueError("out must be [R*DQL, out_cols] with unit column stride")
     _check(lib.qsa_mqa_decode_typed(
+        _ptr(q), q_fmt, q.stride(0), q.stride(1), q.stride(2), _ptr(k_cache), k_fmt, float(k_scale),
+        k_cache.shape[0], k_cache.shape[1], _ptr(page_table), page_table.stride(0), page_table.shape[1],
+        _ptr(comp_lens), _ptr(visible), num_reqs, dql, heads, dim, float(scale), _ptr(out),
+        out.stride(0), out.shape[1], _stream_handle(stream)))
+    return out
+
+
+def qsa_mqa_decode_static_plan(q: torch.Tensor, k_cache: torch.Tensor, page_table: torch.Tensor,
+                               comp_lens: torch.Tensor, visible: torch.Tensor | None = None,
+                               out_cols: int | None = None, k_scale: float = 1.0,
+                               scale: float = DEFAULT_SCALE, out: torch.Tensor | None = None,
+                               stream=None) -> torch.Tensor:
+    """The planned decode with the task table in the library's own device
+    memory (no allocation inside the call).  Arguments as
+    qsa_mqa_decode_typed; pass `out` to keep the call itself free of
+    allocations."""
+    lib = load_library()
+    q_fmt = _gpu_format("q", q, (torch.bfloat16, torch.float16))
+    k_fmt = _gpu_format("k_cache", k_cache, (torch.bfloat16, torch.float16, torch.float8_e4m3fn))
+    _gpu("page_table", page_table, torch.int32)
+    _gpu("comp_lens", comp_lens, torch.int32)
+    if q.dim() != 4 or k_cache.dim() != 4 or page_table.dim() != 2:
+        raise ValueError("q must be [R, DQL, H, D], k_cache [P, page_size, 1, D], page_table [R, W]")
+    num_reqs, dql, heads, dim = q.shape
+    if q.stride(3) != 1 and dim > 1:
+        raise QSAError(QSA_ERR_LAYOUT, "q needs unit feature stride")
+    if k_cache.shape[2] != 1 or k_cache.shape[3] != dim or not k_cache.is_contiguous():
+        raise ValueError("k_cache must be a contiguous [P, page_size, 1, 128] tensor")
+    if page_table.shape[0] != num_reqs or (page_table.shape[1] > 1 and page_table.stride(1) != 1):
+        raise ValueError("page_table must be [R, W] with unit column stride")
+    if comp_lens.numel() != num_reqs or not comp_lens.is_contiguous():
+        raise ValueError("comp_lens must be a contiguous [R] tensor")
+    if visible is not None:
+        _gpu("visible", visible, torch.int32)
+        if visible.numel() != num_reqs * dql or not visible.is_contiguous():
+            raise ValueError("visible must be a contiguous [R*DQL] tensor")
+    if out is None:
+        if out_cols is None:
+            raise ValueError("give out_cols or out")
+        out = torch.empty((num_reqs * dql, out_cols), dtype=torch.float32, device=q.device)
+    _gpu("out", out, torch.float32)
+    if out.dim() != 2 or out.shape[0] != num_reqs * dql or (out.shape[1] > 1 and out.stride(1) != 1):
+        raise ValueError("out must be [R*DQL, out_cols] with unit column stride")
+    _check(lib.qsa_mqa_decode_static_plan(
         _ptr(q), q_fmt, q.stride(0), q.stride(1), q.stride(2), _ptr(k_cache), k_fmt, float(k_scale),
         k_cache.shape[0], k_cache.shape[1], _ptr(page_table), page_table.stride(0), page_table.shape[1],
         _ptr(comp_lens), _ptr(visible), num_reqs, dql, heads, dim, float(scale), _ptr(out),

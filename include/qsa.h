@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 8
+#define QSA_ABI_VERSION 9
 
 enum qsa_status {
     QSA_OK = 0,
@@ -78,7 +78,8 @@ const char *qsa_last_error(void);
  *   duration, without the dispatch latency that an event pair recorded on
  *   the stream around the call adds.  Each entry point below launches one
  *   kernel (none when it has nothing to compute), except
- *   qsa_build_cache_metadata (up to two) and qsa_mqa_prefill_topk (four):
+ *   qsa_build_cache_metadata (up to two), qsa_mqa_decode_static_plan (two)
+ *   and qsa_mqa_prefill_topk (four):
  *   for those the start event marks the first kernel's begin and the stop
  *   event the last kernel's end.
  *   start_event, stop_event : hipEvent_t handles created by the caller (may
@@ -380,6 +381,35 @@ int qsa_mqa_decode_typed(const void *q, int32_t q_dtype, int64_t q_stride_req,
  *   Errors: as qsa_mqa_decode_typed, plus INVALID_ARGUMENT for a NULL plan
  *   or plan_bytes below the table's size, and LAYOUT for a misaligned plan.
  */
+/* qsa_mqa_decode_static_plan -- the planned decode with the task table in
+ * the library's own device memory, for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It calls no allocating routine: the table lives in a
+ * 4 MiB array (262,144 entries) that each device holds from the library's
+ * first use on it until the process ends.
+ *   Arguments, output and errors as qsa_mqa_decode_typed (comp_lens and
+ *   the page table are read to build the table).  The call enqueues two
+ *   kernels on stream: qsa_build_decode_plan into the library's table, then
+ *   qsa_mqa_decode_planned from it; the scores equal qsa_mqa_decode_planned's
+ *   with a table built by qsa_build_decode_plan, bit for bit.
+ *   Limits: num_reqs * ceil(out_cols / 64) <= 262,144 and num_reqs <=
+ *   4,096, else UNSUPPORTED (no launch).  DEVICE if the table's address
+ *   cannot be obtained.
+ *   Every call on one device shares that device's table: calls that overlap
+ *   on one GPU (other streams, other threads) race and give wrong scores;
+ *   calls in one stream are ordered and safe.  The table keeps the last
+ *   call's contents, and nothing needs clearing: each call writes every
+ *   entry it reads.
+ */
+int qsa_mqa_decode_static_plan(const void *q, int32_t q_dtype, int64_t q_stride_req,
+                               int64_t q_stride_row, int64_t q_stride_head, const void *k_cache,
+                               int32_t k_dtype, float k_scale, int64_t num_pages, int32_t page_size,
+                               const int32_t *page_table, int64_t page_table_stride,
+                               int32_t page_table_cols, const int32_t *comp_lens,
+                               const int32_t *visible, int32_t num_reqs, int32_t dql,
+                               int32_t num_heads, int32_t head_dim, float scale, float *out,
+                               int64_t out_stride, int32_t out_cols, void *stream);
+
 int qsa_decode_plan_bytes(int32_t num_reqs, int32_t out_cols, int64_t *bytes);
 
 int qsa_build_decode_plan(const int32_t *comp_lens, const int32_t *page_table,

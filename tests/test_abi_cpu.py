@@ -322,6 +322,18 @@ def test_decode_planned_rejects(lib, kw, code, text):
     assert "qsa_mqa_decode_planned" in _err(lib)
 
 
+def test_decode_static_plan_capacity_checked_on_the_host(lib):
+    """Beyond the library's 262,144-entry table the call is refused before
+    any device work (the pointers here are never dereferenced)."""
+    def call(num_reqs, out_cols):
+        return lib.qsa_mqa_decode_static_plan(FAKE, 0, 512, 512, 128, FAKE, 0, 1.0, 4, 64, FAKE, 4, 4, FAKE,
+                                              None, num_reqs, 1, 4, 128, 0.088, FAKE, out_cols, out_cols, None)
+    assert call(1025, 256 * 64) == 2
+    assert "262144" in _err(lib) and "qsa_mqa_decode_static_plan" in _err(lib)
+    assert call(4097, 64) == 2 and "4096" in _err(lib)
+    assert call(0, 64) == 0
+
+
 def test_decode_planned_zero_work_and_plan_size(lib):
     assert _planned(lib, num_reqs=0, plan=None, q=None, out=None) == 0
     assert _planned(lib, out_cols=0, out_stride=0, plan=None) == 0
