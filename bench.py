@@ -162,21 +162,60 @@ class HipEvents:
         self.ev = []
 
 
-def cpu_baseline(dec_inp, dec_vis, min_cpu_seconds: float = 12.0, max_passes: int = 64):
-    """The oracle, as it stands, on this host's cores: full decode passes over
-    the decode workload until about min_cpu_seconds of CPU work (wall x
-    threads) have run."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(dec_inp, dec_vis, pre_inp, pre_ks, pre_ke, min_cpu_seconds: float = 12.0,
+                 max_passes: int = 64):
+    """The oracle, as it stands, on this host's cores.
+
+    Headline (value): full decode passes over the spec-decode batch on all
+    the host's threads until about min_cpu_seconds of CPU work (wall x
+    threads) have run, in GB/s under the pages' accounting.  Also: one decode
+    pass on one thread, and the oracle prefill on a fixed subset of the
+    1x8K-over-100K rows (GFLOP/s, 2*4*128 FLOP per visible block) on all
+    threads and on one thread."""
+    import numpy as np
+
     from oracle import oracle as O
     threads = O._threads(None)
     comp = O.comp_lens(dec_inp.seq_lens)
-    passes, wall = 0, 0.0
-    while passes < max_passes and wall * threads < min_cpu_seconds:
+
+    def decode_pass(n_threads):
         t0 = time.perf_counter()
         O.decode(dec_inp.q, dec_inp.k_pool, dec_inp.page_table, comp, dec_vis, dec_inp.out_cols,
-                 threads=threads)
-        wall += time.perf_counter() - t0
+                 threads=n_threads)
+        return time.perf_counter() - t0
+
+    passes, wall = 0, 0.0
+    while passes < max_passes and wall * threads < min_cpu_seconds:
+        wall += decode_pass(threads)
         passes += 1
     nbytes = decode_bytes(dec_inp.num_reqs, dec_inp.dql, float(comp.sum()))
+    one_wall = decode_pass(1)
+
+    T = pre_inp.q.shape[0]
+    rows_all = np.linspace(0, T - 1, 128).astype(np.int64)   # 128 rows spread over the chunk
+    rows_one = rows_all[::8]                                 # 16 of them on one thread
+
+    def prefill_rate(rows, n_threads):
+        t0 = time.perf_counter()
+        O.prefill(pre_inp.q, pre_inp.k, pre_ks, pre_ke, pre_inp.out_cols, rows=rows, threads=n_threads)
+        dt = time.perf_counter() - t0
+        vis = float(np.maximum(pre_ke[rows].astype(np.int64) - pre_ks[rows], 0).sum())
+        return prefill_flops(vis) / dt / 1e9, dt
+
+    pf_all, pf_all_s = prefill_rate(rows_all, threads)
+    pf_one, pf_one_s = prefill_rate(rows_one, 1)
     return {
         "value": round(nbytes / (wall / passes) / 1e9, 4),
         "unit": "GB/s",
@@ -185,6 +224,14 @@ def cpu_baseline(dec_inp, dec_vis, min_cpu_seconds: float = 12.0, max_passes: in
         "sample": f"{passes} full pass(es) of the oracle decode over the 16-request DQL-4 batch "
                   f"(64 rows x {dec_inp.out_cols} columns, {int(comp.sum())} keys), "
                   f"{wall:.2f} s wall on {threads} threads",
+        "cpu_model": cpu_model(),
+        "decode_1_thread": {"value": round(nbytes / one_wall / 1e9, 4), "unit": "GB/s", "cores": 1,
+                            "sample": f"1 full pass, {one_wall:.2f} s wall"},
+        "prefill_all_threads": {"value": round(pf_all, 3), "unit": "GFLOP/s", "cores": threads,
+                                "sample": f"oracle prefill on 128 of the {T} rows of the 1x8K-over-100K chunk "
+                                          f"(every {T // 128}th), {pf_all_s:.2f} s wall"},
+        "prefill_1_thread": {"value": round(pf_one, 3), "unit": "GFLOP/s", "cores": 1,
+                             "sample": f"16 of those rows, {pf_one_s:.2f} s wall"},
     }
 
 
@@ -506,6 +553,91 @@ def main(argv=None) -> int:
         e.close()
     del q16, k16
 
+    # The other workload configurations, for context: each timed over its own
+    # launches with the same per-kernel events, inputs resident in HBM.
+    #   tiny_decode (1 request, context 256, page size 16) and decode_100k
+    #   (1 request, context 100,000, page size 64; 48 key pools rotated, more
+    #   than the Infinity Cache holds): planned decode, us and GB/s;
+    #   prefill_1x8k_8k and prefill_4x4k_100k: prefill us, TFLOP/s, fraction
+    #   of dense bf16 MFMA peak; and the top-512 of the 4x4K rows, us and GB/s.
+    def timed(n, warm, launch):
+        evs = [HipEvents(2) for _ in range(n)]
+        for j in range(n + warm):
+            if j >= warm:
+                check(lib.qsa_set_launch_events(evs[j - warm].ev[0], evs[j - warm].ev[1]))
+            launch(j)
+            check(lib.qsa_set_launch_events(None, None))
+        torch.cuda.synchronize()
+        us = [e.elapsed_us(0, 1) for e in evs]
+        for e in evs:
+            e.close()
+        return float(np.mean(us)), float(np.median(us))
+
+    configs = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    for name, n_pools in (("tiny_decode", 1), ("decode_100k", 48)):
+        w = WORKLOADS[name].make()
+        c_pools = [to_bf16(w.k_pool)] + [
+            torch.randn(w.k_pool.shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(n_pools - 1)]
+        c_pt = to_i32(w.page_table)
+        c_q = to_bf16(w.q)
+        c_comp, c_vis = qsa.qsa_decode_visible_blocks(to_i32(w.seq_lens), w.dql)
+        c_plan = qsa.qsa_build_decode_plan(c_comp, c_pt, c_pools[0].shape[0], w.page_size, w.out_cols)
+        c_out = torch.empty((w.num_reqs * w.dql, w.out_cols), dtype=torch.float32, device=dev)
+
+        def c_launch(j, c_pools=c_pools, c_pt=c_pt, c_q=c_q, c_vis=c_vis, c_plan=c_plan, c_out=c_out, w=w):
+            pool = c_pools[j % len(c_pools)]
+            check(lib.qsa_mqa_decode_planned(
+                c_plan.data_ptr(), c_plan.numel(), c_q.data_ptr(), qsa.QSA_DTYPE_BF16, c_q.stride(0), c_q.stride(1),
+                c_q.stride(2), pool.data_ptr(), qsa.QSA_DTYPE_BF16, 1.0, pool.shape[0], pool.shape[1],
+                c_pt.data_ptr(), c_pt.stride(0), c_pt.shape[1], c_vis.data_ptr(), w.num_reqs, w.dql, 4, 128, scale,
+                c_out.data_ptr(), c_out.stride(0), c_out.shape[1], sh))
+
+        c_mean, c_med = timed(50, 5, c_launch)
+        c_bytes = decode_bytes(w.num_reqs, w.dql, float(c_comp.sum().item()))
+        configs[name] = {"kernel": "decode (planned)", "us": round(c_mean, 3), "us_median": round(c_med, 3),
+                         "bytes": c_bytes, "gbps": round(c_bytes / (c_mean * 1e-6) / 1e9, 2),
+                         "frac_of_hbm": round(c_bytes / (c_mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "key_pools": len(c_pools)}
+        del c_pools, c_out
+    for name, n_launch in (("prefill_1x8k_8k", 20), ("prefill_4x4k_100k", 6)):
+        w = WORKLOADS[name].make()
+        Tw = w.q.shape[0]
+        w_q, w_k = to_bf16(w.q), to_bf16(w.k)
+        w_meta = qsa.qsa_build_metadata(to_i32(w.query_start_loc), to_i32(w.seq_lens), Tw,
+                                        key_offsets=to_i32(w.key_offsets))
+        w_out = torch.empty((Tw, w.out_cols), dtype=torch.float32, device=dev)
+
+        def p_launch(j, w_q=w_q, w_k=w_k, w_meta=w_meta, w_out=w_out, Tw=Tw):
+            check(lib.qsa_mqa_prefill(
+                w_q.data_ptr(), w_q.stride(0), w_q.stride(1), w_k.data_ptr(), w_k.stride(0), w_k.shape[0],
+                w_meta["row_k_start"].data_ptr(), w_meta["row_k_end"].data_ptr(), Tw, 4, 128, scale,
+                w_out.data_ptr(), w_out.stride(0), w_out.shape[1], sh))
+
+        p_mean, p_med = timed(n_launch, 2, p_launch)
+        w_flops = prefill_flops(int(w_meta["visible"].to(torch.int64).sum().item()))
+        w_tflops = w_flops / (p_mean * 1e-6) / 1e12
+        configs[name] = {"kernel": "prefill", "us": round(p_mean, 3), "us_median": round(p_med, 3),
+                         "flops": w_flops, "tflops": round(w_tflops, 2),
+                         "frac_of_mfma": round(w_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "out_bytes": float(Tw) * w.out_cols * 4}
+        if name == "prefill_4x4k_100k":
+            w_top = torch.empty((Tw, TOPK), dtype=torch.int32, device=dev)
+
+            def t_launch(j, w_out=w_out, w_top=w_top, Tw=Tw):
+                check(lib.qsa_topk_blocks(w_out.data_ptr(), w_out.stride(0), Tw, w_out.shape[1], TOPK,
+                                          w_top.data_ptr(), TOPK, sh))
+
+            t_mean, t_med = timed(n_launch, 2, t_launch)
+            t_bytes = topk_bytes(Tw, w.out_cols, TOPK)
+            configs[name + "_topk512"] = {"kernel": "top-k", "us": round(t_mean, 3), "us_median": round(t_med, 3),
+                                          "bytes": t_bytes, "gbps": round(t_bytes / (t_mean * 1e-6) / 1e9, 2),
+                                          "frac_of_hbm": round(t_bytes / (t_mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+            del w_top
+        del w_out
+    result["configs"] = configs
+
     # The compressed-cache metadata of the step's batch (the decode requests'
     # page tables and a block table for the prefill chunk, page size 64,
     # 4,096 work-item slots), and the paged-key gather of the decode batch's
@@ -640,7 +772,9 @@ def main(argv=None) -> int:
     if not args.no_cpu_baseline:
         from oracle import oracle as O
         _, _, dec_vis = O.token_metadata(dec.query_start_loc, dec.seq_lens, T_dec)
-        result["cpu_baseline"] = cpu_baseline(dec, dec_vis)
+        p_req, _, p_vis = O.token_metadata(pre.query_start_loc, pre.seq_lens, T_pre)
+        p_ks, p_ke = O.prefill_intervals(p_req, p_vis, pre.key_offsets)
+        result["cpu_baseline"] = cpu_baseline(dec, dec_vis, pre, p_ks, p_ke)
     print(json.dumps(result), flush=True)
     return 0
 
