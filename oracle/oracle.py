@@ -80,6 +80,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_prepare_q.argtypes = [P, i64, i32, P, i64, i64, P, ctypes.c_int, i64, P, ctypes.c_int, f32,
                                      P, P, ctypes.c_int, f32, i64, i64, i32, i32]
     lib.oracle_prepare_q.restype = None
+    lib.oracle_ring_slots.argtypes = [P, P, i32, i32, P, i64, i32, i32, P]
+    lib.oracle_ring_slots.restype = None
+    lib.oracle_write_keys.argtypes = [P, i64, i32, P, P, ctypes.c_int, i64, i64, f32, P, i64, i64]
+    lib.oracle_write_keys.restype = None
     return lib
 
 
@@ -395,6 +399,48 @@ def k_work(query_start_loc, seq_lens, max_num_work: int, compress_ratio: int = 4
     seq = np.ascontiguousarray(seq_lens, dtype=np.int32)
     out = np.empty((max_num_work, 2), np.int32)
     lib.oracle_k_work(_ptr(qsl), _ptr(seq), len(seq), compress_ratio, _ptr(out), max_num_work)
+    return out
+
+
+def ring_slots(query_start_loc, seq_lens, num_tokens: int, block_table, ring_size: int):
+    """int64 [num_tokens]: the raw-key ring row each token writes, or -1
+    (see oracle_ring_slots)."""
+    lib = load()
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    seq = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    assert bt.ndim == 2 and ring_size >= 1
+    out = np.empty(num_tokens, np.int64)
+    lib.oracle_ring_slots(_ptr(qsl), _ptr(seq), len(seq), num_tokens, _ptr(bt), bt.shape[1], bt.shape[1],
+                          int(ring_size), _ptr(out))
+    return out
+
+
+def write_keys(keys, slots, cache, fmt: str = "bf16", scale: float = 1.0, positions=None):
+    """Key rows written to cache rows (see oracle_write_keys), on a copy of
+    `cache`, which is returned.  keys: uint16 bf16 bits [T, 128]; slots:
+    int64 [T]; cache: [..., W] rows of uint16 (fmt "bf16", W >= 128, or
+    W >= 140 with positions) or uint8 e4m3 codes (fmt "fp8_e4m3", W >= 128);
+    positions: int64 [3, T] or None."""
+    lib = load()
+    k = np.ascontiguousarray(keys, dtype=np.uint16)
+    assert k.ndim == 2 and k.shape[1] == DIM
+    sl = np.ascontiguousarray(slots, dtype=np.int64)
+    assert sl.shape == (k.shape[0],)
+    out = np.array(cache, copy=True)
+    width = out.shape[-1]
+    if fmt == "fp8_e4m3":
+        assert out.dtype == np.uint8 and width >= DIM and positions is None
+        code = FORMATS["fp8_e4m3"][0]
+    else:
+        assert fmt == "bf16" and out.dtype == np.uint16 and width >= DIM
+        code = FORMATS["bf16"][0]
+    pos = None
+    if positions is not None:
+        pos = np.ascontiguousarray(positions, dtype=np.int64)
+        assert pos.shape == (3, k.shape[0]) and width >= DIM + 12
+    lib.oracle_write_keys(_ptr(k), DIM, k.shape[0], _ptr(sl), out.ctypes.data, code, width, out.size // width,
+                          float(np.float32(scale)), _ptr(pos), k.shape[0] if pos is not None else 0, 1)
     return out
 
 

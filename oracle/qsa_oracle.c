@@ -387,6 +387,80 @@ void oracle_k_work(const int32_t *query_start_loc, const int32_t *seq_lens, int3
 }
 
 /* ---------------------------------------------------------------------- */
+/* Raw-key ring and key-cache writes [QSA-CACHE: the circular branch of      */
+/* _build_qsa_metadata_kernel and circular_qsa_slot_mapping; the caches      */
+/* QSAKeyStateCache and QSACompressedKeyCache; QSA-PREP _to_dst_dtype].       */
+
+static uint8_t float_to_e4m3_bits(float f);  /* defined with the query preparation below */
+
+/* Ring slot of each query token.  Request r owns one ring of ring_size rows
+ * in block block_table[r][0]; block 0 is the null block, owned by dummy and
+ * padding requests, and is never written.  Token t of request r at logical
+ * position pos >= 0 writes row pos % ring_size of the ring when it is one
+ * of the last ring_size query tokens of its request (t + ring_size >= the
+ * request's query end): slot = block * ring_size + pos % ring_size.  -1 for
+ * every other token, for padding tokens and when the table has no
+ * columns. */
+void oracle_ring_slots(const int32_t *query_start_loc, const int32_t *seq_lens, int32_t num_reqs,
+                       int32_t num_tokens, const int32_t *block_table, int64_t block_table_stride,
+                       int32_t block_table_cols, int32_t ring_size, int64_t *slot_mapping)
+{
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        int64_t slot = -1;
+        for (int32_t r = 0; r < num_reqs; ++r) {
+            if (t < query_start_loc[r] || t >= query_start_loc[r + 1]) continue;
+            int64_t query_end = query_start_loc[r + 1];
+            int64_t query_len = query_end - query_start_loc[r];
+            int64_t pos = (int64_t)seq_lens[r] - query_len + (t - query_start_loc[r]);
+            if (pos < 0) break;
+            if ((int64_t)t + ring_size < query_end) break;
+            if (block_table_cols <= 0) break;
+            int64_t block = block_table[r * block_table_stride];
+            if (block <= 0) break;
+            slot = block * ring_size + pos % ring_size;
+            break;
+        }
+        slot_mapping[t] = slot;
+    }
+}
+
+/* Key rows written to cache rows.  Row t of keys (128 bf16 elements, rows
+ * key_stride elements apart) goes to cache row slots[t] when 0 <= slots[t]
+ * < num_slots; cache rows are row_stride elements of the cache's format
+ * apart, and rows no token writes are left as they are.  Cache format
+ * ORACLE_BF16: the bits as they are.  ORACLE_FP8_E4M3: each value divided
+ * by scale in fp32, then the nearest e4m3 code [_to_dst_dtype: round to
+ * bf16, which the keys already are, divide by the scale, convert].
+ * positions (bf16 caches only): NULL, or int64 positions of three axes
+ * (element a * pos_stride_axis + t * pos_stride_token) that follow the key
+ * in the row as three little-endian int64 from element 128
+ * [QSAKeyStateCache: raw bf16 key, then exact int64 MRoPE positions]. */
+void oracle_write_keys(const uint16_t *keys, int64_t key_stride, int32_t num_tokens, const int64_t *slots,
+                       void *cache, int cache_format, int64_t row_stride, int64_t num_slots, float scale,
+                       const int64_t *positions, int64_t pos_stride_axis, int64_t pos_stride_token)
+{
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        int64_t s = slots[t];
+        if (s < 0 || s >= num_slots) continue;
+        const uint16_t *src = keys + (int64_t)t * key_stride;
+        if (cache_format == ORACLE_FP8_E4M3) {
+            uint8_t *dst = (uint8_t *)cache + s * row_stride;
+            for (int d = 0; d < QSA_ORACLE_DIM; ++d)
+                dst[d] = float_to_e4m3_bits((float)bf16_bits_to_double(src[d]) / scale);
+        } else {
+            uint16_t *dst = (uint16_t *)cache + s * row_stride;
+            for (int d = 0; d < QSA_ORACLE_DIM; ++d) dst[d] = src[d];
+            if (positions) {
+                for (int a = 0; a < 3; ++a) {
+                    int64_t v = positions[a * pos_stride_axis + (int64_t)t * pos_stride_token];
+                    memcpy(dst + QSA_ORACLE_DIM + 4 * a, &v, sizeof v);
+                }
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Top-k block selection [MATE-QSA intro: the caller keeps the best blocks;  */
 /* "Core Attention": request-local int32 indices, -1 padding].              */
 

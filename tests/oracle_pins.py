@@ -157,6 +157,103 @@ def pin_prefill_intervals_golden():
     assert list(ke) == list(want[:, 5]), list(ke)
 
 
+def pin_ring_slots_golden():
+    """tests/golden/ring_slots.txt: ring rows of a decode, a speculative
+    decode, a prefill chunk longer than the ring, a request starting before
+    position 0, a request on the null block, an empty request and padding."""
+    head = {r[0]: [int(x) for x in r[1:]] for r in _read_golden("ring_slots.txt")}
+    bt = np.stack([head["block_col0"], head["block_col1"]], axis=1).astype(np.int32)
+    got = O.ring_slots(np.array(head["query_start_loc"], np.int32), np.array(head["seq_lens"], np.int32),
+                       head["num_tokens"][0], bt, head["ring_size"][0])
+    assert list(got) == head["slots"], list(got)
+
+
+def pin_ring_slots_counting():
+    """Random batches, characterised by counting: in every request with a
+    non-null block, exactly its last min(ring, query_len) tokens with a
+    position >= 0 get a slot, inside the request's own ring, at row pos %
+    ring, all distinct; every other token gets -1."""
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        R = int(rng.integers(1, 7))
+        ring = int(rng.choice([4, 8, 12]))
+        qlens = rng.integers(0, 20, R)
+        seq = np.maximum(qlens + rng.integers(-3, 50, R), 0).astype(np.int32)
+        qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+        T = int(qsl[-1]) + int(rng.integers(0, 4))
+        bt = rng.integers(0, 9, (R, 2)).astype(np.int32)
+        got = O.ring_slots(qsl, seq, T, bt, ring)
+        want = np.full(T, -1, np.int64)
+        for r in range(R):
+            block = int(bt[r, 0])
+            for i in range(int(qlens[r])):
+                t = int(qsl[r]) + i
+                pos = int(seq[r]) - int(qlens[r]) + i
+                if block > 0 and pos >= 0 and i >= int(qlens[r]) - ring:
+                    want[t] = block * ring + pos % ring
+        assert np.array_equal(got, want)
+        for r in range(R):
+            mine = got[qsl[r]:qsl[r + 1]]
+            mine = mine[mine >= 0]
+            assert len(set(mine.tolist())) == len(mine)
+            assert np.all(mine // ring == bt[r, 0])
+
+
+def pin_write_keys_labels():
+    """Labelled key rows: after the write, cache row s holds the key of the
+    token whose slot is s, rows no token names keep their sentinel, slots
+    outside the cache are skipped, and positions follow a ring row's key as
+    exact int64."""
+    rng = np.random.default_rng(12)
+    T, rows = 30, 48
+    keys = np.zeros((T, 128), np.uint16)
+    keys[:, 0] = np.arange(T) + 1
+    keys[:, 127] = 0x4000 + np.arange(T)
+    slots = rng.permutation(rows)[:T].astype(np.int64)
+    slots[3], slots[7], slots[11] = -1, rows, 1 << 40          # skipped
+    cache = np.full((6, 8, 1, 140), 0xBEEF, np.uint16)
+    pos = rng.integers(-(1 << 62), 1 << 62, (3, T)).astype(np.int64)
+    out = O.write_keys(keys, slots, cache, positions=pos).reshape(rows, 140)
+    written = set()
+    for t in range(T):
+        s = int(slots[t])
+        if 0 <= s < rows:
+            written.add(s)
+            assert np.array_equal(out[s, :128], keys[t])
+            assert np.array_equal(out[s, 128:140].copy().view(np.int64), pos[:, t])
+    for s in range(rows):
+        if s not in written:
+            assert np.all(out[s] == 0xBEEF)
+    plain = O.write_keys(keys, slots, np.full((rows, 128), 7, np.uint16))
+    for t in range(T):
+        if 0 <= int(slots[t]) < rows:
+            assert np.array_equal(plain[int(slots[t])], keys[t])
+
+
+def pin_write_keys_e4m3_matches_library():
+    """The e4m3 cache write [_to_dst_dtype]: each bf16 key value divided by
+    the scale in fp32, converted by torch's float8_e4m3fn (RNE) wherever the
+    quotient is below 448 in magnitude; larger quotients saturate to 448."""
+    import torch
+    rng = np.random.default_rng(13)
+    T = 64
+    keys = bf16_bits(rng.standard_normal((T, 128)).astype(np.float32) * 3.0)
+    keys[0, :4] = bf16_bits(np.array([0.0, -0.0, 1e-30, -7.5], np.float32))
+    keys[1, :3] = bf16_bits(np.array([100.0, -100.0, 3e38], np.float32))
+    scale = 0.0173
+    slots = np.arange(T, dtype=np.int64)
+    out = O.write_keys(keys, slots, np.zeros((T, 128), np.uint8), fmt="fp8_e4m3", scale=scale)
+    with np.errstate(over="ignore"):                      # 3e38 / scale: +inf, which saturates
+        q = (bits_to_f32(keys) / np.float32(scale)).astype(np.float32)
+    small = np.abs(q) < 448.0
+    lib = torch.from_numpy(np.where(small, q, 0.0).astype(np.float32)).to(torch.float8_e4m3fn)
+    assert np.array_equal(out[small], lib.view(torch.uint8).numpy()[small])
+    big = ~small
+    assert big.any()
+    assert np.all(out[big] & 0x7F == 0x7E)
+    assert np.array_equal(out[big] >> 7, (q[big] < 0).astype(np.uint8))
+
+
 def pin_visible_counts_complete_blocks():
     # Independent characterisation: the number of 4-token blocks whose last
     # token is at or before pos, among the blocks complete within seq_len.

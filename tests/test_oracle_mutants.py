@@ -38,6 +38,18 @@ MUTANTS = {
                                   "int32_t start = key_offsets[t % 4];"),
     "intervals_end_without_offset": ("row_k_end[t] = start + visible[t];", "row_k_end[t] = visible[t];"),
     "intervals_end_one_short": ("row_k_end[t] = start + visible[t];", "row_k_end[t] = start + visible[t] - 1;"),
+    "ring_null_block_written": ("if (block <= 0) break;\n            slot = block * ring_size", "if (block < 0) break;\n            slot = block * ring_size"),
+    "ring_every_token_writes": ("if ((int64_t)t + ring_size < query_end) break;", ""),
+    "ring_row_by_division": ("slot = block * ring_size + pos % ring_size;", "slot = block * ring_size + pos / ring_size;"),
+    "ring_column_one": ("int64_t block = block_table[r * block_table_stride];", "int64_t block = block_table[r * block_table_stride + 1];"),
+    "ring_negative_positions_written": ("if (pos < 0) break;\n            if ((int64_t)t + ring_size", "if (pos < -1) break;\n            if ((int64_t)t + ring_size"),
+    "write_e4m3_scale_multiplies": ("float_to_e4m3_bits((float)bf16_bits_to_double(src[d]) / scale)",
+                                    "float_to_e4m3_bits((float)bf16_bits_to_double(src[d]) * scale)"),
+    "write_positions_axes_swapped": ("int64_t v = positions[a * pos_stride_axis + (int64_t)t * pos_stride_token];",
+                                     "int64_t v = positions[(2 - a) * pos_stride_axis + (int64_t)t * pos_stride_token];"),
+    "write_slot_upper_bound_unchecked": ("if (s < 0 || s >= num_slots) continue;", "if (s < 0) continue;"),
+    "write_key_stride_ignored": ("const uint16_t *src = keys + (int64_t)t * key_stride;",
+                                 "const uint16_t *src = keys + (int64_t)t * 64;"),
     "prefill_absolute_columns": ("int64_t n = (int64_t)row_k_start[t] + c;", "int64_t n = c;"),
     "prefill_end_inclusive": ("n < row_k_end[t])", "n <= row_k_end[t])"),
     "prefill_no_lower_bound": ("if (n >= 0 && n < num_keys", "if (n >= -2 && n < num_keys"),
