@@ -91,6 +91,41 @@ __global__ __launch_bounds__(kWaves * 64) void gather_keys_kernel(GatherParams p
     }
 }
 
+// Key rows written to cache rows: the compressed-key cache
+// (QSACompressedKeyCache: one normed key per complete group, bf16 or e4m3)
+// and the raw-key ring (QSAKeyStateCache: raw bf16 keys, optionally followed
+// by the three int64 MRoPE positions), at the slots of the cache metadata.
+// Row t of the keys goes to cache row slots[t] when 0 <= slots[t] <
+// num_slots.  An e4m3 cache takes each bf16 value divided by the scale in
+// fp32, rounded to the nearest e4m3 value with ties to even and saturated
+// at 448 (qsa_prepare's _to_dst_dtype; the keys are bf16 already).  Half a
+// wavefront moves one row: 32 lanes of 4 elements (8 bytes in; 8 bytes out,
+// or 4 e4m3 bytes), lanes 0..2 also the positions.
+constexpr int kWriteThreads = 256;
+
+template <bool kFp8, bool kPositions>
+__global__ __launch_bounds__(kWriteThreads) void write_keys_kernel(WriteKeysParams p) {
+    const int64_t t = ((int64_t)blockIdx.x * kWriteThreads + threadIdx.x) / 32;
+    const int l = threadIdx.x & 31;
+    if (t >= p.num_tokens) return;
+    const int64_t s = p.slots[t];
+    if (s < 0 || s >= p.num_slots) return;
+    const uint2 v = *reinterpret_cast<const uint2 *>(p.keys + t * p.key_stride + 4 * l);
+    if constexpr (kFp8) {
+        const float f[4] = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                            __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w |= e4m3_rne_sat(f[i] / p.scale) << (8 * i);
+        *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(p.cache) + s * p.row_stride + 4 * l) = w;
+    } else {
+        uint16_t *row = static_cast<uint16_t *>(p.cache) + s * p.row_stride;
+        *reinterpret_cast<uint2 *>(row + 4 * l) = v;
+        if (kPositions && l < 3)
+            *reinterpret_cast<int64_t *>(row + kDim + 4 * l) = p.positions[l * p.pos_stride_axis + t * p.pos_stride_token];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gather_keys(const GatherParams &p, hipStream_t stream) {
@@ -112,6 +147,14 @@ hipError_t launch_gather_keys(const GatherParams &p, hipStream_t stream) {
     }
     if (one_page) return launch_kernel(gather_keys_kernel<256, 256, 0, true>, grid, block, stream, p);
     return launch_kernel(gather_keys_kernel<256, 256, 0, false>, grid, block, stream, p);
+}
+
+hipError_t launch_write_keys(const WriteKeysParams &p, hipStream_t stream) {
+    const dim3 grid((unsigned)(((int64_t)p.num_tokens * 32 + kWriteThreads - 1) / kWriteThreads));
+    const dim3 block(kWriteThreads);
+    if (p.fp8) return launch_kernel(write_keys_kernel<true, false>, grid, block, stream, p);
+    if (p.positions) return launch_kernel(write_keys_kernel<false, true>, grid, block, stream, p);
+    return launch_kernel(write_keys_kernel<false, false>, grid, block, stream, p);
 }
 
 }  // namespace qsa

@@ -100,6 +100,29 @@ __global__ __launch_bounds__(kThreads) void cache_slots_kernel(CacheMetaParams p
     p.slot_mapping[t] = slot;
 }
 
+// Raw-key ring slot of each token (vLLM qsa_cache.py, the circular branch
+// of _build_qsa_metadata_kernel; circular_qsa_slot_mapping): request r owns
+// one ring of ring_size rows in block block_table[r][0], block 0 being the
+// null block that is never written; a query token at logical position
+// pos >= 0 among the last ring_size query tokens of its request writes row
+// pos % ring_size.  -1 otherwise and for padding tokens.
+__global__ __launch_bounds__(kThreads) void ring_slots_kernel(RingSlotParams p) {
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t >= p.num_tokens) return;
+    int64_t slot = -1;
+    const int req = token_request(p.query_start_loc, p.num_reqs, t);
+    if (req >= 0 && p.block_table_cols > 0) {
+        const int64_t qs = p.query_start_loc[req];
+        const int64_t qe = p.query_start_loc[req + 1];
+        const int64_t pos = (int64_t)p.seq_lens[req] - (qe - qs) + (t - qs);
+        if (pos >= 0 && t + p.ring_size >= qe) {
+            const int64_t block = p.block_table[(int64_t)req * p.block_table_stride];
+            if (block > 0) slot = block * p.ring_size + pos % p.ring_size;
+        }
+    }
+    p.slot_mapping[t] = slot;
+}
+
 // Work items of the compressed-cache writer (_build_qsa_metadata_kernel,
 // k_work_metadata): a request with query tokens owns max(groups, 1) items,
 // groups = seq_len/cr - (seq_len - query_len)/cr (floor division), numbered
@@ -186,6 +209,11 @@ __global__ __launch_bounds__(kThreads) void decode_visible_kernel(DecodeVisibleP
 
 hipError_t launch_cache_slots(const CacheMetaParams &p, hipStream_t stream) {
     return launch_kernel(cache_slots_kernel, dim3((unsigned)((p.num_tokens + kThreads - 1) / kThreads)),
+                         dim3(kThreads), stream, p);
+}
+
+hipError_t launch_ring_slots(const RingSlotParams &p, hipStream_t stream) {
+    return launch_kernel(ring_slots_kernel, dim3((unsigned)((p.num_tokens + kThreads - 1) / kThreads)),
                          dim3(kThreads), stream, p);
 }
 

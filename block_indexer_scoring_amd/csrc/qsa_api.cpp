@@ -242,6 +242,65 @@ int qsa_build_cache_metadata(const int32_t *query_start_loc, const int32_t *seq_
     return device_status(fn, err);
 }
 
+int qsa_build_ring_slots(const int32_t *query_start_loc, const int32_t *seq_lens, int32_t num_reqs,
+                         int32_t num_tokens, const int32_t *block_table, int64_t block_table_stride,
+                         int32_t block_table_cols, int32_t ring_size, int64_t *slot_mapping, void *stream) {
+    const char *fn = "qsa_build_ring_slots";
+    if (num_reqs < 0 || num_tokens < 0 || block_table_cols < 0)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative count", fn);
+    if (ring_size < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: ring_size < 1", fn);
+    if (num_reqs > 1 && block_table_cols > 0 && block_table_stride < block_table_cols)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: block_table_stride < block_table_cols", fn);
+    if (num_tokens == 0) return ok();
+    if (!query_start_loc || !slot_mapping) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL query_start_loc or slot_mapping", fn);
+    if (num_reqs > 0 && !seq_lens) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL seq_lens", fn);
+    if (num_reqs > 0 && block_table_cols > 0 && !block_table)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL block_table", fn);
+    qsa::RingSlotParams p{query_start_loc, seq_lens, num_reqs, num_tokens, block_table, block_table_stride,
+                          block_table ? block_table_cols : 0, ring_size, slot_mapping};
+    return device_status(fn, qsa::launch_ring_slots(p, static_cast<hipStream_t>(stream)));
+}
+
+int qsa_write_keys(const void *keys, int64_t key_stride, int32_t num_tokens, const int64_t *slots, void *cache,
+                   int32_t cache_dtype, int64_t row_stride, int64_t num_slots, float scale, const int64_t *positions,
+                   int64_t pos_stride_axis, int64_t pos_stride_token, void *stream) {
+    const char *fn = "qsa_write_keys";
+    if (cache_dtype != QSA_DTYPE_BF16 && cache_dtype != QSA_DTYPE_FP8_E4M3)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: cache format %d is not bf16 or e4m3", fn, cache_dtype);
+    const bool fp8 = cache_dtype == QSA_DTYPE_FP8_E4M3;
+    if (num_tokens < 0 || num_slots < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+    if (fp8 && !(std::isfinite(scale) && scale > 0.0f))
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: scale must be finite and > 0 for an e4m3 cache", fn);
+    if (positions && fp8) return fail(QSA_ERR_UNSUPPORTED, "%s: positions go with a bf16 cache only", fn);
+    const int64_t min_row = positions ? 128 + 12 : 128;
+    if (row_stride < min_row)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: row_stride %lld below the %lld elements a row needs", fn,
+                    (long long)row_stride, (long long)min_row);
+    if (num_tokens > 1 && key_stride < 128) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: key_stride < 128", fn);
+    if (num_tokens == 0 || num_slots == 0) return ok();
+    if (!keys || !slots || !cache) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL keys, slots or cache", fn);
+    if (!aligned(keys, 8) || (num_tokens > 1 && key_stride % 4 != 0) || !aligned(cache, 8) || row_stride % 4 != 0 ||
+        !aligned(slots, 8) || (positions && !aligned(positions, 8)))
+        return fail(QSA_ERR_LAYOUT, "%s: keys, slots, cache and positions must be 8-byte aligned and the key and "
+                                    "cache row strides multiples of 4 elements (8-byte moves)", fn);
+    if (num_slots > ((int64_t)1 << 50) / row_stride) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: cache too large", fn);
+    if ((int64_t)num_tokens * 32 >= INT32_MAX) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
+    qsa::WriteKeysParams p{};
+    p.keys = static_cast<const uint16_t *>(keys);
+    p.key_stride = num_tokens > 1 ? key_stride : 128;
+    p.num_tokens = num_tokens;
+    p.slots = slots;
+    p.cache = cache;
+    p.row_stride = row_stride;
+    p.num_slots = num_slots;
+    p.fp8 = fp8;
+    p.scale = scale;
+    p.positions = positions;
+    p.pos_stride_axis = pos_stride_axis;
+    p.pos_stride_token = pos_stride_token;
+    return device_status(fn, qsa::launch_write_keys(p, static_cast<hipStream_t>(stream)));
+}
+
 int qsa_gather_keys(const void *k_cache, int32_t k_dtype, int64_t num_pages, int32_t page_size,
                     const int32_t *page_table, int64_t page_table_stride, int32_t page_table_cols,
                     const int32_t *key_counts, const int32_t *key_offsets, int32_t num_reqs, int32_t max_keys,

@@ -123,4 +123,20 @@ __device__ __forceinline__ u32x4 e4m3x8_to_16bit(uint32_t w0, uint32_t w1) {
     return r;
 }
 
+// Nearest finite OCP e4m3 value, ties to the even code; NaN -> 0x7f (the
+// e4m3 store of qsa_prepare's _to_dst_dtype: magnitudes from 448 up,
+// infinities included, saturate to 448).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return 0x7fu;
+    if (a >= 0x43e00000u) return sign | 0x7eu;  // >= 448, infinities included
+    if (a < 0x3c800000u)                         // below 2^-6: multiples of 2^-9
+        return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;  // biased exponent and 3 fraction bits
+    const uint32_t code = r - ((127u - 7u) << 3);
+    return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
 }  // namespace qsa

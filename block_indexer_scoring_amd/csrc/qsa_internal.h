@@ -140,6 +140,28 @@ struct CacheMetaParams {
 };
 constexpr int kCacheMetaMaxReqs = 8192;  // requests one work-item block scans in LDS
 
+struct RingSlotParams {
+    const int32_t *query_start_loc, *seq_lens;
+    int32_t num_reqs, num_tokens;
+    const int32_t *block_table;
+    int64_t block_table_stride;
+    int32_t block_table_cols, ring_size;
+    int64_t *slot_mapping;
+};
+
+struct WriteKeysParams {
+    const uint16_t *keys;               // bf16 [num_tokens][key_stride]
+    int64_t key_stride;
+    int32_t num_tokens;
+    const int64_t *slots;               // [num_tokens]
+    void *cache;                        // rows of row_stride elements (bf16 or e4m3 codes)
+    int64_t row_stride, num_slots;
+    int32_t fp8;                        // e4m3 cache
+    float scale;                        // e4m3: value / scale
+    const int64_t *positions;           // null, or int64 [3 axes] after each bf16 key
+    int64_t pos_stride_axis, pos_stride_token;
+};
+
 struct GatherParams {
     const uint8_t *k_cache;              // [num_pages][page_size][row_bytes]
     int32_t row_bytes;                   // 256 (2-byte elements) or 128 (e4m3)
@@ -210,6 +232,8 @@ hipError_t launch_decode_visible(const DecodeVisibleParams &p, hipStream_t strea
 hipError_t launch_cache_slots(const CacheMetaParams &p, hipStream_t stream);  // p.slot_mapping set
 hipError_t launch_k_work(const CacheMetaParams &p, hipStream_t stream);       // p.k_work set
 hipError_t launch_gather_keys(const GatherParams &p, hipStream_t stream);
+hipError_t launch_ring_slots(const RingSlotParams &p, hipStream_t stream);
+hipError_t launch_write_keys(const WriteKeysParams &p, hipStream_t stream);
 hipError_t launch_prepare_q(const PrepareQParams &p, hipStream_t stream);
 
 }  // namespace qsa

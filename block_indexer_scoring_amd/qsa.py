@@ -21,14 +21,15 @@ QSA_ERR_INVALID_ARGUMENT = 1
 QSA_ERR_UNSUPPORTED = 2
 QSA_ERR_LAYOUT = 3
 QSA_ERR_DEVICE = 4
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_set_launch_events", "qsa_split_batch",
            "qsa_build_metadata", "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks",
            "qsa_mqa_prefill_topk", "qsa_prefill_topk_workspace_bytes", "qsa_mqa_decode_typed",
            "qsa_mqa_prefill_typed", "qsa_build_cache_metadata", "qsa_gather_keys", "qsa_prepare_q",
            "qsa_decode_plan_bytes", "qsa_build_decode_plan", "qsa_mqa_decode_planned",
-           "qsa_decode_visible_blocks", "qsa_mqa_decode_static_plan")
+           "qsa_decode_visible_blocks", "qsa_mqa_decode_static_plan", "qsa_build_ring_slots",
+           "qsa_write_keys")
 
 # enum qsa_dtype
 QSA_DTYPE_BF16 = 0
@@ -101,6 +102,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_mqa_decode_static_plan.argtypes = [P, i32, i64, i64, i64, P, i32, f32, i64, i32, P, i64, i32, P, P,
                                                i32, i32, i32, i32, f32, P, i64, i32, P]
     lib.qsa_mqa_decode_static_plan.restype = ctypes.c_int
+    lib.qsa_build_ring_slots.argtypes = [P, P, i32, i32, P, i64, i32, i32, P, P]
+    lib.qsa_build_ring_slots.restype = ctypes.c_int
+    lib.qsa_write_keys.argtypes = [P, i64, i32, P, P, i32, i64, i64, f32, P, i64, i64, P]
+    lib.qsa_write_keys.restype = ctypes.c_int
     lib.qsa_decode_plan_bytes.argtypes = [i32, i32, P]
     lib.qsa_decode_plan_bytes.restype = ctypes.c_int
     lib.qsa_build_decode_plan.argtypes = [P, P, i64, i32, i64, i32, i32, i32, P, i64, P]
@@ -340,6 +345,51 @@ def qsa_build_cache_metadata(query_start_loc: torch.Tensor, seq_lens: torch.Tens
         block_table.stride(0), block_table.shape[1], storage_block_size, _ptr(common_slot_mapping),
         _ptr(slot_mapping), _ptr(k_work), max_num_work if k_work is not None else 0, _stream_handle(stream)))
     return slot_mapping, k_work
+
+
+def qsa_build_ring_slots(query_start_loc: torch.Tensor, seq_lens: torch.Tensor, num_tokens: int,
+                         block_table: torch.Tensor, ring_size: int, stream=None) -> torch.Tensor:
+    """int64 [num_tokens]: the raw-key ring slot of each query token, or -1."""
+    lib = load_library()
+    _gpu("query_start_loc", query_start_loc, torch.int32)
+    _gpu("seq_lens", seq_lens, torch.int32)
+    _gpu("block_table", block_table, torch.int32)
+    assert query_start_loc.is_contiguous() and seq_lens.is_contiguous()
+    if block_table.dim() != 2 or (block_table.shape[1] > 1 and block_table.stride(1) != 1):
+        raise ValueError("block_table must be [R, W] with unit column stride")
+    num_reqs = seq_lens.numel()
+    out = torch.empty(int(num_tokens), dtype=torch.int64, device=seq_lens.device)
+    _check(lib.qsa_build_ring_slots(_ptr(query_start_loc), _ptr(seq_lens), num_reqs, int(num_tokens),
+                                    _ptr(block_table), block_table.stride(0), block_table.shape[1], int(ring_size),
+                                    _ptr(out), _stream_handle(stream)))
+    return out
+
+
+def qsa_write_keys(keys: torch.Tensor, slots: torch.Tensor, cache: torch.Tensor, scale: float = 1.0,
+                   positions: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Write bf16 key rows [T, >=128] to the rows of `cache` ([..., W]: bf16,
+    or float8_e4m3fn for an e4m3 cache; contiguous) named by int64 slots [T];
+    positions: int64 [3, T] (bf16 caches with W >= 140) or None.  In place;
+    returns cache."""
+    lib = load_library()
+    _gpu("keys", keys, torch.bfloat16)
+    _gpu("slots", slots, torch.int64)
+    fmt = _gpu_format("cache", cache, (torch.bfloat16, torch.float8_e4m3fn))
+    if keys.dim() != 2 or keys.stride(1) != 1 or not slots.is_contiguous() or slots.numel() != keys.shape[0]:
+        raise ValueError("keys must be [T, >=128] with unit feature stride and slots a contiguous [T] tensor")
+    if not cache.is_contiguous():
+        raise ValueError("cache must be contiguous")
+    width = cache.shape[-1]
+    pa, pt = 0, 0
+    if positions is not None:
+        _gpu("positions", positions, torch.int64)
+        if positions.dim() != 2 or positions.shape != (3, keys.shape[0]):
+            raise ValueError("positions must be [3, T]")
+        pa, pt = positions.stride(0), positions.stride(1)
+    _check(lib.qsa_write_keys(_ptr(keys), keys.stride(0), keys.shape[0], _ptr(slots), _ptr(cache), fmt, width,
+                              cache.numel() // max(width, 1), float(scale), _ptr(positions), pa, pt,
+                              _stream_handle(stream)))
+    return cache
 
 
 def qsa_gather_keys(k_cache: torch.Tensor, page_table: torch.Tensor, key_counts: torch.Tensor,

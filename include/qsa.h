@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 9
+#define QSA_ABI_VERSION 10
 
 enum qsa_status {
     QSA_OK = 0,
@@ -196,6 +196,73 @@ int qsa_build_cache_metadata(const int32_t *query_start_loc, const int32_t *seq_
                              int32_t block_table_cols, int32_t storage_block_size,
                              const int64_t *common_slot_mapping, int64_t *slot_mapping,
                              int32_t *k_work, int32_t max_num_work, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Cache updates upstream of the scores: the raw-key ring (the compressor's
+ * state) and the compressed-key cache.
+ *
+ * qsa_build_ring_slots -- the raw-key ring row each query token writes.
+ *   Source: vLLM qsa_cache.py, the circular branch of
+ *   _build_qsa_metadata_kernel and circular_qsa_slot_mapping; the ring's
+ *   capacity in QSAKeyStateCache (compress_ratio plus the speculative
+ *   tokens, rounded up to whole groups).
+ *   Request r owns one ring of ring_size rows in block block_table[r][0];
+ *   block 0 is the null block of dummy and padding requests and is never
+ *   written.  A query token at logical position pos = seq_len - query_len +
+ *   (t - query_start) >= 0 that is one of the last ring_size query tokens of
+ *   its request writes slot block * ring_size + pos % ring_size; every other
+ *   token (and padding past query_start_loc[num_reqs], and every token when
+ *   the table has no columns) gets -1.
+ *   query_start_loc : device int32 [num_reqs+1];  seq_lens : device int32 [num_reqs]
+ *   block_table     : device int32 [num_reqs][block_table_cols], row stride
+ *                     block_table_stride (only column 0 is read)
+ *   slot_mapping    : device int64 [num_tokens] out
+ *   Errors: INVALID_ARGUMENT for negative counts, ring_size < 1, a short
+ *   block_table_stride or a NULL pointer that has work to feed.  One kernel.
+ */
+int qsa_build_ring_slots(const int32_t *query_start_loc, const int32_t *seq_lens, int32_t num_reqs,
+                         int32_t num_tokens, const int32_t *block_table, int64_t block_table_stride,
+                         int32_t block_table_cols, int32_t ring_size, int64_t *slot_mapping,
+                         void *stream);
+
+/* qsa_write_keys -- key rows written to cache rows at given slots.
+ *   Source: vLLM qsa_cache.py, QSACompressedKeyCache (one normed key per
+ *   complete group, at the slots of compressed_qsa_slot_mapping /
+ *   qsa_build_cache_metadata) and QSAKeyStateCache (raw bf16 keys,
+ *   optionally followed by exact int64 MRoPE positions, at the ring slots);
+ *   qsa_prepare's _to_dst_dtype for an fp8 cache (round to bf16, divide by
+ *   the cache scale, convert to e4m3).  The keys themselves (the raw keys,
+ *   or the compressed ones, whose 4 -> 1 compression is not on the pages)
+ *   are the caller's.
+ *   keys       : device bf16 [num_tokens][key_stride] (128 used per row),
+ *                8-byte aligned, key_stride a multiple of 4.
+ *   slots      : device int64 [num_tokens]: row t goes to cache row slots[t]
+ *                when 0 <= slots[t] < num_slots; other tokens write nothing.
+ *                Two tokens naming one slot race (unspecified winner).
+ *   cache      : device rows of row_stride elements of cache_dtype, 8-byte
+ *                aligned (a paged cache [pages][page_size][1][W] is
+ *                pages * page_size rows of stride W); rows no token names
+ *                are left as they are.
+ *   cache_dtype: QSA_DTYPE_BF16 (the bits as they are) or
+ *                QSA_DTYPE_FP8_E4M3 (each value divided by `scale` in fp32
+ *                and rounded to the nearest e4m3 code, ties to even,
+ *                saturating at 448; NaN gives 0x7F).
+ *   row_stride : elements per cache row, a multiple of 4, at least 128
+ *                (140 with positions).
+ *   positions  : NULL, or (bf16 caches) device int64 [3 axes][num_tokens] at
+ *                element a * pos_stride_axis + t * pos_stride_token: written
+ *                after the key as three little-endian int64 from element 128
+ *                of the row (QSAKeyStateCache's rope_position_offset), 8-byte
+ *                aligned.
+ *   Errors: UNSUPPORTED for another cache format or positions with an e4m3
+ *   cache; INVALID_ARGUMENT for negative sizes, a short row or key stride,
+ *   a bad scale (e4m3) or a NULL pointer that has work to feed; LAYOUT for
+ *   misaligned pointers or strides.  One kernel.
+ */
+int qsa_write_keys(const void *keys, int64_t key_stride, int32_t num_tokens, const int64_t *slots,
+                   void *cache, int32_t cache_dtype, int64_t row_stride, int64_t num_slots, float scale,
+                   const int64_t *positions, int64_t pos_stride_axis, int64_t pos_stride_token,
+                   void *stream);
 
 /* ------------------------------------------------------------------------
  * qsa_gather_keys -- paged compressed keys gathered into contiguous rows,

@@ -390,6 +390,57 @@ def test_decode_visible_blocks_nothing_to_do(lib):
     assert lib.qsa_decode_visible_blocks(None, 5, 4, None, None, None) == 0
 
 
+def _write_keys(lib, **kw):
+    a = dict(keys=FAKE, ks=128, T=10, slots=FAKE, cache=FAKE, dtype=0, rs=128, ns=100, scale=1.0, pos=None, pa=0, pt=0)
+    a.update(kw)
+    return lib.qsa_write_keys(a["keys"], a["ks"], a["T"], a["slots"], a["cache"], a["dtype"], a["rs"], a["ns"],
+                              a["scale"], a["pos"], a["pa"], a["pt"], None)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(dtype=1), 2, "cache format"),
+    (dict(dtype=3), 2, "cache format"),
+    (dict(dtype=2, pos=FAKE, rs=140), 2, "positions"),
+    (dict(dtype=2, scale=0.0), 1, "scale"),
+    (dict(dtype=2, scale=float("nan")), 1, "scale"),
+    (dict(T=-1), 1, "negative"),
+    (dict(ns=-1), 1, "negative"),
+    (dict(rs=120), 1, "row_stride"),
+    (dict(rs=136, pos=FAKE), 1, "row_stride"),
+    (dict(ks=64), 1, "key_stride"),
+    (dict(keys=None), 1, "NULL"),
+    (dict(slots=None), 1, "NULL"),
+    (dict(cache=None), 1, "NULL"),
+    (dict(keys=FAKE + 4), 3, "aligned"),
+    (dict(ks=130), 3, "aligned"),
+    (dict(rs=130), 3, "aligned"),
+    (dict(cache=FAKE + 2), 3, "aligned"),
+])
+def test_write_keys_rejects(lib, kw, code, text):
+    assert _write_keys(lib, **kw) == code
+    assert text in _err(lib)
+
+
+def test_write_keys_and_ring_slots_nothing_to_do(lib):
+    assert _write_keys(lib, T=0, keys=None, slots=None, cache=None) == 0
+    assert _write_keys(lib, ns=0, keys=None, slots=None, cache=None) == 0
+    assert lib.qsa_build_ring_slots(None, None, 0, 0, None, 0, 0, 8, None, None) == 0
+
+
+@pytest.mark.parametrize("args,code,text", [
+    ((FAKE, FAKE, -1, 4, FAKE, 2, 2, 8, FAKE), 1, "negative"),
+    ((FAKE, FAKE, 2, 4, FAKE, 2, 2, 0, FAKE), 1, "ring_size"),
+    ((FAKE, FAKE, 2, 4, FAKE, 1, 2, 8, FAKE), 1, "block_table_stride"),
+    ((None, FAKE, 2, 4, FAKE, 2, 2, 8, FAKE), 1, "NULL"),
+    ((FAKE, FAKE, 2, 4, FAKE, 2, 2, 8, None), 1, "NULL"),
+    ((FAKE, None, 2, 4, FAKE, 2, 2, 8, FAKE), 1, "NULL seq_lens"),
+    ((FAKE, FAKE, 2, 4, None, 2, 2, 8, FAKE), 1, "NULL block_table"),
+])
+def test_ring_slots_rejects(lib, args, code, text):
+    assert lib.qsa_build_ring_slots(*args, None) == code
+    assert text in _err(lib)
+
+
 def test_decode_zero_work_is_ok_without_device(lib):
     assert _decode(lib, num_reqs=0, q=None, comp=None, out=None) == 0
     assert _decode(lib, out_cols=0, out_stride=0, q=None, out=None) == 0

@@ -8,7 +8,7 @@ import torch
 from oracle import oracle as O
 from tests.oracle_pins import _CM_BT, _CM_QSL, _CM_SEQ, _read_golden
 from tests.parity import bf16_to_device, f32_bits, i32_to_device
-from workloads import FP8_K_SCALE, WORKLOADS, decode_inputs, fp8_e4m3_cache
+from workloads import FP8_K_SCALE, WORKLOADS, bf16_bits, decode_inputs, fp8_e4m3_cache
 
 pytestmark = pytest.mark.gpu
 
@@ -200,3 +200,115 @@ def test_prefill_over_widened_e4m3_cache():
                           inp.out_cols, k_scale=FP8_K_SCALE, rows=rows)
     assert_scores_match(pre[torch.from_numpy(rows).cuda()], ref, "prefill over the widened e4m3 cache")
     assert_scores_match(pre, dec.cpu().numpy(), "prefill vs e4m3 decode")
+
+
+# ----------------------------------------------------------------------------
+# Raw-key ring slots and key-cache writes
+
+
+def test_ring_slots_golden_batch():
+    qsa = _qsa()
+    head = {r[0]: [int(x) for x in r[1:]] for r in _read_golden("ring_slots.txt")}
+    bt = np.stack([head["block_col0"], head["block_col1"]], axis=1).astype(np.int32)
+    got = qsa.qsa_build_ring_slots(i32_to_device(head["query_start_loc"]), i32_to_device(head["seq_lens"]),
+                                   head["num_tokens"][0], i32_to_device(bt), head["ring_size"][0])
+    torch.cuda.synchronize()
+    assert got.cpu().numpy().tolist() == head["slots"]
+
+
+@pytest.mark.parametrize("seed,n,ring", [(1, 7, 8), (2, 300, 4), (3, 8192, 12)])
+def test_ring_slots_random_batches(seed, n, ring):
+    qsa = _qsa()
+    rng = np.random.default_rng(seed)
+    qlens = rng.integers(0, 10, n)
+    qlens[rng.integers(0, n)] = 700                         # one long prefill chunk
+    seqs = np.maximum(qlens + rng.integers(-4, 5000, n), 0).astype(np.int32)
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qsl[-1]) + 21                                   # padding tokens
+    bt = rng.integers(0, 1 << 20, (n, 3)).astype(np.int32)
+    bt[rng.random(n) < 0.1, 0] = 0                          # null blocks
+    got = qsa.qsa_build_ring_slots(i32_to_device(qsl), i32_to_device(seqs), T, i32_to_device(bt), ring)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), O.ring_slots(qsl, seqs, T, bt, ring))
+
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt,width,with_pos", [("bf16", 128, False), ("bf16", 140, True), ("bf16", 136, False),
+                                                ("fp8_e4m3", 128, False), ("fp8_e4m3", 132, False)])
+def test_write_keys_matches_oracle(fmt, width, with_pos):
+    qsa = _qsa()
+    rng = np.random.default_rng(width + len(fmt))
+    T, rows = 1500, 2048
+    keys = bf16_bits_noise(rng, T)
+    keys[5, :4] = bf16_bits(np.array([0.0, -0.0, 3e38, -1e-30], np.float32))
+    slots = rng.permutation(rows + 200)[:T].astype(np.int64) - 100   # some negative, some past the cache
+    pos = rng.integers(-(1 << 62), 1 << 62, (3, T)).astype(np.int64) if with_pos else None
+    scale = 0.0173 if fmt == "fp8_e4m3" else 1.0
+    if fmt == "bf16":
+        cache0 = rng.integers(0, 1 << 16, (rows, width)).astype(np.uint16)
+        dev = torch.from_numpy(cache0.view(np.int16)).to("cuda").view(torch.bfloat16)
+    else:
+        cache0 = rng.integers(0, 256, (rows, width)).astype(np.uint8)
+        dev = torch.from_numpy(cache0).to("cuda").view(torch.float8_e4m3fn)
+    key_dev = _bf16_dev(np.pad(keys, ((0, 0), (0, 8))))[:, :128]      # a padded row stride
+    pos_dev = None if pos is None else torch.from_numpy(pos).to("cuda")
+    qsa.qsa_write_keys(key_dev, torch.from_numpy(slots).to("cuda"), dev, scale=scale, positions=pos_dev)
+    torch.cuda.synchronize()
+    got = dev.view(torch.int16 if fmt == "bf16" else torch.uint8).cpu().numpy()
+    want = O.write_keys(keys, slots, cache0, fmt=fmt, scale=scale, positions=pos)
+    assert np.array_equal(got.view(want.dtype), want)
+
+
+def bf16_bits_noise(rng, T):
+    from workloads import normal_bf16
+    return normal_bf16(rng, (T, 128))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3"])
+def test_compressed_keys_round_trip_through_decode(fmt):
+    """A step's compressed keys written at the cache slots of
+    qsa_build_cache_metadata into a paged cache that holds earlier keys,
+    then decode over that cache: equal to the oracle's write and decode."""
+    qsa = _qsa()
+    rng = np.random.default_rng(51)
+    R, ps, cr = 6, 16, 4
+    qlens = np.array([4, 4, 4, 4, 37, 1], np.int64)            # decodes of DQL 4, a prefill chunk, one token
+    seqs = np.array([403, 64, 1000, 7, 900, 129], np.int32)
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qsl[-1])
+    cols = int(seqs.max()) // cr // ps + 1
+    pages = R * cols + 3
+    bt = rng.permutation(pages)[:R * cols].reshape(R, cols).astype(np.int32)
+    slots_dev, _ = qsa.qsa_build_cache_metadata(i32_to_device(qsl), i32_to_device(seqs), T, i32_to_device(bt), ps, cr,
+                                                slot_mapping=torch.empty(T, dtype=torch.int64, device="cuda"))
+    slots = O.cache_slots(qsl, seqs, T, bt, ps, cr)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots_dev.cpu().numpy(), slots)
+    new_keys = bf16_bits_noise(rng, T)
+    old = bf16_bits_noise(rng, pages * ps).reshape(pages, ps, 1, 128)   # earlier steps' keys
+    scale = FP8_K_SCALE
+    if fmt == "bf16":
+        cache0, dev = old, bf16_to_device(old)
+    else:
+        cache0 = fp8_e4m3_cache(old)
+        dev = torch.from_numpy(cache0).to("cuda").view(torch.float8_e4m3fn)
+    qsa.qsa_write_keys(_bf16_dev(new_keys), slots_dev, dev, scale=scale)
+    want_cache = O.write_keys(new_keys, slots, cache0, fmt=fmt, scale=scale)
+    # Decode rows of the first four requests (DQL 4) over the updated cache.
+    dec_q = bf16_bits_noise(rng, 4 * 4 * 4).reshape(4, 4, 4, 128)
+    comp = O.comp_lens(seqs[:4])
+    dqsl = (np.arange(5) * 4).astype(np.int32)
+    _, _, vis = O.token_metadata(dqsl, seqs[:4], 16)
+    out = torch.full((16, 260), float("nan"), device="cuda")
+    qsa.qsa_mqa_decode_typed(bf16_to_device(dec_q), dev, i32_to_device(bt[:4]), i32_to_device(comp),
+                             i32_to_device(vis), k_scale=scale if fmt == "fp8_e4m3" else 1.0, out=out)
+    torch.cuda.synchronize()
+    got_cache = dev.view(torch.int16 if fmt == "bf16" else torch.uint8).cpu().numpy()
+    assert np.array_equal(got_cache.view(want_cache.dtype), want_cache)
+    ref = O.decode_typed(dec_q, "bf16", want_cache, fmt, bt[:4], comp, vis, 260,
+                         k_scale=scale if fmt == "fp8_e4m3" else 1.0)
+    from tests.parity import assert_scores_match
+    assert_scores_match(out, ref, f"round trip {fmt}")
