@@ -13,18 +13,23 @@
 // needed; a cell is picked if key > T, or key == T and fewer than `need`
 // equal keys precede it.
 //
-// Rows up to 32768 columns stay in registers, each thread owning a
-// contiguous run of columns (kept as the keys' top 16 bits), so thread order
-// is column order and the picks are placed with a single prefix sum.
-// Before the select, a floor F is taken from the maxima of four sub-runs per
-// thread: each maximum is a distinct key, so when k of them are >= F at least
-// k keys are, and T >= F.  The keys >= F (a few hundred for score rows) are
-// compacted in column order into an LDS list, and one wave runs the select
-// over the list without workgroup barriers: 11 + 5 bits on the top halves,
-// then, only if some of the keys sharing T's top half are left out, those
-// keys are re-read in full and two 8-bit passes finish T.  If the list would
-// overflow, the select runs over the row itself.  Longer rows are re-read
-// from memory in each phase.
+// Rows up to 32768 columns stay in registers (as the keys' top 16 bits).
+// Thread t of a workgroup of n threads holds the 4-column chunks t, t + n,
+// t + 2n, ...: each of its 16-byte loads is part of one contiguous read of
+// 16n bytes by the workgroup, so every 128-byte line is fetched by one
+// instruction.  Before the select, a floor F is taken from the maxima of
+// four sub-sets of each thread's keys: each maximum is a distinct key, so
+// when k of them are >= F at least k keys are, and T >= F.  The keys >= F (a
+// few hundred for score rows) are compacted in column order into an LDS
+// list: column order is chunk-major, so each wave's segment of each chunk is
+// placed by a DPP scan of per-lane counts and a scan over the per-(chunk,
+// wave) totals.  One wave runs the select over the list without workgroup
+// barriers: 11 + 5 bits on the top halves, then, only if some of the keys
+// sharing T's top half are left out, those keys are re-read in full and two
+// 8-bit passes finish T.  The picks are placed from the list, in column
+// order, with a single prefix sum.  Rows with at most k candidates, and
+// lists that would overflow, re-read the row as one contiguous run of
+// columns per thread.  Longer rows are re-read from memory in each phase.
 #include <climits>
 
 #include "qsa_device.h"
@@ -364,7 +369,12 @@ void topk_resident_kernel(TopkParams p) {
     constexpr int kListCap = THREADS * 4;  // keys >= floor kept in LDS
     constexpr int kSub = 4;  // sub-runs per thread, one maximum each
     constexpr int kSubLen = (E + kSub - 1) / kSub;
+    constexpr int kChunks = E / 4;  // 16-byte loads per thread
+    constexpr int kWords = (kChunks + 2) / 3;
+    constexpr int kWaves = THREADS / 64;
+    static_assert(E % 4 == 0 && THREADS % 64 == 0 && THREADS <= 1024, "layout");
     __shared__ SelectShared sh;
+    __shared__ int seg_count[kChunks * kWaves];
     __shared__ __attribute__((aligned(16))) int hist_list[2048];  // listed keys by their top 11 bits
     __shared__ uint32_t list_key[kListCap];
     __shared__ int list_col[kListCap];
@@ -373,10 +383,11 @@ void topk_resident_kernel(TopkParams p) {
     __shared__ int s_need;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int64_t row = blockIdx.x;
     const float *x = p.logits + row * p.logits_stride;
     int32_t *out = p.out + row * p.out_stride;
-    const int col0 = tid * E;  // this thread's columns: col0 .. col0 + E - 1
+    const int col0 = tid * E;  // the thread's run for the re-reading paths: col0 .. col0 + E - 1
 
     for (int b = tid; b < 2048; b += THREADS) {
         sh.hist[b] = 0;
@@ -387,6 +398,9 @@ void topk_resident_kernel(TopkParams p) {
     // to test key >= floor exactly (the floor is a multiple of 2^21).  The
     // maximum of each sub-run of the thread's keys is kept in full; the
     // sub-run maxima are distinct keys, each witnessing one key >= itself.
+    // Element j = 4e + i of this thread is column 4 * (tid + THREADS * e) + i:
+    // load e of the workgroup covers 16 * THREADS contiguous bytes, every
+    // 128-byte line read by one instruction of one wave.
     uint32_t top16[(E + 1) / 2];
     uint32_t smax[kSub] = {};
     int cand = 0;
@@ -396,18 +410,25 @@ void topk_resident_kernel(TopkParams p) {
         if (e % 2 == 0) top16[e / 2] = k >> 16;
         else top16[e / 2] |= k & 0xffff0000u;
     };
-    if (p.vec && col0 + E <= p.num_cols) {
-        // The whole run is inside the row: 16-byte loads, all in flight at
-        // once (so each cache line is read while its neighbours' loads are
-        // still pending, before it can be evicted).
-        f32x4 v[E / 4];
+    auto chunk_col = [&](int e) { return 4 * (tid + THREADS * e); };
+    if (p.vec && (p.num_cols & 3) == 0) {
+        // All of the thread's 16-byte loads in flight at once.
+        const float ni = neg_inf();
+        f32x4 v[kChunks];
 #pragma unroll
-        for (int e = 0; e < E / 4; ++e) v[e] = *reinterpret_cast<const f32x4 *>(x + col0 + 4 * e);
+        for (int e = 0; e < kChunks; ++e) {
+            const int c = chunk_col(e);
+            v[e] = c < p.num_cols ? *reinterpret_cast<const f32x4 *>(x + c) : f32x4{ni, ni, ni, ni};
+        }
 #pragma unroll
         for (int e = 0; e < E; ++e) absorb(e, order_key(v[e / 4][e % 4]));
     } else {
+        // Rows without 16-byte alignment or with a ragged last chunk.
 #pragma unroll
-        for (int e = 0; e < E; ++e) absorb(e, col0 + e < p.num_cols ? order_key(x[col0 + e]) : 0u);
+        for (int e = 0; e < E; ++e) {
+            const int c = chunk_col(e / 4) + e % 4;
+            absorb(e, c < p.num_cols ? order_key(x[c]) : 0u);
+        }
     }
     auto key_top = [&](int e) { return e % 2 == 0 ? (top16[e / 2] & 0xffffu) : (top16[e / 2] >> 16); };
     int num_cand;
@@ -439,29 +460,59 @@ void topk_resident_kernel(TopkParams p) {
         // integer arithmetic: for 16-bit t and f, (t + 2^16 - f) >> 16 is
         // 1 exactly when t >= f.
         const uint32_t floor_top = max(floor >> 16, 1u);
-        uint32_t mine_u = 0;
+        // The list in column order is chunk-major (chunk e of wave w covers
+        // columns 2048e + 256w .. +255 at 512 threads): wave w's segment of
+        // chunk e follows every segment of chunks before e and those of
+        // waves before w in chunk e.  Per-lane counts of each chunk, three
+        // 10-bit fields to a word (a wave's count per chunk is at most 256),
+        // are scanned across the wave with DPP.
+        uint32_t packed[kWords], incl[kWords];
 #pragma unroll
-        for (int e = 0; e < E; ++e) mine_u += (key_top(e) + 0x10000u - floor_top) >> 16;
-        const int mine = (int)mine_u;
-        int listed;
-        const int at = block_exclusive_scan<THREADS>(mine, sh.wave_tmp, &listed);
+        for (int w = 0; w < kWords; ++w) packed[w] = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            packed[e / 12] += ((key_top(e) + 0x10000u - floor_top) >> 16) << (10 * ((e / 4) % 3));
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) incl[w] = wave_inclusive_scan(packed[w]);
+        if (lane == 63) {
+#pragma unroll
+            for (int e = 0; e < kChunks; ++e) seg_count[e * kWaves + wave] = (int)((incl[e / 3] >> (10 * (e % 3))) & 1023u);
+        }
+        __syncthreads();
+        // Lane c (< kChunks) of every wave: the chunk's total and this wave's
+        // offset within it, then a scan over chunks.
+        int tot = 0, pre = 0;
+        if (lane < kChunks) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const int sc = seg_count[lane * kWaves + w];
+                tot += sc;
+                pre += w < wave ? sc : 0;
+            }
+        }
+        const int tot_incl = (int)wave_inclusive_scan((uint32_t)tot);
+        const int seg_off = tot_incl - tot + pre;
+        const int listed = __builtin_amdgcn_readlane(tot_incl, 63);
         int need = 0;
         if (listed <= kListCap) {
             // The keys >= floor in column order (top halves), counted by
             // their top 11 bits.
-            if (mine > 0) {
-                int w = at;
-                // The same test as the count above, against a copy of the
-                // floor the compiler cannot prove equal, so it recomputes the
-                // tests here instead of keeping one lane mask per key alive.
-                const uint32_t floor_top2 = __builtin_amdgcn_readfirstlane(floor_top);
+            const uint32_t floor_top2 = __builtin_amdgcn_readfirstlane(floor_top);
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const uint32_t t = key_top(e);
+            for (int e = 0; e < kChunks; ++e) {
+                int w = __builtin_amdgcn_readlane(seg_off, e) +
+                        (int)(((incl[e / 3] - packed[e / 3]) >> (10 * (e % 3))) & 1023u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // The same test as the count above, against a copy of the
+                    // floor the compiler cannot prove equal, so it recomputes
+                    // the tests here instead of keeping one lane mask per key
+                    // alive.
+                    const uint32_t t = key_top(4 * e + i);
                     const bool in = t >= floor_top2;
                     if (in) {
                         list_key[w] = t << 16;
-                        list_col[w] = col0 + e;
+                        list_col[w] = chunk_col(e) + i;
                         atomicAdd(&hist_list[t >> 5], 1);
                     }
                     w += in;
