@@ -186,8 +186,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 4 
     const int q4 = lane >> 4;
     const int c0 = span * kSpan;
 
-    if (!compute) {
+    if (__builtin_expect(!compute, 0)) {
         // -inf only: spans span .. span + kPadSpans - 1 (clipped to out_cols).
+        // Laid out after the key path (unlikely), so a key-reading wave's
+        // first instructions are contiguous from the kernel's entry.
         const float ni = neg_inf();
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 4 
     // Query fragments first: tile mt holds rows j = 4*mt .. 4*mt+3.
     u32x4 qa[MT][4];
     const int qh = n & 3;
-    if (p.q_vec) {
+    if (__builtin_expect(p.q_vec, 1)) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int j = 4 * mt + (n >> 2);
