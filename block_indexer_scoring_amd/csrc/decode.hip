@@ -161,6 +161,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 4 
     const int lane = threadIdx.x & 63;
     const int task_id = blockIdx.x;
 
+    // Every kernel argument the key path reads is loaded here, before the
+    // first branch: their scalar loads then go out together in one round
+    // trip, rather than one round trip for each branch that first needs
+    // some of them (the start-up of a short launch like this one is a chain
+    // of such round trips).  The empty asm only requires the values.
+    asm volatile("" ::"s"(p.q), "s"(p.q_stride_req), "s"(p.q_stride_row), "s"(p.q_stride_head), "s"(p.k),
+                 "s"(p.num_pages), "s"(p.page_size), "s"(p.visible), "s"(p.num_reqs), "s"(p.dql), "s"(p.scale));
+    asm volatile("" ::"s"(p.out), "s"(p.out_stride), "s"(p.out_cols), "s"(p.spans), "s"(p.q_vec), "s"(p.out_vec));
+    if (SRC == kPlanned) asm volatile("" ::"s"(p.plan));
+    else asm volatile("" ::"s"(p.comp_lens), "s"(p.page_table), "s"(p.page_table_stride), "s"(p.page_table_cols));
+
     int r, span, comp, page = -1;
     bool compute;
     if (SRC == kPlanned) {
