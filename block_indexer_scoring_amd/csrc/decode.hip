@@ -154,7 +154,7 @@ __device__ Task map_task(const DecodeParams &p, int task, int lane) {
 }
 
 template <int MT, int PAGE_MODE, int FMT, int SRC>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 4 : 2))) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MT <= 1 ? 5 : (MT <= 2 ? 4 : 2)))) void decode_kernel(DecodeParams p) {
     constexpr bool kQF16 = FMT == kFp16 || FMT == kFp16Fp8;
     constexpr bool kKFp8 = FMT == kBf16Fp8 || FMT == kFp16Fp8;
     constexpr bool kUniform = PAGE_MODE != kPageGeneric;
