@@ -146,12 +146,10 @@ void prefill_kernel(PrefillParams p) {
     __shared__ int s_end[kBM];  // min(row_k_end, num_keys)
     __shared__ int s_done[kBM];
     __shared__ int s_cur, s_lim;
-    // kModeCandidates, per row of the workgroup: the floor key, the segment's
-    // offset and size in the row's candidate pool, keys equal to the floor
-    // seen so far in this chunk, and candidates written.
+    // kModeCandidates, per row of the workgroup: the floor key and the
+    // segment's offset and size in the row's candidate pool.
     __shared__ uint32_t c_fkey[kFused ? kBM : 1];
-    __shared__ int c_seg0[kFused ? kBM : 1], c_segn[kFused ? kBM : 1], c_teq[kFused ? kBM : 1],
-        c_ncand[kFused ? kBM : 1];
+    __shared__ int c_seg0[kFused ? kBM : 1], c_segn[kFused ? kBM : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -278,6 +276,11 @@ void prefill_kernel(PrefillParams p) {
         float gm[4];        // kModeGroupMax: maximum of the open group
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) gm[mt] = neg_inf();
+        // kModeCandidates, per slice row of this lane: keys equal to the
+        // floor seen so far in this chunk, and candidates written.  Every
+        // lane of the row's 16 keeps the same copy in registers, so a slice
+        // updates them with no memory round trip.
+        int c_teq[4] = {}, c_ncand[4] = {};
         if (kMode == kModeCandidates) {
             for (int i = tid; i < kBM; i += kThreads) {
                 const int row = row0 + i;
@@ -287,8 +290,6 @@ void prefill_kernel(PrefillParams p) {
                 c_fkey[i] = cand ? p.floor_key[row] : 0u;
                 c_seg0[i] = s0;
                 c_segn[i] = cand ? min(so[1], p.pool_cap) - s0 : 0;  // within the pool in any case
-                c_teq[i] = 0;
-                c_ncand[i] = 0;
             }
             __syncthreads();
         }
@@ -458,16 +459,16 @@ void prefill_kernel(PrefillParams p) {
                 const uint32_t packed = ((uint32_t)ngt << 16) | (uint32_t)neq;
                 const uint32_t incl = row16_inclusive_scan(packed);
                 const uint32_t excl = incl - packed;
-                const uint32_t tot = (uint32_t)__shfl((int)incl, (lane & 48) + 15, 64);
-                const int teq = c_teq[ri], nc = c_ncand[ri], segn = c_segn[ri];
+                // The row's totals: lane 15 of each 16-lane row, broadcast within
+                // the row by DPP (row_newbcast:15), with no LDS round trip.
+                const uint32_t tot = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x15F, 0xf, 0xf, false);
+                const int teq = c_teq[mt], nc = c_ncand[mt], segn = c_segn[ri];
                 const int avail = max(p.topk - teq, 0);
                 const int nw = (int)(tot >> 16) + min((int)(tot & 0xffffu), avail);
                 int eqi = (int)(excl & 0xffffu);
                 int pos = nc + (int)(excl >> 16) + min(eqi, avail);
-                if (n == 0) {  // one lane per row keeps the row's counters
-                    c_teq[ri] = teq + (int)(tot & 0xffffu);
-                    c_ncand[ri] = nc + nw;
-                }
+                c_teq[mt] = teq + (int)(tot & 0xffffu);
+                c_ncand[mt] = nc + nw;
                 const int64_t sbase = (int64_t)row * p.pool_cap + c_seg0[ri];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
@@ -502,6 +503,13 @@ void prefill_kernel(PrefillParams p) {
             }
             __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);      // the store
         };
+        auto interleave_valu = [&]() {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+            }
+        };
         auto load_b = [&](const uint16_t *tile, u32x4 (&b)[4][4]) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
@@ -513,14 +521,20 @@ void prefill_kernel(PrefillParams p) {
             const bool full = p.out_vec && tile_c + kBN <= c_end;
             if (kFused) {
                 if (!masked && !prev_masked) {
+                    // The group-maximum epilogue is plain VALU work: interleaved
+                    // with the MFMAs like the score path's.
                     multiply(0, b, accA);
                     finish_topk(3, prev_c, false, accB);
+                    if (kMode == kModeGroupMax) interleave_valu();
                     multiply(1, b, accB);
                     finish_topk(0, tile_c, false, accA);
+                    if (kMode == kModeGroupMax) interleave_valu();
                     multiply(2, b, accA);
                     finish_topk(1, tile_c, false, accB);
+                    if (kMode == kModeGroupMax) interleave_valu();
                     multiply(3, b, accB);
                     finish_topk(2, tile_c, false, accA);
+                    if (kMode == kModeGroupMax) interleave_valu();
                 } else {
                     multiply(0, b, accA);
                     finish_topk(3, prev_c, prev_masked, accB);
@@ -622,9 +636,10 @@ void prefill_kernel(PrefillParams p) {
                     store4(out_wg + row_elem(mt, cs), true, cs, c_end, keep[mt][0], keep[mt][1], keep[mt][2], keep[mt][3]);
         }
         if (kMode == kModeCandidates) {
-            __syncthreads();  // every wave's last counter updates are in LDS
-            for (int i = tid; i < kBM; i += kThreads)
-                if (!s_done[i] && s_start[i] == cur) p.cand_cnt[(int64_t)(row0 + i) * p.col_chunks + cc] = c_ncand[i];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                if (n == 0 && in_pass[mt])
+                    p.cand_cnt[(int64_t)(row0 + a_w + dl * (4 * mt + q4)) * p.col_chunks + cc] = c_ncand[mt];
         }
         if (kMode == kModeGroupMax) {
             // Close the group the last computed tile left open, and give the

@@ -55,8 +55,9 @@ bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 // floor key, the offsets of the column chunks' segments in the row's
 // candidate pool, a candidate count per chunk, and the pool (keys,
 // columns).  The pool holds every key above the floor (at most 16 (k - 1))
-// and at most k keys equal to it per chunk, so it never overflows; the
-// floor kernel sizes each segment from the group maxima.
+// and at most k keys equal to it per chunk, and no chunk more than its
+// columns, so it never overflows; the floor kernel sizes each segment from
+// the group maxima.
 constexpr int64_t kFusedMaxKStride = (int64_t)1 << 14;
 struct FusedLayout {
     int chunk;
@@ -65,17 +66,28 @@ struct FusedLayout {
 };
 FusedLayout fused_layout(int32_t num_rows, int32_t out_cols, int32_t topk, int num_cus) {
     FusedLayout L{};
-    // Column chunks on 256-column group boundaries; sized for the largest
-    // key stride accepted, so the same layout serves every call.
-    int chunk = qsa::prefill_col_chunk(num_rows, out_cols, kFusedMaxKStride, num_cus) / 256 * 256;
-    L.chunk = chunk < 256 ? 256 : chunk;
+    // Column chunks on 256-column group boundaries, as few as still give one
+    // workgroup per CU (row blocks x chunks), so both passes run in one round
+    // of workgroups.  The layout depends on the sizes and the CU count only,
+    // so the same layout serves every call.
+    const int64_t row_blocks = ((int64_t)num_rows + qsa::prefill_rows_per_block() - 1) / qsa::prefill_rows_per_block();
+    const int64_t cus = num_cus > 0 ? num_cus : 256;
+    const int64_t want = row_blocks > 0 && row_blocks < cus ? cus / row_blocks : 1;
+    // At most 32,512 columns, so a chunk's key offsets stay 32-bit at the
+    // largest key stride accepted.
+    const int64_t max_chunk = (((int64_t)1 << 30) / (64 * kFusedMaxKStride * 2) - 1) * 64 / 256 * 256;
+    const int64_t chunk = ((((int64_t)out_cols + want - 1) / want) + 255) / 256 * 256;
+    L.chunk = (int)(chunk < 256 ? 256 : (chunk > max_chunk ? max_chunk : chunk));
     L.col_chunks = out_cols > 0 ? ((int64_t)out_cols + L.chunk - 1) / L.chunk : 0;
     if (L.col_chunks > qsa::kFusedMaxSegs) {  // wide rows: fewer, wider chunks
         L.chunk = (int)((((int64_t)out_cols + qsa::kFusedMaxSegs - 1) / qsa::kFusedMaxSegs + 255) / 256 * 256);
         L.col_chunks = ((int64_t)out_cols + L.chunk - 1) / L.chunk;
     }
     L.groups = 16 * (((int64_t)out_cols + 255) / 256);
+    // Each segment's room is also capped by its chunk's columns, so a row
+    // never needs more than its columns.
     L.pool_cap = 16 * (int64_t)(topk - 1) + L.col_chunks * topk;
+    if (L.pool_cap > out_cols) L.pool_cap = out_cols;
     auto seg = [](int64_t b) { return (b + 255) / 256 * 256; };
     int64_t o = 0;
     L.off_gmax = o; o += seg((int64_t)num_rows * L.groups * 4);
@@ -793,6 +805,7 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     fp.seg_off = reinterpret_cast<int32_t *>(ws + L.off_segoff);
     fp.segs = (int32_t)L.col_chunks;
     fp.groups_per_seg = L.chunk / 16;
+    fp.out_cols = out_cols;
     fp.pool_cap = (int32_t)L.pool_cap;
     fp.out = out_idx;
     fp.out_stride = out_stride;

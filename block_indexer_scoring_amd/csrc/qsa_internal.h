@@ -108,6 +108,7 @@ struct FusedTopkParams {
     const int32_t *cand_cnt;    // [rows][segs]
     int32_t segs;               // column chunks
     int32_t groups_per_seg;     // groups per column chunk
+    int32_t out_cols;           // columns per row (the last chunk may be partial)
     int32_t pool_cap;
     int32_t *out;
     int64_t out_stride;

@@ -715,7 +715,12 @@ __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
     for (int s0 = 0; s0 < p.segs; s0 += 64) {
         const int sg = s0 + lane;
         int room = 0;
-        if (sg < p.segs) room = 16 * cgt[sg] + min(p.k, 16 * (cgt[sg] + ceq[sg]));
+        if (sg < p.segs) {
+            // No more than the chunk's cells either, so a row's segments
+            // never exceed its columns.
+            const int seg_cols = min(16 * p.groups_per_seg, p.out_cols - sg * 16 * p.groups_per_seg);
+            room = min(16 * cgt[sg] + min(p.k, 16 * (cgt[sg] + ceq[sg])), seg_cols);
+        }
         const int incl = (int)wave_inclusive_scan((uint32_t)room);
         if (sg < p.segs) off[sg] = run + incl - room;
         run += __builtin_amdgcn_readlane(incl, 63);
