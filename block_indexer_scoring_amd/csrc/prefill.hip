@@ -338,6 +338,18 @@ void prefill_kernel(PrefillParams p) {
             p.out + (int64_t)row0 * p.out_stride, 0,
             kExact ? (int)((int64_t)min(kBM, p.num_rows - row0) * p.out_stride * 4) : 0, kBufferWord3);
         constexpr uint32_t kDropped = 0x80000000u;
+        // The fused passes' outputs of this workgroup's rows as one raw
+        // buffer (group maxima, or candidate pools), for the same reason:
+        // every slice issues a fixed number of stores.
+        const int wg_rows = min(kBM, p.num_rows - row0);
+        const __amdgpu_buffer_rsrc_t fused_rsrc =
+            kMode == kModeGroupMax
+                ? __builtin_amdgcn_make_buffer_rsrc(p.gmax + (int64_t)row0 * p.gmax_stride, 0,
+                                                    wg_rows * p.gmax_stride * 4, kBufferWord3)
+            : kMode == kModeCandidates
+                ? __builtin_amdgcn_make_buffer_rsrc(p.cand + (int64_t)row0 * p.pool_cap * 2, 0,
+                                                    wg_rows * p.pool_cap * 8, kBufferWord3)
+                : __builtin_amdgcn_make_buffer_rsrc(p.out, 0, 0, kBufferWord3);
         // Byte offset of (row, column sc) in out_rsrc, modulo 2^32: it is
         // negative for row 0 and lanes n < rot, whose stores then lie at
         // least one tile in (the first tile's are dropped).
@@ -424,8 +436,17 @@ void prefill_kernel(PrefillParams p) {
         // Fused top-k epilogue of one slice (kModeGroupMax, kModeCandidates).
         // `masked` is a literal at each call, so the unmasked form folds.
         auto finish_topk = [&](int mt, int tile_c, bool masked, const f32x4 (&acc)[4]) {
-            if (tile_c < 0) return;  // placeholder before a pass's first tile
-            const int row = row0 + a_w + dl * (4 * mt + q4);
+            if (tile_c < 0) {  // placeholder before a pass's first tile: dropped stores only
+                if (kMode == kModeGroupMax)
+                    __builtin_amdgcn_raw_buffer_store_b32(0u, fused_rsrc, kDropped, 0, 0);
+                else
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, fused_rsrc, kDropped, 0, 0);
+                return;
+            }
+            const int ri = a_w + dl * (4 * mt + q4);  // row in the workgroup
+            const int row = row0 + ri;
             const int col = tile_c + lc;
             f32x4 v;
 #pragma unroll
@@ -437,16 +458,19 @@ void prefill_kernel(PrefillParams p) {
             if (kMode == kModeGroupMax) {
                 gm[mt] = max(gm[mt], max(max(v[0], v[1]), max(v[2], v[3])));
                 const int tix = tile_c / kBN;  // chunks start on group boundaries
-                if (tix % kGroupTiles == kGroupTiles - 1 || tile_c + kBN >= c_end) {
-                    if (in_pass[mt]) p.gmax[(int64_t)row * p.gmax_stride + (tix / kGroupTiles) * 16 + n] = gm[mt];
-                    gm[mt] = neg_inf();
-                }
+                // Exactly one store per slice (dropped unless the group closes).
+                const bool closes = tix % kGroupTiles == kGroupTiles - 1 || tile_c + kBN >= c_end;
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __float_as_uint(gm[mt]), fused_rsrc,
+                    closes && in_pass[mt] ? (uint32_t)((ri * p.gmax_stride + (tix / kGroupTiles) * 16 + n) * 4)
+                                          : kDropped,
+                    0, 0);
+                if (closes) gm[mt] = neg_inf();
             } else {
                 // Cells above the floor, and the first `topk` cells equal to
                 // it in this chunk, appended in column order to the row's
                 // segment for this chunk (lanes 16q4 .. 16q4+15 hold this
                 // row's keys 4n .. 4n+3).
-                const int ri = a_w + dl * (4 * mt + q4);  // row in the workgroup
                 const uint32_t fk = c_fkey[ri];
                 uint32_t kv[4];
                 int ngt = 0, neq = 0;
@@ -469,16 +493,17 @@ void prefill_kernel(PrefillParams p) {
                 int pos = nc + (int)(excl >> 16) + min(eqi, avail);
                 c_teq[mt] = teq + (int)(tot & 0xffffu);
                 c_ncand[mt] = nc + nw;
-                const int64_t sbase = (int64_t)row * p.pool_cap + c_seg0[ri];
+                // Exactly four 8-byte stores per slice, one per cell (dropped
+                // unless the cell is taken and fits the segment).
+                const int sbase = ri * p.pool_cap + c_seg0[ri];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const bool is_gt = kv[g] > fk;
                     const bool is_eq = kv[g] == fk && kv[g] != 0u;
                     const bool take = is_gt || (is_eq && eqi < avail);
-                    if (take && pos < segn) {
-                        p.cand_key[sbase + pos] = kv[g];
-                        p.cand_col[sbase + pos] = col + g;
-                    }
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{kv[g], (uint32_t)(col + g)}, fused_rsrc,
+                                                          take && pos < segn ? (uint32_t)(sbase + pos) * 8u : kDropped,
+                                                          0, 0);
                     pos += take;
                     eqi += is_eq;
                 }
@@ -579,15 +604,21 @@ void prefill_kernel(PrefillParams p) {
             for (int h = 0; h < kTilesPerStage; ++h)
                 if (it + h < n_compute) stage(c_begin + (it + h) * kBN, buf + h * kTileElems);
         };
-        // Stores issued after a buffer's loads: one per slice, 4 per tile.
-        constexpr int kStoresPerStage = 4 * kTilesPerStage;
-        static_assert(kStoresInFlight <= kStoresPerStage && kStoresInFlight <= 15, "vmcnt field");
+        // Stores issued after a buffer's loads: per slice one (scores, group
+        // maxima) or four (candidates); 4 slices per tile.
+        constexpr int kStoresPerSlice = kMode == kModeCandidates ? 4 : 1;
+        constexpr int kStoresPerStage = 4 * kStoresPerSlice * kTilesPerStage;
+        constexpr bool kFixedStores = kExact || kFused;
+        constexpr int kInFlight = kMode == kModeCandidates ? 16 : kStoresInFlight;
+        static_assert(kInFlight <= kStoresPerStage && kInFlight <= 63, "vmcnt field");
+        // s_waitcnt vmcnt(kInFlight) lgkmcnt(0) (vmcnt split over bits 3:0 and 15:14).
+        constexpr int kStageWait = ((kInFlight >> 4) << 14) | 0x0070 | (kInFlight & 15);
         auto run_stage = [&](int it, const uint16_t *cur_buf, uint16_t *next_buf) {
             // The buffer is in LDS once every wave's loads for it have
             // landed.  Vector-memory ops complete in issue order, and the
             // previous stage issued exactly kStoresPerStage stores after
             // them, so up to that many may stay in flight.
-            if (kExact) __builtin_amdgcn_s_waitcnt(0x0070 | kStoresInFlight);  // vmcnt(N) lgkmcnt(0)
+            if (kFixedStores) __builtin_amdgcn_s_waitcnt(kStageWait);
             else __builtin_amdgcn_s_waitcnt(0);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_s_barrier();
@@ -610,6 +641,12 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt)
                         __builtin_amdgcn_raw_buffer_store_b128(f32x4{0.f, 0.f, 0.f, 0.f}, out_rsrc, kDropped, 0, 0);
+                } else if (kFused) {
+#pragma unroll
+                    for (int i = 0; i < 4 * kStoresPerSlice; ++i) {
+                        if (kMode == kModeGroupMax) __builtin_amdgcn_raw_buffer_store_b32(0u, fused_rsrc, kDropped, 0, 0);
+                        else __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, fused_rsrc, kDropped, 0, 0);
+                    }
                 }
             }
         };

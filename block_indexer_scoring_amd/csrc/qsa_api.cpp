@@ -53,8 +53,8 @@ bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 // Fused prefill top-k workspace: per row the maxima of 16-key groups, the
 // floor key, the offsets of the column chunks' segments in the row's
-// candidate pool, a candidate count per chunk, and the pool (keys,
-// columns).  The pool holds every key above the floor (at most 16 (k - 1))
+// candidate pool, a candidate count per chunk, and the pool (8-byte entries:
+// score key, column).  The pool holds every key above the floor (at most 16 (k - 1))
 // and at most k keys equal to it per chunk, and no chunk more than its
 // columns, so it never overflows; the floor kernel sizes each segment from
 // the group maxima.
@@ -62,7 +62,7 @@ constexpr int64_t kFusedMaxKStride = (int64_t)1 << 14;
 struct FusedLayout {
     int chunk;
     int64_t col_chunks, groups, pool_cap;
-    int64_t off_gmax, off_floor, off_segoff, off_cnt, off_key, off_col, total;
+    int64_t off_gmax, off_floor, off_segoff, off_cnt, off_cand, total;
 };
 FusedLayout fused_layout(int32_t num_rows, int32_t out_cols, int32_t topk, int num_cus) {
     FusedLayout L{};
@@ -94,8 +94,7 @@ FusedLayout fused_layout(int32_t num_rows, int32_t out_cols, int32_t topk, int n
     L.off_floor = o; o += seg((int64_t)num_rows * 4);
     L.off_segoff = o; o += seg((int64_t)num_rows * (L.col_chunks + 1) * 4);
     L.off_cnt = o; o += seg((int64_t)num_rows * L.col_chunks * 4);
-    L.off_key = o; o += seg((int64_t)num_rows * L.pool_cap * 4);
-    L.off_col = o; o += seg((int64_t)num_rows * L.pool_cap * 4);
+    L.off_cand = o; o += seg((int64_t)num_rows * L.pool_cap * 8);
     L.total = o;
     return L;
 }
@@ -799,8 +798,7 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     fp.gmax = reinterpret_cast<float *>(ws + L.off_gmax);
     fp.gmax_stride = (int32_t)L.groups;
     fp.floor_key = reinterpret_cast<uint32_t *>(ws + L.off_floor);
-    fp.cand_key = reinterpret_cast<uint32_t *>(ws + L.off_key);
-    fp.cand_col = reinterpret_cast<int32_t *>(ws + L.off_col);
+    fp.cand = reinterpret_cast<uint32_t *>(ws + L.off_cand);
     fp.cand_cnt = reinterpret_cast<int32_t *>(ws + L.off_cnt);
     fp.seg_off = reinterpret_cast<int32_t *>(ws + L.off_segoff);
     fp.segs = (int32_t)L.col_chunks;
@@ -825,7 +823,9 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     if (k_stride > kFusedMaxKStride)
         return fail(QSA_ERR_UNSUPPORTED, "%s: k_stride %lld exceeds %lld elements", fn, (long long)k_stride,
                     (long long)kFusedMaxKStride);
-    if (((int64_t)L.chunk + 64) * k_stride * 2 > ((int64_t)1 << 30))  // 32-bit key offsets per chunk
+    if (((int64_t)L.chunk + 64) * k_stride * 2 > ((int64_t)1 << 30) ||  // 32-bit key offsets per chunk
+        (int64_t)qsa::prefill_rows_per_block() * L.groups * 4 >= ((int64_t)1 << 31) ||  // and per workgroup's
+        (int64_t)qsa::prefill_rows_per_block() * L.pool_cap * 8 >= ((int64_t)1 << 31))  // maxima and pools
         return fail(QSA_ERR_UNSUPPORTED, "%s: rows of %d columns are too wide", fn, out_cols);
 
     qsa::PrefillParams p{};
@@ -849,8 +849,7 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     p.gmax = reinterpret_cast<float *>(ws + L.off_gmax);
     p.gmax_stride = fp.gmax_stride;
     p.floor_key = fp.floor_key;
-    p.cand_key = reinterpret_cast<uint32_t *>(ws + L.off_key);
-    p.cand_col = reinterpret_cast<int32_t *>(ws + L.off_col);
+    p.cand = reinterpret_cast<uint32_t *>(ws + L.off_cand);
     p.cand_cnt = reinterpret_cast<int32_t *>(ws + L.off_cnt);
     p.seg_off = fp.seg_off;
     p.pool_cap = fp.pool_cap;

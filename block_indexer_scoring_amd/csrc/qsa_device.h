@@ -9,6 +9,7 @@ namespace qsa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Head geometry fixed by the indexer: 4 query heads share one 128-wide key.
 constexpr int kHeads = 4;

@@ -746,8 +746,7 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
     const int k = p.k;
     const int segs = p.segs;
     const int64_t rbase = row * (int64_t)p.pool_cap;
-    const uint32_t *gkey = p.cand_key + rbase;
-    const int32_t *gcol = p.cand_col + rbase;
+    const uint32_t *gcand = p.cand + 2 * rbase;  // entry e: key at 2e, column at 2e + 1
     const int32_t *off = p.seg_off + row * (segs + 1);
     __shared__ int seg_base[kFusedMaxSegs];
     {
@@ -772,15 +771,15 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
         return (int64_t)seg_base[lo] + (pos - seg_start[lo]);
     };
     if (n <= k) {
-        for (int pos = tid; pos < k; pos += kThreads) out[pos] = pos < n ? gcol[locate(pos)] : -1;
+        for (int pos = tid; pos < k; pos += kThreads) out[pos] = pos < n ? (int32_t)gcand[2 * locate(pos) + 1] : -1;
         return;
     }
     const RowView none{nullptr, 0, 0, 0};
     if (n <= kFusedListCap) {
         for (int pos = tid; pos < n; pos += kThreads) {
             const int64_t e = locate(pos);
-            lkey[pos] = gkey[e];
-            lcol[pos] = gcol[e];
+            lkey[pos] = gcand[2 * e];
+            lcol[pos] = (int32_t)gcand[2 * e + 1];
         }
         __syncthreads();
         const ListView list{lkey, lcol, n};
@@ -803,9 +802,9 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
         __syncthreads();
         for (int sgi = 0; sgi < segs; ++sgi) {
             const int cnt = seg_start[sgi + 1] - seg_start[sgi];
-            const uint32_t *sk = gkey + seg_base[sgi];
+            const uint32_t *sk = gcand + 2 * (int64_t)seg_base[sgi];
             for (int i = tid; i < cnt; i += kThreads) {
-                const uint32_t key = sk[i];
+                const uint32_t key = sk[2 * i];
                 if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1);
             }
         }
@@ -835,7 +834,7 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
         int sgi = seg_of(lo);
         for (int pos = lo; pos < hi; ++pos) {
             while (pos >= seg_start[sgi + 1]) ++sgi;
-            const uint32_t key = gkey[(int64_t)seg_base[sgi] + (pos - seg_start[sgi])];
+            const uint32_t key = gcand[2 * ((int64_t)seg_base[sgi] + (pos - seg_start[sgi]))];
             gt += key > T;
             eq += key == T;
         }
@@ -848,10 +847,10 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
         for (int pos = lo; pos < hi; ++pos) {
             while (pos >= seg_start[sgi + 1]) ++sgi;
             const int64_t e = (int64_t)seg_base[sgi] + (pos - seg_start[sgi]);
-            const uint32_t key = gkey[e];
+            const uint32_t key = gcand[2 * e];
             const bool is_gt = key > T, is_eq = key == T;
-            if (is_gt) out[gt_before + min(eq_before, need)] = gcol[e];
-            else if (is_eq && eq_before < need) out[gt_before + eq_before] = gcol[e];
+            if (is_gt) out[gt_before + min(eq_before, need)] = (int32_t)gcand[2 * e + 1];
+            else if (is_eq && eq_before < need) out[gt_before + eq_before] = (int32_t)gcand[2 * e + 1];
             gt_before += is_gt;
             eq_before += is_eq;
         }

@@ -74,9 +74,12 @@ def _pattern_rows(rng, rows, cols):
     return x
 
 
-@pytest.mark.parametrize("cols,k", [(5000, 512), (26024, 512), (32768, 512), (27048, 2048)])
+@pytest.mark.parametrize("cols,k", [(5000, 512), (26024, 512), (32768, 512), (27048, 2048),
+                                    (27047, 512), (5003, 100), (30001, 512), (4097, 4096)])
 def test_topk_patterns_many_rows(cols, k):
-    """Enough rows for the many-row launch shape, with the edge patterns."""
+    """Enough rows for the many-row launch shapes, with the edge patterns;
+    column counts that are not a multiple of 4 take the element-load path
+    (a ragged last 4-column chunk)."""
     rng = np.random.default_rng(cols ^ k)
     x = _pattern_rows(rng, 300, cols)
     got = _topk_gpu(x, k)
