@@ -545,15 +545,19 @@ int qsa_topk_blocks(const float *logits, int64_t logits_stride, int32_t num_rows
  *   workspace  : device memory of at least qsa_prefill_topk_workspace_bytes
  *                bytes, 256-byte aligned, owned by the caller; its contents
  *                on entry do not matter and are clobbered.  About
- *                num_rows * (8 * (16 * (topk - 1) + 2 * topk) + out_cols / 4)
- *                bytes at the usual sizes, of which a call touches a few
- *                percent.
+ *                num_rows * (8 * min(16 * (topk - 1) + chunks * topk, out_cols)
+ *                + out_cols / 4) bytes, chunks being the column chunks per
+ *                row (as few as fill the CUs with row blocks of 128 rows; 4
+ *                for 8,192 rows on 256 CUs), of which a call touches a few
+ *                percent.  The size depends on the sizes and the device's CU
+ *                count only.
  *   The call enqueues four kernels on stream (a group-maximum pass over the
  *   scores, the per-row floor over the group maxima, a candidate pass over
  *   the scores, the final select); with timing events armed the start event
  *   marks the first kernel's begin and the stop event the last kernel's
  *   end.
- *   Errors: as qsa_mqa_prefill (UNSUPPORTED also for k_stride > 16,384),
+ *   Errors: as qsa_mqa_prefill (UNSUPPORTED also for k_stride > 16,384 and
+ *   for rows whose per-workgroup workspace offsets would pass 2^31 bytes),
  *   INVALID_ARGUMENT for topk outside [1, 2048], out_stride < topk, a NULL
  *   out_idx or workspace, or a workspace below the size needed; LAYOUT for a
  *   misaligned out_idx or workspace.
