@@ -154,30 +154,38 @@ __device__ Task map_task(const DecodeParams &p, int task, int lane) {
 }
 
 template <int MT, int PAGE_MODE, int FMT, int SRC>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MT <= 1 ? 5 : (MT <= 2 ? 4 : 2)))) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MT <= 1 ? 5 : (MT <= 2 ? 4 : 2)))) void decode_kernel(
+    const int32_t *plan, DecodeParams p) {
     constexpr bool kQF16 = FMT == kFp16 || FMT == kFp16Fp8;
     constexpr bool kKFp8 = FMT == kBf16Fp8 || FMT == kFp16Fp8;
     constexpr bool kUniform = PAGE_MODE != kPageGeneric;
     const int lane = threadIdx.x & 63;
     const int task_id = blockIdx.x;
 
-    // Every kernel argument the key path reads is loaded here, before the
-    // first branch: their scalar loads then go out together in one round
-    // trip, rather than one round trip for each branch that first needs
-    // some of them (the start-up of a short launch like this one is a chain
-    // of such round trips).  The empty asm only requires the values.
-    asm volatile("" ::"s"(p.q), "s"(p.q_stride_req), "s"(p.q_stride_row), "s"(p.q_stride_head), "s"(p.k),
-                 "s"(p.num_pages), "s"(p.page_size), "s"(p.visible), "s"(p.num_reqs), "s"(p.dql), "s"(p.scale));
-    asm volatile("" ::"s"(p.out), "s"(p.out_stride), "s"(p.out_cols), "s"(p.spans), "s"(p.q_vec), "s"(p.out_vec));
-    if (SRC == kPlanned) asm volatile("" ::"s"(p.plan));
-    else asm volatile("" ::"s"(p.comp_lens), "s"(p.page_table), "s"(p.page_table_stride), "s"(p.page_table_cols));
+    // Every kernel argument the key path reads is required before the first
+    // branch: their scalar loads then go out together in one round trip,
+    // rather than one round trip for each branch that first needs some of
+    // them (the start-up of a short launch like this one is a chain of such
+    // round trips).  The empty asm only requires the values.
+    auto require_args = [&]() {
+        asm volatile("" ::"s"(p.q), "s"(p.q_stride_req), "s"(p.q_stride_row), "s"(p.q_stride_head), "s"(p.k),
+                     "s"(p.num_pages), "s"(p.page_size), "s"(p.visible), "s"(p.num_reqs), "s"(p.dql), "s"(p.scale));
+        asm volatile("" ::"s"(p.out), "s"(p.out_stride), "s"(p.out_cols), "s"(p.spans), "s"(p.q_vec), "s"(p.out_vec));
+        if (SRC == kMapped)
+            asm volatile("" ::"s"(p.comp_lens), "s"(p.page_table), "s"(p.page_table_stride), "s"(p.page_table_cols));
+    };
 
     int r, span, comp, page = -1;
     bool compute;
     if (SRC == kPlanned) {
         // The entry is wave-uniform: one scalar load.  Any contents are safe:
         // requests, spans and pages outside the launch's ranges are refused.
-        const i32x4 e = load_uniform(reinterpret_cast<const i32x4 *>(p.plan) + task_id);
+        // The table pointer is the first kernel argument (preloaded into
+        // SGPRs at wave launch), so the entry's load goes out with the other
+        // arguments' loads: one round trip for all of them.
+        const i32x4 e = load_uniform(reinterpret_cast<const i32x4 *>(plan) + task_id);
+        asm volatile("" ::"s"(e[0]), "s"(e[1]), "s"(e[2]), "s"(e[3]));
+        require_args();
         r = e[0];
         if (r < 0 || r >= p.num_reqs) return;
         span = e[1] & 0x7fffffff;
@@ -186,6 +194,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MT <= 1 ? 5 
         page = e[2];
         comp = e[3] > 0 ? e[3] : 0;
     } else {
+        require_args();
         const Task task = map_task(p, task_id, lane);
         if (!task.valid) return;
         r = __builtin_amdgcn_readfirstlane(task.r);
@@ -492,10 +501,13 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(PlanParams p)
 
 template <int MT, int FMT, int SRC>
 hipError_t launch_fmt(const DecodeParams &p, hipStream_t stream, dim3 grid, dim3 block) {
-    if (p.page_size == kSpan) return launch_kernel(decode_kernel<MT, kPage64, FMT, SRC>, grid, block, stream, p);
+    // The task table goes first among the kernel arguments, where it can be
+    // preloaded into SGPRs at wave launch.
+    const int32_t *plan = SRC == kPlanned ? p.plan : nullptr;
+    if (p.page_size == kSpan) return launch_kernel(decode_kernel<MT, kPage64, FMT, SRC>, grid, block, stream, plan, p);
     if (p.page_size % kSpan == 0)
-        return launch_kernel(decode_kernel<MT, kPageMultiple64, FMT, SRC>, grid, block, stream, p);
-    return launch_kernel(decode_kernel<MT, kPageGeneric, FMT, SRC>, grid, block, stream, p);
+        return launch_kernel(decode_kernel<MT, kPageMultiple64, FMT, SRC>, grid, block, stream, plan, p);
+    return launch_kernel(decode_kernel<MT, kPageGeneric, FMT, SRC>, grid, block, stream, plan, p);
 }
 
 template <int MT, int SRC>

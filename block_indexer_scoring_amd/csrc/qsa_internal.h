@@ -210,6 +210,14 @@ hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t s
                               ev.start, ev.stop, 0);
 }
 
+template <typename A, typename P>
+hipError_t launch_kernel(void (*kernel)(A, P), dim3 grid, dim3 block, hipStream_t stream, A a, P p) {
+    const LaunchEvents ev = launch_events();
+    void *args[] = {&a, &p};
+    return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, args, 0, stream,
+                              ev.start, ev.stop, 0);
+}
+
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);  // p.plan selects the planned kernel
 hipError_t launch_decode_plan(const PlanParams &p, hipStream_t stream);
 // The library's own decode task table on the current device (for callers
