@@ -23,9 +23,10 @@ def command(out: str = LIB, extra=()):
     return [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # Packed fp32 VALU ops are kept out of the generated code.
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # The first two dwords of kernel arguments (the decode's task
-            # table pointer) are preloaded into SGPRs at wave launch.
-            "-mllvm", "-amdgpu-kernarg-preload-count=2",
+            # Leading scalar kernel arguments, up to six dwords (the decode's
+            # task table pointer; the top-k rows' address and shape), are
+            # preloaded into SGPRs at wave launch.
+            "-mllvm", "-amdgpu-kernarg-preload-count=6",
             "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
             *extra, *sources(), "-o", out]
 

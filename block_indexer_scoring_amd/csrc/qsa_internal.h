@@ -2,6 +2,8 @@
 // HIP kernels.  Everything here has already been validated by the caller.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -201,20 +203,14 @@ struct LaunchEvents {
 };
 LaunchEvents launch_events();
 
-// Launches kernel(p) on stream with the calling thread's timing events.
-template <typename P>
-hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t stream, P p) {
+// Launches kernel(args...) on stream with the calling thread's timing events.
+// (The arguments' types are taken from the kernel, not deduced from the call.)
+template <typename... A>
+hipError_t launch_kernel(void (*kernel)(A...), dim3 grid, dim3 block, hipStream_t stream,
+                         typename std::common_type<A>::type... args) {
     const LaunchEvents ev = launch_events();
-    void *args[] = {&p};
-    return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, args, 0, stream,
-                              ev.start, ev.stop, 0);
-}
-
-template <typename A, typename P>
-hipError_t launch_kernel(void (*kernel)(A, P), dim3 grid, dim3 block, hipStream_t stream, A a, P p) {
-    const LaunchEvents ev = launch_events();
-    void *args[] = {&a, &p};
-    return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, args, 0, stream,
+    void *ptrs[] = {&args...};
+    return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, stream,
                               ev.start, ev.stop, 0);
 }
 

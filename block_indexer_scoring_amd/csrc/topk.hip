@@ -363,9 +363,13 @@ __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *
 }
 
 // THREADS threads per row; WPE waves per SIMD the registers are sized for.
+// The row's address, length and load shape come first among the kernel
+// arguments, where they are preloaded into SGPRs at wave launch: a
+// workgroup's row loads go out without waiting on an argument load.
 template <int E, int THREADS, int WPE>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE)))
-void topk_resident_kernel(TopkParams p) {
+void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t num_cols, int32_t vec_rows,
+                          TopkParams p) {
     constexpr int kListCap = THREADS * 4;  // keys >= floor kept in LDS
     constexpr int kSub = 4;  // sub-runs per thread, one maximum each
     constexpr int kSubLen = (E + kSub - 1) / kSub;
@@ -385,14 +389,9 @@ void topk_resident_kernel(TopkParams p) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int64_t row = blockIdx.x;
-    const float *x = p.logits + row * p.logits_stride;
+    const float *x = logits + row * logits_stride;
     int32_t *out = p.out + row * p.out_stride;
     const int col0 = tid * E;  // the thread's run for the re-reading paths: col0 .. col0 + E - 1
-
-    for (int b = tid; b < 2048; b += THREADS) {
-        sh.hist[b] = 0;
-        hist_list[b] = 0;
-    }
 
     // Keys stay in registers as their top 16 bits, two per register: enough
     // to test key >= floor exactly (the floor is a multiple of 2^21).  The
@@ -411,14 +410,14 @@ void topk_resident_kernel(TopkParams p) {
         else top16[e / 2] |= k & 0xffff0000u;
     };
     auto chunk_col = [&](int e) { return 4 * (tid + THREADS * e); };
-    if (p.vec && (p.num_cols & 3) == 0) {
+    if (vec_rows) {
         // All of the thread's 16-byte loads in flight at once.
         const float ni = neg_inf();
         f32x4 v[kChunks];
 #pragma unroll
         for (int e = 0; e < kChunks; ++e) {
             const int c = chunk_col(e);
-            v[e] = c < p.num_cols ? *reinterpret_cast<const f32x4 *>(x + c) : f32x4{ni, ni, ni, ni};
+            v[e] = c < num_cols ? *reinterpret_cast<const f32x4 *>(x + c) : f32x4{ni, ni, ni, ni};
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) absorb(e, order_key(v[e / 4][e % 4]));
@@ -427,16 +426,21 @@ void topk_resident_kernel(TopkParams p) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int c = chunk_col(e / 4) + e % 4;
-            absorb(e, c < p.num_cols ? order_key(x[c]) : 0u);
+            absorb(e, c < num_cols ? order_key(x[c]) : 0u);
         }
     }
     auto key_top = [&](int e) { return e % 2 == 0 ? (top16[e / 2] & 0xffffu) : (top16[e / 2] >> 16); };
+    // The histograms are cleared after the row's loads are issued.
+    for (int b = tid; b < 2048; b += THREADS) {
+        sh.hist[b] = 0;
+        hist_list[b] = 0;
+    }
     int num_cand;
     block_exclusive_scan<THREADS>(cand, sh.wave_tmp, &num_cand);  // its barriers also publish the cleared histograms
 
     // Paths that need every key again (few candidates, or a list overflow)
     // re-read this thread's run of the row.
-    const RowView run{x, p.num_cols, 0, col0};
+    const RowView run{x, num_cols, 0, col0};
     const ListView no_list{nullptr, nullptr, 0};
     if (num_cand <= p.k) {
         place_picks<E, kFromRowRun, THREADS>(no_list, run, 0, 0, 0u, 0, out, sh);  // every candidate
@@ -859,8 +863,10 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
 
 template <int E, int THREADS, int WPE>
 hipError_t launch_resident(const TopkParams &p, hipStream_t stream) {
-    return launch_kernel(topk_resident_kernel<E, THREADS, WPE>, dim3((unsigned)p.num_rows),
-                         dim3(THREADS), stream, p);
+    // 16-byte loads for rows 16-byte aligned with whole 4-column chunks.
+    const int32_t vec_rows = p.vec && (p.num_cols & 3) == 0;
+    return launch_kernel(topk_resident_kernel<E, THREADS, WPE>, dim3((unsigned)p.num_rows), dim3(THREADS), stream,
+                         p.logits, p.logits_stride, p.num_cols, vec_rows, p);
 }
 
 // Columns per thread, rounded up to a multiple of 4 (16-byte loads), up to
