@@ -100,12 +100,12 @@ constexpr int kStoreNT = 2;
 //                     the number of vector-memory ops after each key
 //                     prefetch is fixed on every path;
 //   kModeGroupMax     (fused top-k, first pass) keep the maximum of each
-//                     16-key group of a row: the keys 4n .. 4n+3 of four
+//                     8-key group of a row: the keys 4n .. 4n+3 of two
 //                     consecutive tiles that lane n holds;
 //   kModeCandidates   (fused top-k, second pass) append the cells at or
 //                     above the row's floor to the row's candidate list.
 constexpr int kModeScores = 0, kModeScoresExact = 1, kModeGroupMax = 2, kModeCandidates = 3;
-constexpr int kGroupTiles = 4;  // tiles per group in kModeGroupMax (columns per group row: 256)
+constexpr int kGroupTiles = kFusedGroupTiles;  // tiles per group in kModeGroupMax (16 groups per row of them)
 
 // Inclusive prefix sum within each 16-lane row of a wavefront (DPP
 // row_shr 1, 2, 4, 8 with zero fill).

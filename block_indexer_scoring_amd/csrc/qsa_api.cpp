@@ -51,10 +51,10 @@ int current_cu_count() {
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-// Fused prefill top-k workspace: per row the maxima of 16-key groups, the
+// Fused prefill top-k workspace: per row the maxima of 8-key groups, the
 // floor key, the offsets of the column chunks' segments in the row's
 // candidate pool, a candidate count per chunk, and the pool (8-byte entries:
-// score key, column).  The pool holds every key above the floor (at most 16 (k - 1))
+// score key, column).  The pool holds every key above the floor (at most 8 (k - 1))
 // and at most k keys equal to it per chunk, and no chunk more than its
 // columns, so it never overflows; the floor kernel sizes each segment from
 // the group maxima.
@@ -83,10 +83,11 @@ FusedLayout fused_layout(int32_t num_rows, int32_t out_cols, int32_t topk, int n
         L.chunk = (int)((((int64_t)out_cols + qsa::kFusedMaxSegs - 1) / qsa::kFusedMaxSegs + 255) / 256 * 256);
         L.col_chunks = ((int64_t)out_cols + L.chunk - 1) / L.chunk;
     }
-    L.groups = 16 * (((int64_t)out_cols + 255) / 256);
+    constexpr int64_t kGroupRowCols = 64 * qsa::kFusedGroupTiles;  // columns of 16 groups
+    L.groups = 16 * (((int64_t)out_cols + kGroupRowCols - 1) / kGroupRowCols);
     // Each segment's room is also capped by its chunk's columns, so a row
     // never needs more than its columns.
-    L.pool_cap = 16 * (int64_t)(topk - 1) + L.col_chunks * topk;
+    L.pool_cap = qsa::kFusedGroupKeys * (int64_t)(topk - 1) + L.col_chunks * topk;
     if (L.pool_cap > out_cols) L.pool_cap = out_cols;
     auto seg = [](int64_t b) { return (b + 255) / 256 * 256; };
     int64_t o = 0;
@@ -802,7 +803,7 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     fp.cand_cnt = reinterpret_cast<int32_t *>(ws + L.off_cnt);
     fp.seg_off = reinterpret_cast<int32_t *>(ws + L.off_segoff);
     fp.segs = (int32_t)L.col_chunks;
-    fp.groups_per_seg = L.chunk / 16;
+    fp.groups_per_seg = L.chunk / qsa::kFusedGroupKeys;
     fp.out_cols = out_cols;
     fp.pool_cap = (int32_t)L.pool_cap;
     fp.out = out_idx;

@@ -98,6 +98,10 @@ struct TopkParams {
 // Fused prefill top-k: floor and final select (see topk.hip).
 constexpr int kFusedMaxK = 2048;
 constexpr int kFusedMaxSegs = 256;   // column chunks per row
+// Keys per group maximum: a lane's 4 columns of kFusedGroupTiles consecutive
+// 64-column tiles, so 16 groups per 64 * kFusedGroupTiles columns.
+constexpr int kFusedGroupTiles = 2;
+constexpr int kFusedGroupKeys = 4 * kFusedGroupTiles;
 struct FusedTopkParams {
     int32_t num_rows, k;
     const float *gmax;

@@ -620,10 +620,11 @@ __global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
 // ---- Fused prefill top-k: the per-row floor and the final select. ----
 //
 // The fused path never writes the score matrix.  A first pass over the
-// scores keeps, per row, the maximum of each 16-key group.  The k-th largest
-// group maximum is the floor F: at least k keys of the row are >= F, so every
-// key of the row's top k is >= F; and keys > F can lie only in the fewer
-// than k groups whose maximum is > F (at most 16 (k-1) keys).  Of the keys
+// scores keeps, per row, the maximum of each group of G = kFusedGroupKeys
+// keys.  The k-th largest group maximum is the floor F: at least k keys of
+// the row are >= F, so every key of the row's top k is >= F; and keys > F
+// can lie only in the fewer than k groups whose maximum is > F (at most
+// G (k-1) keys).  Of the keys
 // equal to F only the lowest columns can be picked, so each column chunk
 // keeps at most its first k of them.  A second pass writes those candidates,
 // per (row, column chunk) segment in column order, and the select below
@@ -633,10 +634,11 @@ __global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
 // F per row as a score key: the k-th largest group maximum, or 0 (every
 // visible key is a candidate) when fewer than k groups hold a visible key.
 // One wave per row, an exact radix select over the keys' 11 + 11 + 10 bits.
-// Then each column chunk's room in the row's candidate pool: 16 per group
+// Then each column chunk's room in the row's candidate pool: G per group
 // whose maximum is above F (every key in it may be), plus the keys equal to
-// F it may keep, at most k and at most 16 per group whose maximum is >= F.
-// These sum to at most 16 (k - 1) + chunks * k, the pool's size.
+// F it may keep, at most k and at most G per group whose maximum is >= F,
+// and never more than the chunk's columns.  These sum to at most
+// min(G (k - 1) + chunks * k, columns), the pool's size.
 __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
     __shared__ __attribute__((aligned(16))) int hist[4][2048];
     __shared__ int groups_gt[4][kFusedMaxSegs], groups_eq[4][kFusedMaxSegs];
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
     // Rows of up to 64 * kFloorRegs groups keep their keys in registers
     // (lane l: groups l, l + 64, ...), loaded all at once; longer rows are
     // read from memory in each pass.
-    constexpr int kFloorRegs = 32;
+    constexpr int kFloorRegs = 64;
     const bool in_regs = p.gmax_stride <= 64 * kFloorRegs;
     uint32_t rk[kFloorRegs];
 #pragma unroll
@@ -722,8 +724,9 @@ __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
         if (sg < p.segs) {
             // No more than the chunk's cells either, so a row's segments
             // never exceed its columns.
-            const int seg_cols = min(16 * p.groups_per_seg, p.out_cols - sg * 16 * p.groups_per_seg);
-            room = min(16 * cgt[sg] + min(p.k, 16 * (cgt[sg] + ceq[sg])), seg_cols);
+            constexpr int G = kFusedGroupKeys;
+            const int seg_cols = min(G * p.groups_per_seg, p.out_cols - sg * G * p.groups_per_seg);
+            room = min(G * cgt[sg] + min(p.k, G * (cgt[sg] + ceq[sg])), seg_cols);
         }
         const int incl = (int)wave_inclusive_scan((uint32_t)room);
         if (sg < p.segs) off[sg] = run + incl - room;

@@ -545,8 +545,8 @@ int qsa_topk_blocks(const float *logits, int64_t logits_stride, int32_t num_rows
  *   workspace  : device memory of at least qsa_prefill_topk_workspace_bytes
  *                bytes, 256-byte aligned, owned by the caller; its contents
  *                on entry do not matter and are clobbered.  About
- *                num_rows * (8 * min(16 * (topk - 1) + chunks * topk, out_cols)
- *                + out_cols / 4) bytes, chunks being the column chunks per
+ *                num_rows * (8 * min(8 * (topk - 1) + chunks * topk, out_cols)
+ *                + out_cols / 2) bytes, chunks being the column chunks per
  *                row (as few as fill the CUs with row blocks of 128 rows; 4
  *                for 8,192 rows on 256 CUs), of which a call touches a few
  *                percent.  The size depends on the sizes and the device's CU

@@ -517,9 +517,10 @@ def test_fused_prefill_topk_zero_rows_and_workspace_size(lib):
     assert _fused(lib, rows=0, q=None, out=None, ws=None) == 0
     n = ctypes.c_int64(-1)
     assert lib.qsa_prefill_topk_workspace_bytes(8192, 27048, 512, ctypes.byref(n)) == 0
-    # Group maxima, top-k group indices and two candidate arrays of
-    # 16 (k - 1) + chunks * k entries per row, each a few bytes per entry.
-    assert 8192 * 8 * (16 * 511 + 512) < n.value < 8192 * (8 * (16 * 511 + 8 * 512) + 27048)
+    # Group maxima of 8-key groups (4 B each) and a candidate pool of
+    # 8 (k - 1) + chunks * k 8-byte entries per row: under the 512 MiB the
+    # 886 MB score matrix would exceed.
+    assert 8192 * 8 * (8 * 511 + 512) < n.value < 512 * 2**20
     m = ctypes.c_int64(-1)
     assert lib.qsa_prefill_topk_workspace_bytes(100, 27048, 512, ctypes.byref(m)) == 0
     assert 0 < m.value < n.value
