@@ -304,7 +304,12 @@ def main(argv=None) -> int:
         "row_k_end": torch.empty(T_all, dtype=torch.int32, device=dev),
     }
     dec_out = torch.empty((T_dec, dec.out_cols), dtype=torch.float32, device=dev)
-    pre_out = torch.empty((T_pre, pre.out_cols), dtype=torch.float32, device=dev)
+    # The score matrix's rows start on 128-byte lines (a row pitch rounded up
+    # to 32 floats: 27,072 for 27,048 columns), a layout the caller chooses;
+    # the padding is never written or read.  An unpadded pitch runs the
+    # kernel's line-aligned store layout instead (`prefill_natural_pitch`).
+    pre_pitch = (pre.out_cols + 31) // 32 * 32
+    pre_out = torch.empty((T_pre, pre_pitch), dtype=torch.float32, device=dev)[:, :pre.out_cols]
     TOPK = 512
     dec_top = torch.empty((T_dec, TOPK), dtype=torch.int32, device=dev)
     pre_top = torch.empty((T_pre, TOPK), dtype=torch.int32, device=dev)
@@ -420,6 +425,7 @@ def main(argv=None) -> int:
             "decode_requests": R, "decode_query_len": DQL, "decode_keys": int(comp_total),
             "page_size": dec.page_size, "decode_key_pools": len(pools),
             "prefill_rows": T_pre, "prefill_keys": int(pre.k.shape[0]), "topk": TOPK,
+            "score_row_pitch": pre_pitch,
         },
         "roofline": roof("hbm", decode_gbps, HBM_PEAK_GBPS, "GB/s",
                          read_traffic("decode.hip", "decode")),
@@ -498,6 +504,33 @@ def main(argv=None) -> int:
     }
     del fz_ws
 
+    # The same prefill rows with an unpadded row pitch (27,048 floats, rows
+    # not on 128-byte lines): the kernel's line-aligned (rotated) store
+    # layout.  6 launches after 4 warmup ones, back to back; compared with
+    # the step's own last scores (still in pre_out).
+    nat_out = torch.empty((T_pre, pre.out_cols), dtype=torch.float32, device=dev)
+    nat_ev = [HipEvents(2) for _ in range(6)]
+    for j in range(6 + 4):
+        if j >= 4:
+            check(lib.qsa_set_launch_events(nat_ev[j - 4].ev[0], nat_ev[j - 4].ev[1]))
+        check(lib.qsa_mqa_prefill(
+            q_pre.data_ptr(), q_pre.stride(0), q_pre.stride(1), k_pre.data_ptr(), k_pre.stride(0),
+            k_pre.shape[0], meta["row_k_start"].data_ptr() + 4 * T_dec,
+            meta["row_k_end"].data_ptr() + 4 * T_dec, T_pre, 4, 128, scale, nat_out.data_ptr(),
+            nat_out.stride(0), nat_out.shape[1], sh))
+        check(lib.qsa_set_launch_events(None, None))
+    torch.cuda.synchronize()
+    nat_us = float(np.mean([e.elapsed_us(0, 1) for e in nat_ev]))
+    result["prefill_natural_pitch"] = {
+        "us": round(nat_us, 3), "row_pitch": pre.out_cols, "step_row_pitch": pre_pitch,
+        "tflops": round(pflops / (nat_us * 1e-6) / 1e12, 2),
+        "frac_of_mfma": round(pflops / (nat_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "matches_step": bool(torch.equal(nat_out, pre_out)),
+    }
+    for e in nat_ev:
+        e.close()
+    del nat_out
+
     # The typed entry points on the same workloads, for context.  Decode
     # reads the batch's key caches written as e4m3 codes (the fp8 cache write
     # rule of the shared input generator): the 8 pools' codes and their
@@ -552,6 +585,7 @@ def main(argv=None) -> int:
     for e in ty_ev:
         e.close()
     del q16, k16
+
 
     # The other workload configurations, for context: each timed over its own
     # launches with the same per-kernel events, inputs resident in HBM.
