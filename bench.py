@@ -641,7 +641,9 @@ def main(argv=None) -> int:
         w_q, w_k = to_bf16(w.q), to_bf16(w.k)
         w_meta = qsa.qsa_build_metadata(to_i32(w.query_start_loc), to_i32(w.seq_lens), Tw,
                                         key_offsets=to_i32(w.key_offsets))
-        w_out = torch.empty((Tw, w.out_cols), dtype=torch.float32, device=dev)
+        # Rows on 128-byte lines, as in the step.
+        w_pitch = (w.out_cols + 31) // 32 * 32
+        w_out = torch.empty((Tw, w_pitch), dtype=torch.float32, device=dev)[:, :w.out_cols]
 
         def p_launch(j, w_q=w_q, w_k=w_k, w_meta=w_meta, w_out=w_out, Tw=Tw):
             check(lib.qsa_mqa_prefill(
@@ -655,7 +657,7 @@ def main(argv=None) -> int:
         configs[name] = {"kernel": "prefill", "us": round(p_mean, 3), "us_median": round(p_med, 3),
                          "flops": w_flops, "tflops": round(w_tflops, 2),
                          "frac_of_mfma": round(w_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "out_bytes": float(Tw) * w.out_cols * 4}
+                         "out_bytes": float(Tw) * w.out_cols * 4, "row_pitch": w_pitch}
         if name == "prefill_4x4k_100k":
             w_top = torch.empty((Tw, TOPK), dtype=torch.int32, device=dev)
 
