@@ -117,15 +117,6 @@ __device__ __forceinline__ uint32_t row16_inclusive_scan(uint32_t x) {
     return x;
 }
 
-// Order-preserving key of a score (scores are >= +0 or -inf): 0 for -inf,
-// so every visible cell has a key above 0.
-__device__ __forceinline__ uint32_t score_key(float v) {
-    if (!(v > neg_inf())) return 0u;
-    uint32_t u = __float_as_uint(v);
-    if ((u << 1) == 0u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 // kF16: Q and K are fp16 rather than bf16 (the same layout and staging; only
 // the MFMA's operand type differs).  kRotate (kModeScoresExact only): the
 // line-aligned store layout below, for outputs whose rows do not all start
@@ -146,9 +137,10 @@ void prefill_kernel(PrefillParams p) {
     __shared__ int s_end[kBM];  // min(row_k_end, num_keys)
     __shared__ int s_done[kBM];
     __shared__ int s_cur, s_lim;
-    // kModeCandidates, per row of the workgroup: the floor key and the
-    // segment's offset and size in the row's candidate pool.
-    __shared__ uint32_t c_fkey[kFused ? kBM : 1];
+    // kModeCandidates, per row of the workgroup: the floor as the float
+    // thresholds for "above" and "equal", and the segment's offset and size
+    // in the row's candidate pool.
+    __shared__ float c_fgt[kFused ? kBM : 1], c_feq[kFused ? kBM : 1];
     __shared__ int c_seg0[kFused ? kBM : 1], c_segn[kFused ? kBM : 1];
 
     const int tid = threadIdx.x;
@@ -287,7 +279,15 @@ void prefill_kernel(PrefillParams p) {
                 const bool cand = !s_done[i] && s_start[i] == cur;
                 const int32_t *so = p.seg_off + (int64_t)row * (p.col_chunks + 1) + cc;
                 const int s0 = cand ? min(so[0], p.pool_cap) : 0;
-                c_fkey[i] = cand ? p.floor_key[row] : 0u;
+                // The float whose key is the floor key F.  Keys order like
+                // the floats (-0 with +0; -inf and NaN have key 0), so for
+                // any score x: key(x) > F iff x > f, and key(x) == F iff
+                // x == f.  F = 0 (no floor): every visible score is above
+                // -inf, and none equals NaN.
+                const uint32_t fk = cand ? p.floor_key[row] : 0u;
+                const float f = __uint_as_float((fk & 0x80000000u) ? (fk & 0x7fffffffu) : ~fk);
+                c_fgt[i] = fk == 0u ? neg_inf() : f;
+                c_feq[i] = fk == 0u ? __uint_as_float(0x7fc00000u) : f;
                 c_seg0[i] = s0;
                 c_segn[i] = cand ? min(so[1], p.pool_cap) - s0 : 0;  // within the pool in any case
             }
@@ -470,42 +470,65 @@ void prefill_kernel(PrefillParams p) {
                 // Cells above the floor, and the first `topk` cells equal to
                 // it in this chunk, appended in column order to the row's
                 // segment for this chunk (lanes 16q4 .. 16q4+15 hold this
-                // row's keys 4n .. 4n+3).
-                const uint32_t fk = c_fkey[ri];
-                uint32_t kv[4];
-                int ngt = 0, neq = 0;
+                // row's keys 4n .. 4n+3).  The floor is compared as a float
+                // (fgt for "above", feq for "equal"), which orders scores as
+                // their keys do.  Entries hold the score's bits: a taken score
+                // is >= +0, so its key is those bits with the sign bit set.
+                const float fgt = c_fgt[ri], feq = c_feq[ri];
+                bool gt[4], eq[4];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    kv[g] = score_key(v[g]);
-                    ngt += kv[g] > fk;
-                    neq += kv[g] == fk && kv[g] != 0u;
+                    gt[g] = v[g] > fgt;
+                    eq[g] = v[g] == feq;
                 }
-                const uint32_t packed = ((uint32_t)ngt << 16) | (uint32_t)neq;
-                const uint32_t incl = row16_inclusive_scan(packed);
-                const uint32_t excl = incl - packed;
-                // The row's totals: lane 15 of each 16-lane row, broadcast within
-                // the row by DPP (row_newbcast:15), with no LDS round trip.
-                const uint32_t tot = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x15F, 0xf, 0xf, false);
-                const int teq = c_teq[mt], nc = c_ncand[mt], segn = c_segn[ri];
-                const int avail = max(p.topk - teq, 0);
-                const int nw = (int)(tot >> 16) + min((int)(tot & 0xffffu), avail);
-                int eqi = (int)(excl & 0xffffu);
-                int pos = nc + (int)(excl >> 16) + min(eqi, avail);
-                c_teq[mt] = teq + (int)(tot & 0xffffu);
-                c_ncand[mt] = nc + nw;
-                // Exactly four 8-byte stores per slice, one per cell (dropped
-                // unless the cell is taken and fits the segment).
+                const int nc = c_ncand[mt], segn = c_segn[ri];
                 const int sbase = ri * p.pool_cap + c_seg0[ri];
+                // The row's totals below: lane 15 of each 16-lane row,
+                // broadcast within the row by DPP (row_newbcast:15).
+                if (__builtin_expect(__ballot((eq[0] || eq[1]) || (eq[2] || eq[3])) == 0, 1)) {
+                    // No cell of the wave equals its row's floor (the usual
+                    // case): the cells above it, in column order.
+                    const uint32_t cnt = (uint32_t)(((int)gt[0] + (int)gt[1]) + ((int)gt[2] + (int)gt[3]));
+                    const uint32_t incl = row16_inclusive_scan(cnt);
+                    const uint32_t tot = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x15F, 0xf, 0xf, false);
+                    int pos = nc + (int)(incl - cnt);
+                    c_ncand[mt] = nc + (int)tot;
+                    // Exactly four 8-byte stores per slice, one per cell
+                    // (dropped unless the cell is taken and fits the segment).
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const bool is_gt = kv[g] > fk;
-                    const bool is_eq = kv[g] == fk && kv[g] != 0u;
-                    const bool take = is_gt || (is_eq && eqi < avail);
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{kv[g], (uint32_t)(col + g)}, fused_rsrc,
-                                                          take && pos < segn ? (uint32_t)(sbase + pos) * 8u : kDropped,
-                                                          0, 0);
-                    pos += take;
-                    eqi += is_eq;
+                    for (int g = 0; g < 4; ++g) {
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            u32x2{__float_as_uint(v[g]), (uint32_t)(col + g)}, fused_rsrc,
+                            gt[g] && pos < segn ? (uint32_t)(sbase + pos) * 8u : kDropped, 0, 0);
+                        pos += gt[g];
+                    }
+                } else {
+                    int ngt = 0, neq = 0;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        ngt += gt[g];
+                        neq += eq[g];
+                    }
+                    const uint32_t packed = ((uint32_t)ngt << 16) | (uint32_t)neq;
+                    const uint32_t incl = row16_inclusive_scan(packed);
+                    const uint32_t excl = incl - packed;
+                    const uint32_t tot = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x15F, 0xf, 0xf, false);
+                    const int teq = c_teq[mt];
+                    const int avail = max(p.topk - teq, 0);
+                    const int nw = (int)(tot >> 16) + min((int)(tot & 0xffffu), avail);
+                    int eqi = (int)(excl & 0xffffu);
+                    int pos = nc + (int)(excl >> 16) + min(eqi, avail);
+                    c_teq[mt] = teq + (int)(tot & 0xffffu);
+                    c_ncand[mt] = nc + nw;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const bool take = gt[g] || (eq[g] && eqi < avail);
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            u32x2{__float_as_uint(v[g]), (uint32_t)(col + g)}, fused_rsrc,
+                            take && pos < segn ? (uint32_t)(sbase + pos) * 8u : kDropped, 0, 0);
+                        pos += take;
+                        eqi += eq[g];
+                    }
                 }
             }
         };

@@ -81,7 +81,7 @@ struct PrefillParams {
     int32_t gmax_stride;        // groups per row: 16 * ceil(out_cols / 256)
     const uint32_t *floor_key;  // [rows] per-row floor (score key)
     const int32_t *seg_off;     // [rows][col_chunks + 1] segment offsets in the row's pool
-    uint32_t *cand;             // [rows][pool_cap][2] candidates: score key, column
+    uint32_t *cand;             // [rows][pool_cap][2] candidates: score bits (>= +0), column
     int32_t *cand_cnt;          // [rows][col_chunks] candidates per segment
     int32_t pool_cap;
 };
@@ -108,7 +108,7 @@ struct FusedTopkParams {
     int32_t gmax_stride;        // groups per row
     uint32_t *floor_key;        // [rows] the floor as a score key
     int32_t *seg_off;           // [rows][segs + 1] segment offsets in the row's pool
-    const uint32_t *cand;       // [rows][pool_cap][2]: score key, column
+    const uint32_t *cand;       // [rows][pool_cap][2]: score bits (>= +0), column
     const int32_t *cand_cnt;    // [rows][segs]
     int32_t segs;               // column chunks
     int32_t groups_per_seg;     // groups per column chunk

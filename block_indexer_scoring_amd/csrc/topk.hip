@@ -633,12 +633,15 @@ __global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
 
 // F per row as a score key: the k-th largest group maximum, or 0 (every
 // visible key is a candidate) when fewer than k groups hold a visible key.
-// One wave per row, an exact radix select over the keys' 11 + 11 + 10 bits.
-// Then each column chunk's room in the row's candidate pool: G per group
-// whose maximum is above F (every key in it may be), plus the keys equal to
-// F it may keep, at most k and at most G per group whose maximum is >= F,
-// and never more than the chunk's columns.  These sum to at most
-// min(G (k - 1) + chunks * k, columns), the pool's size.
+// One wave per row, an exact radix select over the keys' bits below the
+// ones every visible group maximum shares: those are known from the row's
+// OR and AND, so the first 11-bit histogram spreads over the row's own range
+// (the top bits of similar scores fall in a few bins, whose LDS atomics
+// would serialise).  Then each column chunk's room in the row's candidate
+// pool: G per group whose maximum is above F (every key in it may be), plus
+// the keys equal to F it may keep, at most k and at most G per group whose
+// maximum is >= F, and never more than the chunk's columns.  These sum to at
+// most min(G (k - 1) + chunks * k, columns), the pool's size.
 __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
     __shared__ __attribute__((aligned(16))) int hist[4][2048];
     __shared__ int groups_gt[4][kFusedMaxSegs], groups_eq[4][kFusedMaxSegs];
@@ -648,51 +651,87 @@ __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
     if (row >= p.num_rows) return;  // wave-uniform; this wave works alone below
     const float *g = p.gmax + row * p.gmax_stride;
     int *h = hist[wave];
-    uint32_t prefix = 0u, mask = 0u;
-    int kk = p.k;
-    bool found = true;
     // Rows of up to 64 * kFloorRegs groups keep their keys in registers
     // (lane l: groups l, l + 64, ...), loaded all at once; longer rows are
     // read from memory in each pass.
     constexpr int kFloorRegs = 64;
     const bool in_regs = p.gmax_stride <= 64 * kFloorRegs;
-    uint32_t rk[kFloorRegs];
+    uint32_t rk[kFloorRegs] = {};
+    if (in_regs) {
+        // Unconditional loads (indices clamped into the row), so all of them
+        // are in flight at once; lanes past the row's end then drop theirs.
+        float v[kFloorRegs];
 #pragma unroll
-    for (int j = 0; j < kFloorRegs; ++j) {
-        const int i = lane + 64 * j;
-        rk[j] = (in_regs && i < p.gmax_stride) ? order_key(g[i]) : 0u;
+        for (int j = 0; j < kFloorRegs; ++j) v[j] = g[min(lane + 64 * j, p.gmax_stride - 1)];
+#pragma unroll
+        for (int j = 0; j < kFloorRegs; ++j) rk[j] = lane + 64 * j < p.gmax_stride ? order_key(v[j]) : 0u;
     }
+    // Count, OR and AND of the visible keys (key 0 is never picked).
+    uint32_t kor = 0u, kand = ~0u;
+    int nz = 0;
+    if (in_regs) {
+#pragma unroll
+        for (int j = 0; j < kFloorRegs; ++j) {
+            const uint32_t key = rk[j];
+            kor |= key;
+            kand &= key != 0u ? key : ~0u;
+            nz += key != 0u;
+        }
+    } else {
+        for (int i = lane; i < p.gmax_stride; i += 64) {
+            const uint32_t key = order_key(g[i]);
+            kor |= key;
+            kand &= key != 0u ? key : ~0u;
+            nz += key != 0u;
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        kor |= (uint32_t)__shfl_xor((int)kor, o);
+        kand &= (uint32_t)__shfl_xor((int)kand, o);
+        nz += __shfl_xor(nz, o);
+    }
+    // Fewer than k visible group maxima: no floor (every visible key is a
+    // candidate).  Otherwise the low `bits` bits are still open.
+    const bool found = __builtin_amdgcn_readfirstlane(nz) >= p.k;
+    const uint32_t diff = __builtin_amdgcn_readfirstlane(kor ^ kand);
+    int bits = diff == 0u ? 0 : 32 - __builtin_clz(diff);
+    uint32_t mask = bits == 32 ? 0u : ~0u << bits;
+    uint32_t prefix = __builtin_amdgcn_readfirstlane(kand) & mask;
+    int kk = p.k;
     // One wave: its LDS operations take effect in issue order.
 #pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const int nb = pass == 2 ? 1024 : 2048;
-        for (int b = lane; b < nb; b += 64) h[b] = 0;
+    while (found && bits > 0) {
+        const int w = bits < 11 ? bits : 11;
+        const int shift = bits - w;
+        const uint32_t digit = (1u << w) - 1u;
+        // wave_find_bin scans all 2048 bins: clear them all.
+#pragma unroll
+        for (int b = 0; b < 2048 / 256; ++b) reinterpret_cast<int4 *>(h)[lane + 64 * b] = int4{0, 0, 0, 0};
         if (in_regs) {
 #pragma unroll
             for (int j = 0; j < kFloorRegs; ++j) {
                 const uint32_t key = rk[j];
-                if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & (nb - 1)], 1);
+                if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & digit], 1);
             }
         } else {
             for (int i = lane; i < p.gmax_stride; i += 64) {
                 const uint32_t key = order_key(g[i]);
-                if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & (nb - 1)], 1);
+                if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & digit], 1);
             }
         }
         int above;
-        const int bin = nb == 2048 ? wave_find_bin<2048>(h, kk, &above) : wave_find_bin<1024>(h, kk, &above);
-        if (bin < 0) {  // fewer than k visible group maxima
-            found = false;
-            break;
-        }
+        const int bin = wave_find_bin<2048>(h, kk, &above);  // >= 0: at least kk keys match the prefix
         kk -= above;
         prefix |= (uint32_t)bin << shift;
-        mask |= (uint32_t)(nb - 1) << shift;
+        mask |= digit << shift;
+        bits = shift;
     }
     const uint32_t T = found ? prefix : 0u;
     if (lane == 0) p.floor_key[row] = T;
     int *cgt = groups_gt[wave], *ceq = groups_eq[wave];
+    // In registers, i / groups_per_seg as a multiply-high: exact while
+    // i * groups_per_seg < 2^32 (here both are at most 4,096).
+    const uint32_t seg_magic = 0xFFFFFFFFu / (uint32_t)p.groups_per_seg + 1u;
     for (int sg = lane; sg < p.segs; sg += 64) {
         cgt[sg] = 0;
         ceq[sg] = 0;
@@ -703,7 +742,7 @@ __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
             const int i = lane + 64 * j;
             const uint32_t key = rk[j];
             if (i < p.gmax_stride) {
-                const int sg = i / p.groups_per_seg;
+                const int sg = (int)__umulhi((uint32_t)i, seg_magic);
                 if (key > T) atomicAdd(&cgt[sg], 1);
                 else if (key == T && key != 0u) atomicAdd(&ceq[sg], 1);
             }
@@ -753,7 +792,9 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
     const int k = p.k;
     const int segs = p.segs;
     const int64_t rbase = row * (int64_t)p.pool_cap;
-    const uint32_t *gcand = p.cand + 2 * rbase;  // entry e: key at 2e, column at 2e + 1
+    // Entry e: the score's bits at 2e (a score >= +0: its key is them with
+    // the sign bit set), its column at 2e + 1.
+    const uint32_t *gcand = p.cand + 2 * rbase;
     const int32_t *off = p.seg_off + row * (segs + 1);
     __shared__ int seg_base[kFusedMaxSegs];
     {
@@ -785,7 +826,7 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
     if (n <= kFusedListCap) {
         for (int pos = tid; pos < n; pos += kThreads) {
             const int64_t e = locate(pos);
-            lkey[pos] = gcand[2 * e];
+            lkey[pos] = gcand[2 * e] | 0x80000000u;
             lcol[pos] = (int32_t)gcand[2 * e + 1];
         }
         __syncthreads();
@@ -811,7 +852,7 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
             const int cnt = seg_start[sgi + 1] - seg_start[sgi];
             const uint32_t *sk = gcand + 2 * (int64_t)seg_base[sgi];
             for (int i = tid; i < cnt; i += kThreads) {
-                const uint32_t key = sk[2 * i];
+                const uint32_t key = sk[2 * i] | 0x80000000u;
                 if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1);
             }
         }
@@ -841,7 +882,7 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
         int sgi = seg_of(lo);
         for (int pos = lo; pos < hi; ++pos) {
             while (pos >= seg_start[sgi + 1]) ++sgi;
-            const uint32_t key = gcand[2 * ((int64_t)seg_base[sgi] + (pos - seg_start[sgi]))];
+            const uint32_t key = gcand[2 * ((int64_t)seg_base[sgi] + (pos - seg_start[sgi]))] | 0x80000000u;
             gt += key > T;
             eq += key == T;
         }
@@ -854,10 +895,12 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
         for (int pos = lo; pos < hi; ++pos) {
             while (pos >= seg_start[sgi + 1]) ++sgi;
             const int64_t e = (int64_t)seg_base[sgi] + (pos - seg_start[sgi]);
-            const uint32_t key = gcand[2 * e];
+            const uint32_t key = gcand[2 * e] | 0x80000000u;
             const bool is_gt = key > T, is_eq = key == T;
-            if (is_gt) out[gt_before + min(eq_before, need)] = (int32_t)gcand[2 * e + 1];
-            else if (is_eq && eq_before < need) out[gt_before + eq_before] = (int32_t)gcand[2 * e + 1];
+            // Slots below k by construction (gt_total + need = k); checked
+            // all the same, so an inconsistent pool cannot write past the row.
+            const int at = is_gt ? gt_before + min(eq_before, need) : gt_before + eq_before;
+            if ((is_gt || (is_eq && eq_before < need)) && at < k) out[at] = (int32_t)gcand[2 * e + 1];
             gt_before += is_gt;
             eq_before += is_eq;
         }
