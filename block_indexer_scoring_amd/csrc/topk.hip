@@ -39,6 +39,7 @@ namespace qsa {
 namespace {
 
 constexpr int kMaxWaves = 16;  // workgroups of at most 1024 threads
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: raw dword access
 
 __device__ __forceinline__ uint32_t order_key(float v) {
     if (!(v > neg_inf())) return 0u;  // -inf and NaN are never picked
@@ -645,7 +646,7 @@ __global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
 __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
     __shared__ __attribute__((aligned(16))) int hist[4][2048];
     __shared__ int groups_gt[4][kFusedMaxSegs], groups_eq[4][kFusedMaxSegs];
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: row, g and g_rsrc are scalar
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave;
     if (row >= p.num_rows) return;  // wave-uniform; this wave works alone below
@@ -656,16 +657,18 @@ __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
     // read from memory in each pass.
     constexpr int kFloorRegs = 64;
     const bool in_regs = p.gmax_stride <= 64 * kFloorRegs;
-    uint32_t rk[kFloorRegs] = {};
-    if (in_regs) {
-        // Unconditional loads (indices clamped into the row), so all of them
-        // are in flight at once; lanes past the row's end then drop theirs.
-        float v[kFloorRegs];
+    // Unconditional loads through a buffer resource bounded by the row (a
+    // load past its end returns 0, and none are made when the row is read
+    // from memory instead), so all of them are in flight at once; lanes past
+    // the row's end then drop theirs.
+    const __amdgpu_buffer_rsrc_t g_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(g), 0, in_regs ? p.gmax_stride * 4 : 0, kBufferWord3);
+    uint32_t rk[kFloorRegs];
 #pragma unroll
-        for (int j = 0; j < kFloorRegs; ++j) v[j] = g[min(lane + 64 * j, p.gmax_stride - 1)];
+    for (int j = 0; j < kFloorRegs; ++j) rk[j] = __builtin_amdgcn_raw_buffer_load_b32(g_rsrc, lane * 4, 256 * j, 0);
 #pragma unroll
-        for (int j = 0; j < kFloorRegs; ++j) rk[j] = lane + 64 * j < p.gmax_stride ? order_key(v[j]) : 0u;
-    }
+    for (int j = 0; j < kFloorRegs; ++j)
+        rk[j] = lane < p.gmax_stride - 64 * j ? order_key(__uint_as_float(rk[j])) : 0u;
     // Count, OR and AND of the visible keys (key 0 is never picked).
     uint32_t kor = 0u, kand = ~0u;
     int nz = 0;
@@ -729,23 +732,45 @@ __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
     const uint32_t T = found ? prefix : 0u;
     if (lane == 0) p.floor_key[row] = T;
     int *cgt = groups_gt[wave], *ceq = groups_eq[wave];
-    // In registers, i / groups_per_seg as a multiply-high: exact while
-    // i * groups_per_seg < 2^32 (here both are at most 4,096).
-    const uint32_t seg_magic = 0xFFFFFFFFu / (uint32_t)p.groups_per_seg + 1u;
     for (int sg = lane; sg < p.segs; sg += 64) {
         cgt[sg] = 0;
         ceq[sg] = 0;
     }
     if (in_regs) {
+        // Segments hold a multiple of 32 groups (chunks are multiples of 256
+        // columns), so lanes 0-31 and 32-63 of register j each lie in one
+        // segment: counted by ballots, summed in scalar registers and
+        // written once per segment (segments come in increasing order).
+        // The segment of group i is a multiply-high, exact while
+        // i * groups_per_seg < 2^32 (here both are at most 4,096).
+        const uint32_t seg_magic = 0xFFFFFFFFu / (uint32_t)p.groups_per_seg + 1u;
+        int cur = 0, agt = 0, aeq = 0;
+        auto add_half = [&](int sg, int ng, int ne) {
+            if (sg != cur) {
+                if (lane == 0) {
+                    cgt[cur] = agt;
+                    ceq[cur] = aeq;
+                }
+                cur = sg;
+                agt = 0;
+                aeq = 0;
+            }
+            agt += ng;
+            aeq += ne;
+        };
 #pragma unroll
         for (int j = 0; j < kFloorRegs; ++j) {
-            const int i = lane + 64 * j;
-            const uint32_t key = rk[j];
-            if (i < p.gmax_stride) {
-                const int sg = (int)__umulhi((uint32_t)i, seg_magic);
-                if (key > T) atomicAdd(&cgt[sg], 1);
-                else if (key == T && key != 0u) atomicAdd(&ceq[sg], 1);
+            if (64 * j < p.gmax_stride) {  // keys past the row's end are 0: never counted
+                const uint64_t mg = __ballot(rk[j] > T);
+                const uint64_t me = __ballot(rk[j] == T && rk[j] != 0u);
+                add_half((int)__umulhi((uint32_t)(64 * j), seg_magic), __popc((uint32_t)mg), __popc((uint32_t)me));
+                add_half((int)__umulhi((uint32_t)(64 * j + 32), seg_magic), __popc((uint32_t)(mg >> 32)),
+                         __popc((uint32_t)(me >> 32)));
             }
+        }
+        if (lane == 0) {
+            cgt[cur] = agt;
+            ceq[cur] = aeq;
         }
     } else {
         for (int i = lane; i < p.gmax_stride; i += 64) {
