@@ -137,11 +137,10 @@ void prefill_kernel(PrefillParams p) {
     __shared__ int s_end[kBM];  // min(row_k_end, num_keys)
     __shared__ int s_done[kBM];
     __shared__ int s_cur, s_lim;
-    // kModeCandidates, per row of the workgroup: the floor as the float
-    // thresholds for "above" and "equal", and the segment's offset and size
-    // in the row's candidate pool.
-    __shared__ float c_fgt[kFused ? kBM : 1], c_feq[kFused ? kBM : 1];
-    __shared__ int c_seg0[kFused ? kBM : 1], c_segn[kFused ? kBM : 1];
+    // kModeCandidates, per row of the workgroup: the floor as a float, and
+    // the segment's start (an entry index in the workgroup's pools) and size.
+    __shared__ float c_floor[kFused ? kBM : 1];
+    __shared__ int c_sbase[kFused ? kBM : 1], c_segn[kFused ? kBM : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -279,16 +278,17 @@ void prefill_kernel(PrefillParams p) {
                 const bool cand = !s_done[i] && s_start[i] == cur;
                 const int32_t *so = p.seg_off + (int64_t)row * (p.col_chunks + 1) + cc;
                 const int s0 = cand ? min(so[0], p.pool_cap) : 0;
-                // The float whose key is the floor key F.  Keys order like
-                // the floats (-0 with +0; -inf and NaN have key 0), so for
-                // any score x: key(x) > F iff x > f, and key(x) == F iff
-                // x == f.  F = 0 (no floor): every visible score is above
-                // -inf, and none equals NaN.
+                // The float f whose key is the floor key F.  Keys order like
+                // the floats (-0 with +0; -inf and NaN have key 0), so for a
+                // score x: key(x) > F iff x > f, and key(x) == F iff x == f.
+                // F = 0 (no floor): f = -inf, which every visible score is
+                // above and none equals.  Rows outside this pass: f = NaN,
+                // which nothing is above or equal to; cells outside a row's
+                // keys are NaN in the epilogue for the same reason.
                 const uint32_t fk = cand ? p.floor_key[row] : 0u;
                 const float f = __uint_as_float((fk & 0x80000000u) ? (fk & 0x7fffffffu) : ~fk);
-                c_fgt[i] = fk == 0u ? neg_inf() : f;
-                c_feq[i] = fk == 0u ? __uint_as_float(0x7fc00000u) : f;
-                c_seg0[i] = s0;
+                c_floor[i] = !cand ? __uint_as_float(0x7fc00000u) : (fk == 0u ? neg_inf() : f);
+                c_sbase[i] = i * p.pool_cap + s0;
                 c_segn[i] = cand ? min(so[1], p.pool_cap) - s0 : 0;  // within the pool in any case
             }
             __syncthreads();
@@ -446,14 +446,16 @@ void prefill_kernel(PrefillParams p) {
                 return;
             }
             const int ri = a_w + dl * (4 * mt + q4);  // row in the workgroup
-            const int row = row0 + ri;
             const int col = tile_c + lc;
+            // Rows outside this pass are never stored (group maxima) or have
+            // a NaN floor (candidates), so only the key range is checked.
             f32x4 v;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int c = col + g;
-                const bool ok = in_pass[mt] && (!masked || (c < row_lim[mt] && c >= col_min && c < c_end));
-                v[g] = ok ? head_sum_score(acc[g], p.scale) : neg_inf();
+                const bool ok = !masked || (c < row_lim[mt] && c >= col_min && c < c_end);
+                v[g] = ok ? head_sum_score(acc[g], p.scale)
+                          : (kMode == kModeCandidates ? __uint_as_float(0x7fc00000u) : neg_inf());
             }
             if (kMode == kModeGroupMax) {
                 gm[mt] = max(gm[mt], max(max(v[0], v[1]), max(v[2], v[3])));
@@ -470,19 +472,18 @@ void prefill_kernel(PrefillParams p) {
                 // Cells above the floor, and the first `topk` cells equal to
                 // it in this chunk, appended in column order to the row's
                 // segment for this chunk (lanes 16q4 .. 16q4+15 hold this
-                // row's keys 4n .. 4n+3).  The floor is compared as a float
-                // (fgt for "above", feq for "equal"), which orders scores as
-                // their keys do.  Entries hold the score's bits: a taken score
-                // is >= +0, so its key is those bits with the sign bit set.
-                const float fgt = c_fgt[ri], feq = c_feq[ri];
+                // row's keys 4n .. 4n+3).  The floor is compared as a float,
+                // which orders scores as their keys do.  Entries hold the
+                // score's bits: a taken score is >= +0, so its key is those
+                // bits with the sign bit set.
+                const float f = c_floor[ri];
                 bool gt[4], eq[4];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    gt[g] = v[g] > fgt;
-                    eq[g] = v[g] == feq;
+                    gt[g] = v[g] > f;
+                    eq[g] = v[g] == f;
                 }
-                const int nc = c_ncand[mt], segn = c_segn[ri];
-                const int sbase = ri * p.pool_cap + c_seg0[ri];
+                const int nc = c_ncand[mt], segn = c_segn[ri], sbase = c_sbase[ri];
                 // The row's totals below: lane 15 of each 16-lane row,
                 // broadcast within the row by DPP (row_newbcast:15).
                 if (__builtin_expect(__ballot((eq[0] || eq[1]) || (eq[2] || eq[3])) == 0, 1)) {
@@ -491,15 +492,18 @@ void prefill_kernel(PrefillParams p) {
                     const uint32_t cnt = (uint32_t)(((int)gt[0] + (int)gt[1]) + ((int)gt[2] + (int)gt[3]));
                     const uint32_t incl = row16_inclusive_scan(cnt);
                     const uint32_t tot = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x15F, 0xf, 0xf, false);
-                    int pos = nc + (int)(incl - cnt);
+                    int pos = nc + (int)incl - (int)cnt;
                     c_ncand[mt] = nc + (int)tot;
+                    // The segment holds every candidate by construction; a
+                    // lane whose cells would not all fit drops them all.
+                    const bool fits = pos + (int)cnt <= segn;
                     // Exactly four 8-byte stores per slice, one per cell
-                    // (dropped unless the cell is taken and fits the segment).
+                    // (dropped unless the cell is taken).
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         __builtin_amdgcn_raw_buffer_store_b64(
                             u32x2{__float_as_uint(v[g]), (uint32_t)(col + g)}, fused_rsrc,
-                            gt[g] && pos < segn ? (uint32_t)(sbase + pos) * 8u : kDropped, 0, 0);
+                            gt[g] && fits ? (uint32_t)(sbase + pos) * 8u : kDropped, 0, 0);
                         pos += gt[g];
                     }
                 } else {
