@@ -54,7 +54,7 @@ bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 // Fused prefill top-k workspace: per row the maxima of 8-key groups, the
 // floor key, the offsets of the column chunks' segments in the row's
 // candidate pool, a candidate count per chunk, and the pool (8-byte entries:
-// score key, column).  The pool holds every key above the floor (at most 8 (k - 1))
+// the score's bits, column).  The pool holds every key above the floor (at most 8 (k - 1))
 // and at most k keys equal to it per chunk, and no chunk more than its
 // columns, so it never overflows; the floor kernel sizes each segment from
 // the group maxima.
