@@ -283,7 +283,7 @@ __device__ __forceinline__ void place_picks(const ListView &list, const RowView 
 // row and written back into the list; with at most 64 of them, one per
 // lane, T is the kk-th largest by direct comparison, otherwise two 8-bit
 // passes over the list finish it.  Keys with other top halves compare with
-// T correctly either way.  tied_idx is 64 ints of scratch.  Requires at
+// T correctly either way.  tied_idx is 128 ints of scratch.  Requires at
 // least k listed keys.
 __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *cols, int n, int k,
                                                      const int *hist0, int *hist, int *tied_idx,
@@ -298,11 +298,13 @@ __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *
 #pragma unroll 1
     for (int i0 = 0; i0 < n; i0 += 256) {
         uint32_t key[4];
+        // Unconditional reads (index clamped into the list) so the four are
+        // in flight together; entries past the end are then dropped.
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = i0 + 64 * u + lane;
-            key[u] = i < n ? list[i] : 0u;
-        }
+        for (int u = 0; u < 4; ++u) key[u] = list[min(i0 + 64 * u + lane, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + 64 * u + lane >= n) key[u] = 0u;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             if ((key[u] >> 21) == (uint32_t)b0) atomicAdd(&hist[(key[u] >> 16) & 31], 1);
@@ -316,15 +318,26 @@ __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *
         return top << 16;
     }
     if (tied <= 64) {
-        // Lane p takes the p-th tied entry in list (column) order.
+        // Lane p takes the p-th tied entry in list (column) order; four
+        // 64-entry blocks per step, their reads in flight together.
         int base = 0;
 #pragma unroll 1
-        for (int i0 = 0; i0 < n; i0 += 64) {
-            const int i = i0 + lane;
-            const bool match = i < n && (list[i] >> 16) == top;
-            const uint64_t m = __ballot(match);
-            if (match) tied_idx[base + __popcll(m & ((1ull << lane) - 1ull))] = i;
-            base += __popcll(m);
+        for (int i0 = 0; i0 < n; i0 += 256) {
+            uint32_t key4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) key4[u] = list[min(i0 + 64 * u + lane, n - 1)];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + 64 * u + lane;
+                const bool match = i < n && (key4[u] >> 16) == top;
+                const uint64_t m = __ballot(match);
+                // Without a branch: lanes that do not match write a slot of
+                // their own past the first 64.
+                const int at = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                tied_idx[match ? at : 64 + lane] = i;
+                base += __popcll(m);
+            }
         }
         uint32_t key = 0u;
         if (lane < tied) {
@@ -332,16 +345,23 @@ __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *
             key = order_key(x[cols[idx]]);
             list[idx] = key;
         }
-        int gt = 0, eq = 0;
-        for (int m = 0; m < tied; ++m) {
-            const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)key, m);
-            gt += km > key;
-            eq += km == key;
+        // The kk-th largest of the tied keys (kk <= tied), which share the
+        // top half: most significant bit first over the low half, counting
+        // the keys that still match by ballot.  Keys with a 1 where T has a
+        // 0 are above T, so kr ends as the number of keys equal to T picked.
+        const bool act = lane < tied;
+        uint32_t t = 0u, msk = 0u;
+        int kr = kk;
+#pragma unroll
+        for (int bit = 15; bit >= 0; --bit) {
+            const uint32_t b = 1u << bit;
+            const int ones = __popcll(__ballot(act && (key & msk) == t && (key & b) != 0u));
+            if (kr <= ones) t |= b;
+            else kr -= ones;
+            msk |= b;
         }
-        const uint64_t hit = __ballot(lane < tied && gt < kk && kk <= gt + eq);
-        const int src = __builtin_ctzll(hit);
-        *need_out = kk - __builtin_amdgcn_readlane(gt, src);
-        return (uint32_t)__builtin_amdgcn_readlane((int)key, src);
+        *need_out = kr;
+        return (top << 16) | t;
     }
     for (int i = lane; i < n; i += 64)
         if ((list[i] >> 16) == top) list[i] = order_key(x[cols[i]]);
@@ -383,7 +403,7 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
     __shared__ __attribute__((aligned(16))) int hist_list[2048];  // listed keys by their top 11 bits
     __shared__ uint32_t list_key[kListCap];
     __shared__ int list_col[kListCap];
-    __shared__ int tied_idx[64];
+    __shared__ int tied_idx[128];
     __shared__ uint32_t s_floor, s_T;
     __shared__ int s_need;
     const int tid = threadIdx.x;
