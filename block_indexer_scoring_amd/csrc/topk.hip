@@ -189,8 +189,16 @@ __device__ __forceinline__ void count_bins(const ListView &list, const RowView &
             visit(c < row.cols ? order_key(row.x[c]) : 0u);
         }
     } else if (SRC == kFromList) {
+        // Four reads in flight per step (index clamped into the list).
 #pragma unroll 1
-        for (int i = threadIdx.x; i < list.size; i += THREADS) visit(list.key[i]);
+        for (int i0 = threadIdx.x; i0 < list.size; i0 += 4 * THREADS) {
+            uint32_t kb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kb[u] = list.key[min(i0 + u * THREADS, list.size - 1)];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i0 + u * THREADS < list.size) visit(kb[u]);
+        }
     } else {
 #pragma unroll 1
         for (int e = 0; e < row.slots; ++e) {
@@ -822,14 +830,14 @@ __global__ __launch_bounds__(256) void topk_floor_kernel(FusedTopkParams p) {
 // The exact top k of one row's candidates: larger keys first, equal keys to
 // the lower column (the earlier position, segments being in column order);
 // the picks are written in ascending column order, -1 padded.  Lists of up
-// to kFusedListCap entries are staged in LDS and reuse the row select above;
+// to kCap entries are staged in LDS and reuse the row select above;
 // longer ones are read in place.  One workgroup per row.
-constexpr int kFusedListCap = 2048;
+template <int kCap>
 __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p) {
     constexpr int kThreads = 256;
     __shared__ SelectShared sh;
-    __shared__ uint32_t lkey[kFusedListCap];
-    __shared__ int lcol[kFusedListCap];
+    __shared__ uint32_t lkey[kCap];
+    __shared__ int lcol[kCap];
     __shared__ int seg_start[kFusedMaxSegs + 1];
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
@@ -868,11 +876,22 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
         return;
     }
     const RowView none{nullptr, 0, 0, 0};
-    if (n <= kFusedListCap) {
-        for (int pos = tid; pos < n; pos += kThreads) {
-            const int64_t e = locate(pos);
-            lkey[pos] = gcand[2 * e] | 0x80000000u;
-            lcol[pos] = (int32_t)gcand[2 * e + 1];
+    if (n <= kCap) {
+        // Every entry's 8-byte load in flight at once (positions past the
+        // list read its last entry again and are dropped).
+        constexpr int kPer = kCap / kThreads;
+        u32x2 ent[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (j * kThreads < n)  // uniform
+                ent[j] = *reinterpret_cast<const u32x2 *>(gcand + 2 * locate(min(tid + kThreads * j, n - 1)));
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int pos = tid + kThreads * j;
+            if (j * kThreads < n && pos < n) {
+                lkey[pos] = ent[j][0] | 0x80000000u;
+                lcol[pos] = (int32_t)ent[j][1];
+            }
         }
         __syncthreads();
         const ListView list{lkey, lcol, n};
@@ -883,8 +902,26 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
         place_picks<1, kFromList, kThreads>(list, none, lo, hi, T, need, out, sh);
         return;
     }
-    // Long lists, read in place: the same radix select, counting segment by
-    // segment, then placement over contiguous position slices.
+    // Long lists, read in place: the same radix select, then placement over
+    // contiguous position slices.  Entries are read kBatch at a time with
+    // their loads in flight together; a thread's positions only increase,
+    // so its segment is tracked as it goes.
+    constexpr int kBatch = 8;
+    // The segment holding position pos (the last one starting at or before it).
+    auto seg_of = [&](int pos) {
+        int a = 0, b = segs - 1;
+        while (a < b) {
+            const int mid = (a + b + 1) >> 1;
+            if (seg_start[mid] <= pos) a = mid;
+            else b = mid - 1;
+        }
+        return a;
+    };
+    // Entry index of position pos (< n), at or after the last one asked for.
+    auto entry_of = [&](int pos, int &sgi) {
+        while (pos >= seg_start[sgi + 1]) ++sgi;
+        return (int64_t)seg_base[sgi] + (pos - seg_start[sgi]);
+    };
     uint32_t prefix = 0u, mask = 0u;
     int kk = k;
 #pragma unroll 1
@@ -893,12 +930,17 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
         const int nb = pass == 2 ? 1024 : 2048;
         for (int b = tid; b < nb; b += kThreads) sh.hist[b] = 0;
         __syncthreads();
-        for (int sgi = 0; sgi < segs; ++sgi) {
-            const int cnt = seg_start[sgi + 1] - seg_start[sgi];
-            const uint32_t *sk = gcand + 2 * (int64_t)seg_base[sgi];
-            for (int i = tid; i < cnt; i += kThreads) {
-                const uint32_t key = sk[2 * i] | 0x80000000u;
-                if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1);
+        int sgi = seg_of(min(tid, n - 1));
+#pragma unroll 1
+        for (int p0 = 0; p0 < n; p0 += kThreads * kBatch) {
+            uint32_t kb[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) kb[j] = gcand[2 * entry_of(min(p0 + tid + kThreads * j, n - 1), sgi)];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const uint32_t key = kb[j] | 0x80000000u;
+                if (p0 + tid + kThreads * j < n && (key & mask) == prefix)
+                    atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1);
             }
         }
         __syncthreads();
@@ -913,23 +955,21 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
     const int per = (n + kThreads - 1) / kThreads;
     const int lo = min(tid * per, n), hi = min(lo + per, n);
     int gt = 0, eq = 0;
-    // The segment holding position pos (the last one starting at or before it).
-    auto seg_of = [&](int pos) {
-        int a = 0, b = segs - 1;
-        while (a < b) {
-            const int mid = (a + b + 1) >> 1;
-            if (seg_start[mid] <= pos) a = mid;
-            else b = mid - 1;
-        }
-        return a;
-    };
     if (lo < hi) {
         int sgi = seg_of(lo);
-        for (int pos = lo; pos < hi; ++pos) {
-            while (pos >= seg_start[sgi + 1]) ++sgi;
-            const uint32_t key = gcand[2 * ((int64_t)seg_base[sgi] + (pos - seg_start[sgi]))] | 0x80000000u;
-            gt += key > T;
-            eq += key == T;
+#pragma unroll 1
+        for (int b0 = lo; b0 < hi; b0 += kBatch) {
+            uint32_t kb[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) kb[j] = gcand[2 * entry_of(min(b0 + j, hi - 1), sgi)];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const uint32_t key = kb[j] | 0x80000000u;
+                if (b0 + j < hi) {
+                    gt += key > T;
+                    eq += key == T;
+                }
+            }
         }
     }
     int gt_total, eq_total;
@@ -937,17 +977,24 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
     int eq_before = block_exclusive_scan<kThreads>(eq, sh.wave_tmp, &eq_total);
     if (lo < hi) {
         int sgi = seg_of(lo);
-        for (int pos = lo; pos < hi; ++pos) {
-            while (pos >= seg_start[sgi + 1]) ++sgi;
-            const int64_t e = (int64_t)seg_base[sgi] + (pos - seg_start[sgi]);
-            const uint32_t key = gcand[2 * e] | 0x80000000u;
-            const bool is_gt = key > T, is_eq = key == T;
-            // Slots below k by construction (gt_total + need = k); checked
-            // all the same, so an inconsistent pool cannot write past the row.
-            const int at = is_gt ? gt_before + min(eq_before, need) : gt_before + eq_before;
-            if ((is_gt || (is_eq && eq_before < need)) && at < k) out[at] = (int32_t)gcand[2 * e + 1];
-            gt_before += is_gt;
-            eq_before += is_eq;
+#pragma unroll 1
+        for (int b0 = lo; b0 < hi; b0 += kBatch) {
+            u32x2 eb[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                eb[j] = *reinterpret_cast<const u32x2 *>(gcand + 2 * entry_of(min(b0 + j, hi - 1), sgi));
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (b0 + j >= hi) break;
+                const uint32_t key = eb[j][0] | 0x80000000u;
+                const bool is_gt = key > T, is_eq = key == T;
+                // Slots below k by construction (gt_total + need = k); checked
+                // all the same, so an inconsistent pool cannot write past the row.
+                const int at = is_gt ? gt_before + min(eq_before, need) : gt_before + eq_before;
+                if ((is_gt || (is_eq && eq_before < need)) && at < k) out[at] = (int32_t)eb[j][1];
+                gt_before += is_gt;
+                eq_before += is_eq;
+            }
         }
     }
 }
@@ -977,7 +1024,12 @@ hipError_t launch_topk_floor(const FusedTopkParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_topk_candidates(const FusedTopkParams &p, hipStream_t stream) {
-    return launch_kernel(topk_candidates_kernel, dim3((unsigned)p.num_rows), dim3(256), stream, p);
+    // Pools of at most 4,096 entries (short rows, where most cells are
+    // candidates) always fit the larger LDS list; otherwise the smaller list
+    // keeps more rows per CU, and longer lists are read in place.
+    if (p.pool_cap <= 4096)
+        return launch_kernel(topk_candidates_kernel<4096>, dim3((unsigned)p.num_rows), dim3(256), stream, p);
+    return launch_kernel(topk_candidates_kernel<2048>, dim3((unsigned)p.num_rows), dim3(256), stream, p);
 }
 
 hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus) {
