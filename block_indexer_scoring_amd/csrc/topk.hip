@@ -474,9 +474,12 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
     if (num_cand <= p.k) {
         place_picks<E, kFromRowRun, THREADS>(no_list, run, 0, 0, 0u, 0, out, sh);  // every candidate
     } else {
-        // Floor: the lower edge of the 11-bit bin holding the k-th largest
-        // sub-run maximum; at least k keys are >= it.  1 (no filtering) when
-        // fewer than k sub-runs hold a candidate.
+        // Floor: the lower edge of the 16-bit bin holding the k-th largest
+        // sub-run maximum (its top 11 bits, then the next 5 among the
+        // maxima in that bin); at least k keys are >= it.  16 bits rather
+        // than 11 keep the list short when scores spread evenly over the
+        // 11-bit bin.  1 (no filtering) when fewer than k sub-runs hold a
+        // candidate.
 #pragma unroll
         for (int j = 0; j < kSub; ++j)
             if (smax[j] != 0u) atomicAdd(&sh.hist[smax[j] >> 21], 1);
@@ -484,9 +487,26 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
         if (tid < 64) {
             int above;
             const int bin = wave_find_bin<2048>(sh.hist, p.k, &above);
-            if (lane == 0) s_floor = bin <= 0 ? 1u : ((uint32_t)bin << 21);
+            if (lane == 0) {
+                s_floor = bin <= 0 ? 1u : ((uint32_t)bin << 21);
+                s_need = p.k - above;  // rank of the k-th largest maximum within its bin
+            }
         }
         __syncthreads();
+        if (s_floor > 1u) {  // uniform; hist_list is still all zero here
+            const uint32_t b0 = s_floor >> 21;
+#pragma unroll
+            for (int j = 0; j < kSub; ++j)
+                if ((smax[j] >> 21) == b0) atomicAdd(&hist_list[(smax[j] >> 16) & 31], 1);
+            __syncthreads();
+            if (tid < 64) {
+                int above;
+                const int b1 = wave_find_bin<32>(hist_list, s_need, &above);
+                if (lane == 0) s_floor |= (uint32_t)b1 << 16;
+            }
+            __syncthreads();
+            if (tid < 32) hist_list[tid] = 0;  // the list's histogram starts from zero
+        }
         const uint32_t floor = s_floor;
         // Listed: top half >= floor_top (candidates' top halves are never 0,
         // so floor_top >= 1 also drops the non-candidates).  Counted with

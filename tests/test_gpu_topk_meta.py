@@ -87,6 +87,30 @@ def test_topk_patterns_many_rows(cols, k):
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
+@pytest.mark.parametrize("rows,cols,k", [(300, 27048, 512), (64, 25600, 512), (300, 27048, 2048), (300, 5000, 512)])
+def test_topk_scores_spread_over_one_binade(rows, cols, k):
+    """Scores spread evenly over one binade, or over a narrow part of one:
+    the k-th largest sits in an 11-bit key bin holding most of the row, so
+    the floor is taken to 16 bits; in the narrowest rows even that bin holds
+    more keys than the list (the select then reads the row itself)."""
+    rng = np.random.default_rng(rows * 7 + cols + k)
+    x = np.empty((rows, cols), dtype=np.float32)
+    for r in range(rows):
+        kind = r % 4
+        if kind == 0:
+            x[r] = rng.uniform(2.0, 4.0, cols)          # one binade
+        elif kind == 1:
+            x[r] = rng.uniform(0.0, 3.0, cols)          # about two binades
+        elif kind == 2:
+            x[r] = rng.uniform(2.0, 2.001, cols)        # a sliver of one 16-bit key prefix
+        else:
+            x[r] = 2.0 + np.round(rng.uniform(0.0, 1.0, cols) * 256) / 256  # ties at 16-bit prefixes
+    x[rows // 2, cols // 2:] = -np.inf                  # a short row among them
+    got = _topk_gpu(x, k)
+    want = O.topk(x, k)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
 def test_topk_many_rows_and_strided_logits():
     rng = np.random.default_rng(5)
     big = rng.standard_normal((300, 700)).astype(np.float32)
