@@ -13,7 +13,8 @@
 // needed; a cell is picked if key > T, or key == T and fewer than `need`
 // equal keys precede it.
 //
-// Rows up to 32768 columns stay in registers (as the keys' top 16 bits).
+// Rows up to 32,768 columns (65,535 when there is at most one row per CU)
+// stay in registers (as the keys' top 16 bits).
 // Thread t of a workgroup of n threads holds the 4-column chunks t, t + n,
 // t + 2n, ...: each of its 16-byte loads is part of one contiguous read of
 // 16n bytes by the workgroup, so every 128-byte line is fetched by one
@@ -238,7 +239,7 @@ __device__ __forceinline__ uint32_t radix_threshold(const ListView &list, const 
 // Writes the picks of this thread's keys, which it visits in column order
 // (a run of the row, or the contiguous list slice [lo, hi)): one prefix sum
 // of packed (greater, equal) counts places every pick.  Counts stay below
-// 2^16 (at most 32768 keys per row here), so the low half never carries
+// 2^16 (at most 65,535 keys per row here), so the low half never carries
 // into the high half.
 template <int E, int SRC, int THREADS>
 __device__ __forceinline__ void place_picks(const ListView &list, const RowView &row, int lo, int hi,
@@ -1053,13 +1054,16 @@ hipError_t launch_topk_candidates(const FusedTopkParams &p, hipStream_t stream) 
 }
 
 hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus) {
-    if (p.num_cols > 32768)  // longer than the register-resident shapes hold
-        return launch_kernel(topk_streaming_kernel, dim3((unsigned)p.num_rows), dim3(1024), stream, p);
     // At most one row per CU: the latency of one row is the whole cost, so
-    // 1024-thread rows (registers for four waves per SIMD).  Many rows:
-    // 512-thread rows, four per CU (registers for eight waves per SIMD),
-    // up to 56 columns per thread; longer rows, 1024-thread rows two per CU.
-    if (p.num_rows <= (num_cus > 0 ? num_cus : 256)) return launch_config<1024, 4, 32>(p, stream);
+    // 1024-thread rows (registers for four waves per SIMD), up to 64 columns
+    // per thread (fewer than 2^16 per row, which the packed counts need).
+    // Many rows: 512-thread rows, four per CU (registers for eight waves per
+    // SIMD), up to 56 columns per thread; longer rows, 1024-thread rows two
+    // per CU.  Rows longer than these shapes hold are streamed.
+    const bool few = p.num_rows <= (num_cus > 0 ? num_cus : 256);
+    if (few && p.num_cols < 65536) return launch_config<1024, 4, 64>(p, stream);
+    if (p.num_cols > 32768)
+        return launch_kernel(topk_streaming_kernel, dim3((unsigned)p.num_rows), dim3(1024), stream, p);
     if (p.num_cols <= 512 * 56) return launch_config<512, 8, 56>(p, stream);
     return launch_config<1024, 8, 32>(p, stream);
 }

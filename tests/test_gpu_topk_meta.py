@@ -29,7 +29,7 @@ def _topk_gpu(x: np.ndarray, k: int):
 
 @pytest.mark.parametrize("cols,k", [(1, 1), (50, 7), (1000, 64), (4096, 512), (5000, 512),
                                     (26024, 512), (25600, 2048), (32768, 512), (40000, 512),
-                                    (3000, 4000), (9000, 1)])
+                                    (65535, 512), (65536, 512), (3000, 4000), (9000, 1)])
 def test_topk_bit_exact_on_given_logits(cols, k):
     rng = np.random.default_rng(cols + k)
     x = (np.abs(rng.standard_normal((9, cols))) * 3).astype(np.float32)
