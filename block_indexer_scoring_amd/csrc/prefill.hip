@@ -103,8 +103,12 @@ constexpr int kStoreNT = 2;
 //                     8-key group of a row: the keys 4n .. 4n+3 of two
 //                     consecutive tiles that lane n holds;
 //   kModeCandidates   (fused top-k, second pass) append the cells at or
-//                     above the row's floor to the row's candidate list.
-constexpr int kModeScores = 0, kModeScoresExact = 1, kModeGroupMax = 2, kModeCandidates = 3;
+//                     above the row's floor to the row's candidate list;
+//   kModeKeys16       (fused top-k) store the top 16 bits of each cell's
+//                     order key (2 bytes per cell, 0 outside a row's keys),
+//                     as exactly one 8-byte buffer store per lane and slice,
+//                     every row written out to its 64-column padded end.
+constexpr int kModeScores = 0, kModeScoresExact = 1, kModeGroupMax = 2, kModeCandidates = 3, kModeKeys16 = 4;
 constexpr int kGroupTiles = kFusedGroupTiles;  // tiles per group in kModeGroupMax (16 groups per row of them)
 
 // Inclusive prefix sum within each 16-lane row of a wavefront (DPP
@@ -128,6 +132,7 @@ void prefill_kernel(PrefillParams p) {
     constexpr bool kExact = kMode == kModeScoresExact;
     static_assert(!kRotate || kExact, "line-aligned layout is for exact score stores");
     constexpr bool kFused = kMode == kModeGroupMax || kMode == kModeCandidates;
+    constexpr bool kKeys = kMode == kModeKeys16;
     // Two separate LDS objects (not one [2][...] array), so the compiler can
     // tell the buffer being read from the one being filled and does not wait
     // for the prefetch before reading the current tile.
@@ -180,6 +185,7 @@ void prefill_kernel(PrefillParams p) {
     const int rot = kRotate ? __builtin_amdgcn_readfirstlane(
                                   (int)((((uintptr_t)p.out + (uint64_t)(row0 + a_w) * (uint64_t)p.out_stride * 4) >> 4) & 7))
                             : 0;
+    if (kKeys && blockIdx.x == 0 && tid == 0) *p.hard_count = 0;  // read by the selects that follow
     const int lc = 4 * ((n - rot) & 15);  // first tile column of this lane's cells
     const int sc = 4 * (n - rot);         // first column of this lane's store, relative to the tile
     const bool lo = kRotate && n < rot;   // stores the previous tile's cells
@@ -334,9 +340,13 @@ void prefill_kernel(PrefillParams p) {
         // slice before a pass's first tile, store to an offset past the
         // buffer's end, which the hardware drops.  With that fixed count the
         // wait for a buffer of keys can leave the latest stores in flight.
-        const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            p.out + (int64_t)row0 * p.out_stride, 0,
-            kExact ? (int)((int64_t)min(kBM, p.num_rows - row0) * p.out_stride * 4) : 0, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t out_rsrc =
+            kKeys ? __builtin_amdgcn_make_buffer_rsrc(p.keys16 + (int64_t)row0 * p.keys_stride, 0,
+                                                      (int)((int64_t)min(kBM, p.num_rows - row0) * p.keys_stride * 2),
+                                                      kBufferWord3)
+                  : __builtin_amdgcn_make_buffer_rsrc(
+                        p.out + (int64_t)row0 * p.out_stride, 0,
+                        kExact ? (int)((int64_t)min(kBM, p.num_rows - row0) * p.out_stride * 4) : 0, kBufferWord3);
         constexpr uint32_t kDropped = 0x80000000u;
         // The fused passes' outputs of this workgroup's rows as one raw
         // buffer (group maxima, or candidate pools), for the same reason:
@@ -357,7 +367,9 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const int idx = a_w + dl * (4 * mt + q4);
-            row_boff[mt] = in_pass[mt] ? (uint32_t)(((int64_t)idx * p.out_stride + sc) * 4) : kDropped;
+            row_boff[mt] = !in_pass[mt] ? kDropped
+                           : kKeys      ? (uint32_t)(((int64_t)idx * p.keys_stride + sc) * 2)
+                                        : (uint32_t)(((int64_t)idx * p.out_stride + sc) * 4);
         }
         // Element offset of (row of slice mt, column col) from out_wg, for the
         // plain stores of partial and -inf-only tiles.
@@ -385,7 +397,11 @@ void prefill_kernel(PrefillParams p) {
         auto finish_fast = [&](int mt, int tile_c, const f32x4 (&acc)[4]) {
             const f32x4 v{head_sum_score(acc[0], p.scale), head_sum_score(acc[1], p.scale),
                           head_sum_score(acc[2], p.scale), head_sum_score(acc[3], p.scale)};
-            if constexpr (kRotate) {
+            if constexpr (kKeys) {
+                const u32x2 kw{score_keys16(v[0], v[1]), score_keys16(v[2], v[3])};
+                __builtin_amdgcn_raw_buffer_store_b64(kw, out_rsrc, tile_c >= 0 ? row_boff[mt] : kDropped,
+                                                      2 * max(tile_c, 0), kStoreNT);
+            } else if constexpr (kRotate) {
                 const f32x4 w = lo ? keep[mt] : v;
                 keep[mt] = v;
                 const bool drop = tile_c < 0 || (lo && tile_c == c_begin);
@@ -398,6 +414,23 @@ void prefill_kernel(PrefillParams p) {
         };
         // Any slice: mask per cell, partial tiles and unbounded rows.
         auto finish_general = [&](int mt, int tile_c, bool masked, const f32x4 (&acc)[4]) {
+            if constexpr (kKeys) {
+                // Cells outside the row's keys, or past the chunk's end (the
+                // row's padding), get key 0; the store covers the whole tile.
+                const int col = tile_c + lc;
+                bool ok[4];
+                f32x4 v;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c = col + g;
+                    ok[g] = !masked || (c < row_lim[mt] && c >= col_min && c < c_end);
+                    v[g] = head_sum_score(acc[g], p.scale);
+                }
+                const u32x2 kw{score_keys16(v[0], v[1], ok[0], ok[1]), score_keys16(v[2], v[3], ok[2], ok[3])};
+                __builtin_amdgcn_raw_buffer_store_b64(kw, out_rsrc, tile_c >= 0 ? row_boff[mt] : kDropped,
+                                                      2 * max(tile_c, 0), kStoreNT);
+                return;
+            }
             f32x4 v;
             if (!masked) {
                 v = f32x4{head_sum_score(acc[0], p.scale), head_sum_score(acc[1], p.scale),
@@ -569,7 +602,8 @@ void prefill_kernel(PrefillParams p) {
                 for (int g = 0; g < 4; ++g) b[ks][g] = *reinterpret_cast<const u32x4 *>(&tile[rd_off[ks] + g * kDim]);
         };
         auto do_tile = [&](int tile_c, const u32x4 (&b)[4][4]) {
-            const bool masked = !(tile_c + kBN <= wave_lim && tile_c >= col_min) || (kFused && tile_c + kBN > c_end);
+            const bool masked =
+                !(tile_c + kBN <= wave_lim && tile_c >= col_min) || ((kFused || kKeys) && tile_c + kBN > c_end);
             const bool full = p.out_vec && tile_c + kBN <= c_end;
             if (kFused) {
                 if (!masked && !prev_masked) {
@@ -597,7 +631,7 @@ void prefill_kernel(PrefillParams p) {
                     multiply(3, b, accB);
                     finish_topk(2, tile_c, masked, accA);
                 }
-            } else if (kExact && full && !masked && !prev_masked) {
+            } else if ((kKeys || (kExact && full)) && !masked && !prev_masked) {
                 multiply(0, b, accA);
                 finish_fast(3, prev_c, accB);
                 interleave();
@@ -635,7 +669,7 @@ void prefill_kernel(PrefillParams p) {
         // maxima) or four (candidates); 4 slices per tile.
         constexpr int kStoresPerSlice = kMode == kModeCandidates ? 4 : 1;
         constexpr int kStoresPerStage = 4 * kStoresPerSlice * kTilesPerStage;
-        constexpr bool kFixedStores = kExact || kFused;
+        constexpr bool kFixedStores = kExact || kFused || kKeys;
         constexpr int kInFlight = kMode == kModeCandidates ? 16 : kStoresInFlight;
         static_assert(kInFlight <= kStoresPerStage && kInFlight <= 63, "vmcnt field");
         // s_waitcnt vmcnt(kInFlight) lgkmcnt(0) (vmcnt split over bits 3:0 and 15:14).
@@ -668,6 +702,10 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt)
                         __builtin_amdgcn_raw_buffer_store_b128(f32x4{0.f, 0.f, 0.f, 0.f}, out_rsrc, kDropped, 0, 0);
+                } else if (kKeys) {
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, out_rsrc, kDropped, 0, 0);
                 } else if (kFused) {
 #pragma unroll
                     for (int i = 0; i < 4 * kStoresPerSlice; ++i) {
@@ -732,9 +770,18 @@ void prefill_kernel(PrefillParams p) {
             }
         }
 
-        // Tiles that no row of this pass can see: -inf only (score modes).
+        // Tiles that no row of this pass can see: -inf only (score modes),
+        // key 0 (key mode, whole tiles).
+        for (int it = n_compute; kKeys && it < n_tiles; ++it) {
+            const int col = c_begin + it * kBN + 4 * n;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                if (in_pass[mt])
+                    *reinterpret_cast<u32x2 *>(p.keys16 + (int64_t)(row0 + a_w + dl * (4 * mt + q4)) * p.keys_stride + col) =
+                        u32x2{0u, 0u};
+        }
         const float ni = neg_inf();
-        for (int it = n_compute; !kFused && it < n_tiles; ++it) {
+        for (int it = n_compute; !kFused && !kKeys && it < n_tiles; ++it) {
             const int tile_c = c_begin + it * kBN;
             const int col = tile_c + 4 * n;
 #pragma unroll
@@ -794,6 +841,11 @@ hipError_t launch_prefill_group_max(const PrefillParams &p, hipStream_t stream) 
 hipError_t launch_prefill_candidates(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
     return launch_kernel(prefill_kernel<kModeCandidates, false, false>, grid, dim3(kThreads), stream, p);
+}
+
+hipError_t launch_prefill_keys16(const PrefillParams &p, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
+    return launch_kernel(prefill_kernel<kModeKeys16, false, false>, grid, dim3(kThreads), stream, p);
 }
 
 int prefill_rows_per_block() { return kBM; }

@@ -100,6 +100,27 @@ FusedLayout fused_layout(int32_t num_rows, int32_t out_cols, int32_t topk, int n
     return L;
 }
 
+// Workspace of the score-key path (rows of 1 .. kKeys16MaxCols columns):
+// the cells' 16-bit key prefixes on rows padded to 64 columns, the count and
+// list of rows left to the fallback, and one fp32 scratch row per fallback
+// workgroup.
+struct Keys16Layout {
+    int64_t stride, off_keys, off_count, off_hard, off_scratch, total;
+};
+Keys16Layout keys16_layout(int32_t num_rows, int32_t out_cols) {
+    Keys16Layout L{};
+    auto seg = [](int64_t b) { return (b + 255) / 256 * 256; };
+    L.stride = ((int64_t)out_cols + 63) / 64 * 64;
+    int64_t o = 0;
+    L.off_keys = o; o += seg((int64_t)num_rows * L.stride * 2);
+    L.off_count = o; o += 256;
+    L.off_hard = o; o += seg((int64_t)num_rows * 4);
+    L.off_scratch = o; o += seg((int64_t)qsa::kKeys16FallbackGroups * L.stride * 4);
+    L.total = o;
+    return L;
+}
+bool use_keys16(int32_t out_cols) { return out_cols > 0 && out_cols <= qsa::kKeys16MaxCols; }
+
 // Vector-load layout rule: 16-byte aligned base, and every axis with more
 // than one element has a positive stride that is a multiple of 8 bf16.
 bool axis_ok(int64_t size, int64_t stride) { return size <= 1 || (stride > 0 && stride % 8 == 0); }
@@ -766,8 +787,97 @@ int qsa_prefill_topk_workspace_bytes(int32_t num_rows, int32_t out_cols, int32_t
     if (num_rows < 0 || out_cols < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
     if (topk < 1 || topk > qsa::kFusedMaxK)
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: topk must be in [1, %d], got %d", fn, qsa::kFusedMaxK, topk);
-    *bytes = fused_layout(num_rows, out_cols, topk, current_cu_count()).total;
+    *bytes = use_keys16(out_cols) ? keys16_layout(num_rows, out_cols).total
+                                  : fused_layout(num_rows, out_cols, topk, current_cu_count()).total;
     return ok();
+}
+
+// qsa_mqa_prefill_topk on rows of 1 .. kKeys16MaxCols columns: the prefill
+// pass storing the cells' 16-bit key prefixes, the select over them
+// (rescoring the cells that tie the k-th largest prefix), and the fallback
+// for rows that select leaves.  Arguments already checked by the caller:
+// sizes, scale, topk, out_idx and the workspace's alignment.
+static int prefill_topk_keys16(const char *fn, const void *q, int64_t q_stride_row, int64_t q_stride_head,
+                               const void *k, int64_t k_stride, int64_t num_keys, const int32_t *row_k_start,
+                               const int32_t *row_k_end, int32_t num_rows, float scale, int32_t out_cols,
+                               int32_t topk, int32_t *out_idx, int64_t out_stride, void *workspace,
+                               int64_t workspace_bytes, void *stream, int cus) {
+    const Keys16Layout L = keys16_layout(num_rows, out_cols);
+    if (workspace_bytes < L.total)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: workspace of %lld bytes, %lld needed", fn,
+                    (long long)workspace_bytes, (long long)L.total);
+    if (!q || !row_k_start || !row_k_end) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL q, row_k_start or row_k_end", fn);
+    if (num_keys > 0 && !k) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: NULL k", fn);
+    if (!aligned(q, 16) || !axis_ok(num_rows, q_stride_row) || !axis_ok(4, q_stride_head) ||
+        (num_keys > 0 && (!aligned(k, 16) || !axis_ok(num_keys, k_stride))))
+        return fail(QSA_ERR_LAYOUT,
+                    "%s: q and k need a 16-byte aligned base and positive strides that are multiples "
+                    "of 8 elements on every axis longer than 1 (16-byte vector loads)", fn);
+    if (num_keys <= 1) k_stride = 128;
+    if (k_stride > qsa::prefill_max_k_stride())
+        return fail(QSA_ERR_UNSUPPORTED, "%s: k_stride %lld exceeds %lld elements", fn, (long long)k_stride,
+                    (long long)qsa::prefill_max_k_stride());
+    const int bm = qsa::prefill_rows_per_block();
+    const int chunk = qsa::prefill_col_chunk(num_rows, out_cols, k_stride, cus);
+    const int64_t row_blocks = ((int64_t)num_rows + bm - 1) / bm;
+    const int64_t col_chunks = ((int64_t)out_cols + chunk - 1) / chunk;
+    if (row_blocks * col_chunks >= INT32_MAX)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "%s: problem too large for one launch", fn);
+    char *ws = static_cast<char *>(workspace);
+
+    qsa::PrefillParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.q_stride_row = q_stride_row;
+    p.q_stride_head = q_stride_head;
+    p.k = static_cast<const uint16_t *>(k);
+    p.k_stride = k_stride;
+    p.num_keys = num_keys;
+    p.row_k_start = row_k_start;
+    p.row_k_end = row_k_end;
+    p.num_rows = num_rows;
+    p.scale = scale;
+    p.out_cols = out_cols;
+    p.col_chunk = chunk;
+    p.row_blocks = (int32_t)row_blocks;
+    p.col_chunks = (int32_t)col_chunks;
+    p.keys16 = reinterpret_cast<uint16_t *>(ws + L.off_keys);
+    p.keys_stride = L.stride;
+    p.hard_count = reinterpret_cast<int32_t *>(ws + L.off_count);
+
+    qsa::Keys16TopkParams t{};
+    t.keys = p.keys16;
+    t.keys_stride = L.stride;
+    t.num_rows = num_rows;
+    t.num_cols = out_cols;
+    t.k = topk;
+    t.out = out_idx;
+    t.out_stride = out_stride;
+    t.q = p.q;
+    t.q_stride_row = q_stride_row;
+    t.q_stride_head = q_stride_head;
+    t.kv = p.k;
+    t.k_stride = k_stride;
+    t.num_keys = num_keys;
+    t.row_k_start = row_k_start;
+    t.row_k_end = row_k_end;
+    t.scale = scale;
+    t.hard_count = p.hard_count;
+    t.hard_rows = reinterpret_cast<int32_t *>(ws + L.off_hard);
+    t.scratch = reinterpret_cast<float *>(ws + L.off_scratch);
+    t.scratch_stride = L.stride;
+    t.scratch_rows = qsa::kKeys16FallbackGroups;
+
+    // Three launches; armed timing events span them.
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const qsa::LaunchEvents ev = g_launch_events;
+    g_launch_events = {ev.start, nullptr};
+    hipError_t err = qsa::launch_prefill_keys16(p, st);
+    g_launch_events = {nullptr, nullptr};
+    if (err == hipSuccess) err = qsa::launch_topk_keys16(t, st);
+    g_launch_events = {nullptr, ev.stop};
+    if (err == hipSuccess) err = qsa::launch_topk_keys16_fallback(t, st);
+    g_launch_events = ev;
+    return device_status(fn, err);
 }
 
 int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
@@ -788,6 +898,10 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     if (!aligned(out_idx, 4)) return fail(QSA_ERR_LAYOUT, "%s: out_idx must be 4-byte aligned", fn);
     if (!aligned(workspace, 256)) return fail(QSA_ERR_LAYOUT, "%s: workspace must be 256-byte aligned", fn);
     const int cus = current_cu_count();
+    if (use_keys16(out_cols))
+        return prefill_topk_keys16(fn, q, q_stride_row, q_stride_head, k, k_stride, num_keys, row_k_start, row_k_end,
+                                   num_rows, scale, out_cols, topk, out_idx, out_stride, workspace, workspace_bytes,
+                                   stream, cus);
     const FusedLayout L = fused_layout(num_rows, out_cols, topk, cus);
     if (workspace_bytes < L.total)
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: workspace of %lld bytes, %lld needed", fn,

@@ -84,6 +84,28 @@ __device__ __forceinline__ float head_sum_score(f32x4 acc, float scale) {
     return s * scale;
 }
 
+// Order-preserving 32-bit key of a score: unsigned comparison of keys
+// orders the floats, +0 and -0 share one key, and -inf and NaN get 0 (below
+// every other value: never picked).
+__device__ __forceinline__ uint32_t order_key(float v) {
+    if (!(v > neg_inf())) return 0u;
+    uint32_t u = __float_as_uint(v);
+    if ((u << 1) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Top halves of the order keys of two scores a, b that are >= +0, +inf or
+// NaN (what the score epilogue gives for a positive scale), packed as
+// (key(b) >> 16) << 16 | key(a) >> 16.  For such a score the top half is
+// (bits >> 16) | 0x8000 (the sign bit is clear); a NaN is first replaced by
+// the bits of -0, whose top half 0x8000 then becomes 0, the key of a cell
+// that is never picked.  Cells outside a row's keys pass ok = false (0).
+__device__ __forceinline__ uint32_t score_keys16(float a, float b, bool ok_a = true, bool ok_b = true) {
+    const uint32_t ua = ok_a && a == a ? __float_as_uint(a) : 0x80000000u;
+    const uint32_t ub = ok_b && b == b ? __float_as_uint(b) : 0x80000000u;
+    return __builtin_amdgcn_perm(ub, ua, 0x07060302u) ^ 0x80008000u;
+}
+
 // 16x16x32 bf16 MFMA (gfx950): lane l supplies A[m = l%16][k = 8*(l/16) .. +7]
 // and B[k = 8*(l/16) .. +7][n = l%16]; it receives C[4*(l/16) + i][l%16].
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {

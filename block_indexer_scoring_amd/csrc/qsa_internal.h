@@ -84,6 +84,10 @@ struct PrefillParams {
     uint32_t *cand;             // [rows][pool_cap][2] candidates: score bits (>= +0), column
     int32_t *cand_cnt;          // [rows][col_chunks] candidates per segment
     int32_t pool_cap;
+    // Score-key pass (qsa_mqa_prefill_topk on rows that fit the key select).
+    uint16_t *keys16;           // [rows][keys_stride] top halves of the cells' order keys
+    int64_t keys_stride;        // a multiple of 64 elements, >= out_cols
+    int32_t *hard_count;        // set to 0 by the pass (rows left to the fallback select)
 };
 
 struct TopkParams {
@@ -117,6 +121,33 @@ struct FusedTopkParams {
     int32_t *out;
     int64_t out_stride;
 };
+
+// Top-k over the score keys' top halves (qsa_mqa_prefill_topk).  Cells
+// whose 16-bit prefix ties the k-th largest are rescored with the prefill's
+// own MFMA sequence for their full keys; rows the in-register select cannot
+// finish (list overflow, more than 64 such ties) are listed for a fallback
+// that rescores the whole row into scratch.
+struct Keys16TopkParams {
+    const uint16_t *keys;       // [num_rows][keys_stride]
+    int64_t keys_stride;
+    int32_t num_rows, num_cols, k;
+    int32_t *out;
+    int64_t out_stride;
+    // The prefill's inputs, for rescoring.
+    const uint16_t *q;
+    int64_t q_stride_row, q_stride_head;
+    const uint16_t *kv;
+    int64_t k_stride, num_keys;
+    const int32_t *row_k_start, *row_k_end;
+    float scale;
+    int32_t *hard_count;        // rows listed for the fallback
+    int32_t *hard_rows;         // [num_rows]
+    float *scratch;             // [scratch_rows][scratch_stride] fp32 rows of the fallback
+    int64_t scratch_stride;
+    int32_t scratch_rows;
+};
+constexpr int kKeys16MaxCols = 32768;  // columns the 512-thread key select holds in registers
+constexpr int kKeys16FallbackGroups = 64;  // fallback workgroups (one scratch row each)
 
 struct MetaParams {
     const int32_t *query_start_loc, *seq_lens, *key_offsets;
@@ -234,6 +265,9 @@ hipError_t launch_prefill_candidates(const PrefillParams &p, hipStream_t stream)
 hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus);
 hipError_t launch_topk_floor(const FusedTopkParams &p, hipStream_t stream);
 hipError_t launch_topk_candidates(const FusedTopkParams &p, hipStream_t stream);
+hipError_t launch_prefill_keys16(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_topk_keys16(const Keys16TopkParams &p, hipStream_t stream);
+hipError_t launch_topk_keys16_fallback(const Keys16TopkParams &p, hipStream_t stream);
 hipError_t launch_metadata(const MetaParams &p, hipStream_t stream);
 hipError_t launch_decode_visible(const DecodeVisibleParams &p, hipStream_t stream);
 hipError_t launch_cache_slots(const CacheMetaParams &p, hipStream_t stream);  // p.slot_mapping set

@@ -42,12 +42,6 @@ namespace {
 constexpr int kMaxWaves = 16;  // workgroups of at most 1024 threads
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: raw dword access
 
-__device__ __forceinline__ uint32_t order_key(float v) {
-    if (!(v > neg_inf())) return 0u;  // -inf and NaN are never picked
-    uint32_t u = __float_as_uint(v);
-    if ((u << 1) == 0u) u = 0u;       // -0 ties +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Inclusive prefix sum over a wavefront with DPP moves (no LDS): a
 // Hillis-Steele scan inside each 16-lane row (row_shr 1, 2, 4, 8 with zero
@@ -600,9 +594,11 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
     for (int i = picked + tid; i < p.k; i += THREADS) out[i] = -1;
 }
 
-// Rows longer than the register-resident limit: each phase re-reads the row,
-// column c owned by thread c % 1024; picks are placed slot by slot.
-__global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
+// One row x[0 .. num_cols) by a 1024-thread workgroup, re-read from memory
+// in each phase: column c owned by thread c % 1024; picks are placed slot by
+// slot.  Used for rows longer than the register-resident limit, and by the
+// fused path's fallback on rows it rescored into scratch.
+__device__ __forceinline__ void streaming_select(const float *x, int num_cols, int32_t *out, int k) {
     constexpr int kThreads = 1024;
     constexpr int kWaves = kThreads / 64;
     __shared__ SelectShared sh;
@@ -610,13 +606,10 @@ __global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t row = blockIdx.x;
-    const float *x = p.logits + row * p.logits_stride;
-    int32_t *out = p.out + row * p.out_stride;
-    const int slots = (p.num_cols + kThreads - 1) / kThreads;
+    const int slots = (num_cols + kThreads - 1) / kThreads;
     auto key_at = [&](int e) {
         const int i = e * kThreads + tid;
-        return i < p.num_cols ? order_key(x[i]) : 0u;
+        return i < num_cols ? order_key(x[i]) : 0u;
     };
 
     int cand = 0;
@@ -626,10 +619,10 @@ __global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
 
     uint32_t T = 0u;
     int need = 0;
-    if (num_cand > p.k) {
+    if (num_cand > k) {
         const ListView no_list{nullptr, nullptr, 0};
-        const RowView mem{x, p.num_cols, slots, 0};
-        T = radix_threshold<1, kFromMemory, kThreads>(no_list, mem, p.k, 1u, sh, &need);
+        const RowView mem{x, num_cols, slots, 0};
+        T = radix_threshold<1, kFromMemory, kThreads>(no_list, mem, k, 1u, sh, &need);
     }
 
     int gt_run = 0, eq_run = 0;  // greater / equal keys in earlier slots
@@ -663,8 +656,13 @@ __global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
         eq_run += eq_slot;
         __syncthreads();
     }
-    const int picked = min(num_cand, p.k);
-    for (int i = picked + tid; i < p.k; i += kThreads) out[i] = -1;
+    const int picked = min(num_cand, k);
+    for (int i = picked + tid; i < k; i += kThreads) out[i] = -1;
+}
+
+__global__ __launch_bounds__(1024) void topk_streaming_kernel(TopkParams p) {
+    const int64_t row = blockIdx.x;
+    streaming_select(p.logits + row * p.logits_stride, p.num_cols, p.out + row * p.out_stride, p.k);
 }
 
 // ---- Fused prefill top-k: the per-row floor and the final select. ----
@@ -1020,6 +1018,324 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
     }
 }
 
+// ---- Fused prefill top-k over score keys (rows of at most 32,768 columns). ----
+//
+// The prefill pass stores, per cell, the top 16 bits of the score's order
+// key (2 bytes instead of the 4-byte score).  Picking on those prefixes is
+// exact except among the cells whose prefix equals that of the k-th largest
+// key: only there do the low 16 bits decide.  Those cells (a few dozen per
+// row on score rows) are rescored with the prefill's own MFMA sequence (the
+// same operands, instruction, feature order and epilogue, so the same bits)
+// and ranked on their full keys.  Rows the in-register select cannot finish
+// go to a fallback that rescores the whole row.
+
+// Full order keys of 64 cells of prefill row `row`, one per lane: lane l's
+// cell is key index key_idx (which every lane must hold in [0, num_keys)).
+// The MFMA layout is the prefill kernel's: A lane (n, q4) holds head n % 4
+// of the row, features 32 ks + 8 q4 .. +7 in k-step ks, so every group of 4
+// result rows holds the 4 head dots; B lane (n, q4) of group g holds the
+// same features of lane 16 g + n's key.  Lane l = 16 q4 + n takes group q4's
+// result, which its own lane holds.
+__device__ __forceinline__ uint32_t rescore_key(const Keys16TopkParams &p, int64_t row, int64_t key_idx) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, q4 = lane >> 4;
+    const uint16_t *qrow = p.q + row * p.q_stride_row + (int64_t)(n & 3) * p.q_stride_head + 8 * q4;
+    u32x4 a[4], b[4][4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[ks] = load_u32x4(qrow + 32 * ks);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int lo = __shfl((int)(uint32_t)key_idx, 16 * g + n, 64);
+        const int hi = __shfl((int)(uint32_t)((uint64_t)key_idx >> 32), 16 * g + n, 64);
+        const int64_t kg = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+        const uint16_t *krow = p.kv + kg * p.k_stride + 8 * q4;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) b[g][ks] = load_u32x4(krow + 32 * ks);
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc[g] = mfma16x16x32(a[ks], b[g][ks], acc[g]);
+    }
+    const f32x4 mine = q4 == 0 ? acc[0] : (q4 == 1 ? acc[1] : (q4 == 2 ? acc[2] : acc[3]));
+    return order_key(head_sum_score(mine, p.scale));
+}
+
+// Wave 0's select over the listed keys (entries key16 << 16 | column, in
+// column order; hist0 counts them by the top 11 bits of key16).  Returns
+// T16 such that the picks are exactly the entries whose key16 is > T16,
+// after rewriting the entries that share the k-th largest prefix: a picked
+// one gets key16 0xffff, the others 0.  Returns -1 when the row needs the
+// fallback (more than 64 entries share that prefix and only some are
+// picked, or a rescored key disagrees with its stored prefix).  Requires
+// more than k listed entries.
+__device__ __forceinline__ int wave_select_keys16(uint32_t *list, int n, int k, const int *hist0, int *hist,
+                                                  int *tied_idx, const Keys16TopkParams &p, int64_t row,
+                                                  int64_t start) {
+    const int lane = threadIdx.x & 63;
+    int above;
+    int kk = k;
+    const int b0 = wave_find_bin<2048>(hist0, kk, &above);
+    kk -= above;
+    // One wave: its LDS operations take effect in issue order.
+    if (lane < 32) hist[lane] = 0;
+#pragma unroll 1
+    for (int i0 = 0; i0 < n; i0 += 256) {
+        uint32_t e[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = list[min(i0 + 64 * u + lane, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + 64 * u + lane < n && (e[u] >> 21) == (uint32_t)b0) atomicAdd(&hist[(e[u] >> 16) & 31], 1);
+    }
+    const int b1 = wave_find_bin<32>(hist, kk, &above);
+    kk -= above;
+    const uint32_t top = ((uint32_t)b0 << 5) | (uint32_t)b1;
+    const int tied = hist[b1];  // entries whose key16 is `top`
+    if (kk == tied) return (int)top - 1;  // all of them are picked
+    if (tied > 64) return -1;
+    // Lane p takes the p-th tied entry in list (column) order.
+    int base = 0;
+#pragma unroll 1
+    for (int i0 = 0; i0 < n; i0 += 256) {
+        uint32_t e[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = list[min(i0 + 64 * u + lane, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + 64 * u + lane;
+            const bool match = i < n && (e[u] >> 16) == top;
+            const uint64_t m = __ballot(match);
+            const int at = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            tied_idx[match ? at : 64 + lane] = i;
+            base += __popcll(m);
+        }
+    }
+    const bool act = lane < tied;
+    const int idx = tied_idx[act ? lane : 0];
+    const uint32_t entry = list[idx];
+    const int col = (int)(entry & 0xffffu);
+    const uint32_t key = rescore_key(p, row, start + col);
+    if (__ballot(act && (key >> 16) != top) != 0ull) return -1;
+    // The kk-th largest of the tied keys (kk < tied), most significant bit
+    // first over the low half; kr ends as the number of keys equal to T
+    // that are picked (the lowest columns, i.e. the lowest lanes).
+    uint32_t t = 0u, msk = 0u;
+    int kr = kk;
+#pragma unroll
+    for (int bit = 15; bit >= 0; --bit) {
+        const uint32_t bb = 1u << bit;
+        const int ones = __popcll(__ballot(act && (key & msk) == t && (key & bb) != 0u));
+        if (kr <= ones) t |= bb;
+        else kr -= ones;
+        msk |= bb;
+    }
+    const uint32_t T = (top << 16) | t;
+    const uint64_t eqm = __ballot(act && key == T);
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const bool picked = act && (key > T || (key == T && __popcll(eqm & below) < kr));
+    if (act) list[idx] = (picked ? 0xffff0000u : 0u) | (entry & 0xffffu);
+    return (int)top;
+}
+
+// One row per workgroup of THREADS threads, E keys per thread (a multiple
+// of 8): thread t holds the 8-key chunks t, t + THREADS, ..., as loaded (two
+// keys per register), so each 16-byte load is part of one contiguous read
+// of 16 * THREADS bytes.  The row buffer resource covers the row's padded
+// width; the padding holds key 0, and loads past it return 0.  Floor from
+// the maxima of the chunks (distinct cells), list of the keys >= floor in
+// column order, one-wave select, placement from the list.
+template <int E, int THREADS, int WPE>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE)))
+void topk_keys16_kernel(const uint16_t *keys, int64_t keys_stride, Keys16TopkParams p) {
+    constexpr int kChunks = E / 8;
+    constexpr int kWaves = THREADS / 64;
+    constexpr int kListCap = 4096;
+    static_assert(E % 8 == 0 && E <= 64 && THREADS % 64 == 0, "layout");
+    __shared__ SelectShared sh;
+    __shared__ int seg_count[kChunks * kWaves];
+    __shared__ __attribute__((aligned(16))) int hist_list[2048];  // listed keys by their top 11 bits
+    __shared__ uint32_t list[kListCap];
+    __shared__ int tied_idx[128];
+    __shared__ uint32_t s_floor;
+    __shared__ int s_need, s_T;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t row = blockIdx.x;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(keys + row * keys_stride), 0, (int)(keys_stride * 2), kBufferWord3);
+    u32x4 w[kChunks];
+#pragma unroll
+    for (int e = 0; e < kChunks; ++e)
+        w[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * (tid + THREADS * e), 0, 0));
+    auto chunk_col = [&](int e) { return 8 * (tid + THREADS * e); };
+    auto key_at = [&](int j) {  // key j (0 .. E-1) of this thread
+        const uint32_t v = w[j / 8][(j % 8) / 2];
+        return (j & 1) ? (v >> 16) : (v & 0xffffu);
+    };
+    for (int b = tid; b < 2048; b += THREADS) {
+        sh.hist[b] = 0;
+        hist_list[b] = 0;
+    }
+    const int64_t start = p.row_k_start[row];
+    int32_t *out = p.out + row * p.out_stride;
+    __syncthreads();
+
+    // Floor: the lower edge of the 16-bit bin holding the k-th largest chunk
+    // maximum (top 11 bits, then the next 5 among the maxima in that bin);
+    // at least k keys are >= it.  1 when fewer than k chunks hold a
+    // candidate (every candidate is listed).
+    uint32_t cmax[kChunks];
+#pragma unroll
+    for (int e = 0; e < kChunks; ++e) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, max(w[e][i] & 0xffffu, w[e][i] >> 16));
+        cmax[e] = m;
+        if (m != 0u) atomicAdd(&sh.hist[m >> 5], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        int above;
+        const int bin = wave_find_bin<2048>(sh.hist, p.k, &above);
+        if (lane == 0) {
+            s_floor = bin <= 0 ? 1u : ((uint32_t)bin << 5);
+            s_need = p.k - above;
+        }
+    }
+    __syncthreads();
+    if (s_floor > 1u) {  // uniform; hist_list is still all zero here
+        const uint32_t b0 = s_floor >> 5;
+#pragma unroll
+        for (int e = 0; e < kChunks; ++e)
+            if ((cmax[e] >> 5) == b0) atomicAdd(&hist_list[cmax[e] & 31], 1);
+        __syncthreads();
+        if (tid < 64) {
+            int above;
+            const int b1 = wave_find_bin<32>(hist_list, s_need, &above);
+            if (lane == 0) s_floor |= (uint32_t)b1;
+        }
+        __syncthreads();
+        if (tid < 32) hist_list[tid] = 0;
+    }
+    const uint32_t floor_top = s_floor;
+    // Column order is chunk-major (chunk e of wave w covers columns
+    // 8 (THREADS e + 64 w) .. +511): per-lane counts of each chunk (at most
+    // 8), three 10-bit fields to a word, scanned across the wave with DPP.
+    constexpr int kCntWords = (kChunks + 2) / 3;
+    uint32_t packed[kCntWords], incl[kCntWords];
+#pragma unroll
+    for (int c = 0; c < kCntWords; ++c) packed[c] = 0u;
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        packed[j / 24] += ((key_at(j) + 0x10000u - floor_top) >> 16) << (10 * ((j / 8) % 3));
+#pragma unroll
+    for (int c = 0; c < kCntWords; ++c) incl[c] = wave_inclusive_scan(packed[c]);
+    if (lane == 63) {
+#pragma unroll
+        for (int e = 0; e < kChunks; ++e) seg_count[e * kWaves + wave] = (int)((incl[e / 3] >> (10 * (e % 3))) & 1023u);
+    }
+    __syncthreads();
+    int tot = 0, pre = 0;
+    if (lane < kChunks) {
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            const int sc = seg_count[lane * kWaves + v];
+            tot += sc;
+            pre += v < wave ? sc : 0;
+        }
+    }
+    const int tot_incl = (int)wave_inclusive_scan((uint32_t)tot);
+    const int seg_off = tot_incl - tot + pre;
+    const int listed = __builtin_amdgcn_readlane(tot_incl, 63);
+    int T16 = -1;
+    if (listed <= kListCap) {
+        const uint32_t floor_top2 = __builtin_amdgcn_readfirstlane(floor_top);
+#pragma unroll
+        for (int e = 0; e < kChunks; ++e) {
+            int at = __builtin_amdgcn_readlane(seg_off, e) + (int)(((incl[e / 3] - packed[e / 3]) >> (10 * (e % 3))) & 1023u);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t t = key_at(8 * e + i);
+                const bool in = t >= floor_top2;
+                if (in) {
+                    list[at] = (t << 16) | (uint32_t)(chunk_col(e) + i);
+                    atomicAdd(&hist_list[t >> 5], 1);
+                }
+                at += in;
+            }
+        }
+        __syncthreads();
+        if (listed <= p.k) {
+            T16 = 0;  // every listed key is picked
+        } else {
+            if (tid < 64) {
+                const int t = wave_select_keys16(list, listed, p.k, hist_list, sh.hist, tied_idx, p, row, start);
+                if (lane == 0) s_T = t;
+            }
+            __syncthreads();
+            T16 = s_T;
+        }
+    }
+    if (T16 < 0) {  // uniform: the fallback writes this row
+        if (tid == 0) p.hard_rows[atomicAdd(p.hard_count, 1)] = (int32_t)row;
+        return;
+    }
+    // Picks: the entries with key16 > T16, in column order, from contiguous
+    // slices of the list.
+    const int per = (listed + THREADS - 1) / THREADS;
+    const int lo = min(tid * per, listed), hi = min(lo + per, listed);
+    int gt = 0;
+#pragma unroll 1
+    for (int i = lo; i < hi; ++i) gt += (int)(list[i] >> 16) > T16;
+    int total;
+    int before = block_exclusive_scan<THREADS>(gt, sh.wave_tmp, &total);
+#pragma unroll 1
+    for (int i = lo; i < hi; ++i) {
+        const uint32_t e = list[i];
+        if ((int)(e >> 16) > T16 && before < p.k) out[before++] = (int32_t)(e & 0xffffu);
+    }
+    for (int i = total + tid; i < p.k; i += THREADS) out[i] = -1;
+}
+
+// Rows the key select left: each workgroup takes hard rows blockIdx.x,
+// blockIdx.x + gridDim.x, ..., rescores the whole row into its scratch row
+// (-inf outside the row's keys, as the score kernel writes) and selects over
+// it.  The rescoring is the prefill's arithmetic (rescore_key), so the scores
+// and the picks are those of the score matrix.
+__global__ __launch_bounds__(1024) void topk_keys16_fallback_kernel(Keys16TopkParams p) {
+    const int count = *p.hard_count;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    float *x = p.scratch + (int64_t)blockIdx.x * p.scratch_stride;
+    for (int i = blockIdx.x; i < count && p.num_keys > 0; i += gridDim.x) {
+        const int64_t row = p.hard_rows[i];
+        const int64_t start = p.row_k_start[row];
+        const int64_t end = min((int64_t)p.row_k_end[row], p.num_keys);
+        for (int c0 = 64 * wave; c0 < p.num_cols; c0 += 64 * 16) {  // wave-uniform
+            const int c = c0 + lane;
+            const int64_t kidx = start + c;
+            const bool vis = c < p.num_cols && kidx >= 0 && kidx < end;
+            // Lanes outside the row's keys rescore a key that exists (their
+            // result is dropped); a hard row has at least one key.
+            const int64_t safe = kidx < 0 ? 0 : (kidx >= p.num_keys ? p.num_keys - 1 : kidx);
+            const uint32_t key = rescore_key(p, row, safe);
+            if (c < p.num_cols) {
+                // The score back from its key: scores here are >= +0, +inf or
+                // NaN (key 0, stored as NaN so that it is never picked).
+                x[c] = !vis ? neg_inf() : (key == 0u ? __uint_as_float(0x7fc00000u) : __uint_as_float(key & 0x7fffffffu));
+            }
+        }
+        __syncthreads();
+        streaming_select(x, p.num_cols, p.out + row * p.out_stride, p.k);
+        __syncthreads();
+    }
+}
+
 template <int E, int THREADS, int WPE>
 hipError_t launch_resident(const TopkParams &p, hipStream_t stream) {
     // 16-byte loads for rows 16-byte aligned with whole 4-column chunks.
@@ -1066,6 +1382,25 @@ hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus) {
         return launch_kernel(topk_streaming_kernel, dim3((unsigned)p.num_rows), dim3(1024), stream, p);
     if (p.num_cols <= 512 * 56) return launch_config<512, 8, 56>(p, stream);
     return launch_config<1024, 8, 32>(p, stream);
+}
+
+template <int E>
+hipError_t launch_keys16(const Keys16TopkParams &p, hipStream_t stream) {
+    if (p.num_cols > 512 * E) {
+        if constexpr (E + 8 <= 64) return launch_keys16<E + 8>(p, stream);
+        return hipErrorInvalidValue;
+    }
+    return launch_kernel(topk_keys16_kernel<E, 512, 8>, dim3((unsigned)p.num_rows), dim3(512), stream, p.keys,
+                         p.keys_stride, p);
+}
+
+hipError_t launch_topk_keys16(const Keys16TopkParams &p, hipStream_t stream) {
+    if (p.num_cols > kKeys16MaxCols) return hipErrorInvalidValue;
+    return launch_keys16<8>(p, stream);
+}
+
+hipError_t launch_topk_keys16_fallback(const Keys16TopkParams &p, hipStream_t stream) {
+    return launch_kernel(topk_keys16_fallback_kernel, dim3((unsigned)p.scratch_rows), dim3(1024), stream, p);
 }
 
 }  // namespace qsa

@@ -79,7 +79,7 @@ const char *qsa_last_error(void);
  *   the stream around the call adds.  Each entry point below launches one
  *   kernel (none when it has nothing to compute), except
  *   qsa_build_cache_metadata (up to two), qsa_mqa_decode_static_plan (two)
- *   and qsa_mqa_prefill_topk (four):
+ *   and qsa_mqa_prefill_topk (three, or four on rows wider than 32,768 columns):
  *   for those the start event marks the first kernel's begin and the stop
  *   event the last kernel's end.
  *   start_event, stop_event : hipEvent_t handles created by the caller (may
@@ -544,20 +544,29 @@ int qsa_topk_blocks(const float *logits, int64_t logits_stride, int32_t num_rows
  *   out_idx    : device int32 [num_rows][topk], row stride out_stride (>= topk).
  *   workspace  : device memory of at least qsa_prefill_topk_workspace_bytes
  *                bytes, 256-byte aligned, owned by the caller; its contents
- *                on entry do not matter and are clobbered.  About
- *                num_rows * (8 * min(8 * (topk - 1) + chunks * topk, out_cols)
- *                + out_cols / 2) bytes, chunks being the column chunks per
- *                row (as few as fill the CUs with row blocks of 128 rows; 4
- *                for 8,192 rows on 256 CUs), of which a call touches a few
- *                percent.  The size depends on the sizes and the device's CU
- *                count only.
- *   The call enqueues four kernels on stream (a group-maximum pass over the
- *   scores, the per-row floor over the group maxima, a candidate pass over
- *   the scores, the final select); with timing events armed the start event
- *   marks the first kernel's begin and the stop event the last kernel's
- *   end.
- *   Errors: as qsa_mqa_prefill (UNSUPPORTED also for k_stride > 16,384 and
- *   for rows whose per-workgroup workspace offsets would pass 2^31 bytes),
+ *                on entry do not matter and are clobbered.
+ *   Rows of 1 .. 32,768 columns: the prefill pass stores the top 16 bits of
+ *   each cell's order key (2 bytes per cell instead of the 4-byte score), a
+ *   select picks on them and rescores, with the prefill's own MFMA sequence
+ *   (hence the same bits), only the cells whose prefix ties that of the k-th
+ *   largest key; rows it cannot finish (more than 4,096 keys at or above its
+ *   floor, or more than 64 such ties) are rescored whole by a fallback.
+ *   Workspace about num_rows * 2 * round_up(out_cols, 64) + 256 *
+ *   round_up(out_cols, 64) bytes (half the fp32 score matrix).  Three
+ *   kernels: the key pass, the select, the fallback (which returns at once
+ *   when no row was left to it).
+ *   Wider rows (and out_cols 0): a group-maximum pass over the scores, the
+ *   per-row floor over the group maxima, a candidate pass over the scores
+ *   and the final select (four kernels); workspace about
+ *   num_rows * (8 * min(8 * (topk - 1) + chunks * topk, out_cols)
+ *   + out_cols / 2) bytes, chunks being the column chunks per row, of which
+ *   a call touches a few percent.
+ *   The size depends on the sizes and the device's CU count only.  With
+ *   timing events armed the start event marks the first kernel's begin and
+ *   the stop event the last kernel's end.
+ *   Errors: as qsa_mqa_prefill (UNSUPPORTED also, for rows wider than
+ *   32,768 columns, for k_stride > 16,384 and for rows whose per-workgroup
+ *   workspace offsets would pass 2^31 bytes),
  *   INVALID_ARGUMENT for topk outside [1, 2048], out_stride < topk, a NULL
  *   out_idx or workspace, or a workspace below the size needed; LAYOUT for a
  *   misaligned out_idx or workspace.

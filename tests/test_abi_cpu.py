@@ -506,7 +506,11 @@ def _fused(lib, **kw):
     (dict(ws_bytes=1000), 1, "needed"),
     (dict(q=None), 1, "NULL"),
     (dict(k=FAKE + 4), 3, "16-byte"),
-    (dict(sk=(1 << 14) + 8), 2, "k_stride"),
+    # Rows of at most 32,768 columns take the score-key path, whose key
+    # offsets are the prefill's; wider rows take the group-maximum path,
+    # whose chunks hold at most 2^14-element key strides.
+    (dict(sk=(1 << 22) + 8), 2, "k_stride"),
+    (dict(out_cols=40000, sk=(1 << 14) + 8), 2, "k_stride"),
 ])
 def test_fused_prefill_topk_rejects(lib, kw, code, text):
     assert _fused(lib, **kw) == code
@@ -517,10 +521,16 @@ def test_fused_prefill_topk_zero_rows_and_workspace_size(lib):
     assert _fused(lib, rows=0, q=None, out=None, ws=None) == 0
     n = ctypes.c_int64(-1)
     assert lib.qsa_prefill_topk_workspace_bytes(8192, 27048, 512, ctypes.byref(n)) == 0
-    # Group maxima of 8-key groups (4 B each) and a candidate pool of
-    # 8 (k - 1) + chunks * k 8-byte entries per row: under the 512 MiB the
-    # 886 MB score matrix would exceed.
-    assert 8192 * 8 * (8 * 511 + 512) < n.value < 512 * 2**20
+    # The cells' 16-bit key prefixes on rows padded to 64 columns, plus the
+    # fallback's 64 fp32 scratch rows: half the 886 MB score matrix, under
+    # the 512 MiB logits workspace.
+    assert 8192 * 27072 * 2 + 64 * 27072 * 4 <= n.value < 8192 * 27072 * 2 + 8 * 2**20
+    assert n.value < 512 * 2**20
+    w = ctypes.c_int64(-1)
+    # Wider rows: group maxima of 8-key groups (4 B each) and a candidate
+    # pool of 8 (k - 1) + chunks * k 8-byte entries per row.
+    assert lib.qsa_prefill_topk_workspace_bytes(1024, 40000, 512, ctypes.byref(w)) == 0
+    assert 1024 * 8 * (8 * 511 + 512) < w.value
     m = ctypes.c_int64(-1)
     assert lib.qsa_prefill_topk_workspace_bytes(100, 27048, 512, ctypes.byref(m)) == 0
     assert 0 < m.value < n.value

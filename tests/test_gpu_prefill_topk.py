@@ -147,3 +147,35 @@ def test_fused_workspace_reuse_and_zero_columns():
                              topk, out=out)
     torch.cuda.synchronize()
     assert torch.all(out == -1)
+
+
+def test_fused_rows_left_to_the_fallback():
+    # k = 2048 over rows of 5,000-12,000 visible keys: fewer than k of the
+    # 8-key chunks bound the floor, so more than the in-register list holds
+    # is listed, and those rows are rescored whole by the fallback (more rows
+    # than it has workgroups, so each takes several).
+    rng = np.random.default_rng(61)
+    T, NK, cols, topk = 200, 12000, 12000, 2048
+    q = normal_bf16(rng, (T, 4, 128))
+    k = normal_bf16(rng, (NK, 128))
+    ks = np.zeros(T, np.int32)
+    ke = rng.integers(5000, NK + 1, T).astype(np.int32)
+    ke[::7] = rng.integers(0, 2000, len(ke[::7]))  # and some rows the list holds
+    fused, composed, _ = _both(q, k, ks, ke, cols, topk)
+    _assert_same(fused, composed, "fallback rows")
+    rows = np.array([0, 1, 7, 100, T - 1])
+    assert_topk_valid(fused[torch.from_numpy(rows).cuda()], O.prefill(q, k, ks, ke, cols, rows=rows), topk)
+
+
+def test_fused_wide_rows():
+    # Rows wider than 32,768 columns take the group-maximum path.
+    rng = np.random.default_rng(71)
+    T, NK, cols, topk = 96, 41000, 40000, 512
+    q = normal_bf16(rng, (T, 4, 128))
+    k = normal_bf16(rng, (NK, 128))
+    ks = rng.integers(-100, 900, T).astype(np.int32)
+    ke = (ks + rng.integers(0, cols + 200, T)).astype(np.int32)
+    fused, composed, _ = _both(q, k, ks, ke, cols, topk)
+    _assert_same(fused, composed, "wide rows")
+    rows = np.array([0, 5, T - 1])
+    assert_topk_valid(fused[torch.from_numpy(rows).cuda()], O.prefill(q, k, ks, ke, cols, rows=rows), topk)
