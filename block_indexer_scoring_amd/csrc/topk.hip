@@ -40,6 +40,7 @@ namespace qsa {
 namespace {
 
 constexpr int kMaxWaves = 16;  // workgroups of at most 1024 threads
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: raw dword access
 
 
@@ -408,7 +409,7 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
     __shared__ int list_col[kListCap];
     __shared__ int tied_idx[128];
     __shared__ uint32_t s_floor, s_T;
-    __shared__ int s_need;
+    __shared__ int s_need, s_num_cand;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -418,9 +419,9 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
     const int col0 = tid * E;  // the thread's run for the re-reading paths: col0 .. col0 + E - 1
 
     // Keys stay in registers as their top 16 bits, two per register: enough
-    // to test key >= floor exactly (the floor is a multiple of 2^21).  The
-    // maximum of each sub-run of the thread's keys is kept in full; the
-    // sub-run maxima are distinct keys, each witnessing one key >= itself.
+    // to test key >= floor exactly (the floor is a multiple of 2^16).  The
+    // maximum top half of each sub-run of the thread's keys is kept; the
+    // sub-run maxima are distinct cells, each witnessing one key >= itself.
     // Element j = 4e + i of this thread is column 4 * (tid + THREADS * e) + i:
     // load e of the workgroup covers 16 * THREADS contiguous bytes, every
     // 128-byte line read by one instruction of one wave.
@@ -429,22 +430,63 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
     int cand = 0;
     auto absorb = [&](int e, uint32_t k) {
         cand += k != 0u;
-        smax[e / kSubLen] = max(smax[e / kSubLen], k);
+        smax[e / kSubLen] = max(smax[e / kSubLen], k >> 16);
         if (e % 2 == 0) top16[e / 2] = k >> 16;
         else top16[e / 2] |= k & 0xffff0000u;
     };
     auto chunk_col = [&](int e) { return 4 * (tid + THREADS * e); };
     if (vec_rows) {
-        // All of the thread's 16-byte loads in flight at once.
-        const float ni = neg_inf();
+        // All of the thread's 16-byte loads in flight at once, and none of
+        // them conditional, so each chunk's keys are formed as soon as its
+        // load lands: the row is one buffer resource (a load past its end
+        // returns zeros), and the cells of chunks past the end are compared
+        // with +inf instead of -inf, so none of them is a candidate.
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(x), 0, num_cols * 4, kBufferWord3);
         f32x4 v[kChunks];
 #pragma unroll
+        for (int e = 0; e < kChunks; ++e)
+            v[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * (tid + THREADS * e), 0, 0));
+        // Every load issued before any key is formed: the chunks are then
+        // consumed in load order, each freeing its registers.
+        __builtin_amdgcn_sched_barrier(0);
+        // The key of a candidate f (> -inf, not NaN) is order_key(f): the
+        // bits of f + 0 (which turns -0 into +0 and changes nothing else,
+        // fp32 denormals being kept) with the sign bit set when it is clear,
+        // all bits flipped when it is set.  Candidates are counted per wave
+        // (ballot) rather than per lane.
+        uint32_t wcand = 0u;
+#pragma unroll
         for (int e = 0; e < kChunks; ++e) {
-            const int c = chunk_col(e);
-            v[e] = c < num_cols ? *reinterpret_cast<const f32x4 *>(x + c) : f32x4{ni, ni, ni, ni};
+            const float bound = chunk_col(e) < num_cols ? neg_inf() : __builtin_inff();
+            uint32_t k[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float f = v[e][i];
+                const bool is_cand = f > bound;
+                const uint32_t u = __float_as_uint(f + 0.0f);
+                const uint32_t sgn = (uint32_t)((int32_t)u >> 31);
+                k[i] = is_cand ? u ^ (sgn | 0x80000000u) : 0u;
+                wcand += (uint32_t)__popcll(__ballot(is_cand));
+            }
+            // Top halves, two to a register (even key low).
+            top16[2 * e] = __builtin_amdgcn_perm(k[1], k[0], 0x07060302u);
+            top16[2 * e + 1] = __builtin_amdgcn_perm(k[3], k[2], 0x07060302u);
+        }
+        cand = lane == 0 ? (int)wcand : 0;
+        // Sub-run maxima of the top halves (sub-run j: the chunks e with
+        // kSub e / kChunks == j), two halves at a time.
+        u16x2 m2[kSub];
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) m2[j] = u16x2{0, 0};
+#pragma unroll
+        for (int e = 0; e < kChunks; ++e) {
+            const int j = kSub * e / kChunks;
+            m2[j] = __builtin_elementwise_max(m2[j], __builtin_elementwise_max(__builtin_bit_cast(u16x2, top16[2 * e]),
+                                                                               __builtin_bit_cast(u16x2, top16[2 * e + 1])));
         }
 #pragma unroll
-        for (int e = 0; e < E; ++e) absorb(e, order_key(v[e / 4][e % 4]));
+        for (int j = 0; j < kSub; ++j) smax[j] = max((uint32_t)m2[j][0], (uint32_t)m2[j][1]);
     } else {
         // Rows without 16-byte alignment or with a ragged last chunk.
 #pragma unroll
@@ -461,6 +503,7 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
     }
     int num_cand;
     block_exclusive_scan<THREADS>(cand, sh.wave_tmp, &num_cand);  // its barriers also publish the cleared histograms
+    if (tid == 0) s_num_cand = num_cand;  // read after later barriers
 
     // Paths that need every key again (few candidates, or a list overflow)
     // re-read this thread's run of the row.
@@ -477,7 +520,7 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
         // candidate.
 #pragma unroll
         for (int j = 0; j < kSub; ++j)
-            if (smax[j] != 0u) atomicAdd(&sh.hist[smax[j] >> 21], 1);
+            if (smax[j] != 0u) atomicAdd(&sh.hist[smax[j] >> 5], 1);
         __syncthreads();
         if (tid < 64) {
             int above;
@@ -492,7 +535,7 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
             const uint32_t b0 = s_floor >> 21;
 #pragma unroll
             for (int j = 0; j < kSub; ++j)
-                if ((smax[j] >> 21) == b0) atomicAdd(&hist_list[(smax[j] >> 16) & 31], 1);
+                if ((smax[j] >> 5) == b0) atomicAdd(&hist_list[smax[j] & 31], 1);
             __syncthreads();
             if (tid < 64) {
                 int above;
@@ -514,6 +557,12 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
         // waves before w in chunk e.  Per-lane counts of each chunk, three
         // 10-bit fields to a word (a wave's count per chunk is at most 256),
         // are scanned across the wave with DPP.
+        // Bit i of chunk_bits(e, f): key 4e + i is listed (top half >= f).
+        auto chunk_bits = [&](int e, uint32_t f) {
+            const uint32_t a = top16[2 * e], b = top16[2 * e + 1];
+            return (uint32_t)((a & 0xffffu) >= f) | ((uint32_t)((a >> 16) >= f) << 1) |
+                   ((uint32_t)((b & 0xffffu) >= f) << 2) | ((uint32_t)((b >> 16) >= f) << 3);
+        };
         uint32_t packed[kWords], incl[kWords];
 #pragma unroll
         for (int w = 0; w < kWords; ++w) packed[w] = 0u;
@@ -526,6 +575,8 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
 #pragma unroll
             for (int e = 0; e < kChunks; ++e) seg_count[e * kWaves + wave] = (int)((incl[e / 3] >> (10 * (e % 3))) & 1023u);
         }
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) incl[w] -= packed[w];  // exclusive from here on
         __syncthreads();
         // Lane c (< kChunks) of every wave: the chunk's total and this wave's
         // offset within it, then a scan over chunks.
@@ -544,18 +595,17 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
         int need = 0;
         if (listed <= kListCap) {
             // The keys >= floor in column order (top halves), counted by
-            // their top 11 bits.
+            // their top 11 bits.  Each lane visits only its listed keys of a
+            // chunk (a few percent of the cells on score rows), by their
+            // bits; the bits are formed again, against a copy of the floor
+            // the compiler cannot prove equal, rather than kept from the
+            // count above (one register per chunk).
             const uint32_t floor_top2 = __builtin_amdgcn_readfirstlane(floor_top);
 #pragma unroll
             for (int e = 0; e < kChunks; ++e) {
-                int w = __builtin_amdgcn_readlane(seg_off, e) +
-                        (int)(((incl[e / 3] - packed[e / 3]) >> (10 * (e % 3))) & 1023u);
+                int w = __builtin_amdgcn_readlane(seg_off, e) + (int)((incl[e / 3] >> (10 * (e % 3))) & 1023u);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    // The same test as the count above, against a copy of the
-                    // floor the compiler cannot prove equal, so it recomputes
-                    // the tests here instead of keeping one lane mask per key
-                    // alive.
                     const uint32_t t = key_top(4 * e + i);
                     const bool in = t >= floor_top2;
                     if (in) {
@@ -590,7 +640,9 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
             place_picks<E, kFromRowRun, THREADS>(no_list, run, 0, 0, T, need, out, sh);
         }
     }
-    const int picked = min(num_cand, p.k);
+    // The candidate count from LDS rather than a register kept live (and
+    // spilled) through the select.
+    const int picked = min(s_num_cand, p.k);
     for (int i = picked + tid; i < p.k; i += THREADS) out[i] = -1;
 }
 
