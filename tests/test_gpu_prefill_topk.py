@@ -179,3 +179,29 @@ def test_fused_wide_rows():
     _assert_same(fused, composed, "wide rows")
     rows = np.array([0, 5, T - 1])
     assert_topk_valid(fused[torch.from_numpy(rows).cuda()], O.prefill(q, k, ks, ke, cols, rows=rows), topk)
+
+
+def test_fused_non_finite_inputs():
+    # NaN and +-inf in queries and keys give NaN and +inf scores: a NaN cell
+    # is never picked and +inf cells rank first, in the fused path (16-bit
+    # key prefixes, rescored ties) as in the composition.
+    rng = np.random.default_rng(81)
+    T, NK, cols, topk = 160, 1500, 1400, 200
+    q = normal_bf16(rng, (T, 4, 128))
+    k = normal_bf16(rng, (NK, 128))
+    nan, pinf, ninf = np.uint16(0x7FC0), np.uint16(0x7F80), np.uint16(0xFF80)
+    q[3, 0, 5] = nan           # row 3: a NaN head, so every visible score is NaN or the other heads' sum
+    q[7, :, :] = 0
+    q[7, 1, 9] = pinf          # row 7: +inf x key feature -> +inf, NaN (x 0) or -inf dots
+    k[11, 17] = nan            # key 11: NaN in every row's dot with it
+    k[40, 2] = pinf
+    k[41, 2] = ninf
+    k[300:340] = k[299]        # a run of identical keys: ties across the picked boundary
+    ks = np.zeros(T, np.int32)
+    ke = rng.integers(topk // 2, cols + 1, T).astype(np.int32)
+    ke[3] = ke[7] = cols
+    fused, composed, scores = _both(q, k, ks, ke, cols, topk)
+    _assert_same(fused, composed, "non-finite inputs")
+    want = O.topk(scores.cpu().numpy(), topk)
+    assert np.array_equal(fused.cpu().numpy(), want)
+    assert 11 not in fused[5].cpu().numpy().tolist()   # the NaN key's cell is never picked
