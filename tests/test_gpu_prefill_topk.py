@@ -205,3 +205,20 @@ def test_fused_non_finite_inputs():
     want = O.topk(scores.cpu().numpy(), topk)
     assert np.array_equal(fused.cpu().numpy(), want)
     assert 11 not in fused[5].cpu().numpy().tolist()   # the NaN key's cell is never picked
+
+
+@pytest.mark.parametrize("cols", [28_700, 32_768, 32_769])
+def test_fused_widest_key_select_rows(cols):
+    # The key select's widest shape (64 key prefixes per thread, up to 32,768
+    # columns) and the first width past it (the group-maximum path).
+    rng = np.random.default_rng(cols)
+    T, topk = 48, 512
+    NK = cols + 300
+    q = normal_bf16(rng, (T, 4, 128))
+    k = normal_bf16(rng, (NK, 128))
+    ks = rng.integers(-50, 250, T).astype(np.int32)
+    ke = (ks + rng.integers(cols // 2, cols + 100, T)).astype(np.int32)
+    fused, composed, _ = _both(q, k, ks, ke, cols, topk)
+    _assert_same(fused, composed, f"{cols} columns")
+    rows = np.array([0, T - 1])
+    assert_topk_valid(fused[torch.from_numpy(rows).cuda()], O.prefill(q, k, ks, ke, cols, rows=rows), topk)
