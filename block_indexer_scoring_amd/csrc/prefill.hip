@@ -845,6 +845,7 @@ hipError_t launch_prefill_candidates(const PrefillParams &p, hipStream_t stream)
 
 hipError_t launch_prefill_keys16(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.row_blocks * p.col_chunks));
+    if (p.f16) return launch_kernel(prefill_kernel<kModeKeys16, true, false>, grid, dim3(kThreads), stream, p);
     return launch_kernel(prefill_kernel<kModeKeys16, false, false>, grid, dim3(kThreads), stream, p);
 }
 

@@ -798,7 +798,7 @@ int qsa_prefill_topk_workspace_bytes(int32_t num_rows, int32_t out_cols, int32_t
 // for rows that select leaves.  Arguments already checked by the caller:
 // sizes, scale, topk, out_idx and the workspace's alignment.
 static int prefill_topk_keys16(const char *fn, const void *q, int64_t q_stride_row, int64_t q_stride_head,
-                               const void *k, int64_t k_stride, int64_t num_keys, const int32_t *row_k_start,
+                               const void *k, int64_t k_stride, int64_t num_keys, bool f16, const int32_t *row_k_start,
                                const int32_t *row_k_end, int32_t num_rows, float scale, int32_t out_cols,
                                int32_t topk, int32_t *out_idx, int64_t out_stride, void *workspace,
                                int64_t workspace_bytes, void *stream, int cus) {
@@ -840,6 +840,7 @@ static int prefill_topk_keys16(const char *fn, const void *q, int64_t q_stride_r
     p.col_chunk = chunk;
     p.row_blocks = (int32_t)row_blocks;
     p.col_chunks = (int32_t)col_chunks;
+    p.f16 = f16;
     p.keys16 = reinterpret_cast<uint16_t *>(ws + L.off_keys);
     p.keys_stride = L.stride;
     p.hard_count = reinterpret_cast<int32_t *>(ws + L.off_count);
@@ -861,6 +862,7 @@ static int prefill_topk_keys16(const char *fn, const void *q, int64_t q_stride_r
     t.row_k_start = row_k_start;
     t.row_k_end = row_k_end;
     t.scale = scale;
+    t.f16 = f16;
     t.hard_count = p.hard_count;
     t.hard_rows = reinterpret_cast<int32_t *>(ws + L.off_hard);
     t.scratch = reinterpret_cast<float *>(ws + L.off_scratch);
@@ -880,15 +882,17 @@ static int prefill_topk_keys16(const char *fn, const void *q, int64_t q_stride_r
     return device_status(fn, err);
 }
 
-int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
-                         int64_t k_stride, int64_t num_keys, const int32_t *row_k_start,
-                         const int32_t *row_k_end, int32_t num_rows, int32_t num_heads, int32_t head_dim,
-                         float scale, int32_t out_cols, int32_t topk, int32_t *out_idx, int64_t out_stride,
-                         void *workspace, int64_t workspace_bytes, void *stream) {
-    const char *fn = "qsa_mqa_prefill_topk";
+static int prefill_topk_impl(const char *fn, const void *q, int64_t q_stride_row, int64_t q_stride_head,
+                             const void *k, int64_t k_stride, int64_t num_keys, int32_t dtype,
+                             const int32_t *row_k_start, const int32_t *row_k_end, int32_t num_rows,
+                             int32_t num_heads, int32_t head_dim, float scale, int32_t out_cols, int32_t topk,
+                             int32_t *out_idx, int64_t out_stride, void *workspace, int64_t workspace_bytes,
+                             void *stream) {
     int rc;
     if ((rc = check_heads(fn, num_heads, head_dim))) return rc;
     if ((rc = check_scale(fn, scale))) return rc;
+    if (dtype != QSA_DTYPE_BF16 && dtype != QSA_DTYPE_FP16)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: format %d is not QSA_DTYPE_BF16 or QSA_DTYPE_FP16", fn, dtype);
     if (num_rows < 0 || out_cols < 0 || num_keys < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
     if (topk < 1 || topk > qsa::kFusedMaxK)
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: topk must be in [1, %d], got %d", fn, qsa::kFusedMaxK, topk);
@@ -899,9 +903,12 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     if (!aligned(workspace, 256)) return fail(QSA_ERR_LAYOUT, "%s: workspace must be 256-byte aligned", fn);
     const int cus = current_cu_count();
     if (use_keys16(out_cols))
-        return prefill_topk_keys16(fn, q, q_stride_row, q_stride_head, k, k_stride, num_keys, row_k_start, row_k_end,
-                                   num_rows, scale, out_cols, topk, out_idx, out_stride, workspace, workspace_bytes,
-                                   stream, cus);
+        return prefill_topk_keys16(fn, q, q_stride_row, q_stride_head, k, k_stride, num_keys, dtype == QSA_DTYPE_FP16,
+                                   row_k_start, row_k_end, num_rows, scale, out_cols, topk, out_idx, out_stride,
+                                   workspace, workspace_bytes, stream, cus);
+    if (dtype != QSA_DTYPE_BF16 && out_cols > 0)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: fp16 rows wider than %d columns are not supported", fn,
+                    qsa::kKeys16MaxCols);
     const FusedLayout L = fused_layout(num_rows, out_cols, topk, cus);
     if (workspace_bytes < L.total)
         return fail(QSA_ERR_INVALID_ARGUMENT, "%s: workspace of %lld bytes, %lld needed", fn,
@@ -984,6 +991,26 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
     if (err == hipSuccess) err = qsa::launch_topk_candidates(fp, st);
     g_launch_events = ev;
     return device_status(fn, err);
+}
+
+int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
+                         int64_t k_stride, int64_t num_keys, const int32_t *row_k_start,
+                         const int32_t *row_k_end, int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                         float scale, int32_t out_cols, int32_t topk, int32_t *out_idx, int64_t out_stride,
+                         void *workspace, int64_t workspace_bytes, void *stream) {
+    return prefill_topk_impl("qsa_mqa_prefill_topk", q, q_stride_row, q_stride_head, k, k_stride, num_keys,
+                             QSA_DTYPE_BF16, row_k_start, row_k_end, num_rows, num_heads, head_dim, scale, out_cols,
+                             topk, out_idx, out_stride, workspace, workspace_bytes, stream);
+}
+
+int qsa_mqa_prefill_topk_typed(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
+                               int64_t k_stride, int64_t num_keys, int32_t dtype, const int32_t *row_k_start,
+                               const int32_t *row_k_end, int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                               float scale, int32_t out_cols, int32_t topk, int32_t *out_idx, int64_t out_stride,
+                               void *workspace, int64_t workspace_bytes, void *stream) {
+    return prefill_topk_impl("qsa_mqa_prefill_topk_typed", q, q_stride_row, q_stride_head, k, k_stride, num_keys,
+                             dtype, row_k_start, row_k_end, num_rows, num_heads, head_dim, scale, out_cols, topk,
+                             out_idx, out_stride, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

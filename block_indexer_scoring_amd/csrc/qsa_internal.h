@@ -140,6 +140,7 @@ struct Keys16TopkParams {
     int64_t k_stride, num_keys;
     const int32_t *row_k_start, *row_k_end;
     float scale;
+    int32_t f16;                // queries and keys are fp16, not bf16
     int32_t *hard_count;        // rows listed for the fallback
     int32_t *hard_rows;         // [num_rows]
     float *scratch;             // [scratch_rows][scratch_stride] fp32 rows of the fallback

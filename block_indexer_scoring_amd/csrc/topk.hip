@@ -1083,11 +1083,11 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
 
 // Full order keys of 64 cells of prefill row `row`, one per lane: lane l's
 // cell is key index key_idx (which every lane must hold in [0, num_keys)).
-// The MFMA layout is the prefill kernel's: A lane (n, q4) holds head n % 4
-// of the row, features 32 ks + 8 q4 .. +7 in k-step ks, so every group of 4
-// result rows holds the 4 head dots; B lane (n, q4) of group g holds the
-// same features of lane 16 g + n's key.  Lane l = 16 q4 + n takes group q4's
-// result, which its own lane holds.
+// The MFMA instruction (bf16 or fp16) and layout are the prefill kernel's:
+// A lane (n, q4) holds head n % 4 of the row, features 32 ks + 8 q4 .. +7 in
+// k-step ks, so every group of 4 result rows holds the 4 head dots; B lane
+// (n, q4) of group g holds the same features of lane 16 g + n's key.  Lane
+// l = 16 q4 + n takes group q4's result, which its own lane holds.
 __device__ __forceinline__ uint32_t rescore_key(const Keys16TopkParams &p, int64_t row, int64_t key_idx) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, q4 = lane >> 4;
@@ -1108,8 +1108,13 @@ __device__ __forceinline__ uint32_t rescore_key(const Keys16TopkParams &p, int64
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (p.f16) {  // wave-uniform: the fp16 product of the fp16 key pass
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc[g] = mfma16x16x32(a[ks], b[g][ks], acc[g]);
+            for (int ks = 0; ks < 4; ++ks) acc[g] = mfma_qk<true>(a[ks], b[g][ks], acc[g]);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) acc[g] = mfma_qk<false>(a[ks], b[g][ks], acc[g]);
+        }
     }
     const f32x4 mine = q4 == 0 ? acc[0] : (q4 == 1 ? acc[1] : (q4 == 2 ? acc[2] : acc[3]));
     return order_key(head_sum_score(mine, p.scale));

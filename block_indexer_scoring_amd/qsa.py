@@ -21,7 +21,7 @@ QSA_ERR_INVALID_ARGUMENT = 1
 QSA_ERR_UNSUPPORTED = 2
 QSA_ERR_LAYOUT = 3
 QSA_ERR_DEVICE = 4
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_set_launch_events", "qsa_split_batch",
            "qsa_build_metadata", "qsa_mqa_decode", "qsa_mqa_prefill", "qsa_topk_blocks",
@@ -29,7 +29,7 @@ SYMBOLS = ("qsa_abi_version", "qsa_last_error", "qsa_set_launch_events", "qsa_sp
            "qsa_mqa_prefill_typed", "qsa_build_cache_metadata", "qsa_gather_keys", "qsa_prepare_q",
            "qsa_decode_plan_bytes", "qsa_build_decode_plan", "qsa_mqa_decode_planned",
            "qsa_decode_visible_blocks", "qsa_mqa_decode_static_plan", "qsa_build_ring_slots",
-           "qsa_write_keys")
+           "qsa_write_keys", "qsa_mqa_prefill_topk_typed")
 
 # enum qsa_dtype
 QSA_DTYPE_BF16 = 0
@@ -92,6 +92,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_mqa_prefill_topk.argtypes = [P, i64, i64, P, i64, i64, P, P, i32, i32, i32, f32, i32, i32,
                                          P, i64, P, i64, P]
     lib.qsa_mqa_prefill_topk.restype = ctypes.c_int
+    lib.qsa_mqa_prefill_topk_typed.argtypes = [P, i64, i64, P, i64, i64, i32, P, P, i32, i32, i32, f32, i32,
+                                               i32, P, i64, P, i64, P]
+    lib.qsa_mqa_prefill_topk_typed.restype = ctypes.c_int
     lib.qsa_prefill_topk_workspace_bytes.argtypes = [i32, i32, i32, P]
     lib.qsa_prefill_topk_workspace_bytes.restype = ctypes.c_int
     lib.qsa_prepare_q.argtypes = [P, i64, i32, i32, P, i64, i64, P, i32, i64, P, i32, f32, P, P, i32, f32,
@@ -655,12 +658,14 @@ def qsa_mqa_prefill_topk(q: torch.Tensor, k: torch.Tensor, row_k_start: torch.Te
                          scale: float = DEFAULT_SCALE, out: torch.Tensor | None = None,
                          workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Prefill scores and per-row top-k in one call, without the score matrix:
-    int32 [T, topk], equal to qsa_topk_blocks(qsa_mqa_prefill(...), topk).
-    workspace: uint8 device tensor of at least qsa_prefill_topk_workspace_bytes
-    bytes (allocated here when not given)."""
+    int32 [T, topk], equal to qsa_topk_blocks(qsa_mqa_prefill(...), topk)
+    (qsa_mqa_prefill_typed for fp16 q and k).  workspace: uint8 device tensor
+    of at least qsa_prefill_topk_workspace_bytes bytes (allocated here when
+    not given)."""
     lib = load_library()
-    _gpu("q", q, torch.bfloat16)
-    _gpu("k", k, torch.bfloat16)
+    fmt = _gpu_format("q", q, (torch.bfloat16, torch.float16))
+    if _gpu_format("k", k, (torch.bfloat16, torch.float16)) != fmt:
+        raise TypeError("q and k must share their dtype")
     _gpu("row_k_start", row_k_start, torch.int32)
     _gpu("row_k_end", row_k_end, torch.int32)
     if q.dim() != 3 or k.dim() != 2:
@@ -682,10 +687,13 @@ def qsa_mqa_prefill_topk(q: torch.Tensor, k: torch.Tensor, row_k_start: torch.Te
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _gpu("workspace", workspace, torch.uint8)
-    _check(lib.qsa_mqa_prefill_topk(
-        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.shape[0], _ptr(row_k_start),
-        _ptr(row_k_end), num_rows, heads, dim, float(scale), int(out_cols), int(topk), _ptr(out),
-        out.stride(0), _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+    args = (_ptr(row_k_start), _ptr(row_k_end), num_rows, heads, dim, float(scale), int(out_cols), int(topk),
+            _ptr(out), out.stride(0), _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    if fmt == QSA_DTYPE_BF16:
+        _check(lib.qsa_mqa_prefill_topk(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.shape[0], *args))
+    else:
+        _check(lib.qsa_mqa_prefill_topk_typed(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0),
+                                              k.shape[0], fmt, *args))
     return out
 
 

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 10
+#define QSA_ABI_VERSION 11
 
 enum qsa_status {
     QSA_OK = 0,
@@ -79,7 +79,8 @@ const char *qsa_last_error(void);
  *   the stream around the call adds.  Each entry point below launches one
  *   kernel (none when it has nothing to compute), except
  *   qsa_build_cache_metadata (up to two), qsa_mqa_decode_static_plan (two)
- *   and qsa_mqa_prefill_topk (three, or four on rows wider than 32,768 columns):
+ *   and qsa_mqa_prefill_topk / qsa_mqa_prefill_topk_typed (three, or four
+ *   on rows wider than 32,768 columns):
  *   for those the start event marks the first kernel's begin and the stop
  *   event the last kernel's end.
  *   start_event, stop_event : hipEvent_t handles created by the caller (may
@@ -577,7 +578,24 @@ int qsa_mqa_prefill_topk(const void *q, int64_t q_stride_row, int64_t q_stride_h
                          float scale, int32_t out_cols, int32_t topk, int32_t *out_idx, int64_t out_stride,
                          void *workspace, int64_t workspace_bytes, void *stream);
 
+/* qsa_mqa_prefill_topk_typed -- qsa_mqa_prefill_topk with BF16 or FP16
+ *   queries and keys (dtype QSA_DTYPE_BF16 or QSA_DTYPE_FP16; both share it).
+ *   Source: MATE "QSA (Qwen Sparse Attention)", section "MQA score" (BF16 or
+ *   FP16 query and key), composed with the top-k as above.
+ *   Result: equal to qsa_topk_blocks applied to the output of
+ *   qsa_mqa_prefill_typed with the same arguments, bit for bit (fp16 rows
+ *   are scored and rescored with the fp16 product).  Workspace, arguments
+ *   and errors as qsa_mqa_prefill_topk, plus UNSUPPORTED for any other
+ *   dtype and for FP16 rows wider than 32,768 columns.
+ */
+int qsa_mqa_prefill_topk_typed(const void *q, int64_t q_stride_row, int64_t q_stride_head, const void *k,
+                               int64_t k_stride, int64_t num_keys, int32_t dtype, const int32_t *row_k_start,
+                               const int32_t *row_k_end, int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                               float scale, int32_t out_cols, int32_t topk, int32_t *out_idx, int64_t out_stride,
+                               void *workspace, int64_t workspace_bytes, void *stream);
+
 /* qsa_prefill_topk_workspace_bytes -- workspace size qsa_mqa_prefill_topk
+ *   (and qsa_mqa_prefill_topk_typed)
  *   needs for these sizes on the current device (host only; the column
  *   split depends on the device's compute-unit count).
  *   Errors: INVALID_ARGUMENT for a NULL bytes, negative sizes or topk

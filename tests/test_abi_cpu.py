@@ -517,6 +517,29 @@ def test_fused_prefill_topk_rejects(lib, kw, code, text):
     assert text in _err(lib)
 
 
+def _fused_typed(lib, dtype, **kw):
+    a = dict(q=FAKE, sq=512, sh=128, k=FAKE, sk=128, nk=100, ks=FAKE, ke=FAKE, rows=10, heads=4,
+             dim=128, scale=0.088, out_cols=100, topk=16, out=FAKE, out_stride=16, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.qsa_mqa_prefill_topk_typed(a["q"], a["sq"], a["sh"], a["k"], a["sk"], a["nk"], dtype, a["ks"],
+                                          a["ke"], a["rows"], a["heads"], a["dim"], a["scale"], a["out_cols"],
+                                          a["topk"], a["out"], a["out_stride"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("dtype,kw,code,text", [
+    (2, {}, 2, "format"),                                   # e4m3 queries and keys: not a prefill format
+    (3, {}, 2, "format"),
+    (1, dict(out_cols=40000), 2, "fp16 rows wider"),        # fp16 takes the key-prefix path only
+    (1, dict(topk=0), 1, "topk"),
+    (1, dict(ws_bytes=1000), 1, "needed"),
+    (1, dict(rows=0, q=None, out=None, ws=None), 0, ""),
+])
+def test_fused_prefill_topk_typed_rejects(lib, dtype, kw, code, text):
+    assert _fused_typed(lib, dtype, **kw) == code
+    if code:
+        assert text in _err(lib)
+
+
 def test_fused_prefill_topk_zero_rows_and_workspace_size(lib):
     assert _fused(lib, rows=0, q=None, out=None, ws=None) == 0
     n = ctypes.c_int64(-1)

@@ -222,3 +222,38 @@ def test_fused_widest_key_select_rows(cols):
     _assert_same(fused, composed, f"{cols} columns")
     rows = np.array([0, T - 1])
     assert_topk_valid(fused[torch.from_numpy(rows).cuda()], O.prefill(q, k, ks, ke, cols, rows=rows), topk)
+
+
+def _f16(bits_bf16):
+    """bf16 bit patterns -> the same values as an fp16 device tensor (values
+    drawn N(0,1) are well inside fp16's range; rounding to fp16 is fine: both
+    sides of the comparison get the same fp16 inputs)."""
+    f = torch.from_numpy(bits_bf16.astype(np.uint32) << 16).view(torch.float32)
+    return f.to(torch.float16).cuda()
+
+
+@pytest.mark.parametrize("name", ["prefill_1x8k_100k", None])
+def test_fused_fp16_equals_typed_composition(name):
+    qsa = _qsa()
+    if name:
+        inp = WORKLOADS[name].make()
+        q, k, cols, topk = inp.q, inp.k, inp.out_cols, 512
+        ks, ke = _intervals(inp)
+    else:
+        rng = np.random.default_rng(91)
+        T, NK, cols, topk = 260, 3000, 2900, 300
+        q = normal_bf16(rng, (T, 4, 128))
+        base = normal_bf16(rng, (60, 128))
+        k = base[rng.integers(0, 60, NK)]      # repeated keys: exact ties
+        q[2] = 0                               # a row of +0 scores (the fallback)
+        ks = rng.integers(-40, 80, T).astype(np.int32)
+        ke = (ks + rng.integers(0, cols + 60, T)).astype(np.int32)
+    qd, kd = _f16(q), _f16(k)
+    ksd, ked = i32_to_device(ks), i32_to_device(ke)
+    fused = qsa.qsa_mqa_prefill_topk(qd, kd, ksd, ked, cols, topk)
+    scores = qsa.qsa_mqa_prefill_typed(qd, kd, ksd, ked, cols)
+    composed = qsa.qsa_topk_blocks(scores, topk)
+    torch.cuda.synchronize()
+    _assert_same(fused, composed, f"fp16 {name or 'small with ties'}")
+    if not name:
+        assert np.array_equal(fused.cpu().numpy(), O.topk(scores.cpu().numpy(), topk))
