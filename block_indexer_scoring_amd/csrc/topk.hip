@@ -1088,10 +1088,15 @@ __global__ __launch_bounds__(256) void topk_candidates_kernel(FusedTopkParams p)
 // k-step ks, so every group of 4 result rows holds the 4 head dots; B lane
 // (n, q4) of group g holds the same features of lane 16 g + n's key.  Lane
 // l = 16 q4 + n takes group q4's result, which its own lane holds.
-__device__ __forceinline__ uint32_t rescore_key(const Keys16TopkParams &p, int64_t row, int64_t key_idx) {
+// q_lds: the row's four heads (4 x 128 elements, head-major) staged in LDS,
+// or null to read them from memory.
+template <bool kF16>
+__device__ __forceinline__ uint32_t rescore_key(const Keys16TopkParams &p, int64_t row, int64_t key_idx,
+                                                const uint16_t *q_lds = nullptr) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, q4 = lane >> 4;
-    const uint16_t *qrow = p.q + row * p.q_stride_row + (int64_t)(n & 3) * p.q_stride_head + 8 * q4;
+    const uint16_t *qrow = q_lds ? q_lds + (n & 3) * 128 + 8 * q4
+                                 : p.q + row * p.q_stride_row + (int64_t)(n & 3) * p.q_stride_head + 8 * q4;
     u32x4 a[4], b[4][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) a[ks] = load_u32x4(qrow + 32 * ks);
@@ -1108,13 +1113,8 @@ __device__ __forceinline__ uint32_t rescore_key(const Keys16TopkParams &p, int64
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (p.f16) {  // wave-uniform: the fp16 product of the fp16 key pass
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) acc[g] = mfma_qk<true>(a[ks], b[g][ks], acc[g]);
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) acc[g] = mfma_qk<false>(a[ks], b[g][ks], acc[g]);
-        }
+        for (int ks = 0; ks < 4; ++ks) acc[g] = mfma_qk<kF16>(a[ks], b[g][ks], acc[g]);
     }
     const f32x4 mine = q4 == 0 ? acc[0] : (q4 == 1 ? acc[1] : (q4 == 2 ? acc[2] : acc[3]));
     return order_key(head_sum_score(mine, p.scale));
@@ -1128,9 +1128,10 @@ __device__ __forceinline__ uint32_t rescore_key(const Keys16TopkParams &p, int64
 // fallback (more than 64 entries share that prefix and only some are
 // picked, or a rescored key disagrees with its stored prefix).  Requires
 // more than k listed entries.
+template <bool kF16>
 __device__ __forceinline__ int wave_select_keys16(uint32_t *list, int n, int k, const int *hist0, int *hist,
                                                   int *tied_idx, const Keys16TopkParams &p, int64_t row,
-                                                  int64_t start) {
+                                                  int64_t start, const uint16_t *q_lds) {
     const int lane = threadIdx.x & 63;
     int above;
     int kk = k;
@@ -1175,7 +1176,7 @@ __device__ __forceinline__ int wave_select_keys16(uint32_t *list, int n, int k, 
     const int idx = tied_idx[act ? lane : 0];
     const uint32_t entry = list[idx];
     const int col = (int)(entry & 0xffffu);
-    const uint32_t key = rescore_key(p, row, start + col);
+    const uint32_t key = rescore_key<kF16>(p, row, start + col, q_lds);
     if (__ballot(act && (key >> 16) != top) != 0ull) return -1;
     // The kk-th largest of the tied keys (kk < tied), most significant bit
     // first over the low half; kr ends as the number of keys equal to T
@@ -1205,7 +1206,7 @@ __device__ __forceinline__ int wave_select_keys16(uint32_t *list, int n, int k, 
 // width; the padding holds key 0, and loads past it return 0.  Floor from
 // the maxima of the chunks (distinct cells), list of the keys >= floor in
 // column order, one-wave select, placement from the list.
-template <int E, int THREADS, int WPE>
+template <int E, int THREADS, int WPE, bool kF16>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE)))
 void topk_keys16_kernel(const uint16_t *keys, int64_t keys_stride, Keys16TopkParams p) {
     constexpr int kChunks = E / 8;
@@ -1219,10 +1220,15 @@ void topk_keys16_kernel(const uint16_t *keys, int64_t keys_stride, Keys16TopkPar
     __shared__ int tied_idx[128];
     __shared__ uint32_t s_floor;
     __shared__ int s_need, s_T;
+    __shared__ __attribute__((aligned(16))) uint16_t q_lds[kHeads * kDim];  // the row's queries, for rescoring
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int64_t row = blockIdx.x;
+    // The row's queries (1 KB) are read ahead of its keys and staged in LDS,
+    // so the rescoring of tied cells does not wait on them.
+    u32x4 qv = zero_u32x4();
+    if (tid < 64) qv = load_u32x4(p.q + row * p.q_stride_row + (int64_t)(tid >> 4) * p.q_stride_head + 8 * (tid & 15));
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(keys + row * keys_stride), 0, (int)(keys_stride * 2), kBufferWord3);
     u32x4 w[kChunks];
@@ -1238,6 +1244,7 @@ void topk_keys16_kernel(const uint16_t *keys, int64_t keys_stride, Keys16TopkPar
         sh.hist[b] = 0;
         hist_list[b] = 0;
     }
+    if (tid < 64) *reinterpret_cast<u32x4 *>(&q_lds[8 * tid]) = qv;
     const int64_t start = p.row_k_start[row];
     int32_t *out = p.out + row * p.out_stride;
     __syncthreads();
@@ -1331,7 +1338,7 @@ void topk_keys16_kernel(const uint16_t *keys, int64_t keys_stride, Keys16TopkPar
             T16 = 0;  // every listed key is picked
         } else {
             if (tid < 64) {
-                const int t = wave_select_keys16(list, listed, p.k, hist_list, sh.hist, tied_idx, p, row, start);
+                const int t = wave_select_keys16<kF16>(list, listed, p.k, hist_list, sh.hist, tied_idx, p, row, start, q_lds);
                 if (lane == 0) s_T = t;
             }
             __syncthreads();
@@ -1364,6 +1371,7 @@ void topk_keys16_kernel(const uint16_t *keys, int64_t keys_stride, Keys16TopkPar
 // (-inf outside the row's keys, as the score kernel writes) and selects over
 // it.  The rescoring is the prefill's arithmetic (rescore_key), so the scores
 // and the picks are those of the score matrix.
+template <bool kF16>
 __global__ __launch_bounds__(1024) void topk_keys16_fallback_kernel(Keys16TopkParams p) {
     const int count = *p.hard_count;
     const int lane = threadIdx.x & 63;
@@ -1380,7 +1388,7 @@ __global__ __launch_bounds__(1024) void topk_keys16_fallback_kernel(Keys16TopkPa
             // Lanes outside the row's keys rescore a key that exists (their
             // result is dropped); a hard row has at least one key.
             const int64_t safe = kidx < 0 ? 0 : (kidx >= p.num_keys ? p.num_keys - 1 : kidx);
-            const uint32_t key = rescore_key(p, row, safe);
+            const uint32_t key = rescore_key<kF16>(p, row, safe);
             if (c < p.num_cols) {
                 // The score back from its key: scores here are >= +0, +inf or
                 // NaN (key 0, stored as NaN so that it is never picked).
@@ -1447,7 +1455,10 @@ hipError_t launch_keys16(const Keys16TopkParams &p, hipStream_t stream) {
         if constexpr (E + 8 <= 64) return launch_keys16<E + 8>(p, stream);
         return hipErrorInvalidValue;
     }
-    return launch_kernel(topk_keys16_kernel<E, 512, 8>, dim3((unsigned)p.num_rows), dim3(512), stream, p.keys,
+    if (p.f16)
+        return launch_kernel(topk_keys16_kernel<E, 512, 8, true>, dim3((unsigned)p.num_rows), dim3(512), stream,
+                             p.keys, p.keys_stride, p);
+    return launch_kernel(topk_keys16_kernel<E, 512, 8, false>, dim3((unsigned)p.num_rows), dim3(512), stream, p.keys,
                          p.keys_stride, p);
 }
 
@@ -1457,7 +1468,9 @@ hipError_t launch_topk_keys16(const Keys16TopkParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_topk_keys16_fallback(const Keys16TopkParams &p, hipStream_t stream) {
-    return launch_kernel(topk_keys16_fallback_kernel, dim3((unsigned)p.scratch_rows), dim3(1024), stream, p);
+    if (p.f16)
+        return launch_kernel(topk_keys16_fallback_kernel<true>, dim3((unsigned)p.scratch_rows), dim3(1024), stream, p);
+    return launch_kernel(topk_keys16_fallback_kernel<false>, dim3((unsigned)p.scratch_rows), dim3(1024), stream, p);
 }
 
 }  // namespace qsa
