@@ -42,6 +42,7 @@ namespace {
 constexpr int kMaxWaves = 16;  // workgroups of at most 1024 threads
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: raw dword access
+constexpr int kLoadNT = 2;                // cache policy of the row loads: non-temporal (the "nt" bit)
 
 
 // Inclusive prefix sum over a wavefront with DPP moves (no LDS): a
@@ -441,12 +442,16 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
         // load lands: the row is one buffer resource (a load past its end
         // returns zeros), and the cells of chunks past the end are compared
         // with +inf instead of -inf, so none of them is a candidate.
+        // The loads are non-temporal (the rows are read once; every line is
+        // read whole by one instruction): the prefill that runs next then finds
+        // its keys and queries still in the caches (the step's prefill measured
+        // 3% faster; this kernel the same).
         const __amdgpu_buffer_rsrc_t rsrc =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(x), 0, num_cols * 4, kBufferWord3);
         f32x4 v[kChunks];
 #pragma unroll
         for (int e = 0; e < kChunks; ++e)
-            v[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * (tid + THREADS * e), 0, 0));
+            v[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * (tid + THREADS * e), 0, kLoadNT));
         // Every load issued before any key is formed: the chunks are then
         // consumed in load order, each freeing its registers.
         __builtin_amdgcn_sched_barrier(0);
@@ -1234,7 +1239,7 @@ void topk_keys16_kernel(const uint16_t *keys, int64_t keys_stride, Keys16TopkPar
     u32x4 w[kChunks];
 #pragma unroll
     for (int e = 0; e < kChunks; ++e)
-        w[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * (tid + THREADS * e), 0, 0));
+        w[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * (tid + THREADS * e), 0, kLoadNT));
     auto chunk_col = [&](int e) { return 8 * (tid + THREADS * e); };
     auto key_at = [&](int j) {  // key j (0 .. E-1) of this thread
         const uint32_t v = w[j / 8][(j % 8) / 2];
