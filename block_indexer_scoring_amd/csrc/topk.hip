@@ -411,6 +411,7 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
     __shared__ int tied_idx[128];
     __shared__ uint32_t s_floor, s_T;
     __shared__ int s_need, s_num_cand;
+    __shared__ uint32_t s_range[kWaves];  // per wave: largest sub-run maximum << 16 | smallest nonzero one
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -506,6 +507,23 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
         sh.hist[b] = 0;
         hist_list[b] = 0;
     }
+    // The range of the sub-run maxima (top halves) per wave, published by
+    // the scan's barriers: when they span fewer than 2,048 values the floor
+    // takes one histogram pass.
+    {
+        uint32_t mx = 0u, mn = 0xffffu;
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            mx = max(mx, smax[j]);
+            mn = min(mn, smax[j] != 0u ? smax[j] : 0xffffu);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+            mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+        }
+        if (lane == 0) s_range[wave] = (mx << 16) | mn;
+    }
     int num_cand;
     block_exclusive_scan<THREADS>(cand, sh.wave_tmp, &num_cand);  // its barriers also publish the cleared histograms
     if (tid == 0) s_num_cand = num_cand;  // read after later barriers
@@ -523,20 +541,31 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
         // than 11 keep the list short when scores spread evenly over the
         // 11-bit bin.  1 (no filtering) when fewer than k sub-runs hold a
         // candidate.
+        uint32_t mx = 0u, mn = 0xffffu;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            mx = max(mx, s_range[w] >> 16);
+            mn = min(mn, s_range[w] & 0xffffu);
+        }
+        // One pass when the maxima span fewer than 2,048 values: bin b is the
+        // top half mn + b itself, so the bin of the k-th largest maximum is
+        // the 16-bit floor.
+        const bool one_pass = mn <= mx && mx - mn < 2048u;
 #pragma unroll
         for (int j = 0; j < kSub; ++j)
-            if (smax[j] != 0u) atomicAdd(&sh.hist[smax[j] >> 5], 1);
+            if (smax[j] != 0u) atomicAdd(&sh.hist[one_pass ? smax[j] - mn : smax[j] >> 5], 1);
         __syncthreads();
         if (tid < 64) {
             int above;
             const int bin = wave_find_bin<2048>(sh.hist, p.k, &above);
             if (lane == 0) {
-                s_floor = bin <= 0 ? 1u : ((uint32_t)bin << 21);
+                if (one_pass) s_floor = bin < 0 ? 1u : ((mn + (uint32_t)bin) << 16);
+                else s_floor = bin <= 0 ? 1u : ((uint32_t)bin << 21);
                 s_need = p.k - above;  // rank of the k-th largest maximum within its bin
             }
         }
         __syncthreads();
-        if (s_floor > 1u) {  // uniform; hist_list is still all zero here
+        if (!one_pass && s_floor > 1u) {  // uniform; hist_list is still all zero here
             const uint32_t b0 = s_floor >> 21;
 #pragma unroll
             for (int j = 0; j < kSub; ++j)
@@ -1224,6 +1253,7 @@ void topk_keys16_kernel(const uint16_t *keys, int64_t keys_stride, Keys16TopkPar
     __shared__ uint32_t list[kListCap];
     __shared__ int tied_idx[128];
     __shared__ uint32_t s_floor;
+    __shared__ uint32_t s_range[kWaves];  // per wave: largest chunk maximum << 16 | smallest nonzero one
     __shared__ int s_need, s_T;
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[kHeads * kDim];  // the row's queries, for rescoring
     const int tid = threadIdx.x;
@@ -1252,32 +1282,54 @@ void topk_keys16_kernel(const uint16_t *keys, int64_t keys_stride, Keys16TopkPar
     if (tid < 64) *reinterpret_cast<u32x4 *>(&q_lds[8 * tid]) = qv;
     const int64_t start = p.row_k_start[row];
     int32_t *out = p.out + row * p.out_stride;
-    __syncthreads();
 
-    // Floor: the lower edge of the 16-bit bin holding the k-th largest chunk
-    // maximum (top 11 bits, then the next 5 among the maxima in that bin);
-    // at least k keys are >= it.  1 when fewer than k chunks hold a
-    // candidate (every candidate is listed).
+    // Floor: the k-th largest chunk maximum; at least k keys are >= it.  When
+    // the maxima span fewer than 2,048 values (published per wave with the
+    // cleared histograms), one histogram pass over maximum - smallest gives
+    // it exactly; otherwise the lower edge of its 16-bit bin (top 11 bits,
+    // then the next 5 among the maxima in that bin).  1 when fewer than k
+    // chunks hold a candidate (every candidate is listed).
     uint32_t cmax[kChunks];
+    uint32_t mx = 0u, mn = 0xffffu;
 #pragma unroll
     for (int e = 0; e < kChunks; ++e) {
         uint32_t m = 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = max(m, max(w[e][i] & 0xffffu, w[e][i] >> 16));
         cmax[e] = m;
-        if (m != 0u) atomicAdd(&sh.hist[m >> 5], 1);
+        mx = max(mx, m);
+        mn = min(mn, m != 0u ? m : 0xffffu);
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    }
+    if (lane == 0) s_range[wave] = (mx << 16) | mn;
+    __syncthreads();
+    mx = 0u;
+    mn = 0xffffu;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        mx = max(mx, s_range[v] >> 16);
+        mn = min(mn, s_range[v] & 0xffffu);
+    }
+    const bool one_pass = mn <= mx && mx - mn < 2048u;
+#pragma unroll
+    for (int e = 0; e < kChunks; ++e)
+        if (cmax[e] != 0u) atomicAdd(&sh.hist[one_pass ? cmax[e] - mn : cmax[e] >> 5], 1);
     __syncthreads();
     if (tid < 64) {
         int above;
         const int bin = wave_find_bin<2048>(sh.hist, p.k, &above);
         if (lane == 0) {
-            s_floor = bin <= 0 ? 1u : ((uint32_t)bin << 5);
+            if (one_pass) s_floor = bin < 0 ? 1u : mn + (uint32_t)bin;
+            else s_floor = bin <= 0 ? 1u : ((uint32_t)bin << 5);
             s_need = p.k - above;
         }
     }
     __syncthreads();
-    if (s_floor > 1u) {  // uniform; hist_list is still all zero here
+    if (!one_pass && s_floor > 1u) {  // uniform; hist_list is still all zero here
         const uint32_t b0 = s_floor >> 5;
 #pragma unroll
         for (int e = 0; e < kChunks; ++e)
