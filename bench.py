@@ -247,8 +247,8 @@ def main(argv=None) -> int:
                     help="also run a plain device copy of this many MiB (PMC calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "the indexer path has no multi-GPU mode here.", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only (got --gpus {args.gpus}); "
+              "the indexer path has no multi-GPU mode.", file=sys.stderr)
         return 2
 
     import numpy as np
