@@ -290,6 +290,8 @@ __device__ __forceinline__ void place_picks(const ListView &list, const RowView 
 // passes over the list finish it.  Keys with other top halves compare with
 // T correctly either way.  tied_idx is 128 ints of scratch.  Requires at
 // least k listed keys.
+// kFull: the list already holds full keys (nothing is re-read).
+template <bool kFull>
 __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *cols, int n, int k,
                                                      const int *hist0, int *hist, int *tied_idx,
                                                      const float *x, int *need_out) {
@@ -347,8 +349,12 @@ __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *
         uint32_t key = 0u;
         if (lane < tied) {
             const int idx = tied_idx[lane];
-            key = order_key(x[cols[idx]]);
-            list[idx] = key;
+            if (kFull) {
+                key = list[idx];
+            } else {
+                key = order_key(x[cols[idx]]);
+                list[idx] = key;
+            }
         }
         // The kk-th largest of the tied keys (kk <= tied), which share the
         // top half: most significant bit first over the low half, counting
@@ -369,7 +375,7 @@ __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *
         return (top << 16) | t;
     }
     for (int i = lane; i < n; i += 64)
-        if ((list[i] >> 16) == top) list[i] = order_key(x[cols[i]]);
+        if (!kFull && (list[i] >> 16) == top) list[i] = order_key(x[cols[i]]);
     uint32_t prefix = top << 16, shift_mask = 0xffffu << 16;
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
@@ -392,7 +398,10 @@ __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *
 // The row's address, length and load shape come first among the kernel
 // arguments, where they are preloaded into SGPRs at wave launch: a
 // workgroup's row loads go out without waiting on an argument load.
-template <int E, int THREADS, int WPE>
+// kFull (rows of at most one per CU, where registers are plentiful): the
+// full keys are kept in registers as well and listed in full, so the select
+// never re-reads the row for the keys that share T's top half.
+template <int E, int THREADS, int WPE, bool kFull>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE)))
 void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t num_cols, int32_t vec_rows,
                           TopkParams p) {
@@ -428,9 +437,11 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
     // load e of the workgroup covers 16 * THREADS contiguous bytes, every
     // 128-byte line read by one instruction of one wave.
     uint32_t top16[(E + 1) / 2];
+    uint32_t full[kFull ? E : 1];
     uint32_t smax[kSub] = {};
     int cand = 0;
     auto absorb = [&](int e, uint32_t k) {
+        if (kFull) full[e] = k;
         cand += k != 0u;
         smax[e / kSubLen] = max(smax[e / kSubLen], k >> 16);
         if (e % 2 == 0) top16[e / 2] = k >> 16;
@@ -473,6 +484,7 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
                 const uint32_t u = __float_as_uint(f + 0.0f);
                 const uint32_t sgn = (uint32_t)((int32_t)u >> 31);
                 k[i] = is_cand ? u ^ (sgn | 0x80000000u) : 0u;
+                if (kFull) full[4 * e + i] = k[i];
                 wcand += (uint32_t)__popcll(__ballot(is_cand));
             }
             // Top halves, two to a register (even key low).
@@ -643,7 +655,7 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
                     const uint32_t t = key_top(4 * e + i);
                     const bool in = t >= floor_top2;
                     if (in) {
-                        list_key[w] = t << 16;
+                        list_key[w] = kFull ? full[4 * e + i] : t << 16;
                         list_col[w] = chunk_col(e) + i;
                         atomicAdd(&hist_list[t >> 5], 1);
                     }
@@ -652,7 +664,8 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
             }
             __syncthreads();
             if (tid < 64) {
-                const uint32_t T = wave_list_select(list_key, list_col, listed, p.k, hist_list, sh.hist, tied_idx, x, &need);
+                const uint32_t T =
+                    wave_list_select<kFull>(list_key, list_col, listed, p.k, hist_list, sh.hist, tied_idx, x, &need);
                 if (lane == 0) {
                     s_T = T;
                     s_need = need;
@@ -1458,21 +1471,21 @@ __global__ __launch_bounds__(1024) void topk_keys16_fallback_kernel(Keys16TopkPa
     }
 }
 
-template <int E, int THREADS, int WPE>
+template <int E, int THREADS, int WPE, bool kFull>
 hipError_t launch_resident(const TopkParams &p, hipStream_t stream) {
     // 16-byte loads for rows 16-byte aligned with whole 4-column chunks.
     const int32_t vec_rows = p.vec && (p.num_cols & 3) == 0;
-    return launch_kernel(topk_resident_kernel<E, THREADS, WPE>, dim3((unsigned)p.num_rows), dim3(THREADS), stream,
-                         p.logits, p.logits_stride, p.num_cols, vec_rows, p);
+    return launch_kernel(topk_resident_kernel<E, THREADS, WPE, kFull>, dim3((unsigned)p.num_rows), dim3(THREADS),
+                         stream, p.logits, p.logits_stride, p.num_cols, vec_rows, p);
 }
 
 // Columns per thread, rounded up to a multiple of 4 (16-byte loads), up to
 // MAXE; the caller routes longer rows elsewhere.
-template <int THREADS, int WPE, int MAXE, int E = 4>
+template <int THREADS, int WPE, int MAXE, bool kFull = false, int E = 4>
 hipError_t launch_config(const TopkParams &p, hipStream_t stream) {
     const int per = ((p.num_cols + THREADS - 1) / THREADS + 3) / 4 * 4;
-    if (per <= E || E == MAXE) return launch_resident<E, THREADS, WPE>(p, stream);
-    if constexpr (E + 4 <= MAXE) return launch_config<THREADS, WPE, MAXE, E + 4>(p, stream);
+    if (per <= E || E == MAXE) return launch_resident<E, THREADS, WPE, kFull>(p, stream);
+    if constexpr (E + 4 <= MAXE) return launch_config<THREADS, WPE, MAXE, kFull, E + 4>(p, stream);
     return hipErrorInvalidValue;  // not reached
 }
 
@@ -1494,11 +1507,14 @@ hipError_t launch_topk_candidates(const FusedTopkParams &p, hipStream_t stream) 
 hipError_t launch_topk(const TopkParams &p, hipStream_t stream, int num_cus) {
     // At most one row per CU: the latency of one row is the whole cost, so
     // 1024-thread rows (registers for four waves per SIMD), up to 64 columns
-    // per thread (fewer than 2^16 per row, which the packed counts need).
+    // per thread (fewer than 2^16 per row, which the packed counts need);
+    // up to 56 per thread the full keys also stay in registers, so the
+    // select re-reads nothing.
     // Many rows: 512-thread rows, four per CU (registers for eight waves per
     // SIMD), up to 56 columns per thread; longer rows, 1024-thread rows two
     // per CU.  Rows longer than these shapes hold are streamed.
     const bool few = p.num_rows <= (num_cus > 0 ? num_cus : 256);
+    if (few && p.num_cols <= 1024 * 56) return launch_config<1024, 4, 56, true>(p, stream);  // full keys kept
     if (few && p.num_cols < 65536) return launch_config<1024, 4, 64>(p, stream);
     if (p.num_cols > 32768)
         return launch_kernel(topk_streaming_kernel, dim3((unsigned)p.num_rows), dim3(1024), stream, p);
