@@ -294,12 +294,20 @@ __device__ __forceinline__ void place_picks(const ListView &list, const RowView 
 template <bool kFull>
 __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *cols, int n, int k,
                                                      const int *hist0, int *hist, int *tied_idx,
-                                                     const float *x, int *need_out) {
+                                                     const float *x, int *need_out, uint32_t rel_base) {
     const int lane = threadIdx.x & 63;
     int above;
     int kk = k;
     const int b0 = wave_find_bin<2048>(hist0, kk, &above);
     kk -= above;
+    uint32_t top;
+    int tied;
+    if (rel_base != 0u) {
+        // hist0 counts the listed top halves t by t - rel_base: the bin is
+        // T's top half itself, and no second pass over the list is needed.
+        top = rel_base + (uint32_t)b0;
+        tied = hist0[b0];
+    } else {
     // One wave: its LDS operations take effect in issue order.
     if (lane < 32) hist[lane] = 0;
 #pragma unroll 1
@@ -318,8 +326,9 @@ __device__ __forceinline__ uint32_t wave_list_select(uint32_t *list, const int *
     }
     const int b1 = wave_find_bin<32>(hist, kk, &above);
     kk -= above;
-    const uint32_t top = ((uint32_t)b0 << 5) | (uint32_t)b1;
-    const int tied = hist[b1];  // listed keys whose top half is `top`
+    top = ((uint32_t)b0 << 5) | (uint32_t)b1;
+    tied = hist[b1];  // listed keys whose top half is `top`
+    }
     if (kk == tied) {           // all of them are picked
         *need_out = kk;
         return top << 16;
@@ -597,6 +606,11 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
         // integer arithmetic: for 16-bit t and f, (t + 2^16 - f) >> 16 is
         // 1 exactly when t >= f.
         const uint32_t floor_top = max(floor >> 16, 1u);
+        // The list's histogram: by t - floor_top when every listed top half
+        // lies within 2,048 values of the floor (mx is the row's largest),
+        // so that its bin is the exact top half; else by the top 11 bits.
+        const uint32_t rel_base = mx >= floor_top && mx - floor_top < 2048u ? floor_top : 0u;
+        const uint32_t hist_shift = rel_base != 0u ? 0u : 5u;
         // The list in column order is chunk-major (chunk e of wave w covers
         // columns 2048e + 256w .. +255 at 512 threads): wave w's segment of
         // chunk e follows every segment of chunks before e and those of
@@ -657,7 +671,7 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
                     if (in) {
                         list_key[w] = kFull ? full[4 * e + i] : t << 16;
                         list_col[w] = chunk_col(e) + i;
-                        atomicAdd(&hist_list[t >> 5], 1);
+                        atomicAdd(&hist_list[(t - rel_base) >> hist_shift], 1);
                     }
                     w += in;
                 }
@@ -665,7 +679,8 @@ void topk_resident_kernel(const float *logits, int64_t logits_stride, int32_t nu
             __syncthreads();
             if (tid < 64) {
                 const uint32_t T =
-                    wave_list_select<kFull>(list_key, list_col, listed, p.k, hist_list, sh.hist, tied_idx, x, &need);
+                    wave_list_select<kFull>(list_key, list_col, listed, p.k, hist_list, sh.hist, tied_idx, x, &need,
+                                            rel_base);
                 if (lane == 0) {
                     s_T = T;
                     s_need = need;
