@@ -111,6 +111,35 @@ def test_topk_scores_spread_over_one_binade(rows, cols, k):
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
+@pytest.mark.parametrize("rows,cols,k", [(300, 27048, 512), (64, 25600, 512), (300, 26024, 512), (300, 5000, 100)])
+def test_topk_outliers_over_many_binades(rows, cols, k):
+    """Rows whose listed keys reach 16 or more binades above the floor (a
+    few huge outliers over unit-range scores, or log-uniform scores over
+    60 decades): the list is then counted by its top 11 bits and the select
+    takes two radix passes, where rows within 2,048 top-half values of the
+    floor take one."""
+    rng = np.random.default_rng(rows * 13 + cols + k)
+    x = rng.uniform(1.0, 2.0, (rows, cols)).astype(np.float32)
+    for r in range(rows):
+        kind = r % 4
+        if kind == 0:    # fewer outliers than k: the k-th key is a unit-range one
+            n = int(rng.integers(1, k))
+            x[r, rng.choice(cols, n, replace=False)] = 10.0 ** rng.uniform(10, 30, n)
+        elif kind == 1:  # more outliers than k, spread over 20 decades
+            n = min(cols, 2 * k + int(rng.integers(0, k)))
+            x[r, rng.choice(cols, n, replace=False)] = 10.0 ** rng.uniform(10, 30, n)
+        elif kind == 2:  # log-uniform over 60 decades
+            x[r] = (10.0 ** rng.uniform(-30, 30, cols)).astype(np.float32)
+        else:            # outliers tied at one value, with -inf and NaN cells
+            n = int(rng.integers(k // 2, 2 * k))
+            x[r, rng.choice(cols, n, replace=False)] = 1e25
+            x[r, ::7] = -np.inf
+            x[r, 3::11] = np.nan
+    got = _topk_gpu(x, k)
+    want = O.topk(x, k)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
 def test_topk_many_rows_and_strided_logits():
     rng = np.random.default_rng(5)
     big = rng.standard_normal((300, 700)).astype(np.float32)
